@@ -1,0 +1,208 @@
+/*
+ * smd.h -- C ABI of libsmd, sparse multi-head-latent-attention (MLA) decode
+ * for AMD Instinct MI355X (gfx950).
+ *
+ * The operation (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
+ * decode on gfx950", section Design): for every query token t and head h, a
+ * list of indices selects rows of one latent KV pool that all heads share.
+ * Each selected row is 512 wide: 448 NoPE dims followed by 64 RoPE dims.  The
+ * score is one 512-wide dot product s_j = softmax_scale * <q[t,h], k_{i_j}>;
+ * an online softmax over the selected rows also counts a per-head sink logit
+ * in its denominator; the output is the probability-weighted sum of the same
+ * 512-wide rows (V is the row itself).  Invalid indices contribute zero
+ * probability.
+ *
+ *   Z      = sum_{valid j} exp(s_j) + exp(sink_h)
+ *   out    = sum_{valid j} exp(s_j) / Z * row_{i_j}          (bf16, [T,H,512])
+ *   lse    = ln Z                                            (fp32, [T,H])
+ *
+ * The work may be split along the index list into FP32 partials plus their
+ * log-sum-exp and merged afterwards (aiter page "[ASM][HIP][MLA v4 nm] Split
+ * plan helper and persistent decode kernel", Summary part 1: uniform split
+ * plan, stage-2 merge that always reduces FP32 partials).
+ *
+ * Conventions for every entry point:
+ *  - Every data pointer is device memory owned by the caller.  The library
+ *    allocates no device memory and keeps no state between calls, so the
+ *    launches may be captured into a HIP graph.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are
+ *    asynchronous; no entry point synchronises the device.
+ *  - All arguments are checked on the host before any launch; on a failed
+ *    check nothing is launched or written, the call returns a negative
+ *    SMD_ERR_* code and smd_last_error() describes the failure.
+ *  - Index values are data, not arguments: any index i < 0 or i >= num_rows
+ *    is masked (contributes exactly zero), never an error.
+ *  - bf16 is the 16-bit brain float format; fp32 is IEEE binary32.
+ */
+#ifndef SMD_H_
+#define SMD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  SMD_OK = 0,
+  SMD_ERR_INVALID_ARG = -1, /* a pointer, size, stride or alignment is wrong */
+  SMD_ERR_UNSUPPORTED = -2, /* a shape outside the supported set            */
+  SMD_ERR_WORKSPACE = -3,   /* workspace missing or too small               */
+  SMD_ERR_HIP = -4          /* a HIP launch reported an error               */
+};
+
+enum {
+  SMD_KV_BF16 = 0,          /* rows are 512 bf16 values                                */
+  SMD_KV_FP8_E4M3_UE8M0 = 1 /* 448 OCP E4M3FN bytes + 7 UE8M0 codes + 64 bf16 RoPE dims */
+};
+
+/* Largest split count of the split-KV entry points. */
+#define SMD_MAX_SPLITS 32
+/* Index positions of one split are a multiple of this (except the last). */
+#define SMD_SPLIT_ALIGN 64
+
+/* Message describing this thread's most recent failure ("" if none). */
+const char *smd_last_error(void);
+
+/*
+ * A latent KV pool: num_rows rows, each 448 NoPE dims then 64 RoPE dims.
+ *
+ * SMD_KV_BF16:
+ *   nope  bf16 [num_rows, >=448], row stride nope_stride ELEMENTS
+ *   rope  bf16 [num_rows, >=64],  row stride rope_stride ELEMENTS
+ *   scale must be NULL.  A packed [N,512] pool is nope = base,
+ *   rope = base + 448, both strides 512.
+ * SMD_KV_FP8_E4M3_UE8M0 (vLLM page, Design: UE8M0 codes, one per 64-dim block):
+ *   nope  uint8 [num_rows, >=448] OCP E4M3FN, row stride nope_stride BYTES
+ *   scale uint8 [num_rows, >=8]: 7 UE8M0 codes + 1 pad byte per row (all
+ *         8 bytes are read), row stride scale_stride BYTES, a multiple of 4,
+ *         base 4-byte aligned; NoPE dim d decodes to
+ *         e4m3(byte_d) * 2^(scale[d/64] - 127)
+ *   rope  bf16 [num_rows, >=64], row stride rope_stride ELEMENTS (not scaled)
+ * Alignment: nope and rope base addresses and row strides in bytes must be
+ * multiples of 16.  The struct itself is read during the call only.
+ */
+typedef struct smd_kv_pool {
+  int32_t dtype; /* SMD_KV_* */
+  int32_t reserved;
+  int64_t num_rows;
+  const void *nope;
+  int64_t nope_stride;
+  const void *rope;
+  int64_t rope_stride;
+  const uint8_t *scale;
+  int64_t scale_stride;
+} smd_kv_pool;
+
+/*
+ * Cost model of the host split planner (aiter page, Summary part 1: the
+ * split count minimises workgroup waves x per-wave KV time plus the
+ * partial-write / stage-2 cost of splitting).  All times in picoseconds.
+ *
+ *   G        = ceil(M / min(M, 64)), M = num_heads * q_per_seq
+ *   waves(s) = ceil(num_seqs * G * s / (num_cus * wg_per_cu))
+ *   tiles(s) = ceil(ceil(kv_len / s) / 64)
+ *   cost(s)  = waves(s) * (fixed + tile[kv_dtype] * tiles(s))
+ *            + (s > 1) * (merge + part * num_seqs * M * s)
+ *
+ * s ranges over [1, min(cap, ceil(kv_len / 64))] with cap = short_cap when
+ * kv_len < long_kv, else long_cap (both <= SMD_MAX_SPLITS); the smallest s of
+ * minimum cost wins.
+ */
+typedef struct smd_plan_model {
+  int64_t fixed_ps;   /* per-wave fixed cost                  */
+  int64_t tile_ps[2]; /* per 64-row tile, by kv dtype          */
+  int64_t merge_ps;   /* fixed cost of the stage-2 merge       */
+  int64_t part_ps;    /* per query row and split (write+read)  */
+  int32_t wg_per_cu;  /* resident decode workgroups per CU     */
+  int32_t short_cap;  /* split cap when kv_len < long_kv        */
+  int32_t long_cap;   /* split cap otherwise                   */
+  int32_t long_kv;    /* threshold between the two caps        */
+} smd_plan_model;
+
+/*
+ * Host split planner: the number of KV splits s in [1, SMD_MAX_SPLITS] for the
+ * split-KV decode of `num_seqs` index rows, each shared by q_per_seq tokens
+ * of num_heads heads, with kv_len indices per row.  Pure host integer
+ * arithmetic with the library's fitted MI355X coefficients; touches no
+ * device and depends on nothing but its arguments (aiter page, Summary
+ * part 1).  num_cus <= 0 means 256 (MI355X).  Returns s, or a negative
+ * SMD_ERR_* code for negative sizes or an unsupported kv_dtype.
+ * num_seqs == 0 or kv_len == 0 returns 1.
+ */
+int smd_plan_num_kv_splits(int32_t num_seqs, int32_t num_heads, int32_t q_per_seq, int32_t kv_len,
+                           int32_t kv_dtype, int32_t num_cus);
+
+/* The same planner with explicit coefficients (model must not be NULL). */
+int smd_plan_num_kv_splits_model(int32_t num_seqs, int32_t num_heads, int32_t q_per_seq,
+                                 int32_t kv_len, int32_t kv_dtype, int32_t num_cus,
+                                 const smd_plan_model *model);
+
+/* Copy the library's built-in coefficient table into *model. */
+int smd_plan_default_model(smd_plan_model *model);
+
+/*
+ * Index positions [*begin, *end) of split `split` out of num_splits over a
+ * list of kv_len indices: chunk = roundup(ceil(kv_len / num_splits), 64),
+ * split r covers [min(r*chunk, kv_len), min((r+1)*chunk, kv_len)).  Trailing
+ * splits may be empty.  This is the rule the decode kernels apply.
+ */
+int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t *begin,
+                     int32_t *end);
+
+/*
+ * Split-KV sparse MLA decode over dense index rows.
+ *
+ *  q_nope   bf16 [num_tokens, num_heads, 448], contiguous, 16-byte aligned
+ *  q_rope   bf16 [num_tokens, num_heads, 64],  contiguous, 16-byte aligned
+ *  num_heads in {16, 32, 64, 128}; q_per_seq in [1, 8]; num_tokens a
+ *           multiple of q_per_seq.  Token t uses index row t / q_per_seq
+ *           (multi-token prediction positions share their row; no causal
+ *           mask among them).
+ *  kv       the pool (see smd_kv_pool).
+ *  indices  int32 [num_tokens / q_per_seq, >= topk], row stride
+ *           indices_stride elements; topk >= 0.
+ *  sink     fp32 [num_heads] logits in the scaled score domain, or NULL.
+ *  softmax_scale multiplies every dot product.
+ *  num_splits in [1, SMD_MAX_SPLITS]; split r covers the positions
+ *           smd_split_bounds() gives.
+ *  partial_o   fp32 [num_tokens, num_heads, num_splits, 512]
+ *  partial_lse fp32 [num_tokens, num_heads, num_splits]
+ *           Required when num_splits > 1 or out == NULL.  Partial r holds
+ *           o_r = sum_{j in r} e^{s_j - lse_r} row_j and
+ *           lse_r = ln sum_{j in r} e^{s_j} (no sink); an empty or
+ *           all-invalid split holds o_r = 0, lse_r = -inf.
+ *  out      bf16 [num_tokens, num_heads, 512] or NULL (partials only)
+ *  lse      fp32 [num_tokens, num_heads] or NULL; ln Z including the sink.
+ *  With num_splits > 1 and out != NULL the call also launches the merge
+ *  (smd_merge_partials).  A row with no valid index gets out = 0 and
+ *  lse = sink_h (-inf without a sink).  topk == 0 or num_tokens == 0
+ *  launches nothing.
+ */
+int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                          int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
+                          const int32_t *indices, int64_t indices_stride, int32_t topk,
+                          const float *sink, float softmax_scale, int32_t num_splits,
+                          float *partial_o, float *partial_lse, void *out, float *lse,
+                          void *stream);
+
+/*
+ * Stage-2 merge (aiter page, Summary part 1: always reduce the FP32
+ * partials, even with one split per row):
+ *   LSE = ln(sum_r e^{lse_r} + e^{sink_h}),  out = sum_r e^{lse_r - LSE} o_r.
+ *  partial_o fp32 [num_tokens, num_heads, num_splits, 512], partial_lse fp32
+ *  [num_tokens, num_heads, num_splits]; sink fp32 [num_heads] or NULL;
+ *  out bf16 [num_tokens, num_heads, 512] (required); lse fp32
+ *  [num_tokens, num_heads] or NULL.  num_splits in [1, 1024].  No finite
+ *  term and no sink gives out = 0, lse = -inf.
+ */
+int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t num_tokens,
+                       int32_t num_heads, int32_t num_splits, const float *sink, void *out,
+                       float *lse, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMD_H_ */

@@ -1,0 +1,311 @@
+"""Python binding of libsmd (sparse MLA decode for MI355X).
+
+Argument marshalling only: every step of the decode runs in the library's HIP
+kernels.  Tensors supply device memory and the current HIP stream; shapes and
+dtypes are checked here, everything else by the library before it launches.
+The library is loaded from this package directory and must have been built
+(``python -m sparse_mla_decode_index_amd.build``); there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from pathlib import Path
+from typing import Optional
+
+import torch
+
+NOPE = 448
+ROPE = 64
+DIM = 512
+MAX_SPLITS = 32
+SPLIT_ALIGN = 64
+
+KV_BF16 = 0
+KV_FP8_E4M3_UE8M0 = 1
+
+_LIB_PATH = Path(__file__).resolve().parent / "libsmd.so"
+_lib = None
+
+
+class SmdError(RuntimeError):
+    """A libsmd entry point returned a negative status."""
+
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed ({code}): {msg}")
+        self.code = code
+
+
+class _KVPool(ctypes.Structure):
+    _fields_ = [
+        ("dtype", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("num_rows", ctypes.c_int64),
+        ("nope", ctypes.c_void_p),
+        ("nope_stride", ctypes.c_int64),
+        ("rope", ctypes.c_void_p),
+        ("rope_stride", ctypes.c_int64),
+        ("scale", ctypes.c_void_p),
+        ("scale_stride", ctypes.c_int64),
+    ]
+
+
+class PlanModel(ctypes.Structure):
+    """Coefficients of the host split planner's cost model (picoseconds)."""
+
+    _fields_ = [
+        ("fixed_ps", ctypes.c_int64),
+        ("tile_ps", ctypes.c_int64 * 2),
+        ("merge_ps", ctypes.c_int64),
+        ("part_ps", ctypes.c_int64),
+        ("wg_per_cu", ctypes.c_int32),
+        ("short_cap", ctypes.c_int32),
+        ("long_cap", ctypes.c_int32),
+        ("long_kv", ctypes.c_int32),
+    ]
+
+
+def library_path() -> Path:
+    return _LIB_PATH
+
+
+def lib() -> ctypes.CDLL:
+    """Load libsmd.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not _LIB_PATH.exists():
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with "
+                           "`python -m sparse_mla_decode_index_amd.build`")
+    L = ctypes.CDLL(str(_LIB_PATH))
+    i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+    L.smd_last_error.restype = ctypes.c_char_p
+    L.smd_last_error.argtypes = []
+    L.smd_plan_num_kv_splits.restype = ctypes.c_int
+    L.smd_plan_num_kv_splits.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.smd_plan_num_kv_splits_model.restype = ctypes.c_int
+    L.smd_plan_num_kv_splits_model.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(PlanModel)]
+    L.smd_plan_default_model.restype = ctypes.c_int
+    L.smd_plan_default_model.argtypes = [ctypes.POINTER(PlanModel)]
+    L.smd_split_bounds.restype = ctypes.c_int
+    L.smd_split_bounds.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    L.smd_sparse_mla_decode.restype = ctypes.c_int
+    L.smd_sparse_mla_decode.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
+                                        vp, f32, i32, vp, vp, vp, vp, vp]
+    L.smd_merge_partials.restype = ctypes.c_int
+    L.smd_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    _lib = L
+    return L
+
+
+def _check(fn: str, rc: int) -> int:
+    if rc < 0:
+        raise SmdError(fn, rc, lib().smd_last_error().decode())
+    return rc
+
+
+def _ptr(t: Optional[torch.Tensor]) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _need(t: torch.Tensor, name: str, dtype, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} must be on {device}, got {t.device}")
+
+
+# ----------------------------------------------------------------------------
+# KV pools
+# ----------------------------------------------------------------------------
+@dataclass
+class KVPool:
+    """A latent KV pool on the device: rows of 448 NoPE dims then 64 RoPE dims.
+
+    bf16:  nope bf16 [N, >=448] and rope bf16 [N, >=64] (row-strided views; a
+           packed [N, 512] tensor gives nope = kv[:, :448], rope = kv[:, 448:]).
+    fp8:   nope uint8 [N, >=448] OCP E4M3FN bytes, scale uint8 [N, >=7] UE8M0
+           codes (one per 64-dim NoPE block), rope bf16 [N, >=64].
+    """
+
+    dtype: int
+    nope: torch.Tensor
+    rope: torch.Tensor
+    scale: Optional[torch.Tensor] = None
+
+    @staticmethod
+    def bf16(kv: torch.Tensor) -> "KVPool":
+        _need(kv, "kv", torch.bfloat16)
+        if kv.dim() != 2 or kv.shape[1] < DIM or kv.stride(1) != 1:
+            raise ValueError("kv must be a row-major [N, 512] bf16 tensor")
+        return KVPool(KV_BF16, kv[:, :NOPE], kv[:, NOPE:DIM])
+
+    @staticmethod
+    def fp8(nope: torch.Tensor, scale: torch.Tensor, rope: torch.Tensor) -> "KVPool":
+        _need(nope, "nope", torch.uint8)
+        _need(scale, "scale", torch.uint8)
+        _need(rope, "rope", torch.bfloat16)
+        return KVPool(KV_FP8_E4M3_UE8M0, nope, rope, scale)
+
+    @property
+    def num_rows(self) -> int:
+        return self.nope.shape[0]
+
+    @property
+    def device(self):
+        return self.nope.device
+
+    def _struct(self) -> _KVPool:
+        if self.nope.stride(-1) != 1 or self.rope.stride(-1) != 1:
+            raise ValueError("pool rows must be contiguous in their last dimension")
+        s = _KVPool()
+        s.dtype = self.dtype
+        s.num_rows = self.num_rows
+        s.nope = self.nope.data_ptr()
+        s.nope_stride = self.nope.stride(0)
+        s.rope = self.rope.data_ptr()
+        s.rope_stride = self.rope.stride(0)
+        if self.scale is not None:
+            if self.scale.stride(-1) != 1:
+                raise ValueError("scale rows must be contiguous")
+            s.scale = self.scale.data_ptr()
+            s.scale_stride = self.scale.stride(0)
+        else:
+            s.scale = None
+            s.scale_stride = 0
+        return s
+
+
+# ----------------------------------------------------------------------------
+# planner
+# ----------------------------------------------------------------------------
+def plan_num_kv_splits(num_seqs: int, num_heads: int, kv_len: int, q_per_seq: int = 1,
+                       kv_dtype: int = KV_BF16, num_cus: int = 0,
+                       model: Optional[PlanModel] = None) -> int:
+    """Host split count in [1, 32] from the cost model (no device work)."""
+    L = lib()
+    if model is None:
+        return _check("smd_plan_num_kv_splits",
+                      L.smd_plan_num_kv_splits(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype, num_cus))
+    return _check("smd_plan_num_kv_splits_model",
+                  L.smd_plan_num_kv_splits_model(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype,
+                                                 num_cus, ctypes.byref(model)))
+
+
+def plan_default_model() -> PlanModel:
+    m = PlanModel()
+    _check("smd_plan_default_model", lib().smd_plan_default_model(ctypes.byref(m)))
+    return m
+
+
+def split_bounds(kv_len: int, num_splits: int, split: int) -> tuple[int, int]:
+    b, e = ctypes.c_int32(), ctypes.c_int32()
+    _check("smd_split_bounds", lib().smd_split_bounds(kv_len, num_splits, split, ctypes.byref(b),
+                                                       ctypes.byref(e)))
+    return b.value, e.value
+
+
+# ----------------------------------------------------------------------------
+# decode and merge
+# ----------------------------------------------------------------------------
+def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, indices: torch.Tensor,
+                      sink: Optional[torch.Tensor], softmax_scale: float, *,
+                      num_splits: Optional[int] = None, q_per_seq: int = 1,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      partial_o: Optional[torch.Tensor] = None,
+                      partial_lse: Optional[torch.Tensor] = None,
+                      partials_only: bool = False):
+    """Split-KV sparse MLA decode.
+
+    q_nope bf16 [T,H,448], q_rope bf16 [T,H,64], indices int32 [T/q_per_seq, K]
+    (row stride free), sink fp32 [H] or None.  Returns (out, lse) — bf16
+    [T,H,512] and fp32 [T,H] — or, with partials_only, (partial_o, partial_lse)
+    of shapes [T,H,s,512] and [T,H,s].  num_splits=None asks the host planner.
+    """
+    dev = q_nope.device
+    _need(q_nope, "q_nope", torch.bfloat16, device=dev)
+    if q_nope.dim() != 3 or q_nope.shape[2] != NOPE:
+        raise ValueError("q_nope must be [T, H, 448]")
+    T, H, _ = q_nope.shape
+    _need(q_rope, "q_rope", torch.bfloat16, (T, H, ROPE), dev)
+    if not (q_nope.is_contiguous() and q_rope.is_contiguous()):
+        raise ValueError("q_nope and q_rope must be contiguous")
+    _need(indices, "indices", torch.int32, device=dev)
+    if indices.dim() != 2 or indices.shape[0] * q_per_seq != T or (indices.shape[1] > 0 and indices.stride(1) != 1):
+        raise ValueError("indices must be [T / q_per_seq, K] with unit column stride")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,), dev)
+    if kv.device != dev:
+        raise ValueError("kv pool must be on the same device as q")
+    K = indices.shape[1]
+    if num_splits is None:
+        num_splits = plan_num_kv_splits(T // q_per_seq, H, K, q_per_seq,
+                                        kv.dtype if K > 0 else KV_BF16)
+    need_partials = partials_only or num_splits > 1
+    if need_partials:
+        if partial_o is None:
+            partial_o = torch.empty((T, H, num_splits, DIM), dtype=torch.float32, device=dev)
+        if partial_lse is None:
+            partial_lse = torch.empty((T, H, num_splits), dtype=torch.float32, device=dev)
+        _need(partial_o, "partial_o", torch.float32, (T, H, num_splits, DIM), dev)
+        _need(partial_lse, "partial_lse", torch.float32, (T, H, num_splits), dev)
+    if not partials_only:
+        if out is None:
+            out = torch.empty((T, H, DIM), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
+        _need(lse, "lse", torch.float32, (T, H), dev)
+    pool = kv._struct()
+    rc = lib().smd_sparse_mla_decode(
+        q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool),
+        indices.data_ptr() if indices.numel() else None, indices.stride(0) if K > 0 else 0, K,
+        _ptr(sink), float(softmax_scale), num_splits,
+        _ptr(partial_o), _ptr(partial_lse),
+        None if partials_only else out.data_ptr(), None if partials_only else lse.data_ptr(),
+        _stream(q_nope))
+    _check("smd_sparse_mla_decode", rc)
+    if partials_only:
+        return partial_o, partial_lse
+    return out, lse
+
+
+def merge_partials(partial_o: torch.Tensor, partial_lse: torch.Tensor, sink: Optional[torch.Tensor], *,
+                   out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Stage-2 merge of FP32 partials [T,H,s,512] + [T,H,s] into bf16 out and fp32 lse."""
+    dev = partial_o.device
+    _need(partial_o, "partial_o", torch.float32, device=dev)
+    if partial_o.dim() != 4 or partial_o.shape[3] != DIM or not partial_o.is_contiguous():
+        raise ValueError("partial_o must be contiguous [T, H, s, 512]")
+    T, H, S, _ = partial_o.shape
+    _need(partial_lse, "partial_lse", torch.float32, (T, H, S), dev)
+    if not partial_lse.is_contiguous():
+        raise ValueError("partial_lse must be contiguous")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,), dev)
+    if out is None:
+        out = torch.empty((T, H, DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
+    _need(lse, "lse", torch.float32, (T, H), dev)
+    rc = lib().smd_merge_partials(partial_o.data_ptr(), partial_lse.data_ptr(), T, H, S, _ptr(sink),
+                                  out.data_ptr(), lse.data_ptr(), _stream(partial_o))
+    _check("smd_merge_partials", rc)
+    return out, lse
+
+
+__all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
+           "sparse_mla_decode", "merge_partials", "lib", "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0"]
+
+if os.environ.get("SMD_EAGER_LOAD") == "1":
+    lib()

@@ -1,0 +1,230 @@
+// C ABI entry points of libsmd: argument checks on the host, then kernel
+// launches on the caller's stream.  Nothing is allocated and nothing is
+// launched when a check fails.
+#include <hip/hip_runtime.h>
+#include <limits.h>
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/smd.h"
+#include "smd_internal.h"
+
+namespace smd {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+
+static bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+static bool heads_ok(int32_t h) { return h == 16 || h == 32 || h == 64 || h == 128; }
+
+// Checks shared by the decode entry points.  On success fills the pool part of `a`.
+static int check_pool(const char *fn, const smd_kv_pool *kv, DecodeArgs &a) {
+  if (!kv) {
+    set_error("%s: kv pool is NULL", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (kv->dtype != SMD_KV_BF16 && kv->dtype != SMD_KV_FP8_E4M3_UE8M0) {
+    set_error("%s: unknown kv dtype %d", fn, kv->dtype);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (kv->num_rows < 0) {
+    set_error("%s: negative num_rows", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!kv->nope || !kv->rope) {
+    set_error("%s: kv nope/rope pointer is NULL", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!aligned16(kv->nope) || !aligned16(kv->rope)) {
+    set_error("%s: kv nope/rope base must be 16-byte aligned", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  const bool fp8 = kv->dtype == SMD_KV_FP8_E4M3_UE8M0;
+  const int64_t nope_b = fp8 ? kv->nope_stride : kv->nope_stride * 2;
+  const int64_t rope_b = kv->rope_stride * 2;
+  if (kv->nope_stride < kNope || kv->rope_stride < kRope) {
+    set_error("%s: kv row strides (%lld, %lld) below the row widths (448, 64)", fn,
+              (long long)kv->nope_stride, (long long)kv->rope_stride);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if ((nope_b & 15) || (rope_b & 15)) {
+    set_error("%s: kv row strides must be multiples of 16 bytes", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (fp8) {
+    if (!kv->scale) {
+      set_error("%s: fp8 pool needs a scale (UE8M0 code) array", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (kv->scale_stride < 8 || (kv->scale_stride & 3) || ((uintptr_t)kv->scale & 3)) {
+      set_error("%s: scale rows must hold 8 bytes (7 codes + pad) with a stride that is a multiple "
+                "of 4 and a 4-byte aligned base (stride %lld)", fn, (long long)kv->scale_stride);
+      return SMD_ERR_INVALID_ARG;
+    }
+  } else if (kv->scale) {
+    set_error("%s: bf16 pool must not pass a scale array", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  a.kv_nope = (const uint8_t *)kv->nope;
+  a.nope_stride_b = nope_b;
+  a.kv_rope = (const uint8_t *)kv->rope;
+  a.rope_stride_b = rope_b;
+  a.kv_scale = kv->scale;
+  a.scale_stride_b = kv->scale_stride;
+  a.num_rows = kv->num_rows;
+  return SMD_OK;
+}
+
+static int waves_for(int32_t M) { return M >= 64 ? 4 : M / 16; }
+
+}  // namespace smd
+
+using namespace smd;
+
+extern "C" const char *smd_last_error(void) { return g_err; }
+
+extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                     int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
+                                     const int32_t *indices, int64_t indices_stride, int32_t topk,
+                                     const float *sink, float softmax_scale, int32_t num_splits,
+                                     float *partial_o, float *partial_lse, void *out, float *lse,
+                                     void *stream) {
+  static const char *fn = "smd_sparse_mla_decode";
+  g_err[0] = 0;
+  if (num_tokens < 0 || topk < 0 || indices_stride < 0) {
+    set_error("%s: negative size (num_tokens=%d topk=%d indices_stride=%lld)", fn, num_tokens, topk,
+              (long long)indices_stride);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!heads_ok(num_heads)) {
+    set_error("%s: num_heads=%d not in {16,32,64,128}", fn, num_heads);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (q_per_seq < 1 || q_per_seq > 8) {
+    set_error("%s: q_per_seq=%d not in [1,8]", fn, q_per_seq);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (num_tokens % q_per_seq) {
+    set_error("%s: num_tokens=%d is not a multiple of q_per_seq=%d", fn, num_tokens, q_per_seq);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (num_splits < 1 || num_splits > SMD_MAX_SPLITS) {
+    set_error("%s: num_splits=%d not in [1,%d]", fn, num_splits, SMD_MAX_SPLITS);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!isfinite(softmax_scale)) {
+    set_error("%s: softmax_scale is not finite", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  DecodeArgs a = {};
+  int rc = check_pool(fn, kv, a);
+  if (rc) return rc;
+  if (num_tokens > 0 && topk > 0) {
+    if (!q_nope || !q_rope || !indices) {
+      set_error("%s: q_nope, q_rope and indices are required", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (!aligned16(q_nope) || !aligned16(q_rope)) {
+      set_error("%s: q_nope/q_rope must be 16-byte aligned", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (indices_stride < topk && num_tokens / q_per_seq > 1) {
+      set_error("%s: indices_stride=%lld below topk=%d", fn, (long long)indices_stride, topk);
+      return SMD_ERR_INVALID_ARG;
+    }
+  }
+  const bool need_partials = num_splits > 1 || out == nullptr;
+  if (need_partials && (!partial_o || !partial_lse)) {
+    set_error("%s: partial_o and partial_lse are required when num_splits > 1 or out is NULL", fn);
+    return SMD_ERR_WORKSPACE;
+  }
+  if (partial_o && !aligned16(partial_o)) {
+    set_error("%s: partial_o must be 16-byte aligned", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (out && !aligned16(out)) {
+    set_error("%s: out must be 16-byte aligned", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (num_tokens == 0 || topk == 0) return SMD_OK;
+
+  const int32_t M = num_heads * q_per_seq;
+  const int waves = waves_for(M);
+  const int32_t rows = num_tokens / q_per_seq;
+  // chunk = roundup(ceil(topk / s), 64), as smd_split_bounds.
+  const int64_t per = ((int64_t)topk + num_splits - 1) / num_splits;
+  const int64_t chunk = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+  a.q_nope = (const uint16_t *)q_nope;
+  a.q_rope = (const uint16_t *)q_rope;
+  a.indices = indices;
+  a.indices_stride = indices_stride;
+  a.topk = topk;
+  a.chunk = (int32_t)(chunk < INT32_MAX ? chunk : INT32_MAX);
+  a.sink = sink;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.H = num_heads;
+  a.qps = q_per_seq;
+  a.M = M;
+  a.S = num_splits;
+  a.num_units = rows * num_splits;
+  a.G = M / (waves * 16);
+  a.part_o = need_partials ? partial_o : nullptr;
+  a.part_lse = need_partials ? partial_lse : nullptr;
+  a.out = need_partials ? nullptr : (uint16_t *)out;
+  a.lse = need_partials ? nullptr : lse;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_decode(a, waves, kv->dtype == SMD_KV_FP8_E4M3_UE8M0, st);
+  if (e != hipSuccess) {
+    set_error("%s: decode launch failed: %s", fn, hipGetErrorString(e));
+    return SMD_ERR_HIP;
+  }
+  if (need_partials && out) {
+    e = launch_merge(partial_o, partial_lse, num_tokens * num_heads, num_heads, num_splits, sink,
+                     (uint16_t *)out, lse, st);
+    if (e != hipSuccess) {
+      set_error("%s: merge launch failed: %s", fn, hipGetErrorString(e));
+      return SMD_ERR_HIP;
+    }
+  }
+  return SMD_OK;
+}
+
+extern "C" int smd_merge_partials(const float *partial_o, const float *partial_lse,
+                                  int32_t num_tokens, int32_t num_heads, int32_t num_splits,
+                                  const float *sink, void *out, float *lse, void *stream) {
+  static const char *fn = "smd_merge_partials";
+  g_err[0] = 0;
+  if (num_tokens < 0 || num_heads < 1) {
+    set_error("%s: invalid num_tokens=%d num_heads=%d", fn, num_tokens, num_heads);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (num_splits < 1 || num_splits > 1024) {
+    set_error("%s: num_splits=%d not in [1,1024]", fn, num_splits);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (num_tokens == 0) return SMD_OK;
+  if (!partial_o || !partial_lse || !out) {
+    set_error("%s: partial_o, partial_lse and out are required", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!aligned16(partial_o) || !aligned16(out)) {
+    set_error("%s: partial_o and out must be 16-byte aligned", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  hipError_t e = launch_merge(partial_o, partial_lse, num_tokens * num_heads, num_heads, num_splits,
+                              sink, (uint16_t *)out, lse, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("%s: merge launch failed: %s", fn, hipGetErrorString(e));
+    return SMD_ERR_HIP;
+  }
+  return SMD_OK;
+}

@@ -1,0 +1,48 @@
+// Internal declarations shared by the host entry points and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace smd {
+
+constexpr int kNope = 448;
+constexpr int kRope = 64;
+constexpr int kDim = 512;
+constexpr int kSplitAlign = 64;
+
+// Arguments of the split-KV decode kernel.  Pointers are device pointers.
+struct DecodeArgs {
+  const uint16_t *q_nope;  // bf16 [T, H, 448]
+  const uint16_t *q_rope;  // bf16 [T, H, 64]
+  const uint8_t *kv_nope;  // row base; bf16 or e4m3 bytes
+  int64_t nope_stride_b;   // bytes
+  const uint8_t *kv_rope;  // bf16 rows
+  int64_t rope_stride_b;   // bytes
+  const uint8_t *kv_scale; // UE8M0 codes (fp8 pools)
+  int64_t scale_stride_b;  // bytes
+  int64_t num_rows;
+  const int32_t *indices;
+  int64_t indices_stride;  // elements
+  int32_t topk;
+  int32_t chunk;           // index positions per split (multiple of 64)
+  const float *sink;       // [H] or null
+  float scale_log2;        // softmax_scale * log2(e)
+  int32_t H, qps, M;       // heads, tokens per index row, M = H * qps
+  int32_t S;               // splits
+  int32_t num_units;       // index rows * S
+  int32_t G;               // row groups per index row
+  float *part_o;           // [T, H, S, 512] or null
+  float *part_lse;         // [T, H, S] or null
+  uint16_t *out;           // bf16 [T, H, 512] (direct output when S == 1)
+  float *lse;              // [T, H] or null
+};
+
+// Launch the split-KV decode.  waves = query-row blocks of 16 per workgroup.
+hipError_t launch_decode(const DecodeArgs &a, int waves, bool fp8, hipStream_t stream);
+
+hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
+                        int32_t S, const float *sink, uint16_t *out, float *lse,
+                        hipStream_t stream);
+
+}  // namespace smd

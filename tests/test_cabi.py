@@ -1,0 +1,192 @@
+"""CPU tests of libsmd's C ABI: exported symbols, host-side argument checks
+(which run before any HIP call, so no GPU is needed), and the integer host
+logic -- split bounds and the planner -- bit-exact against the oracle."""
+import ctypes
+import re
+from pathlib import Path
+
+import numpy as np
+import pytest
+
+import sparse_mla_decode_index_amd as smd
+from oracle import plan_ref, ref
+
+HEADER = Path(__file__).resolve().parents[1] / "include" / "smd.h"
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(smd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = smd.lib()
+    names = declared_functions()
+    assert "smd_sparse_mla_decode" in names and "smd_merge_partials" in names
+    assert "smd_plan_num_kv_splits" in names
+    for n in names:
+        assert hasattr(L, n), f"libsmd.so does not export {n}"
+
+
+def test_split_bounds_bit_exact_vs_oracle():
+    rng = np.random.default_rng(0)
+    cases = [(0, 1), (1, 1), (63, 2), (64, 4), (2176, 4), (65664, 32), (2048, 8)]
+    cases += [(int(rng.integers(0, 100000)), int(rng.integers(1, 33))) for _ in range(300)]
+    for K, s in cases:
+        want = ref.split_bounds(K, s)
+        got = [smd.split_bounds(K, s, r) for r in range(s)]
+        assert got == want, (K, s)
+
+
+def test_split_bounds_rejects_bad_args():
+    with pytest.raises(smd.SmdError):
+        smd.split_bounds(10, 0, 0)
+    with pytest.raises(smd.SmdError):
+        smd.split_bounds(10, 4, 4)
+    with pytest.raises(smd.SmdError):
+        smd.split_bounds(-1, 4, 0)
+
+
+def _model_pair(rng):
+    fixed = int(rng.integers(1, 10_000_000))
+    tiles = (int(rng.integers(1, 3_000_000)), int(rng.integers(1, 3_000_000)))
+    merge = int(rng.integers(0, 10_000_000))
+    part = int(rng.integers(0, 5_000))
+    wg = int(rng.integers(1, 4))
+    sc = int(rng.integers(1, 33))
+    lc = int(rng.integers(1, 33))
+    lk = int(rng.integers(1, 20000))
+    c = smd.PlanModel()
+    c.fixed_ps, c.merge_ps, c.part_ps = fixed, merge, part
+    c.tile_ps[0], c.tile_ps[1] = tiles
+    c.wg_per_cu, c.short_cap, c.long_cap, c.long_kv = wg, sc, lc, lk
+    return c, plan_ref.PlanModel(fixed, tiles, merge, part, wg, sc, lc, lk)
+
+
+def test_planner_formula_bit_exact_vs_oracle():
+    rng = np.random.default_rng(1)
+    for _ in range(400):
+        cm, pm = _model_pair(rng)
+        args = (int(rng.integers(0, 300)), int(rng.choice([16, 32, 64, 128])), int(rng.integers(1, 9)),
+                int(rng.integers(0, 200000)), int(rng.integers(0, 2)), int(rng.choice([0, 80, 256, 304])))
+        got = smd.plan_num_kv_splits(args[0], args[1], args[3], args[2], args[4], args[5], model=cm)
+        want = plan_ref.num_kv_splits(*args, pm)
+        assert got == want, (args, pm)
+
+
+def test_default_planner_properties():
+    """Properties the pages state; the exact fitted choice is parity unpinned."""
+    for rows in [1, 2, 8, 32, 64, 256]:
+        for H in [16, 64, 128]:
+            for K in [64, 384, 2176, 6528, 32128, 65664]:
+                s = smd.plan_num_kv_splits(rows, H, K)
+                assert 1 <= s <= 32
+                if K < 8192:
+                    assert s <= 4          # short workloads: at most four splits
+                assert s <= -(-K // 64)    # never more splits than 64-row chunks
+    # depends only on its arguments
+    assert smd.plan_num_kv_splits(8, 64, 2176) == smd.plan_num_kv_splits(8, 64, 2176)
+    # a batch that already fills the machine with one split per row stays unsplit
+    assert smd.plan_num_kv_splits(1024, 128, 2048) == 1
+    assert smd.plan_num_kv_splits(0, 128, 2048) == 1 and smd.plan_num_kv_splits(4, 128, 0) == 1
+
+
+def test_planner_rejects_bad_args():
+    with pytest.raises(smd.SmdError):
+        smd.plan_num_kv_splits(-1, 16, 100)
+    with pytest.raises(smd.SmdError):
+        smd.plan_num_kv_splits(1, 16, 100, kv_dtype=7)
+
+
+# ----------------------------------------------------------------------------
+# host validation of the decode entry points (no launch happens on failure)
+# ----------------------------------------------------------------------------
+def _pool(**kw):
+    p = smd._KVPool()
+    p.dtype = kw.get("dtype", smd.KV_BF16)
+    p.num_rows = kw.get("num_rows", 1024)
+    p.nope = kw.get("nope", 0x10000)
+    p.nope_stride = kw.get("nope_stride", 512)
+    p.rope = kw.get("rope", 0x10000 + 896)
+    p.rope_stride = kw.get("rope_stride", 512)
+    p.scale = kw.get("scale", None)
+    p.scale_stride = kw.get("scale_stride", 0)
+    return p
+
+
+def _decode(pool=None, **kw):
+    a = dict(q_nope=0x20000, q_rope=0x30000, T=4, H=64, qps=1, idx=0x40000, idx_stride=100, topk=100, sink=None,
+             scale=0.04, s=1, po=None, pl=None, out=0x50000, lse=0x60000)
+    a.update(kw)
+    p = pool if pool is not None else _pool()
+    rc = smd.lib().smd_sparse_mla_decode(a["q_nope"], a["q_rope"], a["T"], a["H"], a["qps"], ctypes.byref(p),
+                                         a["idx"], a["idx_stride"], a["topk"], a["sink"], a["scale"], a["s"],
+                                         a["po"], a["pl"], a["out"], a["lse"], None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(H=17), -2, "num_heads"),
+    (dict(H=256), -2, "num_heads"),
+    (dict(qps=0), -2, "q_per_seq"),
+    (dict(qps=9), -2, "q_per_seq"),
+    (dict(T=3, qps=2), -1, "multiple"),
+    (dict(s=0), -1, "num_splits"),
+    (dict(s=33), -1, "num_splits"),
+    (dict(T=-1), -1, "negative"),
+    (dict(topk=-5), -1, "negative"),
+    (dict(s=2), -3, "partial_o"),
+    (dict(out=None), -3, "partial_o"),
+    (dict(q_nope=None), -1, "required"),
+    (dict(q_nope=0x20008), -1, "aligned"),
+    (dict(idx_stride=50), -1, "indices_stride"),
+    (dict(scale=float("inf")), -1, "softmax_scale"),
+    (dict(out=0x50008), -1, "aligned"),
+])
+def test_decode_rejects(kw, code, msg):
+    rc, err = _decode(**kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+@pytest.mark.parametrize("pkw,code,msg", [
+    (dict(dtype=5), -2, "dtype"),
+    (dict(num_rows=-1), -1, "num_rows"),
+    (dict(nope=None), -1, "NULL"),
+    (dict(nope=0x10004), -1, "aligned"),
+    (dict(nope_stride=100), -1, "stride"),
+    (dict(rope_stride=60), -1, "stride"),
+    (dict(nope_stride=452), -1, "multiples of 16"),
+    (dict(scale=0x70000, scale_stride=8), -1, "scale"),
+    (dict(dtype=1, nope_stride=448, rope_stride=64), -1, "scale"),
+    (dict(dtype=1, nope_stride=448, rope_stride=64, scale=0x70000, scale_stride=7), -1, "scale"),
+    (dict(dtype=1, nope_stride=448, rope_stride=64, scale=0x70001, scale_stride=8), -1, "scale"),
+])
+def test_decode_rejects_bad_pool(pkw, code, msg):
+    rc, err = _decode(pool=_pool(**pkw))
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_decode_null_pool():
+    L = smd.lib()
+    rc = L.smd_sparse_mla_decode(0x20000, 0x30000, 4, 64, 1, None, 0x40000, 100, 100, None, 0.04, 1, None, None,
+                                 0x50000, 0x60000, None)
+    assert rc == -1
+
+
+def test_empty_problems_launch_nothing():
+    # T == 0 and topk == 0 return OK before any HIP call (so this runs without a GPU)
+    assert _decode(T=0)[0] == 0
+    assert _decode(topk=0, idx=None)[0] == 0
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0x1000, 0x2000, 4, 64, 0, None, 0x3000, 0x4000), -1),     # s = 0
+    ((0x1000, 0x2000, 4, 64, 1025, None, 0x3000, 0x4000), -1),  # s too large
+    ((None, 0x2000, 4, 64, 2, None, 0x3000, 0x4000), -1),       # no partials
+    ((0x1000, 0x2000, 4, 64, 2, None, None, 0x4000), -1),       # no out
+    ((0x1004, 0x2000, 4, 64, 2, None, 0x3000, 0x4000), -1),     # misaligned
+    ((0x1000, 0x2000, -1, 64, 2, None, 0x3000, 0x4000), -1),    # negative tokens
+])
+def test_merge_rejects(args, code):
+    assert smd.lib().smd_merge_partials(*args, None) == code
