@@ -81,10 +81,22 @@ static int check_pool(const char *fn, const smd_kv_pool *kv, DecodeArgs &a) {
   a.kv_scale = kv->scale;
   a.scale_stride_b = kv->scale_stride;
   a.num_rows = kv->num_rows;
+  a.num_rows32 = (uint32_t)(kv->num_rows < INT32_MAX ? kv->num_rows : INT32_MAX);
+  a.packed = !fp8 && (const uint8_t *)kv->rope == (const uint8_t *)kv->nope + 2 * kNope && nope_b == rope_b &&
+             nope_b < (int64_t)UINT32_MAX;
+  a.row_stride32 = a.packed ? (uint32_t)nope_b : 0u;
   return SMD_OK;
 }
 
-static int waves_for(int32_t M) { return M >= 64 ? 4 : M / 16; }
+// Query-row blocks of 16 per workgroup (RB; the 4 waves split the 512 dims
+// DS = 4 / RB ways).  Start from the widest block that M allows and narrow it
+// while the grid has fewer workgroups than the GPU has CUs: the narrower
+// blocks re-read KV rows from L2 but keep every CU busy.
+static int row_blocks_for(int32_t M, int64_t units, int num_cus) {
+  int rb = M >= 64 ? 4 : M / 16;
+  while (rb > 1 && units * (M / (16 * rb)) < num_cus) rb /= 2;
+  return rb;
+}
 
 }  // namespace smd
 
@@ -158,8 +170,8 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
   if (num_tokens == 0 || topk == 0) return SMD_OK;
 
   const int32_t M = num_heads * q_per_seq;
-  const int waves = waves_for(M);
   const int32_t rows = num_tokens / q_per_seq;
+  const int rb = row_blocks_for(M, (int64_t)rows * num_splits, 256);
   // chunk = roundup(ceil(topk / s), 64), as smd_split_bounds.
   const int64_t per = ((int64_t)topk + num_splits - 1) / num_splits;
   const int64_t chunk = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
@@ -176,13 +188,13 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
   a.M = M;
   a.S = num_splits;
   a.num_units = rows * num_splits;
-  a.G = M / (waves * 16);
+  a.G = M / (rb * 16);
   a.part_o = need_partials ? partial_o : nullptr;
   a.part_lse = need_partials ? partial_lse : nullptr;
   a.out = need_partials ? nullptr : (uint16_t *)out;
   a.lse = need_partials ? nullptr : lse;
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_decode(a, waves, kv->dtype == SMD_KV_FP8_E4M3_UE8M0, st);
+  hipError_t e = launch_decode(a, rb, kv->dtype == SMD_KV_FP8_E4M3_UE8M0, st);
   if (e != hipSuccess) {
     set_error("%s: decode launch failed: %s", fn, hipGetErrorString(e));
     return SMD_ERR_HIP;

@@ -65,40 +65,6 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// HBM -> LDS copy of 16 bytes per active lane: lane l writes LDS bytes
-// [lds + 16l, lds + 16l + 16).  Written as inline assembly so that the
-// compiler does not order later LDS reads of the *other* tile buffer behind
-// it; every caller waits for completion explicitly (s_waitcnt vmcnt(0))
-// before the copied tile is read.
-// M0 is reserved by the compiler, so the assembly saves and restores it.
-__device__ __forceinline__ void dma16(const void *src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
-}
-// The same with 4 bytes per lane (lane l writes [lds + 4l, lds + 4l + 4)).
-__device__ __forceinline__ void dma4(const void *src, uint32_t lds) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(src), "s"(lds)
-      : "memory");
-}
-__device__ __forceinline__ uint32_t lds_addr(const void SMD_LDS *p) {
-  return (uint32_t)(uintptr_t)p;
-}
 
 __device__ __forceinline__ float wave_xor(float v, int mask) {
   return __shfl_xor(v, mask, 64);
@@ -116,103 +82,169 @@ __device__ __forceinline__ float ue8m0_scale(uint32_t code) {
   return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
 }
 
-// fp8 rows are first copied raw into LDS (448 e4m3 bytes, 128 RoPE bytes, 8
-// code bytes per row), then expanded to the bf16 tile layout in one pass.
-constexpr int kRawRow = 592;                 // 576 data bytes + 8 code bytes + pad
-constexpr int kRawBytes = kBK * kRawRow;     // 18944
 // A row's reference max is fixed at its first tile with a valid entry; a later
 // score more than this far above it (log2 domain) sends the workgroup through
 // an exact-max second pass, so every p = 2^(x - m_ref) stays <= 2^32.
 constexpr float kRefSlackLog2 = 32.f;
 
-template <int WAVES, bool FP8>
+// Index lists are staged through LDS in blocks of kIdxBlock positions (8 tiles),
+// double-buffered and refilled kIdxBlock/32 - 3 tiles before first use, so no
+// per-tile global read sits on the critical path of the row gather.
+constexpr int kIdxBlock = 256;
+constexpr int kTilesPerIdxBlock = kIdxBlock / kBK;  // 8
+
+template <int DS>
 struct Smem {
-  uint8_t tile[2][kTileBytes];
-  uint8_t raw[FP8 ? kRawBytes : 16];
+  uint8_t tile[2][kTileBytes];          // double-buffered bf16 tiles
+  float sx[DS > 1 ? 4 * 64 * 8 : 4];    // partial S^T tiles of the dim-split waves
+  int32_t ibuf[2][kIdxBlock];           // index blocks (tiles 8k .. 8k+7 in ibuf[k & 1])
 };
 
-// Issue the HBM -> LDS copies of the tile rows this wave owns.  `idx_v` holds,
-// in lane rr < 32, the pool row of tile row rr; bit rr of `valid` says whether
-// that row is gathered (else the zero row is copied).
-template <int WAVES, bool FP8>
-__device__ __forceinline__ void issue_tile(const DecodeArgs &a, uint8_t SMD_LDS *tile,
-                                           uint8_t SMD_LDS *raw, int wave, int lane, int idx_v,
-                                           uint64_t valid) {
-  constexpr int kRowsPerWave = kBK / WAVES;
+// Index block k (positions p0 + 256k + tid, tid < 256), clamped into [p0, p1)
+// (p1 > p0) so that the load is unconditional: every step issues the same
+// memory operations and the compiler's wait counts stay exact.  Positions at
+// or beyond p1 are masked where the indices are used.
+__device__ __forceinline__ int load_idx_block(const int32_t *row_idx, int p0, int p1, int k) {
+  return row_idx[min(p0 + k * kIdxBlock + (int)threadIdx.x, p1 - 1)];
+}
+
+// Row data of one tile held in registers between its global loads and its
+// LDS stores.  Wave w handles tile rows 8w .. 8w+7.
+//   bf16: v[i] = logical 16-byte chunk lane ^ swz(rr) of row rr = 8w + i.
+//   fp8:  v[j] (j < 4) = 16 e4m3 bytes of chunk (lane & 31) (clamped to 27) of
+//         row 8w + 2j + (lane >> 5); rope = 16 RoPE bytes, chunk lane & 7 of
+//         row 8w + (lane >> 3); code = UE8M0 byte (lane & 7) of that row.
+template <bool FP8>
+struct Staged {
+  u32x4 v[FP8 ? 4 : kBK / 4];
+  u32x4 rope;
+  uint32_t code;
+};
+
+// Per-wave constants of the gather, computed once.
+struct GatherLanes {
+  uint32_t voff[kBK / 4];  // bf16: byte offset of this lane's chunk in row 8w+i
+  uint32_t sel_rope;       // bf16, split layout: bit i set when that chunk is RoPE
+};
+
+__device__ __forceinline__ GatherLanes make_gather_lanes(int wave, int lane) {
+  GatherLanes g;
+  g.sel_rope = 0;
 #pragma unroll
-  for (int k = 0; k < kRowsPerWave; ++k) {
-    const int rr = wave + k * WAVES;
-    const int idx = __builtin_amdgcn_readlane(idx_v, rr);
-    const bool v = (valid >> rr) & 1;
-    if constexpr (!FP8) {
-      // lane copies logical 16-byte chunk c of the row into physical slot `lane`
-      const int c = lane ^ swz(rr);
-      const uint8_t *nb = v ? a.kv_nope + (int64_t)idx * a.nope_stride_b : g_zero_row;
-      const uint8_t *rb = v ? a.kv_rope + (int64_t)idx * a.rope_stride_b - kNope * 2 : g_zero_row;
-      const uint8_t *src = (c < kNope / 8 ? nb : rb) + c * 16;
-      dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(tile + rr * kLdsRow)));
-    } else {
-      const uint8_t *nb = v ? a.kv_nope + (int64_t)idx * a.nope_stride_b : g_zero_row;
-      const uint8_t *rb = v ? a.kv_rope + (int64_t)idx * a.rope_stride_b - kNope : g_zero_row;
-      const uint8_t *sb = v ? a.kv_scale + (int64_t)idx * a.scale_stride_b : g_zero_row;
-      if (lane < 36) {
-        const uint8_t *src = (lane < 28 ? nb : rb) + lane * 16;
-        dma16(src, __builtin_amdgcn_readfirstlane(lds_addr(raw + rr * kRawRow)));
-      }
-      if (lane < 2) {
-        dma4(sb + lane * 4, __builtin_amdgcn_readfirstlane(lds_addr(raw + rr * kRawRow + 576)));
+  for (int i = 0; i < kBK / 4; ++i) {
+    const int c = lane ^ swz(wave * (kBK / 4) + i);
+    g.voff[i] = (uint32_t)c * 16u;
+    g.sel_rope |= (c >= kNope / 8 ? 1u : 0u) << i;
+  }
+  return g;
+}
+
+// Global loads of this wave's 8 rows of a tile (indices at tidx in LDS).
+// Invalid rows (index outside [0, N), or past the split) read the zero row, so
+// stale LDS contents (even NaN) never reach the MFMAs and every tile issues
+// the same loads.  bf16 rows whose RoPE part follows the NoPE part (the packed
+// [N, 512] layout) need one scalar row base per row; other layouts select the
+// NoPE or RoPE base per lane.
+template <bool FP8, bool PACKED>
+__device__ __forceinline__ void load_rows(const DecodeArgs &a, const uint8_t *zrow, const GatherLanes &gl,
+                                          const int32_t SMD_LDS *tidx, int first_pos, int p1, int wave,
+                                          int lane, Staged<FP8> &st) {
+  const int32_t SMD_LDS *widx = tidx + wave * (kBK / 4);  // this wave's 8 indices
+  const int rows_left = p1 - first_pos - wave * (kBK / 4);  // rows of this wave below p1
+  if constexpr (!FP8) {
+    const u32x4 ia = *(const u32x4 SMD_LDS *)(widx);
+    const u32x4 ib = *(const u32x4 SMD_LDS *)(widx + 4);
+    // byte offsets from the NoPE base; the zero row as an offset from it
+    const uint64_t zoff = (uint64_t)(zrow - a.kv_nope);
+#pragma unroll
+    for (int i = 0; i < kBK / 4; ++i) {
+      const uint32_t idx = __builtin_amdgcn_readfirstlane(i < 4 ? ia[i & 3] : ib[i & 3]);
+      const bool v = (i < rows_left) & (idx < a.num_rows32);  // idx < 0 wraps to a huge value
+      if constexpr (PACKED) {
+        const uint64_t off = v ? (uint64_t)idx * a.row_stride32 : zoff;
+        st.v[i] = *(const u32x4 *)(a.kv_nope + off + gl.voff[i]);
+      } else {
+        const uint64_t zr = (uint64_t)(zrow - a.kv_rope) + kNope * 2;
+        const uint64_t noff = v ? (uint64_t)idx * (uint64_t)a.nope_stride_b : zoff;
+        const uint64_t roff = v ? (uint64_t)idx * (uint64_t)a.rope_stride_b : zr;
+        const uint8_t *nb = a.kv_nope + noff;
+        const uint8_t *rb = a.kv_rope + roff - kNope * 2;
+        st.v[i] = *(const u32x4 *)((((gl.sel_rope >> i) & 1) ? rb : nb) + gl.voff[i]);
       }
     }
+  } else {
+    const u32x4 ia = *(const u32x4 SMD_LDS *)(widx);
+    const u32x4 ib = *(const u32x4 SMD_LDS *)(widx + 4);
+    const int c = min(lane & 31, 27);
+    const uint64_t zoff = (uint64_t)(zrow - a.kv_nope);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t ia_ = __builtin_amdgcn_readfirstlane(j < 2 ? ia[(2 * j) & 3] : ib[(2 * j) & 3]);
+      const uint32_t ib_ = __builtin_amdgcn_readfirstlane(j < 2 ? ia[(2 * j + 1) & 3] : ib[(2 * j + 1) & 3]);
+      const bool va = (2 * j < rows_left) & (ia_ < a.num_rows32);
+      const bool vb = (2 * j + 1 < rows_left) & (ib_ < a.num_rows32);
+      const uint64_t oa = va ? (uint64_t)ia_ * (uint64_t)a.nope_stride_b : zoff;
+      const uint64_t ob = vb ? (uint64_t)ib_ * (uint64_t)a.nope_stride_b : zoff;
+      st.v[j] = *(const u32x4 *)(a.kv_nope + (lane < 32 ? oa : ob) + c * 16);
+    }
+    // RoPE and codes of the 8 rows: lane l serves row l >> 3
+    const uint32_t il = (uint32_t)widx[lane >> 3];
+    const bool vl = ((lane >> 3) < rows_left) & (il < a.num_rows32);
+    const uint8_t *rp = vl ? a.kv_rope + (uint64_t)il * (uint64_t)a.rope_stride_b : zrow;
+    const uint8_t *sp = vl ? a.kv_scale + (uint64_t)il * (uint64_t)a.scale_stride_b : zrow;
+    st.rope = *(const u32x4 *)(rp + (lane & 7) * 16);
+    st.code = sp[lane & 7];
   }
 }
 
-// fp8 raw rows -> bf16 tile rows: e4m3 x 2^(code-127) (exact in bf16), RoPE copied.
-template <int WAVES>
-__device__ __forceinline__ void dequant_tile(uint8_t SMD_LDS *tile, const uint8_t SMD_LDS *raw) {
-  constexpr int kJobs = kBK * 36;
-  constexpr int kThreads = WAVES * 64;
+// LDS stores of the staged rows into `tile` (bf16 layout, chunks swizzled);
+// fp8 rows are dequantised on the way: e4m3 x 2^(code-127) is exact in bf16.
+template <bool FP8>
+__device__ __forceinline__ void store_rows(uint8_t SMD_LDS *tile, int wave, int lane, const Staged<FP8> &st) {
+  if constexpr (!FP8) {
 #pragma unroll
-  for (int j0 = 0; j0 < kJobs; j0 += kThreads) {
-    const int job = j0 + (int)threadIdx.x;
-    if (kJobs % kThreads == 0 || job < kJobs) {
-      const int rr = job / 36, ch = job - rr * 36;
-      const uint8_t SMD_LDS *src = raw + rr * kRawRow;
-      uint8_t SMD_LDS *dst = tile + rr * kLdsRow;
-      const int f = swz(rr);
-      const u32x4 w = *(const u32x4 SMD_LDS *)(src + ch * 16);
-      if (ch < 28) {
-        const float sc = ue8m0_scale(src[576 + (ch >> 2)]);
+    for (int i = 0; i < kBK / 4; ++i)
+      *(u32x4 SMD_LDS *)(tile + (wave * (kBK / 4) + i) * kLdsRow + lane * 16) = st.v[i];
+  } else {
+    const int c = lane & 31;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int rl = 2 * j + (lane >> 5);            // row within the wave's 8
+      // the code of block c/4 of that row sits in lane rl*8 + c/4
+      const uint32_t code = (uint32_t)__shfl((int)st.code, rl * 8 + (min(c, 27) >> 2), 64) & 0xffu;
+      if (c < 28) {
+        const int rr = wave * (kBK / 4) + rl;
+        const int f = swz(rr);
+        uint8_t SMD_LDS *row = tile + rr * kLdsRow;
+        const float sc = ue8m0_scale(code);
         u32x4 lo, hi;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], sc, false));
-          const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)w[q], sc, true));
+          const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[j][q], sc, false));
+          const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[j][q], sc, true));
           if (q < 2) { lo[2 * q] = u0; lo[2 * q + 1] = u1; }
           else { hi[2 * q - 4] = u0; hi[2 * q - 3] = u1; }
         }
-        *(u32x4 SMD_LDS *)(dst + (((2 * ch) ^ f) << 4)) = lo;
-        *(u32x4 SMD_LDS *)(dst + (((2 * ch + 1) ^ f) << 4)) = hi;
-      } else {
-        *(u32x4 SMD_LDS *)(dst + (((kNope / 8 + ch - 28) ^ f) << 4)) = w;
+        *(u32x4 SMD_LDS *)(row + (((2 * c) ^ f) << 4)) = lo;
+        *(u32x4 SMD_LDS *)(row + (((2 * c + 1) ^ f) << 4)) = hi;
       }
     }
+    const int rr = wave * (kBK / 4) + (lane >> 3);
+    *(u32x4 SMD_LDS *)(tile + rr * kLdsRow + (((kNope / 8 + (lane & 7)) ^ swz(rr)) << 4)) = st.rope;
   }
 }
 
-// Indices of tile `t` of positions [p0, p1): lane rr < 32 holds the pool row of
-// tile row rr, or -1 beyond p1.
-__device__ __forceinline__ int load_tile_indices(const int32_t *row_idx, int p0, int p1, int t, int lane) {
-  const int pos = p0 + t * kBK + lane;
-  return (lane < kBK && pos < p1) ? row_idx[pos] : -1;
+// Valid-row bits of a tile (first position first_pos, indices at tidx).
+__device__ __forceinline__ uint32_t tile_valid_bits(const int32_t SMD_LDS *tidx, int first_pos, int p1, int lane,
+                                                    uint32_t num_rows) {
+  const int idx_v = tidx[lane & (kBK - 1)];
+  return (uint32_t)__ballot(lane < kBK && first_pos + lane < p1 && (uint32_t)idx_v < (uint32_t)num_rows);
 }
 
-__device__ __forceinline__ uint64_t tile_valid_mask(int idx_v, int64_t num_rows) {
-  return __ballot(idx_v >= 0 && (int64_t)idx_v < num_rows) & 0xffffffffull;
-}
-
-// Per-wave state of the softmax and the O^T accumulator.
+// Per-wave state of the softmax and the O^T accumulator (ND 16-dim blocks).
+template <int ND>
 struct WaveState {
-  f32x4 acc[32];  // acc[d][i] = sum_j 2^(x_j - m_ref) V[j][16d + 4grp + i]
+  f32x4 acc[ND];  // acc[d][i] = sum_j 2^(x_j - m_ref) V[j][16(d0+d) + 4grp + i]
   float m_ref;    // reference max (log2 domain), same in the four 16-lane groups
   float l_run;    // this lane's share of sum_j 2^(x_j - m_ref)
   bool overflow;  // some score exceeded m_ref + kRefSlackLog2 (this lane)
@@ -220,25 +252,31 @@ struct WaveState {
 
 enum Pass { kPassMain = 0, kPassMax = 1, kPassFixed = 2 };
 
-// QK, softmax weights and PV over one 32-row tile.  qk_base[c&3] and
-// pv_base[d&7] are per-lane LDS byte offsets relative to the tile.
-//   kPassMain:  m_ref is set at the row's first valid tile, later tiles only
+// QK, softmax weights and PV over one 32-row tile for one wave: 16 query rows
+// and the 512/DS dims starting at chunk c0 (QK, 32-dim chunks) / block d0
+// (PV, 16-dim blocks).  With DS > 1 the partial scores of the DS waves that
+// share the query rows are summed through LDS (fixed order, so the DS waves
+// hold bit-identical scores and take identical softmax decisions).
+//   kPassMain:  m_ref is set at the row's first valid tile; later tiles only
 //               flag scores above m_ref + kRefSlackLog2.
-//   kPassMax:   QK only; m_ref becomes the exact running max.
+//   kPassMax:   scores only; m_ref becomes the exact running max.
 //   kPassFixed: m_ref is already the exact max.
 // The O accumulator is only ever touched by MFMAs here, never rescaled.
-template <int PASS, bool P_HILO>
-__device__ __forceinline__ void compute_tile(const uint8_t SMD_LDS *tile, const bf16x8 (&qreg)[16],
-                                             const int (&qk_base)[4], const int (&pv_base)[8],
-                                             uint64_t valid_t, int grp, float scale_log2,
-                                             WaveState &w) {
-  // ---- QK: S^T tiles for kv rows 0..15 (s0) and 16..31 (s1)
-  // Operands are read kPre steps ahead of the MFMAs that consume them.
-  constexpr int kPre = 4;
+template <int RB, int DS, int PASS, bool P_HILO>
+__device__ __forceinline__ void compute_tile(const uint8_t SMD_LDS *tile, float SMD_LDS *sx,
+                                             const bf16x8 (&qreg)[16 / DS], const int (&qk_base)[4],
+                                             const int (&pv_base)[8], uint32_t vbits, int wave,
+                                             int lane, int grp, int ds, float scale_log2,
+                                             WaveState<32 / DS> &w) {
+  constexpr int NC = 16 / DS, ND = 32 / DS;
+  const int c0 = ds * NC, d0 = ds * ND;
+  // ---- QK: S^T tiles for kv rows 0..15 (s0) and 16..31 (s1) over this wave's dims
+  constexpr int kPre = NC < 4 ? NC : 4;
   f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
   bf16x8 k0[kPre], k1[kPre];
   auto qk_load = [&](int c) {
-    const uint8_t SMD_LDS *p = tile + qk_base[c & 3] + 256 * (c >> 2);
+    const int cg = c0 + c;
+    const uint8_t SMD_LDS *p = tile + qk_base[cg & 3] + 256 * (cg >> 2);
     k0[c % kPre] = *(const bf16x8 SMD_LDS *)(p);
     k1[c % kPre] = *(const bf16x8 SMD_LDS *)(p + 16 * kLdsRow);
   };
@@ -246,16 +284,30 @@ __device__ __forceinline__ void compute_tile(const uint8_t SMD_LDS *tile, const 
   for (int c = 0; c < kPre; ++c) qk_load(c);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
+  for (int c = 0; c < NC; ++c) {
     const bf16x8 a0 = k0[c % kPre], a1 = k1[c % kPre];
-    if (c + kPre < 16) qk_load(c + kPre);
+    if (c + kPre < NC) qk_load(c + kPre);
     s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c], s0, 0, 0, 0);
     s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c], s1, 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);  // keep the reads kPre steps ahead
   }
+  if constexpr (DS > 1) {
+    f32x4 SMD_LDS *mine = (f32x4 SMD_LDS *)(sx + (wave * 64 + lane) * 8);
+    mine[0] = s0;
+    mine[1] = s1;
+    __syncthreads();
+    const int rb = wave % RB;
+    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
+    s1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int e = 0; e < DS; ++e) {
+      const f32x4 SMD_LDS *o = (const f32x4 SMD_LDS *)(sx + ((rb + e * RB) * 64 + lane) * 8);
+      s0 += o[0];
+      s1 += o[1];
+    }
+  }
 
   // ---- scores; this lane holds kv rows 4grp+i (s0) and 16+4grp+i (s1)
-  const uint32_t vbits = (uint32_t)valid_t;
   float x[8];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -287,81 +339,96 @@ __device__ __forceinline__ void compute_tile(const uint8_t SMD_LDS *tile, const 
   }
   w.l_run += psum;
 
-  // ---- PV: O^T[16d.., m] += V^T . P^T, V^T read transposed from LDS
-  bf16x4 vlo[kPre], vhi[kPre];
+  // ---- PV: O^T[16d.., m] += V^T . P^T for this wave's dims, V^T read transposed
+  constexpr int kPv = ND < 4 ? ND : 4;
+  bf16x4 vlo[kPv], vhi[kPv];
   auto pv_load = [&](int d) {
-    const uint8_t SMD_LDS *p = tile + pv_base[d & 7] + 256 * (d >> 3);
-    vlo[d % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p));
-    vhi[d % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p + 16 * kLdsRow));
+    const int dg = d0 + d;
+    const uint8_t SMD_LDS *p = tile + pv_base[dg & 7] + 256 * (dg >> 3);
+    vlo[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p));
+    vhi[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p + 16 * kLdsRow));
   };
 #pragma unroll
-  for (int d = 0; d < kPre; ++d) pv_load(d);
+  for (int d = 0; d < kPv; ++d) pv_load(d);
 #pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    const bf16x8 av = __builtin_shufflevector(vlo[d % kPre], vhi[d % kPre], 0, 1, 2, 3, 4, 5, 6, 7);
-    if (d + kPre < 32) pv_load(d + kPre);
+  for (int d = 0; d < ND; ++d) {
+    const bf16x8 av = __builtin_shufflevector(vlo[d % kPv], vhi[d % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
+    if (d + kPv < ND) pv_load(d + kPv);
     w.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, w.acc[d], 0, 0, 0);
     if constexpr (P_HILO) w.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, w.acc[d], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Walk the split's tiles once: gather (double-buffered, the next tile's
-// copies in flight during the current tile's math) and compute.
-template <int WAVES, bool FP8, bool P_HILO, int PASS>
-__device__ __forceinline__ void run_split(const DecodeArgs &a, uint8_t SMD_LDS *tile0,
-                                          uint8_t SMD_LDS *tile1, uint8_t SMD_LDS *raw,
-                                          const int32_t *row_idx, int p0, int p1, int wave,
-                                          int lane, int grp, const bf16x8 (&qreg)[16],
-                                          const int (&qk_base)[4], const int (&pv_base)[8],
-                                          WaveState &w) {
+// Walk the split's tiles once.  While tile t is computed from LDS, the rows
+// of tiles t+1 and t+2 are in flight into registers; the rows of t+1 are
+// stored to the other LDS buffer after the math, and one barrier per tile
+// publishes them.  Indices come from the LDS index blocks; the block after
+// the current one is re-read every step (cache hits after the first) and
+// stored three tiles before it is first needed.  Every step issues the same
+// loads (rows past the end read the zero row), so the compiler's vmcnt waits
+// let two tiles stay in flight.
+template <int RB, int DS, bool FP8, bool PACKED, bool P_HILO, int PASS>
+__device__ __forceinline__ void run_split(const DecodeArgs &a, Smem<DS> &sm, const int32_t *row_idx, int p0,
+                                          int p1, int wave, int lane, int grp, int ds,
+                                          const bf16x8 (&qreg)[16 / DS], const int (&qk_base)[4],
+                                          const int (&pv_base)[8], WaveState<32 / DS> &w) {
   const int ntiles = (p1 - p0 + kBK - 1) / kBK;
   if (ntiles <= 0) return;
-  int idx_cur = load_tile_indices(row_idx, p0, p1, 0, lane);
-  uint64_t valid_cur = tile_valid_mask(idx_cur, a.num_rows);
-  issue_tile<WAVES, FP8>(a, tile0, raw, wave, lane, idx_cur, valid_cur);
-  int idx_next = (ntiles > 1) ? load_tile_indices(row_idx, p0, p1, 1, lane) : -1;
-  __builtin_amdgcn_s_waitcnt(0);
+  uint8_t SMD_LDS *tile0 = (uint8_t SMD_LDS *)&sm.tile[0][0];
+  float SMD_LDS *sx = (float SMD_LDS *)&sm.sx[0];
+  int32_t SMD_LDS *ib0 = (int32_t SMD_LDS *)&sm.ibuf[0][0];
+  // LDS address of the 32 indices of tile k
+  auto tidx = [&](int k) {
+    return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
+  };
+  Staged<FP8> sa, sb;
+  const uint8_t *zrow = g_zero_row;
+  const GatherLanes gl = make_gather_lanes(wave, lane);
+  const int blk0 = load_idx_block(row_idx, p0, p1, 0);
+  __syncthreads();  // the buffers may still be read by a previous pass
+  ib0[threadIdx.x] = blk0;
   __syncthreads();
-  if constexpr (FP8) {
-    dequant_tile<WAVES>(tile0, raw);
+  load_rows<FP8, PACKED>(a, zrow, gl, tidx(0), p0, p1, wave, lane, sa);
+  load_rows<FP8, PACKED>(a, zrow, gl, tidx(1), p0 + kBK, p1, wave, lane, sb);
+  store_rows<FP8>(tile0, wave, lane, sa);
+  __syncthreads();
+  uint32_t v_cur = tile_valid_bits(tidx(0), p0, p1, lane, a.num_rows32);
+  // step t: tile t in buffer t&1; `nx` holds (in flight) the rows of t+1; the
+  // other staging set is refilled with the rows of t+2.  The loop runs two
+  // steps per iteration so each staging set has fixed registers; a padding
+  // step (t == ntiles) computes an all-masked tile of zero rows, which leaves
+  // every state unchanged, so the math is unconditional (a branch around it
+  // would make the allocator copy the accumulators).
+  auto step = [&](int t, Staged<FP8> &nx, Staged<FP8> &fill) {
+    const int nb = t / kTilesPerIdxBlock + 1;  // the next index block
+    const int blk = load_idx_block(row_idx, p0, p1, nb);
+    load_rows<FP8, PACKED>(a, zrow, gl, tidx(t + 2), p0 + (t + 2) * kBK, p1, wave, lane, fill);
+    compute_tile<RB, DS, PASS, P_HILO>(tile0 + (t & 1) * kTileBytes, sx, qreg, qk_base, pv_base, v_cur, wave,
+                                       lane, grp, ds, a.scale_log2, w);
+    store_rows<FP8>(tile0 + ((t + 1) & 1) * kTileBytes, wave, lane, nx);
+    if (t % kTilesPerIdxBlock == kTilesPerIdxBlock - 3) ib0[(nb & 1) * kIdxBlock + threadIdx.x] = blk;
     __syncthreads();
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    uint8_t SMD_LDS *cur = tile0 + (t & 1) * kTileBytes;
-    uint8_t SMD_LDS *nxt = tile0 + ((t + 1) & 1) * kTileBytes;
-    const uint64_t valid_t = valid_cur;
-    uint64_t valid_nx = 0;
-    int idx_nx2 = -1;
-    const bool more = t + 1 < ntiles;
-    if (more) {
-      valid_nx = tile_valid_mask(idx_next, a.num_rows);
-      issue_tile<WAVES, FP8>(a, nxt, raw, wave, lane, idx_next, valid_nx);
-      if (t + 2 < ntiles) idx_nx2 = load_tile_indices(row_idx, p0, p1, t + 2, lane);
-    }
-    compute_tile<PASS, P_HILO>(cur, qreg, qk_base, pv_base, valid_t, grp, a.scale_log2, w);
-    if (more) __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    if constexpr (FP8) {
-      if (more) {
-        dequant_tile<WAVES>(nxt, raw);
-        __syncthreads();
-      }
-    }
-    valid_cur = valid_nx;
-    idx_next = idx_nx2;
+    v_cur = tile_valid_bits(tidx(t + 1), p0 + (t + 1) * kBK, p1, lane, a.num_rows32);
+  };
+  for (int t = 0; t < ntiles; t += 2) {
+    step(t, sb, sa);
+    step(t + 1, sa, sb);
   }
 }
 
-template <int WAVES, bool FP8, bool P_HILO>
-__global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) Smem<WAVES, FP8> sm;
-  uint8_t SMD_LDS *tile0 = (uint8_t SMD_LDS *)sm.tile[0];
-  uint8_t SMD_LDS *tile1 = (uint8_t SMD_LDS *)sm.tile[1];
-  uint8_t SMD_LDS *raw = (uint8_t SMD_LDS *)sm.raw;
+// Work decomposition: a workgroup (4 waves) owns one index row b, one group g
+// of 16*RB query rows and one split r.  Wave w owns the 16 query rows of
+// block w % RB and the 512/DS dims of slice w / RB (RB * DS = 4).
+template <int RB, bool FP8, bool PACKED, bool P_HILO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1))) void decode_kernel(DecodeArgs a) {
+  constexpr int DS = 4 / RB;
+  constexpr int NC = 16 / DS, ND = 32 / DS;
+  __shared__ __attribute__((aligned(1024))) Smem<DS> sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+  const int rb = wave % RB, ds = wave / RB;
   const int j = lane & 15;   // query row within the wave's block / column
   const int grp = lane >> 4; // 16-lane group
 
@@ -379,17 +446,18 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1
   const int32_t *row_idx = a.indices + (int64_t)b * a.indices_stride;
 
   // This lane's query row m -> (token, head).
-  const int m = g * (WAVES * 16) + wave * 16 + j;
+  const int m = g * (RB * 16) + rb * 16 + j;
   const int tok = b * a.qps + m / a.H;
   const int head = m % a.H;
   const int64_t qrow = (int64_t)tok * a.H + head;
 
   // Q^T as the B operand: chunk c holds dims 32c + 8*grp .. +7 of row m.
-  bf16x8 qreg[16];
+  bf16x8 qreg[NC];
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const uint16_t *src = (c < 14) ? a.q_nope + qrow * kNope + 32 * c + 8 * grp
-                                   : a.q_rope + qrow * kRope + 32 * (c - 14) + 8 * grp;
+  for (int c = 0; c < NC; ++c) {
+    const int cg = ds * NC + c;
+    const uint16_t *src = (cg < 14) ? a.q_nope + qrow * kNope + 32 * cg + 8 * grp
+                                    : a.q_rope + qrow * kRope + 32 * (cg - 14) + 8 * grp;
     qreg[c] = *(const bf16x8 *)src;
   }
 
@@ -410,32 +478,33 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1
       pv_base[d] = tr_row * kLdsRow + (((2 * d + (qq >> 1)) ^ ftr) << 4) + ((qq & 1) << 3);
   }
 
-  WaveState w;
+  WaveState<ND> w;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) w.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int d = 0; d < ND; ++d) w.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   w.m_ref = -INFINITY;
   w.l_run = 0.f;
   w.overflow = false;
-  run_split<WAVES, FP8, P_HILO, kPassMain>(a, tile0, tile1, raw, row_idx, p0, p1, wave, lane, grp, qreg,
-                                   qk_base, pv_base, w);
+  run_split<RB, DS, FP8, PACKED, P_HILO, kPassMain>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg, qk_base,
+                                            pv_base, w);
   if (__syncthreads_or(w.overflow)) {
     // Rare: a score ran far above its row's first-tile max.  Redo the split
-    // with the exact max (found by a QK-only sweep) as the reference.
+    // with the exact max (found by a scores-only sweep) as the reference.
 #pragma unroll
-    for (int d = 0; d < 32; ++d) w.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < ND; ++d) w.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     w.m_ref = -INFINITY;
     w.l_run = 0.f;
-    run_split<WAVES, FP8, P_HILO, kPassMax>(a, tile0, tile1, raw, row_idx, p0, p1, wave, lane, grp, qreg,
-                                    qk_base, pv_base, w);
-    run_split<WAVES, FP8, P_HILO, kPassFixed>(a, tile0, tile1, raw, row_idx, p0, p1, wave, lane, grp,
-                                      qreg, qk_base, pv_base, w);
+    run_split<RB, DS, FP8, PACKED, P_HILO, kPassMax>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg, qk_base,
+                                             pv_base, w);
+    run_split<RB, DS, FP8, PACKED, P_HILO, kPassFixed>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg,
+                                               qk_base, pv_base, w);
   }
 
-  // ---- epilogue: total sum per query row
+  // ---- epilogue: total sum per query row (identical in the DS waves of a block)
   float l_tot = w.l_run;
   l_tot += wave_xor(l_tot, 16);
   l_tot += wave_xor(l_tot, 32);
   const float m_ref = w.m_ref;
+  const int dbase = ds * ND;
 
   const int64_t orow = qrow;  // [T, H] row of this lane's query row
   if (a.S == 1 && a.out != nullptr) {
@@ -448,25 +517,25 @@ __global__ __launch_bounds__(WAVES * 64) __attribute__((amdgpu_waves_per_eu(1, 1
       inv = e / z;
       lse_v = (mf + __log2f(z)) * kLn2;
     }
-    uint16_t *dst = a.out + orow * kDim + 4 * grp;
+    uint16_t *dst = a.out + orow * kDim + 16 * dbase + 4 * grp;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) {
+    for (int d = 0; d < ND; ++d) {
       u32x2 v;
       v[0] = (uint32_t)f32_to_bf16_rne(w.acc[d][0] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[d][1] * inv) << 16);
       v[1] = (uint32_t)f32_to_bf16_rne(w.acc[d][2] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[d][3] * inv) << 16);
       *(u32x2 *)(dst + 16 * d) = v;
     }
-    if (a.lse != nullptr && grp == 0) a.lse[orow] = lse_v;
+    if (a.lse != nullptr && grp == 0 && ds == 0) a.lse[orow] = lse_v;
   } else {
     float inv = 0.f, lse_v = -INFINITY;
     if (l_tot > 0.f) {
       inv = 1.f / l_tot;
       lse_v = (m_ref + __log2f(l_tot)) * kLn2;
     }
-    float *dst = a.part_o + (orow * a.S + r) * kDim + 4 * grp;
+    float *dst = a.part_o + (orow * a.S + r) * kDim + 16 * dbase + 4 * grp;
 #pragma unroll
-    for (int d = 0; d < 32; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[d] * inv;
-    if (grp == 0) a.part_lse[orow * a.S + r] = lse_v;
+    for (int d = 0; d < ND; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[d] * inv;
+    if (grp == 0 && ds == 0) a.part_lse[orow * a.S + r] = lse_v;
   }
 }
 
@@ -511,32 +580,36 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   if (lse && lane == 0) lse[row] = mx + logf(z);
 }
 
-template <int WAVES, bool FP8, bool P_HILO>
+template <int RB, bool FP8, bool PACKED, bool P_HILO>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_kernel<WAVES, FP8, P_HILO>), grid, dim3(WAVES * 64), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<RB, FP8, PACKED, P_HILO>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
+template <int RB, bool P_HILO>
+static hipError_t launch_decode_rb(const DecodeArgs &a, bool fp8, hipStream_t stream) {
+  if (fp8) return launch_decode_t<RB, true, false, P_HILO>(a, stream);
+  return a.packed ? launch_decode_t<RB, false, true, P_HILO>(a, stream)
+                  : launch_decode_t<RB, false, false, P_HILO>(a, stream);
+}
+
 template <bool P_HILO>
-static hipError_t launch_decode_p(const DecodeArgs &a, int waves, bool fp8, hipStream_t stream) {
-  switch (waves * 2 + (fp8 ? 1 : 0)) {
-    case 2: return launch_decode_t<1, false, P_HILO>(a, stream);
-    case 3: return launch_decode_t<1, true, P_HILO>(a, stream);
-    case 4: return launch_decode_t<2, false, P_HILO>(a, stream);
-    case 5: return launch_decode_t<2, true, P_HILO>(a, stream);
-    case 8: return launch_decode_t<4, false, P_HILO>(a, stream);
-    case 9: return launch_decode_t<4, true, P_HILO>(a, stream);
+static hipError_t launch_decode_p(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream) {
+  switch (rb) {
+    case 1: return launch_decode_rb<1, P_HILO>(a, fp8, stream);
+    case 2: return launch_decode_rb<2, P_HILO>(a, fp8, stream);
+    case 4: return launch_decode_rb<4, P_HILO>(a, fp8, stream);
     default: return hipErrorInvalidValue;
   }
 }
 
 // Partials are written with the two-part P (FP32-partial precision); the
 // direct bf16 output uses a single bf16 P.
-hipError_t launch_decode(const DecodeArgs &a, int waves, bool fp8, hipStream_t stream) {
-  return a.out != nullptr ? launch_decode_p<false>(a, waves, fp8, stream)
-                          : launch_decode_p<true>(a, waves, fp8, stream);
+hipError_t launch_decode(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream) {
+  return a.out != nullptr ? launch_decode_p<false>(a, rb, fp8, stream)
+                          : launch_decode_p<true>(a, rb, fp8, stream);
 }
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,

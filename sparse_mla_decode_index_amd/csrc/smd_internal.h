@@ -22,6 +22,9 @@ struct DecodeArgs {
   const uint8_t *kv_scale; // UE8M0 codes (fp8 pools)
   int64_t scale_stride_b;  // bytes
   int64_t num_rows;
+  uint32_t num_rows32;     // min(num_rows, 2^31 - 1): int32 indices cannot exceed it
+  int32_t packed;          // bf16 rows with RoPE right after NoPE (rope == nope + 896 B)
+  uint32_t row_stride32;   // row stride in bytes when packed (< 2^32)
   const int32_t *indices;
   int64_t indices_stride;  // elements
   int32_t topk;
@@ -38,8 +41,9 @@ struct DecodeArgs {
   float *lse;              // [T, H] or null
 };
 
-// Launch the split-KV decode.  waves = query-row blocks of 16 per workgroup.
-hipError_t launch_decode(const DecodeArgs &a, int waves, bool fp8, hipStream_t stream);
+// Launch the split-KV decode with rb query-row blocks of 16 per workgroup
+// (rb in {1, 2, 4}; a.G = M / (16 rb) row groups per index row).
+hipError_t launch_decode(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream);
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
