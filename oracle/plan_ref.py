@@ -67,3 +67,84 @@ def num_kv_splits(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv
         if best is None or cost < best:
             best, best_s = cost, s
     return best_s
+
+
+# ----------------------------------------------------------------------------
+# persistent plan: balanced contiguous partition of all 64-position tiles
+# ----------------------------------------------------------------------------
+# The aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode
+# kernel" (Summary, part 2) has the persistent kernel derive its split plan
+# inside the kernel from the live kv_indptr and merge split rows in the
+# workgroup that arrives last.  The pages do not print the partition rule; the
+# reading used here: every sequence b contributes tiles_b = ceil(K_b / 64)
+# tiles, the tiles of all sequences are concatenated in (b, tile) order, and
+# partition p of P owns the global tiles [floor(p*total/P), floor((p+1)*total/P)).
+# A sequence whose tiles fall in more than one partition is split; its pieces
+# merge in partition order.  A partition holds at most two split pieces (its
+# first and its last sequence), so piece (p, b) has slot 2p when b is the
+# first sequence of p and 2p+1 otherwise.
+
+PERSIST_TILE = 64
+
+
+@dataclass
+class Piece:
+    seq: int         # sequence b
+    begin: int       # first index position of the piece within the sequence
+    end: int         # one past the last position (<= K_b)
+    split: bool      # the sequence has pieces in more than one partition
+    slot: int        # partial slot of a split piece (2p or 2p+1), else -1
+    first_part: int  # first partition holding a piece of the sequence
+    num_pieces: int  # partitions holding a piece of the sequence
+
+
+def partition(kv_indptr, num_partitions: int):
+    """Returns (descriptors, pieces): descriptors[p] = (t0, t1, b_first, b_last)
+    with b_first / b_last the first / last sequence owning a tile of [t0, t1)
+    (-1, -1 for an empty partition); pieces[p] = the list of Piece of p in
+    sequence order."""
+    P = int(num_partitions)
+    if P < 1:
+        raise ValueError("num_partitions must be >= 1")
+    ptr = [int(x) for x in kv_indptr]
+    B = len(ptr) - 1
+    lens = [ptr[b + 1] - ptr[b] for b in range(B)]
+    if any(k < 0 for k in lens):
+        raise ValueError("kv_indptr must be non-decreasing")
+    tiles = [_cdiv(k, PERSIST_TILE) for k in lens]
+    start = [0] * (B + 1)  # first global tile of each sequence
+    for b in range(B):
+        start[b + 1] = start[b] + tiles[b]
+    total = start[B]
+    bounds = [p * total // P for p in range(P + 1)]
+
+    def owner(tile):  # the partition whose range holds global tile `tile`
+        p = 0
+        while bounds[p + 1] <= tile:
+            p += 1
+        return p
+
+    descs, pieces = [], []
+    for p in range(P):
+        t0, t1 = bounds[p], bounds[p + 1]
+        mine = []
+        for b in range(B):
+            lo, hi = max(t0, start[b]), min(t1, start[b + 1])
+            if lo >= hi:
+                continue
+            fp, lp = owner(start[b]), owner(start[b + 1] - 1)
+            first = not mine
+            mine.append(Piece(seq=b, begin=(lo - start[b]) * PERSIST_TILE,
+                              end=min((hi - start[b]) * PERSIST_TILE, lens[b]),
+                              split=lp > fp, slot=(2 * p + (0 if first else 1)) if lp > fp else -1,
+                              first_part=fp, num_pieces=lp - fp + 1))
+        descs.append((t0, t1, mine[0].seq, mine[-1].seq) if mine else (t0, t1, -1, -1))
+        pieces.append(mine)
+    return descs, pieces
+
+
+def default_partitions(num_heads: int, q_per_seq: int, num_cus: int = 256, wg_per_cu: int = 1) -> int:
+    """Partitions that fill the machine once: num_cus * wg_per_cu workgroups over
+    ceil(M / 64) query-row groups of M = num_heads * q_per_seq rows."""
+    M = num_heads * q_per_seq
+    return max(1, (num_cus * wg_per_cu) // _cdiv(M, 64))

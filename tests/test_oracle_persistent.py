@@ -1,0 +1,150 @@
+"""Pins of the oracle's persistent plan (the balanced contiguous partition of
+all 64-position tiles over P partitions) and of the piecewise merge it implies.
+CPU only."""
+import numpy as np
+import pytest
+
+import workloads as wl
+from oracle import plan_ref as pr
+from oracle import ref
+
+
+def test_partition_hand_example():
+    # K_b = 100, 0, 200, 1  ->  tiles 2, 0, 4, 1 (ceil(K/64)); total 7; P = 3:
+    # bounds floor(7p/3) = 0, 2, 4, 7.  Partition 0 = seq 0 (whole); partition
+    # 1 = tiles 2..3 = seq 2 positions [0, 128); partition 2 = tiles 4..6 =
+    # seq 2 positions [128, 200) then seq 3 [0, 1).  Seq 2 is split over
+    # partitions 1 and 2 and is the first sequence of both (slots 2 and 4).
+    # The indptr starts at an offset: only differences matter.
+    descs, pieces = pr.partition([50, 150, 150, 350, 351], 3)
+    assert descs == [(0, 2, 0, 0), (2, 4, 2, 2), (4, 7, 2, 3)]
+    got = [[(x.seq, x.begin, x.end, x.split, x.slot, x.first_part, x.num_pieces) for x in p] for p in pieces]
+    assert got == [[(0, 0, 100, False, -1, 0, 1)],
+                   [(2, 0, 128, True, 2, 1, 2)],
+                   [(2, 128, 200, True, 4, 1, 2), (3, 0, 1, False, -1, 2, 1)]]
+
+
+def test_partition_last_piece_takes_odd_slot():
+    # K = 64, 128 -> tiles 1, 2; P = 2: bounds 0, 1, 3.  Partition 0 = seq 0 only;
+    # partition 1 = seq 1 whole.  Now K = 128, 128, P = 3: bounds 0, 1, 2, 4:
+    # partition 1 = tile 1 (seq 0 second half) -> first sequence, slot 2;
+    # partition 0 = seq 0 first half, slot 0; partition 2 = seq 1 whole.
+    _, pieces = pr.partition([0, 128, 256], 3)
+    assert [(x.seq, x.begin, x.end, x.slot) for x in pieces[0]] == [(0, 0, 64, 0)]
+    assert [(x.seq, x.begin, x.end, x.slot) for x in pieces[1]] == [(0, 64, 128, 2)]
+    assert [(x.seq, x.begin, x.end, x.split) for x in pieces[2]] == [(1, 0, 128, False)]
+    # K = 64, 192, P = 2: tiles 1, 3; bounds 0, 2, 4: partition 0 = seq 0 then
+    # seq 1 tile 0 -> seq 1's piece there is not the first sequence: slot 1.
+    _, pieces = pr.partition([0, 64, 256], 2)
+    assert [(x.seq, x.slot) for x in pieces[0]] == [(0, -1), (1, 1)]
+    assert [(x.seq, x.begin, x.end, x.slot) for x in pieces[1]] == [(1, 64, 192, 2)]
+
+
+def _random_indptr(rng, B, kmax, zero_frac=0.2, offset=0):
+    k = rng.integers(0, kmax + 1, size=B)
+    k[rng.random(B) < zero_frac] = 0
+    return np.concatenate([[offset], offset + np.cumsum(k)]).astype(np.int64)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_partition_invariants(seed):
+    rng = np.random.default_rng(seed)
+    B = int(rng.integers(1, 40))
+    ptr = _random_indptr(rng, B, int(rng.choice([5, 64, 300, 3000])), offset=int(rng.integers(0, 1000)))
+    P = int(rng.choice([1, 2, 3, 7, 32, 64, 300]))
+    descs, pieces = pr.partition(ptr, P)
+    lens = np.diff(ptr)
+    tiles = -(-lens // 64)
+    total = int(tiles.sum())
+    # partition sizes differ by at most one tile and tile the range in order
+    sizes = [d[1] - d[0] for d in descs]
+    assert sum(sizes) == total and max(sizes) - min(sizes) <= 1
+    assert descs[0][0] == 0 and descs[-1][1] == total
+    assert all(descs[p][1] == descs[p + 1][0] for p in range(P - 1))
+    # every position of every sequence is covered exactly once, in (partition, seq) order
+    seen = {b: [] for b in range(B)}
+    for p, plist in enumerate(pieces):
+        assert [x.seq for x in plist] == sorted({x.seq for x in plist})
+        if plist:
+            assert descs[p][2] == plist[0].seq and descs[p][3] == plist[-1].seq
+        else:
+            assert descs[p][2:] == (-1, -1)
+        for x in plist:
+            assert x.begin % 64 == 0 and 0 <= x.begin < x.end <= lens[x.seq]
+            seen[x.seq].append((p, x.begin, x.end))
+    for b in range(B):
+        segs = seen[b]
+        if lens[b] == 0:
+            assert segs == []  # K = 0 sequences get nothing
+            continue
+        ps = [s[0] for s in segs]
+        assert ps == list(range(ps[0], ps[0] + len(ps)))  # consecutive partitions
+        cover = [s[1:] for s in segs]
+        assert cover[0][0] == 0 and cover[-1][1] == lens[b]
+        assert all(cover[i][1] == cover[i + 1][0] for i in range(len(cover) - 1))
+    # split flags, piece counts and slots
+    slots = []
+    for p, plist in enumerate(pieces):
+        for i, x in enumerate(plist):
+            n = len(seen[x.seq])
+            assert x.num_pieces == n and x.split == (n > 1) and x.first_part == seen[x.seq][0][0]
+            if x.split:
+                assert x.slot == 2 * p + (0 if i == 0 else 1)
+                slots.append(x.slot)
+            else:
+                assert x.slot == -1
+    assert len(slots) == len(set(slots)) and all(0 <= s < 2 * P for s in slots)
+
+
+def test_partition_edge_cases():
+    # no work at all: every partition empty
+    descs, pieces = pr.partition([7, 7, 7], 4)
+    assert all(d == (0, 0, -1, -1) for d in descs) and all(p == [] for p in pieces)
+    # more partitions than tiles: the extra ones are empty, each tile is alone
+    descs, pieces = pr.partition([0, 200], 8)  # 4 tiles
+    assert sum(1 for p in pieces if p) == 4
+    assert [(x.begin, x.end, x.slot) for p in pieces for x in p] == [(0, 64, 2), (64, 128, 6), (128, 192, 10),
+                                                                      (192, 200, 14)]
+    with pytest.raises(ValueError):
+        pr.partition([0, 5], 0)
+    with pytest.raises(ValueError):
+        pr.partition([5, 0], 2)
+
+
+def test_default_partitions():
+    assert pr.default_partitions(128, 4) == 32  # M = 512: eight 64-row groups
+    assert pr.default_partitions(128, 1) == 128
+    assert pr.default_partitions(16, 1) == 256
+    assert pr.default_partitions(64, 1, num_cus=80) == 80
+
+
+@pytest.mark.parametrize("seed,P", [(0, 5), (1, 32), (2, 3)])
+def test_piecewise_merge_equals_unsplit(seed, P):
+    """Partials of the pieces, merged in partition order with the sink, equal the
+    unsplit ragged decode (the split-merge identity over the persistent plan)."""
+    w = wl.ragged_workload("persist pin", B=6, q_per_seq=2, H=16, kv_dtype="fp8", pool_rows=700, max_k=400,
+                           zero_rows=2, seed=seed)
+    a = w.arrays
+    pool = {"nope": a["nope"], "scale": a["scale"], "rope": a["rope"]}
+    ptr, flat = a["kv_indptr"], a["kv_indices"]
+    want_o, want_l, written = ref.sparse_mla_decode_ragged(a["q_nope"], a["q_rope"], pool, ptr, flat, a["sink"],
+                                                           w.softmax_scale, 2)
+    q = ref.queries(a["q_nope"], a["q_rope"])
+    H = q.shape[1]
+    n = ref.pool_size(pool)
+    _, pieces = pr.partition(ptr, P)
+    parts = {}
+    for plist in pieces:
+        for x in plist:
+            idx = np.asarray(flat[ptr[x.seq] + x.begin:ptr[x.seq] + x.end])
+            k = ref.pool_rows(pool, idx[ref.valid_mask(idx, n)])
+            qb = q[x.seq * 2:(x.seq + 1) * 2].reshape(-1, 512)
+            parts.setdefault(x.seq, []).append(ref.partial_one(qb, k, w.softmax_scale))
+    for b, lst in parts.items():
+        o = np.stack([p[0] for p in lst], axis=1).reshape(2, H, len(lst), 512)
+        l = np.stack([p[1] for p in lst], axis=1).reshape(2, H, len(lst))
+        mo, ml = ref.merge_partials(o, l, a["sink"])
+        np.testing.assert_allclose(mo, want_o[b * 2:(b + 1) * 2], rtol=0, atol=1e-12)
+        np.testing.assert_allclose(ml, want_l[b * 2:(b + 1) * 2], rtol=0, atol=1e-12)
+    assert set(parts) == {b for b in range(len(ptr) - 1) if ptr[b + 1] > ptr[b]}
+    assert written.sum() == 2 * len(parts)
