@@ -80,8 +80,11 @@ def num_kv_splits(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv
 # tiles, the tiles of all sequences are concatenated in (b, tile) order, and
 # partition p of P owns the global tiles [floor(p*total/P), floor((p+1)*total/P)).
 # A sequence whose tiles fall in more than one partition is split; its pieces
-# merge in partition order.  A partition holds at most two split pieces (its
-# first and its last sequence), so piece (p, b) has slot 2p when b is the
+# merge in partition order.  With fewer tiles than partitions some partitions
+# are empty, and they may sit between two pieces of one sequence, so the piece
+# count is the number of partitions that own a tile of the sequence, not the
+# width of the partition span.  A partition holds at most two split pieces
+# (its first and its last sequence), so piece (p, b) has slot 2p when b is the
 # first sequence of p and 2p+1 otherwise.
 
 PERSIST_TILE = 64
@@ -95,7 +98,7 @@ class Piece:
     split: bool      # the sequence has pieces in more than one partition
     slot: int        # partial slot of a split piece (2p or 2p+1), else -1
     first_part: int  # first partition holding a piece of the sequence
-    num_pieces: int  # partitions holding a piece of the sequence
+    num_pieces: int  # partitions owning a tile of the sequence
 
 
 def partition(kv_indptr, num_partitions: int):
@@ -132,12 +135,13 @@ def partition(kv_indptr, num_partitions: int):
             lo, hi = max(t0, start[b]), min(t1, start[b + 1])
             if lo >= hi:
                 continue
-            fp, lp = owner(start[b]), owner(start[b + 1] - 1)
+            owners = sorted({owner(t) for t in range(start[b], start[b + 1])})
+            fp, lp = owners[0], owners[-1]
             first = not mine
             mine.append(Piece(seq=b, begin=(lo - start[b]) * PERSIST_TILE,
                               end=min((hi - start[b]) * PERSIST_TILE, lens[b]),
                               split=lp > fp, slot=(2 * p + (0 if first else 1)) if lp > fp else -1,
-                              first_part=fp, num_pieces=lp - fp + 1))
+                              first_part=fp, num_pieces=len(owners)))
         descs.append((t0, t1, mine[0].seq, mine[-1].seq) if mine else (t0, t1, -1, -1))
         pieces.append(mine)
     return descs, pieces

@@ -46,12 +46,12 @@ def _random_indptr(rng, B, kmax, zero_frac=0.2, offset=0):
     return np.concatenate([[offset], offset + np.cumsum(k)]).astype(np.int64)
 
 
-@pytest.mark.parametrize("seed", range(12))
+@pytest.mark.parametrize("seed", range(24))
 def test_partition_invariants(seed):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 40))
     ptr = _random_indptr(rng, B, int(rng.choice([5, 64, 300, 3000])), offset=int(rng.integers(0, 1000)))
-    P = int(rng.choice([1, 2, 3, 7, 32, 64, 300]))
+    P = int(rng.choice([1, 2, 3, 7, 32, 64, 300, 5000]))
     descs, pieces = pr.partition(ptr, P)
     lens = np.diff(ptr)
     tiles = -(-lens // 64)
@@ -78,7 +78,9 @@ def test_partition_invariants(seed):
             assert segs == []  # K = 0 sequences get nothing
             continue
         ps = [s[0] for s in segs]
-        assert ps == list(range(ps[0], ps[0] + len(ps)))  # consecutive partitions
+        assert ps == sorted(set(ps))  # increasing partitions ...
+        for q in range(ps[0], ps[-1] + 1):  # ... and any partition between them owns no tile
+            assert q in ps or descs[q][0] == descs[q][1]
         cover = [s[1:] for s in segs]
         assert cover[0][0] == 0 and cover[-1][1] == lens[b]
         assert all(cover[i][1] == cover[i + 1][0] for i in range(len(cover) - 1))
@@ -100,11 +102,14 @@ def test_partition_edge_cases():
     # no work at all: every partition empty
     descs, pieces = pr.partition([7, 7, 7], 4)
     assert all(d == (0, 0, -1, -1) for d in descs) and all(p == [] for p in pieces)
-    # more partitions than tiles: the extra ones are empty, each tile is alone
+    # more partitions than tiles: bounds floor(4p/8) = 0,0,1,1,2,2,3,3,4, so the
+    # odd partitions own one tile each and the even ones are empty -- empty
+    # partitions sit between the pieces, which still number 4 (not 7 = 7 - 1 + 1)
     descs, pieces = pr.partition([0, 200], 8)  # 4 tiles
     assert sum(1 for p in pieces if p) == 4
     assert [(x.begin, x.end, x.slot) for p in pieces for x in p] == [(0, 64, 2), (64, 128, 6), (128, 192, 10),
                                                                       (192, 200, 14)]
+    assert all(x.num_pieces == 4 and x.first_part == 1 for p in pieces for x in p)
     with pytest.raises(ValueError):
         pr.partition([0, 5], 0)
     with pytest.raises(ValueError):
@@ -118,7 +123,7 @@ def test_default_partitions():
     assert pr.default_partitions(64, 1, num_cus=80) == 80
 
 
-@pytest.mark.parametrize("seed,P", [(0, 5), (1, 32), (2, 3)])
+@pytest.mark.parametrize("seed,P", [(0, 5), (1, 32), (2, 3), (3, 200)])
 def test_piecewise_merge_equals_unsplit(seed, P):
     """Partials of the pieces, merged in partition order with the sink, equal the
     unsplit ragged decode (the split-merge identity over the persistent plan)."""
