@@ -61,6 +61,8 @@ enum {
 #define SMD_MAX_SPLITS 32
 /* Index positions of one split are a multiple of this (except the last). */
 #define SMD_SPLIT_ALIGN 64
+/* Largest partition count of the persistent entry point. */
+#define SMD_MAX_PARTITIONS 16384
 
 /* Message describing this thread's most recent failure ("" if none). */
 const char *smd_last_error(void);
@@ -200,6 +202,76 @@ int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_to
 int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t num_tokens,
                        int32_t num_heads, int32_t num_splits, const float *sink, void *out,
                        float *lse, void *stream);
+
+/*
+ * ---------------------------------------------------------------------------
+ * Persistent, graph-safe decode over ragged sequences
+ * ---------------------------------------------------------------------------
+ * The aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent
+ * decode kernel" (Summary, part 2): one launch with a fixed grid; every
+ * workgroup computes the split plan inside the kernel from the live
+ * kv_indptr; rows held by one partition are written as bf16 directly, split
+ * rows write FP32 partials into the workspace and the workgroup that arrives
+ * last merges them; sequences with no index are left unwritten.  Because the
+ * plan is read from device memory on every launch, a captured graph stays
+ * correct when kv_indptr and kv_indices change between replays.
+ *
+ * Plan rule: sequence b contributes ceil(K_b / 64) tiles of 64 index
+ * positions (K_b = kv_indptr[b+1] - kv_indptr[b]); the tiles of all
+ * sequences are concatenated in (sequence, tile) order, and partition p of
+ * num_partitions owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
+ * The kernel runs P x ceil(M / 64) workgroups (M = num_heads * q_per_seq; for
+ * M < 64 one group of M rows).
+ */
+
+/* P that fills num_cus CUs once: num_cus / ceil(M / 64), at least 1
+ * (num_cus <= 0 means 256).  Host only.  Negative SMD_ERR_* on bad shapes. */
+int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, int32_t num_cus);
+
+/* Bytes of workspace the persistent decode needs for these shapes: the plan
+ * (16 bytes per partition), arrival counters (4 bytes per partition and
+ * 16-row group) and 2 * num_partitions partial slots of M * 513 fp32.
+ * Returns 0 for unsupported shapes (smd_last_error says why).  Host only. */
+size_t smd_persistent_workspace_bytes(int32_t num_heads, int32_t q_per_seq, int32_t num_partitions);
+
+/* Zero a persistent workspace (an asynchronous memset of `bytes` bytes on
+ * `stream`).  Call once after allocating it, outside any graph capture; the
+ * kernel returns every counter to zero itself, so later calls (any batch
+ * size, any plan) need no further reset. */
+int smd_persistent_workspace_reset(void *workspace, size_t bytes, void *stream);
+
+/*
+ * Persistent decode.
+ *  q_nope   bf16 [num_seqs * q_per_seq, num_heads, 448], contiguous
+ *  q_rope   bf16 [num_seqs * q_per_seq, num_heads, 64], contiguous
+ *           Tokens b*q_per_seq .. (b+1)*q_per_seq - 1 belong to sequence b
+ *           and share its index list (no causal mask among them).
+ *  num_seqs >= 0 (0 launches nothing); q_per_seq in [1, 8];
+ *  num_heads in {16, 32, 64, 128}.
+ *  kv       the pool (see smd_kv_pool).
+ *  kv_indptr  int32 device [num_seqs + 1], non-decreasing; sequence b owns
+ *           kv_indices[kv_indptr[b] .. kv_indptr[b+1]); kv_indptr[0] may be
+ *           > 0.  (A decreasing pair is read as K_b = 0.)
+ *  kv_indices int32 device, flat; i < 0 or i >= num_rows is masked.
+ *  sink, softmax_scale as for smd_sparse_mla_decode.
+ *  workspace  device memory, 256-byte aligned, >= smd_persistent_workspace_bytes
+ *           (num_heads, q_per_seq, num_partitions) bytes, zeroed once by
+ *           smd_persistent_workspace_reset.  Calls that share a workspace
+ *           must be ordered on the GPU (same stream or synchronised); after
+ *           a call the plan region holds int32 [num_partitions][4] =
+ *           (t0, t1, first sequence, last sequence) of each partition
+ *           (-1, -1 for an empty one).
+ *  num_partitions in [1, SMD_MAX_PARTITIONS].
+ *  out      bf16 [num_seqs * q_per_seq, num_heads, 512] (required)
+ *  lse      fp32 [num_seqs * q_per_seq, num_heads] or NULL; ln Z with the sink.
+ *  Rows of sequences with K_b = 0 are not written.
+ */
+int smd_sparse_mla_decode_persistent(const void *q_nope, const void *q_rope, int32_t num_seqs,
+                                     int32_t q_per_seq, int32_t num_heads, const smd_kv_pool *kv,
+                                     const int32_t *kv_indptr, const int32_t *kv_indices,
+                                     const float *sink, float softmax_scale, void *workspace,
+                                     size_t workspace_bytes, int32_t num_partitions, void *out,
+                                     float *lse, void *stream);
 
 #ifdef __cplusplus
 }

@@ -21,6 +21,7 @@ ROPE = 64
 DIM = 512
 MAX_SPLITS = 32
 SPLIT_ALIGN = 64
+MAX_PARTITIONS = 16384
 
 KV_BF16 = 0
 KV_FP8_E4M3_UE8M0 = 1
@@ -95,6 +96,15 @@ def lib() -> ctypes.CDLL:
                                         vp, f32, i32, vp, vp, vp, vp, vp]
     L.smd_merge_partials.restype = ctypes.c_int
     L.smd_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    L.smd_persistent_default_partitions.restype = i32
+    L.smd_persistent_default_partitions.argtypes = [i32, i32, i32]
+    L.smd_persistent_workspace_bytes.restype = ctypes.c_size_t
+    L.smd_persistent_workspace_bytes.argtypes = [i32, i32, i32]
+    L.smd_persistent_workspace_reset.restype = ctypes.c_int
+    L.smd_persistent_workspace_reset.argtypes = [vp, ctypes.c_size_t, vp]
+    L.smd_sparse_mla_decode_persistent.restype = ctypes.c_int
+    L.smd_sparse_mla_decode_persistent.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, vp, vp, f32,
+                                                   vp, ctypes.c_size_t, i32, vp, vp, vp]
     _lib = L
     return L
 
@@ -304,8 +314,94 @@ def merge_partials(partial_o: torch.Tensor, partial_lse: torch.Tensor, sink: Opt
     return out, lse
 
 
+
+# ----------------------------------------------------------------------------
+# persistent, graph-safe decode over ragged sequences
+# ----------------------------------------------------------------------------
+def persistent_default_partitions(num_heads: int, q_per_seq: int = 1, num_cus: int = 0) -> int:
+    """Partitions that fill num_cus CUs once (num_cus=0: 256)."""
+    return _check("smd_persistent_default_partitions",
+                  lib().smd_persistent_default_partitions(num_heads, q_per_seq, num_cus))
+
+
+def persistent_workspace_bytes(num_heads: int, q_per_seq: int, num_partitions: int) -> int:
+    n = lib().smd_persistent_workspace_bytes(num_heads, q_per_seq, num_partitions)
+    if n == 0:
+        raise SmdError("smd_persistent_workspace_bytes", -1, lib().smd_last_error().decode())
+    return n
+
+
+class PersistentWorkspace:
+    """Device workspace of the persistent decode: allocated with torch and zeroed
+    once (do both outside graph capture).  Calls sharing it must be ordered on
+    the GPU; the kernel resets its counters itself, so it can be reused across
+    batch sizes and graph replays."""
+
+    def __init__(self, num_heads: int, q_per_seq: int = 1, num_partitions: Optional[int] = None,
+                 device=None):
+        dev = torch.device(device if device is not None else "cuda")
+        self.num_heads, self.q_per_seq = num_heads, q_per_seq
+        self.num_partitions = num_partitions or persistent_default_partitions(num_heads, q_per_seq)
+        self.nbytes = persistent_workspace_bytes(num_heads, q_per_seq, self.num_partitions)
+        self.buffer = torch.empty(self.nbytes + 256, dtype=torch.uint8, device=dev)
+        off = (-self.buffer.data_ptr()) % 256
+        self.view = self.buffer[off:off + self.nbytes]
+        _check("smd_persistent_workspace_reset",
+               lib().smd_persistent_workspace_reset(self.view.data_ptr(), self.nbytes, _stream(self.view)))
+
+    def plan(self) -> torch.Tensor:
+        """The plan region: int32 [P, 4] = (t0, t1, first sequence, last sequence)."""
+        return self.view[:16 * self.num_partitions].view(torch.int32).view(self.num_partitions, 4)
+
+
+def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool,
+                                 kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
+                                 sink: Optional[torch.Tensor], softmax_scale: float, *,
+                                 q_per_seq: int = 1, workspace: PersistentWorkspace,
+                                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+    """Persistent decode over ragged sequences: q bf16 [B*q_per_seq, H, 448/64],
+    kv_indptr int32 [B+1], kv_indices int32 flat.  Returns (out, lse); rows of
+    sequences with no index are left as they were in `out` / `lse`."""
+    dev = q_nope.device
+    _need(q_nope, "q_nope", torch.bfloat16, device=dev)
+    if q_nope.dim() != 3 or q_nope.shape[2] != NOPE:
+        raise ValueError("q_nope must be [T, H, 448]")
+    T, H, _ = q_nope.shape
+    _need(q_rope, "q_rope", torch.bfloat16, (T, H, ROPE), dev)
+    if not (q_nope.is_contiguous() and q_rope.is_contiguous()):
+        raise ValueError("q_nope and q_rope must be contiguous")
+    if T % q_per_seq:
+        raise ValueError("the token count must be a multiple of q_per_seq")
+    B = T // q_per_seq
+    _need(kv_indptr, "kv_indptr", torch.int32, (B + 1,), dev)
+    _need(kv_indices, "kv_indices", torch.int32, device=dev)
+    if not (kv_indptr.is_contiguous() and kv_indices.is_contiguous()):
+        raise ValueError("kv_indptr and kv_indices must be contiguous")
+    if sink is not None:
+        _need(sink, "sink", torch.float32, (H,), dev)
+    if kv.device != dev:
+        raise ValueError("kv pool must be on the same device as q")
+    if (workspace.num_heads, workspace.q_per_seq) != (H, q_per_seq):
+        raise ValueError("workspace was sized for other shapes")
+    if out is None:
+        out = torch.empty((T, H, DIM), dtype=torch.bfloat16, device=dev)
+    if lse is None:
+        lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
+    _need(lse, "lse", torch.float32, (T, H), dev)
+    pool = kv._struct()
+    rc = lib().smd_sparse_mla_decode_persistent(
+        q_nope.data_ptr(), q_rope.data_ptr(), B, q_per_seq, H, ctypes.byref(pool), kv_indptr.data_ptr(),
+        kv_indices.data_ptr() if kv_indices.numel() else kv_indptr.data_ptr(), _ptr(sink), float(softmax_scale),
+        workspace.view.data_ptr(), workspace.nbytes, workspace.num_partitions, out.data_ptr(), lse.data_ptr(),
+        _stream(q_nope))
+    _check("smd_sparse_mla_decode_persistent", rc)
+    return out, lse
+
 __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
-           "sparse_mla_decode", "merge_partials", "lib", "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0"]
+           "sparse_mla_decode", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
+           "PersistentWorkspace", "sparse_mla_decode_persistent", "lib", "library_path", "KV_BF16",
+           "KV_FP8_E4M3_UE8M0"]
 
 if os.environ.get("SMD_EAGER_LOAD") == "1":
     lib()

@@ -18,7 +18,7 @@ INCLUDE = PKG.parent / "include"
 LIB = PKG / "libsmd.so"
 BUILD_DIR = PKG.parent / "_build"
 
-SOURCES = ["api.cpp", "plan.cpp", "decode_kernels.hip"]
+SOURCES = ["api.cpp", "plan.cpp", "decode_kernels.hip", "persistent_kernel.hip"]
 ARCH = os.environ.get("SMD_OFFLOAD_ARCH", "gfx950")
 
 
@@ -38,18 +38,23 @@ def common_flags() -> list[str]:
 def build(verbose: bool = False) -> Path:
     cc = hipcc()
     BUILD_DIR.mkdir(exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # the translation units compile in parallel
         obj = BUILD_DIR / (Path(src).stem + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
         cmd = [cc, *common_flags(), "-c", *lang, str(CSRC / src), "-o", str(obj)]
         if verbose:
             print(" ".join(cmd), flush=True)
-        res = subprocess.run(cmd, capture_output=True, text=True)
-        if res.returncode != 0:
-            sys.stderr.write(res.stdout + res.stderr)
-            raise RuntimeError(f"hipcc failed on {src}")
+        procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)))
         objs.append(str(obj))
+    failed = []
+    for src, proc in procs:
+        out, _ = proc.communicate()
+        if proc.returncode != 0:
+            sys.stderr.write(out)
+            failed.append(src)
+    if failed:
+        raise RuntimeError(f"hipcc failed on {', '.join(failed)}")
     tmp = LIB.with_suffix(".so.tmp")
     cmd = [cc, "-shared", f"--offload-arch={ARCH}", "-fPIC", *objs, "-o", str(tmp)]
     res = subprocess.run(cmd, capture_output=True, text=True)

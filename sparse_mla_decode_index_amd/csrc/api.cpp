@@ -240,3 +240,135 @@ extern "C" int smd_merge_partials(const float *partial_o, const float *partial_l
   }
   return SMD_OK;
 }
+
+// ----------------------------------------------------------------------------
+// persistent, graph-safe variant
+// ----------------------------------------------------------------------------
+static int persist_rb(int32_t M) { return M >= 64 ? 4 : M / 16; }
+
+extern "C" int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, int32_t num_cus) {
+  g_err[0] = 0;
+  if (!heads_ok(num_heads) || q_per_seq < 1 || q_per_seq > 8) {
+    set_error("smd_persistent_default_partitions: unsupported num_heads=%d / q_per_seq=%d", num_heads, q_per_seq);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  const int32_t cus = num_cus > 0 ? num_cus : 256;
+  const int32_t M = num_heads * q_per_seq;
+  const int32_t groups = (M + 63) / 64;
+  const int32_t p = cus / groups;
+  return p < 1 ? 1 : (p > SMD_MAX_PARTITIONS ? SMD_MAX_PARTITIONS : p);
+}
+
+extern "C" size_t smd_persistent_workspace_bytes(int32_t num_heads, int32_t q_per_seq, int32_t num_partitions) {
+  g_err[0] = 0;
+  if (!heads_ok(num_heads) || q_per_seq < 1 || q_per_seq > 8 || num_partitions < 1 ||
+      num_partitions > SMD_MAX_PARTITIONS) {
+    set_error("smd_persistent_workspace_bytes: unsupported num_heads=%d q_per_seq=%d num_partitions=%d",
+              num_heads, q_per_seq, num_partitions);
+    return 0;
+  }
+  return persist_layout((int64_t)num_heads * q_per_seq, num_partitions).total;
+}
+
+extern "C" int smd_persistent_workspace_reset(void *workspace, size_t bytes, void *stream) {
+  static const char *fn = "smd_persistent_workspace_reset";
+  g_err[0] = 0;
+  if (!workspace || bytes == 0) {
+    set_error("%s: workspace is NULL or empty", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  hipError_t e = hipMemsetAsync(workspace, 0, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("%s: hipMemsetAsync failed: %s", fn, hipGetErrorString(e));
+    return SMD_ERR_HIP;
+  }
+  return SMD_OK;
+}
+
+extern "C" int smd_sparse_mla_decode_persistent(const void *q_nope, const void *q_rope, int32_t num_seqs,
+                                                int32_t q_per_seq, int32_t num_heads, const smd_kv_pool *kv,
+                                                const int32_t *kv_indptr, const int32_t *kv_indices,
+                                                const float *sink, float softmax_scale, void *workspace,
+                                                size_t workspace_bytes, int32_t num_partitions, void *out,
+                                                float *lse, void *stream) {
+  static const char *fn = "smd_sparse_mla_decode_persistent";
+  g_err[0] = 0;
+  if (num_seqs < 0) {
+    set_error("%s: negative num_seqs=%d", fn, num_seqs);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!heads_ok(num_heads)) {
+    set_error("%s: num_heads=%d not in {16,32,64,128}", fn, num_heads);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (q_per_seq < 1 || q_per_seq > 8) {
+    set_error("%s: q_per_seq=%d not in [1,8]", fn, q_per_seq);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (num_partitions < 1 || num_partitions > SMD_MAX_PARTITIONS) {
+    set_error("%s: num_partitions=%d not in [1,%d]", fn, num_partitions, SMD_MAX_PARTITIONS);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!isfinite(softmax_scale)) {
+    set_error("%s: softmax_scale is not finite", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  DecodeArgs a = {};
+  int rc = check_pool(fn, kv, a);
+  if (rc) return rc;
+  const int32_t M = num_heads * q_per_seq;
+  const PersistLayout lay = persist_layout(M, num_partitions);
+  if (!workspace || ((uintptr_t)workspace & 255u)) {
+    set_error("%s: workspace must be a non-NULL 256-byte aligned device buffer", fn);
+    return SMD_ERR_WORKSPACE;
+  }
+  if (workspace_bytes < lay.total) {
+    set_error("%s: workspace of %zu bytes is below the %zu bytes needed for num_heads=%d q_per_seq=%d "
+              "num_partitions=%d", fn, workspace_bytes, lay.total, num_heads, q_per_seq, num_partitions);
+    return SMD_ERR_WORKSPACE;
+  }
+  if (num_seqs > 0) {
+    if (!q_nope || !q_rope || !kv_indptr || !kv_indices || !out) {
+      set_error("%s: q_nope, q_rope, kv_indptr, kv_indices and out are required", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(out)) {
+      set_error("%s: q_nope, q_rope and out must be 16-byte aligned", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (((uintptr_t)kv_indptr & 3) || ((uintptr_t)kv_indices & 3) || (lse && ((uintptr_t)lse & 3))) {
+      set_error("%s: kv_indptr, kv_indices and lse must be 4-byte aligned", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+  }
+  if (num_seqs == 0) return SMD_OK;
+
+  const int rb = persist_rb(M);
+  PersistArgs pa = {};
+  a.q_nope = (const uint16_t *)q_nope;
+  a.q_rope = (const uint16_t *)q_rope;
+  a.sink = sink;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.H = num_heads;
+  a.qps = q_per_seq;
+  a.M = M;
+  a.S = 1;
+  a.G = M / (16 * rb);
+  a.out = (uint16_t *)out;
+  a.lse = lse;
+  pa.d = a;
+  pa.kv_indptr = kv_indptr;
+  pa.kv_indices = kv_indices;
+  pa.B = num_seqs;
+  pa.P = num_partitions;
+  uint8_t *ws = (uint8_t *)workspace;
+  pa.plan = (int32_t *)(ws + lay.plan_off);
+  pa.counters = (uint32_t *)(ws + lay.ctr_off);
+  pa.slots = (float *)(ws + lay.slot_off);
+  hipError_t e = launch_persistent(pa, rb, kv->dtype == SMD_KV_FP8_E4M3_UE8M0, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SMD_ERR_HIP;
+  }
+  return SMD_OK;
+}

@@ -1,425 +1,16 @@
 // Split-KV sparse MLA decode and stage-2 merge kernels for gfx950 (MI355X).
 //
-// What is computed (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
-// decode on gfx950", Design): per query row, a 512-wide dot product (448 NoPE
-// + 64 RoPE dims) with every selected latent row, an online softmax that also
-// counts a per-head sink logit, and a PV product over the same 512-wide rows.
 // Split partials and their merge follow the aiter page "[ASM][HIP][MLA v4 nm]
-// Split plan helper and persistent decode kernel", Summary part 1.
-//
-// Work decomposition.  A workgroup owns one index row b, one group of
-// 16*WAVES query rows (heads x MTP positions sharing that row) and one split
-// r of the row's index positions.  Each wave owns 16 query rows.
-//
-// Per 32-row KV tile:
-//   gather   every valid selected row is copied HBM -> LDS with one
-//            16-byte-per-lane direct-to-LDS load per row (bf16), or loaded
-//            into registers, dequantised (e4m3 x 2^(code-127) -> bf16) and
-//            stored (fp8).  Invalid or out-of-split rows are copied from a
-//            zero row, so stale LDS contents (even NaN) never reach the MFMAs.
-//   QK       S^T[32 kv x 16 q] = K[32 x 512] . Q^T[512 x 16] with
-//            v_mfma_f32_16x16x32_bf16; K is read from LDS, Q stays in VGPRs.
-//            In this orientation each lane holds scores of one query row, so
-//            the softmax statistics are per-lane values.
-//   softmax  running max m and sum l per query row, reduced across the four
-//            16-lane groups with two cross-lane exchanges; exp2 with the
-//            scale pre-multiplied by log2(e).
-//   PV       O^T[512 x 16] += V^T[512 x 32] . P^T[32 x 16]; P^T is the score
-//            tile itself converted to bf16 in registers (no LDS round trip),
-//            V^T comes from LDS with ds_read_b64_tr_b16 transposed reads.
-// The LDS tile is row-major, 1 KiB per row, with the 16-byte chunks of row r
-// permuted by an XOR of swz(r) so that both the 16-byte QK reads (16 rows, one
-// column) and the 8-byte transposed reads (8 rows, 32 bytes each) touch
-// distinct banks.
-#include "smd_internal.h"
-
-#include <math.h>
+// Split plan helper and persistent decode kernel", Summary part 1: split r of
+// an index row covers a contiguous range of its positions and writes an FP32
+// partial (o_r, lse_r); the merge reweights the partials by their log-sum-exps
+// and folds in the sink.  One split writes the bf16 output directly.
+#include "decode_core.h"
 
 namespace smd {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define SMD_LDS __attribute__((address_space(3)))
-#define SMD_GLOBAL __attribute__((address_space(1)))
-
-constexpr int kBK = 32;                      // KV rows per tile
-constexpr int kLdsRow = 1024;                // bytes per bf16 row in LDS
-constexpr int kTileBytes = kBK * kLdsRow;    // 32 KiB
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// A zero row used as the source of every masked row (1 KiB of zero bytes:
-// bf16 zeros, e4m3 zeros and UE8M0 code 0).
-__device__ __attribute__((aligned(256))) uint8_t g_zero_row[1024];
-
-// XOR permutation of 16-byte chunks for row r of a tile.  Rows r and r+16 share
-// it.  swz is a bijection on 0..15 (QK reads of 16 consecutive rows hit 16
-// distinct chunk slots) and maps rows 0..7 / 8..15 to even / odd values (the
-// transposed reads of 8 rows x 32 bytes cover 256 distinct bytes).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-
-__device__ __forceinline__ float wave_xor(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// UE8M0 code -> fp32 scale 2^(code-127).  Code 0 is the subnormal 2^-127.
-__device__ __forceinline__ float ue8m0_scale(uint32_t code) {
-  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
-}
-
-// A row's reference max is fixed at its first tile with a valid entry; a later
-// score more than this far above it (log2 domain) sends the workgroup through
-// an exact-max second pass, so every p = 2^(x - m_ref) stays <= 2^32.
-constexpr float kRefSlackLog2 = 32.f;
-
-// Index lists are staged through LDS in blocks of kIdxBlock positions (8 tiles),
-// double-buffered and refilled kIdxBlock/32 - 3 tiles before first use, so no
-// per-tile global read sits on the critical path of the row gather.
-constexpr int kIdxBlock = 256;
-constexpr int kTilesPerIdxBlock = kIdxBlock / kBK;  // 8
-
-template <int DS>
-struct Smem {
-  uint8_t tile[2][kTileBytes];          // double-buffered bf16 tiles
-  float sx[DS > 1 ? 4 * 64 * 8 : 4];    // partial S^T tiles of the dim-split waves
-  int32_t ibuf[2][kIdxBlock];           // index blocks (tiles 8k .. 8k+7 in ibuf[k & 1])
-};
-
-// Index block k (positions p0 + 256k + tid, tid < 256), clamped into [p0, p1)
-// (p1 > p0) so that the load is unconditional: every step issues the same
-// memory operations and the compiler's wait counts stay exact.  Positions at
-// or beyond p1 are masked where the indices are used.
-__device__ __forceinline__ int load_idx_block(const int32_t *row_idx, int p0, int p1, int k) {
-  return row_idx[min(p0 + k * kIdxBlock + (int)threadIdx.x, p1 - 1)];
-}
-
-// Row data of one tile held in registers between its global loads and its
-// LDS stores.  Wave w handles tile rows 8w .. 8w+7.
-//   bf16: v[i] = logical 16-byte chunk lane ^ swz(rr) of row rr = 8w + i.
-//   fp8:  v[j] (j < 4) = 16 e4m3 bytes of chunk (lane & 31) (clamped to 27) of
-//         row 8w + 2j + (lane >> 5); rope = 16 RoPE bytes, chunk lane & 7 of
-//         row 8w + (lane >> 3); code = UE8M0 byte (lane & 7) of that row.
-template <bool FP8>
-struct Staged {
-  u32x4 v[FP8 ? 4 : kBK / 4];
-  u32x4 rope;
-  uint32_t code;
-};
-
-// Per-wave constants of the gather, computed once.
-struct GatherLanes {
-  uint32_t voff[kBK / 4];  // bf16: byte offset of this lane's chunk in row 8w+i
-  uint32_t sel_rope;       // bf16, split layout: bit i set when that chunk is RoPE
-};
-
-__device__ __forceinline__ GatherLanes make_gather_lanes(int wave, int lane) {
-  GatherLanes g;
-  g.sel_rope = 0;
-#pragma unroll
-  for (int i = 0; i < kBK / 4; ++i) {
-    const int c = lane ^ swz(wave * (kBK / 4) + i);
-    g.voff[i] = (uint32_t)c * 16u;
-    g.sel_rope |= (c >= kNope / 8 ? 1u : 0u) << i;
-  }
-  return g;
-}
-
-// Global loads of this wave's 8 rows of a tile (indices at tidx in LDS).
-// Invalid rows (index outside [0, N), or past the split) read the zero row, so
-// stale LDS contents (even NaN) never reach the MFMAs and every tile issues
-// the same loads.  bf16 rows whose RoPE part follows the NoPE part (the packed
-// [N, 512] layout) need one scalar row base per row; other layouts select the
-// NoPE or RoPE base per lane.
-template <bool FP8, bool PACKED>
-__device__ __forceinline__ void load_rows(const DecodeArgs &a, const uint8_t *zrow, const GatherLanes &gl,
-                                          const int32_t SMD_LDS *tidx, int first_pos, int p1, int wave,
-                                          int lane, Staged<FP8> &st) {
-  const int32_t SMD_LDS *widx = tidx + wave * (kBK / 4);  // this wave's 8 indices
-  const int rows_left = p1 - first_pos - wave * (kBK / 4);  // rows of this wave below p1
-  if constexpr (!FP8) {
-    const u32x4 ia = *(const u32x4 SMD_LDS *)(widx);
-    const u32x4 ib = *(const u32x4 SMD_LDS *)(widx + 4);
-    // byte offsets from the NoPE base; the zero row as an offset from it
-    const uint64_t zoff = (uint64_t)(zrow - a.kv_nope);
-#pragma unroll
-    for (int i = 0; i < kBK / 4; ++i) {
-      const uint32_t idx = __builtin_amdgcn_readfirstlane(i < 4 ? ia[i & 3] : ib[i & 3]);
-      const bool v = (i < rows_left) & (idx < a.num_rows32);  // idx < 0 wraps to a huge value
-      if constexpr (PACKED) {
-        const uint64_t off = v ? (uint64_t)idx * a.row_stride32 : zoff;
-        st.v[i] = *(const u32x4 *)(a.kv_nope + off + gl.voff[i]);
-      } else {
-        const uint64_t zr = (uint64_t)(zrow - a.kv_rope) + kNope * 2;
-        const uint64_t noff = v ? (uint64_t)idx * (uint64_t)a.nope_stride_b : zoff;
-        const uint64_t roff = v ? (uint64_t)idx * (uint64_t)a.rope_stride_b : zr;
-        const uint8_t *nb = a.kv_nope + noff;
-        const uint8_t *rb = a.kv_rope + roff - kNope * 2;
-        st.v[i] = *(const u32x4 *)((((gl.sel_rope >> i) & 1) ? rb : nb) + gl.voff[i]);
-      }
-    }
-  } else {
-    const u32x4 ia = *(const u32x4 SMD_LDS *)(widx);
-    const u32x4 ib = *(const u32x4 SMD_LDS *)(widx + 4);
-    const int c = min(lane & 31, 27);
-    const uint64_t zoff = (uint64_t)(zrow - a.kv_nope);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t ia_ = __builtin_amdgcn_readfirstlane(j < 2 ? ia[(2 * j) & 3] : ib[(2 * j) & 3]);
-      const uint32_t ib_ = __builtin_amdgcn_readfirstlane(j < 2 ? ia[(2 * j + 1) & 3] : ib[(2 * j + 1) & 3]);
-      const bool va = (2 * j < rows_left) & (ia_ < a.num_rows32);
-      const bool vb = (2 * j + 1 < rows_left) & (ib_ < a.num_rows32);
-      const uint64_t oa = va ? (uint64_t)ia_ * (uint64_t)a.nope_stride_b : zoff;
-      const uint64_t ob = vb ? (uint64_t)ib_ * (uint64_t)a.nope_stride_b : zoff;
-      st.v[j] = *(const u32x4 *)(a.kv_nope + (lane < 32 ? oa : ob) + c * 16);
-    }
-    // RoPE and codes of the 8 rows: lane l serves row l >> 3
-    const uint32_t il = (uint32_t)widx[lane >> 3];
-    const bool vl = ((lane >> 3) < rows_left) & (il < a.num_rows32);
-    const uint8_t *rp = vl ? a.kv_rope + (uint64_t)il * (uint64_t)a.rope_stride_b : zrow;
-    const uint8_t *sp = vl ? a.kv_scale + (uint64_t)il * (uint64_t)a.scale_stride_b : zrow;
-    st.rope = *(const u32x4 *)(rp + (lane & 7) * 16);
-    st.code = sp[lane & 7];
-  }
-}
-
-// LDS stores of the staged rows into `tile` (bf16 layout, chunks swizzled);
-// fp8 rows are dequantised on the way: e4m3 x 2^(code-127) is exact in bf16.
-template <bool FP8>
-__device__ __forceinline__ void store_rows(uint8_t SMD_LDS *tile, int wave, int lane, const Staged<FP8> &st) {
-  if constexpr (!FP8) {
-#pragma unroll
-    for (int i = 0; i < kBK / 4; ++i)
-      *(u32x4 SMD_LDS *)(tile + (wave * (kBK / 4) + i) * kLdsRow + lane * 16) = st.v[i];
-  } else {
-    const int c = lane & 31;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rl = 2 * j + (lane >> 5);            // row within the wave's 8
-      // the code of block c/4 of that row sits in lane rl*8 + c/4
-      const uint32_t code = (uint32_t)__shfl((int)st.code, rl * 8 + (min(c, 27) >> 2), 64) & 0xffu;
-      if (c < 28) {
-        const int rr = wave * (kBK / 4) + rl;
-        const int f = swz(rr);
-        uint8_t SMD_LDS *row = tile + rr * kLdsRow;
-        const float sc = ue8m0_scale(code);
-        u32x4 lo, hi;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[j][q], sc, false));
-          const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[j][q], sc, true));
-          if (q < 2) { lo[2 * q] = u0; lo[2 * q + 1] = u1; }
-          else { hi[2 * q - 4] = u0; hi[2 * q - 3] = u1; }
-        }
-        *(u32x4 SMD_LDS *)(row + (((2 * c) ^ f) << 4)) = lo;
-        *(u32x4 SMD_LDS *)(row + (((2 * c + 1) ^ f) << 4)) = hi;
-      }
-    }
-    const int rr = wave * (kBK / 4) + (lane >> 3);
-    *(u32x4 SMD_LDS *)(tile + rr * kLdsRow + (((kNope / 8 + (lane & 7)) ^ swz(rr)) << 4)) = st.rope;
-  }
-}
-
-// Valid-row bits of a tile (first position first_pos, indices at tidx).
-__device__ __forceinline__ uint32_t tile_valid_bits(const int32_t SMD_LDS *tidx, int first_pos, int p1, int lane,
-                                                    uint32_t num_rows) {
-  const int idx_v = tidx[lane & (kBK - 1)];
-  return (uint32_t)__ballot(lane < kBK && first_pos + lane < p1 && (uint32_t)idx_v < (uint32_t)num_rows);
-}
-
-// Per-wave state of the softmax and the O^T accumulator (ND 16-dim blocks).
-template <int ND>
-struct WaveState {
-  f32x4 acc[ND];  // acc[d][i] = sum_j 2^(x_j - m_ref) V[j][16(d0+d) + 4grp + i]
-  float m_ref;    // reference max (log2 domain), same in the four 16-lane groups
-  float l_run;    // this lane's share of sum_j 2^(x_j - m_ref)
-  bool overflow;  // some score exceeded m_ref + kRefSlackLog2 (this lane)
-};
-
-enum Pass { kPassMain = 0, kPassMax = 1, kPassFixed = 2 };
-
-// QK, softmax weights and PV over one 32-row tile for one wave: 16 query rows
-// and the 512/DS dims starting at chunk c0 (QK, 32-dim chunks) / block d0
-// (PV, 16-dim blocks).  With DS > 1 the partial scores of the DS waves that
-// share the query rows are summed through LDS (fixed order, so the DS waves
-// hold bit-identical scores and take identical softmax decisions).
-//   kPassMain:  m_ref is set at the row's first valid tile; later tiles only
-//               flag scores above m_ref + kRefSlackLog2.
-//   kPassMax:   scores only; m_ref becomes the exact running max.
-//   kPassFixed: m_ref is already the exact max.
-// The O accumulator is only ever touched by MFMAs here, never rescaled.
-template <int RB, int DS, int PASS, bool P_HILO>
-__device__ __forceinline__ void compute_tile(const uint8_t SMD_LDS *tile, float SMD_LDS *sx,
-                                             const bf16x8 (&qreg)[16 / DS], const int (&qk_base)[4],
-                                             const int (&pv_base)[8], uint32_t vbits, int wave,
-                                             int lane, int grp, int ds, float scale_log2,
-                                             WaveState<32 / DS> &w) {
-  constexpr int NC = 16 / DS, ND = 32 / DS;
-  const int c0 = ds * NC, d0 = ds * ND;
-  // ---- QK: S^T tiles for kv rows 0..15 (s0) and 16..31 (s1) over this wave's dims
-  constexpr int kPre = NC < 4 ? NC : 4;
-  f32x4 s0 = {0.f, 0.f, 0.f, 0.f}, s1 = {0.f, 0.f, 0.f, 0.f};
-  bf16x8 k0[kPre], k1[kPre];
-  auto qk_load = [&](int c) {
-    const int cg = c0 + c;
-    const uint8_t SMD_LDS *p = tile + qk_base[cg & 3] + 256 * (cg >> 2);
-    k0[c % kPre] = *(const bf16x8 SMD_LDS *)(p);
-    k1[c % kPre] = *(const bf16x8 SMD_LDS *)(p + 16 * kLdsRow);
-  };
-#pragma unroll
-  for (int c = 0; c < kPre; ++c) qk_load(c);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const bf16x8 a0 = k0[c % kPre], a1 = k1[c % kPre];
-    if (c + kPre < NC) qk_load(c + kPre);
-    s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, qreg[c], s0, 0, 0, 0);
-    s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, qreg[c], s1, 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads kPre steps ahead
-  }
-  if constexpr (DS > 1) {
-    f32x4 SMD_LDS *mine = (f32x4 SMD_LDS *)(sx + (wave * 64 + lane) * 8);
-    mine[0] = s0;
-    mine[1] = s1;
-    __syncthreads();
-    const int rb = wave % RB;
-    s0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    s1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int e = 0; e < DS; ++e) {
-      const f32x4 SMD_LDS *o = (const f32x4 SMD_LDS *)(sx + ((rb + e * RB) * 64 + lane) * 8);
-      s0 += o[0];
-      s1 += o[1];
-    }
-  }
-
-  // ---- scores; this lane holds kv rows 4grp+i (s0) and 16+4grp+i (s1)
-  float x[8];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[i] = ((vbits >> (4 * grp + i)) & 1) ? s0[i] * scale_log2 : -INFINITY;
-    x[4 + i] = ((vbits >> (16 + 4 * grp + i)) & 1) ? s1[i] * scale_log2 : -INFINITY;
-  }
-  float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  tmax = fmaxf(tmax, wave_xor(tmax, 16));
-  tmax = fmaxf(tmax, wave_xor(tmax, 32));
-  if constexpr (PASS == kPassMax) {
-    w.m_ref = fmaxf(w.m_ref, tmax);
-    return;
-  }
-  if constexpr (PASS == kPassMain) {
-    if (w.m_ref == -INFINITY) w.m_ref = tmax;  // nothing accumulated yet for this row
-    w.overflow |= tmax > w.m_ref + kRefSlackLog2;
-  }
-  const float m_use = (w.m_ref == -INFINITY) ? 0.f : w.m_ref;
-  float psum = 0.f;
-  bf16x8 pb, pl;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const float p = exp2_fast(x[i] - m_use);
-    psum += p;
-    pb[i] = (__bf16)p;
-    // P_HILO: p = hi + lo with both parts bf16, so the PV product carries
-    // about 16 significant bits of p instead of 8 (needed for FP32 partials).
-    if constexpr (P_HILO) pl[i] = (__bf16)(p - (float)pb[i]);
-  }
-  w.l_run += psum;
-
-  // ---- PV: O^T[16d.., m] += V^T . P^T for this wave's dims, V^T read transposed
-  constexpr int kPv = ND < 4 ? ND : 4;
-  bf16x4 vlo[kPv], vhi[kPv];
-  auto pv_load = [&](int d) {
-    const int dg = d0 + d;
-    const uint8_t SMD_LDS *p = tile + pv_base[dg & 7] + 256 * (dg >> 3);
-    vlo[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p));
-    vhi[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p + 16 * kLdsRow));
-  };
-#pragma unroll
-  for (int d = 0; d < kPv; ++d) pv_load(d);
-#pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    const bf16x8 av = __builtin_shufflevector(vlo[d % kPv], vhi[d % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
-    if (d + kPv < ND) pv_load(d + kPv);
-    w.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb, w.acc[d], 0, 0, 0);
-    if constexpr (P_HILO) w.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl, w.acc[d], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Walk the split's tiles once.  While tile t is computed from LDS, the rows
-// of tiles t+1 and t+2 are in flight into registers; the rows of t+1 are
-// stored to the other LDS buffer after the math, and one barrier per tile
-// publishes them.  Indices come from the LDS index blocks; the block after
-// the current one is re-read every step (cache hits after the first) and
-// stored three tiles before it is first needed.  Every step issues the same
-// loads (rows past the end read the zero row), so the compiler's vmcnt waits
-// let two tiles stay in flight.
-template <int RB, int DS, bool FP8, bool PACKED, bool P_HILO, int PASS>
-__device__ __forceinline__ void run_split(const DecodeArgs &a, Smem<DS> &sm, const int32_t *row_idx, int p0,
-                                          int p1, int wave, int lane, int grp, int ds,
-                                          const bf16x8 (&qreg)[16 / DS], const int (&qk_base)[4],
-                                          const int (&pv_base)[8], WaveState<32 / DS> &w) {
-  const int ntiles = (p1 - p0 + kBK - 1) / kBK;
-  if (ntiles <= 0) return;
-  uint8_t SMD_LDS *tile0 = (uint8_t SMD_LDS *)&sm.tile[0][0];
-  float SMD_LDS *sx = (float SMD_LDS *)&sm.sx[0];
-  int32_t SMD_LDS *ib0 = (int32_t SMD_LDS *)&sm.ibuf[0][0];
-  // LDS address of the 32 indices of tile k
-  auto tidx = [&](int k) {
-    return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
-  };
-  Staged<FP8> sa, sb;
-  const uint8_t *zrow = g_zero_row;
-  const GatherLanes gl = make_gather_lanes(wave, lane);
-  const int blk0 = load_idx_block(row_idx, p0, p1, 0);
-  __syncthreads();  // the buffers may still be read by a previous pass
-  ib0[threadIdx.x] = blk0;
-  __syncthreads();
-  load_rows<FP8, PACKED>(a, zrow, gl, tidx(0), p0, p1, wave, lane, sa);
-  load_rows<FP8, PACKED>(a, zrow, gl, tidx(1), p0 + kBK, p1, wave, lane, sb);
-  store_rows<FP8>(tile0, wave, lane, sa);
-  __syncthreads();
-  uint32_t v_cur = tile_valid_bits(tidx(0), p0, p1, lane, a.num_rows32);
-  // step t: tile t in buffer t&1; `nx` holds (in flight) the rows of t+1; the
-  // other staging set is refilled with the rows of t+2.  The loop runs two
-  // steps per iteration so each staging set has fixed registers; a padding
-  // step (t == ntiles) computes an all-masked tile of zero rows, which leaves
-  // every state unchanged, so the math is unconditional (a branch around it
-  // would make the allocator copy the accumulators).
-  auto step = [&](int t, Staged<FP8> &nx, Staged<FP8> &fill) {
-    const int nb = t / kTilesPerIdxBlock + 1;  // the next index block
-    const int blk = load_idx_block(row_idx, p0, p1, nb);
-    load_rows<FP8, PACKED>(a, zrow, gl, tidx(t + 2), p0 + (t + 2) * kBK, p1, wave, lane, fill);
-    compute_tile<RB, DS, PASS, P_HILO>(tile0 + (t & 1) * kTileBytes, sx, qreg, qk_base, pv_base, v_cur, wave,
-                                       lane, grp, ds, a.scale_log2, w);
-    store_rows<FP8>(tile0 + ((t + 1) & 1) * kTileBytes, wave, lane, nx);
-    if (t % kTilesPerIdxBlock == kTilesPerIdxBlock - 3) ib0[(nb & 1) * kIdxBlock + threadIdx.x] = blk;
-    __syncthreads();
-    v_cur = tile_valid_bits(tidx(t + 1), p0 + (t + 1) * kBK, p1, lane, a.num_rows32);
-  };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(t, sb, sa);
-    step(t + 1, sa, sb);
-  }
-}
-
 // Work decomposition: a workgroup (4 waves) owns one index row b, one group g
-// of 16*RB query rows and one split r.  Wave w owns the 16 query rows of
-// block w % RB and the 512/DS dims of slice w / RB (RB * DS = 4).
+// of 16*RB query rows and one split r.
 template <int RB, bool FP8, bool PACKED, bool P_HILO>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1))) void decode_kernel(DecodeArgs a) {
   constexpr int DS = 4 / RB;
@@ -449,93 +40,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
   const int m = g * (RB * 16) + rb * 16 + j;
   const int tok = b * a.qps + m / a.H;
   const int head = m % a.H;
-  const int64_t qrow = (int64_t)tok * a.H + head;
+  const int64_t qrow = (int64_t)tok * a.H + head;  // [T, H] row
 
-  // Q^T as the B operand: chunk c holds dims 32c + 8*grp .. +7 of row m.
   bf16x8 qreg[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    const int cg = ds * NC + c;
-    const uint16_t *src = (cg < 14) ? a.q_nope + qrow * kNope + 32 * cg + 8 * grp
-                                    : a.q_rope + qrow * kRope + 32 * (cg - 14) + 8 * grp;
-    qreg[c] = *(const bf16x8 *)src;
-  }
-
-  // Per-lane LDS offsets.  QK: row j, logical chunk 4c+grp -> physical
-  // (4c+grp) ^ swz(j); the xor only touches the low 4 chunk bits, so c>>2 is an
-  // immediate 256-byte step.  PV: lanes 4t+q of a group supply row 4grp+t at
-  // dims 16d+4q, logical chunk 2d+(q>>1), byte 8(q&1) within it.
+  load_q<DS>(a, qrow, ds, grp, qreg);
   int qk_base[4], pv_base[8];
-  {
-    const int fj = swz(j);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) qk_base[c] = j * kLdsRow + (((4 * c + grp) ^ fj) << 4);
-    const int tq = j >> 2, qq = j & 3;
-    const int tr_row = 4 * grp + tq;
-    const int ftr = swz(tr_row);
-#pragma unroll
-    for (int d = 0; d < 8; ++d)
-      pv_base[d] = tr_row * kLdsRow + (((2 * d + (qq >> 1)) ^ ftr) << 4) + ((qq & 1) << 3);
-  }
+  lds_bases(j, grp, qk_base, pv_base);
 
   WaveState<ND> w;
-#pragma unroll
-  for (int d = 0; d < ND; ++d) w.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  w.m_ref = -INFINITY;
-  w.l_run = 0.f;
-  w.overflow = false;
-  run_split<RB, DS, FP8, PACKED, P_HILO, kPassMain>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg, qk_base,
-                                            pv_base, w);
-  if (__syncthreads_or(w.overflow)) {
-    // Rare: a score ran far above its row's first-tile max.  Redo the split
-    // with the exact max (found by a scores-only sweep) as the reference.
-#pragma unroll
-    for (int d = 0; d < ND; ++d) w.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    w.m_ref = -INFINITY;
-    w.l_run = 0.f;
-    run_split<RB, DS, FP8, PACKED, P_HILO, kPassMax>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg, qk_base,
-                                             pv_base, w);
-    run_split<RB, DS, FP8, PACKED, P_HILO, kPassFixed>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg,
-                                               qk_base, pv_base, w);
-  }
+  attend_range<RB, FP8, PACKED, P_HILO>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg, qk_base, pv_base, w);
 
-  // ---- epilogue: total sum per query row (identical in the DS waves of a block)
-  float l_tot = w.l_run;
-  l_tot += wave_xor(l_tot, 16);
-  l_tot += wave_xor(l_tot, 32);
-  const float m_ref = w.m_ref;
-  const int dbase = ds * ND;
-
-  const int64_t orow = qrow;  // [T, H] row of this lane's query row
+  const float l_tot = row_total(w.l_run);
+  const int dcol = 16 * (ds * ND) + 4 * grp;
+  const bool lse_lane = grp == 0 && ds == 0;
   if (a.S == 1 && a.out != nullptr) {
-    const float sink2 = a.sink ? a.sink[head] * kLog2e : -INFINITY;
-    const float mf = fmaxf(m_ref, sink2);
-    float inv = 0.f, lse_v = -INFINITY;
-    if (mf != -INFINITY) {
-      const float e = exp2_fast(m_ref - mf);
-      const float z = l_tot * e + exp2_fast(sink2 - mf);
-      inv = e / z;
-      lse_v = (mf + __log2f(z)) * kLn2;
-    }
-    uint16_t *dst = a.out + orow * kDim + 16 * dbase + 4 * grp;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) {
-      u32x2 v;
-      v[0] = (uint32_t)f32_to_bf16_rne(w.acc[d][0] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[d][1] * inv) << 16);
-      v[1] = (uint32_t)f32_to_bf16_rne(w.acc[d][2] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[d][3] * inv) << 16);
-      *(u32x2 *)(dst + 16 * d) = v;
-    }
-    if (a.lse != nullptr && grp == 0 && ds == 0) a.lse[orow] = lse_v;
+    write_direct(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
+                 (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
   } else {
-    float inv = 0.f, lse_v = -INFINITY;
-    if (l_tot > 0.f) {
-      inv = 1.f / l_tot;
-      lse_v = (m_ref + __log2f(l_tot)) * kLn2;
-    }
-    float *dst = a.part_o + (orow * a.S + r) * kDim + 16 * dbase + 4 * grp;
-#pragma unroll
-    for (int d = 0; d < ND; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[d] * inv;
-    if (grp == 0 && ds == 0) a.part_lse[orow * a.S + r] = lse_v;
+    write_partial(w, l_tot, a.part_o + (qrow * a.S + r) * kDim + dcol,
+                  lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
   }
 }
 

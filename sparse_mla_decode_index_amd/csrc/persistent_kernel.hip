@@ -1,0 +1,298 @@
+// Persistent, graph-safe sparse MLA decode over ragged sequences (gfx950).
+//
+// The aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent
+// decode kernel" (Summary, part 2) describes one launch with a fixed grid in
+// which every workgroup derives the split plan inside the kernel from the live
+// kv_indptr, unsplit rows are written as bf16 directly, and split rows are
+// merged by the workgroup that arrives last.  The plan rule here (the pages do
+// not print one): sequence b contributes tiles_b = ceil(K_b / 64) tiles, the
+// tiles of all sequences are concatenated in (sequence, tile) order, and
+// partition p of P owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
+//
+// Grid: P partitions x G query-row groups (16*RB rows each).  Workgroup (p, g)
+// walks the sequences of partition p and attends row group g of each over the
+// piece of its index list that p owns.  A sequence inside one partition is
+// written directly.  A sequence spread over partitions fp..lp is split: each
+// piece writes an FP32 partial (o = O/l, lse = m + ln l) to its slot, releases
+// it with an agent-scope fence and bumps the arrival counter of (g, fp); the
+// workgroup that sees the count of the other pieces (the non-empty partitions
+// of the span, minus one) merges the pieces in partition order
+// (with the sink), writes bf16 out and lse, and resets the counter to zero, so
+// the kernel can be replayed in a graph without any host-side reset.
+// Sequences with K_b = 0 own no tile and are never written.
+#include "decode_core.h"
+
+namespace smd {
+
+PersistLayout persist_layout(int64_t M, int64_t P) {
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  PersistLayout l;
+  l.plan_off = 0;
+  l.ctr_off = up((size_t)P * 4 * sizeof(int32_t));
+  l.slot_off = l.ctr_off + up((size_t)(M / 16) * (size_t)P * sizeof(uint32_t));
+  l.total = l.slot_off + (size_t)2 * (size_t)P * (size_t)M * 513 * sizeof(float);
+  return l;
+}
+
+// Inclusive prefix sum over the 256 threads of the workgroup; `total` gets the
+// sum of all 256 values.  s_red holds 4 ints and is free again on return.
+__device__ __forceinline__ int block_incl_scan(int v, int *s_red, int &total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  if (lane == 63) s_red[wave] = v;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const int x = s_red[w];
+    off += w < wave ? x : 0;
+    total += x;
+  }
+  __syncthreads();
+  return v + off;
+}
+
+__device__ __forceinline__ int seq_tiles(const int32_t *ptr, int b) {
+  return (max(ptr[b + 1] - ptr[b], 0) + kSplitAlign - 1) / kSplitAlign;  // decreasing: K_b = 0
+}
+
+// The partition whose tile range holds global tile x: the largest p with
+// floor(p*total/P) <= x, i.e. floor(((x+1)*P - 1) / total).
+__device__ __forceinline__ int tile_owner(int x, int total, int P) {
+  return (int)(((int64_t)(x + 1) * P - 1) / total);
+}
+
+// Partition p owns no tile when floor(p*total/P) == floor((p+1)*total/P)
+// (possible only when total < P).
+__device__ __forceinline__ bool part_empty(int p, int total, int P) {
+  return (int64_t)p * total / P == (int64_t)(p + 1) * total / P;
+}
+
+// Merge of the pieces of one split sequence for the workgroup's 16*RB query
+// rows: LSE = ln(sum_q e^(lse_q) + e^(sink)), out = sum_q e^(lse_q - LSE) o_q.
+// The pieces are held by the non-empty partitions among fp..lp, in that
+// order.  The piece of partition q sits in slot 2q, except the first piece,
+// which sits in slot 2fp+1 when the sequence is not the first of partition fp.
+// One wave per query row, 8 dims per lane; lane k looks at partition fp + k.
+__device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g, int rows, int fp, int lp,
+                                             int first_slot, int total) {
+  const DecodeArgs &a = pa.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lp - fp + 1;  // partitions in the span (empty ones hold nothing)
+  const size_t slot_floats = (size_t)a.M * 513;
+  for (int r = wave; r < rows; r += 4) {
+    const int m = g * rows + r;
+    const int tok = b * a.qps + m / a.H;
+    const int head = m % a.H;
+    const int64_t qrow = (int64_t)tok * a.H + head;
+    const float sink = a.sink ? a.sink[head] : -INFINITY;
+    // max over the pieces' lse and the sink
+    float mx = sink;
+    for (int q0 = 0; q0 < n; q0 += 64) {
+      const int q = q0 + lane;
+      float l = -INFINITY;
+      if (q < n && !part_empty(fp + q, total, pa.P)) {
+        const int slot = q == 0 ? first_slot : 2 * (fp + q);
+        l = pa.slots[slot * slot_floats + (size_t)a.M * 512 + m];
+      }
+      for (int o = 32; o > 0; o >>= 1) l = fmaxf(l, __shfl_xor(l, o, 64));
+      mx = fmaxf(mx, l);
+    }
+    uint16_t *dst = a.out + qrow * kDim + lane * 8;
+    if (mx == -INFINITY) {
+      *(u32x4 *)dst = u32x4{0u, 0u, 0u, 0u};
+      if (a.lse != nullptr && lane == 0) a.lse[qrow] = -INFINITY;
+      continue;
+    }
+    float z = exp2_fast((sink - mx) * kLog2e);
+    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < n; q0 += 64) {
+      const int ql = q0 + lane;
+      float wl = 0.f;
+      const bool held = ql < n && !part_empty(fp + ql, total, pa.P);
+      if (held) {
+        const int slot = ql == 0 ? first_slot : 2 * (fp + ql);
+        wl = exp2_fast((pa.slots[slot * slot_floats + (size_t)a.M * 512 + m] - mx) * kLog2e);
+      }
+      const uint64_t held_mask = __ballot(held);
+      const int cnt = min(64, n - q0);
+      for (int k = 0; k < cnt; ++k) {
+        if (!((held_mask >> k) & 1)) continue;  // an empty partition in the span
+        const float wq = __shfl(wl, k, 64);
+        const int q = q0 + k;
+        const int slot = q == 0 ? first_slot : 2 * (fp + q);
+        const float *src = pa.slots + slot * slot_floats + (size_t)m * kDim + lane * 8;
+        const f32x4 v0 = *(const f32x4 *)src;
+        const f32x4 v1 = *(const f32x4 *)(src + 4);
+        z += wq;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] += wq * v0[i];
+          o[4 + i] += wq * v1[i];
+        }
+      }
+    }
+    const float inv = 1.f / z;
+    u32x4 v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
+    *(u32x4 *)dst = v;
+    if (a.lse != nullptr && lane == 0) a.lse[qrow] = mx + logf(z);
+  }
+}
+
+template <int RB, bool FP8, bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void persistent_kernel(PersistArgs pa) {
+  constexpr int DS = 4 / RB;
+  constexpr int NC = 16 / DS, ND = 32 / DS;
+  constexpr int ROWS = 16 * RB;
+  __shared__ __attribute__((aligned(1024))) Smem<DS> sm;
+  __shared__ int s_red[4];
+  __shared__ int s_first[2];
+  __shared__ int s_last;
+  __shared__ uint32_t s_arrived;
+  const DecodeArgs &a = pa.d;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rb = wave % RB, ds = wave / RB;
+  const int j = lane & 15;
+  const int grp = lane >> 4;
+
+  // Workgroup -> (partition p, row group g); the G groups of a partition read
+  // the same KV rows and are spaced 8 apart to share one XCD's L2.
+  const int per = 8 * a.G;
+  const int g = (int)(blockIdx.x % per) / 8;
+  const int p = (int)(blockIdx.x / per) * 8 + (int)(blockIdx.x % 8);
+  if (p >= pa.P) return;
+  const int32_t *ptr = pa.kv_indptr;
+  const int B = pa.B;
+
+  // ---- the plan, from the live kv_indptr: total tiles, then this partition's
+  // tile range and its first and last sequence
+  int total;
+  {
+    int loc = 0;
+    for (int b = threadIdx.x; b < B; b += 256) loc += seq_tiles(ptr, b);
+    block_incl_scan(loc, s_red, total);
+  }
+  const int t0 = (int)((int64_t)p * total / pa.P);
+  const int t1 = (int)((int64_t)(p + 1) * total / pa.P);
+  if (threadIdx.x == 0) {
+    s_first[0] = -1;
+    s_first[1] = 0;
+    s_last = -1;
+  }
+  __syncthreads();
+  if (t0 < t1) {
+    int run = 0;
+    for (int base = 0; base < B; base += 256) {
+      const int b = base + (int)threadIdx.x;
+      const int tb = b < B ? seq_tiles(ptr, b) : 0;
+      int chunk;
+      const int st = run + block_incl_scan(tb, s_red, chunk) - tb;
+      if (tb > 0 && st <= t0 && t0 < st + tb) {
+        s_first[0] = b;
+        s_first[1] = st;
+      }
+      if (tb > 0 && st < t1 && t1 <= st + tb) s_last = b;
+      run += chunk;
+      if (run >= t1) break;  // the same in every thread
+    }
+  }
+  __syncthreads();
+  const int b_first = s_first[0], b_last = s_last;
+  if (g == 0 && threadIdx.x == 0) {
+    int32_t *d = pa.plan + 4 * p;
+    d[0] = t0;
+    d[1] = t1;
+    d[2] = b_first;
+    d[3] = b_last;
+  }
+  if (t0 >= t1) return;
+
+  int qk_base[4], pv_base[8];
+  lds_bases(j, grp, qk_base, pv_base);
+  const int dcol = 16 * (ds * ND) + 4 * grp;
+  const bool lse_lane = grp == 0 && ds == 0;
+  const int m = g * ROWS + rb * 16 + j;  // this lane's query row within a sequence
+  const int head = m % a.H;
+  const size_t slot_floats = (size_t)a.M * 513;
+
+  int start = s_first[1];  // first global tile of sequence b
+  for (int b = b_first; b <= b_last; ++b) {
+    const int k0 = ptr[b];
+    const int kb = max(ptr[b + 1] - k0, 0);
+    const int tb = (kb + kSplitAlign - 1) / kSplitAlign;
+    if (tb == 0) continue;
+    const int lo = max(t0, start), hi = min(t1, start + tb);
+    const int pos0 = (lo - start) * kSplitAlign;
+    const int pos1 = min((hi - start) * kSplitAlign, kb);
+    const int fp = tile_owner(start, total, pa.P);
+    const int lp = tile_owner(start + tb - 1, total, pa.P);
+
+    const int64_t qrow = (int64_t)(b * a.qps + m / a.H) * a.H + head;
+    bf16x8 qreg[NC];
+    load_q<DS>(a, qrow, ds, grp, qreg);
+    WaveState<ND> w;
+    attend_range<RB, FP8, PACKED, false>(a, sm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, ds, qreg,
+                                         qk_base, pv_base, w);
+    const float l_tot = row_total(w.l_run);
+    if (fp == lp) {
+      write_direct(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
+                   (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
+    } else {
+      const int slot = 2 * p + (b == b_first ? 0 : 1);
+      float *sb = pa.slots + slot * slot_floats;
+      write_partial(w, l_tot, sb + (size_t)m * kDim + dcol, lse_lane ? sb + (size_t)a.M * kDim + m : nullptr);
+      __threadfence();  // release this piece (agent scope: other XCDs read it)
+      __syncthreads();
+      uint32_t *ctr = pa.counters + (size_t)g * pa.P + fp;
+      if (threadIdx.x == 0) s_arrived = atomicAdd(ctr, 1u);
+      __syncthreads();
+      // pieces = non-empty partitions of the span: all of them when total >= P,
+      // otherwise every partition holds at most one tile, so one per tile
+      const int pieces = total >= pa.P ? lp - fp + 1 : tb;
+      if (s_arrived == (uint32_t)(pieces - 1)) {
+        __threadfence();  // acquire the other pieces
+        const int t0_fp = (int)((int64_t)fp * total / pa.P);
+        merge_pieces(pa, b, g, ROWS, fp, lp, 2 * fp + (start == t0_fp ? 0 : 1), total);
+        if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+      __syncthreads();  // s_arrived is rewritten by the next piece
+    }
+    start += tb;
+  }
+}
+
+template <int RB, bool FP8, bool PACKED>
+static hipError_t launch_persistent_t(const PersistArgs &a, hipStream_t stream) {
+  const int blocks8 = (a.P + 7) / 8;
+  const dim3 grid((unsigned)(blocks8 * 8 * a.d.G));
+  hipLaunchKernelGGL((persistent_kernel<RB, FP8, PACKED>), grid, dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int RB>
+static hipError_t launch_persistent_rb(const PersistArgs &a, bool fp8, hipStream_t stream) {
+  if (fp8) return launch_persistent_t<RB, true, false>(a, stream);
+  return a.d.packed ? launch_persistent_t<RB, false, true>(a, stream)
+                    : launch_persistent_t<RB, false, false>(a, stream);
+}
+
+hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream) {
+  switch (rb) {
+    case 1: return launch_persistent_rb<1>(a, fp8, stream);
+    case 2: return launch_persistent_rb<2>(a, fp8, stream);
+    case 4: return launch_persistent_rb<4>(a, fp8, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace smd

@@ -49,4 +49,26 @@ hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows
                         int32_t S, const float *sink, uint16_t *out, float *lse,
                         hipStream_t stream);
 
+// Arguments of the persistent kernel.  The decode fields carry the queries,
+// pool, sink, scale, H, qps, M, G, out and lse (indices, chunk, S and the
+// partial pointers are unused).
+struct PersistArgs {
+  DecodeArgs d;
+  const int32_t *kv_indptr;   // [B + 1], non-decreasing; kv_indptr[0] may be > 0
+  const int32_t *kv_indices;  // flat index array
+  int32_t B;                  // sequences
+  int32_t P;                  // partitions
+  int32_t *plan;              // [P][4]: t0, t1, first and last sequence
+  uint32_t *counters;         // [M / 16][P] arrival counters (row group g, first partition)
+  float *slots;               // [2P][M * 513]: per slot o [M][512] then lse [M]
+};
+
+// Workspace layout of the persistent kernel (byte offsets, 256-byte aligned).
+struct PersistLayout {
+  size_t plan_off, ctr_off, slot_off, total;
+};
+PersistLayout persist_layout(int64_t M, int64_t P);
+
+hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream);
+
 }  // namespace smd

@@ -190,3 +190,78 @@ def test_empty_problems_launch_nothing():
 ])
 def test_merge_rejects(args, code):
     assert smd.lib().smd_merge_partials(*args, None) == code
+
+
+# ----------------------------------------------------------------------------
+# persistent entry points: sizing, defaults and host validation
+# ----------------------------------------------------------------------------
+def _up256(x):
+    return -(-x // 256) * 256
+
+
+@pytest.mark.parametrize("H,qps,P", [(128, 4, 32), (16, 1, 256), (64, 2, 7), (32, 8, 1), (128, 1, 16384)])
+def test_persistent_workspace_bytes(H, qps, P):
+    # plan 16 B per partition, counters 4 B per (16-row group, partition), then
+    # 2P slots of M x 513 fp32; each region starts 256-byte aligned
+    M = H * qps
+    want = _up256(16 * P) + _up256(4 * (M // 16) * P) + 2 * P * M * 513 * 4
+    assert smd.persistent_workspace_bytes(H, qps, P) == want
+
+
+def test_persistent_default_partitions_vs_oracle():
+    for H in (16, 32, 64, 128):
+        for qps in range(1, 9):
+            for cus in (0, 80, 256, 304):
+                want = plan_ref.default_partitions(H, qps, num_cus=cus or 256)
+                assert smd.persistent_default_partitions(H, qps, cus) == want
+
+
+@pytest.mark.parametrize("args", [(17, 1, 4), (128, 0, 4), (128, 9, 4), (128, 1, 0), (128, 1, 16385)])
+def test_persistent_workspace_bytes_rejects(args):
+    with pytest.raises(smd.SmdError):
+        smd.persistent_workspace_bytes(*args)
+
+
+def _persist(pool=None, **kw):
+    a = dict(q_nope=0x20000, q_rope=0x30000, B=4, qps=1, H=64, ptr=0x40000, flat=0x48000, sink=None, scale=0.04,
+             ws=0x100000, ws_bytes=1 << 30, P=8, out=0x50000, lse=0x60000)
+    a.update(kw)
+    p = pool if pool is not None else _pool()
+    rc = smd.lib().smd_sparse_mla_decode_persistent(a["q_nope"], a["q_rope"], a["B"], a["qps"], a["H"],
+                                                    ctypes.byref(p), a["ptr"], a["flat"], a["sink"], a["scale"],
+                                                    a["ws"], a["ws_bytes"], a["P"], a["out"], a["lse"], None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(B=-1), -1, "negative"),
+    (dict(H=48), -2, "num_heads"),
+    (dict(qps=9), -2, "q_per_seq"),
+    (dict(P=0), -1, "num_partitions"),
+    (dict(P=16385), -1, "num_partitions"),
+    (dict(scale=float("nan")), -1, "softmax_scale"),
+    (dict(ws=None), -3, "workspace"),
+    (dict(ws=0x100010), -3, "256-byte"),
+    (dict(ws_bytes=1000), -3, "below"),
+    (dict(ptr=None), -1, "required"),
+    (dict(flat=None), -1, "required"),
+    (dict(out=None), -1, "required"),
+    (dict(out=0x50008), -1, "aligned"),
+    (dict(ptr=0x40002), -1, "4-byte"),
+])
+def test_persistent_rejects(kw, code, msg):
+    rc, err = _persist(**kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_persistent_rejects_bad_pool():
+    rc, err = _persist(pool=_pool(dtype=1, nope_stride=448, rope_stride=64))
+    assert rc == -1 and "scale" in err
+
+
+def test_persistent_empty_batch_launches_nothing():
+    assert _persist(B=0)[0] == 0
+
+
+def test_persistent_workspace_reset_rejects_null():
+    assert smd.lib().smd_persistent_workspace_reset(None, 100, None) == -1
