@@ -1,18 +1,21 @@
 #!/usr/bin/env python3
 """Benchmark of sparse MLA decode on one MI355X.
 
-A step is one pass of the whole hot path over one batch: the host split
-planner, the split-KV decode kernel and (for more than one split) the stage-2
-merge kernel.  The default workload is the bf16 decode of T=8 tokens x 64
-heads, 2048 top-k + 128 sliding-window indices (1% invalid) into a
-32768-row pool.  Inputs are seeded synthetic data resident in HBM before the
-timed region; the K timed steps are captured into one HIP graph and replayed
-once, bracketed by device synchronisation.
+A step is one pass of the whole hot path over one batch.  For dense index
+lists that is the host split planner, the split-KV decode kernel and (for more
+than one split) the stage-2 merge kernel; for the ragged workload it is one
+launch of the persistent kernel (in-kernel plan, decode, last-arriving merge).
+The default workload is the bf16 decode of T=8 tokens x 64 heads, 2048 top-k +
+128 sliding-window indices (1% invalid) into a 32768-row pool.  Inputs are
+seeded synthetic data resident in HBM before the timed region; the K timed
+steps are captured into one HIP graph and replayed once, bracketed by device
+synchronisation.
 
-The `roofline` object reports the decode kernel alone: algorithmic bytes per
-launch over its average duration, measured with HIP events on the stream it
-runs on (a graph of back-to-back decode launches).  `cpu_baseline` times the
-float64 oracle on the host on a bounded sample of the same workload.
+The `roofline` object reports the dominant kernel alone (the decode kernel, or
+the persistent kernel): algorithmic bytes (or flops) per launch over its
+average duration, measured with HIP events on the stream it runs on (a graph
+of back-to-back launches).  `cpu_baseline` times the float64 oracle on the
+host on a bounded sample of the same workload.
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
 """
@@ -30,7 +33,7 @@ sys.path.insert(0, ROOT)
 import numpy as np  # noqa: E402
 
 METRIC = "sparse-MLA decode µs/call + achieved HBM GB/s (% roofline), T x ctx matrix"
-HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
 
 
@@ -39,12 +42,16 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=1, help="workload index 0..4 (1 = bf16 T=8 H=64 K=2176)")
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload 0..4 (1 = bf16 T=8 H=64 K=2176; 4 = ragged MTP4 fp8, persistent kernel)")
     ap.add_argument("--cell", type=str, default=None, help="T x ctx matrix cell T:ctx:variant instead of --config")
     ap.add_argument("--splits", type=int, default=None, help="override the planner's split count")
+    ap.add_argument("--partitions", type=int, default=None, help="persistent kernel: override the partition count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--kernel-launches", type=int, default=50)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -69,34 +76,73 @@ def to_device(w, dev):
     else:
         pool = smd.KVPool.fp8(torch.from_numpy(a["nope"]).to(dev), torch.from_numpy(a["scale"]).to(dev),
                               bf(a["rope"]))
-    return dict(q_nope=bf(a["q_nope"]), q_rope=bf(a["q_rope"]), pool=pool,
-                indices=torch.from_numpy(a["indices"]).to(dev), sink=torch.from_numpy(a["sink"]).to(dev))
+    d = dict(q_nope=bf(a["q_nope"]), q_rope=bf(a["q_rope"]), pool=pool, sink=torch.from_numpy(a["sink"]).to(dev))
+    if w.ragged:
+        d["kv_indptr"] = torch.from_numpy(a["kv_indptr"]).to(dev)
+        d["kv_indices"] = torch.from_numpy(a["kv_indices"]).to(dev)
+    else:
+        d["indices"] = torch.from_numpy(a["indices"]).to(dev)
+    return d
 
 
 def cpu_baseline(w, target_s: float):
-    """Time the float64 oracle on index rows of the same workload until about
-    target_s seconds of CPU work; scale to a whole call."""
+    """Time the float64 oracle on index rows (sequences) of the same workload
+    until about target_s seconds of CPU work; scale to a whole call by the
+    share of gathered rows the sample covered."""
     from oracle import ref
     a = w.arrays
     pool = {"kv": a["kv"]} if w.kv_dtype == "bf16" else {"nope": a["nope"], "scale": a["scale"], "rope": a["rope"]}
-    R = w.num_index_rows
     qps = w.q_per_seq
-    done, t_used = 0, 0.0
+    if w.ragged:
+        ptr = a["kv_indptr"]
+        rows = [b for b in range(len(ptr) - 1) if ptr[b + 1] > ptr[b]]
+        lens = {b: int(ptr[b + 1] - ptr[b]) for b in rows}
+    else:
+        rows = list(range(w.num_index_rows))
+        lens = {b: a["indices"].shape[1] for b in rows}
+    total_len = sum(lens.values())
+    done, covered, t_used = 0, 0, 0.0
     t0 = time.perf_counter()
     while t_used < target_s and done < 100000:
-        b = done % R
-        ref.sparse_mla_decode(a["q_nope"][b * qps:(b + 1) * qps], a["q_rope"][b * qps:(b + 1) * qps], pool,
-                              a["indices"][b:b + 1], a["sink"], w.softmax_scale, qps)
+        b = rows[done % len(rows)]
+        qn, qr = a["q_nope"][b * qps:(b + 1) * qps], a["q_rope"][b * qps:(b + 1) * qps]
+        if w.ragged:
+            ref.sparse_mla_decode_ragged(qn, qr, pool, np.array([0, lens[b]]), a["kv_indices"][ptr[b]:ptr[b + 1]],
+                                         a["sink"], w.softmax_scale, qps)
+        else:
+            ref.sparse_mla_decode(qn, qr, pool, a["indices"][b:b + 1], a["sink"], w.softmax_scale, qps)
         done += 1
+        covered += lens[b]
         t_used = time.perf_counter() - t0
-    per_row = t_used / done
-    per_call = per_row * R
+    per_call = t_used * total_len / covered
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:
         cores = 1
-    return per_call, done, t_used, cores
+    what = "sequences" if w.ragged else "index rows"
+    sample = (f"{done} {what} of the same workload, cycled ({covered} gathered positions in {t_used:.1f} s; "
+              f"one call gathers {total_len}), scaled to one call by gathered positions")
+    return per_call, sample, cores
+
+
+def graph_time(torch, stream, fn, n):
+    """Average µs of fn() over n back-to-back launches captured in one graph,
+    timed with events recorded on the stream the graph replays on."""
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(n):
+            fn()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        g.replay()
+        e0.record(stream)
+        g.replay()
+        e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
 
 
 def main():
@@ -113,71 +159,91 @@ def main():
     w = make_workload(args)
     d = to_device(w, dev)
     T, H, qps = w.num_tokens, w.num_heads, w.q_per_seq
-    K = w.arrays["indices"].shape[1]
     kvd = smd.KV_BF16 if w.kv_dtype == "bf16" else smd.KV_FP8_E4M3_UE8M0
-    R = w.num_index_rows
-
-    def plan():
-        return args.splits or smd.plan_num_kv_splits(R, H, K, qps, kvd)
-
-    s = plan()
     out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    po = torch.empty((T, H, s, 512), dtype=torch.float32, device=dev)
-    pl = torch.empty((T, H, s), dtype=torch.float32, device=dev)
-
-    def step(num_splits):
-        smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
-                              num_splits=num_splits, q_per_seq=qps, out=out, lse=lse,
-                              partial_o=po if num_splits > 1 else None, partial_lse=pl if num_splits > 1 else None)
-
     stream = torch.cuda.Stream()
+    cfg = {"workload": w.name, "num_tokens": T, "num_heads": H, "q_per_seq": qps, "pool_rows": w.pool_rows,
+           "kv_dtype": w.kv_dtype, "parallelism": "1 gpu"}
+
+    if w.ragged:
+        P = args.partitions or smd.persistent_default_partitions(H, qps)
+        ws = smd.PersistentWorkspace(H, qps, P, device=dev)
+        torch.cuda.synchronize()
+
+        def step():
+            smd.sparse_mla_decode_persistent(d["q_nope"], d["q_rope"], d["pool"], d["kv_indptr"], d["kv_indices"],
+                                             d["sink"], w.softmax_scale, q_per_seq=qps, workspace=ws, out=out,
+                                             lse=lse)
+
+        plan = None
+        kernel_step = step
+        kernel_name = "smd::persistent_kernel"
+        cfg.update({"num_seqs": T // qps, "sum_k": int(w.arrays["kv_indptr"][-1] - w.arrays["kv_indptr"][0]),
+                    "num_partitions": P, "kernel": "persistent"})
+    else:
+        K = w.arrays["indices"].shape[1]
+        R = w.num_index_rows
+
+        def plan():
+            return args.splits or smd.plan_num_kv_splits(R, H, K, qps, kvd)
+
+        s = plan()
+        po = torch.empty((T, H, s, 512), dtype=torch.float32, device=dev)
+        pl = torch.empty((T, H, s), dtype=torch.float32, device=dev)
+
+        def step():
+            smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
+                                  num_splits=s, q_per_seq=qps, out=out, lse=lse,
+                                  partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
+
+        def kernel_step():  # the decode kernel alone (partials when split)
+            if s > 1:
+                smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
+                                      num_splits=s, q_per_seq=qps, partials_only=True, partial_o=po,
+                                      partial_lse=pl)
+            else:
+                step()
+
+        kernel_name = "smd::decode_kernel"
+        cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv"})
+
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
-            step(plan())
+            if plan is not None:
+                plan()
+            step()
     torch.cuda.synchronize()
 
-    # K whole-path steps captured into one graph (planner runs on the host per step)
+    # K whole-path steps captured into one graph (the host planner runs per step)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
         for _ in range(args.steps):
-            step(s)
+            step()
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         g.replay()  # one untimed replay of the captured graph
     torch.cuda.synchronize()
 
     t0 = time.perf_counter()
-    for _ in range(args.steps):
-        s_k = plan()
-    assert s_k == s
+    if plan is not None:
+        for _ in range(args.steps):
+            assert plan() == cfg["num_splits"]
     with torch.cuda.stream(stream):
         g.replay()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # decode kernel alone: back-to-back launches in a graph, HIP events on its stream
-    nk = args.kernel_launches
-    gk = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(gk, stream=stream):
-        for _ in range(nk):
-            if s > 1:
-                smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"],
-                                      w.softmax_scale, num_splits=s, q_per_seq=qps, partials_only=True,
-                                      partial_o=po, partial_lse=pl)
-            else:
-                step(1)
-    torch.cuda.synchronize()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
-    with torch.cuda.stream(stream):
-        gk.replay()
-        e0.record(stream)
-        gk.replay()
-        e1.record(stream)
-    torch.cuda.synchronize()
-    kern_us = e0.elapsed_time(e1) * 1e3 / nk
+    kern_us = graph_time(torch, stream, kernel_step, args.kernel_launches)
+
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+        torch.cuda.synchronize()
 
     alg_bytes = wl.algorithmic_bytes(w)
     alg_flops = wl.algorithmic_flops(w)
@@ -187,15 +253,15 @@ def main():
     kern_tfs = alg_flops / (kern_us * 1e6)
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e3)
     t_mfma = alg_flops / (BF16_MFMA_PEAK_TFS * 1e6)
-    bound = "hbm" if t_hbm >= t_mfma else "mfma"
-    if bound == "hbm":
+    if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None}
     else:
         roof = {"bound": "mfma", "achieved": round(kern_tfs, 1), "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
-    roof.update({"kernel": "smd::decode_kernel", "kernel_us": round(kern_us, 3),
-                 "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops})
+    roof.update({"kernel": kernel_name, "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": alg_bytes,
+                 "alg_flops_per_launch": alg_flops, "hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                 "mfma_frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4)})
 
     res = {
         "metric": METRIC,
@@ -212,16 +278,13 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3/ue8m0 in, bf16 mfma",
         "data": "synthetic",
-        "config": {"workload": w.name, "num_tokens": T, "num_heads": H, "q_per_seq": qps, "topk": K,
-                   "pool_rows": w.pool_rows, "kv_dtype": w.kv_dtype, "num_splits": s, "parallelism": "1 gpu"},
+        "config": cfg,
         "roofline": roof,
     }
     if not args.no_cpu_baseline:
-        per_call, rows, secs, cores = cpu_baseline(w, args.cpu_seconds)
+        per_call, sample, cores = cpu_baseline(w, args.cpu_seconds)
         res["cpu_baseline"] = {"value": round(alg_bytes / (per_call * 1e9), 4), "unit": "GB/s", "cores": cores,
-                               "kind": "oracle", "us_per_call": round(per_call * 1e6, 1),
-                               "sample": f"{rows} index rows of the same workload ({secs:.1f} s), "
-                                         f"scaled to one call of {R} rows"}
+                               "kind": "oracle", "us_per_call": round(per_call * 1e6, 1), "sample": sample}
     print(json.dumps(res), flush=True)
 
 
