@@ -14,7 +14,8 @@ synchronisation.
 The `roofline` object reports the dominant kernel alone (the decode kernel, or
 the persistent kernel): algorithmic bytes (or flops) per launch over its
 average duration, measured with HIP events on the stream it runs on (a graph
-of back-to-back launches).  `cpu_baseline` times the float64 oracle on the
+of back-to-back launches; for a split plan, decode + merge launches minus the
+merge launches timed alone).  `cpu_baseline` times the float64 oracle on the
 host on a bounded sample of the same workload.
 
 Prints one JSON line.  --gpus above 1 is refused: this build runs on one GPU.
@@ -197,13 +198,10 @@ def main():
                                   num_splits=s, q_per_seq=qps, out=out, lse=lse,
                                   partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
 
-        def kernel_step():  # the decode kernel alone (partials when split)
-            if s > 1:
-                smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
-                                      num_splits=s, q_per_seq=qps, partials_only=True, partial_o=po,
-                                      partial_lse=pl)
-            else:
-                step()
+        kernel_step = step  # decode (+ merge when split; its time is subtracted below)
+
+        def merge_only():
+            smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
         kernel_name = "smd::decode_kernel"
         cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv"})
@@ -236,6 +234,11 @@ def main():
     ms_per_step = wall * 1e3 / args.steps
 
     kern_us = graph_time(torch, stream, kernel_step, args.kernel_launches)
+    merge_us = 0.0
+    if not w.ragged and cfg["num_splits"] > 1:
+        # the decode kernel as the step launches it = (decode + merge) - merge alone
+        merge_us = graph_time(torch, stream, merge_only, args.kernel_launches)
+        kern_us -= merge_us
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -259,7 +262,8 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(kern_tfs, 1), "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
-    roof.update({"kernel": kernel_name, "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": alg_bytes,
+    roof.update({"kernel": kernel_name, "kernel_us": round(kern_us, 3), "merge_us": round(merge_us, 3),
+                 "alg_bytes_per_launch": alg_bytes,
                  "alg_flops_per_launch": alg_flops, "hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4)})
 

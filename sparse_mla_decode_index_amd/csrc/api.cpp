@@ -193,6 +193,7 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
   a.part_lse = need_partials ? partial_lse : nullptr;
   a.out = need_partials ? nullptr : (uint16_t *)out;
   a.lse = need_partials ? nullptr : lse;
+  a.hilo = out == nullptr;  // FP32 partials are the result only without out
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = launch_decode(a, rb, kv->dtype == SMD_KV_FP8_E4M3_UE8M0, st);
   if (e != hipSuccess) {

@@ -128,11 +128,11 @@ static hipError_t launch_decode_p(const DecodeArgs &a, int rb, bool fp8, hipStre
   }
 }
 
-// Partials are written with the two-part P (FP32-partial precision); the
-// direct bf16 output uses a single bf16 P.
+// Partials the caller reads are written with the two-part P (FP32-partial
+// precision); partials that only feed the merge into bf16, and the direct
+// bf16 output, use a single bf16 P.
 hipError_t launch_decode(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream) {
-  return a.out != nullptr ? launch_decode_p<false>(a, rb, fp8, stream)
-                          : launch_decode_p<true>(a, rb, fp8, stream);
+  return a.hilo ? launch_decode_p<true>(a, rb, fp8, stream) : launch_decode_p<false>(a, rb, fp8, stream);
 }
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,

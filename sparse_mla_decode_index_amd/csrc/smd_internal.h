@@ -39,6 +39,7 @@ struct DecodeArgs {
   float *part_lse;         // [T, H, S] or null
   uint16_t *out;           // bf16 [T, H, 512] (direct output when S == 1)
   float *lse;              // [T, H] or null
+  int32_t hilo;            // partials are returned to the caller: carry p as bf16 hi + lo
 };
 
 // Launch the split-KV decode with rb query-row blocks of 16 per workgroup
