@@ -5,27 +5,25 @@
 // an index row covers a contiguous range of its positions and writes an FP32
 // partial (o_r, lse_r); the merge reweights the partials by their log-sum-exps
 // and folds in the sink.  One split writes the bf16 output directly.
-#include "decode_core.h"
+#include "ks_core.h"
 
 namespace smd {
 
-// Work decomposition: a workgroup (4 waves) owns one index row b, one group g
-// of 16*RB query rows and one split r.
-template <int RB, bool FP8, bool PACKED, bool P_HILO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2 : 1, RB == 1 ? 2 : 1))) void decode_kernel(DecodeArgs a) {
-  constexpr int DS = 4 / RB;
-  constexpr int NC = 16 / DS, ND = 32 / DS;
-  __shared__ __attribute__((aligned(1024))) Smem<DS> sm;
+using namespace ks;
+
+// Work decomposition: a workgroup (4 waves) owns one index row b, one block g
+// of 16 query rows and one split r; its waves share the split's positions
+// (interleaved half-tiles of 16) and merge their states at the end.
+template <bool PACKED, bool P_HILO>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) ks::Smem sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-  const int rb = wave % RB, ds = wave / RB;
-  const int j = lane & 15;   // query row within the wave's block / column
-  const int grp = lane >> 4; // 16-lane group
 
-  // Workgroup -> (work unit u = b*S + r, row group g).  The G row groups of a
-  // unit read the same KV rows; consecutive workgroups land on consecutive
-  // XCDs, so the groups of one unit are spaced 8 apart to share one XCD's L2.
+  // Workgroup -> (work unit u = b*S + r, row block g).  The G blocks of a unit
+  // read the same KV rows; consecutive workgroups land on consecutive XCDs,
+  // so the blocks of one unit are spaced 8 apart to share one XCD's L2.
   const int per = 8 * a.G;
   const int g = (int)(blockIdx.x % per) / 8;
   const int u = (int)(blockIdx.x / per) * 8 + (int)(blockIdx.x % 8);
@@ -36,29 +34,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(RB == 1 ? 2
   const int p1 = min(p0 + a.chunk, a.topk);
   const int32_t *row_idx = a.indices + (int64_t)b * a.indices_stride;
 
+  const ks::Lane L = ks::make_lane(lane);
   // This lane's query row m -> (token, head).
-  const int m = g * (RB * 16) + rb * 16 + j;
+  const int m = g * 16 + L.j;
   const int tok = b * a.qps + m / a.H;
   const int head = m % a.H;
   const int64_t qrow = (int64_t)tok * a.H + head;  // [T, H] row
 
-  bf16x8 qreg[NC];
-  load_q<DS>(a, qrow, ds, grp, qreg);
-  int qk_base[4], pv_base[8];
-  lds_bases(j, grp, qk_base, pv_base);
+  ks::bf16x8 qreg[16];
+  ks::load_q(a, qrow, L.q, qreg);
+  ks::State st;
+  uint8_t SMD_LDS *wbuf = (uint8_t SMD_LDS *)&sm.buf[wave][0];
+  ks::attend<PACKED, P_HILO>(a, row_idx, p0, p1, wave, L, qreg, wbuf, st);
 
-  WaveState<ND> w;
-  attend_range<RB, FP8, PACKED, P_HILO>(a, sm, row_idx, p0, p1, wave, lane, grp, ds, qreg, qk_base, pv_base, w);
-
-  const float l_tot = row_total(w.l_run);
-  const int dcol = 16 * (ds * ND) + 4 * grp;
-  const bool lse_lane = grp == 0 && ds == 0;
+  ks::f32x4 o[8];
+  float mm, ll;
+  ks::merge_waves(sm, wave, L, st, o, mm, ll);
+  const int dcol = 128 * wave + 4 * L.g;
+  const bool lse_lane = L.g == 0 && wave == 0;
   if (a.S == 1 && a.out != nullptr) {
-    write_direct(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
-                 (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
+    ks::write_direct(o, mm, ll, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
+                     (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
   } else {
-    write_partial(w, l_tot, a.part_o + (qrow * a.S + r) * kDim + dcol,
-                  lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
+    ks::write_partial(o, mm, ll, a.part_o + (qrow * a.S + r) * kDim + dcol,
+                      lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
   }
 }
 
@@ -103,36 +102,22 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   if (lse && lane == 0) lse[row] = mx + logf(z);
 }
 
-template <int RB, bool FP8, bool PACKED, bool P_HILO>
+template <bool PACKED, bool P_HILO>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_kernel<RB, FP8, PACKED, P_HILO>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<PACKED, P_HILO>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int RB, bool P_HILO>
-static hipError_t launch_decode_rb(const DecodeArgs &a, bool fp8, hipStream_t stream) {
-  if (fp8) return launch_decode_t<RB, true, false, P_HILO>(a, stream);
-  return a.packed ? launch_decode_t<RB, false, true, P_HILO>(a, stream)
-                  : launch_decode_t<RB, false, false, P_HILO>(a, stream);
-}
-
-template <bool P_HILO>
-static hipError_t launch_decode_p(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream) {
-  switch (rb) {
-    case 1: return launch_decode_rb<1, P_HILO>(a, fp8, stream);
-    case 2: return launch_decode_rb<2, P_HILO>(a, fp8, stream);
-    case 4: return launch_decode_rb<4, P_HILO>(a, fp8, stream);
-    default: return hipErrorInvalidValue;
-  }
-}
-
-// Partials the caller reads are written with the two-part P (FP32-partial
-// precision); partials that only feed the merge into bf16, and the direct
-// bf16 output, use a single bf16 P.
-hipError_t launch_decode(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream) {
-  return a.hilo ? launch_decode_p<true>(a, rb, fp8, stream) : launch_decode_p<false>(a, rb, fp8, stream);
+// bf16 pools (fp8 pools go to launch_decode_rb).  Partials the caller reads
+// are written with the two-part P (FP32-partial precision); partials that only
+// feed the merge into bf16, and the direct bf16 output, use a single bf16 P.
+// a.G must be M / 16.
+hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream) {
+  if (fp8) return hipErrorInvalidValue;
+  if (a.hilo) return a.packed ? launch_decode_t<true, true>(a, stream) : launch_decode_t<false, true>(a, stream);
+  return a.packed ? launch_decode_t<true, false>(a, stream) : launch_decode_t<false, false>(a, stream);
 }
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
