@@ -5,18 +5,18 @@
 // an index row covers a contiguous range of its positions and writes an FP32
 // partial (o_r, lse_r); the merge reweights the partials by their log-sum-exps
 // and folds in the sink.  One split writes the bf16 output directly.
-#include "ks_core.h"
+#include "ks8_core.h"
 
 namespace smd {
 
 using namespace ks;
 
-// Work decomposition: a workgroup (4 waves) owns one index row b, one block g
-// of 16 query rows and one split r; its waves share the split's positions
-// (interleaved half-tiles of 16) and merge their states at the end.
+// Work decomposition: a workgroup (8 waves, two per SIMD) owns one index row
+// b, one block g of 16 query rows and one split r; its waves share the split's
+// positions (interleaved half-tiles of 16) and merge their states at the end.
 template <bool PACKED, bool P_HILO>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_kernel(DecodeArgs a) {
-  __shared__ __attribute__((aligned(1024))) ks::Smem sm;
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) ks8::Smem sm;
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
@@ -41,15 +41,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int head = m % a.H;
   const int64_t qrow = (int64_t)tok * a.H + head;  // [T, H] row
 
-  ks::bf16x8 qreg[16];
-  ks::load_q(a, qrow, L.q, qreg);
+  ks8::stage_q(a, qrow, wave, L, sm);
+  __syncthreads();
   ks::State st;
-  uint8_t SMD_LDS *wbuf = (uint8_t SMD_LDS *)&sm.buf[wave][0];
-  ks::attend<PACKED, P_HILO>(a, row_idx, p0, p1, wave, L, qreg, wbuf, st);
-
+  ks8::attend<PACKED, P_HILO>(a, row_idx, p0, p1, wave, L, (const uint8_t SMD_LDS *)&sm.q[0],
+                              (uint8_t SMD_LDS *)&sm.buf[wave][0], st);
   ks::f32x4 o[8];
   float mm, ll;
-  ks::merge_waves(sm, wave, L, st, o, mm, ll);
+  if (!ks8::merge_waves(sm, wave, L, st, o, mm, ll)) return;
   const int dcol = 128 * wave + 4 * L.g;
   const bool lse_lane = L.g == 0 && wave == 0;
   if (a.S == 1 && a.out != nullptr) {
@@ -106,7 +105,7 @@ template <bool PACKED, bool P_HILO>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_kernel<PACKED, P_HILO>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<PACKED, P_HILO>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,240 @@
+// Device core of the wave-independent sparse MLA decode (bf16 pools).
+//
+// A workgroup of 8 waves owns one block of 16 query rows (heads x MTP
+// positions sharing one index list) and a range of index positions, cut into
+// half-tiles of 16 positions; wave w takes half-tiles w, w+8, w+16, ... and
+// computes all 512 dims of the 16 query rows, so the main loop needs no
+// barrier: the waves only meet at the end, where their (O, m, l) states are
+// merged through LDS.  It is laid out for two waves per SIMD, so that one
+// wave's memory and LDS waits overlap the other's issue:
+//   - Q^T sits once in LDS (16 KiB, shared by the 8 waves) instead of in
+//     every wave's VGPRs; QK reads its B operand from there;
+//   - one gathered register set per wave: the rows of half-tile k+1 are in
+//     flight while half-tile k is computed;
+//   - one 16 KiB LDS buffer per wave; PV runs per half-tile with
+//     v_mfma_f32_16x16x16_bf16 (k = 16 rows), V^T by ds_read_b64_tr_b16.
+// LDS: 16 KiB + 8 x 16 KiB = 144 KiB per workgroup.
+#pragma once
+
+#include "ks_core.h"
+
+namespace smd {
+namespace ks8 {
+
+using ks::bf16x4;
+using ks::bf16x8;
+using ks::f32x4;
+using ks::Half;
+using ks::Lane;
+using ks::State;
+using ks::u32x2;
+using ks::u32x4;
+
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 8;
+constexpr int kHalf = ks::kHalf;
+constexpr int kHalfBytes = ks::kHalfBytes;
+
+struct Smem {
+  uint8_t q[16 * 64 * 16];         // Q^T: 16 B per (k-step, lane)
+  uint8_t buf[kWaves][kHalfBytes];  // one half-tile buffer per wave
+  float stat_m[4][16];
+  float stat_l[4][16];
+};
+
+// Q^T of the block into LDS: B operand of k-step ks for lane l = dims
+// 32ks + 8(l/16) .. +8 of query row l % 16.  Each wave stores two k-steps.
+__device__ __forceinline__ void stage_q(const DecodeArgs &a, int64_t qrow, int wave, const Lane &L, Smem &sm) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int ks = 2 * wave + h;
+    const uint16_t *src = ks < 14 ? a.q_nope + qrow * kNope + 32 * ks + 8 * L.q
+                                  : a.q_rope + qrow * kRope + 32 * (ks - 14) + 8 * L.q;
+    *(u32x4 SMD_LDS *)((uint8_t SMD_LDS *)sm.q + (ks * 64 + L.lane) * 16) = *(const u32x4 *)src;
+  }
+}
+
+// Gathered rows of a half-tile into the wave's buffer: row i, chunk `lane`
+// -> physical chunk lane ^ swz(i) (one row of 64 distinct chunks per store).
+__device__ __forceinline__ void store_half(const Half &h, uint8_t SMD_LDS *buf, const Lane &L) {
+#pragma unroll
+  for (int i = 0; i < 16; ++i) *(u32x4 SMD_LDS *)(buf + i * ks::kRowBytes + ((L.lane ^ ks::swz(i)) << 4)) = h.v[i];
+}
+
+// QK over the half-tile in `buf`: A operands from the buffer, B operands from
+// the shared Q^T.
+__device__ __forceinline__ f32x4 qk_lds(const uint8_t SMD_LDS *qs, const uint8_t SMD_LDS *buf, const Lane &L) {
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  constexpr int kPre = 2;
+  bf16x8 ka[kPre], kb[kPre];
+  auto load = [&](int ks) {
+    ka[ks % kPre] = *(const bf16x8 SMD_LDS *)(buf + L.wb[ks & 3] + 256 * (ks >> 2));
+    kb[ks % kPre] = *(const bf16x8 SMD_LDS *)(qs + (ks * 64 + L.lane) * 16);
+  };
+#pragma unroll
+  for (int ks = 0; ks < kPre; ++ks) load(ks);
+#pragma unroll
+  for (int ks = 0; ks < 16; ++ks) {
+    const bf16x8 k = ka[ks % kPre], q = kb[ks % kPre];
+    if (ks + kPre < 16) load(ks + kPre);
+    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, q, s, 0, 0, 0);
+  }
+  return s;
+}
+
+// PV over one half-tile (after the half-tile's softmax): O^T[512 x 16] += V^T[512 x 16] . P^T[16 x 16]; lane
+// (j, g) supplies P of kv rows 4g..4g+3 for query row j, the transposed read
+// gives dim 16d + (lane % 16) of rows 4g..4g+3.
+template <bool P_HILO>
+__device__ __forceinline__ void pv_half(const uint8_t SMD_LDS *buf, bf16x4 p, bf16x4 pl, const Lane &L, State &st) {
+  const s16x4 pb = __builtin_bit_cast(s16x4, p);
+  s16x4 plb;
+  if constexpr (P_HILO) plb = __builtin_bit_cast(s16x4, pl);
+  constexpr int kPre = 4;
+  bf16x4 v[kPre];
+  auto load = [&](int d) {
+    v[d % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(buf + L.pv[d & 7] + 256 * (d >> 3)));
+  };
+#pragma unroll
+  for (int d = 0; d < kPre; ++d) load(d);
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const s16x4 va = __builtin_bit_cast(s16x4, v[d % kPre]);
+    if (d + kPre < 32) load(d + kPre);
+    st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, pb, st.acc[d], 0, 0, 0);
+    if constexpr (P_HILO) st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(va, plb, st.acc[d], 0, 0, 0);
+  }
+}
+
+// One wave's sweep over its half-tiles of [p0, p1) (half-tile k of this wave
+// covers positions p0 + 16*(wave + 8k) + 0..15).  Per half-tile k: store the
+// gathered rows of k, refill the register set with the rows of k+1 (whose
+// indices were loaded one step earlier), load the indices of k+2, then QK,
+// softmax and PV of k from LDS while k+1 is in flight.  Every step issues the
+// same loads (positions past p1 read the zero row), so the compiler's wait
+// counts stay exact.
+template <bool PACKED, bool P_HILO, int PASS>
+__device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
+                                      const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st) {
+  const int nh = (p1 - p0 + kHalf - 1) / kHalf;
+  const int nk = nh > wave ? (nh - wave + kWaves - 1) / kWaves : 0;
+  if (nk == 0) return;
+  auto pos_of = [&](int k) { return p0 + kHalf * (wave + kWaves * k) + L.r; };
+  auto load_idx = [&](int k) { return row_idx[min(pos_of(k), p1 - 1)]; };
+  auto valid_of = [&](int k, int32_t idx) { return pos_of(k) < p1 && (uint32_t)idx < a.num_rows32; };
+
+  Half h;
+  const int32_t i0 = load_idx(0);
+  int32_t i_next = load_idx(1);
+  const bool v0 = valid_of(0, i0);
+  ks::issue_half<PACKED>(a, (uint32_t)i0, v0, L, h);
+  uint32_t vb_cur = (uint32_t)__ballot(v0) & 0xffffu;
+  for (int k = 0; k < nk; ++k) {
+    // store the rows of k, refill the registers with the rows of k+1 (their
+    // indices were loaded one step earlier), load the indices of k+2, then
+    // compute k from LDS while k+1 is in flight
+    store_half(h, buf, L);
+    const bool vn = valid_of(k + 1, i_next);
+    ks::issue_half<PACKED>(a, (uint32_t)i_next, vn, L, h);
+    i_next = load_idx(k + 2);
+    const uint32_t vb = vb_cur;
+    vb_cur = (uint32_t)__ballot(vn) & 0xffffu;
+    const f32x4 s = qk_lds(qs, buf, L);
+    bf16x4 p, pl;
+    ks::softmax_half<PASS, P_HILO>(s, vb, a.scale_log2, L, st, p, pl);
+    if constexpr (PASS != ks::kPassMax) pv_half<P_HILO>(buf, p, pl, L, st);
+  }
+}
+
+template <bool PACKED, bool P_HILO>
+__device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
+                                       const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st) {
+#pragma unroll
+  for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+  st.m_ref = -INFINITY;
+  st.l_run = 0.f;
+  st.overflow = false;
+  sweep<PACKED, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, wave, L, qs, buf, st);
+  if (__ballot(st.overflow)) {  // wave-uniform
+    // Rare: a score ran far above its row's first-half-tile max.  Redo this
+    // wave's share with the exact max (a scores-only sweep) as the reference.
+#pragma unroll
+    for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_ref = -INFINITY;
+    st.l_run = 0.f;
+    sweep<PACKED, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, wave, L, qs, buf, st);
+    sweep<PACKED, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, wave, L, qs, buf, st);
+  }
+}
+
+// Merge of the eight waves' states.  Waves 4..7 hand their states to waves
+// 0..3 through LDS; then each of waves 0..3 dumps its state and reduces a
+// quarter of the dims over the four: each ends
+// with dims 16d + 4g + i, d = 8w .. 8w+7, of this lane's query row j in o,
+// the merged reference max m and weight sum l.  Returns false on waves 4..7.
+__device__ __forceinline__ bool merge_waves(Smem &sm, int wave, const Lane &L, State &st, f32x4 (&o)[8], float &m,
+                                            float &l) {
+  __syncthreads();  // every wave is done with Q^T and its buffer
+  uint8_t SMD_LDS *base = (uint8_t SMD_LDS *)&sm.buf[0][0];  // 128 KiB: 4 states of 32 KiB
+  f32x4 SMD_LDS *dump = (f32x4 SMD_LDS *)(base + (wave & 3) * 32768);
+  float SMD_LDS *side = (float SMD_LDS *)&sm.q[0] + (wave & 3) * 128;  // m_ref, l_run per lane
+  if (wave >= 4) {
+#pragma unroll
+    for (int d = 0; d < 32; ++d) dump[d * 64 + L.lane] = st.acc[d];
+    side[L.lane] = st.m_ref;
+    side[64 + L.lane] = st.l_run;
+  }
+  __syncthreads();
+  if (wave < 4) {
+    const float mb = side[L.lane], lb = side[64 + L.lane];
+    const float mm = fmaxf(st.m_ref, mb);
+    const float sa = st.m_ref == -INFINITY ? 0.f : ks::exp2_fast(st.m_ref - mm);
+    const float sb = mb == -INFINITY ? 0.f : ks::exp2_fast(mb - mm);
+#pragma unroll
+    for (int d = 0; d < 32; ++d) st.acc[d] = st.acc[d] * sa + dump[d * 64 + L.lane] * sb;
+    st.m_ref = mm;
+    st.l_run = st.l_run * sa + lb * sb;
+  }
+  __syncthreads();
+  // four-wave merge over the same 128 KiB (each of waves 0..3 dumps its state
+  // into its own 32 KiB)
+  if (wave < 4) {
+#pragma unroll
+    for (int d = 0; d < 32; ++d) dump[d * 64 + L.lane] = st.acc[d];
+    const float l_row = ks::group_sum(st.l_run);
+    if (L.g == 0) {
+      sm.stat_m[wave][L.j] = st.m_ref;
+      sm.stat_l[wave][L.j] = l_row;
+    }
+  }
+  __syncthreads();
+  if (wave >= 4) return false;
+  float mw[4], lw[4];
+  m = -INFINITY;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    mw[w] = sm.stat_m[w][L.j];
+    lw[w] = sm.stat_l[w][L.j];
+    m = fmaxf(m, mw[w]);
+  }
+  l = 0.f;
+  float sc[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    sc[w] = mw[w] == -INFINITY ? 0.f : ks::exp2_fast(mw[w] - m);
+    l += sc[w] * lw[w];
+  }
+#pragma unroll
+  for (int d = 0; d < 8; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    const f32x4 SMD_LDS *src = (const f32x4 SMD_LDS *)(base + w * 32768);
+#pragma unroll
+    for (int d = 0; d < 8; ++d) o[d] += sc[w] * src[(8 * wave + d) * 64 + L.lane];
+  }
+  return true;
+}
+
+}  // namespace ks8
+}  // namespace smd

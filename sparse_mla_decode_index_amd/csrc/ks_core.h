@@ -1,42 +1,26 @@
-// Device core of sparse MLA decode for gfx950 (MI355X): wave-independent
-// attention of one 16-query-row block over a range of index positions.
+// Building blocks of the wave-independent sparse MLA decode for gfx950
+// (MI355X), bf16 pools: row gather, softmax step, output epilogues.  The
+// kernel's work decomposition and pipeline are in ks8_core.h.
 //
 // What is computed (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
 // decode on gfx950", Design): per query row, a 512-wide dot product (448 NoPE
 // + 64 RoPE dims) with every selected latent row, an online softmax that also
 // counts a per-head sink logit, and a PV product over the same 512-wide rows.
 //
-// Work decomposition.  A workgroup of 4 waves owns one block of 16 query rows
-// (heads x MTP positions sharing one index list) and a range [p0, p1) of index
-// positions.  The range is cut into half-tiles of 16 positions; wave w takes
-// half-tiles w, w+4, w+8, ...  Each wave owns all 512 dims of the 16 query
-// rows, so the main loop needs no barrier: the waves only meet at the end,
-// where their (O, m, l) states are merged through LDS.
+// Gather: one load instruction per selected row, 16 bytes per lane, so a row
+// is one contiguous 1 KiB read (the row base comes from a per-lane address
+// vector by readlane).  Loading straight into MFMA operand order would put 16
+// different rows on consecutive lanes, which costs the L1 one tag lookup per
+// lane.  Invalid indices and positions past the range address a zero row, so
+// every half-tile issues the same loads and the compiler's wait counts stay
+// exact.
 //
-// Per half-tile, per wave:
-//   gather   bf16 pools (fp8 pools use the row-block kernel): one load
-//            instruction per selected row, 16 bytes per lane, so a row is one
-//            contiguous 1 KiB read (the row base comes from a per-lane address
-//            vector by readlane).  Each wave stores its rows to its own LDS
-//            buffer (16 KiB, 16-byte chunks XOR-swizzled), from which QK reads
-//            its A operands and PV its transposed V^T.  (Loading straight into
-//            MFMA operand order would put 16 different rows on consecutive
-//            lanes, which costs the L1 one tag lookup per lane.)  Invalid
-//            indices and positions past p1 address a zero row, so every
-//            half-tile issues the same loads and the compiler's wait counts
-//            stay exact.
-//   QK       S^T[16 kv x 16 q] = K . Q^T with v_mfma_f32_16x16x32_bf16; Q^T
-//            stays resident (64 VGPRs).  In this orientation lane (j, g) holds
-//            the scores of query row j for kv rows 4g..4g+3, so the softmax
-//            statistics are per-lane values.
-//   softmax  a reference max per query row, fixed at its first valid
-//            half-tile (exp2 domain, scale pre-multiplied by log2(e)); a score
-//            more than 2^32 above it sends the wave through an exact-max
-//            second pass, so the accumulators are never rescaled.
-//   PV       every second half-tile,
-//            O^T[512 x 16] += V^T[512 x 32] . P^T[32 x 16] with V^T read by
-//            ds_read_b64_tr_b16 from the two buffers and P^T taken from the
-//            softmax registers.
+// Orientation: S^T[16 kv x 16 q] = K . Q^T with v_mfma_f32_16x16x32_bf16, so
+// lane (j, g) holds the scores of query row j for kv rows 4g..4g+3 and the
+// softmax statistics are per-lane values.  The softmax keeps a reference max
+// per query row, fixed at its first valid half-tile (exp2 domain, scale
+// pre-multiplied by log2(e)); a score more than 2^32 above it sends the wave
+// through an exact-max second pass, so the accumulators are never rescaled.
 #pragma once
 
 #include "smd_internal.h"
@@ -54,11 +38,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define SMD_LDS __attribute__((address_space(3)))
 
-constexpr int kWaves = 4;                        // waves per workgroup
 constexpr int kHalf = 16;                        // index positions per half-tile
 constexpr int kRowBytes = 1024;                  // one bf16 row in LDS
 constexpr int kHalfBytes = kHalf * kRowBytes;    // 16 KiB
-constexpr int kWaveLds = 2 * kHalfBytes;         // two half-tile buffers per wave
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 // A row's reference max is fixed at its first valid half-tile; a later score
@@ -67,15 +49,6 @@ constexpr float kRefSlackLog2 = 32.f;
 
 // Zero bytes read in place of every masked row.
 static __device__ __attribute__((aligned(256))) uint8_t g_zero_row[1024];
-
-// Shared memory of a workgroup: the waves' half-tile buffers, reused at the end
-// for the cross-wave merge (each wave then dumps its accumulators into its
-// own 32 KiB), plus the per-row statistics of the merge.
-struct Smem {
-  uint8_t buf[kWaves][kWaveLds];
-  float stat_m[kWaves][16];
-  float stat_l[kWaves][16];
-};
 
 // XOR permutation of the 16-byte chunks of row r in a half-tile buffer.  It
 // only touches the low 4 chunk bits and makes conflict-free both the 16-byte
@@ -140,17 +113,6 @@ __device__ __forceinline__ Lane make_lane(int lane) {
   return L;
 }
 
-// Q^T as the B operand of the QK MFMAs: step ks = dims 32ks + 8q .. +8
-// (ks < 14 from q_nope, 14 and 15 from q_rope).
-__device__ __forceinline__ void load_q(const DecodeArgs &a, int64_t qrow, int q, bf16x8 (&qreg)[16]) {
-  const uint16_t *qn = a.q_nope + qrow * kNope;
-  const uint16_t *qr = a.q_rope + qrow * kRope;
-#pragma unroll
-  for (int s = 0; s < 14; ++s) qreg[s] = *(const bf16x8 *)(qn + 32 * s + 8 * q);
-#pragma unroll
-  for (int s = 0; s < 2; ++s) qreg[14 + s] = *(const bf16x8 *)(qr + 32 * s + 8 * q);
-}
-
 // Address of row l % 16 of a half-tile in lane l: the selected NoPE row, or
 // the zero row when the position is past the range or the index is invalid.
 template <bool PACKED>
@@ -183,29 +145,6 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, uint32_t idx, bo
       h.v[i] = *(const u32x4 *)p;
     }
   }
-}
-
-// QK over one half-tile: the gathered rows are stored to the LDS buffer `buf`
-// (row i, chunk `lane` -> physical chunk lane ^ swz(i): one row of 64 distinct
-// chunks per instruction, conflict-free) and the A operands read back (step
-// ks: 16 rows x chunks 4ks + q, also conflict-free).
-__device__ __forceinline__ f32x4 qk_half(const Half &h, const bf16x8 (&qreg)[16], uint8_t SMD_LDS *buf,
-                                         const Lane &L) {
-#pragma unroll
-  for (int i = 0; i < 16; ++i) *(u32x4 SMD_LDS *)(buf + i * kRowBytes + ((L.lane ^ swz(i)) << 4)) = h.v[i];
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  constexpr int kPre = 4;  // LDS reads issued ahead of the QK MFMAs
-  bf16x8 ka[kPre];
-#pragma unroll
-  for (int ks = 0; ks < kPre; ++ks) ka[ks] = *(const bf16x8 SMD_LDS *)(buf + L.wb[ks & 3] + 256 * (ks >> 2));
-#pragma unroll
-  for (int ks = 0; ks < 16; ++ks) {
-    const bf16x8 k = ka[ks % kPre];
-    if (ks + kPre < 16)
-      ka[ks % kPre] = *(const bf16x8 SMD_LDS *)(buf + L.wb[(ks + kPre) & 3] + 256 * ((ks + kPre) >> 2));
-    s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, qreg[ks], s, 0, 0, 0);
-  }
-  return s;
 }
 
 // Per-wave softmax state and O^T accumulator: acc[d][i] = sum over rows of
@@ -251,157 +190,10 @@ __device__ __forceinline__ void softmax_half(f32x4 s, uint32_t vbits, float scal
   st.l_run += psum;
 }
 
-// PV over a pair of half-tiles held in LDS buffers ba (positions of the first
-// half) and bb (second half): k slot 8g + u is row 4g + u of the first half
-// for u < 4 and row 4g + u - 4 of the second half otherwise, in both operands.
-template <bool P_HILO>
-__device__ __forceinline__ void pv_pair(const uint8_t SMD_LDS *ba, const uint8_t SMD_LDS *bb, bf16x4 pa, bf16x4 pb,
-                                        bf16x4 la, bf16x4 lb, const Lane &L, State &st) {
-  const bf16x8 p = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
-  bf16x8 pl;
-  if constexpr (P_HILO) pl = __builtin_shufflevector(la, lb, 0, 1, 2, 3, 4, 5, 6, 7);
-  constexpr int kPre = 4;  // transposed-read pairs issued ahead of the PV MFMAs
-  bf16x4 va[kPre], vb[kPre];
-  auto load = [&](int d) {
-    const int off = L.pv[d & 7] + 256 * (d >> 3);
-    va[d % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(ba + off));
-    vb[d % kPre] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(bb + off));
-  };
-#pragma unroll
-  for (int d = 0; d < kPre; ++d) load(d);
-#pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    const bf16x8 v = __builtin_shufflevector(va[d % kPre], vb[d % kPre], 0, 1, 2, 3, 4, 5, 6, 7);
-    if (d + kPre < 32) load(d + kPre);
-    st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, p, st.acc[d], 0, 0, 0);
-    if constexpr (P_HILO) st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v, pl, st.acc[d], 0, 0, 0);
-  }
-}
-
-// One wave's sweep over its half-tiles of [p0, p1) (half-tile k of this wave
-// covers positions p0 + 16*(wave + 4k) + 0..15).  Pipeline per half-tile k:
-// load the indices of k+3, consume the gathered registers of k (QK, LDS
-// store), refill them with the rows of k+2, softmax, and every second
-// half-tile PV over the pair.  Two register sets alternate, so the rows of
-// one half-tile are always in flight while another is computed; every step
-// issues the same loads (positions past p1 read the zero row), which keeps the
-// compiler's wait counts exact.  Odd counts are padded with an all-masked
-// half-tile, which leaves the state unchanged.
-template <bool PACKED, bool P_HILO, int PASS>
-__device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                      const Lane &L, const bf16x8 (&qreg)[16], uint8_t SMD_LDS *wbuf, State &st) {
-  const int nh = (p1 - p0 + kHalf - 1) / kHalf;              // half-tiles of the range
-  const int nk = nh > wave ? (nh - wave + kWaves - 1) / kWaves : 0;  // ... of this wave
-  if (nk == 0) return;
-  const int nk2 = (nk + 1) & ~1;
-  auto pos_of = [&](int k) { return p0 + kHalf * (wave + kWaves * k) + L.r; };
-  auto load_idx = [&](int k) { return row_idx[min(pos_of(k), p1 - 1)]; };
-  auto valid_of = [&](int k, int32_t idx) { return pos_of(k) < p1 && (uint32_t)idx < a.num_rows32; };
-
-  Half hx, hy;
-  int32_t i0 = load_idx(0), i1 = load_idx(1);
-  int32_t i2 = load_idx(2);
-  bool v0 = valid_of(0, i0), v1 = valid_of(1, i1);
-  issue_half<PACKED>(a, (uint32_t)i0, v0, L, hx);
-  issue_half<PACKED>(a, (uint32_t)i1, v1, L, hy);
-  uint32_t vb_x = (uint32_t)__ballot(v0) & 0xffffu, vb_y = (uint32_t)__ballot(v1) & 0xffffu;
-  int32_t i_even = i2, i_odd = 0;  // indices of half-tiles k+2 for the next even / odd step
-  bf16x4 pa, la, pb, lb;
-
-  for (int k = 0; k < nk2; k += 2) {
-    // ---- even step: half-tile k in hx (buffer 0)
-    i_odd = load_idx(k + 3);
-    {
-      const f32x4 s = qk_half(hx, qreg, wbuf, L);
-      const uint32_t vb = vb_x;
-      const bool vn = valid_of(k + 2, i_even);
-      issue_half<PACKED>(a, (uint32_t)i_even, vn, L, hx);
-      vb_x = (uint32_t)__ballot(vn) & 0xffffu;
-      softmax_half<PASS, P_HILO>(s, vb, a.scale_log2, L, st, pa, la);
-    }
-    // ---- odd step: half-tile k+1 in hy (buffer 1), then PV over the pair
-    i_even = load_idx(k + 4);
-    {
-      const f32x4 s = qk_half(hy, qreg, wbuf + kHalfBytes, L);
-      const uint32_t vb = vb_y;
-      const bool vn = valid_of(k + 3, i_odd);
-      issue_half<PACKED>(a, (uint32_t)i_odd, vn, L, hy);
-      vb_y = (uint32_t)__ballot(vn) & 0xffffu;
-      softmax_half<PASS, P_HILO>(s, vb, a.scale_log2, L, st, pb, lb);
-    }
-    if constexpr (PASS != kPassMax) pv_pair<P_HILO>(wbuf, wbuf + kHalfBytes, pa, pb, la, lb, L, st);
-  }
-}
-
-// The wave's attention over its share of [p0, p1): the main sweep, and the
-// exact-max redo when a score overflowed the reference max.
-template <bool PACKED, bool P_HILO>
-__device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                       const Lane &L, const bf16x8 (&qreg)[16], uint8_t SMD_LDS *wbuf, State &st) {
-#pragma unroll
-  for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-  st.m_ref = -INFINITY;
-  st.l_run = 0.f;
-  st.overflow = false;
-  sweep<PACKED, P_HILO, kPassMain>(a, row_idx, p0, p1, wave, L, qreg, wbuf, st);
-  if (__ballot(st.overflow)) {  // wave-uniform
-    // Rare: a score ran far above its row's first-half-tile max.  Redo this
-    // wave's share with the exact max (a scores-only sweep) as the reference.
-#pragma unroll
-    for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-    st.m_ref = -INFINITY;
-    st.l_run = 0.f;
-    sweep<PACKED, P_HILO, kPassMax>(a, row_idx, p0, p1, wave, L, qreg, wbuf, st);
-    sweep<PACKED, P_HILO, kPassFixed>(a, row_idx, p0, p1, wave, L, qreg, wbuf, st);
-  }
-}
-
-// Merge of the four waves' states through LDS.  Afterwards wave v holds, for
-// this lane's query row j, the merged sum over dims 16d + 4g + i with
-// d = 8v .. 8v+7 in o[d - 8v], the merged reference max m (log2 domain, -inf
-// when no valid entry) and the merged weight sum l.
-__device__ __forceinline__ void merge_waves(Smem &sm, int wave, const Lane &L, const State &st, f32x4 (&o)[8],
-                                            float &m, float &l) {
-  // each wave dumps its accumulators into its own buffers (its reads of them
-  // are complete: LDS operations of one wave execute in order)
-  f32x4 SMD_LDS *dump = (f32x4 SMD_LDS *)&sm.buf[wave][0];
-#pragma unroll
-  for (int d = 0; d < 32; ++d) dump[d * 64 + L.lane] = st.acc[d];
-  const float l_row = group_sum(st.l_run);
-  if (L.g == 0) {
-    sm.stat_m[wave][L.j] = st.m_ref;
-    sm.stat_l[wave][L.j] = l_row;
-  }
-  __syncthreads();
-  float mw[kWaves], lw[kWaves];
-  m = -INFINITY;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    mw[w] = sm.stat_m[w][L.j];
-    lw[w] = sm.stat_l[w][L.j];
-    m = fmaxf(m, mw[w]);
-  }
-  l = 0.f;
-  float sc[kWaves];
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    sc[w] = mw[w] == -INFINITY ? 0.f : exp2_fast(mw[w] - m);
-    l += sc[w] * lw[w];
-  }
-#pragma unroll
-  for (int d = 0; d < 8; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) {
-    const f32x4 SMD_LDS *src = (const f32x4 SMD_LDS *)&sm.buf[w][0];
-#pragma unroll
-    for (int d = 0; d < 8; ++d) o[d] += sc[w] * src[(8 * wave + d) * 64 + L.lane];
-  }
-}
-
 // Final bf16 output of one query row with the sink folded in:
 // out = O / (l + e^(sink - m)), lse = m + ln(l + e^(sink - m)) (natural log).
-// dst points at dim 128*wave + 4g of the row; the lse is written when lse_dst
-// is non-null.
+// dst points at dim 128*w + 4g of the row for the w-th quarter of the dims;
+// the lse is written when lse_dst is non-null.
 __device__ __forceinline__ void write_direct(const f32x4 (&o)[8], float m, float l, float sink_ln, uint16_t *dst,
                                              float *lse_dst) {
   const float sink2 = sink_ln * kLog2e;
