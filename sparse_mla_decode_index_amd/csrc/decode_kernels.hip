@@ -41,11 +41,14 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int head = m % a.H;
   const int64_t qrow = (int64_t)tok * a.H + head;  // [T, H] row
 
+  // the first indices and rows are in flight while Q^T is staged
+  ks8::Pipe pipe;
+  ks8::prime<PACKED>(a, row_idx, p0, p1, wave, L, pipe);
   ks8::stage_q(a, qrow, wave, L, sm);
   __syncthreads();
   ks::State st;
   ks8::attend<PACKED, P_HILO>(a, row_idx, p0, p1, wave, L, (const uint8_t SMD_LDS *)&sm.q[0],
-                              (uint8_t SMD_LDS *)&sm.buf[wave][0], st);
+                              (uint8_t SMD_LDS *)&sm.buf[wave][0], st, pipe);
   ks::f32x4 o[8];
   float mm, ll;
   if (!ks8::merge_waves(sm, wave, L, st, o, mm, ll)) return;
@@ -60,7 +63,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Stage-2 merge: one wave per [T,H] row, 8 dims per lane.
+// Stage-2 merge: one wave per [T,H] row, 8 dims per lane.  The partials are
+// read four at a time (their lse and o in one round trip) and folded into a
+// running max / sum, so a plan of up to four splits costs one round trip.
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po,
                                                     const float *__restrict__ plse, int rows, int H,
                                                     int S, const float *__restrict__ sink,
@@ -70,34 +75,53 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   const int lane = threadIdx.x & 63;
   const int head = row % H;
   const float *ls = plse + (int64_t)row * S;
-  float mx = sink ? sink[head] : -INFINITY;
-  for (int r = 0; r < S; ++r) mx = fmaxf(mx, ls[r]);
+  const float *src = po + (int64_t)row * S * kDim + lane * 8;
+  const float sk = sink ? sink[head] : -INFINITY;
+  float mx = sk;   // running max of the lse terms (natural log)
+  float z = 1.f;   // sum of e^(term - mx) (the sink, or nothing yet)
+  if (mx == -INFINITY) z = 0.f;
+  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int r0 = 0; r0 < S; r0 += 4) {
+    float l[4];
+    f32x4 v[4][2];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int r = min(r0 + c, S - 1);  // clamped: every chunk issues the same loads
+      l[c] = r0 + c < S ? ls[r] : -INFINITY;
+      v[c][0] = *(const f32x4 *)(src + (int64_t)r * kDim);
+      v[c][1] = *(const f32x4 *)(src + (int64_t)r * kDim + 4);
+    }
+    const float cm = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
+    if (cm == -INFINITY) continue;
+    const float nm = fmaxf(mx, cm);
+    const float rescale = mx == -INFINITY ? 0.f : exp2_fast((mx - nm) * kLog2e);
+    z *= rescale;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) o[i] *= rescale;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float w = l[c] == -INFINITY ? 0.f : exp2_fast((l[c] - nm) * kLog2e);
+      z += w;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        o[i] += w * v[c][0][i];
+        o[4 + i] += w * v[c][1][i];
+      }
+    }
+    mx = nm;
+  }
   uint16_t *dst = out + (int64_t)row * kDim + lane * 8;
   if (mx == -INFINITY) {
     *(u32x4 *)dst = u32x4{0u, 0u, 0u, 0u};
     if (lse && lane == 0) lse[row] = -INFINITY;
     return;
   }
-  float z = sink ? exp2_fast((sink[head] - mx) * kLog2e) : 0.f;
-  float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  const float *src = po + (int64_t)row * S * kDim + lane * 8;
-  for (int r = 0; r < S; ++r) {
-    const float w = exp2_fast((ls[r] - mx) * kLog2e);
-    z += w;
-    const f32x4 v0 = *(const f32x4 *)(src + (int64_t)r * kDim);
-    const f32x4 v1 = *(const f32x4 *)(src + (int64_t)r * kDim + 4);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      o[i] += w * v0[i];
-      o[4 + i] += w * v1[i];
-    }
-  }
   const float inv = 1.f / z;
-  u32x4 v;
+  u32x4 vo;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    v[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
-  *(u32x4 *)dst = v;
+    vo[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
+  *(u32x4 *)dst = vo;
   if (lse && lane == 0) lse[row] = mx + logf(z);
 }
 

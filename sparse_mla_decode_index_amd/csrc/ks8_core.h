@@ -107,39 +107,52 @@ __device__ __forceinline__ void pv_half(const uint8_t SMD_LDS *buf, bf16x4 p, bf
   }
 }
 
-// One wave's sweep over its half-tiles of [p0, p1) (half-tile k of this wave
-// covers positions p0 + 16*(wave + 8k) + 0..15).  Per half-tile k: store the
-// gathered rows of k, refill the register set with the rows of k+1 (whose
-// indices were loaded one step earlier), load the indices of k+2, then QK,
-// softmax and PV of k from LDS while k+1 is in flight.  Every step issues the
-// same loads (positions past p1 read the zero row), so the compiler's wait
-// counts stay exact.
+// The gather pipeline of one wave: the register set with the rows of the
+// next half-tile to compute, the indices of the half-tile after it, and the
+// valid-row bits of the rows in the register set.
+struct Pipe {
+  Half h;
+  int32_t i_next;
+  uint32_t vb;
+  int nk;  // half-tiles of this wave
+};
+
+// Half-tile k of this wave covers positions p0 + 16*(wave + 8k) + 0..15.
+__device__ __forceinline__ int pos_of(int p0, int wave, int k, const Lane &L) {
+  return p0 + kHalf * (wave + kWaves * k) + L.r;
+}
+
+// Start the pipeline: indices of half-tiles 0 and 1, rows of half-tile 0.
+template <bool PACKED>
+__device__ __forceinline__ void prime(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
+                                      const Lane &L, Pipe &pp) {
+  const int nh = (p1 - p0 + kHalf - 1) / kHalf;
+  pp.nk = nh > wave ? (nh - wave + kWaves - 1) / kWaves : 0;
+  if (pp.nk == 0) return;
+  const int32_t i0 = row_idx[min(pos_of(p0, wave, 0, L), p1 - 1)];
+  pp.i_next = row_idx[min(pos_of(p0, wave, 1, L), p1 - 1)];
+  const bool v0 = pos_of(p0, wave, 0, L) < p1 && (uint32_t)i0 < a.num_rows32;
+  ks::issue_half<PACKED>(a, (uint32_t)i0, v0, L, pp.h);
+  pp.vb = (uint32_t)__ballot(v0) & 0xffffu;
+}
+
+// One wave's sweep over its half-tiles of [p0, p1), from a primed pipeline.
+// Per half-tile k: store the gathered rows of k, refill the register set with
+// the rows of k+1 (their indices were loaded one step earlier), load the
+// indices of k+2, then QK, softmax and PV of k from LDS while k+1 is in
+// flight.  Every step issues the same loads (positions past p1 read the zero
+// row), so the compiler's wait counts stay exact.
 template <bool PACKED, bool P_HILO, int PASS>
 __device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                      const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st) {
-  const int nh = (p1 - p0 + kHalf - 1) / kHalf;
-  const int nk = nh > wave ? (nh - wave + kWaves - 1) / kWaves : 0;
-  if (nk == 0) return;
-  auto pos_of = [&](int k) { return p0 + kHalf * (wave + kWaves * k) + L.r; };
-  auto load_idx = [&](int k) { return row_idx[min(pos_of(k), p1 - 1)]; };
-  auto valid_of = [&](int k, int32_t idx) { return pos_of(k) < p1 && (uint32_t)idx < a.num_rows32; };
-
-  Half h;
-  const int32_t i0 = load_idx(0);
-  int32_t i_next = load_idx(1);
-  const bool v0 = valid_of(0, i0);
-  ks::issue_half<PACKED>(a, (uint32_t)i0, v0, L, h);
-  uint32_t vb_cur = (uint32_t)__ballot(v0) & 0xffffu;
-  for (int k = 0; k < nk; ++k) {
-    // store the rows of k, refill the registers with the rows of k+1 (their
-    // indices were loaded one step earlier), load the indices of k+2, then
-    // compute k from LDS while k+1 is in flight
-    store_half(h, buf, L);
-    const bool vn = valid_of(k + 1, i_next);
-    ks::issue_half<PACKED>(a, (uint32_t)i_next, vn, L, h);
-    i_next = load_idx(k + 2);
-    const uint32_t vb = vb_cur;
-    vb_cur = (uint32_t)__ballot(vn) & 0xffffu;
+                                      const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st,
+                                      Pipe &pp) {
+  for (int k = 0; k < pp.nk; ++k) {
+    store_half(pp.h, buf, L);
+    const bool vn = pos_of(p0, wave, k + 1, L) < p1 && (uint32_t)pp.i_next < a.num_rows32;
+    ks::issue_half<PACKED>(a, (uint32_t)pp.i_next, vn, L, pp.h);
+    pp.i_next = row_idx[min(pos_of(p0, wave, k + 2, L), p1 - 1)];
+    const uint32_t vb = pp.vb;
+    pp.vb = (uint32_t)__ballot(vn) & 0xffffu;
     const f32x4 s = qk_lds(qs, buf, L);
     bf16x4 p, pl;
     ks::softmax_half<PASS, P_HILO>(s, vb, a.scale_log2, L, st, p, pl);
@@ -147,15 +160,18 @@ __device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_id
   }
 }
 
+// The wave's attention over its share of [p0, p1) from a primed pipeline: the
+// main sweep, and the exact-max redo when a score overflowed the reference.
 template <bool PACKED, bool P_HILO>
 __device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                       const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st) {
+                                       const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st,
+                                       Pipe &pp) {
 #pragma unroll
   for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_ref = -INFINITY;
   st.l_run = 0.f;
   st.overflow = false;
-  sweep<PACKED, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, wave, L, qs, buf, st);
+  sweep<PACKED, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
   if (__ballot(st.overflow)) {  // wave-uniform
     // Rare: a score ran far above its row's first-half-tile max.  Redo this
     // wave's share with the exact max (a scores-only sweep) as the reference.
@@ -163,8 +179,10 @@ __device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_i
     for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m_ref = -INFINITY;
     st.l_run = 0.f;
-    sweep<PACKED, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, wave, L, qs, buf, st);
-    sweep<PACKED, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, wave, L, qs, buf, st);
+    prime<PACKED>(a, row_idx, p0, p1, wave, L, pp);
+    sweep<PACKED, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
+    prime<PACKED>(a, row_idx, p0, p1, wave, L, pp);
+    sweep<PACKED, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
   }
 }
 
