@@ -127,6 +127,35 @@ def cpu_baseline(w, target_s: float):
     return per_call, sample, cores
 
 
+def kernel_sources_sha() -> str:
+    """sha256 over the HIP kernel sources (file names and bytes, sorted)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "sparse_mla_decode_index_amd", "csrc")
+    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
+        h.update(os.path.basename(p).encode())
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from the FETCH_SIZE /
+    WRITE_SIZE profiles in profiles/traffic.json, scaled by a plain device
+    copy; None when the kernels changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None, None
+    e = t.get("workloads", {}).get(workload)
+    if e is None or e.get("kernel") != kernel or t.get("kernel_sources_sha256") != kernel_sources_sha():
+        return None, None
+    return e["bytes_per_launch"], e.get("summary")
+
+
 def graph_time(torch, stream, fn, n):
     """Average µs of fn() over n back-to-back launches captured in one graph,
     timed with events recorded on the stream the graph replays on."""
@@ -203,7 +232,7 @@ def main():
         def merge_only():
             smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
-        kernel_name = "smd::decode_kernel"
+        kernel_name = "smd::decode_kernel" if w.kv_dtype == "bf16" else "smd::decode_rb_kernel"
         cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv"})
 
     with torch.cuda.stream(stream):
@@ -262,6 +291,10 @@ def main():
     else:
         roof = {"bound": "mfma", "achieved": round(kern_tfs, 1), "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                 "frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
+    traffic, traffic_src = measured_traffic(w.name, kernel_name)
+    roof["traffic"] = traffic
+    if traffic_src:
+        roof["traffic_source"] = traffic_src
     roof.update({"kernel": kernel_name, "kernel_us": round(kern_us, 3), "merge_us": round(merge_us, 3),
                  "alg_bytes_per_launch": alg_bytes,
                  "alg_flops_per_launch": alg_flops, "hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4),
