@@ -74,8 +74,19 @@ __device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 
-__device__ __forceinline__ float wave_xor(float v, int mask) {
-  return __shfl_xor(v, mask, 64);
+// max / sum over the four 16-lane groups (lanes j, j+16, j+32, j+48) with the
+// gfx950 permlane swaps (VALU, no LDS round trip).
+__device__ __forceinline__ float group_max(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float group_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
@@ -120,13 +131,14 @@ __device__ __forceinline__ int load_idx_block(const int32_t *row_idx, int p0, in
 // LDS stores.  Wave w handles tile rows 8w .. 8w+7.
 //   bf16: v[i] = logical 16-byte chunk lane ^ swz(rr) of row rr = 8w + i.
 //   fp8:  v[j] (j < 4) = 16 e4m3 bytes of chunk (lane & 31) (clamped to 27) of
-//         row 8w + 2j + (lane >> 5); rope = 16 RoPE bytes, chunk lane & 7 of
-//         row 8w + (lane >> 3); code = UE8M0 byte (lane & 7) of that row.
+//         row 8w + 2j + (lane >> 5) and code[j] = the UE8M0 code of that
+//         chunk's 64-dim block; rope = 16 RoPE bytes, chunk lane & 7 of row
+//         8w + (lane >> 3).
 template <bool FP8>
 struct Staged {
   u32x4 v[FP8 ? 4 : kBK / 4];
   u32x4 rope;
-  uint32_t code;
+  uint32_t code[FP8 ? 4 : 1];
 };
 
 // Per-wave constants of the gather, computed once.
@@ -194,14 +206,15 @@ __device__ __forceinline__ void load_rows(const DecodeArgs &a, const uint8_t *zr
       const uint64_t oa = va ? (uint64_t)ia_ * (uint64_t)a.nope_stride_b : zoff;
       const uint64_t ob = vb ? (uint64_t)ib_ * (uint64_t)a.nope_stride_b : zoff;
       st.v[j] = *(const u32x4 *)(a.kv_nope + (lane < 32 ? oa : ob) + c * 16);
+      const uint8_t *sa = va ? a.kv_scale + (uint64_t)ia_ * (uint64_t)a.scale_stride_b : zrow;
+      const uint8_t *sb = vb ? a.kv_scale + (uint64_t)ib_ * (uint64_t)a.scale_stride_b : zrow;
+      st.code[j] = (lane < 32 ? sa : sb)[c >> 2];
     }
     // RoPE and codes of the 8 rows: lane l serves row l >> 3
     const uint32_t il = (uint32_t)widx[lane >> 3];
     const bool vl = ((lane >> 3) < rows_left) & (il < a.num_rows32);
     const uint8_t *rp = vl ? a.kv_rope + (uint64_t)il * (uint64_t)a.rope_stride_b : zrow;
-    const uint8_t *sp = vl ? a.kv_scale + (uint64_t)il * (uint64_t)a.scale_stride_b : zrow;
     st.rope = *(const u32x4 *)(rp + (lane & 7) * 16);
-    st.code = sp[lane & 7];
   }
 }
 
@@ -218,8 +231,7 @@ __device__ __forceinline__ void store_rows(uint8_t SMD_LDS *tile, int wave, int 
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int rl = 2 * j + (lane >> 5);            // row within the wave's 8
-      // the code of block c/4 of that row sits in lane rl*8 + c/4
-      const uint32_t code = (uint32_t)__shfl((int)st.code, rl * 8 + (min(c, 27) >> 2), 64) & 0xffu;
+      const uint32_t code = st.code[j];
       if (c < 28) {
         const int rr = wave * (kBK / 4) + rl;
         const int f = swz(rr);
@@ -323,8 +335,7 @@ __device__ __forceinline__ void compute_tile(const uint8_t SMD_LDS *tile, float 
     x[4 + i] = ((vbits >> (16 + 4 * grp + i)) & 1) ? s1[i] * scale_log2 : -INFINITY;
   }
   float tmax = fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-  tmax = fmaxf(tmax, wave_xor(tmax, 16));
-  tmax = fmaxf(tmax, wave_xor(tmax, 32));
+  tmax = group_max(tmax);
   if constexpr (PASS == kPassMax) {
     w.m_ref = fmaxf(w.m_ref, tmax);
     return;
@@ -494,8 +505,7 @@ __device__ __forceinline__ void attend_range(const DecodeArgs &a, Smem<4 / RB> &
 // Total weight sum of this lane's query row (the same in all four 16-lane groups).
 __device__ __forceinline__ float row_total(float l_run) {
   float l = l_run;
-  l += wave_xor(l, 16);
-  l += wave_xor(l, 32);
+  l = group_sum(l);
   return l;
 }
 

@@ -37,6 +37,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 #define SMD_LDS __attribute__((address_space(3)))
+#define SMD_GLOBAL __attribute__((address_space(1)))
 
 constexpr int kHalf = 16;                        // index positions per half-tile
 constexpr int kRowBytes = 1024;                  // one bf16 row in LDS
@@ -131,18 +132,22 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, uint32_t idx, bo
   if constexpr (!PACKED)
     raddr = valid ? (uint64_t)(uintptr_t)(a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b)
                   : (uint64_t)(uintptr_t)g_zero_row + 2 * kNope;
+  // The rebuilt row pointers are global-address-space pointers, so the loads
+  // are global loads with the row base in SGPRs: a generic (flat) load would
+  // also count against the LDS wait counter and stall every LDS wait on it.
+  typedef const uint8_t SMD_GLOBAL *gptr;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const uint64_t nb = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(naddr >> 32), i) << 32) |
                         (uint32_t)__builtin_amdgcn_readlane((uint32_t)naddr, i);
     if constexpr (PACKED) {
-      h.v[i] = *(const u32x4 *)((const uint8_t *)(uintptr_t)nb + 16 * L.lane);
+      h.v[i] = *(const u32x4 SMD_GLOBAL *)((gptr)(uintptr_t)nb + 16 * L.lane);
     } else {
       const uint64_t rb = ((uint64_t)__builtin_amdgcn_readlane((uint32_t)(raddr >> 32), i) << 32) |
                           (uint32_t)__builtin_amdgcn_readlane((uint32_t)raddr, i);
-      const uint8_t *p = L.lane < kNope / 8 ? (const uint8_t *)(uintptr_t)nb + 16 * L.lane
-                                            : (const uint8_t *)(uintptr_t)rb + 16 * (L.lane - kNope / 8);
-      h.v[i] = *(const u32x4 *)p;
+      const gptr p = L.lane < kNope / 8 ? (gptr)(uintptr_t)nb + 16 * L.lane
+                                        : (gptr)(uintptr_t)rb + 16 * (L.lane - kNope / 8);
+      h.v[i] = *(const u32x4 SMD_GLOBAL *)p;
     }
   }
 }
