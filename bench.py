@@ -232,9 +232,12 @@ def main():
         def merge_only():
             smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
-        kernel_name = "smd::decode_kernel" if w.kv_dtype == "bf16" else "smd::decode_rb_kernel"
+        kernel_name = "smd::decode_kernel"
         cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv"})
 
+    # the inputs and outputs were made on the default stream: order the side
+    # stream after them before it touches them
+    torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for _ in range(args.warmup):
             if plan is not None:

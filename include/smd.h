@@ -100,27 +100,36 @@ typedef struct smd_kv_pool {
 /*
  * Cost model of the host split planner (aiter page, Summary part 1: the
  * split count minimises workgroup waves x per-wave KV time plus the
- * partial-write / stage-2 cost of splitting).  All times in picoseconds.
+ * partial-write / stage-2 cost of splitting).  All times in picoseconds.  A
+ * decode workgroup owns rows_per_wg query rows of one index row and one
+ * split; its waves_per_wg waves share the split's positions in steps of 16.
  *
- *   G        = ceil(M / min(M, 64)), M = num_heads * q_per_seq
- *   waves(s) = ceil(num_seqs * G * s / (num_cus * wg_per_cu))
- *   tiles(s) = ceil(ceil(kv_len / s) / 64)
- *   cost(s)  = waves(s) * (fixed + tile[kv_dtype] * tiles(s))
- *            + (s > 1) * (merge + part * num_seqs * M * s)
+ *   M         = num_heads * q_per_seq,   G = ceil(M / rows_per_wg)
+ *   slots     = num_cus * wg_per_cu
+ *   wgs(s)    = num_seqs * G * s
+ *   waves(s)  = ceil(wgs(s) / slots),    busy(s) = min(wgs(s), slots)
+ *   chunk(s)  = roundup(ceil(kv_len / s), 64)   (the split length)
+ *   steps(s)  = ceil(ceil(min(chunk(s), kv_len) / 16) / waves_per_wg)
+ *   cost(s)   = waves(s) * (fixed + steps(s) * (step + floor(step_load * busy(s) / slots)))
+ *             + (s > 1) * (merge + part * num_seqs * M * s)
  *
  * s ranges over [1, min(cap, ceil(kv_len / 64))] with cap = short_cap when
  * kv_len < long_kv, else long_cap (both <= SMD_MAX_SPLITS); the smallest s of
- * minimum cost wins.
+ * minimum cost wins.  bf16 and fp8 pools run the same kernel and share the
+ * coefficients.
  */
 typedef struct smd_plan_model {
-  int64_t fixed_ps;   /* per-wave fixed cost                  */
-  int64_t tile_ps[2]; /* per 64-row tile, by kv dtype          */
-  int64_t merge_ps;   /* fixed cost of the stage-2 merge       */
-  int64_t part_ps;    /* per query row and split (write+read)  */
-  int32_t wg_per_cu;  /* resident decode workgroups per CU     */
-  int32_t short_cap;  /* split cap when kv_len < long_kv        */
-  int32_t long_cap;   /* split cap otherwise                   */
-  int32_t long_kv;    /* threshold between the two caps        */
+  int64_t fixed_ps;     /* per workgroup wave: prologue, wave merge, epilogue */
+  int64_t step_ps;      /* per 16-position step of a wave, GPU otherwise idle */
+  int64_t step_load_ps; /* added per step with every slot busy (pro rata)     */
+  int64_t merge_ps;     /* fixed cost of the stage-2 merge                    */
+  int64_t part_ps;      /* per query row and split (partial write + read)     */
+  int32_t rows_per_wg;  /* query rows per decode workgroup                    */
+  int32_t waves_per_wg; /* waves sharing one workgroup's positions            */
+  int32_t wg_per_cu;    /* resident decode workgroups per CU                  */
+  int32_t short_cap;    /* split cap when kv_len < long_kv                    */
+  int32_t long_cap;     /* split cap otherwise                                */
+  int32_t long_kv;      /* threshold between the two caps                     */
 } smd_plan_model;
 
 /*

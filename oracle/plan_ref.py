@@ -27,43 +27,59 @@ def _cdiv(a: int, b: int) -> int:
 @dataclass
 class PlanModel:
     fixed_ps: int
-    tile_ps: tuple  # (bf16, fp8)
+    step_ps: int
+    step_load_ps: int
     merge_ps: int
     part_ps: int
+    rows_per_wg: int
+    waves_per_wg: int
     wg_per_cu: int
     short_cap: int
     long_cap: int
     long_kv: int
 
 
+def split_cost(s: int, num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, num_cus: int,
+               model: PlanModel) -> int:
+    """Modelled picoseconds of a plan with s splits:
+
+        waves(s) * (fixed + steps(s) * (step + floor(step_load * busy(s) / slots)))
+          + [s > 1] * (merge + part * num_seqs * M * s)
+
+    M = num_heads * q_per_seq query rows per index row, G = ceil(M / rows_per_wg)
+    workgroups per index row and split, slots = num_cus * wg_per_cu,
+    wgs(s) = num_seqs * G * s, waves(s) = ceil(wgs(s) / slots), busy(s) = min(wgs(s), slots),
+    chunk(s) = the split length of ``ref.split_bounds`` (ceil(kv_len / s) rounded up
+    to 64), steps(s) = ceil(ceil(min(chunk(s), kv_len) / 16) / waves_per_wg)."""
+    cus = num_cus if num_cus > 0 else 256
+    M = num_heads * q_per_seq
+    G = _cdiv(M, model.rows_per_wg)
+    slots = cus * model.wg_per_cu
+    wgs = num_seqs * G * s
+    waves = _cdiv(wgs, slots)
+    busy = min(wgs, slots)
+    chunk = _cdiv(_cdiv(kv_len, s), SPLIT_ALIGN) * SPLIT_ALIGN
+    steps = _cdiv(_cdiv(min(chunk, kv_len), 16), model.waves_per_wg)
+    cost = waves * (model.fixed_ps + steps * (model.step_ps + model.step_load_ps * busy // slots))
+    if s > 1:
+        cost += model.merge_ps + model.part_ps * num_seqs * M * s
+    return cost
+
+
 def num_kv_splits(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv_dtype: int, num_cus: int,
                   model: PlanModel) -> int:
-    """argmin over s of
-
-        waves(s) * (fixed + tile[dtype] * tiles(s)) + [s > 1] * (merge + part * num_seqs * M * s)
-
-    with M = num_heads * q_per_seq query rows per index row, G = ceil(M / min(M, 64))
-    row groups, waves(s) = ceil(num_seqs * G * s / (num_cus * wg_per_cu)) and
-    tiles(s) = ceil(ceil(kv_len / s) / 64).  s runs over 1 .. min(cap, ceil(kv_len / 64)),
-    cap = short_cap below long_kv indices, long_cap from there on; ties keep the
-    smaller s.  Empty problems plan one split."""
+    """argmin of ``split_cost`` over s = 1 .. min(cap, ceil(kv_len / 64)), cap =
+    short_cap below long_kv indices, long_cap from there on; ties keep the
+    smaller s.  Empty problems plan one split; kv_dtype does not enter the cost."""
     if min(num_seqs, num_heads, q_per_seq, kv_len) < 0:
         raise ValueError("negative size")
     if num_seqs == 0 or kv_len == 0 or num_heads == 0 or q_per_seq == 0:
         return 1
-    cus = num_cus if num_cus > 0 else 256
-    M = num_heads * q_per_seq
-    G = _cdiv(M, min(M, 64))
-    slots = cus * model.wg_per_cu
     cap = model.short_cap if kv_len < model.long_kv else model.long_cap
     cap = min(cap, _cdiv(kv_len, SPLIT_ALIGN))
     best_s, best = 1, None
     for s in range(1, cap + 1):
-        waves = _cdiv(num_seqs * G * s, slots)
-        tiles = _cdiv(_cdiv(kv_len, s), SPLIT_ALIGN)
-        cost = waves * (model.fixed_ps + model.tile_ps[kv_dtype] * tiles)
-        if s > 1:
-            cost += model.merge_ps + model.part_ps * num_seqs * M * s
+        cost = split_cost(s, num_seqs, num_heads, q_per_seq, kv_len, num_cus, model)
         if best is None or cost < best:
             best, best_s = cost, s
     return best_s

@@ -57,9 +57,12 @@ class PlanModel(ctypes.Structure):
 
     _fields_ = [
         ("fixed_ps", ctypes.c_int64),
-        ("tile_ps", ctypes.c_int64 * 2),
+        ("step_ps", ctypes.c_int64),
+        ("step_load_ps", ctypes.c_int64),
         ("merge_ps", ctypes.c_int64),
         ("part_ps", ctypes.c_int64),
+        ("rows_per_wg", ctypes.c_int32),
+        ("waves_per_wg", ctypes.c_int32),
         ("wg_per_cu", ctypes.c_int32),
         ("short_cap", ctypes.c_int32),
         ("long_cap", ctypes.c_int32),

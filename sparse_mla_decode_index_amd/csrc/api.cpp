@@ -88,17 +88,6 @@ static int check_pool(const char *fn, const smd_kv_pool *kv, DecodeArgs &a) {
   return SMD_OK;
 }
 
-// Row-block workgroups of the fp8 kernel: query-row blocks of 16 per
-// workgroup (RB; the 4 waves split the 512 dims DS = 4 / RB ways).  Start from
-// the widest block that M allows and narrow it while the grid has fewer
-// workgroups than the GPU has CUs: the narrower blocks re-read KV rows from L2
-// but keep every CU busy.
-static int row_blocks_for(int32_t M, int64_t units, int num_cus) {
-  int rb = M >= 64 ? 4 : M / 16;
-  while (rb > 1 && units * (M / (16 * rb)) < num_cus) rb /= 2;
-  return rb;
-}
-
 }  // namespace smd
 
 using namespace smd;
@@ -189,15 +178,14 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
   a.S = num_splits;
   a.num_units = rows * num_splits;
   const bool fp8 = kv->dtype == SMD_KV_FP8_E4M3_UE8M0;
-  const int rb = fp8 ? row_blocks_for(M, (int64_t)rows * num_splits, 256) : 1;
-  a.G = M / (16 * rb);
+  a.G = M / 16;
   a.part_o = need_partials ? partial_o : nullptr;
   a.part_lse = need_partials ? partial_lse : nullptr;
   a.out = need_partials ? nullptr : (uint16_t *)out;
   a.lse = need_partials ? nullptr : lse;
   a.hilo = out == nullptr;  // FP32 partials are the result only without out
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = fp8 ? launch_decode_rb(a, rb, true, st) : launch_decode(a, false, st);
+  hipError_t e = launch_decode(a, fp8, st);
   if (e != hipSuccess) {
     set_error("%s: decode launch failed: %s", fn, hipGetErrorString(e));
     return SMD_ERR_HIP;

@@ -1,5 +1,5 @@
-// Device core of sparse MLA decode for gfx950 (MI355X), shared by the
-// split-KV kernel and the persistent kernel.
+// Row-block device core of the persistent sparse MLA decode for gfx950
+// (MI355X).
 //
 // What is computed (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
 // decode on gfx950", Design): per query row, a 512-wide dot product (448 NoPE

@@ -14,7 +14,7 @@ using namespace ks;
 // Work decomposition: a workgroup (8 waves, two per SIMD) owns one index row
 // b, one block g of 16 query rows and one split r; its waves share the split's
 // positions (interleaved half-tiles of 16) and merge their states at the end.
-template <bool PACKED, bool P_HILO>
+template <int FMT, bool P_HILO>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) ks8::Smem sm;
 
@@ -42,12 +42,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int64_t qrow = (int64_t)tok * a.H + head;  // [T, H] row
 
   // the first indices and rows are in flight while Q^T is staged
-  ks8::Pipe pipe;
-  ks8::prime<PACKED>(a, row_idx, p0, p1, wave, L, pipe);
+  ks8::Pipe<FMT> pipe;
+  ks8::prime<FMT>(a, row_idx, p0, p1, wave, L, pipe);
   ks8::stage_q(a, qrow, wave, L, sm);
   __syncthreads();
   ks::State st;
-  ks8::attend<PACKED, P_HILO>(a, row_idx, p0, p1, wave, L, (const uint8_t SMD_LDS *)&sm.q[0],
+  ks8::attend<FMT, P_HILO>(a, row_idx, p0, p1, wave, L, (const uint8_t SMD_LDS *)&sm.q[0],
                               (uint8_t SMD_LDS *)&sm.buf[wave][0], st, pipe);
   ks::f32x4 o[8];
   float mm, ll;
@@ -63,53 +63,101 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
-// Stage-2 merge: one wave per [T,H] row, 8 dims per lane.  The partials are
-// read four at a time (their lse and o in one round trip) and folded into a
-// running max / sum, so a plan of up to four splits costs one round trip.
+// Stage-2 merge.  WPR waves share one [T,H] row (8 dims per lane); wave w of
+// the row folds the partials r = w, w + WPR, ... into a running max / sum,
+// reading CH of them (their lse and o) per round trip, so a plan of up to
+// CH * WPR splits costs one round trip.  The row's waves then combine
+// their states through LDS and the row's first wave writes the result.
+template <int WPR, int CH>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po,
                                                     const float *__restrict__ plse, int rows, int H,
                                                     int S, const float *__restrict__ sink,
                                                     uint16_t *__restrict__ out, float *__restrict__ lse) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (row >= rows) return;
+  __shared__ float xo[4][8][64];  // [wave][dim][lane]: bank-conflict-free
+  __shared__ float xs[4][2];      // [wave] {max, sum}
+  const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
-  const int head = row % H;
-  const float *ls = plse + (int64_t)row * S;
-  const float *src = po + (int64_t)row * S * kDim + lane * 8;
-  const float sk = sink ? sink[head] : -INFINITY;
-  float mx = sk;   // running max of the lse terms (natural log)
-  float z = 1.f;   // sum of e^(term - mx) (the sink, or nothing yet)
-  if (mx == -INFINITY) z = 0.f;
+  const int w = wave % WPR;
+  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
+  const bool live = row < rows;
+  float mx = -INFINITY;  // running max of the lse terms (natural log)
+  float z = 0.f;         // sum of e^(term - mx)
   float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int r0 = 0; r0 < S; r0 += 4) {
-    float l[4];
-    f32x4 v[4][2];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const int r = min(r0 + c, S - 1);  // clamped: every chunk issues the same loads
-      l[c] = r0 + c < S ? ls[r] : -INFINITY;
-      v[c][0] = *(const f32x4 *)(src + (int64_t)r * kDim);
-      v[c][1] = *(const f32x4 *)(src + (int64_t)r * kDim + 4);
+  if (live) {
+    const float *ls = plse + (int64_t)row * S;
+    const float *src = po + (int64_t)row * S * kDim + lane * 8;
+    if (w == 0 && sink) {
+      mx = sink[row % H];
+      z = mx == -INFINITY ? 0.f : 1.f;
     }
-    const float cm = fmaxf(fmaxf(l[0], l[1]), fmaxf(l[2], l[3]));
-    if (cm == -INFINITY) continue;
-    const float nm = fmaxf(mx, cm);
-    const float rescale = mx == -INFINITY ? 0.f : exp2_fast((mx - nm) * kLog2e);
-    z *= rescale;
+    for (int r0 = w; r0 < S; r0 += CH * WPR) {
+      float l[CH];
+      f32x4 v[CH][2];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) o[i] *= rescale;
+      for (int c = 0; c < CH; ++c) {
+        const int rr = r0 + c * WPR;
+        const int r = rr < S ? rr : r0;  // clamped: every chunk issues the same loads
+        l[c] = rr < S ? ls[r] : -INFINITY;
+        v[c][0] = *(const f32x4 *)(src + (int64_t)r * kDim);
+        v[c][1] = *(const f32x4 *)(src + (int64_t)r * kDim + 4);
+      }
+      float cm = l[0];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float w = l[c] == -INFINITY ? 0.f : exp2_fast((l[c] - nm) * kLog2e);
-      z += w;
+      for (int c = 1; c < CH; ++c) cm = fmaxf(cm, l[c]);
+      if (cm == -INFINITY) continue;
+      const float nm = fmaxf(mx, cm);
+      const float rescale = mx == -INFINITY ? 0.f : exp2_fast((mx - nm) * kLog2e);
+      z *= rescale;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        o[i] += w * v[c][0][i];
-        o[4 + i] += w * v[c][1][i];
+      for (int i = 0; i < 8; ++i) o[i] *= rescale;
+#pragma unroll
+      for (int c = 0; c < CH; ++c) {
+        const float e = l[c] == -INFINITY ? 0.f : exp2_fast((l[c] - nm) * kLog2e);
+        z += e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          o[i] += e * v[c][0][i];
+          o[4 + i] += e * v[c][1][i];
+        }
+      }
+      mx = nm;
+    }
+  }
+  if constexpr (WPR > 1) {
+    if (w != 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xo[wave][i][lane] = o[i];
+      if (lane == 0) {
+        xs[wave][0] = mx;
+        xs[wave][1] = z;
+      }
+    }
+    __syncthreads();
+    if (w != 0 || !live) return;
+    float m2[WPR], z2[WPR];
+    float nm = mx;
+#pragma unroll
+    for (int k = 1; k < WPR; ++k) {
+      m2[k] = xs[wave + k][0];
+      z2[k] = xs[wave + k][1];
+      nm = fmaxf(nm, m2[k]);
+    }
+    if (nm != -INFINITY) {
+      const float e0 = mx == -INFINITY ? 0.f : exp2_fast((mx - nm) * kLog2e);
+      z *= e0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[i] *= e0;
+#pragma unroll
+      for (int k = 1; k < WPR; ++k) {
+        const float e = m2[k] == -INFINITY ? 0.f : exp2_fast((m2[k] - nm) * kLog2e);
+        z += e * z2[k];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] += e * xo[wave + k][i][lane];
       }
     }
     mx = nm;
   }
+  if (!live) return;
   uint16_t *dst = out + (int64_t)row * kDim + lane * 8;
   if (mx == -INFINITY) {
     *(u32x4 *)dst = u32x4{0u, 0u, 0u, 0u};
@@ -125,31 +173,45 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   if (lse && lane == 0) lse[row] = mx + logf(z);
 }
 
-template <bool PACKED, bool P_HILO>
+template <int FMT, bool P_HILO>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_kernel<PACKED, P_HILO>), grid, dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<FMT, P_HILO>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
-// bf16 pools (fp8 pools go to launch_decode_rb).  Partials the caller reads
-// are written with the two-part P (FP32-partial precision); partials that only
-// feed the merge into bf16, and the direct bf16 output, use a single bf16 P.
-// a.G must be M / 16.
+template <int FMT>
+static hipError_t launch_decode_f(const DecodeArgs &a, hipStream_t stream) {
+  return a.hilo ? launch_decode_t<FMT, true>(a, stream) : launch_decode_t<FMT, false>(a, stream);
+}
+
+// Partials the caller reads are written with the two-part P (FP32-partial
+// precision); partials that only feed the merge into bf16, and the direct
+// bf16 output, use a single bf16 P.  a.G must be M / 16.
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream) {
-  if (fp8) return hipErrorInvalidValue;
-  if (a.hilo) return a.packed ? launch_decode_t<true, true>(a, stream) : launch_decode_t<false, true>(a, stream);
-  return a.packed ? launch_decode_t<true, false>(a, stream) : launch_decode_t<false, false>(a, stream);
+  if (fp8) return launch_decode_f<ks8::kFp8>(a, stream);
+  return a.packed ? launch_decode_f<ks8::kBf16Packed>(a, stream) : launch_decode_f<ks8::kBf16Split>(a, stream);
+}
+
+template <int WPR, int CH>
+static hipError_t launch_merge_t(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
+                                 int32_t S, const float *sink, uint16_t *out, float *lse,
+                                 hipStream_t stream) {
+  const int rpb = 4 / WPR;
+  const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
+  hipLaunchKernelGGL((merge_kernel<WPR, CH>), grid, dim3(256), 0, stream, part_o, part_lse, rows, H, S,
+                     sink, out, lse);
+  return hipGetLastError();
 }
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
                         hipStream_t stream) {
-  const dim3 grid((unsigned)((rows + 3) / 4));
-  hipLaunchKernelGGL(merge_kernel, grid, dim3(256), 0, stream, part_o, part_lse, rows, H, S, sink,
-                     out, lse);
-  return hipGetLastError();
+  if (S <= 4) return launch_merge_t<1, 4>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  if (S <= 8) return launch_merge_t<2, 4>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  if (S <= 16) return launch_merge_t<4, 4>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  return launch_merge_t<4, 8>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
 }
 
 }  // namespace smd

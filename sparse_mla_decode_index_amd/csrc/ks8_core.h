@@ -1,4 +1,4 @@
-// Device core of the wave-independent sparse MLA decode (bf16 pools).
+// Device core of the wave-independent sparse MLA decode.
 //
 // A workgroup of 8 waves owns one block of 16 query rows (heads x MTP
 // positions sharing one index list) and a range of index positions, cut into
@@ -13,6 +13,9 @@
 //     flight while half-tile k is computed;
 //   - one 16 KiB LDS buffer per wave; PV runs per half-tile with
 //     v_mfma_f32_16x16x16_bf16 (k = 16 rows), V^T by ds_read_b64_tr_b16.
+// fp8 pools are gathered as e4m3 bytes + UE8M0 codes + bf16 RoPE and
+// dequantised in registers on the way into LDS (e4m3 x 2^(code-127) is exact
+// in bf16), so the buffer layout and everything after it are the bf16 ones.
 // LDS: 16 KiB + 8 x 16 KiB = 144 KiB per workgroup.
 #pragma once
 
@@ -55,11 +58,53 @@ __device__ __forceinline__ void stage_q(const DecodeArgs &a, int64_t qrow, int w
   }
 }
 
-// Gathered rows of a half-tile into the wave's buffer: row i, chunk `lane`
-// -> physical chunk lane ^ swz(i) (one row of 64 distinct chunks per store).
+// Row formats of the pool: bf16 with RoPE right after NoPE in one row, bf16
+// with RoPE in its own array, fp8 e4m3 NoPE + UE8M0 codes + bf16 RoPE.
+enum Fmt { kBf16Packed = 0, kBf16Split = 1, kFp8 = 2 };
+
+template <int FMT>
+struct Gathered {
+  typedef Half type;
+};
+template <>
+struct Gathered<kFp8> {
+  typedef ks::Half8 type;
+};
+
+// Gathered bf16 rows of a half-tile into the wave's buffer: row i, chunk
+// `lane` -> physical chunk lane ^ swz(i) (one row of 64 distinct chunks per
+// store).
 __device__ __forceinline__ void store_half(const Half &h, uint8_t SMD_LDS *buf, const Lane &L) {
 #pragma unroll
   for (int i = 0; i < 16; ++i) *(u32x4 SMD_LDS *)(buf + i * ks::kRowBytes + ((L.lane ^ ks::swz(i)) << 4)) = h.v[i];
+}
+
+// Gathered fp8 rows, dequantised, into the same layout: the 16 e4m3 bytes of
+// block t, quarter s become bf16 chunks 8t + 2s and 8t + 2s + 1; RoPE piece u
+// is chunk 56 + 4u + s.  Odd rows store their odd chunk first, so each
+// 8-lane group of a store covers 8 distinct 16-byte bank groups.
+__device__ __forceinline__ void store_half(const ks::Half8 &h, uint8_t SMD_LDS *buf, const Lane &L) {
+  const int r = L.lane >> 2, s = L.lane & 3;
+  const int sw = ks::swz(r);
+  const int e = r & 1;
+  uint8_t SMD_LDS *row = buf + r * ks::kRowBytes;
+#pragma unroll
+  for (int t = 0; t < 7; ++t) {
+    const float sc = ks::ue8m0_scale((h.code[t >> 2] >> (8 * (t & 3))) & 0xffu);
+    u32x4 c[2];
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      c[w >> 1][2 * (w & 1)] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)h.n[t][w], sc, false));
+      c[w >> 1][2 * (w & 1) + 1] =
+          __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)h.n[t][w], sc, true));
+    }
+    const int c0 = 8 * t + 2 * s;
+    *(u32x4 SMD_LDS *)(row + (((c0 + e) ^ sw) << 4)) = e ? c[1] : c[0];
+    *(u32x4 SMD_LDS *)(row + (((c0 + 1 - e) ^ sw) << 4)) = e ? c[0] : c[1];
+  }
+#pragma unroll
+  for (int u = 0; u < 2; ++u) *(u32x4 SMD_LDS *)(row + (((56 + 4 * u + s) ^ sw) << 4)) = h.r[u];
 }
 
 // QK over the half-tile in `buf`: A operands from the buffer, B operands from
@@ -110,30 +155,62 @@ __device__ __forceinline__ void pv_half(const uint8_t SMD_LDS *buf, bf16x4 p, bf
 // The gather pipeline of one wave: the register set with the rows of the
 // next half-tile to compute, the indices of the half-tile after it, and the
 // valid-row bits of the rows in the register set.
+template <int FMT>
 struct Pipe {
-  Half h;
-  int32_t i_next;
+  typename Gathered<FMT>::type h;
+  int32_t i_next;  // index of row row_of<FMT>(L) of the next-but-one half-tile
   uint32_t vb;
   int nk;  // half-tiles of this wave
 };
 
+// The half-tile row whose index this lane holds (and, for fp8, gathers).
+template <int FMT>
+__device__ __forceinline__ int row_of(const Lane &L) {
+  return FMT == kFp8 ? (L.lane >> 2) : L.r;
+}
+
 // Half-tile k of this wave covers positions p0 + 16*(wave + 8k) + 0..15.
+template <int FMT>
 __device__ __forceinline__ int pos_of(int p0, int wave, int k, const Lane &L) {
-  return p0 + kHalf * (wave + kWaves * k) + L.r;
+  return p0 + kHalf * (wave + kWaves * k) + row_of<FMT>(L);
+}
+
+// Valid-row bits of a half-tile (bit r = row r) from each lane's validity of
+// row row_of<FMT>(lane); fp8 lanes 4r..4r+3 share row r.
+template <int FMT>
+__device__ __forceinline__ uint32_t row_bits(bool v) {
+  uint64_t b = __ballot(v);
+  if constexpr (FMT == kFp8) {
+    b &= 0x1111111111111111ull;
+    b = (b | (b >> 3)) & 0x0303030303030303ull;
+    b = (b | (b >> 6)) & 0x000F000F000F000Full;
+    b = (b | (b >> 12)) & 0x000000FF000000FFull;
+    b = b | (b >> 24);
+  }
+  return (uint32_t)b & 0xffffu;
+}
+
+template <int FMT>
+__device__ __forceinline__ void issue(const DecodeArgs &a, uint32_t idx, bool valid, const Lane &L,
+                                      typename Gathered<FMT>::type &h) {
+  if constexpr (FMT == kFp8)
+    ks::issue_half_fp8(a, idx, valid, L, h);
+  else
+    ks::issue_half<FMT == kBf16Packed>(a, idx, valid, L, h);
 }
 
 // Start the pipeline: indices of half-tiles 0 and 1, rows of half-tile 0.
-template <bool PACKED>
+template <int FMT>
 __device__ __forceinline__ void prime(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                      const Lane &L, Pipe &pp) {
+                                      const Lane &L, Pipe<FMT> &pp) {
   const int nh = (p1 - p0 + kHalf - 1) / kHalf;
   pp.nk = nh > wave ? (nh - wave + kWaves - 1) / kWaves : 0;
   if (pp.nk == 0) return;
-  const int32_t i0 = row_idx[min(pos_of(p0, wave, 0, L), p1 - 1)];
-  pp.i_next = row_idx[min(pos_of(p0, wave, 1, L), p1 - 1)];
-  const bool v0 = pos_of(p0, wave, 0, L) < p1 && (uint32_t)i0 < a.num_rows32;
-  ks::issue_half<PACKED>(a, (uint32_t)i0, v0, L, pp.h);
-  pp.vb = (uint32_t)__ballot(v0) & 0xffffu;
+  const int32_t i0 = row_idx[min(pos_of<FMT>(p0, wave, 0, L), p1 - 1)];
+  pp.i_next = row_idx[min(pos_of<FMT>(p0, wave, 1, L), p1 - 1)];
+  const bool v0 = pos_of<FMT>(p0, wave, 0, L) < p1 && (uint32_t)i0 < a.num_rows32;
+  issue<FMT>(a, (uint32_t)i0, v0, L, pp.h);
+  pp.vb = row_bits<FMT>(v0);
 }
 
 // One wave's sweep over its half-tiles of [p0, p1), from a primed pipeline.
@@ -142,17 +219,17 @@ __device__ __forceinline__ void prime(const DecodeArgs &a, const int32_t *row_id
 // indices of k+2, then QK, softmax and PV of k from LDS while k+1 is in
 // flight.  Every step issues the same loads (positions past p1 read the zero
 // row), so the compiler's wait counts stay exact.
-template <bool PACKED, bool P_HILO, int PASS>
+template <int FMT, bool P_HILO, int PASS>
 __device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
                                       const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st,
-                                      Pipe &pp) {
+                                      Pipe<FMT> &pp) {
   for (int k = 0; k < pp.nk; ++k) {
     store_half(pp.h, buf, L);
-    const bool vn = pos_of(p0, wave, k + 1, L) < p1 && (uint32_t)pp.i_next < a.num_rows32;
-    ks::issue_half<PACKED>(a, (uint32_t)pp.i_next, vn, L, pp.h);
-    pp.i_next = row_idx[min(pos_of(p0, wave, k + 2, L), p1 - 1)];
+    const bool vn = pos_of<FMT>(p0, wave, k + 1, L) < p1 && (uint32_t)pp.i_next < a.num_rows32;
+    issue<FMT>(a, (uint32_t)pp.i_next, vn, L, pp.h);
+    pp.i_next = row_idx[min(pos_of<FMT>(p0, wave, k + 2, L), p1 - 1)];
     const uint32_t vb = pp.vb;
-    pp.vb = (uint32_t)__ballot(vn) & 0xffffu;
+    pp.vb = row_bits<FMT>(vn);
     const f32x4 s = qk_lds(qs, buf, L);
     bf16x4 p, pl;
     ks::softmax_half<PASS, P_HILO>(s, vb, a.scale_log2, L, st, p, pl);
@@ -162,16 +239,16 @@ __device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_id
 
 // The wave's attention over its share of [p0, p1) from a primed pipeline: the
 // main sweep, and the exact-max redo when a score overflowed the reference.
-template <bool PACKED, bool P_HILO>
+template <int FMT, bool P_HILO>
 __device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
                                        const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st,
-                                       Pipe &pp) {
+                                       Pipe<FMT> &pp) {
 #pragma unroll
   for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_ref = -INFINITY;
   st.l_run = 0.f;
   st.overflow = false;
-  sweep<PACKED, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
+  sweep<FMT, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
   if (__ballot(st.overflow)) {  // wave-uniform
     // Rare: a score ran far above its row's first-half-tile max.  Redo this
     // wave's share with the exact max (a scores-only sweep) as the reference.
@@ -179,10 +256,10 @@ __device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_i
     for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m_ref = -INFINITY;
     st.l_run = 0.f;
-    prime<PACKED>(a, row_idx, p0, p1, wave, L, pp);
-    sweep<PACKED, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
-    prime<PACKED>(a, row_idx, p0, p1, wave, L, pp);
-    sweep<PACKED, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
+    prime<FMT>(a, row_idx, p0, p1, wave, L, pp);
+    sweep<FMT, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
+    prime<FMT>(a, row_idx, p0, p1, wave, L, pp);
+    sweep<FMT, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
   }
 }
 

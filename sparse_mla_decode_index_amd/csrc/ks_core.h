@@ -1,5 +1,5 @@
 // Building blocks of the wave-independent sparse MLA decode for gfx950
-// (MI355X), bf16 pools: row gather, softmax step, output epilogues.  The
+// (MI355X): row gather (bf16 and fp8 pools), softmax step, output epilogues.  The
 // kernel's work decomposition and pipeline are in ks8_core.h.
 //
 // What is computed (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
@@ -150,6 +150,41 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, uint32_t idx, bo
       h.v[i] = *(const u32x4 SMD_GLOBAL *)p;
     }
   }
+}
+
+// UE8M0 code -> fp32 scale 2^(code-127); code 0 is the subnormal 2^-127.
+__device__ __forceinline__ float ue8m0_scale(uint32_t code) {
+  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
+}
+
+// Gathered data of one fp8 half-tile.  A row is 448 e4m3 NoPE bytes with one
+// UE8M0 code per 64-byte block, plus 64 bf16 RoPE dims (128 bytes).  Lane l
+// serves row l / 4 and the quarter s = l % 4 of every 64-byte piece of it:
+// n[t] = NoPE bytes 64t + 16s .. +16 (code block t), r[u] = RoPE bytes
+// 64u + 16s .. +16, code = the row's 8 code bytes (7 codes + pad).  Four
+// consecutive lanes read 64 contiguous bytes of one row.
+struct Half8 {
+  u32x4 n[7];
+  u32x4 r[2];
+  uint32_t code[2];
+};
+
+// Loads of one fp8 half-tile; idx / valid are those of row lane / 4.  Masked
+// rows read the zero row (e4m3 zeros, code 0).
+__device__ __forceinline__ void issue_half_fp8(const DecodeArgs &a, uint32_t idx, bool valid, const Lane &L,
+                                               Half8 &h) {
+  typedef const uint8_t SMD_GLOBAL *gptr;
+  const uint8_t *z = g_zero_row;
+  const gptr pn = (gptr)(uintptr_t)(valid ? a.kv_nope + (uint64_t)idx * (uint64_t)a.nope_stride_b : z);
+  const gptr pr = (gptr)(uintptr_t)(valid ? a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b : z);
+  const gptr pc = (gptr)(uintptr_t)(valid ? a.kv_scale + (uint64_t)idx * (uint64_t)a.scale_stride_b : z);
+  const int off = 16 * (L.lane & 3);
+#pragma unroll
+  for (int t = 0; t < 7; ++t) h.n[t] = *(const u32x4 SMD_GLOBAL *)(pn + off + 64 * t);
+#pragma unroll
+  for (int u = 0; u < 2; ++u) h.r[u] = *(const u32x4 SMD_GLOBAL *)(pr + off + 64 * u);
+  h.code[0] = *(const uint32_t SMD_GLOBAL *)pc;
+  h.code[1] = *(const uint32_t SMD_GLOBAL *)(pc + 4);
 }
 
 // Per-wave softmax state and O^T accumulator: acc[d][i] = sum over rows of

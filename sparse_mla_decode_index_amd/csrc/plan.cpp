@@ -1,7 +1,9 @@
 // Host split planner (aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and
 // persistent decode kernel", Summary part 1): the split count minimises
 // workgroup waves x per-wave KV time plus the partial-write / merge cost of
-// splitting, from the call's sizes only.  The caps follow the vLLM page
+// splitting, from the call's sizes only.  The per-wave time is that of this
+// library's decode workgroup: a fixed part plus one step per 16 positions of
+// each wave's share, a step costing more the fuller the GPU.  The caps follow the vLLM page
 // "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on gfx950", Design:
 // at most four splits for short index lists, up to 32 for long ones.
 //
@@ -16,12 +18,17 @@ namespace smd {
 void set_error(const char *fmt, ...);
 }
 
-// MI355X coefficients, fitted to the decode kernels of this library.
+// MI355X coefficients, fitted (log-time least squares) to graph-timed decode
+// + merge over T in {1, 4, 16, 64}, H in {16, 64, 128}, 384 to 65664 indices
+// and s in {1, 2, 4, 8, 16, 32}, bf16 and fp8 pools.
 static const smd_plan_model kDefaultModel = {
-    /*fixed_ps=*/3000000,
-    /*tile_ps=*/{700000, 900000},
-    /*merge_ps=*/2500000,
-    /*part_ps=*/500,
+    /*fixed_ps=*/7194000,
+    /*step_ps=*/1971000,
+    /*step_load_ps=*/569000,
+    /*merge_ps=*/4065000,
+    /*part_ps=*/287,
+    /*rows_per_wg=*/16,
+    /*waves_per_wg=*/8,
     /*wg_per_cu=*/1,
     /*short_cap=*/4,
     /*long_cap=*/32,
@@ -54,16 +61,16 @@ extern "C" int smd_plan_num_kv_splits_model(int32_t num_seqs, int32_t num_heads,
     smd::set_error("smd_plan_num_kv_splits: unknown kv_dtype %d", kv_dtype);
     return SMD_ERR_UNSUPPORTED;
   }
-  if (model->wg_per_cu < 1 || model->short_cap < 1 || model->long_cap < 1 ||
-      model->short_cap > SMD_MAX_SPLITS || model->long_cap > SMD_MAX_SPLITS) {
-    smd::set_error("smd_plan_num_kv_splits: invalid model caps");
+  if (model->wg_per_cu < 1 || model->rows_per_wg < 1 || model->waves_per_wg < 1 || model->short_cap < 1 ||
+      model->long_cap < 1 || model->short_cap > SMD_MAX_SPLITS || model->long_cap > SMD_MAX_SPLITS) {
+    smd::set_error("smd_plan_num_kv_splits: invalid model (sizes and caps must be >= 1, caps <= %d)",
+                   SMD_MAX_SPLITS);
     return SMD_ERR_INVALID_ARG;
   }
   if (num_seqs == 0 || kv_len == 0 || num_heads == 0 || q_per_seq == 0) return 1;
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   const int64_t M = (int64_t)num_heads * q_per_seq;
-  const int64_t m_wg = M < 64 ? M : 64;
-  const int64_t G = ceil_div(M, m_wg);
+  const int64_t G = ceil_div(M, model->rows_per_wg);
   const int64_t slots = cus * model->wg_per_cu;
   const int64_t cap_len = kv_len < model->long_kv ? model->short_cap : model->long_cap;
   const int64_t cap_tiles = ceil_div(kv_len, SMD_SPLIT_ALIGN);
@@ -71,9 +78,14 @@ extern "C" int smd_plan_num_kv_splits_model(int32_t num_seqs, int32_t num_heads,
   int best_s = 1;
   int64_t best_cost = INT64_MAX;
   for (int64_t s = 1; s <= cap; ++s) {
-    const int64_t waves = ceil_div((int64_t)num_seqs * G * s, slots);
-    const int64_t tiles = ceil_div(ceil_div(kv_len, s), SMD_SPLIT_ALIGN);
-    int64_t cost = waves * (model->fixed_ps + model->tile_ps[kv_dtype] * tiles);
+    const int64_t wgs = (int64_t)num_seqs * G * s;
+    const int64_t waves = ceil_div(wgs, slots);
+    const int64_t busy = wgs < slots ? wgs : slots;
+    const int64_t chunk = ceil_div(ceil_div(kv_len, s), SMD_SPLIT_ALIGN) * SMD_SPLIT_ALIGN;
+    const int64_t len = chunk < kv_len ? chunk : kv_len;
+    const int64_t steps = ceil_div(ceil_div(len, 16), model->waves_per_wg);
+    const int64_t step = model->step_ps + model->step_load_ps * busy / slots;
+    int64_t cost = waves * (model->fixed_ps + steps * step);
     if (s > 1) cost += model->merge_ps + model->part_ps * (int64_t)num_seqs * M * s;
     if (cost < best_cost) {
       best_cost = cost;

@@ -46,10 +46,6 @@ struct DecodeArgs {
 // 16 query rows); a.G = M / 16 blocks per index row.
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
 
-// Launch the row-block split-KV decode (fp8 pools): rb query-row blocks of 16
-// per workgroup (rb in {1, 2, 4}; a.G = M / (16 rb) row groups per index row).
-hipError_t launch_decode_rb(const DecodeArgs &a, int rb, bool fp8, hipStream_t stream);
-
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
                         hipStream_t stream);

@@ -49,19 +49,16 @@ def test_split_bounds_rejects_bad_args():
 
 
 def _model_pair(rng):
-    fixed = int(rng.integers(1, 10_000_000))
-    tiles = (int(rng.integers(1, 3_000_000)), int(rng.integers(1, 3_000_000)))
-    merge = int(rng.integers(0, 10_000_000))
-    part = int(rng.integers(0, 5_000))
-    wg = int(rng.integers(1, 4))
-    sc = int(rng.integers(1, 33))
-    lc = int(rng.integers(1, 33))
-    lk = int(rng.integers(1, 20000))
+    v = dict(fixed_ps=int(rng.integers(1, 10_000_000)), step_ps=int(rng.integers(1, 3_000_000)),
+             step_load_ps=int(rng.integers(0, 3_000_000)), merge_ps=int(rng.integers(0, 10_000_000)),
+             part_ps=int(rng.integers(0, 5_000)), rows_per_wg=int(rng.choice([16, 32, 64])),
+             waves_per_wg=int(rng.choice([1, 4, 8])), wg_per_cu=int(rng.integers(1, 4)),
+             short_cap=int(rng.integers(1, 33)), long_cap=int(rng.integers(1, 33)),
+             long_kv=int(rng.integers(1, 20000)))
     c = smd.PlanModel()
-    c.fixed_ps, c.merge_ps, c.part_ps = fixed, merge, part
-    c.tile_ps[0], c.tile_ps[1] = tiles
-    c.wg_per_cu, c.short_cap, c.long_cap, c.long_kv = wg, sc, lc, lk
-    return c, plan_ref.PlanModel(fixed, tiles, merge, part, wg, sc, lc, lk)
+    for k, x in v.items():
+        setattr(c, k, x)
+    return c, plan_ref.PlanModel(**v)
 
 
 def test_planner_formula_bit_exact_vs_oracle():
@@ -265,3 +262,12 @@ def test_persistent_empty_batch_launches_nothing():
 
 def test_persistent_workspace_reset_rejects_null():
     assert smd.lib().smd_persistent_workspace_reset(None, 100, None) == -1
+
+
+def test_library_default_model_is_the_fitted_one():
+    """The built-in coefficients are those the oracle's worked examples use."""
+    from tests.test_oracle_persistent import _fitted_model
+    d = smd.plan_default_model()
+    m = _fitted_model()
+    for k in m.__dataclass_fields__:
+        assert getattr(d, k) == getattr(m, k), k

@@ -82,15 +82,22 @@ def test_mtp_shared_rows(gpu, qps):
     run_case(w, gpu, 2)
 
 
-def test_merge_kernel_alone(gpu):
-    """smd_merge_partials on oracle-computed partials (including empty splits)."""
-    w = wl.dense_workload("merge", T=3, H=32, kv_dtype="bf16", pool_rows=1024, topk=200, invalid=2, seed=61)
+@pytest.mark.parametrize("S,topk,sink", [(6, 200, True), (13, 700, True), (13, 130, False), (32, 2100, True),
+                                          (32, 130, False)])
+def test_merge_kernel_alone(gpu, S, topk, sink):
+    """smd_merge_partials on oracle-computed partials: one to four waves per
+    row, including splits that are all empty and a token with no valid index."""
+    w = wl.dense_workload("merge", T=3, H=32, kv_dtype="bf16", pool_rows=4096, topk=topk, invalid=2, seed=61 + S)
+    w.arrays["indices"][1, :] = -1
     po, pl = ref.sparse_mla_decode_partials(w.arrays["q_nope"], w.arrays["q_rope"], oracle_pool(w),
-                                            w.arrays["indices"], w.softmax_scale, 6)
-    o_ref, l_ref = ref.merge_partials(po, pl, w.arrays["sink"])
+                                            w.arrays["indices"], w.softmax_scale, S)
+    o_ref, l_ref = ref.merge_partials(po, pl, w.arrays["sink"] if sink else None)
+    print(f"merge S={S} topk={topk} sink={sink}", flush=True)
     out, lse = smd.merge_partials(torch.from_numpy(po.astype(np.float32)).to(gpu),
                                   torch.from_numpy(pl.astype(np.float32)).to(gpu),
-                                  torch.from_numpy(w.arrays["sink"]).to(gpu))
+                                  torch.from_numpy(w.arrays["sink"]).to(gpu) if sink else None)
     torch.cuda.synchronize()
     check_out(out, o_ref)
     check_lse(lse, l_ref)
+    if not sink:
+        assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))

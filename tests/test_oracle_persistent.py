@@ -153,3 +153,56 @@ def test_piecewise_merge_equals_unsplit(seed, P):
         np.testing.assert_allclose(ml, want_l[b * 2:(b + 1) * 2], rtol=0, atol=1e-12)
     assert set(parts) == {b for b in range(len(ptr) - 1) if ptr[b + 1] > ptr[b]}
     assert written.sum() == 2 * len(parts)
+
+
+# ----------------------------------------------------------------------------
+# host split planner: the cost formula worked out by hand
+# ----------------------------------------------------------------------------
+def _fitted_model():
+    return pr.PlanModel(fixed_ps=7194000, step_ps=1971000, step_load_ps=569000, merge_ps=4065000,
+                              part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
+                              long_cap=32, long_kv=8192)
+
+
+def test_planner_cost_worked_example_short_list():
+    """8 index rows x 64 heads x 2176 indices on 256 slots, every term by hand.
+    G = 64 / 16 = 4 workgroups per row and split, so wgs(s) = 32 s, one wave.
+      s=1: chunk 2176, 136 half-tiles -> 17 steps, step 1971000 + 569000*32//256
+           = 2042125; 7194000 + 17*2042125                         = 41910125
+      s=2: chunk 1088 -> 68 -> 9 steps, step 2113250; 7194000 + 9*2113250
+           + merge 4065000 + 287*8*64*2                            = 30572138
+      s=3: ceil(2176/3) = 726 -> chunk 768 -> 48 -> 6 steps, step 2184375;
+           7194000 + 6*2184375 + 4065000 + 287*8*64*3                = 24806082
+      s=4: 544 -> chunk 576 -> 36 -> 5 steps, step 2255500;
+           7194000 + 5*2255500 + 4065000 + 287*8*64*4                = 23124276
+    and the short-list cap (2176 < 8192) stops at s = 4."""
+    m = _fitted_model()
+    want = {1: 41910125, 2: 30572138, 3: 24806082, 4: 23124276}
+    for s, c in want.items():
+        assert pr.split_cost(s, 8, 64, 1, 2176, 256, m) == c, s
+    assert pr.num_kv_splits(8, 64, 1, 2176, 0, 256, m) == 4
+
+
+def test_planner_cost_worked_example_long_list_and_waves():
+    """One row x 128 heads x 65664 indices (long cap 32):
+      s=32: chunk ceil(65664/32)=2052 -> 2112, 132 half-tiles -> 17 steps, all
+            256 slots busy (step 2540000): 7194000 + 17*2540000 + 4065000
+            + 287*128*32                                            = 55614552
+      s=31: 2119 -> 2176 -> 136 -> 17 steps, 248 busy, step 1971000 +
+            569000*248//256 = 2522218: 7194000 + 17*2522218 + 4065000
+            + 287*128*31                                            = 55275522
+      s=30: 2189 -> 2240 -> 140 -> 18 steps, step 2504437            = 57440946
+    so 31 splits beat 32 (and every s <= 30 needs 18 or more steps).
+    300 rows x 128 heads x 2048 indices: s=1 runs 2400 workgroups in 10 waves
+    of 16 full-load steps, 10*(7194000 + 16*2540000) = 478340000; s=2 needs 19
+    waves of 8 steps plus the merge, 19*27514000 + 4065000 + 287*300*128*2
+    = 548872600."""
+    m = _fitted_model()
+    assert pr.split_cost(32, 1, 128, 1, 65664, 256, m) == 55614552
+    assert pr.split_cost(31, 1, 128, 1, 65664, 256, m) == 55275522
+    assert pr.split_cost(30, 1, 128, 1, 65664, 256, m) == 57440946
+    assert pr.num_kv_splits(1, 128, 1, 65664, 0, 256, m) == 31
+    assert pr.split_cost(1, 300, 128, 1, 2048, 256, m) == 478340000
+    assert pr.split_cost(2, 300, 128, 1, 2048, 256, m) == 548872600
+    assert pr.num_kv_splits(300, 128, 1, 2048, 1, 256, m) == 1
+
