@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--kernel-launches", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--matrix", type=str, default=None,
+                    help="comma-separated matrix variants (bf16_h128, fp8_h128, bf16_h16): print the T x ctx "
+                         "table of whole-step times instead of the JSON line")
     return ap.parse_args()
 
 
@@ -175,8 +178,65 @@ def graph_time(torch, stream, fn, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
+def matrix(args):
+    """T x ctx table: per cell the whole step (planner + decode + merge), timed
+    like the JSON line's step, and the step's fraction of the binding roof.
+    One progress line per cell, then one markdown table per variant."""
+    import torch
+    import sparse_mla_decode_index_amd as smd
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.Stream()
+    for var in args.matrix.split(","):
+        cells = {}
+        for ctx in wl.MATRIX_CTX:  # the pool depends on ctx only: reuse it over T
+            for T in wl.MATRIX_T:
+                w = wl.matrix_cell(T, ctx, var)
+                d = to_device(w, dev)
+                H = w.num_heads
+                K = w.arrays["indices"].shape[1]
+                kvd = smd.KV_BF16 if w.kv_dtype == "bf16" else smd.KV_FP8_E4M3_UE8M0
+                s = smd.plan_num_kv_splits(w.num_index_rows, H, K, 1, kvd)
+                out = torch.empty((T, H, 512), dtype=torch.bfloat16, device=dev)
+                lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+                po = torch.empty((T, H, s, 512), dtype=torch.float32, device=dev) if s > 1 else None
+                pl = torch.empty((T, H, s), dtype=torch.float32, device=dev) if s > 1 else None
+
+                def step():
+                    smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"],
+                                          w.softmax_scale, num_splits=smd.plan_num_kv_splits(
+                                              w.num_index_rows, H, K, 1, kvd), out=out, lse=lse,
+                                          partial_o=po, partial_lse=pl)
+
+                torch.cuda.synchronize()  # inputs were made on the default stream
+                with torch.cuda.stream(stream):
+                    step()
+                torch.cuda.synchronize()
+                us = graph_time(torch, stream, step, args.kernel_launches)
+                by, fl = wl.algorithmic_bytes(w), wl.algorithmic_flops(w)
+                hbm = by / (us * 1e3) / HBM_PEAK_GBS
+                mfma = fl / (us * 1e6) / BF16_MFMA_PEAK_TFS
+                cells[T, ctx] = f"{us:.1f} ({s}) {max(hbm, mfma) * 100:.1f}% {'H' if hbm >= mfma else 'M'}"
+                print(f"{var} T={T} ctx={ctx} K={K}: {cells[T, ctx]}", flush=True)
+                del d, out, lse, po, pl
+            torch.cuda.empty_cache()
+        print(f"\n{var}: µs per step (splits), fraction of the binding roof (H = HBM, M = bf16 MFMA)\n")
+        print("| T \\ ctx | " + " | ".join(str(c) for c in wl.MATRIX_CTX) + " |")
+        print("|---|" + "---|" * len(wl.MATRIX_CTX))
+        for T in wl.MATRIX_T:
+            print(f"| {T} | " + " | ".join(cells[T, c] for c in wl.MATRIX_CTX) + " |")
+        print("", flush=True)
+
+
 def main():
     args = parse()
+    if args.matrix:
+        if args.gpus != 1:
+            print("this build runs on exactly one GPU; --gpus must be 1")
+            sys.exit(2)
+        matrix(args)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
                           "n_gpus_requested": args.gpus}))

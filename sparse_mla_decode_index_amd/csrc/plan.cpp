@@ -32,7 +32,7 @@ static const smd_plan_model kDefaultModel = {
     /*wg_per_cu=*/1,
     /*short_cap=*/4,
     /*long_cap=*/32,
-    /*long_kv=*/8192,
+    /*long_kv=*/4096,
 };
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }

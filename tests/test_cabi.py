@@ -79,7 +79,7 @@ def test_default_planner_properties():
             for K in [64, 384, 2176, 6528, 32128, 65664]:
                 s = smd.plan_num_kv_splits(rows, H, K)
                 assert 1 <= s <= 32
-                if K < 8192:
+                if K < 4096:
                     assert s <= 4          # short workloads: at most four splits
                 assert s <= -(-K // 64)    # never more splits than 64-row chunks
     # depends only on its arguments

@@ -161,7 +161,7 @@ def test_piecewise_merge_equals_unsplit(seed, P):
 def _fitted_model():
     return pr.PlanModel(fixed_ps=7194000, step_ps=1971000, step_load_ps=569000, merge_ps=4065000,
                               part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
-                              long_cap=32, long_kv=8192)
+                              long_cap=32, long_kv=4096)
 
 
 def test_planner_cost_worked_example_short_list():
@@ -175,7 +175,7 @@ def test_planner_cost_worked_example_short_list():
            7194000 + 6*2184375 + 4065000 + 287*8*64*3                = 24806082
       s=4: 544 -> chunk 576 -> 36 -> 5 steps, step 2255500;
            7194000 + 5*2255500 + 4065000 + 287*8*64*4                = 23124276
-    and the short-list cap (2176 < 8192) stops at s = 4."""
+    and the short-list cap (2176 < 4096) stops at s = 4."""
     m = _fitted_model()
     want = {1: 41910125, 2: 30572138, 3: 24806082, 4: 23124276}
     for s, c in want.items():

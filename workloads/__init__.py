@@ -44,10 +44,12 @@ SCALE_STRIDE = 8  # 7 codes + 1 pad byte per row
 # generator, not part of the decode)
 # ----------------------------------------------------------------------------
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bits, round to nearest even; NaN -> 0x7FC0.  The 32-bit
+    sum cannot wrap for any non-NaN input (the largest, -inf, gives 0xFF807FFF)."""
     x = np.ascontiguousarray(x, dtype=np.float32)
     u = x.view(np.uint32)
     nan = np.isnan(x)
-    r = ((u.astype(np.uint64) + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16)).astype(np.uint16)
     if nan.any():
         r[nan] = 0x7FC0
     return r
@@ -152,17 +154,33 @@ def _set_invalid(rng, idx: np.ndarray, count: int):
         idx[r, pos] = -1
 
 
+_POOL_CACHE: dict = {}
+
+
+def _own_pool(kv_dtype: str, n: int, seed: int) -> dict:
+    """A pool drawn from its own generator (PCG64(seed)); the last one of each
+    (dtype, size, seed) is kept, so table sweeps over T reuse it."""
+    key = (kv_dtype, n, seed)
+    if key not in _POOL_CACHE:
+        _POOL_CACHE.clear()
+        _POOL_CACHE[key] = _pool(np.random.Generator(np.random.PCG64(seed)), kv_dtype, n)
+    return _POOL_CACHE[key]
+
+
 def dense_workload(name: str, *, T: int, H: int, kv_dtype: str, pool_rows: int, topk: int,
                    swa: int = 0, invalid: int = 0, sorted_topk: bool = False, q_per_seq: int = 1,
-                   seed: int = 0, softmax_scale: float | None = None, note: str = "") -> Workload:
+                   seed: int = 0, pool_seed: int | None = None, softmax_scale: float | None = None,
+                   note: str = "") -> Workload:
     """One index row per q_per_seq tokens: `topk` indices drawn uniformly without
     replacement from the pool, then the last `swa` pool rows appended in order,
     then `invalid` positions per row set to -1 (uniformly chosen).
 
-    Draw order: q_nope, q_rope, pool, sink, indices, invalid positions."""
+    Draw order: q_nope, q_rope, pool, sink, indices, invalid positions.  With
+    pool_seed the pool comes from its own generator instead (and is not drawn
+    from the main one)."""
     rng = np.random.Generator(np.random.PCG64(seed))
     q_nope, q_rope = _queries(rng, T, H)
-    pool = _pool(rng, kv_dtype, pool_rows)
+    pool = _pool(rng, kv_dtype, pool_rows) if pool_seed is None else _own_pool(kv_dtype, pool_rows, pool_seed)
     sink = rng.standard_normal(H, dtype=np.float32)
     R = T // q_per_seq
     K = topk + swa
@@ -250,12 +268,16 @@ MATRIX_VARIANTS = {"bf16_h128": ("bf16", 128), "fp8_h128": ("fp8", 128), "bf16_h
 
 def matrix_cell(T: int, ctx: int, variant: str = "bf16_h128", seed: int | None = None) -> Workload:
     """T x context cell: pool of `ctx` rows, K = ctx/16 sorted unique top-k + the
-    last 128 rows as a sliding window, q and sink ~ N(0,1), one index row per token."""
+    last 128 rows as a sliding window, q and sink ~ N(0,1), one index row per token.
+    The pool depends on (ctx, variant) only: seed 100 + ctx index (+ 50 for fp8);
+    q, sink and indices on the cell: seed 1000 + 10 * T index + ctx index."""
     kv_dtype, H = MATRIX_VARIANTS[variant]
+    ic = MATRIX_CTX.index(ctx)
     if seed is None:
-        seed = 100 + 10 * MATRIX_T.index(T) + MATRIX_CTX.index(ctx)
+        seed = 1000 + 10 * MATRIX_T.index(T) + ic
     return dense_workload(f"{variant} T={T} ctx={ctx}", T=T, H=H, kv_dtype=kv_dtype, pool_rows=ctx,
-                          topk=ctx // 16, swa=128, sorted_topk=True, seed=seed)
+                          topk=ctx // 16, swa=128, sorted_topk=True, seed=seed,
+                          pool_seed=100 + ic + (50 if kv_dtype == "fp8" else 0))
 
 
 def algorithmic_bytes(w: Workload) -> int:
