@@ -5,6 +5,7 @@
 #include <limits.h>
 #include <math.h>
 #include <stdarg.h>
+#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -86,6 +87,15 @@ static int check_pool(const char *fn, const smd_kv_pool *kv, DecodeArgs &a) {
              nope_b < (int64_t)UINT32_MAX;
   a.row_stride32 = a.packed ? (uint32_t)nope_b : 0u;
   return SMD_OK;
+}
+
+// The dim-split kernel (32 query rows per workgroup) moves less through LDS
+// per unit of work but has half as many workgroups: it is used when its grid
+// still fills the GPU (256 CUs, one workgroup each).
+static bool use_pairs(int32_t M, int64_t units) {
+  if (M % 32 != 0) return false;
+  if (const char *e = getenv("SMD_DECODE_PAIRS")) return atoi(e) != 0;
+  return units * (M / 32) >= 256;
 }
 
 }  // namespace smd
@@ -178,14 +188,15 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
   a.S = num_splits;
   a.num_units = rows * num_splits;
   const bool fp8 = kv->dtype == SMD_KV_FP8_E4M3_UE8M0;
-  a.G = M / 16;
+  const bool pairs = use_pairs(M, (int64_t)rows * num_splits);
+  a.G = M / (pairs ? 32 : 16);
   a.part_o = need_partials ? partial_o : nullptr;
   a.part_lse = need_partials ? partial_lse : nullptr;
   a.out = need_partials ? nullptr : (uint16_t *)out;
   a.lse = need_partials ? nullptr : lse;
   a.hilo = out == nullptr;  // FP32 partials are the result only without out
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_decode(a, fp8, st);
+  hipError_t e = launch_decode(a, fp8, pairs, st);
   if (e != hipSuccess) {
     set_error("%s: decode launch failed: %s", fn, hipGetErrorString(e));
     return SMD_ERR_HIP;

@@ -5,6 +5,7 @@
 // an index row covers a contiguous range of its positions and writes an FP32
 // partial (o_r, lse_r); the merge reweights the partials by their log-sum-exps
 // and folds in the sink.  One split writes the bf16 output directly.
+#include "kp_core.h"
 #include "ks8_core.h"
 
 namespace smd {
@@ -60,6 +61,70 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   } else {
     ks::write_partial(o, mm, ll, a.part_o + (qrow * a.S + r) * kDim + dcol,
                       lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
+  }
+}
+
+// Work decomposition of the dim-split variant: a workgroup (8 waves = 4 pairs
+// of dim halves) owns one index row b, one block g of 32 query rows and one
+// split r; a.G = M / 32.  Mapping to the grid as in decode_kernel.
+template <int FMT, bool P_HILO>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kp_kernel(DecodeArgs a) {
+  __shared__ __attribute__((aligned(1024))) kp::Smem sm;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int per = 8 * a.G;
+  const int g = (int)(blockIdx.x % per) / 8;
+  const int u = (int)(blockIdx.x / per) * 8 + (int)(blockIdx.x % 8);
+  if (u >= a.num_units) return;
+  const int b = u / a.S;
+  const int r = u % a.S;
+  const int p0 = min(r * a.chunk, a.topk);
+  const int p1 = min(p0 + a.chunk, a.topk);
+  const int32_t *row_idx = a.indices + (int64_t)b * a.indices_stride;
+
+  const ks::Lane L = ks::make_lane(lane);
+  const kp::PLane P = kp::make_plane(L);
+  int64_t qrow[2];
+  int head[2];
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const int m = g * kp::kRows + 16 * qb + L.j;
+    head[qb] = m % a.H;
+    qrow[qb] = (int64_t)(b * a.qps + m / a.H) * a.H + head[qb];
+  }
+  const int k = wave >> 1, h = wave & 1;
+
+  kp::Pipe<FMT> pipe;
+  if (p1 > p0) kp::prime<FMT>(a, row_idx, p0, p1, k, h, L, pipe);  // workgroup-uniform
+  kp::stage_q(a, qrow, wave, L, sm);
+  if (lane == 0) sm.flag[wave] = 0;
+  __syncthreads();
+  kp::State st;
+  kp::attend<FMT, P_HILO>(a, row_idx, p0, p1, wave, L, P, sm, st, pipe);
+  if (!kp::merge_pairs(sm, wave, L, st)) return;
+  // waves 0 and 1: dims [256h, 256h + 256) of both blocks
+  const int dcol = 256 * h + 4 * L.g;
+  const bool lse_lane = L.g == 0 && h == 0;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const float l = ks::group_sum(st.l_run[qb]);
+    ks::f32x4 lo[8], hi[8];
+#pragma unroll
+    for (int d = 0; d < 8; ++d) {
+      lo[d] = st.acc[2 * d + qb];
+      hi[d] = st.acc[2 * (8 + d) + qb];
+    }
+    if (a.S == 1 && a.out != nullptr) {
+      uint16_t *dst = a.out + qrow[qb] * kDim + dcol;
+      const float sk = a.sink ? a.sink[head[qb]] : -INFINITY;
+      ks::write_direct(lo, st.m_ref[qb], l, sk, dst, (a.lse != nullptr && lse_lane) ? a.lse + qrow[qb] : nullptr);
+      ks::write_direct(hi, st.m_ref[qb], l, sk, dst + 128, nullptr);
+    } else {
+      float *dst = a.part_o + (qrow[qb] * a.S + r) * kDim + dcol;
+      ks::write_partial(lo, st.m_ref[qb], l, dst, lse_lane ? a.part_lse + qrow[qb] * a.S + r : nullptr);
+      ks::write_partial(hi, st.m_ref[qb], l, dst + 128, nullptr);
+    }
   }
 }
 
@@ -181,17 +246,29 @@ static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+template <int FMT, bool P_HILO>
+static hipError_t launch_decode_kp_t(const DecodeArgs &a, hipStream_t stream) {
+  const int blocks8 = (a.num_units + 7) / 8;
+  const dim3 grid((unsigned)(blocks8 * 8 * a.G));
+  hipLaunchKernelGGL((decode_kp_kernel<FMT, P_HILO>), grid, dim3(512), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <int FMT>
-static hipError_t launch_decode_f(const DecodeArgs &a, hipStream_t stream) {
+static hipError_t launch_decode_f(const DecodeArgs &a, bool pairs, hipStream_t stream) {
+  if (pairs) return a.hilo ? launch_decode_kp_t<FMT, true>(a, stream) : launch_decode_kp_t<FMT, false>(a, stream);
   return a.hilo ? launch_decode_t<FMT, true>(a, stream) : launch_decode_t<FMT, false>(a, stream);
 }
 
 // Partials the caller reads are written with the two-part P (FP32-partial
 // precision); partials that only feed the merge into bf16, and the direct
-// bf16 output, use a single bf16 P.  a.G must be M / 16.
-hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream) {
-  if (fp8) return launch_decode_f<ks8::kFp8>(a, stream);
-  return a.packed ? launch_decode_f<ks8::kBf16Packed>(a, stream) : launch_decode_f<ks8::kBf16Split>(a, stream);
+// bf16 output, use a single bf16 P.  a.G must be M / 32 with pairs (the
+// dim-split kernel), M / 16 without.
+hipError_t launch_decode(const DecodeArgs &a, bool fp8, bool pairs, hipStream_t stream) {
+  static_assert((int)kp::kBf16Packed == (int)ks8::kBf16Packed && (int)kp::kFp8 == (int)ks8::kFp8, "formats");
+  if (fp8) return launch_decode_f<ks8::kFp8>(a, pairs, stream);
+  return a.packed ? launch_decode_f<ks8::kBf16Packed>(a, pairs, stream)
+                  : launch_decode_f<ks8::kBf16Split>(a, pairs, stream);
 }
 
 template <int WPR, int CH>

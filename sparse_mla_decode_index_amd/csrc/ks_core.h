@@ -198,25 +198,26 @@ struct State {
 
 enum Pass { kPassMain = 0, kPassMax = 1, kPassFixed = 2 };
 
-// Softmax weights of one half-tile for this lane's 4 kv rows (4g..4g+3);
-// vbits bit r = row r of the half-tile is valid.  Returns P as bf16 (and the
-// low part of the two-part P with P_HILO).
+// Softmax weights of one half-tile for this lane's 4 kv rows (4g..4g+3) of
+// one query row, given that row's running state (reference max, this lane's
+// share of the sum, overflow flag); vbits bit r = row r of the half-tile is
+// valid.  Returns P as bf16 (and the low part of the two-part P with P_HILO).
 template <int PASS, bool P_HILO>
-__device__ __forceinline__ void softmax_half(f32x4 s, uint32_t vbits, float scale_log2, const Lane &L, State &st,
-                                             bf16x4 &pb, bf16x4 &pl) {
+__device__ __forceinline__ void softmax_step(f32x4 s, uint32_t vbits, float scale_log2, const Lane &L, float &m_ref,
+                                             float &l_run, bool &overflow, bf16x4 &pb, bf16x4 &pl) {
   float x[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) x[i] = ((vbits >> (4 * L.g + i)) & 1) ? s[i] * scale_log2 : -INFINITY;
   float tmax = group_max(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
   if constexpr (PASS == kPassMax) {
-    st.m_ref = fmaxf(st.m_ref, tmax);
+    m_ref = fmaxf(m_ref, tmax);
     return;
   }
   if constexpr (PASS == kPassMain) {
-    if (st.m_ref == -INFINITY) st.m_ref = tmax;  // nothing accumulated yet for this row
-    st.overflow |= tmax > st.m_ref + kRefSlackLog2;
+    if (m_ref == -INFINITY) m_ref = tmax;  // nothing accumulated yet for this row
+    overflow |= tmax > m_ref + kRefSlackLog2;
   }
-  const float m_use = st.m_ref == -INFINITY ? 0.f : st.m_ref;
+  const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
   float psum = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
@@ -227,7 +228,13 @@ __device__ __forceinline__ void softmax_half(f32x4 s, uint32_t vbits, float scal
     // about 16 significant bits of p instead of 8 (FP32-partial precision).
     if constexpr (P_HILO) pl[i] = (__bf16)(p - (float)pb[i]);
   }
-  st.l_run += psum;
+  l_run += psum;
+}
+
+template <int PASS, bool P_HILO>
+__device__ __forceinline__ void softmax_half(f32x4 s, uint32_t vbits, float scale_log2, const Lane &L, State &st,
+                                             bf16x4 &pb, bf16x4 &pl) {
+  softmax_step<PASS, P_HILO>(s, vbits, scale_log2, L, st.m_ref, st.l_run, st.overflow, pb, pl);
 }
 
 // Final bf16 output of one query row with the sink folded in:

@@ -43,8 +43,9 @@ struct DecodeArgs {
 };
 
 // Launch the split-KV decode: one workgroup per (index row, split, block of
-// 16 query rows); a.G = M / 16 blocks per index row.
-hipError_t launch_decode(const DecodeArgs &a, bool fp8, hipStream_t stream);
+// query rows).  Without pairs a block is 16 rows (a.G = M / 16); with pairs
+// (the dim-split kernel, M a multiple of 32) it is 32 rows (a.G = M / 32).
+hipError_t launch_decode(const DecodeArgs &a, bool fp8, bool pairs, hipStream_t stream);
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
