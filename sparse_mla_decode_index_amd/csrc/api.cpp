@@ -246,7 +246,10 @@ extern "C" int smd_merge_partials(const float *partial_o, const float *partial_l
 // ----------------------------------------------------------------------------
 // persistent, graph-safe variant
 // ----------------------------------------------------------------------------
-static int persist_rb(int32_t M) { return M >= 64 ? 4 : M / 16; }
+// Row blocks per workgroup of the persistent kernel: the largest of 4, 2, 1
+// that divides M / 16, so the 16*rb-row groups cover every query row.
+static int persist_rb(int32_t M) { return M % 64 == 0 ? 4 : (M % 32 == 0 ? 2 : 1); }
+static int32_t persist_groups(int32_t M) { return M / (16 * persist_rb(M)); }
 
 extern "C" int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, int32_t num_cus) {
   g_err[0] = 0;
@@ -256,7 +259,7 @@ extern "C" int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t 
   }
   const int32_t cus = num_cus > 0 ? num_cus : 256;
   const int32_t M = num_heads * q_per_seq;
-  const int32_t groups = (M + 63) / 64;
+  const int32_t groups = persist_groups(M);
   const int32_t p = cus / groups;
   return p < 1 ? 1 : (p > SMD_MAX_PARTITIONS ? SMD_MAX_PARTITIONS : p);
 }
@@ -355,7 +358,7 @@ extern "C" int smd_sparse_mla_decode_persistent(const void *q_nope, const void *
   a.qps = q_per_seq;
   a.M = M;
   a.S = 1;
-  a.G = M / (16 * rb);
+  a.G = persist_groups(M);
   a.out = (uint16_t *)out;
   a.lse = lse;
   pa.d = a;

@@ -9,9 +9,10 @@
 // tiles of all sequences are concatenated in (sequence, tile) order, and
 // partition p of P owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
 //
-// Grid: P partitions x G query-row groups (16*RB rows each).  Workgroup (p, g)
-// walks the sequences of partition p and attends row group g of each over the
-// piece of its index list that p owns.  A sequence inside one partition is
+// Grid: P partitions x G query-row groups of 16*RB rows, RB the largest of 4,
+// 2, 1 that divides M / 16.  Workgroup (p, g) walks the sequences of partition
+// p and attends row group g of each over the piece of its index list that p
+// owns.  A sequence inside one partition is
 // written directly.  A sequence spread over partitions fp..lp is split: each
 // piece writes an FP32 partial (o = O/l, lse = m + ln l) to its slot, releases
 // it with an agent-scope fence and bumps the arrival counter of (g, fp); the
@@ -34,9 +35,11 @@ PersistLayout persist_layout(int64_t M, int64_t P) {
   return l;
 }
 
-// Inclusive prefix sum over the 256 threads of the workgroup; `total` gets the
-// sum of all 256 values.  s_red holds 4 ints and is free again on return.
+// Inclusive prefix sum over the NT threads of the workgroup; `total` gets the
+// sum of all NT values.  s_red holds NT / 64 ints and is free again on return.
+template <int NT>
 __device__ __forceinline__ int block_incl_scan(int v, int *s_red, int &total) {
+  constexpr int NW = NT / 64;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
@@ -48,7 +51,7 @@ __device__ __forceinline__ int block_incl_scan(int v, int *s_red, int &total) {
   int off = 0;
   total = 0;
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
+  for (int w = 0; w < NW; ++w) {
     const int x = s_red[w];
     off += w < wave ? x : 0;
     total += x;
@@ -79,13 +82,14 @@ __device__ __forceinline__ bool part_empty(int p, int total, int P) {
 // order.  The piece of partition q sits in slot 2q, except the first piece,
 // which sits in slot 2fp+1 when the sequence is not the first of partition fp.
 // One wave per query row, 8 dims per lane; lane k looks at partition fp + k.
+template <int NW>
 __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g, int rows, int fp, int lp,
                                              int first_slot, int total) {
   const DecodeArgs &a = pa.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lp - fp + 1;  // partitions in the span (empty ones hold nothing)
   const size_t slot_floats = (size_t)a.M * 513;
-  for (int r = wave; r < rows; r += 4) {
+  for (int r = wave; r < rows; r += NW) {
     const int m = g * rows + r;
     const int tok = b * a.qps + m / a.H;
     const int head = m % a.H;
@@ -147,6 +151,59 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
   }
 }
 
+// The plan of partition p from the live kv_indptr: total tiles, this
+// partition's tile range [t0, t1), its first and last sequence and the first
+// global tile of its first sequence.  Row group 0 writes the descriptor.
+// Returns false (workgroup-uniform) when the partition owns no tile.
+template <int NT>
+__device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int g, int *s_red, int *s_first,
+                                               int *s_last, int &total, int &t0, int &t1, int &b_first, int &b_last,
+                                               int &start) {
+  const int32_t *ptr = pa.kv_indptr;
+  const int B = pa.B;
+  {
+    int loc = 0;
+    for (int b = threadIdx.x; b < B; b += NT) loc += seq_tiles(ptr, b);
+    block_incl_scan<NT>(loc, s_red, total);
+  }
+  t0 = (int)((int64_t)p * total / pa.P);
+  t1 = (int)((int64_t)(p + 1) * total / pa.P);
+  if (threadIdx.x == 0) {
+    s_first[0] = -1;
+    s_first[1] = 0;
+    *s_last = -1;
+  }
+  __syncthreads();
+  if (t0 < t1) {
+    int run = 0;
+    for (int base = 0; base < B; base += NT) {
+      const int b = base + (int)threadIdx.x;
+      const int tb = b < B ? seq_tiles(ptr, b) : 0;
+      int chunk;
+      const int st = run + block_incl_scan<NT>(tb, s_red, chunk) - tb;
+      if (tb > 0 && st <= t0 && t0 < st + tb) {
+        s_first[0] = b;
+        s_first[1] = st;
+      }
+      if (tb > 0 && st < t1 && t1 <= st + tb) *s_last = b;
+      run += chunk;
+      if (run >= t1) break;  // the same in every thread
+    }
+  }
+  __syncthreads();
+  b_first = s_first[0];
+  b_last = *s_last;
+  start = s_first[1];
+  if (g == 0 && threadIdx.x == 0) {
+    int32_t *d = pa.plan + 4 * p;
+    d[0] = t0;
+    d[1] = t1;
+    d[2] = b_first;
+    d[3] = b_last;
+  }
+  return t0 < t1;
+}
+
 template <int RB, bool FP8, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void persistent_kernel(PersistArgs pa) {
   constexpr int DS = 4 / RB;
@@ -172,50 +229,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int p = (int)(blockIdx.x / per) * 8 + (int)(blockIdx.x % 8);
   if (p >= pa.P) return;
   const int32_t *ptr = pa.kv_indptr;
-  const int B = pa.B;
 
-  // ---- the plan, from the live kv_indptr: total tiles, then this partition's
-  // tile range and its first and last sequence
-  int total;
-  {
-    int loc = 0;
-    for (int b = threadIdx.x; b < B; b += 256) loc += seq_tiles(ptr, b);
-    block_incl_scan(loc, s_red, total);
-  }
-  const int t0 = (int)((int64_t)p * total / pa.P);
-  const int t1 = (int)((int64_t)(p + 1) * total / pa.P);
-  if (threadIdx.x == 0) {
-    s_first[0] = -1;
-    s_first[1] = 0;
-    s_last = -1;
-  }
-  __syncthreads();
-  if (t0 < t1) {
-    int run = 0;
-    for (int base = 0; base < B; base += 256) {
-      const int b = base + (int)threadIdx.x;
-      const int tb = b < B ? seq_tiles(ptr, b) : 0;
-      int chunk;
-      const int st = run + block_incl_scan(tb, s_red, chunk) - tb;
-      if (tb > 0 && st <= t0 && t0 < st + tb) {
-        s_first[0] = b;
-        s_first[1] = st;
-      }
-      if (tb > 0 && st < t1 && t1 <= st + tb) s_last = b;
-      run += chunk;
-      if (run >= t1) break;  // the same in every thread
-    }
-  }
-  __syncthreads();
-  const int b_first = s_first[0], b_last = s_last;
-  if (g == 0 && threadIdx.x == 0) {
-    int32_t *d = pa.plan + 4 * p;
-    d[0] = t0;
-    d[1] = t1;
-    d[2] = b_first;
-    d[3] = b_last;
-  }
-  if (t0 >= t1) return;
+  int total, t0, t1, b_first, b_last, start;
+  if (!plan_partition<256>(pa, p, g, s_red, s_first, &s_last, total, t0, t1, b_first, b_last, start)) return;
 
   int qk_base[4], pv_base[8];
   lds_bases(j, grp, qk_base, pv_base);
@@ -225,7 +241,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int head = m % a.H;
   const size_t slot_floats = (size_t)a.M * 513;
 
-  int start = s_first[1];  // first global tile of sequence b
   for (int b = b_first; b <= b_last; ++b) {
     const int k0 = ptr[b];
     const int kb = max(ptr[b + 1] - k0, 0);
@@ -262,7 +277,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (s_arrived == (uint32_t)(pieces - 1)) {
         __threadfence();  // acquire the other pieces
         const int t0_fp = (int)((int64_t)fp * total / pa.P);
-        merge_pieces(pa, b, g, ROWS, fp, lp, 2 * fp + (start == t0_fp ? 0 : 1), total);
+        merge_pieces<4>(pa, b, g, ROWS, fp, lp, 2 * fp + (start == t0_fp ? 0 : 1), total);
         if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();  // s_arrived is rewritten by the next piece
@@ -286,6 +301,7 @@ static hipError_t launch_persistent_rb(const PersistArgs &a, bool fp8, hipStream
                     : launch_persistent_t<RB, false, false>(a, stream);
 }
 
+// rb query-row blocks of 16 per workgroup, a.d.G = M / (16 rb).
 hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream) {
   switch (rb) {
     case 1: return launch_persistent_rb<1>(a, fp8, stream);
