@@ -191,10 +191,11 @@ int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t 
  *  lse = sink_h (-inf without a sink).  topk == 0 or num_tokens == 0
  *  launches nothing.
  *  Kernel choice (results agree to the tolerances above, not bit for bit):
- *  workgroups of 16 query rows, or -- when num_heads * q_per_seq is a
- *  multiple of 32 and (num_tokens / q_per_seq) * num_splits * (M / 32) >= 256
- *  -- the dim-split kernel with 32 query rows per workgroup.  The environment
- *  variable SMD_DECODE_PAIRS=1 / 0 forces that choice (when M allows it).
+ *  workgroups of 16 query rows, or -- when M = num_heads * q_per_seq is a
+ *  multiple of 32 and, with W = (num_tokens / q_per_seq) * num_splits *
+ *  (M / 32), 7 * ceil(W / 256) < 4 * ceil(2W / 256) -- the dim-split kernel
+ *  with 32 query rows per workgroup.  The environment variable
+ *  SMD_DECODE_PAIRS=1 / 0 forces that choice (when M allows it).
  */
 int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
                           int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,

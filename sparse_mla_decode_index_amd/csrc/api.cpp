@@ -90,12 +90,17 @@ static int check_pool(const char *fn, const smd_kv_pool *kv, DecodeArgs &a) {
 }
 
 // The dim-split kernel (32 query rows per workgroup) moves less through LDS
-// per unit of work but has half as many workgroups: it is used when its grid
-// still fills the GPU (256 CUs, one workgroup each).
+// per unit of work but has half as many workgroups, each taking about 7/4 of
+// the time of a 16-row one (measured on full GPUs).  With one workgroup per
+// CU on 256 CUs it wins when 7/4 x its rounds of workgroups is below the
+// 16-row kernel's rounds: a full grid, and not a grid that spills a small
+// last round.
 static bool use_pairs(int32_t M, int64_t units) {
   if (M % 32 != 0) return false;
   if (const char *e = getenv("SMD_DECODE_PAIRS")) return atoi(e) != 0;
-  return units * (M / 32) >= 256;
+  const int64_t w = units * (M / 32);
+  const int64_t rounds_pairs = (w + 255) / 256, rounds_rows = (2 * w + 255) / 256;
+  return 7 * rounds_pairs < 4 * rounds_rows;
 }
 
 }  // namespace smd

@@ -1,7 +1,8 @@
 """GPU parity of the dim-split (wave-pair) decode kernel, through the C ABI.
 
 The library picks that kernel when the query rows per index row are a multiple
-of 32 and its grid of 32-row blocks fills the GPU; SMD_DECODE_PAIRS=1 forces it
+of 32 and its grid of 32-row blocks fills whole rounds of the GPU (the rule in
+the header); SMD_DECODE_PAIRS=1 forces it
 for smaller problems (0 forces the 16-row kernel), so the cases below run it on
 sizes the oracle finishes quickly.  The same bars as the other parity tests:
 bf16 out atol = rtol = 2e-2, FP32 partials and LSE 1e-3, the one-hot gather
