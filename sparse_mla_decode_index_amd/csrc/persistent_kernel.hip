@@ -266,7 +266,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int slot = 2 * p + (b == b_first ? 0 : 1);
       float *sb = pa.slots + slot * slot_floats;
       write_partial(w, l_tot, sb + (size_t)m * kDim + dcol, lse_lane ? sb + (size_t)a.M * kDim + m : nullptr);
-      __threadfence();  // release this piece (agent scope: other XCDs read it)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release this piece (other XCDs read it)
       __syncthreads();
       uint32_t *ctr = pa.counters + (size_t)g * pa.P + fp;
       if (threadIdx.x == 0) s_arrived = atomicAdd(ctr, 1u);
@@ -275,7 +275,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       // otherwise every partition holds at most one tile, so one per tile
       const int pieces = total >= pa.P ? lp - fp + 1 : tb;
       if (s_arrived == (uint32_t)(pieces - 1)) {
-        __threadfence();  // acquire the other pieces
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire the other pieces
         const int t0_fp = (int)((int64_t)fp * total / pa.P);
         merge_pieces<4>(pa, b, g, ROWS, fp, lp, 2 * fp + (start == t0_fp ? 0 : 1), total);
         if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
