@@ -188,6 +188,12 @@ def matrix(args):
 
     dev = torch.device("cuda:0")
     stream = torch.cuda.Stream()
+    # the launch floor: one-element fill kernels back to back in a graph
+    one = torch.zeros(1, device=dev)
+    torch.cuda.synchronize()
+    floor_us = graph_time(torch, stream, lambda: one.fill_(1.0), args.kernel_launches)
+    print(f"empty-launch floor: {floor_us:.2f} µs per launch (graph of {args.kernel_launches} one-element fills); "
+          "cells near it are launch-bound", flush=True)
     for var in args.matrix.split(","):
         cells = {}
         for ctx in wl.MATRIX_CTX:  # the pool depends on ctx only: reuse it over T

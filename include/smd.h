@@ -154,6 +154,15 @@ int smd_plan_num_kv_splits_model(int32_t num_seqs, int32_t num_heads, int32_t q_
 int smd_plan_default_model(smd_plan_model *model);
 
 /*
+ * Bytes of the FP32 partials a split-KV call with num_splits splits writes:
+ * partial_o [num_tokens, num_heads, num_splits, 512] plus partial_lse
+ * [num_tokens, num_heads, num_splits], i.e. num_tokens * num_heads *
+ * num_splits * 513 * 4.  Returns 0 for negative sizes or num_splits outside
+ * [1, SMD_MAX_SPLITS] (smd_last_error() says which).
+ */
+size_t smd_partials_bytes(int32_t num_tokens, int32_t num_heads, int32_t num_splits);
+
+/*
  * Index positions [*begin, *end) of split `split` out of num_splits over a
  * list of kv_len indices: chunk = roundup(ceil(kv_len / num_splits), 64),
  * split r covers [min(r*chunk, kv_len), min((r+1)*chunk, kv_len)).  Trailing

@@ -92,6 +92,8 @@ def lib() -> ctypes.CDLL:
     L.smd_plan_num_kv_splits_model.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(PlanModel)]
     L.smd_plan_default_model.restype = ctypes.c_int
     L.smd_plan_default_model.argtypes = [ctypes.POINTER(PlanModel)]
+    L.smd_partials_bytes.restype = ctypes.c_size_t
+    L.smd_partials_bytes.argtypes = [i32, i32, i32]
     L.smd_split_bounds.restype = ctypes.c_int
     L.smd_split_bounds.argtypes = [i32, i32, i32, ctypes.POINTER(i32), ctypes.POINTER(i32)]
     L.smd_sparse_mla_decode.restype = ctypes.c_int
@@ -212,6 +214,11 @@ def plan_num_kv_splits(num_seqs: int, num_heads: int, kv_len: int, q_per_seq: in
     return _check("smd_plan_num_kv_splits_model",
                   L.smd_plan_num_kv_splits_model(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype,
                                                  num_cus, ctypes.byref(model)))
+
+
+def partials_bytes(num_tokens: int, num_heads: int, num_splits: int) -> int:
+    """Bytes of partial_o + partial_lse for a split-KV call (0 on bad sizes)."""
+    return int(lib().smd_partials_bytes(num_tokens, num_heads, num_splits))
 
 
 def plan_default_model() -> PlanModel:
@@ -402,6 +409,7 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
     return out, lse
 
 __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
+           "partials_bytes",
            "sparse_mla_decode", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
            "PersistentWorkspace", "sparse_mla_decode_persistent", "lib", "library_path", "KV_BF16",
            "KV_FP8_E4M3_UE8M0"]

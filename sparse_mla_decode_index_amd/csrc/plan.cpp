@@ -37,6 +37,9 @@ static const smd_plan_model kDefaultModel = {
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// FP32 values per (token, head, split): 512 of o and one lse.
+static const int64_t kPartialFloats = 513;
+
 extern "C" int smd_plan_default_model(smd_plan_model *model) {
   if (!model) {
     smd::set_error("smd_plan_default_model: model is NULL");
@@ -120,4 +123,13 @@ extern "C" int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t spli
   *begin = (int32_t)a;
   *end = (int32_t)e;
   return SMD_OK;
+}
+
+extern "C" size_t smd_partials_bytes(int32_t num_tokens, int32_t num_heads, int32_t num_splits) {
+  if (num_tokens < 0 || num_heads < 0 || num_splits < 1 || num_splits > SMD_MAX_SPLITS) {
+    smd::set_error("smd_partials_bytes: num_tokens=%d num_heads=%d num_splits=%d out of range", num_tokens,
+                   num_heads, num_splits);
+    return 0;
+  }
+  return (size_t)num_tokens * (size_t)num_heads * (size_t)num_splits * (size_t)(kPartialFloats * 4);
 }

@@ -271,3 +271,12 @@ def test_library_default_model_is_the_fitted_one():
     m = _fitted_model()
     for k in m.__dataclass_fields__:
         assert getattr(d, k) == getattr(m, k), k
+
+
+def test_partials_bytes():
+    """513 fp32 values (o and lse) per token, head and split."""
+    assert smd.partials_bytes(8, 64, 4) == 8 * 64 * 4 * 513 * 4
+    assert smd.partials_bytes(1, 128, 32) == 128 * 32 * 2052
+    assert smd.partials_bytes(0, 16, 1) == 0
+    assert smd.partials_bytes(2, 16, 0) == 0 and "num_splits" in smd.lib().smd_last_error().decode()
+    assert smd.partials_bytes(2, 16, 33) == 0
