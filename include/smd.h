@@ -297,6 +297,30 @@ int smd_sparse_mla_decode_persistent(const void *q_nope, const void *q_rope, int
                                      size_t workspace_bytes, int32_t num_partitions, void *out,
                                      float *lse, void *stream);
 
+/*
+ * fp8/UE8M0 KV-cache writer: quantises bf16 latent rows into an fp8 pool
+ * (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on
+ * gfx950", Design: writers cap the UE8M0 codes at 254 and canonicalise RoPE
+ * NaNs).  For each 64-dim NoPE block b of a row: code c = clamp(ceil(log2(
+ * amax / 448)) + 127, 0, 254) with amax the largest |x| of the block (NaN
+ * ignored; c = 0 for a block of zeros), stored at scale[row][b]; each value
+ * becomes the OCP E4M3FN byte nearest to x * 2^(127 - c), ties to the even
+ * mantissa, non-saturating (values past 464 and infinities give NaN with
+ * their sign).  scale[row][7] = 0.  RoPE dims are copied, every NaN replaced
+ * by 0x7FC0.
+ *  kv        bf16 [num_rows, kv_stride]: NoPE dims 0..447, RoPE 448..511;
+ *            16-byte aligned, kv_stride >= 512 and a multiple of 8
+ *  slots     int32 [num_rows]: the pool row each input row is written to, or
+ *            NULL (row r -> pool row r).  Slots outside [0, pool->num_rows)
+ *            are skipped; valid slots must be distinct.
+ *  pool      an fp8 pool as the decode takes it (nope, rope, scale arrays and
+ *            strides); the writer writes into its arrays.
+ * Checks as the decode's pool checks; SMD_ERR_UNSUPPORTED for a bf16 pool.
+ * num_rows == 0 launches nothing.  Device memory only; no allocation.
+ */
+int smd_write_kv_fp8(const void *kv, int64_t kv_stride, int32_t num_rows, const int32_t *slots,
+                     const smd_kv_pool *pool, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

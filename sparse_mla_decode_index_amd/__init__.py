@@ -101,6 +101,8 @@ def lib() -> ctypes.CDLL:
                                         vp, f32, i32, vp, vp, vp, vp, vp]
     L.smd_merge_partials.restype = ctypes.c_int
     L.smd_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
+    L.smd_write_kv_fp8.restype = ctypes.c_int
+    L.smd_write_kv_fp8.argtypes = [vp, i64, i32, vp, ctypes.POINTER(_KVPool), vp]
     L.smd_persistent_default_partitions.restype = i32
     L.smd_persistent_default_partitions.argtypes = [i32, i32, i32]
     L.smd_persistent_workspace_bytes.restype = ctypes.c_size_t
@@ -299,6 +301,24 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
     return out, lse
 
 
+def write_kv_fp8(kv: torch.Tensor, pool: KVPool, slots: Optional[torch.Tensor] = None) -> None:
+    """fp8/UE8M0 cache writer: bf16 latent rows kv [n, 512] (unit column
+    stride) into the fp8 pool's arrays, row r to pool row slots[r] (int32 [n];
+    None: row r; rows outside the pool are skipped)."""
+    _need(kv, "kv", torch.bfloat16, device=pool.device)
+    if kv.dim() != 2 or kv.shape[1] != DIM or kv.stride(1) != 1:
+        raise ValueError("kv must be [n, 512] bf16 with unit column stride")
+    if pool.dtype != KV_FP8_E4M3_UE8M0:
+        raise ValueError("write_kv_fp8 writes into an fp8 pool")
+    n = kv.shape[0]
+    if slots is not None:
+        _need(slots, "slots", torch.int32, (n,), pool.device)
+    st = pool._struct()
+    rc = lib().smd_write_kv_fp8(kv.data_ptr() if n else None, kv.stride(0) if n else DIM, n, _ptr(slots),
+                                ctypes.byref(st), _stream(kv))
+    _check("smd_write_kv_fp8", rc)
+
+
 def merge_partials(partial_o: torch.Tensor, partial_lse: torch.Tensor, sink: Optional[torch.Tensor], *,
                    out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
     """Stage-2 merge of FP32 partials [T,H,s,512] + [T,H,s] into bf16 out and fp32 lse."""
@@ -409,7 +429,7 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
     return out, lse
 
 __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
-           "partials_bytes",
+           "partials_bytes", "write_kv_fp8",
            "sparse_mla_decode", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
            "PersistentWorkspace", "sparse_mla_decode_persistent", "lib", "library_path", "KV_BF16",
            "KV_FP8_E4M3_UE8M0"]

@@ -382,3 +382,51 @@ extern "C" int smd_sparse_mla_decode_persistent(const void *q_nope, const void *
   }
   return SMD_OK;
 }
+
+// ----------------------------------------------------------------------------
+// fp8/UE8M0 cache writer
+// ----------------------------------------------------------------------------
+extern "C" int smd_write_kv_fp8(const void *kv, int64_t kv_stride, int32_t num_rows, const int32_t *slots,
+                                const smd_kv_pool *pool, void *stream) {
+  static const char *fn = "smd_write_kv_fp8";
+  g_err[0] = 0;
+  if (num_rows < 0) {
+    set_error("%s: negative num_rows", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  DecodeArgs d = {};
+  int rc = check_pool(fn, pool, d);
+  if (rc) return rc;
+  if (pool->dtype != SMD_KV_FP8_E4M3_UE8M0) {
+    set_error("%s: the destination pool must be fp8 (SMD_KV_FP8_E4M3_UE8M0)", fn);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (num_rows == 0) return SMD_OK;
+  if (!kv || !aligned16(kv) || kv_stride < kDim || ((kv_stride * 2) & 15)) {
+    set_error("%s: kv must be non-NULL bf16 rows, 16-byte aligned, with a stride >= 512 elements and a "
+              "multiple of 8 (stride %lld)", fn, (long long)kv_stride);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (slots && ((uintptr_t)slots & 3)) {
+    set_error("%s: slots must be 4-byte aligned", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  WriterArgs a = {};
+  a.kv = (const uint16_t *)kv;
+  a.kv_stride = kv_stride;
+  a.num_rows = num_rows;
+  a.slots = slots;
+  a.pool_rows = pool->num_rows;
+  a.nope = (uint8_t *)pool->nope;
+  a.nope_stride = d.nope_stride_b;
+  a.scale = (uint8_t *)pool->scale;
+  a.scale_stride = d.scale_stride_b;
+  a.rope = (uint16_t *)pool->rope;
+  a.rope_stride = d.rope_stride_b / 2;
+  hipError_t e = launch_write_kv_fp8(a, (hipStream_t)stream);
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SMD_ERR_HIP;
+  }
+  return SMD_OK;
+}

@@ -74,4 +74,21 @@ PersistLayout persist_layout(int64_t M, int64_t P);
 // rb in {1, 2, 4} query-row blocks of 16 per workgroup; a.d.G = M / (16 rb).
 hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream);
 
+// Arguments of the fp8/UE8M0 cache writer.  Pointers are device pointers.
+struct WriterArgs {
+  const uint16_t *kv;      // bf16 [num_rows, kv_stride]
+  int64_t kv_stride;       // elements
+  int32_t num_rows;
+  const int32_t *slots;    // [num_rows] destination pool rows, or null (row r -> r)
+  int64_t pool_rows;       // destination rows; slots outside [0, pool_rows) are skipped
+  uint8_t *nope;           // e4m3 [pool_rows, nope_stride]
+  int64_t nope_stride;     // bytes
+  uint8_t *scale;          // codes [pool_rows, scale_stride]
+  int64_t scale_stride;    // bytes
+  uint16_t *rope;          // bf16 [pool_rows, rope_stride]
+  int64_t rope_stride;     // elements
+};
+
+hipError_t launch_write_kv_fp8(const WriterArgs &a, hipStream_t stream);
+
 }  // namespace smd

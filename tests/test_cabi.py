@@ -280,3 +280,46 @@ def test_partials_bytes():
     assert smd.partials_bytes(0, 16, 1) == 0
     assert smd.partials_bytes(2, 16, 0) == 0 and "num_splits" in smd.lib().smd_last_error().decode()
     assert smd.partials_bytes(2, 16, 33) == 0
+
+
+# ----------------------------------------------------------------------------
+# host validation of the cache writer (no launch happens on failure)
+# ----------------------------------------------------------------------------
+def _fp8_pool(**kw):
+    base = dict(dtype=smd.KV_FP8_E4M3_UE8M0, nope_stride=448, rope_stride=64, scale=0x70000, scale_stride=8)
+    base.update(kw)
+    return _pool(**base)
+
+
+def _write(pool=None, kv=0x20000, kv_stride=512, n=4, slots=None):
+    p = pool if pool is not None else _fp8_pool()
+    rc = smd.lib().smd_write_kv_fp8(kv, kv_stride, n, slots, ctypes.byref(p), None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(n=-1), -1, "negative num_rows"),
+    (dict(kv=None), -1, "kv must be"),
+    (dict(kv=0x20008), -1, "16-byte aligned"),
+    (dict(kv_stride=511), -1, "stride"),
+    (dict(kv_stride=516), -1, "multiple of 8"),
+    (dict(slots=0x80002), -1, "slots must be 4-byte aligned"),
+])
+def test_writer_rejects(kw, code, msg):
+    rc, err = _write(**kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+@pytest.mark.parametrize("pkw,code,msg", [
+    (dict(dtype=smd.KV_BF16, nope_stride=512, rope_stride=512, scale=None), -2, "must be fp8"),
+    (dict(scale=None), -1, "scale"),
+    (dict(nope_stride=440), -1, "below the row widths"),
+    (dict(rope=0x10000 + 900), -1, "16-byte aligned"),
+])
+def test_writer_rejects_bad_pool(pkw, code, msg):
+    rc, err = _write(pool=_fp8_pool(**pkw))
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_writer_empty_launches_nothing():
+    assert _write(n=0, kv=None)[0] == 0
