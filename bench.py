@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--kernel-launches", type=int, default=50)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--writer", action="store_true",
+                    help="time the fp8/UE8M0 cache writer instead of the decode")
+    ap.add_argument("--writer-rows", type=int, default=131072, help="latent rows per writer call")
     ap.add_argument("--matrix", type=str, default=None,
                     help="comma-separated matrix variants (bf16_h128, fp8_h128, bf16_h16): print the T x ctx "
                          "table of whole-step times instead of the JSON line")
@@ -130,23 +133,41 @@ def cpu_baseline(w, target_s: float):
     return per_call, sample, cores
 
 
-def kernel_sources_sha() -> str:
-    """sha256 over the HIP kernel sources (file names and bytes, sorted)."""
-    import glob
+KERNEL_SOURCE = {"smd::decode_kernel": "decode_kernels.hip", "smd::persistent_kernel": "persistent_kernel.hip",
+                 "smd::write_kv_fp8_kernel": "writer_kernel.hip"}
+
+
+def kernel_sources_sha(kernel: str) -> str:
+    """sha256 over the sources `kernel` is compiled from: its .hip file and
+    every header it includes with quotes, transitively (names and bytes)."""
     import hashlib
-    h = hashlib.sha256()
+    import re
     csrc = os.path.join(ROOT, "sparse_mla_decode_index_amd", "csrc")
-    for p in sorted(glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h"))):
-        h.update(os.path.basename(p).encode())
+    inc = os.path.join(ROOT, "include")
+    todo, seen = [os.path.join(csrc, KERNEL_SOURCE[kernel])], {}
+    while todo:
+        p = todo.pop()
+        if p in seen:
+            continue
         with open(p, "rb") as f:
-            h.update(f.read())
+            seen[p] = f.read()
+        for name in re.findall(rb'^\s*#\s*include\s+"([^"]+)"', seen[p], re.M):
+            for d in (os.path.dirname(p), csrc, inc):
+                q = os.path.normpath(os.path.join(d, name.decode()))
+                if os.path.exists(q):
+                    todo.append(q)
+                    break
+    h = hashlib.sha256()
+    for p in sorted(seen):
+        h.update(os.path.relpath(p, ROOT).encode())
+        h.update(seen[p])
     return h.hexdigest()
 
 
 def measured_traffic(workload: str, kernel: str):
     """HBM bytes per launch of `kernel` on `workload` from the FETCH_SIZE /
     WRITE_SIZE profiles in profiles/traffic.json, scaled by a plain device
-    copy; None when the kernels changed since the counters were taken."""
+    copy; None when the kernel's sources changed since the counters were taken."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -154,7 +175,7 @@ def measured_traffic(workload: str, kernel: str):
     except (OSError, ValueError):
         return None, None
     e = t.get("workloads", {}).get(workload)
-    if e is None or e.get("kernel") != kernel or t.get("kernel_sources_sha256") != kernel_sources_sha():
+    if e is None or e.get("kernel") != kernel or e.get("sources_sha256") != kernel_sources_sha(kernel):
         return None, None
     return e["bytes_per_launch"], e.get("summary")
 
@@ -235,8 +256,127 @@ def matrix(args):
         print("", flush=True)
 
 
+def writer_cpu_baseline(wk, target_s: float):
+    """Time the oracle writer (oracle/writer_ref.py) on 4096-row chunks of the
+    same rows, cycled, until about target_s seconds; scaled to a whole call."""
+    from oracle import writer_ref
+    kv, slots, n_pool = wk["kv"], wk["slots"], wk["pool_rows"]
+    nope = np.zeros((n_pool, 448), dtype=np.uint8)
+    codes = np.zeros((n_pool, 8), dtype=np.uint8)
+    rope = np.zeros((n_pool, 64), dtype=np.uint16)
+    chunk, done, t_used = 4096, 0, 0.0
+    t0 = time.perf_counter()
+    while t_used < target_s and done < 100 * kv.shape[0]:
+        r0 = done % kv.shape[0]
+        r1 = min(kv.shape[0], r0 + chunk)
+        writer_ref.write_cache(kv[r0:r1], slots[r0:r1], n_pool, nope, codes, rope)
+        done += r1 - r0
+        t_used = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    sample = (f"{done} rows of the same call in {chunk}-row chunks ({t_used:.1f} s; one call writes "
+              f"{kv.shape[0]} rows), scaled to one call by rows")
+    return t_used * kv.shape[0] / done, sample, cores
+
+
+def writer_main(args):
+    """The fp8/UE8M0 cache writer: one step = one smd_write_kv_fp8 call over
+    --writer-rows latent rows into distinct random slots of a pool twice that
+    size.  HBM-bound; the roofline is algorithmic bytes over the kernel's time."""
+    import torch
+    import sparse_mla_decode_index_amd as smd
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    rows = args.writer_rows
+    wk = wl.writer_workload(rows, 2 * rows)
+    n_pool = wk["pool_rows"]
+    kv = torch.from_numpy(wk["kv"].view(np.int16)).to(dev).view(torch.bfloat16)
+    slots = torch.from_numpy(wk["slots"]).to(dev)
+    pool = smd.KVPool.fp8(torch.zeros((n_pool, 448), dtype=torch.uint8, device=dev),
+                          torch.zeros((n_pool, 8), dtype=torch.uint8, device=dev),
+                          torch.zeros((n_pool, 64), dtype=torch.bfloat16, device=dev))
+    stream = torch.cuda.Stream()
+
+    def step():
+        smd.write_kv_fp8(kv, pool, slots)
+
+    torch.cuda.synchronize()  # inputs were made on the default stream
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    kern_us = graph_time(torch, stream, step, args.kernel_launches)
+    if args.copy_calibration:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        with torch.cuda.stream(stream):
+            for _ in range(3):
+                dst.copy_(src)
+        torch.cuda.synchronize()
+
+    alg_bytes = wl.writer_algorithmic_bytes(rows)
+    us = ms_per_step * 1e3
+    kern_gbs = alg_bytes / (kern_us * 1e3)
+    kernel_name = "smd::write_kv_fp8_kernel"
+    roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None}
+    traffic, traffic_src = measured_traffic(wk["name"], kernel_name)
+    roof["traffic"] = traffic
+    if traffic_src:
+        roof["traffic_source"] = traffic_src
+    roof.update({"kernel": kernel_name, "kernel_us": round(kern_us, 3), "alg_bytes_per_launch": alg_bytes})
+    res = {
+        "metric": "fp8/UE8M0 KV-cache write: achieved HBM GB/s (% roofline)",
+        "value": round(alg_bytes / (us * 1e3), 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_call": round(us, 3),
+        "rows_per_s": round(rows / (us * 1e-6), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 in, fp8-e4m3/ue8m0 out",
+        "data": "synthetic",
+        "config": {"workload": wk["name"], "rows": rows, "pool_rows": n_pool, "slots": "distinct random",
+                   "parallelism": "1 gpu"},
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        per_call, sample, cores = writer_cpu_baseline(wk, args.cpu_seconds)
+        res["cpu_baseline"] = {"value": round(alg_bytes / (per_call * 1e9), 4), "unit": "GB/s", "cores": cores,
+                               "kind": "oracle", "us_per_call": round(per_call * 1e6, 1), "sample": sample}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
+    if args.writer:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                              "n_gpus_requested": args.gpus}))
+            sys.exit(2)
+        writer_main(args)
+        return
     if args.matrix:
         if args.gpus != 1:
             print("this build runs on exactly one GPU; --gpus must be 1")

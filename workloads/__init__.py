@@ -315,3 +315,33 @@ def algorithmic_flops(w: Workload) -> int:
     idx = a["indices"]
     nvalid = int(np.count_nonzero((idx >= 0) & (idx < w.pool_rows)))
     return 2048 * M * nvalid
+
+
+# ----------------------------------------------------------------------------
+# fp8/UE8M0 cache writer
+# ----------------------------------------------------------------------------
+WRITER_ROW_READ = DIM * 2                             # one bf16 latent row
+WRITER_ROW_WRITE = NOPE + SCALE_STRIDE + ROPE * 2     # 448 bytes + 8 code bytes + 128 RoPE bytes
+WRITER_SLOT = 4                                       # int32 destination slot
+
+
+def writer_workload(rows: int, pool_rows: int, seed: int = 7) -> dict:
+    """Latent rows for the cache writer: N(0,1) rounded to bf16, each row
+    scaled by 2^U{-8..8} (so the seven blocks of a row take different codes
+    across rows), written to distinct random slots of a pool_rows-row pool."""
+    assert rows <= pool_rows
+    rng = np.random.default_rng(seed)
+    kv = np.empty((rows, DIM), dtype=np.uint16)
+    for r0 in range(0, rows, 65536):
+        r1 = min(rows, r0 + 65536)
+        x = rng.standard_normal((r1 - r0, DIM), dtype=np.float32)
+        x *= np.exp2(rng.integers(-8, 9, size=(r1 - r0, 1))).astype(np.float32)
+        kv[r0:r1] = f32_to_bf16_bits(x)
+    slots = rng.permutation(pool_rows)[:rows].astype(np.int32)
+    return {"kv": kv, "slots": slots, "pool_rows": pool_rows,
+            "name": f"fp8 cache write rows={rows} pool={pool_rows}"}
+
+
+def writer_algorithmic_bytes(rows: int) -> int:
+    """Each latent row read once, its fp8 row (bytes, codes, RoPE) written once, one slot read."""
+    return rows * (WRITER_ROW_READ + WRITER_ROW_WRITE + WRITER_SLOT)
