@@ -123,6 +123,25 @@ def test_writer_slots_and_strides(gpu):
     assert torch.all(nope[:, 448:] == 0xAA) and torch.all(scale[:, 8:] == 0xAA)
 
 
+def test_writer_two_rows_per_wave(gpu):
+    """Large writes take two rows per wave: an odd row count leaves the last
+    wave one row, and skipped slots fall on either row of a wave."""
+    n_in, n_pool = 65537, 70000
+    rng = np.random.default_rng(11)
+    kv_bits = _rows(n_in, 5)
+    edge = _edge_rows()
+    kv_bits[1000:1000 + len(edge)] = edge      # NaN, infinities, zeros on both rows of a wave
+    kv_bits[-len(edge) - 1:-1] = edge
+    slots = rng.permutation(n_pool)[:n_in].astype(np.int32)
+    slots[rng.choice(n_in, 300, replace=False)] = -1
+    slots[-1] = n_pool + 5
+    nope, scale, rope, pool = _pool(n_pool, gpu)
+    print(f"writer two rows per wave n={n_in}", flush=True)
+    smd.write_kv_fp8(bf16_tensor(kv_bits, gpu), pool, torch.from_numpy(slots).to(gpu))
+    torch.cuda.synchronize()
+    _check((nope, scale, rope), kv_bits, slots, n_pool)
+
+
 def test_writer_round_trip_through_decode(gpu):
     """A pool written by the GPU writer decodes like the oracle's writer +
     oracle decode (the bytes are equal, so this checks the wiring)."""
