@@ -5,7 +5,10 @@ Definitions follow the pages:
 * vLLM "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on gfx950",
   section Design: a 512-wide QK dot made of 448 NoPE and 64 RoPE dims; the
   PV product runs over the same 512-wide latent row (V is the row itself);
-  attention sinks; an invalid index contributes zero probability.
+  attention sinks; an invalid index contributes zero probability; main
+  (top-k) and sliding-window work run as ordered tiles of one softmax, read
+  here as two sources (a main pool and an SWA pool, each with its own index
+  list) whose rows all enter one softmax, main positions first.
 * aiter "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode
   kernel", Summary: split-KV with FP32 partials reduced by a stage-2 merge;
   rows with K = 0 are left unwritten.
@@ -264,6 +267,69 @@ def merge_partials(o: np.ndarray, lse: np.ndarray, sink):
     w = np.where(finite[:, :, None], np.exp(lse - np.where(finite, L, 0.0)[:, :, None]), 0.0)
     out = (w[..., None] * o).sum(axis=2)
     return out, L
+
+
+# ----------------------------------------------------------------------------
+# two sources: the compressed main cache and the sliding-window (SWA) cache
+# ----------------------------------------------------------------------------
+def two_source_rows(main_pool: dict, main_idx, swa_pool: dict, swa_idx) -> np.ndarray:
+    """Rows one index row attends to when its main (top-k) entries index the
+    main pool and its SWA entries index the SWA pool (the vLLM page, Design:
+    main and SWA work run as ordered tiles of one softmax).  Each entry is
+    valid against its own pool's size; the main rows come first."""
+    main_idx = np.asarray(main_idx)
+    swa_idx = np.asarray(swa_idx)
+    km = pool_rows(main_pool, main_idx[valid_mask(main_idx, pool_size(main_pool))])
+    ks = pool_rows(swa_pool, swa_idx[valid_mask(swa_idx, pool_size(swa_pool))])
+    return np.concatenate([km, ks], axis=0)
+
+
+def sparse_mla_decode_two_source(q_nope, q_rope, main_pool: dict, main_indices, swa_pool: dict, swa_indices, sink,
+                                 softmax_scale: float, q_per_seq: int = 1):
+    """Decode over both sources: token t uses main row t // q_per_seq of
+    main_indices (into main_pool) and the same row of swa_indices (into
+    swa_pool), all of them terms of one softmax with the sink.
+
+    Returns out float64 [T, H, 512] and lse float64 [T, H]."""
+    q = queries(q_nope, q_rope)
+    T, H, _ = q.shape
+    sk = _sink64(sink, H)
+    out = np.zeros((T, H, DIM))
+    lse = np.zeros((T, H))
+    mi, si = np.asarray(main_indices), np.asarray(swa_indices)
+    for b in range(mi.shape[0]):
+        k = two_source_rows(main_pool, mi[b], swa_pool, si[b])
+        t0, t1 = b * q_per_seq, (b + 1) * q_per_seq
+        skb = None if sk is None else np.tile(sk, q_per_seq)
+        o, l = attend(q[t0:t1].reshape(-1, DIM), k, softmax_scale, skb)
+        out[t0:t1] = o.reshape(q_per_seq, H, DIM)
+        lse[t0:t1] = l.reshape(q_per_seq, H)
+    return out, lse
+
+
+def sparse_mla_decode_two_source_partials(q_nope, q_rope, main_pool: dict, main_indices, swa_pool: dict,
+                                          swa_indices, softmax_scale: float, num_splits: int, q_per_seq: int = 1):
+    """Split partials over the ordered positions of both sources: position p
+    of an index row is main entry p for p < K_main, else SWA entry p - K_main;
+    split r covers split_bounds(K_main + K_swa, s)[r] of those positions."""
+    q = queries(q_nope, q_rope)
+    T, H, _ = q.shape
+    mi, si = np.asarray(main_indices), np.asarray(swa_indices)
+    k_main, k_swa = mi.shape[1], si.shape[1]
+    bounds = split_bounds(k_main + k_swa, num_splits)
+    o = np.zeros((T, H, num_splits, DIM))
+    lse = np.zeros((T, H, num_splits))
+    for b in range(mi.shape[0]):
+        t0, t1 = b * q_per_seq, (b + 1) * q_per_seq
+        qb = q[t0:t1].reshape(-1, DIM)
+        for r, (a, e) in enumerate(bounds):
+            # positions [a, e): the main part [a, min(e, K_main)), the SWA part from max(a, K_main)
+            k = two_source_rows(main_pool, mi[b, a:min(e, k_main)], swa_pool,
+                                si[b, max(a, k_main) - k_main:max(e, k_main) - k_main])
+            orr, lr = partial_one(qb, k, softmax_scale)
+            o[t0:t1, :, r] = orr.reshape(q_per_seq, H, DIM)
+            lse[t0:t1, :, r] = lr.reshape(q_per_seq, H)
+    return o, lse
 
 
 # ----------------------------------------------------------------------------

@@ -117,6 +117,7 @@ class Workload:
     softmax_scale: float
     arrays: dict = field(default_factory=dict)
     ragged: bool = False
+    two_source: bool = False
     note: str = ""
 
     @property
@@ -226,14 +227,49 @@ def ragged_workload(name: str, *, B: int, q_per_seq: int, H: int, kv_dtype: str,
     return Workload(name, T, H, q_per_seq, kv_dtype, pool_rows, scale, arrays, ragged=True, note=note)
 
 
+def two_source_workload(name: str, *, T: int, H: int, kv_dtype: str, main_rows: int, topk: int, window: int,
+                        invalid: int = 0, swa_invalid: int = 0, q_per_seq: int = 1, seed: int = 0,
+                        softmax_scale: float | None = None, note: str = "") -> Workload:
+    """Main + SWA sources.  Index row b draws `topk` main indices uniformly
+    without replacement from a main pool of main_rows rows (`invalid` of them
+    then set to -1), and owns block b of a sliding-window pool of
+    R * window rows, a ring: its window list is that block's rows starting at
+    a random ring position, the first `swa_invalid` entries -1 (a window not
+    yet full).  Both pools have the same format.
+
+    Draw order: q_nope, q_rope, main pool, SWA pool, sink, main indices,
+    invalid main positions, ring positions."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    q_nope, q_rope = _queries(rng, T, H)
+    R = T // q_per_seq
+    main = _pool(rng, kv_dtype, main_rows)
+    swa = _pool(rng, kv_dtype, R * window)
+    sink = rng.standard_normal(H, dtype=np.float32)
+    midx = np.empty((R, topk), dtype=np.int32)
+    for r in range(R):
+        midx[r] = rng.choice(main_rows, size=topk, replace=False)
+    _set_invalid(rng, midx, invalid)
+    sidx = np.empty((R, window), dtype=np.int32)
+    for r in range(R):
+        start = int(rng.integers(0, window))
+        sidx[r] = r * window + (start + np.arange(window)) % window
+        sidx[r, :swa_invalid] = -1
+    arrays = {"q_nope": q_nope, "q_rope": q_rope, "sink": sink, "main": main, "swa": swa,
+              "main_indices": midx, "swa_indices": sidx}
+    scale = 1.0 / math.sqrt(DIM) if softmax_scale is None else softmax_scale
+    return Workload(name, T, H, q_per_seq, kv_dtype, main_rows, scale, arrays, two_source=True, note=note)
+
+
 # ----------------------------------------------------------------------------
 # the named configurations
 # ----------------------------------------------------------------------------
-CONFIG_NAMES = ("tiny_bf16", "bf16_topk_swa", "fp8_ue8m0", "long_context_bf16", "ragged_mtp4_fp8")
+CONFIG_NAMES = ("tiny_bf16", "bf16_topk_swa", "fp8_ue8m0", "long_context_bf16", "ragged_mtp4_fp8",
+                "fp8_two_source")
 
 
 def config(i: int, **over) -> Workload:
-    """The five workloads of the statement, by position 0..4."""
+    """The five workloads of the statement, by position 0..4, and the
+    two-source (main + SWA) decode as 5."""
     if i == 0:
         kw = dict(T=2, H=16, kv_dtype="bf16", pool_rows=512, topk=64, invalid=8, seed=0)
         kw.update(over)
@@ -258,6 +294,11 @@ def config(i: int, **over) -> Workload:
                   zero_rows=4, seed=4)
         kw.update(over)
         return ragged_workload("ragged MTP4 fp8 B=64x4 H=128 K_b<=8192 pool=262144", **kw)
+    if i == 5:
+        kw = dict(T=32, H=128, kv_dtype="fp8", main_rows=131072, topk=2048, window=128,
+                  invalid=round(0.005 * 2048), seed=5)
+        kw.update(over)
+        return two_source_workload("fp8 two-source T=32 H=128 K=2048 main + 128 swa", **kw)
     raise ValueError(i)
 
 
@@ -285,7 +326,11 @@ def algorithmic_bytes(w: Workload) -> int:
     index row, every index, q, out (bf16), lse (fp32) and sink."""
     a = w.arrays
     rb = w.row_bytes()
-    if w.ragged:
+    if w.two_source:
+        nidx = a["main_indices"].size + a["swa_indices"].size
+        nvalid = _two_source_valid(w)
+        written_tokens = w.num_tokens
+    elif w.ragged:
         flat = a["kv_indices"][int(a["kv_indptr"][0]):]
         nidx = flat.size
         nvalid = int(np.count_nonzero((flat >= 0) & (flat < w.pool_rows)))
@@ -301,10 +346,19 @@ def algorithmic_bytes(w: Workload) -> int:
     return nvalid * rb + nidx * 4 + q + out + H * 4
 
 
+def _two_source_valid(w: Workload) -> int:
+    a = w.arrays
+    n_swa = (a["swa"]["kv"] if "kv" in a["swa"] else a["swa"]["nope"]).shape[0]
+    mi, si = a["main_indices"], a["swa_indices"]
+    return int(np.count_nonzero((mi >= 0) & (mi < w.pool_rows)) + np.count_nonzero((si >= 0) & (si < n_swa)))
+
+
 def algorithmic_flops(w: Workload) -> int:
     """2*512 (QK) + 2*512 (PV) flops per valid gathered row per query row."""
     a = w.arrays
     M = w.num_heads * w.q_per_seq
+    if w.two_source:
+        return 2048 * M * _two_source_valid(w)
     if w.ragged:
         ptr = a["kv_indptr"]
         tot = 0
