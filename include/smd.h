@@ -214,6 +214,37 @@ int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_to
                           void *stream);
 
 /*
+ * Two-source decode: the compressed main cache and the sliding-window (SWA)
+ * cache, each with its own index list, as ordered segments of one softmax
+ * (vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on
+ * gfx950", Design: main and SWA work run in guarded tiles of one kernel).
+ *
+ *  Index row b has K = k_main + k_swa positions: position p < k_main is
+ *  main_indices[b][p], a row of main_kv; position p >= k_main is
+ *  swa_indices[b][p - k_main], a row of swa_kv.  Each index is valid
+ *  against its own pool's num_rows (anything else contributes nothing).
+ *  Every valid row is a term of one softmax with the sink; out, lse and the
+ *  split partials are those of smd_sparse_mla_decode over the K positions
+ *  (split r covers smd_split_bounds(K, num_splits, r) of them, so a split
+ *  may hold main and SWA rows).
+ *  main_kv, swa_kv  both required; same dtype, same row strides and (bf16)
+ *           the same RoPE placement, else SMD_ERR_UNSUPPORTED.  They may be
+ *           the same pool.
+ *  main_indices int32 [num_tokens / q_per_seq, >= k_main], row stride
+ *           main_stride; swa_indices int32 [.., >= k_swa], row stride
+ *           swa_stride.  A list with count 0 may be NULL.
+ *  All other arguments, errors and outputs as smd_sparse_mla_decode; the
+ *  planner's kv_len for this call is k_main + k_swa.
+ */
+int smd_sparse_mla_decode_two_source(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                     int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *main_kv,
+                                     const int32_t *main_indices, int64_t main_stride, int32_t k_main,
+                                     const smd_kv_pool *swa_kv, const int32_t *swa_indices,
+                                     int64_t swa_stride, int32_t k_swa, const float *sink,
+                                     float softmax_scale, int32_t num_splits, float *partial_o,
+                                     float *partial_lse, void *out, float *lse, void *stream);
+
+/*
  * Stage-2 merge (aiter page, Summary part 1: always reduce the FP32
  * partials, even with one split per row):
  *   LSE = ln(sum_r e^{lse_r} + e^{sink_h}),  out = sum_r e^{lse_r - LSE} o_r.

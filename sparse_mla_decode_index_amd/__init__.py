@@ -99,6 +99,10 @@ def lib() -> ctypes.CDLL:
     L.smd_sparse_mla_decode.restype = ctypes.c_int
     L.smd_sparse_mla_decode.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
                                         vp, f32, i32, vp, vp, vp, vp, vp]
+    L.smd_sparse_mla_decode_two_source.restype = ctypes.c_int
+    L.smd_sparse_mla_decode_two_source.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
+                                                   ctypes.POINTER(_KVPool), vp, i64, i32,
+                                                   vp, f32, i32, vp, vp, vp, vp, vp]
     L.smd_merge_partials.restype = ctypes.c_int
     L.smd_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.smd_write_kv_fp8.restype = ctypes.c_int
@@ -239,20 +243,9 @@ def split_bounds(kv_len: int, num_splits: int, split: int) -> tuple[int, int]:
 # ----------------------------------------------------------------------------
 # decode and merge
 # ----------------------------------------------------------------------------
-def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, indices: torch.Tensor,
-                      sink: Optional[torch.Tensor], softmax_scale: float, *,
-                      num_splits: Optional[int] = None, q_per_seq: int = 1,
-                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                      partial_o: Optional[torch.Tensor] = None,
-                      partial_lse: Optional[torch.Tensor] = None,
-                      partials_only: bool = False):
-    """Split-KV sparse MLA decode.
-
-    q_nope bf16 [T,H,448], q_rope bf16 [T,H,64], indices int32 [T/q_per_seq, K]
-    (row stride free), sink fp32 [H] or None.  Returns (out, lse) — bf16
-    [T,H,512] and fp32 [T,H] — or, with partials_only, (partial_o, partial_lse)
-    of shapes [T,H,s,512] and [T,H,s].  num_splits=None asks the host planner.
-    """
+def _decode_buffers(q_nope, q_rope, index_lists, sink, pools, q_per_seq, num_splits, out, lse, partial_o,
+                    partial_lse, partials_only):
+    """Shared checks and output allocation of the dense-index decodes."""
     dev = q_nope.device
     _need(q_nope, "q_nope", torch.bfloat16, device=dev)
     if q_nope.dim() != 3 or q_nope.shape[2] != NOPE:
@@ -261,17 +254,18 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
     _need(q_rope, "q_rope", torch.bfloat16, (T, H, ROPE), dev)
     if not (q_nope.is_contiguous() and q_rope.is_contiguous()):
         raise ValueError("q_nope and q_rope must be contiguous")
-    _need(indices, "indices", torch.int32, device=dev)
-    if indices.dim() != 2 or indices.shape[0] * q_per_seq != T or (indices.shape[1] > 0 and indices.stride(1) != 1):
-        raise ValueError("indices must be [T / q_per_seq, K] with unit column stride")
+    for name, idx in index_lists:
+        _need(idx, name, torch.int32, device=dev)
+        if idx.dim() != 2 or idx.shape[0] * q_per_seq != T or (idx.shape[1] > 0 and idx.stride(1) != 1):
+            raise ValueError(f"{name} must be [T / q_per_seq, K] with unit column stride")
     if sink is not None:
         _need(sink, "sink", torch.float32, (H,), dev)
-    if kv.device != dev:
-        raise ValueError("kv pool must be on the same device as q")
-    K = indices.shape[1]
+    for kv in pools:
+        if kv.device != dev:
+            raise ValueError("kv pool must be on the same device as q")
+    K = sum(idx.shape[1] for _, idx in index_lists)
     if num_splits is None:
-        num_splits = plan_num_kv_splits(T // q_per_seq, H, K, q_per_seq,
-                                        kv.dtype if K > 0 else KV_BF16)
+        num_splits = plan_num_kv_splits(T // q_per_seq, H, K, q_per_seq, pools[0].dtype if K > 0 else KV_BF16)
     need_partials = partials_only or num_splits > 1
     if need_partials:
         if partial_o is None:
@@ -287,15 +281,67 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
             lse = torch.empty((T, H), dtype=torch.float32, device=dev)
         _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
         _need(lse, "lse", torch.float32, (T, H), dev)
+    return T, H, num_splits, out, lse, partial_o, partial_lse
+
+
+def _idx_args(idx: torch.Tensor):
+    K = idx.shape[1]
+    return (idx.data_ptr() if idx.numel() else None), (idx.stride(0) if K > 0 else 0), K
+
+
+def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, indices: torch.Tensor,
+                      sink: Optional[torch.Tensor], softmax_scale: float, *,
+                      num_splits: Optional[int] = None, q_per_seq: int = 1,
+                      out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                      partial_o: Optional[torch.Tensor] = None,
+                      partial_lse: Optional[torch.Tensor] = None,
+                      partials_only: bool = False):
+    """Split-KV sparse MLA decode.
+
+    q_nope bf16 [T,H,448], q_rope bf16 [T,H,64], indices int32 [T/q_per_seq, K]
+    (row stride free), sink fp32 [H] or None.  Returns (out, lse) — bf16
+    [T,H,512] and fp32 [T,H] — or, with partials_only, (partial_o, partial_lse)
+    of shapes [T,H,s,512] and [T,H,s].  num_splits=None asks the host planner.
+    """
+    T, H, num_splits, out, lse, partial_o, partial_lse = _decode_buffers(
+        q_nope, q_rope, [("indices", indices)], sink, [kv], q_per_seq, num_splits, out, lse, partial_o,
+        partial_lse, partials_only)
     pool = kv._struct()
     rc = lib().smd_sparse_mla_decode(
-        q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool),
-        indices.data_ptr() if indices.numel() else None, indices.stride(0) if K > 0 else 0, K,
+        q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool), *_idx_args(indices),
         _ptr(sink), float(softmax_scale), num_splits,
         _ptr(partial_o), _ptr(partial_lse),
         None if partials_only else out.data_ptr(), None if partials_only else lse.data_ptr(),
         _stream(q_nope))
     _check("smd_sparse_mla_decode", rc)
+    if partials_only:
+        return partial_o, partial_lse
+    return out, lse
+
+
+def sparse_mla_decode_two_source(q_nope: torch.Tensor, q_rope: torch.Tensor, main_kv: KVPool,
+                                 main_indices: torch.Tensor, swa_kv: KVPool, swa_indices: torch.Tensor,
+                                 sink: Optional[torch.Tensor], softmax_scale: float, *,
+                                 num_splits: Optional[int] = None, q_per_seq: int = 1,
+                                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                 partial_o: Optional[torch.Tensor] = None,
+                                 partial_lse: Optional[torch.Tensor] = None,
+                                 partials_only: bool = False):
+    """Two-source decode: main_indices [T/q_per_seq, K_main] index main_kv,
+    swa_indices [T/q_per_seq, K_swa] index swa_kv, all one softmax (main
+    positions first).  Pools of the same dtype and strides.  Outputs as
+    sparse_mla_decode; the planner sees K_main + K_swa positions."""
+    T, H, num_splits, out, lse, partial_o, partial_lse = _decode_buffers(
+        q_nope, q_rope, [("main_indices", main_indices), ("swa_indices", swa_indices)], sink, [main_kv, swa_kv],
+        q_per_seq, num_splits, out, lse, partial_o, partial_lse, partials_only)
+    mp, sp = main_kv._struct(), swa_kv._struct()
+    rc = lib().smd_sparse_mla_decode_two_source(
+        q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(mp), *_idx_args(main_indices),
+        ctypes.byref(sp), *_idx_args(swa_indices), _ptr(sink), float(softmax_scale), num_splits,
+        _ptr(partial_o), _ptr(partial_lse),
+        None if partials_only else out.data_ptr(), None if partials_only else lse.data_ptr(),
+        _stream(q_nope))
+    _check("smd_sparse_mla_decode_two_source", rc)
     if partials_only:
         return partial_o, partial_lse
     return out, lse
@@ -430,7 +476,7 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
 
 __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
            "partials_bytes", "write_kv_fp8",
-           "sparse_mla_decode", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
+           "sparse_mla_decode", "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
            "PersistentWorkspace", "sparse_mla_decode_persistent", "lib", "library_path", "KV_BF16",
            "KV_FP8_E4M3_UE8M0"]
 

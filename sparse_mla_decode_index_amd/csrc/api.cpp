@@ -109,17 +109,25 @@ using namespace smd;
 
 extern "C" const char *smd_last_error(void) { return g_err; }
 
-extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
-                                     int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
-                                     const int32_t *indices, int64_t indices_stride, int32_t topk,
-                                     const float *sink, float softmax_scale, int32_t num_splits,
-                                     float *partial_o, float *partial_lse, void *out, float *lse,
-                                     void *stream) {
-  static const char *fn = "smd_sparse_mla_decode";
+// Second source of a two-source decode (the sliding-window pool and its index
+// list); null for one source.
+struct SecondSource {
+  const smd_kv_pool *kv;
+  const int32_t *indices;
+  int64_t indices_stride;
+  int32_t count;
+};
+
+static int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t num_tokens,
+                       int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv, const int32_t *indices,
+                       int64_t indices_stride, int32_t topk, const SecondSource *two, const float *sink,
+                       float softmax_scale, int32_t num_splits, float *partial_o, float *partial_lse, void *out,
+                       float *lse, void *stream) {
   g_err[0] = 0;
-  if (num_tokens < 0 || topk < 0 || indices_stride < 0) {
-    set_error("%s: negative size (num_tokens=%d topk=%d indices_stride=%lld)", fn, num_tokens, topk,
-              (long long)indices_stride);
+  if (num_tokens < 0 || topk < 0 || indices_stride < 0 ||
+      (two && (two->count < 0 || two->indices_stride < 0))) {
+    set_error("%s: negative size (num_tokens=%d counts=%d,%d strides=%lld,%lld)", fn, num_tokens, topk,
+              two ? two->count : 0, (long long)indices_stride, (long long)(two ? two->indices_stride : 0));
     return SMD_ERR_INVALID_ARG;
   }
   if (!heads_ok(num_heads)) {
@@ -145,17 +153,41 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
   DecodeArgs a = {};
   int rc = check_pool(fn, kv, a);
   if (rc) return rc;
-  if (num_tokens > 0 && topk > 0) {
-    if (!q_nope || !q_rope || !indices) {
-      set_error("%s: q_nope, q_rope and indices are required", fn);
+  const int32_t k2 = two ? two->count : 0;
+  if (two) {
+    DecodeArgs b = {};
+    rc = check_pool(fn, two->kv, b);
+    if (rc) return rc;
+    if (two->kv->dtype != kv->dtype || b.nope_stride_b != a.nope_stride_b || b.rope_stride_b != a.rope_stride_b ||
+        b.scale_stride_b != a.scale_stride_b || b.packed != a.packed) {
+      set_error("%s: the main and SWA pools must have the same dtype, row strides and RoPE placement", fn);
+      return SMD_ERR_UNSUPPORTED;
+    }
+    if ((int64_t)topk + k2 > INT32_MAX) {
+      set_error("%s: main + SWA index counts exceed 2^31 - 1", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    a.kv2_nope = b.kv_nope;
+    a.kv2_rope = b.kv_rope;
+    a.kv2_scale = b.kv_scale;
+    a.num_rows2_32 = b.num_rows32;
+  }
+  const int32_t rows = num_tokens / q_per_seq;
+  if (num_tokens > 0 && topk + k2 > 0) {
+    if (!q_nope || !q_rope || (topk > 0 && !indices) || (k2 > 0 && !two->indices)) {
+      set_error("%s: q_nope, q_rope and the index lists are required", fn);
       return SMD_ERR_INVALID_ARG;
     }
     if (!aligned16(q_nope) || !aligned16(q_rope)) {
       set_error("%s: q_nope/q_rope must be 16-byte aligned", fn);
       return SMD_ERR_INVALID_ARG;
     }
-    if (indices_stride < topk && num_tokens / q_per_seq > 1) {
-      set_error("%s: indices_stride=%lld below topk=%d", fn, (long long)indices_stride, topk);
+    if (topk > 0 && indices_stride < topk && rows > 1) {
+      set_error("%s: indices_stride=%lld below its count %d", fn, (long long)indices_stride, topk);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (k2 > 0 && two->indices_stride < k2 && rows > 1) {
+      set_error("%s: swa indices stride=%lld below k_swa=%d", fn, (long long)two->indices_stride, k2);
       return SMD_ERR_INVALID_ARG;
     }
   }
@@ -172,18 +204,36 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
     set_error("%s: out must be 16-byte aligned", fn);
     return SMD_ERR_INVALID_ARG;
   }
-  if (num_tokens == 0 || topk == 0) return SMD_OK;
+  if (num_tokens == 0 || topk + k2 == 0) return SMD_OK;
 
+  const int32_t K = topk + k2;
   const int32_t M = num_heads * q_per_seq;
-  const int32_t rows = num_tokens / q_per_seq;
-  // chunk = roundup(ceil(topk / s), 64), as smd_split_bounds.
-  const int64_t per = ((int64_t)topk + num_splits - 1) / num_splits;
+  // chunk = roundup(ceil(K / s), 64), as smd_split_bounds.
+  const int64_t per = ((int64_t)K + num_splits - 1) / num_splits;
   const int64_t chunk = (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
   a.q_nope = (const uint16_t *)q_nope;
   a.q_rope = (const uint16_t *)q_rope;
+  if (k2 == 0 || topk == 0) {  // one list holds every position: a one-source launch over its pool
+    if (topk == 0) {
+      DecodeArgs b = {};
+      check_pool(fn, two->kv, b);  // passed above
+      a.kv_nope = b.kv_nope;
+      a.kv_rope = b.kv_rope;
+      a.kv_scale = b.kv_scale;
+      a.num_rows = b.num_rows;
+      a.num_rows32 = b.num_rows32;
+      indices = two->indices;
+      indices_stride = two->indices_stride;
+    }
+    a.indices2 = nullptr;
+  } else {
+    a.indices2 = two->indices;
+    a.indices2_stride = two->indices_stride;
+  }
   a.indices = indices;
   a.indices_stride = indices_stride;
-  a.topk = topk;
+  a.k_main = topk;
+  a.topk = K;
   a.chunk = (int32_t)(chunk < INT32_MAX ? chunk : INT32_MAX);
   a.sink = sink;
   a.scale_log2 = softmax_scale * 1.4426950408889634f;
@@ -215,6 +265,30 @@ extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int
     }
   }
   return SMD_OK;
+}
+
+extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                     int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
+                                     const int32_t *indices, int64_t indices_stride, int32_t topk,
+                                     const float *sink, float softmax_scale, int32_t num_splits,
+                                     float *partial_o, float *partial_lse, void *out, float *lse,
+                                     void *stream) {
+  return decode_impl("smd_sparse_mla_decode", q_nope, q_rope, num_tokens, num_heads, q_per_seq, kv, indices,
+                     indices_stride, topk, nullptr, sink, softmax_scale, num_splits, partial_o, partial_lse, out,
+                     lse, stream);
+}
+
+extern "C" int smd_sparse_mla_decode_two_source(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                                int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *main_kv,
+                                                const int32_t *main_indices, int64_t main_stride, int32_t k_main,
+                                                const smd_kv_pool *swa_kv, const int32_t *swa_indices,
+                                                int64_t swa_stride, int32_t k_swa, const float *sink,
+                                                float softmax_scale, int32_t num_splits, float *partial_o,
+                                                float *partial_lse, void *out, float *lse, void *stream) {
+  const SecondSource two{swa_kv, swa_indices, swa_stride, k_swa};
+  return decode_impl("smd_sparse_mla_decode_two_source", q_nope, q_rope, num_tokens, num_heads, q_per_seq, main_kv,
+                     main_indices, main_stride, k_main, &two, sink, softmax_scale, num_splits, partial_o,
+                     partial_lse, out, lse, stream);
 }
 
 extern "C" int smd_merge_partials(const float *partial_o, const float *partial_lse,

@@ -15,7 +15,7 @@ using namespace ks;
 // Work decomposition: a workgroup (8 waves, two per SIMD) owns one index row
 // b, one block g of 16 query rows and one split r; its waves share the split's
 // positions (interleaved half-tiles of 16) and merge their states at the end.
-template <int FMT, bool P_HILO>
+template <int FMT, bool P_HILO, bool TWO>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) ks8::Smem sm;
 
@@ -33,7 +33,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int r = u % a.S;
   const int p0 = min(r * a.chunk, a.topk);
   const int p1 = min(p0 + a.chunk, a.topk);
-  const int32_t *row_idx = a.indices + (int64_t)b * a.indices_stride;
+  const ks::Src<TWO> src{a.indices + (int64_t)b * a.indices_stride,
+                         TWO ? a.indices2 + (int64_t)b * a.indices2_stride : nullptr, a.k_main};
 
   const ks::Lane L = ks::make_lane(lane);
   // This lane's query row m -> (token, head).
@@ -44,11 +45,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 
   // the first indices and rows are in flight while Q^T is staged
   ks8::Pipe<FMT> pipe;
-  ks8::prime<FMT>(a, row_idx, p0, p1, wave, L, pipe);
+  ks8::prime<FMT>(a, src, p0, p1, wave, L, pipe);
   ks8::stage_q(a, qrow, wave, L, sm);
   __syncthreads();
   ks::State st;
-  ks8::attend<FMT, P_HILO>(a, row_idx, p0, p1, wave, L, (const uint8_t SMD_LDS *)&sm.q[0],
+  ks8::attend<FMT, P_HILO>(a, src, p0, p1, wave, L, (const uint8_t SMD_LDS *)&sm.q[0],
                               (uint8_t SMD_LDS *)&sm.buf[wave][0], st, pipe);
   ks::f32x4 o[8];
   float mm, ll;
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // Work decomposition of the dim-split variant: a workgroup (8 waves = 4 pairs
 // of dim halves) owns one index row b, one block g of 32 query rows and one
 // split r; a.G = M / 32.  Mapping to the grid as in decode_kernel.
-template <int FMT, bool P_HILO>
+template <int FMT, bool P_HILO, bool TWO>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void decode_kp_kernel(DecodeArgs a) {
   __shared__ __attribute__((aligned(1024))) kp::Smem sm;
 
@@ -81,7 +82,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int r = u % a.S;
   const int p0 = min(r * a.chunk, a.topk);
   const int p1 = min(p0 + a.chunk, a.topk);
-  const int32_t *row_idx = a.indices + (int64_t)b * a.indices_stride;
+  const ks::Src<TWO> src{a.indices + (int64_t)b * a.indices_stride,
+                         TWO ? a.indices2 + (int64_t)b * a.indices2_stride : nullptr, a.k_main};
 
   const ks::Lane L = ks::make_lane(lane);
   const kp::PLane P = kp::make_plane(L);
@@ -96,12 +98,12 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   const int k = wave >> 1, h = wave & 1;
 
   kp::Pipe<FMT> pipe;
-  if (p1 > p0) kp::prime<FMT>(a, row_idx, p0, p1, k, h, L, pipe);  // workgroup-uniform
+  if (p1 > p0) kp::prime<FMT>(a, src, p0, p1, k, h, L, pipe);  // workgroup-uniform
   kp::stage_q(a, qrow, wave, L, sm);
   if (lane == 0) sm.flag[wave] = 0;
   __syncthreads();
   kp::State st;
-  kp::attend<FMT, P_HILO>(a, row_idx, p0, p1, wave, L, P, sm, st, pipe);
+  kp::attend<FMT, P_HILO>(a, src, p0, p1, wave, L, P, sm, st, pipe);
   if (!kp::merge_pairs(sm, wave, L, st)) return;
   // waves 0 and 1: dims [256h, 256h + 256) of both blocks
   const int dcol = 256 * h + 4 * L.g;
@@ -238,32 +240,38 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   if (lse && lane == 0) lse[row] = mx + logf(z);
 }
 
-template <int FMT, bool P_HILO>
+template <int FMT, bool P_HILO, bool TWO>
 static hipError_t launch_decode_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_kernel<FMT, P_HILO>), grid, dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((decode_kernel<FMT, P_HILO, TWO>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
 }
 
-template <int FMT, bool P_HILO>
+template <int FMT, bool P_HILO, bool TWO>
 static hipError_t launch_decode_kp_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_kp_kernel<FMT, P_HILO>), grid, dim3(512), 0, stream, a);
+  hipLaunchKernelGGL((decode_kp_kernel<FMT, P_HILO, TWO>), grid, dim3(512), 0, stream, a);
   return hipGetLastError();
+}
+
+template <int FMT, bool TWO>
+static hipError_t launch_decode_s(const DecodeArgs &a, bool pairs, hipStream_t stream) {
+  if (pairs)
+    return a.hilo ? launch_decode_kp_t<FMT, true, TWO>(a, stream) : launch_decode_kp_t<FMT, false, TWO>(a, stream);
+  return a.hilo ? launch_decode_t<FMT, true, TWO>(a, stream) : launch_decode_t<FMT, false, TWO>(a, stream);
 }
 
 template <int FMT>
 static hipError_t launch_decode_f(const DecodeArgs &a, bool pairs, hipStream_t stream) {
-  if (pairs) return a.hilo ? launch_decode_kp_t<FMT, true>(a, stream) : launch_decode_kp_t<FMT, false>(a, stream);
-  return a.hilo ? launch_decode_t<FMT, true>(a, stream) : launch_decode_t<FMT, false>(a, stream);
+  return a.indices2 ? launch_decode_s<FMT, true>(a, pairs, stream) : launch_decode_s<FMT, false>(a, pairs, stream);
 }
 
 // Partials the caller reads are written with the two-part P (FP32-partial
 // precision); partials that only feed the merge into bf16, and the direct
 // bf16 output, use a single bf16 P.  a.G must be M / 32 with pairs (the
-// dim-split kernel), M / 16 without.
+// dim-split kernel), M / 16 without.  a.indices2 non-null: two sources.
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, bool pairs, hipStream_t stream) {
   static_assert((int)kp::kBf16Packed == (int)ks8::kBf16Packed && (int)kp::kFp8 == (int)ks8::kFp8, "formats");
   if (fp8) return launch_decode_f<ks8::kFp8>(a, pairs, stream);

@@ -116,20 +116,23 @@ __device__ __forceinline__ int row_of(const Lane &L) {
 // Loads of one half-tile for dims half h; idx / valid are those of row
 // row_of<FMT>(lane).  Masked rows read the zero row.
 template <int FMT>
-__device__ __forceinline__ void issue(const DecodeArgs &a, uint32_t idx, bool valid, int h, const Lane &L,
-                                      typename Gathered<FMT>::type &g) {
+__device__ __forceinline__ void issue(const DecodeArgs &a, uint32_t idx, bool valid, bool second, int h,
+                                      const Lane &L, typename Gathered<FMT>::type &g) {
   typedef const uint8_t SMD_GLOBAL *gptr;
   if constexpr (FMT == kFp8) {
     const uint8_t *z = ks::g_zero_row;
-    const gptr pn = (gptr)(uintptr_t)(valid ? a.kv_nope + (uint64_t)idx * (uint64_t)a.nope_stride_b : z);
-    const gptr pc = (gptr)(uintptr_t)(valid ? a.kv_scale + (uint64_t)idx * (uint64_t)a.scale_stride_b : z);
+    const gptr pn =
+        (gptr)(uintptr_t)(valid ? ks::nope_base(a, second) + (uint64_t)idx * (uint64_t)a.nope_stride_b : z);
+    const gptr pc =
+        (gptr)(uintptr_t)(valid ? ks::scale_base(a, second) + (uint64_t)idx * (uint64_t)a.scale_stride_b : z);
     const int off = 16 * (L.lane & 3);
     if (h == 0) {
 #pragma unroll
       for (int t = 0; t < 4; ++t) g.n[t] = *(const u32x4 SMD_GLOBAL *)(pn + off + 64 * t);
       g.code = *(const uint32_t SMD_GLOBAL *)pc;
     } else {
-      const gptr pr = (gptr)(uintptr_t)(valid ? a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b : z);
+      const gptr pr =
+          (gptr)(uintptr_t)(valid ? ks::rope_base(a, second) + (uint64_t)idx * (uint64_t)a.rope_stride_b : z);
 #pragma unroll
       for (int t = 0; t < 3; ++t) g.n[t] = *(const u32x4 SMD_GLOBAL *)(pn + 256 + off + 64 * t);
 #pragma unroll
@@ -138,10 +141,10 @@ __device__ __forceinline__ void issue(const DecodeArgs &a, uint32_t idx, bool va
     }
   } else {
     constexpr bool PACKED = FMT == kBf16Packed;
-    const uint64_t naddr = ks::row_address<PACKED>(a, idx, valid);
+    const uint64_t naddr = ks::row_address<PACKED>(a, idx, valid, second);
     uint64_t raddr = 0;
     if constexpr (!PACKED)
-      raddr = valid ? (uint64_t)(uintptr_t)(a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b)
+      raddr = valid ? (uint64_t)(uintptr_t)(ks::rope_base(a, second) + (uint64_t)idx * (uint64_t)a.rope_stride_b)
                     : (uint64_t)(uintptr_t)ks::g_zero_row + 2 * kNope;
     const int c = L.lane & 31;
     const bool hi = L.lane >= 32;
@@ -309,13 +312,14 @@ __device__ __forceinline__ uint32_t row_bits(bool v) {
 }
 
 // Start the pipeline: indices of half-tiles 0 and 1, rows of half-tile 0.
-template <int FMT>
-__device__ __forceinline__ void prime(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int k, int h,
+template <int FMT, class SRC>
+__device__ __forceinline__ void prime(const DecodeArgs &a, const SRC &src, int p0, int p1, int k, int h,
                                       const Lane &L, Pipe<FMT> &pp) {
-  const int32_t i0 = row_idx[min(pos_of<FMT>(p0, k, 0, L), p1 - 1)];
-  pp.i_next = row_idx[min(pos_of<FMT>(p0, k, 1, L), p1 - 1)];
-  const bool v0 = pos_of<FMT>(p0, k, 0, L) < p1 && (uint32_t)i0 < a.num_rows32;
-  issue<FMT>(a, (uint32_t)i0, v0, h, L, pp.g);
+  const int q0 = min(pos_of<FMT>(p0, k, 0, L), p1 - 1);
+  const int32_t i0 = src.at(q0);
+  pp.i_next = src.at(min(pos_of<FMT>(p0, k, 1, L), p1 - 1));
+  const bool v0 = pos_of<FMT>(p0, k, 0, L) < p1 && src.row_ok(a, q0, i0);
+  issue<FMT>(a, (uint32_t)i0, v0, src.in_second(q0), h, L, pp.g);
   pp.vb = row_bits<FMT>(v0);
 }
 
@@ -338,17 +342,18 @@ __device__ __forceinline__ void exchange_sync(Smem &sm, int wave, int step, cons
 // pair past its last half-tile reads masked rows.  Exchange slots alternate
 // with the step count; a wave rewrites a slot two exchanges later, by which
 // time its partner, having published the exchange in between, has read it.
-template <int FMT, bool P_HILO, int PASS>
-__device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int nk, int wave,
+template <int FMT, bool P_HILO, int PASS, class SRC>
+__device__ __forceinline__ void sweep(const DecodeArgs &a, const SRC &src, int p0, int p1, int nk, int wave,
                                       const Lane &L, const PLane &P, Smem &sm, State &st, Pipe<FMT> &pp) {
   const int k = wave >> 1, h = wave & 1;
   const uint8_t SMD_LDS *qh = (const uint8_t SMD_LDS *)sm.u.m.q + h * (16 * 64 * 16);
   uint8_t SMD_LDS *buf = (uint8_t SMD_LDS *)sm.u.m.buf[wave];
   for (int i = 0; i < nk; ++i) {
     store(pp.g, h, buf, L);
-    const bool vn = pos_of<FMT>(p0, k, i + 1, L) < p1 && (uint32_t)pp.i_next < a.num_rows32;
-    issue<FMT>(a, (uint32_t)pp.i_next, vn, h, L, pp.g);
-    pp.i_next = row_idx[min(pos_of<FMT>(p0, k, i + 2, L), p1 - 1)];
+    const int qn = min(pos_of<FMT>(p0, k, i + 1, L), p1 - 1);
+    const bool vn = pos_of<FMT>(p0, k, i + 1, L) < p1 && src.row_ok(a, qn, pp.i_next);
+    issue<FMT>(a, (uint32_t)pp.i_next, vn, src.in_second(qn), h, L, pp.g);
+    pp.i_next = src.at(min(pos_of<FMT>(p0, k, i + 2, L), p1 - 1));
     const uint32_t vb = pp.vb;
     pp.vb = row_bits<FMT>(vn);
     f32x4 s0, s1;
@@ -379,8 +384,8 @@ __device__ __forceinline__ void reset(State &st) {
 // The workgroup's attention over [p0, p1): the main sweep, and the exact-max
 // redo of every wave when any score overflowed its reference (the decision is
 // workgroup-wide, so every wave runs the same barriers).
-template <int FMT, bool P_HILO>
-__device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
+template <int FMT, bool P_HILO, class SRC>
+__device__ __forceinline__ void attend(const DecodeArgs &a, const SRC &src, int p0, int p1, int wave,
                                        const Lane &L, const PLane &P, Smem &sm, State &st, Pipe<FMT> &pp) {
   const int nh = (p1 - p0 + 15) / 16;
   const int nk = (nh + kPairs - 1) / kPairs;
@@ -388,15 +393,15 @@ __device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_i
   reset(st);
   st.overflow = false;
   st.step = 0;
-  sweep<FMT, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, nk, wave, L, P, sm, st, pp);
+  sweep<FMT, P_HILO, ks::kPassMain>(a, src, p0, p1, nk, wave, L, P, sm, st, pp);
   if (__syncthreads_or(st.overflow)) {
     // Rare: a score ran far above its row's first-half-tile max.  Redo with
     // the exact max (a scores-only sweep) as the reference.
     reset(st);
-    prime<FMT>(a, row_idx, p0, p1, k, h, L, pp);
-    sweep<FMT, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, nk, wave, L, P, sm, st, pp);
-    prime<FMT>(a, row_idx, p0, p1, k, h, L, pp);
-    sweep<FMT, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, nk, wave, L, P, sm, st, pp);
+    prime<FMT>(a, src, p0, p1, k, h, L, pp);
+    sweep<FMT, P_HILO, ks::kPassMax>(a, src, p0, p1, nk, wave, L, P, sm, st, pp);
+    prime<FMT>(a, src, p0, p1, k, h, L, pp);
+    sweep<FMT, P_HILO, ks::kPassFixed>(a, src, p0, p1, nk, wave, L, P, sm, st, pp);
   }
 }
 

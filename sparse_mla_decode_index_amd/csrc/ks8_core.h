@@ -191,25 +191,26 @@ __device__ __forceinline__ uint32_t row_bits(bool v) {
 }
 
 template <int FMT>
-__device__ __forceinline__ void issue(const DecodeArgs &a, uint32_t idx, bool valid, const Lane &L,
+__device__ __forceinline__ void issue(const DecodeArgs &a, uint32_t idx, bool valid, bool second, const Lane &L,
                                       typename Gathered<FMT>::type &h) {
   if constexpr (FMT == kFp8)
-    ks::issue_half_fp8(a, idx, valid, L, h);
+    ks::issue_half_fp8(a, idx, valid, second, L, h);
   else
-    ks::issue_half<FMT == kBf16Packed>(a, idx, valid, L, h);
+    ks::issue_half<FMT == kBf16Packed>(a, idx, valid, second, L, h);
 }
 
 // Start the pipeline: indices of half-tiles 0 and 1, rows of half-tile 0.
-template <int FMT>
-__device__ __forceinline__ void prime(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                      const Lane &L, Pipe<FMT> &pp) {
+template <int FMT, class SRC>
+__device__ __forceinline__ void prime(const DecodeArgs &a, const SRC &src, int p0, int p1, int wave, const Lane &L,
+                                      Pipe<FMT> &pp) {
   const int nh = (p1 - p0 + kHalf - 1) / kHalf;
   pp.nk = nh > wave ? (nh - wave + kWaves - 1) / kWaves : 0;
   if (pp.nk == 0) return;
-  const int32_t i0 = row_idx[min(pos_of<FMT>(p0, wave, 0, L), p1 - 1)];
-  pp.i_next = row_idx[min(pos_of<FMT>(p0, wave, 1, L), p1 - 1)];
-  const bool v0 = pos_of<FMT>(p0, wave, 0, L) < p1 && (uint32_t)i0 < a.num_rows32;
-  issue<FMT>(a, (uint32_t)i0, v0, L, pp.h);
+  const int q0 = min(pos_of<FMT>(p0, wave, 0, L), p1 - 1);
+  const int32_t i0 = src.at(q0);
+  pp.i_next = src.at(min(pos_of<FMT>(p0, wave, 1, L), p1 - 1));
+  const bool v0 = pos_of<FMT>(p0, wave, 0, L) < p1 && src.row_ok(a, q0, i0);
+  issue<FMT>(a, (uint32_t)i0, v0, src.in_second(q0), L, pp.h);
   pp.vb = row_bits<FMT>(v0);
 }
 
@@ -219,15 +220,15 @@ __device__ __forceinline__ void prime(const DecodeArgs &a, const int32_t *row_id
 // indices of k+2, then QK, softmax and PV of k from LDS while k+1 is in
 // flight.  Every step issues the same loads (positions past p1 read the zero
 // row), so the compiler's wait counts stay exact.
-template <int FMT, bool P_HILO, int PASS>
-__device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                      const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st,
-                                      Pipe<FMT> &pp) {
+template <int FMT, bool P_HILO, int PASS, class SRC>
+__device__ __forceinline__ void sweep(const DecodeArgs &a, const SRC &src, int p0, int p1, int wave, const Lane &L,
+                                      const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st, Pipe<FMT> &pp) {
   for (int k = 0; k < pp.nk; ++k) {
     store_half(pp.h, buf, L);
-    const bool vn = pos_of<FMT>(p0, wave, k + 1, L) < p1 && (uint32_t)pp.i_next < a.num_rows32;
-    issue<FMT>(a, (uint32_t)pp.i_next, vn, L, pp.h);
-    pp.i_next = row_idx[min(pos_of<FMT>(p0, wave, k + 2, L), p1 - 1)];
+    const int qn = min(pos_of<FMT>(p0, wave, k + 1, L), p1 - 1);
+    const bool vn = pos_of<FMT>(p0, wave, k + 1, L) < p1 && src.row_ok(a, qn, pp.i_next);
+    issue<FMT>(a, (uint32_t)pp.i_next, vn, src.in_second(qn), L, pp.h);
+    pp.i_next = src.at(min(pos_of<FMT>(p0, wave, k + 2, L), p1 - 1));
     const uint32_t vb = pp.vb;
     pp.vb = row_bits<FMT>(vn);
     const f32x4 s = qk_lds(qs, buf, L);
@@ -239,16 +240,15 @@ __device__ __forceinline__ void sweep(const DecodeArgs &a, const int32_t *row_id
 
 // The wave's attention over its share of [p0, p1) from a primed pipeline: the
 // main sweep, and the exact-max redo when a score overflowed the reference.
-template <int FMT, bool P_HILO>
-__device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_idx, int p0, int p1, int wave,
-                                       const Lane &L, const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st,
-                                       Pipe<FMT> &pp) {
+template <int FMT, bool P_HILO, class SRC>
+__device__ __forceinline__ void attend(const DecodeArgs &a, const SRC &src, int p0, int p1, int wave, const Lane &L,
+                                       const uint8_t SMD_LDS *qs, uint8_t SMD_LDS *buf, State &st, Pipe<FMT> &pp) {
 #pragma unroll
   for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
   st.m_ref = -INFINITY;
   st.l_run = 0.f;
   st.overflow = false;
-  sweep<FMT, P_HILO, ks::kPassMain>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
+  sweep<FMT, P_HILO, ks::kPassMain>(a, src, p0, p1, wave, L, qs, buf, st, pp);
   if (__ballot(st.overflow)) {  // wave-uniform
     // Rare: a score ran far above its row's first-half-tile max.  Redo this
     // wave's share with the exact max (a scores-only sweep) as the reference.
@@ -256,10 +256,10 @@ __device__ __forceinline__ void attend(const DecodeArgs &a, const int32_t *row_i
     for (int d = 0; d < 32; ++d) st.acc[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m_ref = -INFINITY;
     st.l_run = 0.f;
-    prime<FMT>(a, row_idx, p0, p1, wave, L, pp);
-    sweep<FMT, P_HILO, ks::kPassMax>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
-    prime<FMT>(a, row_idx, p0, p1, wave, L, pp);
-    sweep<FMT, P_HILO, ks::kPassFixed>(a, row_idx, p0, p1, wave, L, qs, buf, st, pp);
+    prime<FMT>(a, src, p0, p1, wave, L, pp);
+    sweep<FMT, P_HILO, ks::kPassMax>(a, src, p0, p1, wave, L, qs, buf, st, pp);
+    prime<FMT>(a, src, p0, p1, wave, L, pp);
+    sweep<FMT, P_HILO, ks::kPassFixed>(a, src, p0, p1, wave, L, qs, buf, st, pp);
   }
 }
 

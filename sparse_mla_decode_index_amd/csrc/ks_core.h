@@ -114,23 +114,58 @@ __device__ __forceinline__ Lane make_lane(int lane) {
   return L;
 }
 
+// The index list of one index row.  With two sources, positions [0, km) are
+// entries of the first list (rows of the first pool) and positions [km, K)
+// entries of the second list (rows of the second pool), in that order; with
+// one source every position is in the first.
+template <bool TWO>
+struct Src {
+  const int32_t *first;
+  const int32_t *second;
+  int km;
+  __device__ __forceinline__ bool in_second(int p) const { return TWO && p >= km; }
+  __device__ __forceinline__ int32_t at(int p) const {
+    if constexpr (TWO)
+      return *(p < km ? first + p : second + (p - km));
+    else
+      return first[p];
+  }
+  // index idx at position p names a row of its pool
+  __device__ __forceinline__ bool row_ok(const DecodeArgs &a, int p, int32_t idx) const {
+    return (uint32_t)idx < (in_second(p) ? a.num_rows2_32 : a.num_rows32);
+  }
+};
+
+// Base of the NoPE / RoPE / code arrays of the pool a row comes from.
+__device__ __forceinline__ const uint8_t *nope_base(const DecodeArgs &a, bool second) {
+  return second ? a.kv2_nope : a.kv_nope;
+}
+__device__ __forceinline__ const uint8_t *rope_base(const DecodeArgs &a, bool second) {
+  return second ? a.kv2_rope : a.kv_rope;
+}
+__device__ __forceinline__ const uint8_t *scale_base(const DecodeArgs &a, bool second) {
+  return second ? a.kv2_scale : a.kv_scale;
+}
+
 // Address of row l % 16 of a half-tile in lane l: the selected NoPE row, or
 // the zero row when the position is past the range or the index is invalid.
 template <bool PACKED>
-__device__ __forceinline__ uint64_t row_address(const DecodeArgs &a, uint32_t idx, bool valid) {
+__device__ __forceinline__ uint64_t row_address(const DecodeArgs &a, uint32_t idx, bool valid, bool second) {
   const uint64_t stride = PACKED ? (uint64_t)a.row_stride32 : (uint64_t)a.nope_stride_b;
-  return valid ? (uint64_t)(uintptr_t)(a.kv_nope + (uint64_t)idx * stride) : (uint64_t)(uintptr_t)g_zero_row;
+  return valid ? (uint64_t)(uintptr_t)(nope_base(a, second) + (uint64_t)idx * stride)
+               : (uint64_t)(uintptr_t)g_zero_row;
 }
 
 // One contiguous 1 KiB load per row; row i's base is read from lane i of the
 // address vector.  Split layouts (RoPE in its own array) take lanes 56..63
 // from the RoPE row.
 template <bool PACKED>
-__device__ __forceinline__ void issue_half(const DecodeArgs &a, uint32_t idx, bool valid, const Lane &L, Half &h) {
-  const uint64_t naddr = row_address<PACKED>(a, idx, valid);
+__device__ __forceinline__ void issue_half(const DecodeArgs &a, uint32_t idx, bool valid, bool second, const Lane &L,
+                                           Half &h) {
+  const uint64_t naddr = row_address<PACKED>(a, idx, valid, second);
   uint64_t raddr = 0;
   if constexpr (!PACKED)
-    raddr = valid ? (uint64_t)(uintptr_t)(a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b)
+    raddr = valid ? (uint64_t)(uintptr_t)(rope_base(a, second) + (uint64_t)idx * (uint64_t)a.rope_stride_b)
                   : (uint64_t)(uintptr_t)g_zero_row + 2 * kNope;
   // The rebuilt row pointers are global-address-space pointers, so the loads
   // are global loads with the row base in SGPRs: a generic (flat) load would
@@ -171,13 +206,13 @@ struct Half8 {
 
 // Loads of one fp8 half-tile; idx / valid are those of row lane / 4.  Masked
 // rows read the zero row (e4m3 zeros, code 0).
-__device__ __forceinline__ void issue_half_fp8(const DecodeArgs &a, uint32_t idx, bool valid, const Lane &L,
-                                               Half8 &h) {
+__device__ __forceinline__ void issue_half_fp8(const DecodeArgs &a, uint32_t idx, bool valid, bool second,
+                                               const Lane &L, Half8 &h) {
   typedef const uint8_t SMD_GLOBAL *gptr;
   const uint8_t *z = g_zero_row;
-  const gptr pn = (gptr)(uintptr_t)(valid ? a.kv_nope + (uint64_t)idx * (uint64_t)a.nope_stride_b : z);
-  const gptr pr = (gptr)(uintptr_t)(valid ? a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b : z);
-  const gptr pc = (gptr)(uintptr_t)(valid ? a.kv_scale + (uint64_t)idx * (uint64_t)a.scale_stride_b : z);
+  const gptr pn = (gptr)(uintptr_t)(valid ? nope_base(a, second) + (uint64_t)idx * (uint64_t)a.nope_stride_b : z);
+  const gptr pr = (gptr)(uintptr_t)(valid ? rope_base(a, second) + (uint64_t)idx * (uint64_t)a.rope_stride_b : z);
+  const gptr pc = (gptr)(uintptr_t)(valid ? scale_base(a, second) + (uint64_t)idx * (uint64_t)a.scale_stride_b : z);
   const int off = 16 * (L.lane & 3);
 #pragma unroll
   for (int t = 0; t < 7; ++t) h.n[t] = *(const u32x4 SMD_GLOBAL *)(pn + off + 64 * t);

@@ -40,6 +40,17 @@ struct DecodeArgs {
   uint16_t *out;           // bf16 [T, H, 512] (direct output when S == 1)
   float *lse;              // [T, H] or null
   int32_t hilo;            // partials are returned to the caller: carry p as bf16 hi + lo
+  // Second source (the sliding-window pool and its index list), same format
+  // and strides as the first; indices2 null for one source.  Positions
+  // [0, k_main) of an index row are entries of `indices`, [k_main, topk)
+  // entries of `indices2`.
+  const uint8_t *kv2_nope;
+  const uint8_t *kv2_rope;
+  const uint8_t *kv2_scale;
+  uint32_t num_rows2_32;
+  const int32_t *indices2;
+  int64_t indices2_stride;  // elements
+  int32_t k_main;
 };
 
 // Launch the split-KV decode: one workgroup per (index row, split, block of

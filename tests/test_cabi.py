@@ -323,3 +323,60 @@ def test_writer_rejects_bad_pool(pkw, code, msg):
 
 def test_writer_empty_launches_nothing():
     assert _write(n=0, kv=None)[0] == 0
+
+
+# ----------------------------------------------------------------------------
+# host validation of the two-source decode
+# ----------------------------------------------------------------------------
+def _two(main=None, swa=None, **kw):
+    a = dict(q_nope=0x20000, q_rope=0x30000, T=4, H=64, qps=1, mi=0x40000, ms=100, km=100, si=0x48000, ss=128,
+             ks=128, sink=None, scale=0.04, s=1, po=None, pl=None, out=0x50000, lse=0x60000)
+    a.update(kw)
+    mp = main if main is not None else _pool()
+    sp = swa if swa is not None else _pool(nope=0x90000, rope=0x90000 + 896, num_rows=512)
+    rc = smd.lib().smd_sparse_mla_decode_two_source(
+        a["q_nope"], a["q_rope"], a["T"], a["H"], a["qps"], ctypes.byref(mp), a["mi"], a["ms"], a["km"],
+        ctypes.byref(sp), a["si"], a["ss"], a["ks"], a["sink"], a["scale"], a["s"], a["po"], a["pl"], a["out"],
+        a["lse"], None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(ks=-1), -1, "negative"),
+    (dict(ss=-4), -1, "negative"),
+    (dict(si=None), -1, "index lists are required"),
+    (dict(mi=None), -1, "index lists are required"),
+    (dict(ss=100), -1, "swa indices stride"),
+    (dict(ms=50), -1, "indices_stride"),
+    (dict(km=2 ** 31 - 100, ms=2 ** 31), -1, "exceed"),
+    (dict(H=24), -2, "num_heads"),
+    (dict(s=2), -3, "partial_o"),
+])
+def test_two_source_rejects(kw, code, msg):
+    rc, err = _two(**kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+@pytest.mark.parametrize("skw,code,msg", [
+    (dict(dtype=smd.KV_FP8_E4M3_UE8M0, nope_stride=448, rope_stride=64, scale=0x70000, scale_stride=8), -2,
+     "same dtype"),
+    (dict(nope=0x90000, rope=0xA0000), -2, "RoPE placement"),        # split arrays against a packed main pool
+    (dict(nope=0x90000, rope=0x90000 + 896, nope_stride=520, rope_stride=520), -2, "row strides"),
+    (dict(nope=0x90008), -1, "16-byte aligned"),
+])
+def test_two_source_rejects_bad_swa_pool(skw, code, msg):
+    rc, err = _two(swa=_pool(**skw))
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_two_source_null_swa_pool():
+    L = smd.lib()
+    p = _pool()
+    rc = L.smd_sparse_mla_decode_two_source(0x20000, 0x30000, 4, 64, 1, ctypes.byref(p), 0x40000, 100, 100, None,
+                                            0x48000, 128, 128, None, 0.04, 1, None, None, 0x50000, 0x60000, None)
+    assert rc == -1 and "NULL" in L.smd_last_error().decode()
+
+
+def test_two_source_empty_launches_nothing():
+    assert _two(km=0, ks=0, mi=None, si=None)[0] == 0
+    assert _two(T=0)[0] == 0

@@ -243,14 +243,14 @@ def two_source_workload(name: str, *, T: int, H: int, kv_dtype: str, main_rows: 
     q_nope, q_rope = _queries(rng, T, H)
     R = T // q_per_seq
     main = _pool(rng, kv_dtype, main_rows)
-    swa = _pool(rng, kv_dtype, R * window)
+    swa = _pool(rng, kv_dtype, max(R * window, 1))
     sink = rng.standard_normal(H, dtype=np.float32)
     midx = np.empty((R, topk), dtype=np.int32)
     for r in range(R):
         midx[r] = rng.choice(main_rows, size=topk, replace=False)
     _set_invalid(rng, midx, invalid)
     sidx = np.empty((R, window), dtype=np.int32)
-    for r in range(R):
+    for r in range(R if window else 0):
         start = int(rng.integers(0, window))
         sidx[r] = r * window + (start + np.arange(window)) % window
         sidx[r, :swa_invalid] = -1
