@@ -44,7 +44,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=1,
-                    help="workload 0..4 (1 = bf16 T=8 H=64 K=2176; 4 = ragged MTP4 fp8, persistent kernel)")
+                    help="workload 0..5 (1 = bf16 T=8 H=64 K=2176; 4 = ragged MTP4 fp8, persistent kernel; "
+                         "5 = fp8 two-source, top-k 2048 main + 128-row window)")
     ap.add_argument("--cell", type=str, default=None, help="T x ctx matrix cell T:ctx:variant instead of --config")
     ap.add_argument("--splits", type=int, default=None, help="override the planner's split count")
     ap.add_argument("--partitions", type=int, default=None, help="persistent kernel: override the partition count")
@@ -78,12 +79,19 @@ def to_device(w, dev):
     def bf(x):
         return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
 
-    if w.kv_dtype == "bf16":
-        pool = smd.KVPool.bf16(bf(a["kv"]))
-    else:
-        pool = smd.KVPool.fp8(torch.from_numpy(a["nope"]).to(dev), torch.from_numpy(a["scale"]).to(dev),
-                              bf(a["rope"]))
-    d = dict(q_nope=bf(a["q_nope"]), q_rope=bf(a["q_rope"]), pool=pool, sink=torch.from_numpy(a["sink"]).to(dev))
+    def dev_pool(p):
+        if "kv" in p:
+            return smd.KVPool.bf16(bf(p["kv"]))
+        return smd.KVPool.fp8(torch.from_numpy(p["nope"]).to(dev), torch.from_numpy(p["scale"]).to(dev),
+                              bf(p["rope"]))
+
+    d = dict(q_nope=bf(a["q_nope"]), q_rope=bf(a["q_rope"]), sink=torch.from_numpy(a["sink"]).to(dev))
+    if w.two_source:
+        d["pool"], d["swa_pool"] = dev_pool(a["main"]), dev_pool(a["swa"])
+        d["indices"] = torch.from_numpy(a["main_indices"]).to(dev)
+        d["swa_indices"] = torch.from_numpy(a["swa_indices"]).to(dev)
+        return d
+    d["pool"] = dev_pool(a)
     if w.ragged:
         d["kv_indptr"] = torch.from_numpy(a["kv_indptr"]).to(dev)
         d["kv_indices"] = torch.from_numpy(a["kv_indices"]).to(dev)
@@ -98,9 +106,16 @@ def cpu_baseline(w, target_s: float):
     share of gathered rows the sample covered."""
     from oracle import ref
     a = w.arrays
-    pool = {"kv": a["kv"]} if w.kv_dtype == "bf16" else {"nope": a["nope"], "scale": a["scale"], "rope": a["rope"]}
     qps = w.q_per_seq
-    if w.ragged:
+    if w.two_source:
+        pool = None
+    else:
+        pool = {"kv": a["kv"]} if w.kv_dtype == "bf16" else {"nope": a["nope"], "scale": a["scale"],
+                                                             "rope": a["rope"]}
+    if w.two_source:
+        rows = list(range(w.num_index_rows))
+        lens = {b: a["main_indices"].shape[1] + a["swa_indices"].shape[1] for b in rows}
+    elif w.ragged:
         ptr = a["kv_indptr"]
         rows = [b for b in range(len(ptr) - 1) if ptr[b + 1] > ptr[b]]
         lens = {b: int(ptr[b + 1] - ptr[b]) for b in rows}
@@ -113,7 +128,10 @@ def cpu_baseline(w, target_s: float):
     while t_used < target_s and done < 100000:
         b = rows[done % len(rows)]
         qn, qr = a["q_nope"][b * qps:(b + 1) * qps], a["q_rope"][b * qps:(b + 1) * qps]
-        if w.ragged:
+        if w.two_source:
+            ref.sparse_mla_decode_two_source(qn, qr, a["main"], a["main_indices"][b:b + 1], a["swa"],
+                                             a["swa_indices"][b:b + 1], a["sink"], w.softmax_scale, qps)
+        elif w.ragged:
             ref.sparse_mla_decode_ragged(qn, qr, pool, np.array([0, lens[b]]), a["kv_indices"][ptr[b]:ptr[b + 1]],
                                          a["sink"], w.softmax_scale, qps)
         else:
@@ -418,7 +436,9 @@ def main():
         cfg.update({"num_seqs": T // qps, "sum_k": int(w.arrays["kv_indptr"][-1] - w.arrays["kv_indptr"][0]),
                     "num_partitions": P, "kernel": "persistent"})
     else:
-        K = w.arrays["indices"].shape[1]
+        two = w.two_source
+        K = (w.arrays["main_indices"].shape[1] + w.arrays["swa_indices"].shape[1] if two
+             else w.arrays["indices"].shape[1])
         R = w.num_index_rows
 
         def plan():
@@ -429,9 +449,15 @@ def main():
         pl = torch.empty((T, H, s), dtype=torch.float32, device=dev)
 
         def step():
-            smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
-                                  num_splits=s, q_per_seq=qps, out=out, lse=lse,
-                                  partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
+            if two:
+                smd.sparse_mla_decode_two_source(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["swa_pool"],
+                                                 d["swa_indices"], d["sink"], w.softmax_scale, num_splits=s,
+                                                 q_per_seq=qps, out=out, lse=lse,
+                                                 partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
+            else:
+                smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
+                                      num_splits=s, q_per_seq=qps, out=out, lse=lse,
+                                      partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
 
         kernel_step = step  # decode (+ merge when split; its time is subtracted below)
 
@@ -440,6 +466,9 @@ def main():
 
         kernel_name = "smd::decode_kernel"
         cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv"})
+        if two:
+            cfg.update({"main_topk": w.arrays["main_indices"].shape[1], "swa_window": w.arrays["swa_indices"].shape[1],
+                        "sources": 2})
 
     # the inputs and outputs were made on the default stream: order the side
     # stream after them before it touches them
