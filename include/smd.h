@@ -275,11 +275,12 @@ int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t
  * positions (K_b = kv_indptr[b+1] - kv_indptr[b]); the tiles of all
  * sequences are concatenated in (sequence, tile) order, and partition p of
  * num_partitions owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
- * The kernel runs P x ceil(M / 64) workgroups (M = num_heads * q_per_seq; for
- * M < 64 one group of M rows).
+ * The kernel runs P x G workgroups, G = M / R query-row groups of R rows
+ * (M = num_heads * q_per_seq; R = 128 when 128 divides M, else 64, 32 or 16,
+ * the largest that divides M).
  */
 
-/* P that fills num_cus CUs once: num_cus / ceil(M / 64), at least 1
+/* P that fills num_cus CUs once: num_cus / G (G as above), at least 1
  * (num_cus <= 0 means 256).  Host only.  Negative SMD_ERR_* on bad shapes. */
 int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, int32_t num_cus);
 

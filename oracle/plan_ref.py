@@ -165,8 +165,8 @@ def partition(kv_indptr, num_partitions: int):
 
 def default_partitions(num_heads: int, q_per_seq: int, num_cus: int = 256, wg_per_cu: int = 1) -> int:
     """Partitions that fill the machine once: num_cus * wg_per_cu workgroups over
-    the query-row groups of M = num_heads * q_per_seq rows.  A group is 64 rows
-    when 64 divides M, else 32 when 32 does, else 16."""
+    the query-row groups of M = num_heads * q_per_seq rows.  A group is 128 rows
+    when 128 divides M, else 64 when 64 does, else 32 when 32 does, else 16."""
     M = num_heads * q_per_seq
-    rows = 64 if M % 64 == 0 else (32 if M % 32 == 0 else 16)
+    rows = 128 if M % 128 == 0 else (64 if M % 64 == 0 else (32 if M % 32 == 0 else 16))
     return max(1, (num_cus * wg_per_cu) // (M // rows))

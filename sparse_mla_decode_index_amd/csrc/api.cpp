@@ -327,7 +327,13 @@ extern "C" int smd_merge_partials(const float *partial_o, const float *partial_l
 // ----------------------------------------------------------------------------
 // Row blocks per workgroup of the persistent kernel: the largest of 4, 2, 1
 // that divides M / 16, so the 16*rb-row groups cover every query row.
-static int persist_rb(int32_t M) { return M % 64 == 0 ? 4 : (M % 32 == 0 ? 2 : 1); }
+static int persist_rb(int32_t M) {
+  if (const char *e = getenv("SMD_PERSIST_RB")) {
+    const int r = atoi(e);
+    if ((r == 1 || r == 2 || r == 4 || r == 8) && M % (16 * r) == 0) return r;
+  }
+  return M % 128 == 0 ? 8 : (M % 64 == 0 ? 4 : (M % 32 == 0 ? 2 : 1));
+}
 static int32_t persist_groups(int32_t M) { return M / (16 * persist_rb(M)); }
 
 extern "C" int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, int32_t num_cus) {

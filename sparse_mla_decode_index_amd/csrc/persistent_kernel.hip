@@ -9,8 +9,9 @@
 // tiles of all sequences are concatenated in (sequence, tile) order, and
 // partition p of P owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
 //
-// Grid: P partitions x G query-row groups of 16*RB rows, RB the largest of 4,
-// 2, 1 that divides M / 16.  Workgroup (p, g) walks the sequences of partition
+// Grid: P partitions x G query-row groups of 16*RB rows, RB the largest of 8,
+// 4, 2, 1 that divides M / 16 (8: the wide waves of decode_core.h, each wave
+// 32 rows, so one gathered tile serves 128 query rows).  Workgroup (p, g) walks the sequences of partition
 // p and attends row group g of each over the piece of its index list that p
 // owns.  A sequence inside one partition is
 // written directly.  A sequence spread over partitions fp..lp is split: each
@@ -22,6 +23,8 @@
 // the kernel can be replayed in a graph without any host-side reset.
 // Sequences with K_b = 0 own no tile and are never written.
 #include "decode_core.h"
+
+#include <type_traits>
 
 namespace smd {
 
@@ -204,12 +207,15 @@ __device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int
   return t0 < t1;
 }
 
+// RB = 8 runs the wide waves of decode_core.h: wave w owns blocks w and w+4
+// of the group's 128 rows, all 512 dims.
 template <int RB, bool FP8, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void persistent_kernel(PersistArgs pa) {
-  constexpr int DS = 4 / RB;
+  constexpr bool WIDE = RB == 8;
+  constexpr int DS = WIDE ? 1 : 4 / RB;
   constexpr int NC = 16 / DS, ND = 32 / DS;
   constexpr int ROWS = 16 * RB;
-  __shared__ __attribute__((aligned(1024))) Smem<DS> sm;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<2>, Smem<DS>> sm;
   __shared__ int s_red[4];
   __shared__ int s_first[2];
   __shared__ int s_last;
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rb = wave % RB, ds = wave / RB;
+  const int rb = WIDE ? wave : wave % RB, ds = WIDE ? 0 : wave / RB;
   const int j = lane & 15;
   const int grp = lane >> 4;
 
@@ -252,20 +258,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int fp = tile_owner(start, total, pa.P);
     const int lp = tile_owner(start + tb - 1, total, pa.P);
 
-    const int64_t qrow = (int64_t)(b * a.qps + m / a.H) * a.H + head;
-    bf16x8 qreg[NC];
-    load_q<DS>(a, qrow, ds, grp, qreg);
-    WaveState<ND> w;
-    attend_range<RB, FP8, PACKED, false>(a, sm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, ds, qreg,
-                                         qk_base, pv_base, w);
-    const float l_tot = row_total(w.l_run);
-    if (fp == lp) {
-      write_direct(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
-                   (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
+    const int slot = 2 * p + (b == b_first ? 0 : 1);
+    float *sb = pa.slots + slot * slot_floats;
+    if constexpr (WIDE) {
+      int64_t qrow[2];
+      int mq[2], hq[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        mq[q] = g * ROWS + (wave + 4 * q) * 16 + j;
+        hq[q] = mq[q] % a.H;
+        qrow[q] = (int64_t)(b * a.qps + mq[q] / a.H) * a.H + hq[q];
+      }
+      bf16x8 qreg[2][kQReg];
+      load_q_wide<2>(a, qrow, lane, grp, (uint8_t SMD_LDS *)&sm.qs[wave][0][0][0], qreg);
+      WideState<2> w;
+      attend_range_wide<2, FP8, PACKED, false>(a, sm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, qreg,
+                                               qk_base, pv_base, w);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const float l_tot = row_total(w.l_run[q]);
+        if (fp == lp)
+          write_direct_wide(w, q, l_tot, a.sink ? a.sink[hq[q]] : -INFINITY, a.out + qrow[q] * kDim + 4 * grp,
+                            (a.lse != nullptr && grp == 0) ? a.lse + qrow[q] : nullptr);
+        else
+          write_partial_wide(w, q, l_tot, sb + (size_t)mq[q] * kDim + 4 * grp,
+                             grp == 0 ? sb + (size_t)a.M * kDim + mq[q] : nullptr);
+      }
     } else {
-      const int slot = 2 * p + (b == b_first ? 0 : 1);
-      float *sb = pa.slots + slot * slot_floats;
-      write_partial(w, l_tot, sb + (size_t)m * kDim + dcol, lse_lane ? sb + (size_t)a.M * kDim + m : nullptr);
+      const int64_t qrow = (int64_t)(b * a.qps + m / a.H) * a.H + head;
+      bf16x8 qreg[NC];
+      load_q<DS>(a, qrow, ds, grp, qreg);
+      WaveState<ND> w;
+      attend_range<RB, FP8, PACKED, false>(a, sm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, ds, qreg,
+                                           qk_base, pv_base, w);
+      const float l_tot = row_total(w.l_run);
+      if (fp == lp)
+        write_direct(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
+                     (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
+      else
+        write_partial(w, l_tot, sb + (size_t)m * kDim + dcol, lse_lane ? sb + (size_t)a.M * kDim + m : nullptr);
+    }
+    if (fp != lp) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release this piece (other XCDs read it)
       __syncthreads();
       uint32_t *ctr = pa.counters + (size_t)g * pa.P + fp;
@@ -301,12 +334,13 @@ static hipError_t launch_persistent_rb(const PersistArgs &a, bool fp8, hipStream
                     : launch_persistent_t<RB, false, false>(a, stream);
 }
 
-// rb query-row blocks of 16 per workgroup, a.d.G = M / (16 rb).
+// rb query-row blocks of 16 per workgroup (8: wide waves), a.d.G = M / (16 rb).
 hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream) {
   switch (rb) {
     case 1: return launch_persistent_rb<1>(a, fp8, stream);
     case 2: return launch_persistent_rb<2>(a, fp8, stream);
     case 4: return launch_persistent_rb<4>(a, fp8, stream);
+    case 8: return launch_persistent_rb<8>(a, fp8, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -82,7 +82,7 @@ struct PersistLayout {
 };
 PersistLayout persist_layout(int64_t M, int64_t P);
 
-// rb in {1, 2, 4} query-row blocks of 16 per workgroup; a.d.G = M / (16 rb).
+// rb in {1, 2, 4, 8} query-row blocks of 16 per workgroup; a.d.G = M / (16 rb).
 hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream);
 
 // Arguments of the fp8/UE8M0 cache writer.  Pointers are device pointers.

@@ -117,8 +117,10 @@ def test_partition_edge_cases():
 
 
 def test_default_partitions():
-    assert pr.default_partitions(128, 4) == 32  # M = 512: eight 64-row groups
-    assert pr.default_partitions(128, 1) == 128
+    assert pr.default_partitions(128, 4) == 64  # M = 512: four 128-row groups
+    assert pr.default_partitions(128, 1) == 256  # M = 128: one group
+    assert pr.default_partitions(64, 2) == 256   # M = 128
+    assert pr.default_partitions(64, 3) == 85    # M = 192: three 64-row groups
     assert pr.default_partitions(16, 1) == 256  # M = 16: one 16-row group
     assert pr.default_partitions(16, 3) == 85   # M = 48: three 16-row groups
     assert pr.default_partitions(32, 3) == 85   # M = 96: three 32-row groups
