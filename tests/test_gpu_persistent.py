@@ -84,16 +84,17 @@ def test_fp8_mtp_small(gpu, P):
     run_persistent(w, gpu, P)
 
 
-@pytest.mark.parametrize("H,qps,P", [(16, 1, 6), (16, 3, 5), (16, 5, 9), (32, 3, 7), (16, 6, 4)])
+@pytest.mark.parametrize("H,qps,P", [(16, 1, 6), (16, 3, 5), (16, 5, 9), (32, 3, 7), (16, 6, 4), (128, 3, 7)])
 def test_row_groups_of_every_width(gpu, H, qps, P):
-    """M = 16, 48, 80 (16-row groups), 96 (32-row groups), 96 via H=16 x 6:
-    every row of every sequence is written."""
+    """M = 16, 48, 80 (16-row groups), 96 (32-row groups), 96 via H=16 x 6,
+    384 (three 128-row groups of wide waves): every row of every sequence is
+    written."""
     w = wl.ragged_workload("persist row groups", B=5, q_per_seq=qps, H=H, kv_dtype="fp8", pool_rows=3000,
                            max_k=600, zero_rows=1, seed=70 + H + qps + P)
     run_persistent(w, gpu, P)
 
 
-@pytest.mark.parametrize("H,qps,P", [(64, 1, 5), (128, 1, 16), (32, 1, 9), (16, 4, 11)])
+@pytest.mark.parametrize("H,qps,P", [(64, 1, 5), (128, 1, 16), (32, 1, 9), (16, 4, 11), (64, 4, 9)])
 def test_bf16_shapes(gpu, H, qps, P):
     w = wl.ragged_workload("persist bf16", B=5, q_per_seq=qps, H=H, kv_dtype="bf16", pool_rows=4096, max_k=900,
                            zero_rows=1, indptr_offset=37, seed=80 + H + qps + P)
