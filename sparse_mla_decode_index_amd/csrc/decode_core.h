@@ -549,275 +549,4 @@ __device__ __forceinline__ void write_partial(const WaveState<ND> &w, float l_to
   if (lse_dst != nullptr) *lse_dst = lse_v;
 }
 
-// ----------------------------------------------------------------------------
-// Wide waves: each of the 4 waves owns NQ blocks of 16 query rows (all 512
-// dims), so every K fragment and every transposed V fragment read from LDS
-// feeds NQ MFMAs, and one gathered tile serves 64*NQ query rows.  With NQ = 2
-// a wave holds 256 accumulator registers and 128 of Q^T, so only one staged
-// register set of rows is in flight (the rows of tile t+1 land while tile t
-// is computed).
-// ----------------------------------------------------------------------------
-
-// Q^T k-steps kQReg.. of the wave's blocks live in LDS (16 B per lane and
-// step, each wave reads only its own region), the first kQReg in VGPRs: the
-// accumulators take all 256 AGPRs, and Q^T entirely in VGPRs would spill.
-#ifndef SMD_WIDE_QREG
-#define SMD_WIDE_QREG 6
-#endif
-#ifndef SMD_WIDE_KPRE
-#define SMD_WIDE_KPRE 2
-#endif
-#ifndef SMD_WIDE_KPV
-#define SMD_WIDE_KPV 8
-#endif
-constexpr int kQReg = SMD_WIDE_QREG;
-
-template <int NQ>
-struct SmemWide {
-  uint8_t tile[2][kTileBytes];                 // double-buffered bf16 tiles
-  int32_t ibuf[2][kIdxBlock];                  // index blocks, as in Smem
-  uint8_t qs[4][NQ][16 - kQReg][64 * 16];      // [wave][block][k-step - kQReg][lane]
-};
-
-template <int NQ>
-struct WideState {
-  f32x4 acc[NQ][32];  // acc[q][d][i] = sum_j 2^(x_j - m_ref[q]) V[j][16d + 4grp + i], block q
-  float m_ref[NQ];    // reference max per block (log2 domain), same in the four 16-lane groups
-  float l_run[NQ];    // this lane's share of sum_j 2^(x_j - m_ref[q])
-  bool overflow;      // some score exceeded its m_ref + kRefSlackLog2 (this lane)
-};
-
-// QK, softmax weights and PV of one 32-row tile for a wide wave.  The two kv
-// halves of the tile (rows 0..15, 16..31) make the 32-deep contraction of the
-// PV MFMA: lane group grp supplies P of kv rows 4grp..4grp+3 and
-// 16+4grp..16+4grp+3, and the two transposed V reads give the same rows.
-// PASS as in compute_tile.
-template <int NQ, int PASS, bool P_HILO>
-__device__ __forceinline__ void compute_tile_wide(const uint8_t SMD_LDS *tile, const bf16x8 (&qreg)[NQ][kQReg],
-                                                  const uint8_t SMD_LDS *qs, const int (&qk_base)[4],
-                                                  const int (&pv_base)[8], uint32_t vbits, int lane, int grp,
-                                                  float scale_log2, WideState<NQ> &w) {
-  // ---- QK: S^T tiles of kv rows 0..15 / 16..31 for each block
-  constexpr int kPre = SMD_WIDE_KPRE;  // LDS reads in flight ahead of their MFMAs
-  f32x4 s[NQ][2];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) s[q][0] = s[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 k0[kPre], k1[kPre], ql[kPre][NQ];
-  auto qk_load = [&](int c) {
-    const uint8_t SMD_LDS *p = tile + qk_base[c & 3] + 256 * (c >> 2);
-    k0[c % kPre] = *(const bf16x8 SMD_LDS *)(p);
-    k1[c % kPre] = *(const bf16x8 SMD_LDS *)(p + 16 * kLdsRow);
-    if (c >= kQReg) {
-#pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        ql[c % kPre][q] = *(const bf16x8 SMD_LDS *)(qs + ((q * (16 - kQReg) + c - kQReg) * 64 + lane) * 16);
-    }
-  };
-#pragma unroll
-  for (int c = 0; c < kPre; ++c) qk_load(c);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const bf16x8 a0 = k0[c % kPre], a1 = k1[c % kPre];
-    bf16x8 b[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) b[q] = c < kQReg ? qreg[q][c < kQReg ? c : 0] : ql[c % kPre][q];
-    if (c + kPre < 16) qk_load(c + kPre);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      s[q][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b[q], s[q][0], 0, 0, 0);
-      s[q][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b[q], s[q][1], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads kPre steps ahead of their MFMAs
-  }
-
-  // ---- softmax weights per block; this lane holds kv rows 4grp+i and 16+4grp+i
-  bf16x8 pb[NQ], pl[NQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    float x[8];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = ((vbits >> (4 * grp + i)) & 1) ? s[q][0][i] * scale_log2 : -INFINITY;
-      x[4 + i] = ((vbits >> (16 + 4 * grp + i)) & 1) ? s[q][1][i] * scale_log2 : -INFINITY;
-    }
-    float tmax =
-        fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    tmax = group_max(tmax);
-    if constexpr (PASS == kPassMax) {
-      w.m_ref[q] = fmaxf(w.m_ref[q], tmax);
-      continue;
-    }
-    if constexpr (PASS == kPassMain) {
-      if (w.m_ref[q] == -INFINITY) w.m_ref[q] = tmax;  // nothing accumulated yet for this row
-      w.overflow |= tmax > w.m_ref[q] + kRefSlackLog2;
-    }
-    const float m_use = (w.m_ref[q] == -INFINITY) ? 0.f : w.m_ref[q];
-    float psum = 0.f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = exp2_fast(x[i] - m_use);
-      psum += p;
-      pb[q][i] = (__bf16)p;
-      if constexpr (P_HILO) pl[q][i] = (__bf16)(p - (float)pb[q][i]);
-    }
-    w.l_run[q] += psum;
-  }
-  if constexpr (PASS == kPassMax) return;
-
-  // ---- PV: O^T[16d.., m] += V^T . P^T, each V^T fragment shared by the NQ blocks
-  constexpr int kPv = SMD_WIDE_KPV;
-  bf16x4 vlo[kPv], vhi[kPv];
-  auto pv_load = [&](int d) {
-    const uint8_t SMD_LDS *p = tile + pv_base[d & 7] + 256 * (d >> 3);
-    vlo[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p));
-    vhi[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p + 16 * kLdsRow));
-  };
-#pragma unroll
-  for (int d = 0; d < kPv; ++d) pv_load(d);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    const bf16x8 av = __builtin_shufflevector(vlo[d % kPv], vhi[d % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
-    if (d + kPv < 32) pv_load(d + kPv);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      w.acc[q][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[q], w.acc[q][d], 0, 0, 0);
-      if constexpr (P_HILO) w.acc[q][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[q], w.acc[q][d], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
-// Walk the range's tiles once with one staged register set (the accumulators
-// and Q^T leave no VGPRs for a second one without spills).  Step t: store the
-// rows of tile t+1 (in flight since step t-1) to the free LDS buffer, issue
-// the loads of tile t+2, compute tile t, one barrier.  Indices come from the
-// LDS index blocks as in run_split.
-template <int NQ, bool FP8, bool PACKED, bool P_HILO, int PASS>
-__device__ __forceinline__ void run_split_wide(const DecodeArgs &a, SmemWide<NQ> &sm, const int32_t *row_idx,
-                                               int p0, int p1, int wave, int lane, int grp,
-                                               const bf16x8 (&qreg)[NQ][kQReg], const int (&qk_base)[4],
-                                               const int (&pv_base)[8], WideState<NQ> &w) {
-  const int ntiles = (p1 - p0 + kBK - 1) / kBK;
-  if (ntiles <= 0) return;
-  uint8_t SMD_LDS *tile0 = (uint8_t SMD_LDS *)&sm.tile[0][0];
-  int32_t SMD_LDS *ib0 = (int32_t SMD_LDS *)&sm.ibuf[0][0];
-  const uint8_t SMD_LDS *qs = (const uint8_t SMD_LDS *)&sm.qs[wave][0][0][0];
-  auto tidx = [&](int k) {
-    return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
-  };
-  Staged<FP8> sa;
-  const uint8_t *zrow = g_zero_row;
-  const GatherLanes gl = make_gather_lanes(wave, lane);
-  const int blk0 = load_idx_block(row_idx, p0, p1, 0);
-  __syncthreads();  // the buffers may still be read by a previous pass
-  ib0[threadIdx.x] = blk0;
-  __syncthreads();
-  load_rows<FP8, PACKED>(a, zrow, gl, tidx(0), p0, p1, wave, lane, sa);
-  store_rows<FP8>(tile0, wave, lane, sa);
-  load_rows<FP8, PACKED>(a, zrow, gl, tidx(1), p0 + kBK, p1, wave, lane, sa);
-  __syncthreads();
-  uint32_t v_cur = tile_valid_bits(tidx(0), p0, p1, lane, a.num_rows32);
-  for (int t = 0; t < ntiles; ++t) {
-    const int nb = t / kTilesPerIdxBlock + 1;  // the next index block
-    const int blk = load_idx_block(row_idx, p0, p1, nb);
-    store_rows<FP8>(tile0 + ((t + 1) & 1) * kTileBytes, wave, lane, sa);
-    load_rows<FP8, PACKED>(a, zrow, gl, tidx(t + 2), p0 + (t + 2) * kBK, p1, wave, lane, sa);
-    compute_tile_wide<NQ, PASS, P_HILO>(tile0 + (t & 1) * kTileBytes, qreg, qs, qk_base, pv_base, v_cur, lane,
-                                        grp, a.scale_log2, w);
-    if (t % kTilesPerIdxBlock == kTilesPerIdxBlock - 3) ib0[(nb & 1) * kIdxBlock + threadIdx.x] = blk;
-    __syncthreads();
-    v_cur = tile_valid_bits(tidx(t + 1), p0 + (t + 1) * kBK, p1, lane, a.num_rows32);
-  }
-}
-
-// Attend the wide wave's query rows over positions [p0, p1) of row_idx: the
-// main pass, and the exact-max two-pass redo when some score overflowed its
-// reference max anywhere in the workgroup.
-template <int NQ, bool FP8, bool PACKED, bool P_HILO>
-__device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<NQ> &sm, const int32_t *row_idx,
-                                                  int p0, int p1, int wave, int lane, int grp,
-                                                  const bf16x8 (&qreg)[NQ][kQReg], const int (&qk_base)[4],
-                                                  const int (&pv_base)[8], WideState<NQ> &w) {
-  auto reset = [&]() {
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-      for (int d = 0; d < 32; ++d) w.acc[q][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      w.m_ref[q] = -INFINITY;
-      w.l_run[q] = 0.f;
-    }
-  };
-  reset();
-  w.overflow = false;
-  run_split_wide<NQ, FP8, PACKED, P_HILO, kPassMain>(a, sm, row_idx, p0, p1, wave, lane, grp, qreg, qk_base,
-                                                     pv_base, w);
-  if (__syncthreads_or(w.overflow)) {
-    reset();
-    run_split_wide<NQ, FP8, PACKED, P_HILO, kPassMax>(a, sm, row_idx, p0, p1, wave, lane, grp, qreg, qk_base,
-                                                      pv_base, w);
-    run_split_wide<NQ, FP8, PACKED, P_HILO, kPassFixed>(a, sm, row_idx, p0, p1, wave, lane, grp, qreg, qk_base,
-                                                        pv_base, w);
-  }
-}
-
-// Q^T of block q of a wide wave (query row qrow[q]) as QK B operands: k-steps
-// below kQReg into VGPRs, the rest into the wave's LDS region (only this wave
-// reads it, after its own stores).
-template <int NQ>
-__device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (&qrow)[NQ], int lane, int grp,
-                                            uint8_t SMD_LDS *qs, bf16x8 (&qreg)[NQ][kQReg]) {
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint16_t *src = (c < 14) ? a.q_nope + qrow[q] * kNope + 32 * c + 8 * grp
-                                     : a.q_rope + qrow[q] * kRope + 32 * (c - 14) + 8 * grp;
-      const bf16x8 v = *(const bf16x8 *)src;
-      if (c < kQReg)
-        qreg[q][c] = v;
-      else
-        *(bf16x8 SMD_LDS *)(qs + ((q * (16 - kQReg) + c - kQReg) * 64 + lane) * 16) = v;
-    }
-  }
-}
-
-// Outputs of block q of a wide wave: bf16 with the sink folded in, or the
-// FP32 partial; dst points at dim 4*grp of the row.
-template <int NQ>
-__device__ __forceinline__ void write_direct_wide(const WideState<NQ> &w, int q, float l_tot, float sink_ln,
-                                                  uint16_t *dst, float *lse_dst) {
-  const float sink2 = sink_ln * kLog2e;
-  const float mf = fmaxf(w.m_ref[q], sink2);
-  float inv = 0.f, lse_v = -INFINITY;
-  if (mf != -INFINITY) {
-    const float e = exp2_fast(w.m_ref[q] - mf);
-    const float z = l_tot * e + exp2_fast(sink2 - mf);
-    inv = e / z;
-    lse_v = (mf + __log2f(z)) * kLn2;
-  }
-#pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    u32x2 v;
-    v[0] = (uint32_t)f32_to_bf16_rne(w.acc[q][d][0] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[q][d][1] * inv) << 16);
-    v[1] = (uint32_t)f32_to_bf16_rne(w.acc[q][d][2] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[q][d][3] * inv) << 16);
-    *(u32x2 *)(dst + 16 * d) = v;
-  }
-  if (lse_dst != nullptr) *lse_dst = lse_v;
-}
-
-template <int NQ>
-__device__ __forceinline__ void write_partial_wide(const WideState<NQ> &w, int q, float l_tot, float *dst,
-                                                   float *lse_dst) {
-  float inv = 0.f, lse_v = -INFINITY;
-  if (l_tot > 0.f) {
-    inv = 1.f / l_tot;
-    lse_v = (w.m_ref[q] + __log2f(l_tot)) * kLn2;
-  }
-#pragma unroll
-  for (int d = 0; d < 32; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[q][d] * inv;
-  if (lse_dst != nullptr) *lse_dst = lse_v;
-}
-
 }  // namespace smd

@@ -10,7 +10,7 @@
 // partition p of P owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
 //
 // Grid: P partitions x G query-row groups of 16*RB rows, RB the largest of 8,
-// 4, 2, 1 that divides M / 16 (8: the wide waves of decode_core.h, each wave
+// 4, 2, 1 that divides M / 16 (8: the wide waves of wide_core.h, each wave
 // 32 rows, so one gathered tile serves 128 query rows).  Workgroup (p, g) walks the sequences of partition
 // p and attends row group g of each over the piece of its index list that p
 // owns.  A sequence inside one partition is
@@ -22,7 +22,7 @@
 // (with the sink), writes bf16 out and lse, and resets the counter to zero, so
 // the kernel can be replayed in a graph without any host-side reset.
 // Sequences with K_b = 0 own no tile and are never written.
-#include "decode_core.h"
+#include "wide_core.h"
 
 #include <type_traits>
 
@@ -207,7 +207,7 @@ __device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int
   return t0 < t1;
 }
 
-// RB = 8 runs the wide waves of decode_core.h: wave w owns blocks w and w+4
+// RB = 8 runs the wide waves of wide_core.h: wave w owns blocks w and w+4
 // of the group's 128 rows, all 512 dims.
 template <int RB, bool FP8, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void persistent_kernel(PersistArgs pa) {
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int DS = WIDE ? 1 : 4 / RB;
   constexpr int NC = 16 / DS, ND = 32 / DS;
   constexpr int ROWS = 16 * RB;
-  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<2>, Smem<DS>> sm;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<FP8>, Smem<DS>> sm;
   __shared__ int s_red[4];
   __shared__ int s_first[2];
   __shared__ int s_last;
@@ -269,10 +269,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         hq[q] = mq[q] % a.H;
         qrow[q] = (int64_t)(b * a.qps + mq[q] / a.H) * a.H + hq[q];
       }
-      bf16x8 qreg[2][kQReg];
-      load_q_wide<2>(a, qrow, lane, grp, (uint8_t SMD_LDS *)&sm.qs[wave][0][0][0], qreg);
+      constexpr int KQ = wide_qreg<FP8>();
+      bf16x8 qreg[2][KQ];
+      load_q_wide<2, KQ>(a, qrow, lane, grp, (uint8_t SMD_LDS *)&sm.qs[wave][0][0][0], qreg);
       WideState<2> w;
-      attend_range_wide<2, FP8, PACKED, false>(a, sm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, qreg,
+      WideDma dm = {nullptr, nullptr};
+      if constexpr (FP8) {
+        __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kRawSlots * kRawSlot];
+        __shared__ __attribute__((aligned(16))) int32_t s_ibuf[2 * kIdxBlock];
+        dm = WideDma{(uint8_t SMD_LDS *)s_raw, (int32_t SMD_LDS *)s_ibuf};
+      }
+      attend_range_wide<2, FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, qreg,
                                                qk_base, pv_base, w);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
