@@ -52,6 +52,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--kernel-launches", type=int, default=50)
+    ap.add_argument("--cold-calls", type=int, default=20,
+                    help="calls timed one by one after a 1 GiB cache flush (the 'cold' object); 0 skips")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (reference for HBM byte counters)")
     ap.add_argument("--writer", action="store_true",
@@ -215,6 +217,29 @@ def graph_time(torch, stream, fn, n):
         e1.record(stream)
     torch.cuda.synchronize()
     return e0.elapsed_time(e1) * 1e3 / n
+
+
+def cold_time(torch, stream, fn, n, flush_bytes=1 << 30):
+    """Median GPU time of one call of `fn` (all its launches) right after a
+    1 GiB device write, which evicts the pool and the queries from the L2
+    caches and the 256 MB Infinity Cache.  HIP events on the stream fn runs on
+    bracket the call only; the write runs before the first event."""
+    buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    marks = []
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            buf.fill_(i & 0xFF)
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            marks.append((a, b))
+    torch.cuda.synchronize()
+    ts = sorted(a.elapsed_time(b) * 1e3 for a, b in marks)
+    del buf
+    return ts[len(ts) // 2]
 
 
 def matrix(args):
@@ -507,6 +532,8 @@ def main():
         merge_us = graph_time(torch, stream, merge_only, args.kernel_launches)
         kern_us -= merge_us
 
+    cold_us = cold_time(torch, stream, step, args.cold_calls) if args.cold_calls > 0 else None
+
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -538,6 +565,19 @@ def main():
                  "alg_flops_per_launch": alg_flops, "hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                  "mfma_frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4)})
 
+    cold = None
+    if cold_us is not None:
+        # the whole call (decode and, for a split plan, the merge) from cold caches
+        if roof["bound"] == "hbm":
+            c_ach = alg_bytes / (cold_us * 1e3)
+            c_frac = c_ach / HBM_PEAK_GBS
+        else:
+            c_ach = alg_flops / (cold_us * 1e6)
+            c_frac = c_ach / BF16_MFMA_PEAK_TFS
+        cold = {"us_per_call": round(cold_us, 3), "achieved": round(c_ach, 1), "unit": roof["unit"],
+                "frac": round(c_frac, 4), "calls": args.cold_calls, "flush_bytes": 1 << 30,
+                "note": "median of single calls, each after a 1 GiB device write; decode + merge"}
+
     res = {
         "metric": METRIC,
         "value": round(gbs, 1),
@@ -556,6 +596,8 @@ def main():
         "config": cfg,
         "roofline": roof,
     }
+    if cold is not None:
+        res["cold"] = cold
     if not args.no_cpu_baseline:
         per_call, sample, cores = cpu_baseline(w, args.cpu_seconds)
         res["cpu_baseline"] = {"value": round(alg_bytes / (per_call * 1e9), 4), "unit": "GB/s", "cores": cores,
