@@ -124,11 +124,13 @@ def test_all_sequences_empty(gpu):
     assert (ws.plan().cpu().numpy()[:, 2:] == -1).all()
 
 
-def test_invalid_entries_in_ragged_lists(gpu):
+@pytest.mark.parametrize("H,kv_dtype", [(32, "fp8"), (128, "fp8"), (128, "bf16")])
+def test_invalid_entries_in_ragged_lists(gpu, H, kv_dtype):
     """Entries -1 and >= N inside the flat list are masked; an all-invalid
-    sequence gives out = 0 and lse = sink."""
-    w = wl.ragged_workload("persist invalid", B=5, q_per_seq=1, H=32, kv_dtype="fp8", pool_rows=2048, max_k=400,
-                           zero_rows=0, seed=94)
+    sequence gives out = 0 and lse = sink.  H = 128 runs the wide waves (fp8:
+    the direct-to-LDS ring, where masked rows read the zero row)."""
+    w = wl.ragged_workload("persist invalid", B=5, q_per_seq=1, H=H, kv_dtype=kv_dtype, pool_rows=2048,
+                           max_k=400, zero_rows=0, seed=94 + H)
     a = w.arrays
     ptr, flat = a["kv_indptr"], a["kv_indices"]
     rng = np.random.default_rng(0)
