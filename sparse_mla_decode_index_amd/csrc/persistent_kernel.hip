@@ -84,73 +84,122 @@ __device__ __forceinline__ bool part_empty(int p, int total, int P) {
 // The pieces are held by the non-empty partitions among fp..lp, in that
 // order.  The piece of partition q sits in slot 2q, except the first piece,
 // which sits in slot 2fp+1 when the sequence is not the first of partition fp.
-// One wave per query row, 8 dims per lane; lane k looks at partition fp + k.
+// A wave per query row (four rows of a wave at a time), 8 dims per lane;
+// lane k looks at partition fp + k.
 template <int NW>
 __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g, int rows, int fp, int lp,
                                              int first_slot, int total) {
+  // The slots were written by other workgroups, mostly on other XCDs, so
+  // every load here is a long-latency miss: each wave keeps RU rows and up
+  // to four pieces per row in flight (32 loads of 16 bytes) instead of one
+  // piece of one row.
+  constexpr int RU = 4;
   const DecodeArgs &a = pa.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lp - fp + 1;  // partitions in the span (empty ones hold nothing)
   const size_t slot_floats = (size_t)a.M * 513;
-  for (int r = wave; r < rows; r += NW) {
-    const int m = g * rows + r;
-    const int tok = b * a.qps + m / a.H;
-    const int head = m % a.H;
-    const int64_t qrow = (int64_t)tok * a.H + head;
-    const float sink = a.sink ? a.sink[head] : -INFINITY;
+  auto slot_base = [&](int q) { return pa.slots + (size_t)(q == 0 ? first_slot : 2 * (fp + q)) * slot_floats; };
+  for (int r0 = wave; r0 < rows; r0 += NW * RU) {
+    int m[RU];
+    int64_t qrow[RU];
+    float sink[RU], mx[RU];
+    bool live[RU];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int r = r0 + NW * u;
+      live[u] = r < rows;
+      m[u] = g * rows + (live[u] ? r : r0);
+      const int head = m[u] % a.H;
+      qrow[u] = (int64_t)(b * a.qps + m[u] / a.H) * a.H + head;
+      sink[u] = a.sink ? a.sink[head] : -INFINITY;
+      mx[u] = sink[u];
+    }
     // max over the pieces' lse and the sink
-    float mx = sink;
     for (int q0 = 0; q0 < n; q0 += 64) {
       const int q = q0 + lane;
-      float l = -INFINITY;
-      if (q < n && !part_empty(fp + q, total, pa.P)) {
-        const int slot = q == 0 ? first_slot : 2 * (fp + q);
-        l = pa.slots[slot * slot_floats + (size_t)a.M * 512 + m];
+      const bool held = q < n && !part_empty(fp + q, total, pa.P);
+      const float *ls = slot_base(held ? q : 0) + (size_t)a.M * kDim;
+      float l[RU];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) l[u] = ls[m[u]];
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+        float v = held ? l[u] : -INFINITY;
+        for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+        mx[u] = fmaxf(mx[u], v);
       }
-      for (int o = 32; o > 0; o >>= 1) l = fmaxf(l, __shfl_xor(l, o, 64));
-      mx = fmaxf(mx, l);
     }
-    uint16_t *dst = a.out + qrow * kDim + lane * 8;
-    if (mx == -INFINITY) {
-      *(u32x4 *)dst = u32x4{0u, 0u, 0u, 0u};
-      if (a.lse != nullptr && lane == 0) a.lse[qrow] = -INFINITY;
-      continue;
+    float z[RU], o[RU][8];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      z[u] = mx[u] == -INFINITY ? 0.f : exp2_fast((sink[u] - mx[u]) * kLog2e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) o[u][i] = 0.f;
     }
-    float z = exp2_fast((sink - mx) * kLog2e);
-    float o[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int q0 = 0; q0 < n; q0 += 64) {
       const int ql = q0 + lane;
-      float wl = 0.f;
       const bool held = ql < n && !part_empty(fp + ql, total, pa.P);
-      if (held) {
-        const int slot = ql == 0 ? first_slot : 2 * (fp + ql);
-        wl = exp2_fast((pa.slots[slot * slot_floats + (size_t)a.M * 512 + m] - mx) * kLog2e);
-      }
-      const uint64_t held_mask = __ballot(held);
-      const int cnt = min(64, n - q0);
-      for (int k = 0; k < cnt; ++k) {
-        if (!((held_mask >> k) & 1)) continue;  // an empty partition in the span
-        const float wq = __shfl(wl, k, 64);
-        const int q = q0 + k;
-        const int slot = q == 0 ? first_slot : 2 * (fp + q);
-        const float *src = pa.slots + slot * slot_floats + (size_t)m * kDim + lane * 8;
-        const f32x4 v0 = *(const f32x4 *)src;
-        const f32x4 v1 = *(const f32x4 *)(src + 4);
-        z += wq;
+      const float *ls = slot_base(held ? ql : 0) + (size_t)a.M * kDim;
+      float wl[RU];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          o[i] += wq * v0[i];
-          o[4 + i] += wq * v1[i];
+      for (int u = 0; u < RU; ++u) {
+        const float l = ls[m[u]];
+        wl[u] = (held && mx[u] != -INFINITY) ? exp2_fast((l - mx[u]) * kLog2e) : 0.f;
+      }
+      uint64_t mask = __ballot(held);  // wave-uniform
+      while (mask) {
+        // up to KP pieces per batch; absent ones repeat the first with weight 0
+        constexpr int KP = 4;
+        int kk[KP];
+        bool has[KP];
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          has[i] = mask != 0;
+          kk[i] = has[i] ? __builtin_ctzll(mask) : kk[0];
+          if (has[i]) mask &= mask - 1;
+        }
+        f32x4 v[KP][RU][2];
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          const float *sp = slot_base(q0 + kk[i]) + lane * 8;
+#pragma unroll
+          for (int u = 0; u < RU; ++u) {
+            v[i][u][0] = *(const f32x4 *)(sp + (size_t)m[u] * kDim);
+            v[i][u][1] = *(const f32x4 *)(sp + (size_t)m[u] * kDim + 4);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+#pragma unroll
+          for (int i = 0; i < KP; ++i) {
+            const float wq = has[i] ? __shfl(wl[u], kk[i], 64) : 0.f;
+            z[u] += wq;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              o[u][e] += wq * v[i][u][0][e];
+              o[u][4 + e] += wq * v[i][u][1][e];
+            }
+          }
         }
       }
     }
-    const float inv = 1.f / z;
-    u32x4 v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      v[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
-    *(u32x4 *)dst = v;
-    if (a.lse != nullptr && lane == 0) a.lse[qrow] = mx + logf(z);
+    for (int u = 0; u < RU; ++u) {
+      if (!live[u]) continue;
+      uint16_t *dst = a.out + qrow[u] * kDim + lane * 8;
+      if (mx[u] == -INFINITY) {
+        *(u32x4 *)dst = u32x4{0u, 0u, 0u, 0u};
+        if (a.lse != nullptr && lane == 0) a.lse[qrow[u]] = -INFINITY;
+        continue;
+      }
+      const float inv = 1.f / z[u];
+      u32x4 v;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        v[i] = (uint32_t)f32_to_bf16_rne(o[u][2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][2 * i + 1] * inv) << 16);
+      *(u32x4 *)dst = v;
+      if (a.lse != nullptr && lane == 0) a.lse[qrow[u]] = mx[u] + logf(z[u]);
+    }
   }
 }
 

@@ -493,6 +493,10 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
 template <int NQ, int KQ>
 __device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (&qrow)[NQ], int lane, int grp,
                                             uint8_t SMD_LDS *qs, bf16x8 (&qreg)[NQ][KQ]) {
+  // Every load is issued before the first LDS store: interleaved, each store
+  // would wait for its own load and the k-steps would arrive one latency at
+  // a time.
+  bf16x8 tmp[NQ][16 - KQ];
 #pragma unroll
   for (int q = 0; q < NQ; ++q) {
 #pragma unroll
@@ -503,8 +507,15 @@ __device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (
       if (c < KQ)
         qreg[q][c < KQ ? c : 0] = v;
       else
-        *(bf16x8 SMD_LDS *)(qs + ((q * (16 - KQ) + c - KQ) * 64 + lane) * 16) = v;
+        tmp[q][c < KQ ? 0 : c - KQ] = v;
     }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int c = KQ; c < 16; ++c)
+      *(bf16x8 SMD_LDS *)(qs + ((q * (16 - KQ) + c - KQ) * 64 + lane) * 16) = tmp[q][c - KQ];
   }
 }
 
