@@ -91,8 +91,9 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
                                              int first_slot, int total) {
   // The slots were written by other workgroups, mostly on other XCDs, so
   // every load here is a long-latency miss: each wave keeps RU rows and up
-  // to four pieces per row in flight (32 loads of 16 bytes) instead of one
-  // piece of one row.
+  // to KP pieces per row in flight (16 loads of 16 bytes) instead of one
+  // piece of one row.  (Larger batches spill at this point of the kernel,
+  // and every spill reload waits for all loads in flight.)
   constexpr int RU = 4;
   const DecodeArgs &a = pa.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -149,7 +150,7 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
       uint64_t mask = __ballot(held);  // wave-uniform
       while (mask) {
         // up to KP pieces per batch; absent ones repeat the first with weight 0
-        constexpr int KP = 4;
+        constexpr int KP = 2;
         int kk[KP];
         bool has[KP];
 #pragma unroll
@@ -199,6 +200,100 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
         v[i] = (uint32_t)f32_to_bf16_rne(o[u][2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][2 * i + 1] * inv) << 16);
       *(u32x4 *)dst = v;
       if (a.lse != nullptr && lane == 0) a.lse[qrow[u]] = mx[u] + logf(z[u]);
+    }
+  }
+}
+
+// merge_pieces for spans of at most 64 partitions (lane k holds piece k),
+// with the rows a template constant: the lse of every row of the wave is
+// loaded in one round trip up front, so the only serial misses left are one
+// batch of slot loads per RU rows (instead of two lse trips per batch).
+template <int NW, int ROWS>
+__device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b, int g, int fp, int n,
+                                                    int first_slot, int total) {
+  constexpr int RPW = ROWS / NW;  // this wave's rows: wave, wave + NW, ...
+  constexpr int RU = RPW < 4 ? RPW : 4, KP = 2;
+  static_assert(ROWS % NW == 0 && RPW % RU == 0, "rows per wave");
+  const DecodeArgs &a = pa.d;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t slot_floats = (size_t)a.M * 513;
+  auto slot_base = [&](int q) { return pa.slots + (size_t)(q == 0 ? first_slot : 2 * (fp + q)) * slot_floats; };
+  const bool held = lane < n && !part_empty(fp + lane, total, pa.P);
+  const uint64_t held_mask = __ballot(held);  // wave-uniform
+  const float *ls = slot_base(held ? lane : 0) + (size_t)a.M * kDim;
+  float l[RPW];
+#pragma unroll
+  for (int i = 0; i < RPW; ++i) l[i] = ls[g * ROWS + wave + NW * i];
+#pragma unroll 1
+  for (int i0 = 0; i0 < RPW; i0 += RU) {
+    int m[RU];
+    float mx[RU], wl[RU], z[RU], o[RU][8];
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      m[u] = g * ROWS + wave + NW * (i0 + u);
+      const float sink = a.sink ? a.sink[m[u] % a.H] : -INFINITY;
+      float v = held ? l[u] : -INFINITY;
+      for (int o2 = 32; o2 > 0; o2 >>= 1) v = fmaxf(v, __shfl_xor(v, o2, 64));
+      mx[u] = fmaxf(v, sink);
+      wl[u] = (held && mx[u] != -INFINITY) ? exp2_fast((l[u] - mx[u]) * kLog2e) : 0.f;
+      z[u] = mx[u] == -INFINITY ? 0.f : exp2_fast((sink - mx[u]) * kLog2e);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[u][e] = 0.f;
+    }
+#pragma unroll
+    for (int j = 0; j + RU < RPW; ++j) l[j] = l[j + RU];  // the next batch's lse moves to the front
+    uint64_t mask = held_mask;
+    while (mask) {
+      // up to KP pieces per batch; absent ones repeat the first with weight 0
+      int kk[KP];
+      bool has[KP];
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        has[i] = mask != 0;
+        kk[i] = has[i] ? __builtin_ctzll(mask) : kk[0];
+        if (has[i]) mask &= mask - 1;
+      }
+      f32x4 v[KP][RU][2];
+#pragma unroll
+      for (int i = 0; i < KP; ++i) {
+        const float *sp = slot_base(kk[i]) + lane * 8;
+#pragma unroll
+        for (int u = 0; u < RU; ++u) {
+          v[i][u][0] = *(const f32x4 *)(sp + (size_t)m[u] * kDim);
+          v[i][u][1] = *(const f32x4 *)(sp + (size_t)m[u] * kDim + 4);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < RU; ++u) {
+#pragma unroll
+        for (int i = 0; i < KP; ++i) {
+          const float wq = has[i] ? __shfl(wl[u], kk[i], 64) : 0.f;
+          z[u] += wq;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            o[u][e] += wq * v[i][u][0][e];
+            o[u][4 + e] += wq * v[i][u][1][e];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < RU; ++u) {
+      const int head = m[u] % a.H;
+      const int64_t qrow = (int64_t)(b * a.qps + m[u] / a.H) * a.H + head;
+      uint16_t *dst = a.out + qrow * kDim + lane * 8;
+      if (mx[u] == -INFINITY) {
+        *(u32x4 *)dst = u32x4{0u, 0u, 0u, 0u};
+        if (a.lse != nullptr && lane == 0) a.lse[qrow] = -INFINITY;
+        continue;
+      }
+      const float inv = 1.f / z[u];
+      u32x4 vv;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        vv[e] = (uint32_t)f32_to_bf16_rne(o[u][2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][2 * e + 1] * inv) << 16);
+      *(u32x4 *)dst = vv;
+      if (a.lse != nullptr && lane == 0) a.lse[qrow] = mx[u] + logf(z[u]);
     }
   }
 }
@@ -366,7 +461,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       if (s_arrived == (uint32_t)(pieces - 1)) {
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire the other pieces
         const int t0_fp = (int)((int64_t)fp * total / pa.P);
-        merge_pieces<4>(pa, b, g, ROWS, fp, lp, 2 * fp + (start == t0_fp ? 0 : 1), total);
+        const int fs = 2 * fp + (start == t0_fp ? 0 : 1);
+        if (lp - fp < 64)
+          merge_pieces_narrow<4, ROWS>(pa, b, g, fp, lp - fp + 1, fs, total);
+        else
+          merge_pieces<4>(pa, b, g, ROWS, fp, lp, fs, total);
         if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       }
       __syncthreads();  // s_arrived is rewritten by the next piece

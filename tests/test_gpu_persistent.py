@@ -107,14 +107,16 @@ def test_no_sink(gpu):
     run_persistent(w, gpu, 6, sink=False)
 
 
-def test_long_sequence_many_pieces(gpu):
-    """One long sequence spread over every partition (a 64-piece merge)."""
-    w = wl.ragged_workload("persist long", B=1, q_per_seq=1, H=128, kv_dtype="bf16", pool_rows=65536, max_k=1,
+@pytest.mark.parametrize("H,kv_dtype,P", [(128, "bf16", 64), (128, "bf16", 100), (16, "fp8", 130)])
+def test_long_sequence_many_pieces(gpu, H, kv_dtype, P):
+    """One long sequence spread over every partition: a merge of 64 pieces (at
+    most one per lane) and of more than 64 (several per lane)."""
+    w = wl.ragged_workload("persist long", B=1, q_per_seq=1, H=H, kv_dtype=kv_dtype, pool_rows=65536, max_k=1,
                            seed=92)
     K = 20000
     w.arrays["kv_indptr"] = np.array([0, K], dtype=np.int32)
     w.arrays["kv_indices"] = np.random.default_rng(2).choice(65536, K, replace=False).astype(np.int32)
-    run_persistent(w, gpu, 64)
+    run_persistent(w, gpu, P)
 
 
 def test_all_sequences_empty(gpu):
