@@ -414,8 +414,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         qrow[q] = (int64_t)(b * a.qps + mq[q] / a.H) * a.H + hq[q];
       }
       constexpr int KQ = wide_qreg<FP8>();
-      bf16x8 qreg[2][KQ];
-      load_q_wide<2, KQ>(a, qrow, lane, grp, (uint8_t SMD_LDS *)&sm.qs[wave][0][0][0], qreg);
+      bf16x8 qreg[2][KQ];  // loaded by attend_range_wide
       WideState<2> w;
       WideDma dm = {nullptr, nullptr};
       if constexpr (FP8) {
@@ -423,8 +422,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __shared__ __attribute__((aligned(16))) int32_t s_ibuf[2 * kIdxBlock];
         dm = WideDma{(uint8_t SMD_LDS *)s_raw, (int32_t SMD_LDS *)s_ibuf};
       }
-      attend_range_wide<2, FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, qreg,
-                                               qk_base, pv_base, w);
+      attend_range_wide<2, FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, qrow,
+                                               qreg, qk_base, pv_base, w);
 #pragma unroll
       for (int q = 0; q < 2; ++q) {
         const float l_tot = row_total(w.l_run[q]);

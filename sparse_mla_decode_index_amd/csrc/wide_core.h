@@ -389,6 +389,38 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Q^T of block q of a wide wave (query row qrow[q]) as QK B operands: k-steps
+// below KQ into VGPRs, the rest into the wave's LDS region (only this wave
+// reads it, after its own stores).
+template <int NQ, int KQ>
+__device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (&qrow)[NQ], int lane, int grp,
+                                            uint8_t SMD_LDS *qs, bf16x8 (&qreg)[NQ][KQ]) {
+  // Every load is issued before the first LDS store: interleaved, each store
+  // would wait for its own load and the k-steps would arrive one latency at
+  // a time.
+  bf16x8 tmp[NQ][16 - KQ];
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const uint16_t *src = (c < 14) ? a.q_nope + qrow[q] * kNope + 32 * c + 8 * grp
+                                     : a.q_rope + qrow[q] * kRope + 32 * (c - 14) + 8 * grp;
+      const bf16x8 v = *(const bf16x8 *)src;
+      if (c < KQ)
+        qreg[q][c < KQ ? c : 0] = v;
+      else
+        tmp[q][c < KQ ? 0 : c - KQ] = v;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int q = 0; q < NQ; ++q) {
+#pragma unroll
+    for (int c = KQ; c < 16; ++c)
+      *(bf16x8 SMD_LDS *)(qs + ((q * (16 - KQ) + c - KQ) * 64 + lane) * 16) = tmp[q][c - KQ];
+  }
+}
+
 // Walk the range's tiles once (fp8 pools) with the raw ring.  Tile k's loads
 // go to slot k % 3 at step k - 3.  Step t:
 //   wait for this wave's loads of tile t (12 younger loads are allowed: the
@@ -424,9 +456,11 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
   // counted by the hardware too, and a wait it would otherwise keep for an
   // earlier load (of Q^T, say) would drain the ring at every step.
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt and lgkmcnt unconstrained
-  __syncthreads();  // the buffers may still be read by a previous pass
-  dma_idx_block(row_idx, p0, p1, 0, wave, lane, ib0);
-  wait_vm<0>();
+  if constexpr (PASS != kPassMain) {  // the main pass's caller has done this, with the Q^T load
+    __syncthreads();  // the buffers may still be read by a previous pass
+    dma_idx_block(row_idx, p0, p1, 0, wave, lane, ib0);
+    wait_vm<0>();
+  }
   __syncthreads();
 #pragma unroll
   for (int k = 0; k < kRawSlots; ++k) dma_rows_fp8(a, tidx(k), p0 + k * kBK, p1, wave, lane, slot(k));
@@ -456,7 +490,7 @@ template <int NQ, bool FP8, bool PACKED, bool P_HILO>
 __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<FP8> &sm, const WideDma &dm,
                                                   const int32_t *row_idx,
                                                   int p0, int p1, int wave, int lane, int grp,
-                                                  const bf16x8 (&qreg)[NQ][wide_qreg<FP8>()],
+                                                  const int64_t (&qrow)[NQ], bf16x8 (&qreg)[NQ][wide_qreg<FP8>()],
                                                   const int (&qk_base)[4], const int (&pv_base)[8],
                                                   WideState<NQ> &w) {
   auto reset = [&]() {
@@ -477,6 +511,13 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
       run_split_wide<NQ, PACKED, P_HILO, PASS>(a, sm, row_idx, p0, p1, wave, lane, grp, qreg, qk_base, pv_base,
                                                w);
   };
+  if constexpr (FP8) {
+    // The first index block of the main pass goes out ahead of the Q^T
+    // loads: the two round trips overlap instead of following each other.
+    __syncthreads();  // the buffers may still be read by a previous piece
+    if (p1 > p0) dma_idx_block(row_idx, p0, p1, 0, wave, lane, dm.ibuf);
+  }
+  load_q_wide<NQ, wide_qreg<FP8>()>(a, qrow, lane, grp, (uint8_t SMD_LDS *)&sm.qs[wave][0][0][0], qreg);
   reset();
   w.overflow = false;
   walk(std::integral_constant<int, kPassMain>{});
@@ -484,38 +525,6 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
     reset();
     walk(std::integral_constant<int, kPassMax>{});
     walk(std::integral_constant<int, kPassFixed>{});
-  }
-}
-
-// Q^T of block q of a wide wave (query row qrow[q]) as QK B operands: k-steps
-// below KQ into VGPRs, the rest into the wave's LDS region (only this wave
-// reads it, after its own stores).
-template <int NQ, int KQ>
-__device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (&qrow)[NQ], int lane, int grp,
-                                            uint8_t SMD_LDS *qs, bf16x8 (&qreg)[NQ][KQ]) {
-  // Every load is issued before the first LDS store: interleaved, each store
-  // would wait for its own load and the k-steps would arrive one latency at
-  // a time.
-  bf16x8 tmp[NQ][16 - KQ];
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint16_t *src = (c < 14) ? a.q_nope + qrow[q] * kNope + 32 * c + 8 * grp
-                                     : a.q_rope + qrow[q] * kRope + 32 * (c - 14) + 8 * grp;
-      const bf16x8 v = *(const bf16x8 *)src;
-      if (c < KQ)
-        qreg[q][c < KQ ? c : 0] = v;
-      else
-        tmp[q][c < KQ ? 0 : c - KQ] = v;
-    }
-  }
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-#pragma unroll
-    for (int c = KQ; c < 16; ++c)
-      *(bf16x8 SMD_LDS *)(qs + ((q * (16 - KQ) + c - KQ) * 64 + lane) * 16) = tmp[q][c - KQ];
   }
 }
 
