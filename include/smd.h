@@ -271,10 +271,14 @@ int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t
  * plan is read from device memory on every launch, a captured graph stays
  * correct when kv_indptr and kv_indices change between replays.
  *
- * Plan rule: sequence b contributes ceil(K_b / 64) tiles of 64 index
- * positions (K_b = kv_indptr[b+1] - kv_indptr[b]); the tiles of all
- * sequences are concatenated in (sequence, tile) order, and partition p of
- * num_partitions owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
+ * Plan rule: sequence b with tiles_b = ceil(K_b / 64) > 0 tiles of 64 index
+ * positions (K_b = kv_indptr[b+1] - kv_indptr[b]) takes tiles_b + 2 plan
+ * units, two charged for the fixed cost of a piece and then one per tile; the
+ * units of all sequences are concatenated in sequence order, partition p of
+ * num_partitions owns units [floor(p*total/P), floor((p+1)*total/P)), and a
+ * tile belongs to the partition owning its unit.  The plan descriptor of
+ * partition p is (first unit, end unit, first and last sequence with a tile
+ * in it, or -1 and -1).
  * The kernel runs P x G workgroups, G = M / R query-row groups of R rows
  * (M = num_heads * q_per_seq; R = 128 when 128 divides M, else 64, 32 or 16,
  * the largest that divides M).

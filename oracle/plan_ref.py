@@ -92,18 +92,24 @@ def num_kv_splits(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv
 # kernel" (Summary, part 2) has the persistent kernel derive its split plan
 # inside the kernel from the live kv_indptr and merge split rows in the
 # workgroup that arrives last.  The pages do not print the partition rule; the
-# reading used here: every sequence b contributes tiles_b = ceil(K_b / 64)
-# tiles, the tiles of all sequences are concatenated in (b, tile) order, and
-# partition p of P owns the global tiles [floor(p*total/P), floor((p+1)*total/P)).
-# A sequence whose tiles fall in more than one partition is split; its pieces
-# merge in partition order.  With fewer tiles than partitions some partitions
+# reading used here: every sequence b with tiles_b = ceil(K_b / 64) > 0
+# takes tiles_b + SEQ_OVERHEAD plan units -- SEQ_OVERHEAD units charged for
+# the fixed cost of a piece, then one unit per tile -- and a sequence with
+# K_b = 0 takes none.  The units of all sequences are concatenated in
+# sequence order, partition p of P owns the units [floor(p*total/P),
+# floor((p+1)*total/P)), and a tile belongs to the partition owning its unit.
+# (With SEQ_OVERHEAD = 0 this is the plain balanced split of the tiles.)  A
+# sequence whose tiles fall in more than one partition is split; its pieces
+# merge in partition order.  With fewer units than partitions some partitions
 # are empty, and they may sit between two pieces of one sequence, so the piece
 # count is the number of partitions that own a tile of the sequence, not the
 # width of the partition span.  A partition holds at most two split pieces
-# (its first and its last sequence), so piece (p, b) has slot 2p when b is the
-# first sequence of p and 2p+1 otherwise.
+# (one that starts at its first unit and one that continues past its end), so
+# piece (p, b) has slot 2p when it starts at p's first unit and 2p+1
+# otherwise.
 
 PERSIST_TILE = 64
+SEQ_OVERHEAD = 2  # plan units charged per sequence with tiles (a measured cost, not the pages')
 
 
 @dataclass
@@ -117,48 +123,52 @@ class Piece:
     num_pieces: int  # partitions owning a tile of the sequence
 
 
-def partition(kv_indptr, num_partitions: int):
-    """Returns (descriptors, pieces): descriptors[p] = (t0, t1, b_first, b_last)
-    with b_first / b_last the first / last sequence owning a tile of [t0, t1)
-    (-1, -1 for an empty partition); pieces[p] = the list of Piece of p in
-    sequence order."""
+def partition(kv_indptr, num_partitions: int, seq_overhead: int = SEQ_OVERHEAD):
+    """Returns (descriptors, pieces): descriptors[p] = (u0, u1, b_first, b_last)
+    with [u0, u1) the units of partition p and b_first / b_last the first /
+    last sequence with a tile in it (-1, -1 when it holds no tile); pieces[p] =
+    the list of Piece of p in sequence order."""
     P = int(num_partitions)
     if P < 1:
         raise ValueError("num_partitions must be >= 1")
+    if seq_overhead < 0:
+        raise ValueError("seq_overhead must be >= 0")
     ptr = [int(x) for x in kv_indptr]
     B = len(ptr) - 1
     lens = [ptr[b + 1] - ptr[b] for b in range(B)]
     if any(k < 0 for k in lens):
         raise ValueError("kv_indptr must be non-decreasing")
     tiles = [_cdiv(k, PERSIST_TILE) for k in lens]
-    start = [0] * (B + 1)  # first global tile of each sequence
+    units = [t + seq_overhead if t > 0 else 0 for t in tiles]
+    first_tile = [0] * B  # global unit of each sequence's first tile
+    u = 0
     for b in range(B):
-        start[b + 1] = start[b] + tiles[b]
-    total = start[B]
+        first_tile[b] = u + (units[b] - tiles[b])
+        u += units[b]
+    total = u
     bounds = [p * total // P for p in range(P + 1)]
 
-    def owner(tile):  # the partition whose range holds global tile `tile`
+    def owner(unit):  # the partition whose range holds `unit`
         p = 0
-        while bounds[p + 1] <= tile:
+        while bounds[p + 1] <= unit:
             p += 1
         return p
 
     descs, pieces = [], []
     for p in range(P):
-        t0, t1 = bounds[p], bounds[p + 1]
+        u0, u1 = bounds[p], bounds[p + 1]
         mine = []
         for b in range(B):
-            lo, hi = max(t0, start[b]), min(t1, start[b + 1])
+            lo, hi = max(u0, first_tile[b]), min(u1, first_tile[b] + tiles[b])
             if lo >= hi:
                 continue
-            owners = sorted({owner(t) for t in range(start[b], start[b + 1])})
+            owners = sorted({owner(first_tile[b] + t) for t in range(tiles[b])})
             fp, lp = owners[0], owners[-1]
-            first = not mine
-            mine.append(Piece(seq=b, begin=(lo - start[b]) * PERSIST_TILE,
-                              end=min((hi - start[b]) * PERSIST_TILE, lens[b]),
-                              split=lp > fp, slot=(2 * p + (0 if first else 1)) if lp > fp else -1,
+            mine.append(Piece(seq=b, begin=(lo - first_tile[b]) * PERSIST_TILE,
+                              end=min((hi - first_tile[b]) * PERSIST_TILE, lens[b]),
+                              split=lp > fp, slot=(2 * p + (0 if lo == u0 else 1)) if lp > fp else -1,
                               first_part=fp, num_pieces=len(owners)))
-        descs.append((t0, t1, mine[0].seq, mine[-1].seq) if mine else (t0, t1, -1, -1))
+        descs.append((u0, u1, mine[0].seq, mine[-1].seq) if mine else (u0, u1, -1, -1))
         pieces.append(mine)
     return descs, pieces
 

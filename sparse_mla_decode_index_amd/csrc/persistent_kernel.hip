@@ -5,9 +5,12 @@
 // which every workgroup derives the split plan inside the kernel from the live
 // kv_indptr, unsplit rows are written as bf16 directly, and split rows are
 // merged by the workgroup that arrives last.  The plan rule here (the pages do
-// not print one): sequence b contributes tiles_b = ceil(K_b / 64) tiles, the
-// tiles of all sequences are concatenated in (sequence, tile) order, and
-// partition p of P owns global tiles [floor(p*total/P), floor((p+1)*total/P)).
+// not print one): sequence b with tiles_b = ceil(K_b / 64) > 0 tiles takes
+// tiles_b + 2 plan units, the first two charging the fixed cost of a piece
+// (Q^T load, first round trips, epilogue) and the rest its tiles; the units of
+// all sequences are concatenated in sequence order, partition p of P owns
+// units [floor(p*total/P), floor((p+1)*total/P)), and a tile belongs to the
+// partition that owns its unit.
 //
 // Grid: P partitions x G query-row groups of 16*RB rows, RB the largest of 8,
 // 4, 2, 1 that divides M / 16 (8: the wide waves of wide_core.h, each wave
@@ -67,14 +70,22 @@ __device__ __forceinline__ int seq_tiles(const int32_t *ptr, int b) {
   return (max(ptr[b + 1] - ptr[b], 0) + kSplitAlign - 1) / kSplitAlign;  // decreasing: K_b = 0
 }
 
-// The partition whose tile range holds global tile x: the largest p with
+// Plan units of a sequence: its tiles plus kSeqOverhead units charged for the
+// fixed cost of a piece (none for K_b = 0).  Its tiles are its last tb units.
+// (Measured on ragged MTP4 batches: a piece costs about two tiles more than
+// its tiles, and charging it evens out the partitions' times.)
+constexpr int kSeqOverhead = 2;
+__device__ __forceinline__ int seq_units(int tb) { return tb > 0 ? tb + kSeqOverhead : 0; }
+
+// The partition whose unit range holds unit x: the largest p with
 // floor(p*total/P) <= x, i.e. floor(((x+1)*P - 1) / total).
 __device__ __forceinline__ int tile_owner(int x, int total, int P) {
   return (int)(((int64_t)(x + 1) * P - 1) / total);
 }
 
-// Partition p owns no tile when floor(p*total/P) == floor((p+1)*total/P)
-// (possible only when total < P).
+// Partition p owns no unit when floor(p*total/P) == floor((p+1)*total/P)
+// (possible only when total < P).  Inside the span of a split sequence every
+// unit is one of its tiles, so there a partition with a unit holds a piece.
 __device__ __forceinline__ bool part_empty(int p, int total, int P) {
   return (int64_t)p * total / P == (int64_t)(p + 1) * total / P;
 }
@@ -298,26 +309,26 @@ __device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b
   }
 }
 
-// The plan of partition p from the live kv_indptr: total tiles, this
-// partition's tile range [t0, t1), its first and last sequence and the first
-// global tile of its first sequence.  Row group 0 writes the descriptor.
-// Returns false (workgroup-uniform) when the partition owns no tile.
+// The plan of partition p from the live kv_indptr: total units, this
+// partition's unit range [t0, t1), its first and last sequence with a tile in
+// it and the first tile unit of that first sequence.  Row group 0 writes the
+// descriptor.  Returns false (workgroup-uniform) when the partition owns no
+// tile (no unit, or only units charged for a piece's fixed cost).
 template <int NT>
-__device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int g, int *s_red, int *s_first,
-                                               int *s_last, int &total, int &t0, int &t1, int &b_first, int &b_last,
-                                               int &start) {
+__device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int g, int *s_red, int *s_last,
+                                               int &total, int &t0, int &t1, int &b_first, int &b_last, int &start) {
   const int32_t *ptr = pa.kv_indptr;
   const int B = pa.B;
   {
     int loc = 0;
-    for (int b = threadIdx.x; b < B; b += NT) loc += seq_tiles(ptr, b);
+    for (int b = threadIdx.x; b < B; b += NT) loc += seq_units(seq_tiles(ptr, b));
     block_incl_scan<NT>(loc, s_red, total);
   }
   t0 = (int)((int64_t)p * total / pa.P);
   t1 = (int)((int64_t)(p + 1) * total / pa.P);
+  __shared__ unsigned long long s_fst;  // (first sequence with a tile in [t0, t1)) << 32 | its first tile unit
   if (threadIdx.x == 0) {
-    s_first[0] = -1;
-    s_first[1] = 0;
+    s_fst = ~0ull;
     *s_last = -1;
   }
   __syncthreads();
@@ -326,21 +337,21 @@ __device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int
     for (int base = 0; base < B; base += NT) {
       const int b = base + (int)threadIdx.x;
       const int tb = b < B ? seq_tiles(ptr, b) : 0;
+      const int ub = seq_units(tb);
       int chunk;
-      const int st = run + block_incl_scan<NT>(tb, s_red, chunk) - tb;
-      if (tb > 0 && st <= t0 && t0 < st + tb) {
-        s_first[0] = b;
-        s_first[1] = st;
+      const int st = run + block_incl_scan<NT>(ub, s_red, chunk) - ub + kSeqOverhead;  // first tile unit
+      if (tb > 0 && st < t1 && st + tb > t0) {
+        atomicMin(&s_fst, ((unsigned long long)b << 32) | (unsigned)st);
+        atomicMax(s_last, b);
       }
-      if (tb > 0 && st < t1 && t1 <= st + tb) *s_last = b;
       run += chunk;
       if (run >= t1) break;  // the same in every thread
     }
   }
   __syncthreads();
-  b_first = s_first[0];
+  b_first = s_fst == ~0ull ? -1 : (int)(s_fst >> 32);
   b_last = *s_last;
-  start = s_first[1];
+  start = (int)(s_fst & 0xffffffffu);
   if (g == 0 && threadIdx.x == 0) {
     int32_t *d = pa.plan + 4 * p;
     d[0] = t0;
@@ -348,7 +359,7 @@ __device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int
     d[2] = b_first;
     d[3] = b_last;
   }
-  return t0 < t1;
+  return b_first >= 0;
 }
 
 // RB = 8 runs the wide waves of wide_core.h: wave w owns blocks w and w+4
@@ -361,7 +372,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int ROWS = 16 * RB;
   __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<FP8>, Smem<DS>> sm;
   __shared__ int s_red[4];
-  __shared__ int s_first[2];
   __shared__ int s_last;
   __shared__ uint32_t s_arrived;
   const DecodeArgs &a = pa.d;
@@ -381,7 +391,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const int32_t *ptr = pa.kv_indptr;
 
   int total, t0, t1, b_first, b_last, start;
-  if (!plan_partition<256>(pa, p, g, s_red, s_first, &s_last, total, t0, t1, b_first, b_last, start)) return;
+  if (!plan_partition<256>(pa, p, g, s_red, &s_last, total, t0, t1, b_first, b_last, start)) return;
 
   int qk_base[4], pv_base[8];
   lds_bases(j, grp, qk_base, pv_base);
@@ -396,13 +406,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int kb = max(ptr[b + 1] - k0, 0);
     const int tb = (kb + kSplitAlign - 1) / kSplitAlign;
     if (tb == 0) continue;
+    if (b != b_first) start += kSeqOverhead;  // this sequence's first tile unit
     const int lo = max(t0, start), hi = min(t1, start + tb);
     const int pos0 = (lo - start) * kSplitAlign;
     const int pos1 = min((hi - start) * kSplitAlign, kb);
     const int fp = tile_owner(start, total, pa.P);
     const int lp = tile_owner(start + tb - 1, total, pa.P);
 
-    const int slot = 2 * p + (b == b_first ? 0 : 1);
+    const int slot = 2 * p + (lo == t0 ? 0 : 1);
     float *sb = pa.slots + slot * slot_floats;
     if constexpr (WIDE) {
       int64_t qrow[2];

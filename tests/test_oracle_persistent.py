@@ -1,5 +1,6 @@
 """Pins of the oracle's persistent plan (the balanced contiguous partition of
-all 64-position tiles over P partitions) and of the piecewise merge it implies.
+the sequences' plan units -- two charged per sequence, then one per
+64-position tile -- over P partitions) and of the piecewise merge it implies.
 CPU only."""
 import numpy as np
 import pytest
@@ -10,13 +11,14 @@ from oracle import ref
 
 
 def test_partition_hand_example():
+    # Without charged units (the plain split of the tiles):
     # K_b = 100, 0, 200, 1  ->  tiles 2, 0, 4, 1 (ceil(K/64)); total 7; P = 3:
     # bounds floor(7p/3) = 0, 2, 4, 7.  Partition 0 = seq 0 (whole); partition
     # 1 = tiles 2..3 = seq 2 positions [0, 128); partition 2 = tiles 4..6 =
     # seq 2 positions [128, 200) then seq 3 [0, 1).  Seq 2 is split over
     # partitions 1 and 2 and is the first sequence of both (slots 2 and 4).
     # The indptr starts at an offset: only differences matter.
-    descs, pieces = pr.partition([50, 150, 150, 350, 351], 3)
+    descs, pieces = pr.partition([50, 150, 150, 350, 351], 3, seq_overhead=0)
     assert descs == [(0, 2, 0, 0), (2, 4, 2, 2), (4, 7, 2, 3)]
     got = [[(x.seq, x.begin, x.end, x.split, x.slot, x.first_part, x.num_pieces) for x in p] for p in pieces]
     assert got == [[(0, 0, 100, False, -1, 0, 1)],
@@ -24,18 +26,43 @@ def test_partition_hand_example():
                    [(2, 128, 200, True, 4, 1, 2), (3, 0, 1, False, -1, 2, 1)]]
 
 
+def test_partition_hand_example_charged_units():
+    # The same lists with two units charged per sequence with tiles: units
+    # 4, 0, 6, 3 (seq 0 = units 0..3, its tiles at 2, 3; seq 2 = units 4..9,
+    # tiles at 6..9; seq 3 = units 10..12, its tile at 12); total 13; P = 3:
+    # bounds floor(13p/3) = 0, 4, 8, 13.  Partition 0 = seq 0 (whole).
+    # Partition 1 = seq 2's charged units 4, 5 and its tiles 0, 1 (units 6, 7):
+    # positions [0, 128), which start after the partition's first unit, so the
+    # piece takes the odd slot 3.  Partition 2 = seq 2 tiles 2, 3 (units 8, 9:
+    # positions [128, 200), starting at the partition's first unit: slot 4),
+    # then seq 3 whole.
+    descs, pieces = pr.partition([50, 150, 150, 350, 351], 3)
+    assert pr.SEQ_OVERHEAD == 2
+    assert descs == [(0, 4, 0, 0), (4, 8, 2, 2), (8, 13, 2, 3)]
+    got = [[(x.seq, x.begin, x.end, x.split, x.slot, x.first_part, x.num_pieces) for x in p] for p in pieces]
+    assert got == [[(0, 0, 100, False, -1, 0, 1)],
+                   [(2, 0, 128, True, 3, 1, 2)],
+                   [(2, 128, 200, True, 4, 1, 2), (3, 0, 1, False, -1, 2, 1)]]
+    # K = 64, 64 -> units 3, 3; P = 6 gives one unit per partition: partitions
+    # 0, 1, 3, 4 own only charged units and hold no piece.
+    descs, pieces = pr.partition([0, 64, 128], 6)
+    assert descs == [(0, 1, -1, -1), (1, 2, -1, -1), (2, 3, 0, 0), (3, 4, -1, -1), (4, 5, -1, -1), (5, 6, 1, 1)]
+    assert [[(x.seq, x.begin, x.end, x.split) for x in p] for p in pieces] == [
+        [], [], [(0, 0, 64, False)], [], [], [(1, 0, 64, False)]]
+
+
 def test_partition_last_piece_takes_odd_slot():
     # K = 64, 128 -> tiles 1, 2; P = 2: bounds 0, 1, 3.  Partition 0 = seq 0 only;
     # partition 1 = seq 1 whole.  Now K = 128, 128, P = 3: bounds 0, 1, 2, 4:
     # partition 1 = tile 1 (seq 0 second half) -> first sequence, slot 2;
     # partition 0 = seq 0 first half, slot 0; partition 2 = seq 1 whole.
-    _, pieces = pr.partition([0, 128, 256], 3)
+    _, pieces = pr.partition([0, 128, 256], 3, seq_overhead=0)
     assert [(x.seq, x.begin, x.end, x.slot) for x in pieces[0]] == [(0, 0, 64, 0)]
     assert [(x.seq, x.begin, x.end, x.slot) for x in pieces[1]] == [(0, 64, 128, 2)]
     assert [(x.seq, x.begin, x.end, x.split) for x in pieces[2]] == [(1, 0, 128, False)]
     # K = 64, 192, P = 2: tiles 1, 3; bounds 0, 2, 4: partition 0 = seq 0 then
     # seq 1 tile 0 -> seq 1's piece there is not the first sequence: slot 1.
-    _, pieces = pr.partition([0, 64, 256], 2)
+    _, pieces = pr.partition([0, 64, 256], 2, seq_overhead=0)
     assert [(x.seq, x.slot) for x in pieces[0]] == [(0, -1), (1, 1)]
     assert [(x.seq, x.begin, x.end, x.slot) for x in pieces[1]] == [(1, 64, 192, 2)]
 
@@ -46,17 +73,20 @@ def _random_indptr(rng, B, kmax, zero_frac=0.2, offset=0):
     return np.concatenate([[offset], offset + np.cumsum(k)]).astype(np.int64)
 
 
+@pytest.mark.parametrize("charged", [0, 2, 5])
 @pytest.mark.parametrize("seed", range(24))
-def test_partition_invariants(seed):
+def test_partition_invariants(seed, charged):
     rng = np.random.default_rng(seed)
     B = int(rng.integers(1, 40))
     ptr = _random_indptr(rng, B, int(rng.choice([5, 64, 300, 3000])), offset=int(rng.integers(0, 1000)))
     P = int(rng.choice([1, 2, 3, 7, 32, 64, 300, 5000]))
-    descs, pieces = pr.partition(ptr, P)
+    descs, pieces = pr.partition(ptr, P, seq_overhead=charged)
     lens = np.diff(ptr)
     tiles = -(-lens // 64)
-    total = int(tiles.sum())
-    # partition sizes differ by at most one tile and tile the range in order
+    units = np.where(tiles > 0, tiles + charged, 0)
+    total = int(units.sum())
+    first_tile = np.cumsum(units) - tiles  # global unit of each sequence's first tile
+    # partition sizes (in units) differ by at most one and cover the range in order
     sizes = [d[1] - d[0] for d in descs]
     assert sum(sizes) == total and max(sizes) - min(sizes) <= 1
     assert descs[0][0] == 0 and descs[-1][1] == total
@@ -71,6 +101,9 @@ def test_partition_invariants(seed):
             assert descs[p][2:] == (-1, -1)
         for x in plist:
             assert x.begin % 64 == 0 and 0 <= x.begin < x.end <= lens[x.seq]
+            # the piece's tiles are units of this partition
+            u_lo, u_hi = first_tile[x.seq] + x.begin // 64, first_tile[x.seq] + -(-x.end // 64)
+            assert descs[p][0] <= u_lo < u_hi <= descs[p][1]
             seen[x.seq].append((p, x.begin, x.end))
     for b in range(B):
         segs = seen[b]
@@ -91,7 +124,8 @@ def test_partition_invariants(seed):
             n = len(seen[x.seq])
             assert x.num_pieces == n and x.split == (n > 1) and x.first_part == seen[x.seq][0][0]
             if x.split:
-                assert x.slot == 2 * p + (0 if i == 0 else 1)
+                starts_at_first_unit = first_tile[x.seq] + x.begin // 64 == descs[p][0]
+                assert x.slot == 2 * p + (0 if starts_at_first_unit else 1)
                 slots.append(x.slot)
             else:
                 assert x.slot == -1
@@ -105,11 +139,20 @@ def test_partition_edge_cases():
     # more partitions than tiles: bounds floor(4p/8) = 0,0,1,1,2,2,3,3,4, so the
     # odd partitions own one tile each and the even ones are empty -- empty
     # partitions sit between the pieces, which still number 4 (not 7 = 7 - 1 + 1)
-    descs, pieces = pr.partition([0, 200], 8)  # 4 tiles
+    descs, pieces = pr.partition([0, 200], 8, seq_overhead=0)  # 4 tiles
     assert sum(1 for p in pieces if p) == 4
     assert [(x.begin, x.end, x.slot) for p in pieces for x in p] == [(0, 64, 2), (64, 128, 6), (128, 192, 10),
                                                                       (192, 200, 14)]
     assert all(x.num_pieces == 4 and x.first_part == 1 for p in pieces for x in p)
+    # with the two charged units: 6 units, bounds floor(6p/8) = 0,0,1,2,3,3,4,5,6;
+    # partitions 1, 2 own the charged units, 3, 5, 6, 7 one tile each
+    descs, pieces = pr.partition([0, 200], 8)
+    assert [d[:2] for d in descs] == [(0, 0), (0, 1), (1, 2), (2, 3), (3, 3), (3, 4), (4, 5), (5, 6)]
+    assert [(x.begin, x.end, x.slot) for p in pieces for x in p] == [(0, 64, 6), (64, 128, 10), (128, 192, 12),
+                                                                      (192, 200, 14)]
+    assert all(x.num_pieces == 4 and x.first_part == 3 for p in pieces for x in p)
+    with pytest.raises(ValueError):
+        pr.partition([0, 5], 2, seq_overhead=-1)
     with pytest.raises(ValueError):
         pr.partition([0, 5], 0)
     with pytest.raises(ValueError):
