@@ -101,6 +101,16 @@ def test_bf16_shapes(gpu, H, qps, P):
     run_persistent(w, gpu, P)
 
 
+@pytest.mark.parametrize("P", [7, 300, 1500])
+def test_many_sequences(gpu, P):
+    """More sequences than a workgroup has threads, so the in-kernel plan scans
+    kv_indptr in several chunks: 600 short lists (40 of them empty), from one
+    partition holding many sequences to partitions holding only charged units."""
+    w = wl.ragged_workload("persist many", B=600, q_per_seq=1, H=16, kv_dtype="bf16", pool_rows=4096, max_k=200,
+                           zero_rows=40, indptr_offset=5, seed=120 + P)
+    run_persistent(w, gpu, P)
+
+
 def test_no_sink(gpu):
     w = wl.ragged_workload("persist no sink", B=4, q_per_seq=1, H=64, kv_dtype="fp8", pool_rows=2048, max_k=500,
                            zero_rows=1, seed=91)
