@@ -117,10 +117,12 @@ def test_no_sink(gpu):
     run_persistent(w, gpu, 6, sink=False)
 
 
-@pytest.mark.parametrize("H,kv_dtype,P", [(128, "bf16", 64), (128, "bf16", 100), (16, "fp8", 130)])
+@pytest.mark.parametrize("H,kv_dtype,P", [(128, "bf16", 64), (128, "bf16", 100), (16, "fp8", 130), (128, "fp8", 12),
+                                          (128, "fp8", 40), (128, "fp8", 100)])
 def test_long_sequence_many_pieces(gpu, H, kv_dtype, P):
-    """One long sequence spread over every partition: a merge of 64 pieces (at
-    most one per lane) and of more than 64 (several per lane)."""
+    """One long sequence spread over every partition: a merge of up to 64
+    pieces (at most one per lane) and of more than 64 (several per lane); on
+    the fp8 wide path, up to 18 pieces (staged in LDS) and more."""
     w = wl.ragged_workload("persist long", B=1, q_per_seq=1, H=H, kv_dtype=kv_dtype, pool_rows=65536, max_k=1,
                            seed=92)
     K = 20000
