@@ -48,6 +48,8 @@ def parse():
                          "5 = fp8 two-source, top-k 2048 main + 128-row window)")
     ap.add_argument("--cell", type=str, default=None, help="T x ctx matrix cell T:ctx:variant instead of --config")
     ap.add_argument("--splits", type=int, default=None, help="override the planner's split count")
+    ap.add_argument("--kernel", type=str, default=None, choices=["rows16", "pairs", "wide"],
+                    help="split-KV kernel family (default: the library's choice)")
     ap.add_argument("--partitions", type=int, default=None, help="persistent kernel: override the partition count")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -477,11 +479,11 @@ def main():
             if two:
                 smd.sparse_mla_decode_two_source(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["swa_pool"],
                                                  d["swa_indices"], d["sink"], w.softmax_scale, num_splits=s,
-                                                 q_per_seq=qps, out=out, lse=lse,
+                                                 q_per_seq=qps, out=out, lse=lse, kernel=args.kernel,
                                                  partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
             else:
                 smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
-                                      num_splits=s, q_per_seq=qps, out=out, lse=lse,
+                                      num_splits=s, q_per_seq=qps, out=out, lse=lse, kernel=args.kernel,
                                       partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
 
         kernel_step = step  # decode (+ merge when split; its time is subtracted below)
@@ -490,7 +492,7 @@ def main():
             smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
         kernel_name = "smd::decode_kernel"
-        cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv"})
+        cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv " + (args.kernel or "auto")})
         if two:
             cfg.update({"main_topk": w.arrays["main_indices"].shape[1], "swa_window": w.arrays["swa_indices"].shape[1],
                         "sources": 2})

@@ -59,12 +59,17 @@ enum {
 
 /* Largest split count of the split-KV entry points. */
 #define SMD_MAX_SPLITS 32
+/* Largest number of partials one merge (smd_merge_partials) combines, e.g.
+ * the splits of several callers' partial decodes of one index list. */
+#define SMD_MAX_MERGE_SPLITS 1024
 /* Index positions of one split are a multiple of this (except the last). */
 #define SMD_SPLIT_ALIGN 64
 /* Largest partition count of the persistent entry point. */
 #define SMD_MAX_PARTITIONS 16384
 
-/* Message describing this thread's most recent failure ("" if none). */
+/* Message describing this thread's most recent failure ("" if none).  Not an
+ * operation of the pages: the error channel of this C ABI.  The pointer stays
+ * valid until this thread's next call into the library. */
 const char *smd_last_error(void);
 
 /*
@@ -98,11 +103,15 @@ typedef struct smd_kv_pool {
 } smd_kv_pool;
 
 /*
- * Cost model of the host split planner (aiter page, Summary part 1: the
- * split count minimises workgroup waves x per-wave KV time plus the
- * partial-write / stage-2 cost of splitting).  All times in picoseconds.  A
- * decode workgroup owns rows_per_wg query rows of one index row and one
- * split; its waves_per_wg waves share the split's positions in steps of 16.
+ * Cost model of the host split planner.  The aiter page "[ASM][HIP][MLA v4
+ * nm] Split plan helper and persistent decode kernel", Summary part 1, picks
+ * the split count from the call's sizes alone by minimising a modelled time
+ * that grows with the rounds of workgroups the GPU must run and with the
+ * extra partial traffic and merge that each split adds.  This library's
+ * formula, all times in picoseconds (the terms are ours; the page prints no
+ * formula or coefficients): a decode workgroup owns rows_per_wg query rows of
+ * one index row and one split, and its waves_per_wg waves share the split's
+ * positions in steps of 16.
  *
  *   M         = num_heads * q_per_seq,   G = ceil(M / rows_per_wg)
  *   slots     = num_cus * wg_per_cu
@@ -154,11 +163,15 @@ int smd_plan_num_kv_splits_model(int32_t num_seqs, int32_t num_heads, int32_t q_
 int smd_plan_default_model(smd_plan_model *model);
 
 /*
- * Bytes of the FP32 partials a split-KV call with num_splits splits writes:
- * partial_o [num_tokens, num_heads, num_splits, 512] plus partial_lse
- * [num_tokens, num_heads, num_splits], i.e. num_tokens * num_heads *
- * num_splits * 513 * 4.  Returns 0 for negative sizes or num_splits outside
- * [1, SMD_MAX_SPLITS] (smd_last_error() says which).
+ * Bytes of FP32 partials for num_splits pieces per (token, head): partial_o
+ * [num_tokens, num_heads, num_splits, 512] plus partial_lse [num_tokens,
+ * num_heads, num_splits], i.e. num_tokens * num_heads * num_splits * 513 * 4.
+ * These are the split partials of the aiter page "[ASM][HIP][MLA v4 nm] Split
+ * plan helper and persistent decode kernel", Summary part 1 (FP32 partials
+ * that a stage-2 merge reduces).  Valid for num_splits in [1,
+ * SMD_MAX_MERGE_SPLITS], the range smd_merge_partials accepts (a split-KV
+ * call itself takes at most SMD_MAX_SPLITS).  Returns 0 for negative sizes or
+ * num_splits outside that range (smd_last_error() says which).
  */
 size_t smd_partials_bytes(int32_t num_tokens, int32_t num_heads, int32_t num_splits);
 
@@ -166,10 +179,46 @@ size_t smd_partials_bytes(int32_t num_tokens, int32_t num_heads, int32_t num_spl
  * Index positions [*begin, *end) of split `split` out of num_splits over a
  * list of kv_len indices: chunk = roundup(ceil(kv_len / num_splits), 64),
  * split r covers [min(r*chunk, kv_len), min((r+1)*chunk, kv_len)).  Trailing
- * splits may be empty.  This is the rule the decode kernels apply.
+ * splits may be empty.  This is the rule the decode kernels apply.  It is a
+ * reading of the aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and
+ * persistent decode kernel", Summary part 1, which describes a uniform split
+ * of each index list into contiguous ranges without printing the rounding;
+ * the 64-position alignment is this library's tile size.  Host only; returns
+ * SMD_ERR_INVALID_ARG for NULL outputs or kv_len < 0, num_splits < 1, split
+ * outside [0, num_splits).
  */
 int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t *begin,
                      int32_t *end);
+
+/*
+ * Kernel families of the split-KV decode (the results agree to the documented
+ * tolerances, not bit for bit).  M = num_heads * q_per_seq.
+ *   SMD_KERNEL_ROWS16  16 query rows per workgroup; 8 waves share the split's
+ *                      positions and merge their states at the end.
+ *   SMD_KERNEL_PAIRS   32 query rows per workgroup, dims split over wave pairs
+ *                      (M a multiple of 32).
+ *   SMD_KERNEL_WIDE    128 query rows per workgroup, 4 waves of 32 rows on
+ *                      32x32 MFMAs sharing every gathered row (M a multiple of
+ *                      128, one source).
+ * SMD_KERNEL_AUTO picks WIDE when it fits and the grid, (num_tokens /
+ * q_per_seq) * num_splits workgroups per group of 128 rows, is at least 128;
+ * otherwise PAIRS when M is a multiple of 32 and, with W = (num_tokens /
+ * q_per_seq) * num_splits * (M / 32), 7 * ceil(W / 256) < 4 * ceil(2W / 256);
+ * otherwise ROWS16.  A named family that does not fit the shape is
+ * SMD_ERR_UNSUPPORTED.
+ */
+enum {
+  SMD_KERNEL_AUTO = 0,
+  SMD_KERNEL_ROWS16 = 1,
+  SMD_KERNEL_PAIRS = 2,
+  SMD_KERNEL_WIDE = 3
+};
+
+/* Options of the _ex entry points; NULL means all defaults (zero). */
+typedef struct smd_decode_options {
+  int32_t kernel;      /* SMD_KERNEL_* */
+  int32_t reserved[7]; /* must be zero */
+} smd_decode_options;
 
 /*
  * Split-KV sparse MLA decode over dense index rows.
@@ -199,12 +248,7 @@ int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t 
  *  (smd_merge_partials).  A row with no valid index gets out = 0 and
  *  lse = sink_h (-inf without a sink).  topk == 0 or num_tokens == 0
  *  launches nothing.
- *  Kernel choice (results agree to the tolerances above, not bit for bit):
- *  workgroups of 16 query rows, or -- when M = num_heads * q_per_seq is a
- *  multiple of 32 and, with W = (num_tokens / q_per_seq) * num_splits *
- *  (M / 32), 7 * ceil(W / 256) < 4 * ceil(2W / 256) -- the dim-split kernel
- *  with 32 query rows per workgroup.  The environment variable
- *  SMD_DECODE_PAIRS=1 / 0 forces that choice (when M allows it).
+ *  The kernel family is SMD_KERNEL_AUTO's choice (see above).
  */
 int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
                           int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
@@ -212,6 +256,15 @@ int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_to
                           const float *sink, float softmax_scale, int32_t num_splits,
                           float *partial_o, float *partial_lse, void *out, float *lse,
                           void *stream);
+
+/* smd_sparse_mla_decode with explicit options (options may be NULL); an
+ * unknown kernel value or a non-zero reserved field is SMD_ERR_INVALID_ARG. */
+int smd_sparse_mla_decode_ex(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                             int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
+                             const int32_t *indices, int64_t indices_stride, int32_t topk,
+                             const float *sink, float softmax_scale, int32_t num_splits,
+                             float *partial_o, float *partial_lse, void *out, float *lse,
+                             const smd_decode_options *options, void *stream);
 
 /*
  * Two-source decode: the compressed main cache and the sliding-window (SWA)
@@ -244,6 +297,17 @@ int smd_sparse_mla_decode_two_source(const void *q_nope, const void *q_rope, int
                                      float softmax_scale, int32_t num_splits, float *partial_o,
                                      float *partial_lse, void *out, float *lse, void *stream);
 
+/* The two-source decode with explicit options (options may be NULL).  With
+ * both lists non-empty SMD_KERNEL_WIDE does not fit (one source only). */
+int smd_sparse_mla_decode_two_source_ex(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                        int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *main_kv,
+                                        const int32_t *main_indices, int64_t main_stride, int32_t k_main,
+                                        const smd_kv_pool *swa_kv, const int32_t *swa_indices,
+                                        int64_t swa_stride, int32_t k_swa, const float *sink,
+                                        float softmax_scale, int32_t num_splits, float *partial_o,
+                                        float *partial_lse, void *out, float *lse,
+                                        const smd_decode_options *options, void *stream);
+
 /*
  * Stage-2 merge (aiter page, Summary part 1: always reduce the FP32
  * partials, even with one split per row):
@@ -251,7 +315,7 @@ int smd_sparse_mla_decode_two_source(const void *q_nope, const void *q_rope, int
  *  partial_o fp32 [num_tokens, num_heads, num_splits, 512], partial_lse fp32
  *  [num_tokens, num_heads, num_splits]; sink fp32 [num_heads] or NULL;
  *  out bf16 [num_tokens, num_heads, 512] (required); lse fp32
- *  [num_tokens, num_heads] or NULL.  num_splits in [1, 1024].  No finite
+ *  [num_tokens, num_heads] or NULL.  num_splits in [1, SMD_MAX_MERGE_SPLITS].  No finite
  *  term and no sink gives out = 0, lse = -inf.
  */
 int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t num_tokens,

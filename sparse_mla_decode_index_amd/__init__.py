@@ -20,11 +20,19 @@ NOPE = 448
 ROPE = 64
 DIM = 512
 MAX_SPLITS = 32
+MAX_MERGE_SPLITS = 1024
 SPLIT_ALIGN = 64
 MAX_PARTITIONS = 16384
 
 KV_BF16 = 0
 KV_FP8_E4M3_UE8M0 = 1
+
+# Kernel families of the split-KV decode (include/smd.h, SMD_KERNEL_*).
+KERNEL_AUTO = 0
+KERNEL_ROWS16 = 1
+KERNEL_PAIRS = 2
+KERNEL_WIDE = 3
+_KERNELS = {"auto": KERNEL_AUTO, "rows16": KERNEL_ROWS16, "pairs": KERNEL_PAIRS, "wide": KERNEL_WIDE}
 
 _LIB_PATH = Path(__file__).resolve().parent / "libsmd.so"
 _lib = None
@@ -50,6 +58,19 @@ class _KVPool(ctypes.Structure):
         ("scale", ctypes.c_void_p),
         ("scale_stride", ctypes.c_int64),
     ]
+
+
+class _DecodeOptions(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+
+
+def _options(kernel) -> Optional[_DecodeOptions]:
+    """A smd_decode_options for `kernel` (a KERNEL_* value or its name), or
+    None for the library's default."""
+    if kernel is None:
+        return None
+    k = _KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
+    return _DecodeOptions(kernel=k)
 
 
 class PlanModel(ctypes.Structure):
@@ -99,10 +120,18 @@ def lib() -> ctypes.CDLL:
     L.smd_sparse_mla_decode.restype = ctypes.c_int
     L.smd_sparse_mla_decode.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
                                         vp, f32, i32, vp, vp, vp, vp, vp]
+    L.smd_sparse_mla_decode_ex.restype = ctypes.c_int
+    L.smd_sparse_mla_decode_ex.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
+                                           vp, f32, i32, vp, vp, vp, vp, ctypes.POINTER(_DecodeOptions), vp]
     L.smd_sparse_mla_decode_two_source.restype = ctypes.c_int
     L.smd_sparse_mla_decode_two_source.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
                                                    ctypes.POINTER(_KVPool), vp, i64, i32,
                                                    vp, f32, i32, vp, vp, vp, vp, vp]
+    L.smd_sparse_mla_decode_two_source_ex.restype = ctypes.c_int
+    L.smd_sparse_mla_decode_two_source_ex.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64,
+                                                      i32, ctypes.POINTER(_KVPool), vp, i64, i32,
+                                                      vp, f32, i32, vp, vp, vp, vp,
+                                                      ctypes.POINTER(_DecodeOptions), vp]
     L.smd_merge_partials.restype = ctypes.c_int
     L.smd_merge_partials.argtypes = [vp, vp, i32, i32, i32, vp, vp, vp, vp]
     L.smd_write_kv_fp8.restype = ctypes.c_int
@@ -295,24 +324,27 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       partial_o: Optional[torch.Tensor] = None,
                       partial_lse: Optional[torch.Tensor] = None,
-                      partials_only: bool = False):
+                      partials_only: bool = False, kernel=None):
     """Split-KV sparse MLA decode.
 
     q_nope bf16 [T,H,448], q_rope bf16 [T,H,64], indices int32 [T/q_per_seq, K]
     (row stride free), sink fp32 [H] or None.  Returns (out, lse) — bf16
     [T,H,512] and fp32 [T,H] — or, with partials_only, (partial_o, partial_lse)
     of shapes [T,H,s,512] and [T,H,s].  num_splits=None asks the host planner.
+    kernel: None (the library's choice) or a kernel family ("rows16", "pairs",
+    "wide" or a KERNEL_* value).
     """
     T, H, num_splits, out, lse, partial_o, partial_lse = _decode_buffers(
         q_nope, q_rope, [("indices", indices)], sink, [kv], q_per_seq, num_splits, out, lse, partial_o,
         partial_lse, partials_only)
     pool = kv._struct()
-    rc = lib().smd_sparse_mla_decode(
+    opt = _options(kernel)
+    rc = lib().smd_sparse_mla_decode_ex(
         q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool), *_idx_args(indices),
         _ptr(sink), float(softmax_scale), num_splits,
         _ptr(partial_o), _ptr(partial_lse),
         None if partials_only else out.data_ptr(), None if partials_only else lse.data_ptr(),
-        _stream(q_nope))
+        ctypes.byref(opt) if opt is not None else None, _stream(q_nope))
     _check("smd_sparse_mla_decode", rc)
     if partials_only:
         return partial_o, partial_lse
@@ -326,21 +358,23 @@ def sparse_mla_decode_two_source(q_nope: torch.Tensor, q_rope: torch.Tensor, mai
                                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                                  partial_o: Optional[torch.Tensor] = None,
                                  partial_lse: Optional[torch.Tensor] = None,
-                                 partials_only: bool = False):
+                                 partials_only: bool = False, kernel=None):
     """Two-source decode: main_indices [T/q_per_seq, K_main] index main_kv,
     swa_indices [T/q_per_seq, K_swa] index swa_kv, all one softmax (main
     positions first).  Pools of the same dtype and strides.  Outputs as
-    sparse_mla_decode; the planner sees K_main + K_swa positions."""
+    sparse_mla_decode (kernel likewise); the planner sees K_main + K_swa
+    positions."""
     T, H, num_splits, out, lse, partial_o, partial_lse = _decode_buffers(
         q_nope, q_rope, [("main_indices", main_indices), ("swa_indices", swa_indices)], sink, [main_kv, swa_kv],
         q_per_seq, num_splits, out, lse, partial_o, partial_lse, partials_only)
     mp, sp = main_kv._struct(), swa_kv._struct()
-    rc = lib().smd_sparse_mla_decode_two_source(
+    opt = _options(kernel)
+    rc = lib().smd_sparse_mla_decode_two_source_ex(
         q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(mp), *_idx_args(main_indices),
         ctypes.byref(sp), *_idx_args(swa_indices), _ptr(sink), float(softmax_scale), num_splits,
         _ptr(partial_o), _ptr(partial_lse),
         None if partials_only else out.data_ptr(), None if partials_only else lse.data_ptr(),
-        _stream(q_nope))
+        ctypes.byref(opt) if opt is not None else None, _stream(q_nope))
     _check("smd_sparse_mla_decode_two_source", rc)
     if partials_only:
         return partial_o, partial_lse

@@ -5,7 +5,6 @@
 #include <limits.h>
 #include <math.h>
 #include <stdarg.h>
-#include <stdlib.h>
 #include <stdio.h>
 #include <string.h>
 
@@ -89,18 +88,38 @@ static int check_pool(const char *fn, const smd_kv_pool *kv, DecodeArgs &a) {
   return SMD_OK;
 }
 
+// The split-KV kernel families (include/smd.h, SMD_KERNEL_*).
+enum Kern { kKernRows16 = 1, kKernPairs = 2, kKernWide = 3 };
+
 // The dim-split kernel (32 query rows per workgroup) moves less through LDS
 // per unit of work but has half as many workgroups, each taking about 7/4 of
 // the time of a 16-row one (measured on full GPUs).  With one workgroup per
 // CU on 256 CUs it wins when 7/4 x its rounds of workgroups is below the
 // 16-row kernel's rounds: a full grid, and not a grid that spills a small
 // last round.
-static bool use_pairs(int32_t M, int64_t units) {
+static bool pairs_pay(int32_t M, int64_t units) {
   if (M % 32 != 0) return false;
-  if (const char *e = getenv("SMD_DECODE_PAIRS")) return atoi(e) != 0;
   const int64_t w = units * (M / 32);
   const int64_t rounds_pairs = (w + 255) / 256, rounds_rows = (2 * w + 255) / 256;
   return 7 * rounds_pairs < 4 * rounds_rows;
+}
+
+// The wide kernel (128 query rows per workgroup on 32x32 MFMAs) shares each
+// gathered row among 128 query rows; it needs M % 128 == 0 and one source,
+// and it pays once its grid fills at least half the GPU.
+static bool wide_fits(int32_t M, bool two) { return M % 128 == 0 && !two; }
+
+// Kernel of a split-KV call: the caller's choice when it names one (checked
+// against the shape), else the rule above.  Returns 0 for an impossible choice.
+static int pick_kernel(int32_t requested, int32_t M, int64_t units, bool two) {
+  switch (requested) {
+    case SMD_KERNEL_ROWS16: return kKernRows16;
+    case SMD_KERNEL_PAIRS: return M % 32 == 0 ? kKernPairs : 0;
+    case SMD_KERNEL_WIDE: return wide_fits(M, two) ? kKernWide : 0;
+    default: break;
+  }
+  if (wide_fits(M, two) && units >= 128) return kKernWide;
+  return pairs_pay(M, units) ? kKernPairs : kKernRows16;
 }
 
 }  // namespace smd
@@ -122,8 +141,20 @@ static int decode_impl(const char *fn, const void *q_nope, const void *q_rope, i
                        int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv, const int32_t *indices,
                        int64_t indices_stride, int32_t topk, const SecondSource *two, const float *sink,
                        float softmax_scale, int32_t num_splits, float *partial_o, float *partial_lse, void *out,
-                       float *lse, void *stream) {
+                       float *lse, const smd_decode_options *opt, void *stream) {
   g_err[0] = 0;
+  if (opt != nullptr) {
+    if (opt->kernel < SMD_KERNEL_AUTO || opt->kernel > SMD_KERNEL_WIDE) {
+      set_error("%s: unknown kernel choice %d", fn, opt->kernel);
+      return SMD_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 7; ++i) {
+      if (opt->reserved[i] != 0) {
+        set_error("%s: options.reserved must be zero", fn);
+        return SMD_ERR_INVALID_ARG;
+      }
+    }
+  }
   if (num_tokens < 0 || topk < 0 || indices_stride < 0 ||
       (two && (two->count < 0 || two->indices_stride < 0))) {
     set_error("%s: negative size (num_tokens=%d counts=%d,%d strides=%lld,%lld)", fn, num_tokens, topk,
@@ -243,15 +274,21 @@ static int decode_impl(const char *fn, const void *q_nope, const void *q_rope, i
   a.S = num_splits;
   a.num_units = rows * num_splits;
   const bool fp8 = kv->dtype == SMD_KV_FP8_E4M3_UE8M0;
-  const bool pairs = use_pairs(M, (int64_t)rows * num_splits);
-  a.G = M / (pairs ? 32 : 16);
+  const int kern = pick_kernel(opt ? opt->kernel : SMD_KERNEL_AUTO, M, (int64_t)rows * num_splits,
+                               a.indices2 != nullptr);
+  if (kern == 0) {
+    set_error("%s: kernel choice %d does not fit M = %d query rows per index row%s", fn, opt->kernel, M,
+              a.indices2 ? " with two sources" : "");
+    return SMD_ERR_UNSUPPORTED;
+  }
+  a.G = M / (kern == kKernWide ? 128 : (kern == kKernPairs ? 32 : 16));
   a.part_o = need_partials ? partial_o : nullptr;
   a.part_lse = need_partials ? partial_lse : nullptr;
   a.out = need_partials ? nullptr : (uint16_t *)out;
   a.lse = need_partials ? nullptr : lse;
   a.hilo = out == nullptr;  // FP32 partials are the result only without out
   hipStream_t st = (hipStream_t)stream;
-  hipError_t e = launch_decode(a, fp8, pairs, st);
+  hipError_t e = kern == kKernWide ? launch_decode_wide(a, fp8, st) : launch_decode(a, fp8, kern == kKernPairs, st);
   if (e != hipSuccess) {
     set_error("%s: decode launch failed: %s", fn, hipGetErrorString(e));
     return SMD_ERR_HIP;
@@ -267,15 +304,38 @@ static int decode_impl(const char *fn, const void *q_nope, const void *q_rope, i
   return SMD_OK;
 }
 
+extern "C" int smd_sparse_mla_decode_ex(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                        int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
+                                        const int32_t *indices, int64_t indices_stride, int32_t topk,
+                                        const float *sink, float softmax_scale, int32_t num_splits,
+                                        float *partial_o, float *partial_lse, void *out, float *lse,
+                                        const smd_decode_options *options, void *stream) {
+  return decode_impl("smd_sparse_mla_decode", q_nope, q_rope, num_tokens, num_heads, q_per_seq, kv, indices,
+                     indices_stride, topk, nullptr, sink, softmax_scale, num_splits, partial_o, partial_lse, out,
+                     lse, options, stream);
+}
+
 extern "C" int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_tokens,
                                      int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
                                      const int32_t *indices, int64_t indices_stride, int32_t topk,
                                      const float *sink, float softmax_scale, int32_t num_splits,
                                      float *partial_o, float *partial_lse, void *out, float *lse,
                                      void *stream) {
-  return decode_impl("smd_sparse_mla_decode", q_nope, q_rope, num_tokens, num_heads, q_per_seq, kv, indices,
-                     indices_stride, topk, nullptr, sink, softmax_scale, num_splits, partial_o, partial_lse, out,
-                     lse, stream);
+  return smd_sparse_mla_decode_ex(q_nope, q_rope, num_tokens, num_heads, q_per_seq, kv, indices, indices_stride,
+                                  topk, sink, softmax_scale, num_splits, partial_o, partial_lse, out, lse, nullptr,
+                                  stream);
+}
+
+extern "C" int smd_sparse_mla_decode_two_source_ex(
+    const void *q_nope, const void *q_rope, int32_t num_tokens, int32_t num_heads, int32_t q_per_seq,
+    const smd_kv_pool *main_kv, const int32_t *main_indices, int64_t main_stride, int32_t k_main,
+    const smd_kv_pool *swa_kv, const int32_t *swa_indices, int64_t swa_stride, int32_t k_swa, const float *sink,
+    float softmax_scale, int32_t num_splits, float *partial_o, float *partial_lse, void *out, float *lse,
+    const smd_decode_options *options, void *stream) {
+  const SecondSource two{swa_kv, swa_indices, swa_stride, k_swa};
+  return decode_impl("smd_sparse_mla_decode_two_source", q_nope, q_rope, num_tokens, num_heads, q_per_seq, main_kv,
+                     main_indices, main_stride, k_main, &two, sink, softmax_scale, num_splits, partial_o,
+                     partial_lse, out, lse, options, stream);
 }
 
 extern "C" int smd_sparse_mla_decode_two_source(const void *q_nope, const void *q_rope, int32_t num_tokens,
@@ -285,10 +345,10 @@ extern "C" int smd_sparse_mla_decode_two_source(const void *q_nope, const void *
                                                 int64_t swa_stride, int32_t k_swa, const float *sink,
                                                 float softmax_scale, int32_t num_splits, float *partial_o,
                                                 float *partial_lse, void *out, float *lse, void *stream) {
-  const SecondSource two{swa_kv, swa_indices, swa_stride, k_swa};
-  return decode_impl("smd_sparse_mla_decode_two_source", q_nope, q_rope, num_tokens, num_heads, q_per_seq, main_kv,
-                     main_indices, main_stride, k_main, &two, sink, softmax_scale, num_splits, partial_o,
-                     partial_lse, out, lse, stream);
+  return smd_sparse_mla_decode_two_source_ex(q_nope, q_rope, num_tokens, num_heads, q_per_seq, main_kv,
+                                             main_indices, main_stride, k_main, swa_kv, swa_indices, swa_stride,
+                                             k_swa, sink, softmax_scale, num_splits, partial_o, partial_lse, out,
+                                             lse, nullptr, stream);
 }
 
 extern "C" int smd_merge_partials(const float *partial_o, const float *partial_lse,
@@ -300,8 +360,8 @@ extern "C" int smd_merge_partials(const float *partial_o, const float *partial_l
     set_error("%s: invalid num_tokens=%d num_heads=%d", fn, num_tokens, num_heads);
     return SMD_ERR_INVALID_ARG;
   }
-  if (num_splits < 1 || num_splits > 1024) {
-    set_error("%s: num_splits=%d not in [1,1024]", fn, num_splits);
+  if (num_splits < 1 || num_splits > SMD_MAX_MERGE_SPLITS) {
+    set_error("%s: num_splits=%d not in [1,%d]", fn, num_splits, SMD_MAX_MERGE_SPLITS);
     return SMD_ERR_INVALID_ARG;
   }
   if (num_tokens == 0) return SMD_OK;
@@ -325,15 +385,9 @@ extern "C" int smd_merge_partials(const float *partial_o, const float *partial_l
 // ----------------------------------------------------------------------------
 // persistent, graph-safe variant
 // ----------------------------------------------------------------------------
-// Row blocks per workgroup of the persistent kernel: the largest of 4, 2, 1
+// Row blocks per workgroup of the persistent kernel: the largest of 8, 4, 2, 1
 // that divides M / 16, so the 16*rb-row groups cover every query row.
-static int persist_rb(int32_t M) {
-  if (const char *e = getenv("SMD_PERSIST_RB")) {
-    const int r = atoi(e);
-    if ((r == 1 || r == 2 || r == 4 || r == 8) && M % (16 * r) == 0) return r;
-  }
-  return M % 128 == 0 ? 8 : (M % 64 == 0 ? 4 : (M % 32 == 0 ? 2 : 1));
-}
+static int persist_rb(int32_t M) { return M % 128 == 0 ? 8 : (M % 64 == 0 ? 4 : (M % 32 == 0 ? 2 : 1)); }
 static int32_t persist_groups(int32_t M) { return M / (16 * persist_rb(M)); }
 
 extern "C" int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, int32_t num_cus) {

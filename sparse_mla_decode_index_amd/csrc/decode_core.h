@@ -39,72 +39,13 @@
 // distinct banks.
 #pragma once
 
-#include "smd_internal.h"
-
-#include <math.h>
+#include "common.h"
 
 namespace smd {
-
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define SMD_LDS __attribute__((address_space(3)))
-#define SMD_GLOBAL __attribute__((address_space(1)))
 
 constexpr int kBK = 32;                      // KV rows per tile
 constexpr int kLdsRow = 1024;                // bytes per bf16 row in LDS
 constexpr int kTileBytes = kBK * kLdsRow;    // 32 KiB
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-
-// A zero row used as the source of every masked row (1 KiB of zero bytes:
-// bf16 zeros, e4m3 zeros and UE8M0 code 0).
-static __device__ __attribute__((aligned(256))) uint8_t g_zero_row[1024];
-
-// XOR permutation of 16-byte chunks for row r of a tile.  Rows r and r+16 share
-// it.  swz is a bijection on 0..15 (QK reads of 16 consecutive rows hit 16
-// distinct chunk slots) and maps rows 0..7 / 8..15 to even / odd values (the
-// transposed reads of 8 rows x 32 bytes cover 256 distinct bytes).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-
-// max / sum over the four 16-lane groups (lanes j, j+16, j+32, j+48) with the
-// gfx950 permlane swaps (VALU, no LDS round trip).
-__device__ __forceinline__ float group_max(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
-// UE8M0 code -> fp32 scale 2^(code-127).  Code 0 is the subnormal 2^-127.
-__device__ __forceinline__ float ue8m0_scale(uint32_t code) {
-  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
-}
-
-// A row's reference max is fixed at its first tile with a valid entry; a later
-// score more than this far above it (log2 domain) sends the workgroup through
-// an exact-max second pass, so every p = 2^(x - m_ref) stays <= 2^32.
-constexpr float kRefSlackLog2 = 32.f;
 
 // Index lists are staged through LDS in blocks of kIdxBlock positions (8 tiles),
 // double-buffered and refilled kIdxBlock/32 - 3 tiles before first use, so no
@@ -129,7 +70,7 @@ __device__ __forceinline__ int load_idx_block(const int32_t *row_idx, int p0, in
 
 // Row data of one tile held in registers between its global loads and its
 // LDS stores.  Wave w handles tile rows 8w .. 8w+7.
-//   bf16: v[i] = logical 16-byte chunk lane ^ swz(rr) of row rr = 8w + i.
+//   bf16: v[i] = logical 16-byte chunk lane ^ tile_swz(rr) of row rr = 8w + i.
 //   fp8:  v[j] (j < 4) = 16 e4m3 bytes of chunk (lane & 31) (clamped to 27) of
 //         row 8w + 2j + (lane >> 5) and code[j] = the UE8M0 code of that
 //         chunk's 64-dim block; rope = 16 RoPE bytes, chunk lane & 7 of row
@@ -147,12 +88,20 @@ struct GatherLanes {
   uint32_t sel_rope;       // bf16, split layout: bit i set when that chunk is RoPE
 };
 
+// Chunk permutation of tile row r: swz (16x16 MFMA operands) or swz32 (32x32).
+enum TileLayout { kLay16 = 0, kLay32 = 1 };
+template <int LAY>
+__device__ __forceinline__ int tile_swz(int r) {
+  return LAY == kLay32 ? swz32(r) : swz(r);
+}
+
+template <int LAY = kLay16>
 __device__ __forceinline__ GatherLanes make_gather_lanes(int wave, int lane) {
   GatherLanes g;
   g.sel_rope = 0;
 #pragma unroll
   for (int i = 0; i < kBK / 4; ++i) {
-    const int c = lane ^ swz(wave * (kBK / 4) + i);
+    const int c = lane ^ tile_swz<LAY>(wave * (kBK / 4) + i);
     g.voff[i] = (uint32_t)c * 16u;
     g.sel_rope |= (c >= kNope / 8 ? 1u : 0u) << i;
   }
@@ -220,38 +169,47 @@ __device__ __forceinline__ void load_rows(const DecodeArgs &a, const uint8_t *zr
 
 // LDS stores of the staged rows into `tile` (bf16 layout, chunks swizzled);
 // fp8 rows are dequantised on the way: e4m3 x 2^(code-127) is exact in bf16.
+// The stores come in kStorePieces<FP8> independent pieces (bf16: one row
+// each; fp8: one row pair each, then the RoPE dims of the 8 rows), so that a
+// caller can spread them between other work.
 template <bool FP8>
-__device__ __forceinline__ void store_rows(uint8_t SMD_LDS *tile, int wave, int lane, const Staged<FP8> &st) {
+constexpr int kStorePieces = FP8 ? 5 : kBK / 4;
+
+template <bool FP8, int LAY = kLay16>
+__device__ __forceinline__ void store_row_piece(uint8_t SMD_LDS *tile, int wave, int lane, const Staged<FP8> &st,
+                                                int i) {
   if constexpr (!FP8) {
-#pragma unroll
-    for (int i = 0; i < kBK / 4; ++i)
-      *(u32x4 SMD_LDS *)(tile + (wave * (kBK / 4) + i) * kLdsRow + lane * 16) = st.v[i];
-  } else {
+    *(u32x4 SMD_LDS *)(tile + (wave * (kBK / 4) + i) * kLdsRow + lane * 16) = st.v[i];
+  } else if (i < 4) {
     const int c = lane & 31;
+    const int rl = 2 * i + (lane >> 5);  // row within the wave's 8
+    const uint32_t code = st.code[i];
+    if (c < 28) {
+      const int rr = wave * (kBK / 4) + rl;
+      const int f = tile_swz<LAY>(rr);
+      uint8_t SMD_LDS *row = tile + rr * kLdsRow;
+      const float sc = ue8m0_scale(code);
+      u32x4 lo, hi;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int rl = 2 * j + (lane >> 5);            // row within the wave's 8
-      const uint32_t code = st.code[j];
-      if (c < 28) {
-        const int rr = wave * (kBK / 4) + rl;
-        const int f = swz(rr);
-        uint8_t SMD_LDS *row = tile + rr * kLdsRow;
-        const float sc = ue8m0_scale(code);
-        u32x4 lo, hi;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[j][q], sc, false));
-          const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[j][q], sc, true));
-          if (q < 2) { lo[2 * q] = u0; lo[2 * q + 1] = u1; }
-          else { hi[2 * q - 4] = u0; hi[2 * q - 3] = u1; }
-        }
-        *(u32x4 SMD_LDS *)(row + (((2 * c) ^ f) << 4)) = lo;
-        *(u32x4 SMD_LDS *)(row + (((2 * c + 1) ^ f) << 4)) = hi;
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t u0 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[i][q], sc, false));
+        const uint32_t u1 = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)st.v[i][q], sc, true));
+        if (q < 2) { lo[2 * q] = u0; lo[2 * q + 1] = u1; }
+        else { hi[2 * q - 4] = u0; hi[2 * q - 3] = u1; }
       }
+      *(u32x4 SMD_LDS *)(row + (((2 * c) ^ f) << 4)) = lo;
+      *(u32x4 SMD_LDS *)(row + (((2 * c + 1) ^ f) << 4)) = hi;
     }
+  } else {
     const int rr = wave * (kBK / 4) + (lane >> 3);
-    *(u32x4 SMD_LDS *)(tile + rr * kLdsRow + (((kNope / 8 + (lane & 7)) ^ swz(rr)) << 4)) = st.rope;
+    *(u32x4 SMD_LDS *)(tile + rr * kLdsRow + (((kNope / 8 + (lane & 7)) ^ tile_swz<LAY>(rr)) << 4)) = st.rope;
   }
+}
+
+template <bool FP8, int LAY = kLay16>
+__device__ __forceinline__ void store_rows(uint8_t SMD_LDS *tile, int wave, int lane, const Staged<FP8> &st) {
+#pragma unroll
+  for (int i = 0; i < kStorePieces<FP8>; ++i) store_row_piece<FP8, LAY>(tile, wave, lane, st, i);
 }
 
 // Valid-row bits of a tile (first position first_pos, indices at tidx).
@@ -269,8 +227,6 @@ struct WaveState {
   float l_run;    // this lane's share of sum_j 2^(x_j - m_ref)
   bool overflow;  // some score exceeded m_ref + kRefSlackLog2 (this lane)
 };
-
-enum Pass { kPassMain = 0, kPassMax = 1, kPassFixed = 2 };
 
 // QK, softmax weights and PV over one 32-row tile for one wave: 16 query rows
 // and the 512/DS dims starting at chunk c0 (QK, 32-dim chunks) / block d0
@@ -509,44 +465,25 @@ __device__ __forceinline__ float row_total(float l_run) {
   return l;
 }
 
-// Final bf16 output of one query row with the sink folded in:
-// out = O / (l + e^(sink - m)), lse = m + ln(l + e^(sink - m)) (natural log).
+// Final bf16 output of one query row with the sink folded in (direct_scale).
 // dst points at dim 16*dbase + 4*grp of the row; the lse is written when
 // lse_dst is non-null.
 template <int ND>
 __device__ __forceinline__ void write_direct(const WaveState<ND> &w, float l_tot, float sink_ln, uint16_t *dst,
                                              float *lse_dst) {
-  const float sink2 = sink_ln * kLog2e;
-  const float mf = fmaxf(w.m_ref, sink2);
-  float inv = 0.f, lse_v = -INFINITY;
-  if (mf != -INFINITY) {
-    const float e = exp2_fast(w.m_ref - mf);
-    const float z = l_tot * e + exp2_fast(sink2 - mf);
-    inv = e / z;
-    lse_v = (mf + __log2f(z)) * kLn2;
-  }
+  const OutScale sc = direct_scale(w.m_ref, l_tot, sink_ln);
 #pragma unroll
-  for (int d = 0; d < ND; ++d) {
-    u32x2 v;
-    v[0] = (uint32_t)f32_to_bf16_rne(w.acc[d][0] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[d][1] * inv) << 16);
-    v[1] = (uint32_t)f32_to_bf16_rne(w.acc[d][2] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[d][3] * inv) << 16);
-    *(u32x2 *)(dst + 16 * d) = v;
-  }
-  if (lse_dst != nullptr) *lse_dst = lse_v;
+  for (int d = 0; d < ND; ++d) *(u32x2 *)(dst + 16 * d) = pack_bf16x4(w.acc[d], sc.inv);
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
-// FP32 partial of one query row (no sink): o = O / l, lse = m + ln l; an
-// empty range gives o = 0, lse = -inf.  dst as in write_direct.
+// FP32 partial of one query row (no sink, partial_scale).  dst as in write_direct.
 template <int ND>
 __device__ __forceinline__ void write_partial(const WaveState<ND> &w, float l_tot, float *dst, float *lse_dst) {
-  float inv = 0.f, lse_v = -INFINITY;
-  if (l_tot > 0.f) {
-    inv = 1.f / l_tot;
-    lse_v = (w.m_ref + __log2f(l_tot)) * kLn2;
-  }
+  const OutScale sc = partial_scale(w.m_ref, l_tot);
 #pragma unroll
-  for (int d = 0; d < ND; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[d] * inv;
-  if (lse_dst != nullptr) *lse_dst = lse_v;
+  for (int d = 0; d < ND; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[d] * sc.inv;
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
 }  // namespace smd

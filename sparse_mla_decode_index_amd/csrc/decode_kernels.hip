@@ -235,7 +235,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   u32x4 vo;
 #pragma unroll
   for (int i = 0; i < 4; ++i)
-    vo[i] = (uint32_t)f32_to_bf16_rne(o[2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[2 * i + 1] * inv) << 16);
+    vo[i] = pack_bf16x2(o[2 * i] * inv, o[2 * i + 1] * inv);
   *(u32x4 *)dst = vo;
   if (lse && lane == 0) lse[row] = mx + logf(z);
 }

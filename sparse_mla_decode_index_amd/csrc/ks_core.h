@@ -23,63 +23,34 @@
 // through an exact-max second pass, so the accumulators are never rescaled.
 #pragma once
 
-#include "smd_internal.h"
-
-#include <math.h>
+#include "common.h"
 
 namespace smd {
 namespace ks {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-#define SMD_LDS __attribute__((address_space(3)))
-#define SMD_GLOBAL __attribute__((address_space(1)))
+using smd::bf16x4;
+using smd::bf16x8;
+using smd::exp2_fast;
+using smd::f32_to_bf16_rne;
+using smd::f32x4;
+using smd::g_zero_row;
+using smd::group_max;
+using smd::group_sum;
+using smd::kLn2;
+using smd::kLog2e;
+using smd::kPassFixed;
+using smd::kPassMain;
+using smd::kPassMax;
+using smd::kRefSlackLog2;
+using smd::Pass;
+using smd::swz;
+using smd::u32x2;
+using smd::u32x4;
+using smd::ue8m0_scale;
 
 constexpr int kHalf = 16;                        // index positions per half-tile
 constexpr int kRowBytes = 1024;                  // one bf16 row in LDS
 constexpr int kHalfBytes = kHalf * kRowBytes;    // 16 KiB
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
-// A row's reference max is fixed at its first valid half-tile; a later score
-// more than this far above it (log2 domain) triggers the exact-max second pass.
-constexpr float kRefSlackLog2 = 32.f;
-
-// Zero bytes read in place of every masked row.
-static __device__ __attribute__((aligned(256))) uint8_t g_zero_row[1024];
-
-// XOR permutation of the 16-byte chunks of row r in a half-tile buffer.  It
-// only touches the low 4 chunk bits and makes conflict-free both the 16-byte
-// stores of the gathered pieces (16 rows x 4 chunks per instruction) and the
-// 8-byte transposed reads (16 rows x 2 chunks per instruction).
-__device__ __forceinline__ int swz(int r) { return ((r & 7) << 1) | ((r >> 3) & 1); }
-
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// max / sum over the four 16-lane groups (lanes j, j+16, j+32, j+48) with the
-// gfx950 permlane swaps (VALU, no LDS round trip).
-__device__ __forceinline__ float group_max(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-__device__ __forceinline__ float group_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
-}
-
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);  // quiet NaN
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
 
 // Gathered data of one half-tile in this lane's registers: v[i] = bytes
 // 16*lane .. +16 of row i of the half-tile (i 0..15).
@@ -187,11 +158,6 @@ __device__ __forceinline__ void issue_half(const DecodeArgs &a, uint32_t idx, bo
   }
 }
 
-// UE8M0 code -> fp32 scale 2^(code-127); code 0 is the subnormal 2^-127.
-__device__ __forceinline__ float ue8m0_scale(uint32_t code) {
-  return code ? __uint_as_float(code << 23) : __uint_as_float(0x00400000u);
-}
-
 // Gathered data of one fp8 half-tile.  A row is 448 e4m3 NoPE bytes with one
 // UE8M0 code per 64-byte block, plus 64 bf16 RoPE dims (128 bytes).  Lane l
 // serves row l / 4 and the quarter s = l % 4 of every 64-byte piece of it:
@@ -230,8 +196,6 @@ struct State {
   float l_run;    // this lane's share of sum 2^(x - m_ref)
   bool overflow;  // a score exceeded m_ref + kRefSlackLog2 (this lane)
 };
-
-enum Pass { kPassMain = 0, kPassMax = 1, kPassFixed = 2 };
 
 // Softmax weights of one half-tile for this lane's 4 kv rows (4g..4g+3) of
 // one query row, given that row's running state (reference max, this lane's
@@ -272,42 +236,23 @@ __device__ __forceinline__ void softmax_half(f32x4 s, uint32_t vbits, float scal
   softmax_step<PASS, P_HILO>(s, vbits, scale_log2, L, st.m_ref, st.l_run, st.overflow, pb, pl);
 }
 
-// Final bf16 output of one query row with the sink folded in:
-// out = O / (l + e^(sink - m)), lse = m + ln(l + e^(sink - m)) (natural log).
+// Final bf16 output of one query row with the sink folded in (direct_scale);
 // dst points at dim 128*w + 4g of the row for the w-th quarter of the dims;
 // the lse is written when lse_dst is non-null.
 __device__ __forceinline__ void write_direct(const f32x4 (&o)[8], float m, float l, float sink_ln, uint16_t *dst,
                                              float *lse_dst) {
-  const float sink2 = sink_ln * kLog2e;
-  const float mf = fmaxf(m, sink2);
-  float inv = 0.f, lse_v = -INFINITY;
-  if (mf != -INFINITY) {
-    const float e = exp2_fast(m - mf);
-    const float z = l * e + exp2_fast(sink2 - mf);
-    inv = e / z;
-    lse_v = (mf + __log2f(z)) * kLn2;
-  }
+  const OutScale sc = direct_scale(m, l, sink_ln);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) {
-    u32x2 v;
-    v[0] = (uint32_t)f32_to_bf16_rne(o[d][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[d][1] * inv) << 16);
-    v[1] = (uint32_t)f32_to_bf16_rne(o[d][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[d][3] * inv) << 16);
-    *(u32x2 *)(dst + 16 * d) = v;
-  }
-  if (lse_dst != nullptr) *lse_dst = lse_v;
+  for (int d = 0; d < 8; ++d) *(u32x2 *)(dst + 16 * d) = pack_bf16x4(o[d], sc.inv);
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
-// FP32 partial of one query row (no sink): o = O / l, lse = m + ln l; an empty
-// range gives o = 0, lse = -inf.  dst as in write_direct.
+// FP32 partial of one query row (no sink, partial_scale).  dst as in write_direct.
 __device__ __forceinline__ void write_partial(const f32x4 (&o)[8], float m, float l, float *dst, float *lse_dst) {
-  float inv = 0.f, lse_v = -INFINITY;
-  if (l > 0.f) {
-    inv = 1.f / l;
-    lse_v = (m + __log2f(l)) * kLn2;
-  }
+  const OutScale sc = partial_scale(m, l);
 #pragma unroll
-  for (int d = 0; d < 8; ++d) *(f32x4 *)(dst + 16 * d) = o[d] * inv;
-  if (lse_dst != nullptr) *lse_dst = lse_v;
+  for (int d = 0; d < 8; ++d) *(f32x4 *)(dst + 16 * d) = o[d] * sc.inv;
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
 }  // namespace ks

@@ -14,7 +14,7 @@
 //
 // Grid: P partitions x G query-row groups of 16*RB rows, RB the largest of 8,
 // 4, 2, 1 that divides M / 16 (8: the wide waves of wide_core.h, each wave
-// 32 rows, so one gathered tile serves 128 query rows).  Workgroup (p, g) walks the sequences of partition
+// 32 rows on 32x32 MFMAs, so one gathered tile serves 128 query rows).  Workgroup (p, g) walks the sequences of partition
 // p and attends row group g of each over the piece of its index list that p
 // owns.  A sequence inside one partition is
 // written directly.  A sequence spread over partitions fp..lp is split: each
@@ -208,7 +208,7 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
       u32x4 v;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        v[i] = (uint32_t)f32_to_bf16_rne(o[u][2 * i] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][2 * i + 1] * inv) << 16);
+        v[i] = pack_bf16x2(o[u][2 * i] * inv, o[u][2 * i + 1] * inv);
       *(u32x4 *)dst = v;
       if (a.lse != nullptr && lane == 0) a.lse[qrow[u]] = mx[u] + logf(z[u]);
     }
@@ -302,7 +302,7 @@ __device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b
       u32x4 vv;
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        vv[e] = (uint32_t)f32_to_bf16_rne(o[u][2 * e] * inv) | ((uint32_t)f32_to_bf16_rne(o[u][2 * e + 1] * inv) << 16);
+        vv[e] = pack_bf16x2(o[u][2 * e] * inv, o[u][2 * e + 1] * inv);
       *(u32x4 *)dst = vv;
       if (a.lse != nullptr && lane == 0) a.lse[qrow] = mx[u] + logf(z[u]);
     }
@@ -362,7 +362,7 @@ __device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int
   return b_first >= 0;
 }
 
-// RB = 8 runs the wide waves of wide_core.h: wave w owns blocks w and w+4
+// RB = 8 runs the wide waves of wide_core.h: wave w owns rows 32w .. 32w+31
 // of the group's 128 rows, all 512 dims.
 template <int RB, bool FP8, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void persistent_kernel(PersistArgs pa) {
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   constexpr int DS = WIDE ? 1 : 4 / RB;
   constexpr int NC = 16 / DS, ND = 32 / DS;
   constexpr int ROWS = 16 * RB;
-  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<FP8>, Smem<DS>> sm;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<wide_ring<FP8>()>, Smem<DS>> sm;
   __shared__ int s_red[4];
   __shared__ int s_last;
   __shared__ uint32_t s_arrived;
@@ -394,7 +394,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (!plan_partition<256>(pa, p, g, s_red, &s_last, total, t0, t1, b_first, b_last, start)) return;
 
   int qk_base[4], pv_base[8];
-  lds_bases(j, grp, qk_base, pv_base);
+  if constexpr (!WIDE) lds_bases(j, grp, qk_base, pv_base);
+  WideLanes wl;
+  if constexpr (WIDE) wl = wide_lanes(lane);
   const int dcol = 16 * (ds * ND) + 4 * grp;
   const bool lse_lane = grp == 0 && ds == 0;
   const int m = g * ROWS + rb * 16 + j;  // this lane's query row within a sequence
@@ -416,35 +418,32 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int slot = 2 * p + (lo == t0 ? 0 : 1);
     float *sb = pa.slots + slot * slot_floats;
     if constexpr (WIDE) {
-      int64_t qrow[2];
-      int mq[2], hq[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        mq[q] = g * ROWS + (wave + 4 * q) * 16 + j;
-        hq[q] = mq[q] % a.H;
-        qrow[q] = (int64_t)(b * a.qps + mq[q] / a.H) * a.H + hq[q];
-      }
-      constexpr int KQ = wide_qreg<FP8>();
-      bf16x8 qreg[2][KQ];  // loaded by attend_range_wide
-      WideState<2> w;
+      // wave w owns query rows 32w .. 32w+31 of the group: the consecutive
+      // rows qbase .. qbase + 31 of the queries; this lane's row is
+      // qbase + lane % 32 (query row mq of sequence b)
+      const int mq0 = g * ROWS + 32 * wave;
+      const int64_t qbase = (int64_t)b * a.M + mq0;
+      const int64_t qrow = qbase + (lane & 31);
+      const int hq = (int)(qrow % a.H);
+      bf16x8 qreg[wide_qreg<wide_ring<FP8>()>()];  // loaded by attend_range_wide
+      WideState w;
       WideDma dm = {nullptr, nullptr};
-      if constexpr (FP8) {
+      if constexpr (WIDE && wide_ring<FP8>()) {
         __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kRawSlots * kRawSlot];
         __shared__ __attribute__((aligned(16))) int32_t s_ibuf[2 * kIdxBlock];
         dm = WideDma{(uint8_t SMD_LDS *)s_raw, (int32_t SMD_LDS *)s_ibuf};
       }
-      attend_range_wide<2, FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, grp, qrow,
-                                               qreg, qk_base, pv_base, w);
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const float l_tot = row_total(w.l_run[q]);
-        if (fp == lp)
-          write_direct_wide(w, q, l_tot, a.sink ? a.sink[hq[q]] : -INFINITY, a.out + qrow[q] * kDim + 4 * grp,
-                            (a.lse != nullptr && grp == 0) ? a.lse + qrow[q] : nullptr);
-        else
-          write_partial_wide(w, q, l_tot, sb + (size_t)mq[q] * kDim + 4 * grp,
-                             grp == 0 ? sb + (size_t)a.M * kDim + mq[q] : nullptr);
-      }
+      attend_range_wide<FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, qbase, qreg,
+                                            wl, w);
+      const float l_tot = half_sum(w.l_run);
+      const bool lse_lane = lane < 32;
+      uint8_t SMD_LDS *stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
+      if (fp == lp)
+        write_direct_wide(w, l_tot, a.sink ? a.sink[hq] : -INFINITY, a.out + qbase * kDim, kDim,
+                          (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr, stage, lane);
+      else
+        write_partial_wide(w, l_tot, sb + (size_t)mq0 * kDim, kDim,
+                           lse_lane ? sb + (size_t)a.M * kDim + mq0 + (lane & 31) : nullptr, stage, lane);
     } else {
       const int64_t qrow = (int64_t)(b * a.qps + m / a.H) * a.H + head;
       bf16x8 qreg[NC];

@@ -1,7 +1,8 @@
 // Host split planner (aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and
-// persistent decode kernel", Summary part 1): the split count minimises
-// workgroup waves x per-wave KV time plus the partial-write / merge cost of
-// splitting, from the call's sizes only.  The per-wave time is that of this
+// persistent decode kernel", Summary part 1): the split count is chosen from
+// the call's sizes alone by minimising a modelled time, the rounds of decode
+// workgroups times one workgroup's time plus what each extra split adds in
+// partial traffic and merge work.  The per-wave time is that of this
 // library's decode workgroup: a fixed part plus one step per 16 positions of
 // each wave's share, a step costing more the fuller the GPU.  The caps follow the vLLM page
 // "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on gfx950", Design:
@@ -126,7 +127,7 @@ extern "C" int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t spli
 }
 
 extern "C" size_t smd_partials_bytes(int32_t num_tokens, int32_t num_heads, int32_t num_splits) {
-  if (num_tokens < 0 || num_heads < 0 || num_splits < 1 || num_splits > SMD_MAX_SPLITS) {
+  if (num_tokens < 0 || num_heads < 0 || num_splits < 1 || num_splits > SMD_MAX_MERGE_SPLITS) {
     smd::set_error("smd_partials_bytes: num_tokens=%d num_heads=%d num_splits=%d out of range", num_tokens,
                    num_heads, num_splits);
     return 0;

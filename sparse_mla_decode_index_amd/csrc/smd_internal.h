@@ -58,6 +58,10 @@ struct DecodeArgs {
 // (the dim-split kernel, M a multiple of 32) it is 32 rows (a.G = M / 32).
 hipError_t launch_decode(const DecodeArgs &a, bool fp8, bool pairs, hipStream_t stream);
 
+// Launch the split-KV decode on the wide waves: one workgroup per (index row,
+// split, group of 128 query rows); a.G = M / 128, one source only.
+hipError_t launch_decode_wide(const DecodeArgs &a, bool fp8, hipStream_t stream);
+
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
                         hipStream_t stream);

@@ -1,21 +1,42 @@
-// Wide waves for the persistent sparse MLA decode (gfx950): each of a
-// workgroup's 4 waves owns NQ = 2 blocks of 16 query rows and all 512 dims,
-// so one gathered 32-row tile serves 128 query rows and every K fragment and
-// every transposed V fragment read from LDS feeds two MFMAs.  The O
-// accumulators fill all 256 AGPRs; Q^T k-steps below KQ sit in VGPRs and the
-// rest in LDS (each wave reads only its own region).
+// Wide waves of the sparse MLA decode (gfx950): each of a workgroup's 4 waves
+// owns 32 query rows and all 512 dims, so one gathered 32-row KV tile serves
+// 128 query rows.  Both contractions run on v_mfma_f32_32x32x16_bf16, the
+// bf16 shape that issues at the highest rate on gfx950 with one wave per SIMD
+// (about 2.4x the rate of 16x16x32 in a back-to-back measurement).
 //
-// The row gather is the long pole (a random row's latency under load), so its
-// depth matters most.  Two walks over a range's tiles:
-//   - bf16 pools: rows staged through one VGPR set, the rows of tile t+1 in
-//     flight while tile t is computed (a second set would spill);
+// Per 32-row tile and wave:
+//   QK       S^T[32 kv x 32 q] = K[32 x 512] . Q^T[512 x 32]: 32 k-steps of 16
+//            dims.  Lane l holds
+//            query row q = l mod 32 and the 16 kv rows 8b + 4u + i (b, i in
+//            0..3, u = l / 32); its partner lane l ^ 32 holds the other 16.
+//   softmax  a reference max per query row fixed at its first valid tile
+//            (exp2 domain); a score more than 2^32 above it sends the
+//            workgroup through an exact-max second pass (common.h), so the
+//            accumulators are never rescaled.  Row max and sum need one
+//            permlane32 swap.
+//   PV       O^T[512 x 32 q] += V^T[512 x 32 kv] . P^T[32 kv x 32 q]: for each
+//            block of 32 dims, two MFMAs over kv rows 0..15 and 16..31.  The
+//            score registers are the B operand as they come out of QK (bf16),
+//            with the contraction index k = 8u + e of MFMA h standing for kv
+//            row 16h + 8(e / 4) + 4u + e mod 4; the V^T operand is read from
+//            LDS in the same order by two ds_read_b64_tr_b16 of 4 rows each.
+// The 16 O^T blocks of 32 x 32 fp32 fill all 256 AGPRs.  Q^T k-steps below KQ
+// sit in VGPRs, the rest in the wave's own LDS region.
+//
+// The tile is row-major, 1 KiB per row, with the 16-byte chunks of row r
+// permuted by an XOR of swz32(r): the QK reads (one chunk column of rows
+// 0..15 per 16 lanes) and the transposed reads (rows 4k..4k+3 x 64 bytes per
+// 32 lanes) touch distinct banks.
+//
+// Two walks over a range's tiles:
+//   - bf16 pools: rows staged through one VGPR set, software-pipelined: the
+//     rows of tile t+1 are stored to the second bf16 tile between the QK
+//     MFMAs of tile t and the loads of tile t+2 go out right after them;
 //   - fp8 pools: direct-to-LDS loads (global_load_lds) fill a ring of three
 //     raw tiles with no VGPRs held, so tiles t+1..t+3 are in flight while t is
 //     computed; each wave dequantises its own rows of the next raw tile into
 //     the shared bf16 tile (e4m3 x 2^(code-127), exact in bf16).  The index
 //     blocks arrive the same way, so no vector load's wait drains the ring.
-// Softmax and PASS semantics are those of decode_core.h (a reference max per
-// row fixed at its first valid tile, exact-max redo on overflow).
 #pragma once
 
 #include "decode_core.h"
@@ -24,40 +45,42 @@
 
 namespace smd {
 
-#ifndef SMD_WIDE_KPRE
-#define SMD_WIDE_KPRE 2
-#endif
-#ifndef SMD_WIDE_KPV
-#define SMD_WIDE_KPV 8
-#endif
+// The lane id from an opaque asm: offsets derived from it are recomputed
+// where they are used instead of being hoisted out of the sequence loop (and
+// spilled, each use then waiting for a scratch reload).
+__device__ __forceinline__ int opaque_lane() {
+  int lane;
+  asm volatile(
+      "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
+      "v_mbcnt_hi_u32_b32 %0, -1, %0"
+      : "=v"(lane));
+  return lane;
+}
 
-constexpr int kWideNQ = 2;
-constexpr int kQRegStaged = 6;  // Q^T k-steps in VGPRs next to a staged row set
-#ifndef SMD_WIDE_QREG_DMA
-#define SMD_WIDE_QREG_DMA 9
-#endif
-#ifndef SMD_WIDE_RAW_SLOTS
-#define SMD_WIDE_RAW_SLOTS 3
-#endif
-constexpr int kQRegDma = SMD_WIDE_QREG_DMA;  // ... when the gather holds no VGPRs
+constexpr int kWideRows = 128;     // query rows per workgroup (4 waves x 32)
+constexpr int kQRegStaged = 12;    // Q^T k-steps (16 dims) in VGPRs next to a staged row set
+constexpr int kQRegDma = 18;       // ... when the gather holds no VGPRs
+constexpr int kQkPre = 3;          // QK: LDS reads in flight ahead of their MFMA
+constexpr int kPvPre = 4;          // PV: V^T operands in flight ahead of their MFMA
 
 // Raw fp8 rows of one tile as the direct-to-LDS loads leave them, per wave
 // (rows 8w..8w+7 of the tile): NoPE [8][32][16 B] at 0 (chunks 28..31 of a
 // row are padding), RoPE [8][8][16 B] at 4096, UE8M0 codes [8][8 B] at 5120
-// (then 192 bytes of padding).
+// (then padding, so that the three slots also hold four 16 KiB staging
+// slices).
 constexpr int kRawNope = 0, kRawRope = 4096, kRawCode = 5120;
-constexpr int kRawWave = 5120 + 256;
+constexpr int kRawWave = 5120 + 384;
 constexpr int kRawSlot = 4 * kRawWave;
-constexpr int kRawSlots = SMD_WIDE_RAW_SLOTS;
+constexpr int kRawSlots = 3;
 
 template <bool FP8>
 struct SmemWide;
 
 template <>
 struct SmemWide<false> {
-  uint8_t tile[2][kTileBytes];                      // double-buffered bf16 tiles
-  int32_t ibuf[2][kIdxBlock];                       // index blocks
-  uint8_t qs[4][kWideNQ][16 - kQRegStaged][64 * 16];  // [wave][block][k-step - KQ][lane]
+  uint8_t tile[2][kTileBytes];                  // double-buffered bf16 tiles
+  int32_t ibuf[2][kIdxBlock];                   // index blocks
+  uint8_t qs[4][32 - kQRegStaged][64 * 16];     // [wave][k-step - KQ][lane]
 };
 
 // The direct-to-LDS targets (the raw ring and the index blocks) are separate
@@ -67,8 +90,8 @@ struct SmemWide<false> {
 // the MFMA path reads lives in this other object.
 template <>
 struct SmemWide<true> {
-  uint8_t tile[1][kTileBytes];                      // the bf16 tile being computed
-  uint8_t qs[4][kWideNQ][16 - kQRegDma][64 * 16];
+  uint8_t tile[1][kTileBytes];                  // the bf16 tile being computed
+  uint8_t qs[4][32 - kQRegDma][64 * 16];
 };
 
 struct WideDma {
@@ -76,157 +99,210 @@ struct WideDma {
   int32_t SMD_LDS *ibuf;  // [2][kIdxBlock]: index blocks
 };
 
+// fp8 pools walk on the direct-to-LDS ring, bf16 pools on the staged walk.
+// (The staged walk also takes fp8 rows; on the ragged MTP4 fp8 workload it ran
+// 6% slower than the ring: 381 against 359 us.)
 template <bool FP8>
-constexpr int wide_qreg() {
-  return FP8 ? kQRegDma : kQRegStaged;
+constexpr bool wide_ring() {
+  return FP8;
 }
 
-template <int NQ>
+template <bool RING>
+constexpr int wide_qreg() {
+  return RING ? kQRegDma : kQRegStaged;
+}
+
+// Softmax state and O^T of a wide wave's 32 query rows.
 struct WideState {
-  f32x4 acc[NQ][32];  // acc[q][d][i] = sum_j 2^(x_j - m_ref[q]) V[j][16d + 4grp + i], block q
-  float m_ref[NQ];    // reference max per block (log2 domain), same in the four 16-lane groups
-  float l_run[NQ];    // this lane's share of sum_j 2^(x_j - m_ref[q])
-  bool overflow;      // some score exceeded its m_ref + kRefSlackLog2 (this lane)
+  f32x16 acc[16];  // acc[D][e] = sum_j 2^(x_j - m_ref) V[j][32D + 8(e/4) + 4u + e%4], query row q
+  float m_ref;     // reference max (log2 domain), the same in lanes l and l ^ 32
+  float l_run;     // this lane's share of sum_j 2^(x_j - m_ref)
+  bool overflow;   // some score exceeded m_ref + kRefSlackLog2 (this lane)
 };
 
-// QK, softmax weights and PV of one 32-row tile for a wide wave.  The two kv
-// halves of the tile (rows 0..15, 16..31) make the 32-deep contraction of the
-// PV MFMA: lane group grp supplies P of kv rows 4grp..4grp+3 and
-// 16+4grp..16+4grp+3, and the two transposed V reads give the same rows.
-// PASS as in compute_tile.
-template <int NQ, int KQ, int PASS, bool P_HILO>
-__device__ __forceinline__ void compute_tile_wide(const uint8_t SMD_LDS *tile, const bf16x8 (&qreg)[NQ][KQ],
-                                                  const uint8_t SMD_LDS *qs, const int (&qk_base)[4],
-                                                  const int (&pv_base)[8], uint32_t vbits, int lane, int grp,
-                                                  float scale_log2, WideState<NQ> &w) {
-  // ---- QK: S^T tiles of kv rows 0..15 / 16..31 for each block
-  constexpr int kPre = SMD_WIDE_KPRE;  // LDS reads in flight ahead of their MFMAs
-  f32x4 s[NQ][2];
+// Per-lane LDS byte offsets of the 32x32 operands in a tile:
+//   qk[m]: QK A operand of k-steps ks with ks mod 8 = m: row l mod 32, logical
+//          chunk 2m + l / 32 (k-step ks adds 256 * (ks / 8));
+//   pv[4a + dd]: transposed read of 4 rows for dim blocks D with D mod 4 = dd:
+//          lane 4t + q of 16-lane group G supplies row 8a + 4(G / 2) + t and
+//          dims 32D + 16(G mod 2) + 4q, so lane j of group G receives dim
+//          32D + 16(G mod 2) + j of those 4 rows (block D adds 256 * (D / 4),
+//          kv half h adds 16 rows).
+struct WideLanes {
+  int qk[8];
+  int pv[8];
+};
+
+__device__ __forceinline__ WideLanes wide_lanes(int lane) {
+  WideLanes L;
+  const int r = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) s[q][0] = s[q][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  bf16x8 k0[kPre], k1[kPre], ql[kPre][NQ];
-  auto qk_load = [&](int c) {
-    const uint8_t SMD_LDS *p = tile + qk_base[c & 3] + 256 * (c >> 2);
-    k0[c % kPre] = *(const bf16x8 SMD_LDS *)(p);
-    k1[c % kPre] = *(const bf16x8 SMD_LDS *)(p + 16 * kLdsRow);
-    if (c >= KQ) {
+  for (int m = 0; m < 8; ++m) L.qk[m] = r * kLdsRow + (((2 * m + u) ^ swz32(r)) << 4);
+  const int G = lane >> 4, t = (lane & 15) >> 2, q = lane & 3;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q)
-        ql[c % kPre][q] = *(const bf16x8 SMD_LDS *)(qs + ((q * (16 - KQ) + c - KQ) * 64 + lane) * 16);
+  for (int a = 0; a < 2; ++a) {
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+      const int row = 8 * a + 4 * (G >> 1) + t;  // swz32 of row + 16h equals swz32(row)
+      const int c = 4 * dd + 2 * (G & 1) + (q >> 1);
+      L.pv[4 * a + dd] = row * kLdsRow + ((c ^ swz32(row)) << 4) + 8 * (q & 1);
     }
+  }
+  return L;
+}
+
+// QK, softmax weights and PV of one 32-row tile for a wide wave.  PASS as in
+// decode_core.h: kPassMain fixes the reference max at the row's first valid
+// tile and flags overflows, kPassMax only finds the exact max, kPassFixed
+// accumulates against it.
+struct NoWork {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+// mid(i), i = 0 .. kMidSlots-1, runs between the QK MFMAs (after k-step
+// 4i + 1) and post(0) right after the last of them: work of the next tile
+// (its LDS stores, the loads of the one after) issued while the matrix core
+// is busy.  It must not touch `tile`.
+constexpr int kMidSlots = 8;
+
+template <int KQ, int PASS, bool P_HILO, class Mid = NoWork, class Post = NoWork>
+__device__ __forceinline__ void compute_tile_wide(const uint8_t SMD_LDS *tile, const bf16x8 (&qreg)[KQ],
+                                                  const uint8_t SMD_LDS *qs, const WideLanes &L, uint32_t vbits,
+                                                  int lane, float scale_log2, WideState &w, Mid mid = Mid(),
+                                                  Post post = Post()) {
+  // ---- QK (one accumulator chain: a second would push O out of the AGPRs)
+  f32x16 s;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[e] = 0.f;
+  bf16x8 ka[kQkPre], ql[kQkPre];
+  auto qk_load = [&](int ks) {
+    ka[ks % kQkPre] = *(const bf16x8 SMD_LDS *)(tile + L.qk[ks & 7] + 256 * (ks >> 3));
+    if (ks >= KQ) ql[ks % kQkPre] = *(const bf16x8 SMD_LDS *)(qs + ((ks - KQ) * 64 + lane) * 16);
   };
 #pragma unroll
-  for (int c = 0; c < kPre; ++c) qk_load(c);
+  for (int ks = 0; ks < kQkPre; ++ks) qk_load(ks);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) {
-    const bf16x8 a0 = k0[c % kPre], a1 = k1[c % kPre];
-    bf16x8 b[NQ];
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) b[q] = c < KQ ? qreg[q][c < KQ ? c : 0] : ql[c % kPre][q];
-    if (c + kPre < 16) qk_load(c + kPre);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      s[q][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0, b[q], s[q][0], 0, 0, 0);
-      s[q][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1, b[q], s[q][1], 0, 0, 0);
-    }
-    __builtin_amdgcn_sched_barrier(0);  // keep the reads kPre steps ahead of their MFMAs
+  for (int ks = 0; ks < 32; ++ks) {
+    const bf16x8 av = ka[ks % kQkPre];
+    const bf16x8 bv = ks < KQ ? qreg[ks < KQ ? ks : 0] : ql[ks % kQkPre];
+    if (ks + kQkPre < 32) qk_load(ks + kQkPre);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, s, 0, 0, 0);
+    if (ks % 4 == 1) mid(ks / 4);
+    __builtin_amdgcn_sched_barrier(0);  // keep the reads kQkPre steps ahead of their MFMAs
   }
+  post(0);
 
-  // ---- softmax weights per block; this lane holds kv rows 4grp+i and 16+4grp+i
-  bf16x8 pb[NQ], pl[NQ];
+  // ---- softmax weights: score e of this lane is kv row 8(e/4) + 4u + e%4.
+  // A tile whose 32 rows are all valid (wave-uniform) skips the masking; the
+  // max then comes from the raw scores (scale_log2 > 0 keeps the order).
+  float tmax;
+  const bool all_valid = vbits == 0xffffffffu && scale_log2 > 0.f;
+  if (all_valid) {
+    tmax = s[0];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
-    float x[8];
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+    tmax *= scale_log2;
+  } else {
+    const uint32_t vb = vbits >> (4 * (lane >> 5));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      x[i] = ((vbits >> (4 * grp + i)) & 1) ? s[q][0][i] * scale_log2 : -INFINITY;
-      x[4 + i] = ((vbits >> (16 + 4 * grp + i)) & 1) ? s[q][1][i] * scale_log2 : -INFINITY;
-    }
-    float tmax =
-        fmaxf(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])), fmaxf(fmaxf(x[4], x[5]), fmaxf(x[6], x[7])));
-    tmax = group_max(tmax);
-    if constexpr (PASS == kPassMax) {
-      w.m_ref[q] = fmaxf(w.m_ref[q], tmax);
-      continue;
-    }
-    if constexpr (PASS == kPassMain) {
-      if (w.m_ref[q] == -INFINITY) w.m_ref[q] = tmax;  // nothing accumulated yet for this row
-      w.overflow |= tmax > w.m_ref[q] + kRefSlackLog2;
-    }
-    const float m_use = (w.m_ref[q] == -INFINITY) ? 0.f : w.m_ref[q];
-    float psum = 0.f;
+    for (int e = 0; e < 16; ++e)
+      s[e] = ((vb >> (8 * (e >> 2) + (e & 3))) & 1) ? s[e] * scale_log2 : -INFINITY;
+    tmax = s[0];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const float p = exp2_fast(x[i] - m_use);
-      psum += p;
-      pb[q][i] = (__bf16)p;
-      if constexpr (P_HILO) pl[q][i] = (__bf16)(p - (float)pb[q][i]);
-    }
-    w.l_run[q] += psum;
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
   }
-  if constexpr (PASS == kPassMax) return;
+  tmax = half_max(tmax);
+  if constexpr (PASS == kPassMax) {
+    w.m_ref = fmaxf(w.m_ref, tmax);
+    return;
+  }
+  if constexpr (PASS == kPassMain) {
+    if (w.m_ref == -INFINITY) w.m_ref = tmax;  // nothing accumulated yet for this row
+    w.overflow |= tmax > w.m_ref + kRefSlackLog2;
+  }
+  const float m_use = (w.m_ref == -INFINITY) ? 0.f : w.m_ref;
+  // p = 2^(x - m_use) with x = s * scale_log2 (unmasked) or s (masked, already scaled)
+  const float mul = all_valid ? scale_log2 : 1.f;
+  float psum = 0.f;
+  bf16x8 pb[2], pl[2];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float p = exp2_fast(__builtin_fmaf(s[e], mul, -m_use));
+    psum += p;
+    pb[e >> 3][e & 7] = (__bf16)p;
+    // P_HILO: p = hi + lo with both parts bf16, so the PV product carries
+    // about 16 significant bits of p instead of 8 (FP32-partial precision).
+    if constexpr (P_HILO) pl[e >> 3][e & 7] = (__bf16)(p - (float)pb[e >> 3][e & 7]);
+  }
+  w.l_run += psum;
 
-  // ---- PV: O^T[16d.., m] += V^T . P^T, each V^T fragment shared by the NQ blocks
-  constexpr int kPv = SMD_WIDE_KPV;
-  bf16x4 vlo[kPv], vhi[kPv];
-  auto pv_load = [&](int d) {
-    const uint8_t SMD_LDS *p = tile + pv_base[d & 7] + 256 * (d >> 3);
-    vlo[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p));
-    vhi[d % kPv] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(p + 16 * kLdsRow));
+  // ---- PV: MFMA i = 16h + D covers dims 32D.. and kv rows 16h..16h+15
+  bf16x8 va[kPvPre];
+  auto pv_load = [&](int i) {
+    const int h = i >> 4, D = i & 15;
+    const uint8_t SMD_LDS *base = tile + 16 * kLdsRow * h + 256 * (D >> 2);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(base + L.pv[D & 3]));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(base + L.pv[4 + (D & 3)]));
+    va[i % kPvPre] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
   };
 #pragma unroll
-  for (int d = 0; d < kPv; ++d) pv_load(d);
+  for (int i = 0; i < kPvPre; ++i) pv_load(i);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    const bf16x8 av = __builtin_shufflevector(vlo[d % kPv], vhi[d % kPv], 0, 1, 2, 3, 4, 5, 6, 7);
-    if (d + kPv < 32) pv_load(d + kPv);
-#pragma unroll
-    for (int q = 0; q < NQ; ++q) {
-      w.acc[q][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pb[q], w.acc[q][d], 0, 0, 0);
-      if constexpr (P_HILO) w.acc[q][d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, pl[q], w.acc[q][d], 0, 0, 0);
-    }
+  for (int i = 0; i < 32; ++i) {
+    const bf16x8 av = va[i % kPvPre];
+    if (i + kPvPre < 32) pv_load(i + kPvPre);
+    const int h = i >> 4, D = i & 15;
+    w.acc[D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[h], w.acc[D], 0, 0, 0);
+    if constexpr (P_HILO) w.acc[D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pl[h], w.acc[D], 0, 0, 0);
     __builtin_amdgcn_sched_barrier(0);
   }
 }
 
-// Walk the range's tiles once with one staged register set (bf16 pools).
-// Step t: store the rows of tile t+1 (in flight since step t-1) to the free
-// LDS buffer, issue the loads of tile t+2, compute tile t, one barrier.
-// Indices come from the LDS index blocks as in run_split.
-template <int NQ, bool PACKED, bool P_HILO, int PASS>
+// Walk the range's tiles once with one staged register set (bf16 and fp8
+// pools), software-pipelined by one tile.  Step t computes tile t from its
+// LDS buffer; between its QK MFMAs the rows of tile t+1 (staged in registers
+// since step t-1) are stored -- fp8 rows dequantised on the way -- to the
+// other buffer, and right after the QK MFMAs the loads of tile t+2 are issued
+// into the freed registers, so the gather, the dequantisation and the stores
+// run while the matrix core is busy.  One barrier per step.  Indices come
+// from the LDS index blocks as in run_split.
+template <bool FP8, bool PACKED, bool P_HILO, int PASS>
 __device__ __forceinline__ void run_split_wide(const DecodeArgs &a, SmemWide<false> &sm, const int32_t *row_idx,
-                                               int p0, int p1, int wave, int lane, int grp,
-                                               const bf16x8 (&qreg)[NQ][kQRegStaged], const int (&qk_base)[4],
-                                               const int (&pv_base)[8], WideState<NQ> &w) {
+                                               int p0, int p1, int wave, int lane,
+                                               const bf16x8 (&qreg)[kQRegStaged], const WideLanes &L,
+                                               WideState &w) {
   const int ntiles = (p1 - p0 + kBK - 1) / kBK;
   if (ntiles <= 0) return;
   uint8_t SMD_LDS *tile0 = (uint8_t SMD_LDS *)&sm.tile[0][0];
   int32_t SMD_LDS *ib0 = (int32_t SMD_LDS *)&sm.ibuf[0][0];
-  const uint8_t SMD_LDS *qs = (const uint8_t SMD_LDS *)&sm.qs[wave][0][0][0];
+  const uint8_t SMD_LDS *qs = (const uint8_t SMD_LDS *)&sm.qs[wave][0][0];
   auto tidx = [&](int k) {
     return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
   };
-  Staged<false> sa;
+  Staged<FP8> sa;
   const uint8_t *zrow = g_zero_row;
-  const GatherLanes gl = make_gather_lanes(wave, lane);
+  const GatherLanes gl = make_gather_lanes<kLay32>(wave, lane);
   const int blk0 = load_idx_block(row_idx, p0, p1, 0);
   __syncthreads();  // the buffers may still be read by a previous pass
   ib0[threadIdx.x] = blk0;
   __syncthreads();
-  load_rows<false, PACKED>(a, zrow, gl, tidx(0), p0, p1, wave, lane, sa);
-  store_rows<false>(tile0, wave, lane, sa);
-  load_rows<false, PACKED>(a, zrow, gl, tidx(1), p0 + kBK, p1, wave, lane, sa);
+  load_rows<FP8, PACKED>(a, zrow, gl, tidx(0), p0, p1, wave, lane, sa);
+  store_rows<FP8, kLay32>(tile0, wave, lane, sa);
+  load_rows<FP8, PACKED>(a, zrow, gl, tidx(1), p0 + kBK, p1, wave, lane, sa);
   __syncthreads();
   uint32_t v_cur = tile_valid_bits(tidx(0), p0, p1, lane, a.num_rows32);
   for (int t = 0; t < ntiles; ++t) {
     const int nb = t / kTilesPerIdxBlock + 1;  // the next index block
     const int blk = load_idx_block(row_idx, p0, p1, nb);
-    store_rows<false>(tile0 + ((t + 1) & 1) * kTileBytes, wave, lane, sa);
-    load_rows<false, PACKED>(a, zrow, gl, tidx(t + 2), p0 + (t + 2) * kBK, p1, wave, lane, sa);
-    compute_tile_wide<NQ, kQRegStaged, PASS, P_HILO>(tile0 + (t & 1) * kTileBytes, qreg, qs, qk_base, pv_base,
-                                                     v_cur, lane, grp, a.scale_log2, w);
+    uint8_t SMD_LDS *next = tile0 + ((t + 1) & 1) * kTileBytes;
+    auto mid = [&](int i) {
+      if (i < kStorePieces<FP8>) store_row_piece<FP8, kLay32>(next, wave, lane, sa, i);
+    };
+    auto post = [&](int) { load_rows<FP8, PACKED>(a, zrow, gl, tidx(t + 2), p0 + (t + 2) * kBK, p1, wave, lane, sa); };
+    compute_tile_wide<kQRegStaged, PASS, P_HILO>(tile0 + (t & 1) * kTileBytes, qreg, qs, L, v_cur, lane,
+                                                 a.scale_log2, w, mid, post);
     if (t % kTilesPerIdxBlock == kTilesPerIdxBlock - 3) ib0[(nb & 1) * kIdxBlock + threadIdx.x] = blk;
     __syncthreads();
     v_cur = tile_valid_bits(tidx(t + 1), p0 + (t + 1) * kBK, p1, lane, a.num_rows32);
@@ -338,11 +414,7 @@ __device__ __forceinline__ void raw_to_staged(const uint8_t SMD_LDS *src, Staged
   // The lane id comes from an opaque asm so that the lane offsets below are
   // recomputed in the loop rather than hoisted: hoisted, they get spilled,
   // and the wait for their reload would land in the loop and drain the ring.
-  int lane;
-  asm volatile(
-      "v_mbcnt_lo_u32_b32 %0, -1, 0\n\t"
-      "v_mbcnt_hi_u32_b32 %0, -1, %0"
-      : "=v"(lane));
+  const int lane = opaque_lane();
   const int c = min(lane & 31, 27);
   const uint32_t a1 = (uint32_t)(uintptr_t)(src + kRawNope + ((lane >> 5) * 32 + c) * 16);
   const uint32_t a2 = (uint32_t)(uintptr_t)(src + kRawCode + (lane >> 5) * 8 + (c >> 2));
@@ -389,35 +461,71 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-// Q^T of block q of a wide wave (query row qrow[q]) as QK B operands: k-steps
-// below KQ into VGPRs, the rest into the wave's LDS region (only this wave
-// reads it, after its own stores).
-template <int NQ, int KQ>
-__device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (&qrow)[NQ], int lane, int grp,
-                                            uint8_t SMD_LDS *qs, bf16x8 (&qreg)[NQ][KQ]) {
-  // Every load is issued before the first LDS store: interleaved, each store
-  // would wait for its own load and the k-steps would arrive one latency at
-  // a time.
-  bf16x8 tmp[NQ][16 - KQ];
+// LDS staging slice of one wave (32 rows x 512 bytes) for the coalesced Q^T
+// loads and output stores: byte c*16 .. c*16+15 of row q sits at chunk
+// (c ^ q) mod 32 of the row, so the row-wise 16-byte accesses (one or two
+// rows per instruction) and the fragment-wise ones (32 rows, one chunk
+// column) both touch distinct banks.
+constexpr int kStageRow = 512;
+constexpr int kStageWave = 32 * kStageRow;  // 16 KiB
+__device__ __forceinline__ int stage_off(int q, int c) { return q * kStageRow + (((c ^ q) & 31) << 4); }
+
+// The staging slice of wave `wave`: a quarter of the double-buffered bf16
+// tiles (bf16 pools) or of the raw ring (fp8 pools), both idle between a
+// range's walk and the next one.
+template <bool RING>
+__device__ __forceinline__ uint8_t SMD_LDS *wide_stage(SmemWide<RING> &sm, const WideDma &dm, int wave) {
+  if constexpr (RING) {
+    static_assert(kRawSlots * kRawSlot >= 4 * kStageWave, "staging slices fit the raw ring");
+    return dm.raw + wave * kStageWave;
+  } else {
+    static_assert(sizeof(sm.tile) >= 4 * kStageWave, "staging slices fit the tiles");
+    return (uint8_t SMD_LDS *)&sm.tile[0][0] + wave * kStageWave;
+  }
+}
+
+// Q^T of the wave's 32 query rows as QK B operands (k-step ks of lane l holds
+// dims 16ks + 8(l / 32) .. +8 of row qbase + l mod 32); k-steps below KQ go to
+// VGPRs, the rest to the wave's qs region.  The wave's rows are consecutive
+// rows qbase .. qbase + 31 of q_nope / q_rope, so they are read row-wise (two
+// rows of 512 bytes per load instruction) into the staging slice in two
+// halves of 256 dims, then picked up fragment-wise.  The caller has made the
+// slice free (a barrier after the last use of the tiles or the ring).
+template <int KQ>
+__device__ __forceinline__ void load_q_wide(const DecodeArgs &a, int64_t qbase, int, uint8_t SMD_LDS *stage,
+                                            uint8_t SMD_LDS *qs, bf16x8 (&qreg)[KQ]) {
+  const int lane = opaque_lane();
+  const int c = lane & 31, hr = lane >> 5;
+  // both halves' loads go out before the first LDS store: one round trip
+  u32x4 v[2][16];
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int c = 0; c < 16; ++c) {
-      const uint16_t *src = (c < 14) ? a.q_nope + qrow[q] * kNope + 32 * c + 8 * grp
-                                     : a.q_rope + qrow[q] * kRope + 32 * (c - 14) + 8 * grp;
-      const bf16x8 v = *(const bf16x8 *)src;
-      if (c < KQ)
-        qreg[q][c < KQ ? c : 0] = v;
+    for (int k = 0; k < 16; ++k) {  // rows 2k + hr, 16-byte chunk c of this half
+      const int64_t row = qbase + 2 * k + hr;
+      const uint16_t *src;
+      if (half == 0)
+        src = a.q_nope + row * kNope + 8 * c;
       else
-        tmp[q][c < KQ ? 0 : c - KQ] = v;
+        src = c < 24 ? a.q_nope + row * kNope + 256 + 8 * c : a.q_rope + row * kRope + 8 * (c - 24);
+      v[half][k] = *(const u32x4 *)src;
     }
   }
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int q = 0; q < NQ; ++q) {
+  for (int half = 0; half < 2; ++half) {
 #pragma unroll
-    for (int c = KQ; c < 16; ++c)
-      *(bf16x8 SMD_LDS *)(qs + ((q * (16 - KQ) + c - KQ) * 64 + lane) * 16) = tmp[q][c - KQ];
+    for (int k = 0; k < 16; ++k) *(u32x4 SMD_LDS *)(stage + stage_off(2 * k + hr, c)) = v[half][k];
+    // fragments: k-step ks = 16 half + j reads chunk 2j + hr of row c
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const int ks = 16 * half + j;
+      const bf16x8 f = *(const bf16x8 SMD_LDS *)(stage + stage_off(c, 2 * j + hr));
+      if (ks < KQ)
+        qreg[ks < KQ ? ks : 0] = f;
+      else
+        *(bf16x8 SMD_LDS *)(qs + ((ks - KQ) * 64 + lane) * 16) = f;
+    }
   }
 }
 
@@ -435,18 +543,17 @@ __device__ __forceinline__ void load_q_wide(const DecodeArgs &a, const int64_t (
 // landed by the wait of step 8k - 4 (four tiles' loads later) and barrier A
 // of that step publishes it.  The block it replaces was last read at step
 // 8(k-1) - 1.
-template <int NQ, bool P_HILO, int PASS>
+template <bool P_HILO, int PASS>
 __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide<true> &sm, const WideDma &dm,
                                                    const int32_t *row_idx, int p0, int p1, int wave, int lane,
-                                                   int grp, const bf16x8 (&qreg)[NQ][kQRegDma],
-                                                   const int (&qk_base)[4], const int (&pv_base)[8],
-                                                   WideState<NQ> &w) {
+                                                   const bf16x8 (&qreg)[kQRegDma], const WideLanes &L,
+                                                   WideState &w) {
   const int ntiles = (p1 - p0 + kBK - 1) / kBK;
   if (ntiles <= 0) return;
   uint8_t SMD_LDS *tile = (uint8_t SMD_LDS *)&sm.tile[0][0];
   uint8_t SMD_LDS *raw = dm.raw;
   int32_t SMD_LDS *ib0 = dm.ibuf;
-  const uint8_t SMD_LDS *qs = (const uint8_t SMD_LDS *)&sm.qs[wave][0][0][0];
+  const uint8_t SMD_LDS *qs = (const uint8_t SMD_LDS *)&sm.qs[wave][0][0];
   auto tidx = [&](int k) {
     return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
   };
@@ -475,49 +582,47 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
       const int nb = t / kTilesPerIdxBlock + 1;
       dma_idx_block(row_idx, p0, p1, nb, wave, lane, ib0 + (nb & 1) * kIdxBlock);
     }
-    store_rows<true>(tile, wave, lane, st);
+    store_rows<true, kLay32>(tile, wave, lane, st);
     barrier_lds();  // B
-    compute_tile_wide<NQ, kQRegDma, PASS, P_HILO>(tile, qreg, qs, qk_base, pv_base, v_cur, lane, grp,
-                                                  a.scale_log2, w);
+    compute_tile_wide<kQRegDma, PASS, P_HILO>(tile, qreg, qs, L, v_cur, lane, a.scale_log2, w);
   }
   wait_vm<0>();  // no load may land in LDS after the walk
 }
 
-// Attend the wide wave's query rows over positions [p0, p1) of row_idx: the
-// main pass, and the exact-max two-pass redo when some score overflowed its
-// reference max anywhere in the workgroup.
-template <int NQ, bool FP8, bool PACKED, bool P_HILO>
-__device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<FP8> &sm, const WideDma &dm,
-                                                  const int32_t *row_idx,
-                                                  int p0, int p1, int wave, int lane, int grp,
-                                                  const int64_t (&qrow)[NQ], bf16x8 (&qreg)[NQ][wide_qreg<FP8>()],
-                                                  const int (&qk_base)[4], const int (&pv_base)[8],
-                                                  WideState<NQ> &w) {
+// Attend the wide wave's 32 query rows (rows qbase .. qbase + 31 of the
+// queries; this lane's row is qbase + lane % 32) over positions [p0, p1) of
+// row_idx: the main pass, and the exact-max two-pass redo when some score
+// overflowed its reference max anywhere in the workgroup.  Ends with a
+// barrier, so the tiles and the ring are free for the epilogue's staging.
+template <bool FP8, bool PACKED, bool P_HILO, bool RING = wide_ring<FP8>()>
+__device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<RING> &sm, const WideDma &dm,
+                                                  const int32_t *row_idx, int p0, int p1, int wave, int lane,
+                                                  int64_t qbase, bf16x8 (&qreg)[wide_qreg<RING>()],
+                                                  const WideLanes &L, WideState &w) {
   auto reset = [&]() {
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int d = 0; d < 16; ++d) {
 #pragma unroll
-      for (int d = 0; d < 32; ++d) w.acc[q][d] = f32x4{0.f, 0.f, 0.f, 0.f};
-      w.m_ref[q] = -INFINITY;
-      w.l_run[q] = 0.f;
+      for (int e = 0; e < 16; ++e) w.acc[d][e] = 0.f;
     }
+    w.m_ref = -INFINITY;
+    w.l_run = 0.f;
   };
   auto walk = [&](auto pass) {
     constexpr int PASS = decltype(pass)::value;
-    if constexpr (FP8)
-      run_split_wide_dma<NQ, P_HILO, PASS>(a, sm, dm, row_idx, p0, p1, wave, lane, grp, qreg, qk_base, pv_base,
-                                           w);
+    if constexpr (RING)
+      run_split_wide_dma<P_HILO, PASS>(a, sm, dm, row_idx, p0, p1, wave, lane, qreg, L, w);
     else
-      run_split_wide<NQ, PACKED, P_HILO, PASS>(a, sm, row_idx, p0, p1, wave, lane, grp, qreg, qk_base, pv_base,
-                                               w);
+      run_split_wide<FP8, PACKED, P_HILO, PASS>(a, sm, row_idx, p0, p1, wave, lane, qreg, L, w);
   };
-  if constexpr (FP8) {
+  __syncthreads();  // the tiles, the ring and the index blocks may still be in use by a previous range
+  if constexpr (RING) {
     // The first index block of the main pass goes out ahead of the Q^T
     // loads: the two round trips overlap instead of following each other.
-    __syncthreads();  // the buffers may still be read by a previous piece
     if (p1 > p0) dma_idx_block(row_idx, p0, p1, 0, wave, lane, dm.ibuf);
   }
-  load_q_wide<NQ, wide_qreg<FP8>()>(a, qrow, lane, grp, (uint8_t SMD_LDS *)&sm.qs[wave][0][0][0], qreg);
+  load_q_wide<wide_qreg<RING>()>(a, qbase, lane, wide_stage<RING>(sm, dm, wave),
+                                 (uint8_t SMD_LDS *)&sm.qs[wave][0][0], qreg);
   reset();
   w.overflow = false;
   walk(std::integral_constant<int, kPassMain>{});
@@ -528,41 +633,74 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
   }
 }
 
-// Outputs of block q of a wide wave: bf16 with the sink folded in, or the
-// FP32 partial; dst points at dim 4*grp of the row.
-template <int NQ>
-__device__ __forceinline__ void write_direct_wide(const WideState<NQ> &w, int q, float l_tot, float sink_ln,
-                                                  uint16_t *dst, float *lse_dst) {
-  const float sink2 = sink_ln * kLog2e;
-  const float mf = fmaxf(w.m_ref[q], sink2);
-  float inv = 0.f, lse_v = -INFINITY;
-  if (mf != -INFINITY) {
-    const float e = exp2_fast(w.m_ref[q] - mf);
-    const float z = l_tot * e + exp2_fast(sink2 - mf);
-    inv = e / z;
-    lse_v = (mf + __log2f(z)) * kLn2;
-  }
-#pragma unroll
-  for (int d = 0; d < 32; ++d) {
-    u32x2 v;
-    v[0] = (uint32_t)f32_to_bf16_rne(w.acc[q][d][0] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[q][d][1] * inv) << 16);
-    v[1] = (uint32_t)f32_to_bf16_rne(w.acc[q][d][2] * inv) | ((uint32_t)f32_to_bf16_rne(w.acc[q][d][3] * inv) << 16);
-    *(u32x2 *)(dst + 16 * d) = v;
-  }
-  if (lse_dst != nullptr) *lse_dst = lse_v;
+// Outputs of a wide wave's 32 query rows, stored row-wise through the wave's
+// staging slice (the accumulators hold dims 32D + 8b + 4u .. +4 of row
+// lane % 32 in acc[D][4b .. 4b+3], u = lane / 32).  dst points at dim 0 of the
+// wave's first row; rows are row_stride elements apart.
+__device__ __forceinline__ f32x4 wide_quad(const f32x16 &v, int b) {
+  return f32x4{v[4 * b], v[4 * b + 1], v[4 * b + 2], v[4 * b + 3]};
 }
 
-template <int NQ>
-__device__ __forceinline__ void write_partial_wide(const WideState<NQ> &w, int q, float l_tot, float *dst,
-                                                   float *lse_dst) {
-  float inv = 0.f, lse_v = -INFINITY;
-  if (l_tot > 0.f) {
-    inv = 1.f / l_tot;
-    lse_v = (w.m_ref[q] + __log2f(l_tot)) * kLn2;
-  }
+// bf16 rows, two passes of 256 dims (512 bytes per row).
+__device__ __forceinline__ void store_rows_bf16(const WideState &w, float inv, uint16_t *dst, int64_t row_stride,
+                                                uint8_t SMD_LDS *stage, int) {
+  const int lane = opaque_lane();
+  const int q = lane & 31, u = lane >> 5;
 #pragma unroll
-  for (int d = 0; d < 32; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[q][d] * inv;
-  if (lse_dst != nullptr) *lse_dst = lse_v;
+  for (int pass = 0; pass < 2; ++pass) {
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)  // dims 32dd + 8b + 4u of the pass: chunk 4dd + b, half u
+        *(u32x2 SMD_LDS *)(stage + stage_off(q, 4 * dd + b) + 8 * u) = pack_bf16x4(wide_quad(w.acc[8 * pass + dd], b), inv);
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {  // rows 2k + u, chunk q
+      const int r = 2 * k + u;
+      const u32x4 v = *(const u32x4 SMD_LDS *)(stage + stage_off(r, q));
+      *(u32x4 *)(dst + r * row_stride + 256 * pass + 8 * q) = v;
+    }
+  }
+}
+
+// fp32 rows, four passes of 128 dims (512 bytes per row).
+__device__ __forceinline__ void store_rows_f32(const WideState &w, float inv, float *dst, int64_t row_stride,
+                                               uint8_t SMD_LDS *stage, int) {
+  const int lane = opaque_lane();
+  const int q = lane & 31, u = lane >> 5;
+#pragma unroll
+  for (int pass = 0; pass < 4; ++pass) {
+#pragma unroll
+    for (int dd = 0; dd < 4; ++dd) {
+#pragma unroll
+      for (int b = 0; b < 4; ++b)  // dims 32dd + 8b + 4u of the pass: chunk 8dd + 2b + u
+        *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * dd + 2 * b + u)) = wide_quad(w.acc[4 * pass + dd], b) * inv;
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const int r = 2 * k + u;
+      const f32x4 v = *(const f32x4 SMD_LDS *)(stage + stage_off(r, q));
+      *(f32x4 *)(dst + r * row_stride + 128 * pass + 4 * q) = v;
+    }
+  }
+}
+
+// bf16 output with the sink folded in; lse_dst (this lane's row) is written
+// when non-null.
+__device__ __forceinline__ void write_direct_wide(const WideState &w, float l_tot, float sink_ln, uint16_t *dst,
+                                                  int64_t row_stride, float *lse_dst, uint8_t SMD_LDS *stage,
+                                                  int lane) {
+  const OutScale sc = direct_scale(w.m_ref, l_tot, sink_ln);
+  store_rows_bf16(w, sc.inv, dst, row_stride, stage, lane);
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
+}
+
+// FP32 partial (no sink).
+__device__ __forceinline__ void write_partial_wide(const WideState &w, float l_tot, float *dst, int64_t row_stride,
+                                                   float *lse_dst, uint8_t SMD_LDS *stage, int lane) {
+  const OutScale sc = partial_scale(w.m_ref, l_tot);
+  store_rows_f32(w, sc.inv, dst, row_stride, stage, lane);
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
 }  // namespace smd

@@ -279,7 +279,10 @@ def test_partials_bytes():
     assert smd.partials_bytes(1, 128, 32) == 128 * 32 * 2052
     assert smd.partials_bytes(0, 16, 1) == 0
     assert smd.partials_bytes(2, 16, 0) == 0 and "num_splits" in smd.lib().smd_last_error().decode()
-    assert smd.partials_bytes(2, 16, 33) == 0
+    # the merge's range: up to SMD_MAX_MERGE_SPLITS pieces
+    assert smd.partials_bytes(2, 16, 33) == 2 * 16 * 33 * 2052
+    assert smd.partials_bytes(1, 16, smd.MAX_MERGE_SPLITS) == 16 * smd.MAX_MERGE_SPLITS * 2052
+    assert smd.partials_bytes(1, 16, smd.MAX_MERGE_SPLITS + 1) == 0
 
 
 # ----------------------------------------------------------------------------

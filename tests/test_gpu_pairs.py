@@ -2,13 +2,12 @@
 
 The library picks that kernel when the query rows per index row are a multiple
 of 32 and its grid of 32-row blocks fills whole rounds of the GPU (the rule in
-the header); SMD_DECODE_PAIRS=1 forces it
-for smaller problems (0 forces the 16-row kernel), so the cases below run it on
-sizes the oracle finishes quickly.  The same bars as the other parity tests:
+the header); the cases below name it explicitly (kernel="pairs", the C ABI's
+smd_decode_options) so that it runs on sizes the oracle finishes quickly.  The same bars as the other parity tests:
 bf16 out atol = rtol = 2e-2, FP32 partials and LSE 1e-3, the one-hot gather
 probe exact.
 """
-import os
+import functools
 
 import numpy as np
 import pytest
@@ -22,15 +21,8 @@ from tests.helpers import bf16_tensor, check_lse, check_out, check_partials, dev
 pytestmark = pytest.mark.gpu
 
 
-@pytest.fixture
-def pairs():
-    old = os.environ.get("SMD_DECODE_PAIRS")
-    os.environ["SMD_DECODE_PAIRS"] = "1"
-    yield
-    if old is None:
-        del os.environ["SMD_DECODE_PAIRS"]
-    else:
-        os.environ["SMD_DECODE_PAIRS"] = old
+# every call below names the dim-split kernel
+_dec = functools.partial(smd.sparse_mla_decode, kernel="pairs")
 
 
 def _run(w, gpu, s, partials=False, sink=True):
@@ -39,14 +31,14 @@ def _run(w, gpu, s, partials=False, sink=True):
     a = w.arrays
     print(f"pairs {w.name} s={s} partials={partials} sink={sink}", flush=True)
     if partials:
-        po, pl = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, None, w.softmax_scale, num_splits=s,
+        po, pl = _dec(q_nope, q_rope, pool, idx, None, w.softmax_scale, num_splits=s,
                                        q_per_seq=w.q_per_seq, partials_only=True)
         torch.cuda.synchronize()
         po_ref, pl_ref = ref.sparse_mla_decode_partials(a["q_nope"], a["q_rope"], oracle_pool(w), a["indices"],
                                                         w.softmax_scale, s, w.q_per_seq)
         check_partials(po, pl, po_ref, pl_ref)
         return
-    out, lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sk if sink else None, w.softmax_scale,
+    out, lse = _dec(q_nope, q_rope, pool, idx, sk if sink else None, w.softmax_scale,
                                      num_splits=s, q_per_seq=w.q_per_seq)
     torch.cuda.synchronize()
     o_ref, l_ref = ref.sparse_mla_decode(a["q_nope"], a["q_rope"], oracle_pool(w), a["indices"],
@@ -56,21 +48,21 @@ def _run(w, gpu, s, partials=False, sink=True):
 
 
 @pytest.mark.parametrize("H,s", [(32, 1), (32, 3), (64, 2), (128, 1), (128, 5)])
-def test_pairs_bf16_ragged_tail(gpu, pairs, H, s):
+def test_pairs_bf16_ragged_tail(gpu, H, s):
     w = wl.dense_workload("pairs bf16", T=3, H=H, kv_dtype="bf16", pool_rows=4096, topk=650, swa=37, invalid=9,
                           seed=211 + H + s)
     _run(w, gpu, s)
 
 
 @pytest.mark.parametrize("H,s", [(64, 1), (128, 2), (128, 7)])
-def test_pairs_fp8_ragged_tail(gpu, pairs, H, s):
+def test_pairs_fp8_ragged_tail(gpu, H, s):
     w = wl.dense_workload("pairs fp8", T=2, H=H, kv_dtype="fp8", pool_rows=4096, topk=700, invalid=4,
                           seed=231 + H + s)
     _run(w, gpu, s)
 
 
 @pytest.mark.parametrize("kv_dtype", ["bf16", "fp8"])
-def test_pairs_partials(gpu, pairs, kv_dtype):
+def test_pairs_partials(gpu, kv_dtype):
     """FP32 partials (two-part P) and an empty trailing split (K=300, s=6)."""
     w = wl.dense_workload("pairs partials", T=2, H=64, kv_dtype=kv_dtype, pool_rows=2048, topk=300, invalid=3,
                           seed=241)
@@ -78,13 +70,13 @@ def test_pairs_partials(gpu, pairs, kv_dtype):
 
 
 @pytest.mark.parametrize("qps", [2, 4])
-def test_pairs_mtp_shared_rows(gpu, pairs, qps):
+def test_pairs_mtp_shared_rows(gpu, qps):
     w = wl.dense_workload("pairs mtp", T=2 * qps, H=32, kv_dtype="bf16", pool_rows=2048, topk=300, invalid=3,
                           q_per_seq=qps, seed=251 + qps)
     _run(w, gpu, 2)
 
 
-def test_pairs_no_sink_and_invalid_rows(gpu, pairs):
+def test_pairs_no_sink_and_invalid_rows(gpu):
     w = wl.dense_workload("pairs invalid", T=3, H=32, kv_dtype="bf16", pool_rows=1024, topk=130, seed=261)
     a = w.arrays
     a["indices"][0, :] = -1
@@ -94,7 +86,7 @@ def test_pairs_no_sink_and_invalid_rows(gpu, pairs):
         _run(w, gpu, 2, sink=sink)
 
 
-def test_pairs_nan_in_unreferenced_rows(gpu, pairs):
+def test_pairs_nan_in_unreferenced_rows(gpu):
     w = wl.dense_workload("pairs nan pool", T=2, H=64, kv_dtype="fp8", pool_rows=2048, topk=333, invalid=7,
                           seed=271)
     a = w.arrays
@@ -106,7 +98,7 @@ def test_pairs_nan_in_unreferenced_rows(gpu, pairs):
     _run(w, gpu, 3)
 
 
-def test_pairs_split_layout_pool(gpu, pairs):
+def test_pairs_split_layout_pool(gpu):
     """bf16 NoPE / RoPE in separate arrays: the RoPE dims come from their own
     array in the upper dims half."""
     w = wl.dense_workload("pairs split layout", T=2, H=32, kv_dtype="bf16", pool_rows=3000, topk=410, invalid=4,
@@ -123,14 +115,14 @@ def test_pairs_split_layout_pool(gpu, pairs):
                                          w.arrays["indices"], w.arrays["sink"], w.softmax_scale)
     for s in (1, 3):
         print(f"pairs split layout s={s}", flush=True)
-        out, lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s)
+        out, lse = _dec(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s)
         torch.cuda.synchronize()
         check_out(out, o_ref)
         check_lse(lse, l_ref)
 
 
 @pytest.mark.parametrize("K,s", [(64, 1), (777, 4), (1500, 7)])
-def test_pairs_one_hot_gather_probe(gpu, pairs, K, s):
+def test_pairs_one_hot_gather_probe(gpu, K, s):
     """q = 0 and pool row r = e_r: each split's partial recovers the exact
     multiset of its valid indices (both dims halves: r < 256 and r >= 256)."""
     n, T, H = 512, 2, 32
@@ -142,7 +134,7 @@ def test_pairs_one_hot_gather_probe(gpu, pairs, K, s):
     q_nope = torch.zeros((T, H, 448), dtype=torch.bfloat16, device=gpu)
     q_rope = torch.zeros((T, H, 64), dtype=torch.bfloat16, device=gpu)
     print(f"pairs one-hot K={K} s={s}", flush=True)
-    po, pl = smd.sparse_mla_decode(q_nope, q_rope, pool, torch.from_numpy(idx).to(gpu), None, 0.0442,
+    po, pl = _dec(q_nope, q_rope, pool, torch.from_numpy(idx).to(gpu), None, 0.0442,
                                    num_splits=s, partials_only=True)
     torch.cuda.synchronize()
     po = po.cpu().numpy().astype(np.float64)
@@ -161,7 +153,7 @@ def test_pairs_one_hot_gather_probe(gpu, pairs, K, s):
             assert np.array_equal(got, np.broadcast_to(want, got.shape)), (t, r)
 
 
-def test_pairs_graph_replay(gpu, pairs):
+def test_pairs_graph_replay(gpu):
     w = wl.dense_workload("pairs graph", T=4, H=64, kv_dtype="bf16", pool_rows=4096, topk=900, invalid=5, seed=291)
     q_nope, q_rope, sink, pool = device_inputs(w, gpu)
     idx = torch.from_numpy(w.arrays["indices"]).to(gpu)
@@ -169,12 +161,12 @@ def test_pairs_graph_replay(gpu, pairs):
     lse = torch.empty((4, 64), dtype=torch.float32, device=gpu)
     po = torch.empty((4, 64, 3, 512), dtype=torch.float32, device=gpu)
     pl = torch.empty((4, 64, 3), dtype=torch.float32, device=gpu)
-    eager_out, eager_lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=3)
+    eager_out, eager_lse = _dec(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=3)
     stream = torch.cuda.Stream()
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=stream):
-        smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=3, out=out, lse=lse,
+        _dec(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=3, out=out, lse=lse,
                               partial_o=po, partial_lse=pl)
     torch.cuda.synchronize()
     for i in range(3):
@@ -190,26 +182,19 @@ def test_pairs_graph_replay(gpu, pairs):
 
 @pytest.mark.slow
 def test_pairs_selected_at_full_size(gpu):
-    """Without the switch: the fp8 workload of 32 tokens x 128 heads at 2 splits
+    """With the library's choice: the fp8 workload of 32 tokens x 128 heads at 2 splits
     (32 x 2 x 4 = 256 blocks of 32 rows) runs the dim-split kernel -- its
     output is bit-identical to the forced dim-split run -- and meets the
     oracle."""
     w = wl.config(2)
     q_nope, q_rope, sink, pool = device_inputs(w, gpu)
     idx = torch.from_numpy(w.arrays["indices"]).to(gpu)
-    old = os.environ.pop("SMD_DECODE_PAIRS", None)
-    try:
-        runs = {}
-        for mode in (None, "1"):
-            if mode is not None:
-                os.environ["SMD_DECODE_PAIRS"] = mode
-            print(f"pairs full size mode={mode}", flush=True)
-            runs[mode] = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=2)
-            torch.cuda.synchronize()
-    finally:
-        os.environ.pop("SMD_DECODE_PAIRS", None)
-        if old is not None:
-            os.environ["SMD_DECODE_PAIRS"] = old
+    runs = {}
+    for mode in (None, "1"):
+        print(f"pairs full size mode={mode}", flush=True)
+        dec = smd.sparse_mla_decode if mode is None else _dec
+        runs[mode] = dec(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=2)
+        torch.cuda.synchronize()
     assert torch.equal(runs[None][0].view(torch.int16), runs["1"][0].view(torch.int16))
     assert torch.equal(runs[None][1], runs["1"][1])
     a = w.arrays

@@ -9,7 +9,6 @@ property.  Outputs, lse and FP32 partials are compared with the float64
 oracle, on every kernel: the 16-row split-KV kernel, the dim-split pair kernel,
 and the persistent kernel's 16-, 64- and 128-row groups.
 """
-import os
 
 import numpy as np
 import pytest
@@ -37,24 +36,20 @@ def _assert_spread(w, idx_row, t=0):
     assert np.any(s[:, 16:].max(axis=1) - s[:, :16].max(axis=1) > 32.0), "inputs do not force the redo"
 
 
-@pytest.mark.parametrize("kv_dtype,H,pairs", [("bf16", 16, "0"), ("fp8", 64, "0"), ("fp8", 64, "1"),
-                                              ("bf16", 128, "1")])
+@pytest.mark.parametrize("kv_dtype,H,kernel", [("bf16", 16, "rows16"), ("fp8", 64, "rows16"), ("fp8", 64, "pairs"),
+                                               ("bf16", 128, "pairs"), ("bf16", 128, "wide"), ("fp8", 128, "wide")])
 @pytest.mark.parametrize("s", [1, 3])
-def test_split_kv_redo(gpu, kv_dtype, H, pairs, s):
+def test_split_kv_redo(gpu, kv_dtype, H, kernel, s):
     w = wl.dense_workload("redo split-kv", T=4, H=H, kv_dtype=kv_dtype, pool_rows=4096, topk=900, invalid=7,
                           seed=300 + H + s, softmax_scale=SCALE)
     _assert_spread(w, w.arrays["indices"][0][w.arrays["indices"][0] >= 0])
     q_nope, q_rope, sink, pool = device_inputs(w, gpu)
     idx = torch.from_numpy(w.arrays["indices"]).to(gpu)
-    os.environ["SMD_DECODE_PAIRS"] = pairs
-    try:
-        print(f"redo split-kv {kv_dtype} H={H} pairs={pairs} s={s}", flush=True)
-        out, lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s)
-        po, pl = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, None, w.softmax_scale, num_splits=s,
-                                       partials_only=True)
-        torch.cuda.synchronize()
-    finally:
-        del os.environ["SMD_DECODE_PAIRS"]
+    print(f"redo split-kv {kv_dtype} H={H} kernel={kernel} s={s}", flush=True)
+    out, lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s, kernel=kernel)
+    po, pl = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, None, w.softmax_scale, num_splits=s,
+                                   partials_only=True, kernel=kernel)
+    torch.cuda.synchronize()
     a = w.arrays
     o_ref, l_ref = ref.sparse_mla_decode(a["q_nope"], a["q_rope"], oracle_pool(w), a["indices"], a["sink"],
                                          w.softmax_scale)

@@ -5,8 +5,6 @@ and dim-split), per-source validity, one empty source, the one-hot gather
 probe, NaN in unreferenced rows, and the fp8 T=32 H=128 top-k 2048 + 128-row
 window workload at full size.  Bars: bf16 out atol = rtol = 2e-2, FP32
 partials and LSE 1e-3."""
-import os
-
 import numpy as np
 import pytest
 import torch
@@ -19,18 +17,16 @@ from tests.helpers import bf16_tensor, check_lse, check_out, check_partials
 pytestmark = pytest.mark.gpu
 
 
+# the kernel family of the calls below (None: the library's choice); set by
+# the `kernel` fixture for the tests that take it
+_KERNEL = {"name": None}
+
+
 @pytest.fixture(params=["auto", "pairs", "rows16"])
 def kernel(request):
-    old = os.environ.get("SMD_DECODE_PAIRS")
-    if request.param == "pairs":
-        os.environ["SMD_DECODE_PAIRS"] = "1"
-    elif request.param == "rows16":
-        os.environ["SMD_DECODE_PAIRS"] = "0"
+    _KERNEL["name"] = None if request.param == "auto" else request.param
     yield request.param
-    if old is None:
-        os.environ.pop("SMD_DECODE_PAIRS", None)
-    else:
-        os.environ["SMD_DECODE_PAIRS"] = old
+    _KERNEL["name"] = None
 
 
 def _dev_pool(p: dict, gpu) -> smd.KVPool:
@@ -51,9 +47,10 @@ def _check(w, gpu, s, partials=False, sink=True):
     a = w.arrays
     qn, qr, sk, mp, mi, sp, si = _inputs(w, gpu)
     print(f"two-source {w.name} s={s} partials={partials} sink={sink} "
-          f"pairs={os.environ.get('SMD_DECODE_PAIRS')}", flush=True)
+          f"kernel={_KERNEL['name']}", flush=True)
     if partials:
         po, pl = smd.sparse_mla_decode_two_source(qn, qr, mp, mi, sp, si, None, w.softmax_scale, num_splits=s,
+                                                  kernel=_KERNEL['name'],
                                                   q_per_seq=w.q_per_seq, partials_only=True)
         torch.cuda.synchronize()
         po_ref, pl_ref = ref.sparse_mla_decode_two_source_partials(
@@ -62,6 +59,7 @@ def _check(w, gpu, s, partials=False, sink=True):
         check_partials(po, pl, po_ref, pl_ref)
         return
     out, lse = smd.sparse_mla_decode_two_source(qn, qr, mp, mi, sp, si, sk if sink else None, w.softmax_scale,
+                                                kernel=_KERNEL['name'],
                                                 num_splits=s, q_per_seq=w.q_per_seq)
     torch.cuda.synchronize()
     o_ref, l_ref = ref.sparse_mla_decode_two_source(a["q_nope"], a["q_rope"], a["main"], a["main_indices"],
@@ -147,11 +145,11 @@ def test_one_hot_gather_probe(gpu, kernel):
     q0 = np.zeros((T, H, 448), dtype=np.uint16)
     r0 = np.zeros((T, H, 64), dtype=np.uint16)
     for s in (1, 2, 4):
-        print(f"two-source one-hot s={s} pairs={os.environ.get('SMD_DECODE_PAIRS')}", flush=True)
+        print(f"two-source one-hot s={s} kernel={_KERNEL['name']}", flush=True)
         po, pl = smd.sparse_mla_decode_two_source(
             bf16_tensor(q0, gpu), bf16_tensor(r0, gpu), smd.KVPool.bf16(bf16_tensor(main, gpu)),
             torch.from_numpy(mi).to(gpu), smd.KVPool.bf16(bf16_tensor(swa, gpu)), torch.from_numpy(si).to(gpu),
-            None, 1.0, num_splits=s, partials_only=True)
+            None, 1.0, num_splits=s, partials_only=True, kernel=_KERNEL['name'])
         torch.cuda.synchronize()
         po_ref, pl_ref = ref.sparse_mla_decode_two_source_partials(q0, r0, {"kv": main}, mi, {"kv": swa}, si, 1.0, s)
         g = po.cpu().numpy().astype(np.float64)
