@@ -1,7 +1,10 @@
 """GPU parity at the full sizes of the named workloads, in the launch
 configuration bench.py times (the host planner's split count, decode + merge
-into bf16), plus the extreme split counts.  Every output element is compared
-with the float64 oracle."""
+into bf16), plus the extreme split counts and every kernel family.  Every
+output element is compared with the float64 oracle, and repeated launches
+must give bit-identical outputs (the aiter page "[FlyDSL] [Perf] pa_decode:
+K/V streaming, MTP query split and sparse split-major on gfx950", PR
+Self-Review: every changed case bit-exact over repeated launches)."""
 import functools
 
 import numpy as np
@@ -28,26 +31,43 @@ def _oracle(i):
                                  w.arrays["sink"], w.softmax_scale, w.q_per_seq)
 
 
-def _run(i, gpu, splits):
+def _run(i, gpu, splits, kernel=None, repeats=1):
     w = _workload(i)
     q_nope, q_rope, sink, pool = device_inputs(w, gpu)
     idx = torch.from_numpy(w.arrays["indices"]).to(gpu)
     K = idx.shape[1]
     kvd = smd.KV_BF16 if w.kv_dtype == "bf16" else smd.KV_FP8_E4M3_UE8M0
     s = smd.plan_num_kv_splits(w.num_index_rows, w.num_heads, K, w.q_per_seq, kvd) if splits == "planner" else splits
-    print(f"full size {w.name} s={s}", flush=True)
-    out, lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s,
-                                     q_per_seq=w.q_per_seq)
-    torch.cuda.synchronize()
+    first = None
+    for rep in range(repeats):
+        print(f"full size {w.name} s={s} kernel={kernel} launch {rep}", flush=True)
+        out, lse = smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s,
+                                         q_per_seq=w.q_per_seq, kernel=kernel)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (out, lse)
+            continue
+        assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), f"launch {rep} differs (out)"
+        assert torch.equal(lse, first[1]), f"launch {rep} differs (lse)"
     o_ref, l_ref = _oracle(i)
-    check_out(out, o_ref, f"{w.name} s={s}")
-    check_lse(lse, l_ref, f"{w.name} s={s}")
+    check_out(first[0], o_ref, f"{w.name} s={s}")
+    check_lse(first[1], l_ref, f"{w.name} s={s}")
 
 
 @pytest.mark.parametrize("i,splits", [(0, "planner"), (1, "planner"), (1, 1), (1, 4), (2, "planner"), (2, 1),
                                       (3, "planner"), (3, 32)])
 def test_config_full_size(gpu, i, splits):
     _run(i, gpu, splits)
+
+
+@pytest.mark.parametrize("i,splits,kernel", [(1, 4, "rows16"), (1, 2, "pairs"), (2, 1, "rows16"), (2, 2, "pairs"),
+                                             (2, 8, "wide"), (3, 31, "rows16")])
+def test_config_repeat_launches_bit_exact(gpu, i, splits, kernel):
+    """Twenty launches of the same call give bit-identical out and lse, on
+    each kernel family at the bf16 (T=8, H=64), fp8 (T=32, H=128) and
+    long-context (T=1, 65664 indices) workloads; the first launch also meets
+    the oracle."""
+    _run(i, gpu, splits, kernel=kernel, repeats=20)
 
 
 def test_long_context_partials_full_size(gpu):

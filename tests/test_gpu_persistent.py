@@ -251,32 +251,45 @@ def test_graph_replay_with_changing_lengths(gpu):
 def test_config5_full_size(gpu):
     """The ragged MTP4 workload at full size (64 x 4 tokens, H=128, fp8 pool of
     262144 rows, K_b <= 8192, 4 empty sequences) with the default partition
-    count.  Every K=0 row is checked untouched and the plan bit-exact; the
-    oracle checks a sample of sequences (split ones included); every other
-    sequence is checked against the split-KV path on the GPU."""
+    count, in the launch configuration bench.py times.  Every non-empty
+    sequence is checked against the float64 oracle (split sequences and the
+    longest and shortest lists among them), every K=0 row is checked
+    untouched, the plan bit-exact, and twenty launches give bit-identical
+    outputs (the fixed merge order of the split sequences makes them
+    deterministic).  As an extra check every sequence also matches the
+    split-KV path."""
     w = wl.config(4)
     a = w.arrays
     q_nope, q_rope, sink, pool, ptr, flat = _ragged_inputs(w, gpu)
     P = smd.persistent_default_partitions(128, 4)
     ws = smd.PersistentWorkspace(128, 4, P, device=gpu)
-    out, lse = _filled(w, gpu)
-    print(f"config 5 full size P={P}", flush=True)
-    smd.sparse_mla_decode_persistent(q_nope, q_rope, pool, ptr, flat, sink, w.softmax_scale, q_per_seq=4,
-                                     workspace=ws, out=out, lse=lse)
-    torch.cuda.synchronize()
+    first = None
+    for rep in range(20):
+        out, lse = _filled(w, gpu)
+        print(f"config 5 full size P={P} launch {rep}", flush=True)
+        smd.sparse_mla_decode_persistent(q_nope, q_rope, pool, ptr, flat, sink, w.softmax_scale, q_per_seq=4,
+                                         workspace=ws, out=out, lse=lse)
+        torch.cuda.synchronize()
+        if first is None:
+            first = (out, lse)
+            continue
+        assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), f"launch {rep} differs (out)"
+        assert torch.equal(lse, first[1]), f"launch {rep} differs (lse)"
+    out, lse = first
     _check_plan(ws, a["kv_indptr"], P)
     ptr_np = a["kv_indptr"]
     B = len(ptr_np) - 1
     _, pieces = plan_ref.partition(ptr_np, P)
-    split = sorted({x.seq for pl in pieces for x in pl if x.split})
+    split = {x.seq for pl in pieces for x in pl if x.split}
     lens = np.diff(ptr_np)
-    nonzero = [b for b in range(B) if lens[b] > 0]
-    sample = sorted(set(split[:3] + [int(np.argmax(lens)), min(nonzero, key=lambda b: lens[b])]))
-    zero = [b for b in range(B) if lens[b] == 0]
-    _check_against_oracle(w, out, lse, seqs=sample + zero)
-    # every sequence against the split-KV entry point (itself checked against the oracle)
+    assert len(split) > 10, "the workload should split many sequences"
+    checked = _check_against_oracle(w, out, lse)  # every sequence; K=0 rows must be untouched
+    assert checked == int(np.count_nonzero(lens))
+    # extra check: every sequence against the split-KV entry point
     o_all, l_all = out.float(), lse
-    for b in nonzero:
+    for b in range(B):
+        if lens[b] == 0:
+            continue
         t0, t1 = 4 * b, 4 * b + 4
         idx = flat[ptr_np[b]:ptr_np[b + 1]].view(1, -1)
         od, ld = smd.sparse_mla_decode(q_nope[t0:t1].contiguous(), q_rope[t0:t1].contiguous(), pool, idx, sink,
