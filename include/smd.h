@@ -309,6 +309,31 @@ int smd_sparse_mla_decode_two_source_ex(const void *q_nope, const void *q_rope, 
                                         const smd_decode_options *options, void *stream);
 
 /*
+ * Allocation-free split-KV decode, for callers that cannot allocate device
+ * memory or pass a workspace (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): smd_sparse_mla_decode_ex with the
+ * FP32 partials of a split plan kept in a library-owned device array of
+ * SMD_NOALLOC_SCRATCH_BYTES per GPU instead of caller buffers.
+ *  - out (bf16 [num_tokens, num_heads, 512]) is required; lse may be NULL.
+ *  - num_splits == 1 needs no scratch; num_splits > 1 needs
+ *    smd_partials_bytes(num_tokens, num_heads, num_splits) <=
+ *    SMD_NOALLOC_SCRATCH_BYTES, else SMD_ERR_WORKSPACE (nothing launched).
+ *  - The array belongs to the device current at the call; each GPU the
+ *    library runs on holds its own copy until the process ends.  The first
+ *    call on a device looks its address up (no allocation, no launch).
+ *  - Calls that overlap on one GPU (concurrent streams, or threads without
+ *    ordering) race on that GPU's array; order them on the GPU.
+ * Everything else (arguments, checks, results, options) as
+ * smd_sparse_mla_decode_ex.  Calls no hipMalloc / hipFree.
+ */
+#define SMD_NOALLOC_SCRATCH_BYTES (32u << 20)
+int smd_sparse_mla_decode_noalloc(const void *q_nope, const void *q_rope, int32_t num_tokens,
+                                  int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
+                                  const int32_t *indices, int64_t indices_stride, int32_t topk,
+                                  const float *sink, float softmax_scale, int32_t num_splits, void *out,
+                                  float *lse, const smd_decode_options *options, void *stream);
+
+/*
  * Stage-2 merge (aiter page, Summary part 1: always reduce the FP32
  * partials, even with one split per row):
  *   LSE = ln(sum_r e^{lse_r} + e^{sink_h}),  out = sum_r e^{lse_r - LSE} o_r.

@@ -21,6 +21,7 @@ ROPE = 64
 DIM = 512
 MAX_SPLITS = 32
 MAX_MERGE_SPLITS = 1024
+NOALLOC_SCRATCH_BYTES = 32 << 20
 SPLIT_ALIGN = 64
 MAX_PARTITIONS = 16384
 
@@ -123,6 +124,9 @@ def lib() -> ctypes.CDLL:
     L.smd_sparse_mla_decode_ex.restype = ctypes.c_int
     L.smd_sparse_mla_decode_ex.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
                                            vp, f32, i32, vp, vp, vp, vp, ctypes.POINTER(_DecodeOptions), vp]
+    L.smd_sparse_mla_decode_noalloc.restype = ctypes.c_int
+    L.smd_sparse_mla_decode_noalloc.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
+                                                vp, f32, i32, vp, vp, ctypes.POINTER(_DecodeOptions), vp]
     L.smd_sparse_mla_decode_two_source.restype = ctypes.c_int
     L.smd_sparse_mla_decode_two_source.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, i64, i32,
                                                    ctypes.POINTER(_KVPool), vp, i64, i32,
@@ -273,8 +277,10 @@ def split_bounds(kv_len: int, num_splits: int, split: int) -> tuple[int, int]:
 # decode and merge
 # ----------------------------------------------------------------------------
 def _decode_buffers(q_nope, q_rope, index_lists, sink, pools, q_per_seq, num_splits, out, lse, partial_o,
-                    partial_lse, partials_only):
-    """Shared checks and output allocation of the dense-index decodes."""
+                    partial_lse, partials_only, allocate=True):
+    """Shared checks and output allocation of the dense-index decodes.  With
+    allocate=False nothing is allocated: out must be given, lse and the
+    partials are checked only when given."""
     dev = q_nope.device
     _need(q_nope, "q_nope", torch.bfloat16, device=dev)
     if q_nope.dim() != 3 or q_nope.shape[2] != NOPE:
@@ -295,7 +301,7 @@ def _decode_buffers(q_nope, q_rope, index_lists, sink, pools, q_per_seq, num_spl
     K = sum(idx.shape[1] for _, idx in index_lists)
     if num_splits is None:
         num_splits = plan_num_kv_splits(T // q_per_seq, H, K, q_per_seq, pools[0].dtype if K > 0 else KV_BF16)
-    need_partials = partials_only or num_splits > 1
+    need_partials = allocate and (partials_only or num_splits > 1)
     if need_partials:
         if partial_o is None:
             partial_o = torch.empty((T, H, num_splits, DIM), dtype=torch.float32, device=dev)
@@ -304,12 +310,15 @@ def _decode_buffers(q_nope, q_rope, index_lists, sink, pools, q_per_seq, num_spl
         _need(partial_o, "partial_o", torch.float32, (T, H, num_splits, DIM), dev)
         _need(partial_lse, "partial_lse", torch.float32, (T, H, num_splits), dev)
     if not partials_only:
-        if out is None:
+        if allocate and out is None:
             out = torch.empty((T, H, DIM), dtype=torch.bfloat16, device=dev)
-        if lse is None:
+        if allocate and lse is None:
             lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+        if out is None:
+            raise ValueError("out is required")
         _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
-        _need(lse, "lse", torch.float32, (T, H), dev)
+        if lse is not None:
+            _need(lse, "lse", torch.float32, (T, H), dev)
     return T, H, num_splits, out, lse, partial_o, partial_lse
 
 
@@ -348,6 +357,27 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
     _check("smd_sparse_mla_decode", rc)
     if partials_only:
         return partial_o, partial_lse
+    return out, lse
+
+
+def sparse_mla_decode_noalloc(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, indices: torch.Tensor,
+                              sink: Optional[torch.Tensor], softmax_scale: float, *, out: torch.Tensor,
+                              lse: Optional[torch.Tensor] = None, num_splits: Optional[int] = None,
+                              q_per_seq: int = 1, kernel=None):
+    """sparse_mla_decode through the allocation-free entry point: the FP32
+    partials of a split plan stay in the library's per-GPU scratch array
+    (NOALLOC_SCRATCH_BYTES), so neither this call nor the library allocates.
+    out (bf16 [T,H,512]) must be given; lse (fp32 [T,H]) is optional."""
+    T, H, num_splits, out, lse, _, _ = _decode_buffers(q_nope, q_rope, [("indices", indices)], sink, [kv], q_per_seq,
+                                                       num_splits, out, lse, None, None, partials_only=False,
+                                                       allocate=False)
+    pool = kv._struct()
+    opt = _options(kernel)
+    rc = lib().smd_sparse_mla_decode_noalloc(
+        q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool), *_idx_args(indices),
+        _ptr(sink), float(softmax_scale), num_splits, out.data_ptr(), _ptr(lse),
+        ctypes.byref(opt) if opt is not None else None, _stream(q_nope))
+    _check("smd_sparse_mla_decode_noalloc", rc)
     return out, lse
 
 
@@ -510,7 +540,7 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
 
 __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
            "partials_bytes", "write_kv_fp8",
-           "sparse_mla_decode", "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
+           "sparse_mla_decode", "sparse_mla_decode_noalloc", "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
            "PersistentWorkspace", "sparse_mla_decode_persistent", "lib", "library_path", "KV_BF16",
            "KV_FP8_E4M3_UE8M0"]
 

@@ -18,7 +18,7 @@ INCLUDE = PKG.parent / "include"
 LIB = PKG / "libsmd.so"
 BUILD_DIR = PKG.parent / "_build"
 
-SOURCES = ["api.cpp", "plan.cpp", "decode_kernels.hip", "wide_kernel.hip", "persistent_kernel.hip",
+SOURCES = ["api.cpp", "plan.cpp", "noalloc.hip", "decode_kernels.hip", "wide_kernel.hip", "persistent_kernel.hip",
            "writer_kernel.hip"]
 ARCH = os.environ.get("SMD_OFFLOAD_ARCH", "gfx950")
 

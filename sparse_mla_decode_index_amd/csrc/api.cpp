@@ -128,16 +128,8 @@ using namespace smd;
 
 extern "C" const char *smd_last_error(void) { return g_err; }
 
-// Second source of a two-source decode (the sliding-window pool and its index
-// list); null for one source.
-struct SecondSource {
-  const smd_kv_pool *kv;
-  const int32_t *indices;
-  int64_t indices_stride;
-  int32_t count;
-};
-
-static int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t num_tokens,
+namespace smd {
+int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t num_tokens,
                        int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv, const int32_t *indices,
                        int64_t indices_stride, int32_t topk, const SecondSource *two, const float *sink,
                        float softmax_scale, int32_t num_splits, float *partial_o, float *partial_lse, void *out,
@@ -303,6 +295,8 @@ static int decode_impl(const char *fn, const void *q_nope, const void *q_rope, i
   }
   return SMD_OK;
 }
+
+}  // namespace smd
 
 extern "C" int smd_sparse_mla_decode_ex(const void *q_nope, const void *q_rope, int32_t num_tokens,
                                         int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "../../include/smd.h"
+
 namespace smd {
 
 constexpr int kNope = 448;
@@ -105,5 +107,26 @@ struct WriterArgs {
 };
 
 hipError_t launch_write_kv_fp8(const WriterArgs &a, hipStream_t stream);
+
+// Error message of the calling thread's last failure (set by every entry point).
+void set_error(const char *fmt, ...);
+
+// Second source of a two-source decode (the sliding-window pool and its index
+// list); null for one source.
+struct SecondSource {
+  const smd_kv_pool *kv;
+  const int32_t *indices;
+  int64_t indices_stride;
+  int32_t count;
+};
+
+// The split-KV decode behind the public entry points (checks, kernel choice,
+// decode launch and, for s > 1 with out, the merge); fn names the caller in
+// error messages.
+int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t num_tokens, int32_t num_heads,
+                int32_t q_per_seq, const smd_kv_pool *kv, const int32_t *indices, int64_t indices_stride,
+                int32_t topk, const SecondSource *two, const float *sink, float softmax_scale, int32_t num_splits,
+                float *partial_o, float *partial_lse, void *out, float *lse, const smd_decode_options *opt,
+                void *stream);
 
 }  // namespace smd
