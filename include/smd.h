@@ -214,10 +214,27 @@ enum {
   SMD_KERNEL_WIDE = 3
 };
 
+/*
+ * How the persistent decode merges a split row group (the split-KV entry
+ * points take SMD_MERGE_AUTO only).  Both give the same bits.
+ *   SMD_MERGE_AUTO       a piece that finds every other piece of its row
+ *                        group arrived (and at most 8 of them) merges straight
+ *                        from its registers and writes no partial of its own;
+ *                        the rest write FP32 partials and the last to arrive
+ *                        merges from the workspace.
+ *   SMD_MERGE_WORKSPACE  every piece writes its partial and the last to
+ *                        arrive merges from the workspace.
+ */
+enum {
+  SMD_MERGE_AUTO = 0,
+  SMD_MERGE_WORKSPACE = 1
+};
+
 /* Options of the _ex entry points; NULL means all defaults (zero). */
 typedef struct smd_decode_options {
-  int32_t kernel;      /* SMD_KERNEL_* */
-  int32_t reserved[7]; /* must be zero */
+  int32_t kernel;      /* SMD_KERNEL_* (SMD_KERNEL_AUTO for the persistent decode) */
+  int32_t merge;       /* SMD_MERGE_* */
+  int32_t reserved[6]; /* must be zero */
 } smd_decode_options;
 
 /*
@@ -356,7 +373,9 @@ int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t
  * workgroup computes the split plan inside the kernel from the live
  * kv_indptr; rows held by one partition are written as bf16 directly, split
  * rows write FP32 partials into the workspace and the workgroup that arrives
- * last merges them; sequences with no index are left unwritten.  Because the
+ * last merges them; sequences with no index are left unwritten.  (Here the
+ * piece that finds all the others arrived merges without writing a partial
+ * of its own when the row group has 128 rows; see SMD_MERGE_*.)  Because the
  * plan is read from device memory on every launch, a captured graph stays
  * correct when kv_indptr and kv_indices change between replays.
  *
@@ -421,6 +440,15 @@ int smd_sparse_mla_decode_persistent(const void *q_nope, const void *q_rope, int
                                      const float *sink, float softmax_scale, void *workspace,
                                      size_t workspace_bytes, int32_t num_partitions, void *out,
                                      float *lse, void *stream);
+
+/* The same with options (NULL = defaults): options->kernel must be
+ * SMD_KERNEL_AUTO; options->merge selects SMD_MERGE_*. */
+int smd_sparse_mla_decode_persistent_ex(const void *q_nope, const void *q_rope, int32_t num_seqs,
+                                        int32_t q_per_seq, int32_t num_heads, const smd_kv_pool *kv,
+                                        const int32_t *kv_indptr, const int32_t *kv_indices,
+                                        const float *sink, float softmax_scale, void *workspace,
+                                        size_t workspace_bytes, int32_t num_partitions, void *out,
+                                        float *lse, const smd_decode_options *options, void *stream);
 
 /*
  * fp8/UE8M0 KV-cache writer: quantises bf16 latent rows into an fp8 pool

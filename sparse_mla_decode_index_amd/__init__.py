@@ -62,16 +62,23 @@ class _KVPool(ctypes.Structure):
 
 
 class _DecodeOptions(ctypes.Structure):
-    _fields_ = [("kernel", ctypes.c_int32), ("reserved", ctypes.c_int32 * 7)]
+    _fields_ = [("kernel", ctypes.c_int32), ("merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
 
 
-def _options(kernel) -> Optional[_DecodeOptions]:
-    """A smd_decode_options for `kernel` (a KERNEL_* value or its name), or
-    None for the library's default."""
-    if kernel is None:
+MERGE_AUTO = 0
+MERGE_WORKSPACE = 1
+_MERGES = {"auto": MERGE_AUTO, "workspace": MERGE_WORKSPACE}
+
+
+def _options(kernel=None, merge=None) -> Optional[_DecodeOptions]:
+    """A smd_decode_options for `kernel` (a KERNEL_* value or its name) and
+    `merge` (a MERGE_* value or its name), or None for the library's
+    defaults."""
+    if kernel is None and merge is None:
         return None
-    k = _KERNELS[kernel] if isinstance(kernel, str) else int(kernel)
-    return _DecodeOptions(kernel=k)
+    k = 0 if kernel is None else (_KERNELS[kernel] if isinstance(kernel, str) else int(kernel))
+    m = 0 if merge is None else (_MERGES[merge] if isinstance(merge, str) else int(merge))
+    return _DecodeOptions(kernel=k, merge=m)
 
 
 class PlanModel(ctypes.Structure):
@@ -149,6 +156,10 @@ def lib() -> ctypes.CDLL:
     L.smd_sparse_mla_decode_persistent.restype = ctypes.c_int
     L.smd_sparse_mla_decode_persistent.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, vp, vp, f32,
                                                    vp, ctypes.c_size_t, i32, vp, vp, vp]
+    L.smd_sparse_mla_decode_persistent_ex.restype = ctypes.c_int
+    L.smd_sparse_mla_decode_persistent_ex.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, vp, vp,
+                                                      f32, vp, ctypes.c_size_t, i32, vp, vp,
+                                                      ctypes.POINTER(_DecodeOptions), vp]
     _lib = L
     return L
 
@@ -498,10 +509,12 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
                                  kv_indptr: torch.Tensor, kv_indices: torch.Tensor,
                                  sink: Optional[torch.Tensor], softmax_scale: float, *,
                                  q_per_seq: int = 1, workspace: PersistentWorkspace,
-                                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None):
+                                 out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                                 merge=None):
     """Persistent decode over ragged sequences: q bf16 [B*q_per_seq, H, 448/64],
     kv_indptr int32 [B+1], kv_indices int32 flat.  Returns (out, lse); rows of
-    sequences with no index are left as they were in `out` / `lse`."""
+    sequences with no index are left as they were in `out` / `lse`.  merge:
+    None / "auto" or "workspace" (smd.h SMD_MERGE_*; both give the same bits)."""
     dev = q_nope.device
     _need(q_nope, "q_nope", torch.bfloat16, device=dev)
     if q_nope.dim() != 3 or q_nope.shape[2] != NOPE:
@@ -530,11 +543,12 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
     _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
     _need(lse, "lse", torch.float32, (T, H), dev)
     pool = kv._struct()
-    rc = lib().smd_sparse_mla_decode_persistent(
+    opts = _options(merge=merge)
+    rc = lib().smd_sparse_mla_decode_persistent_ex(
         q_nope.data_ptr(), q_rope.data_ptr(), B, q_per_seq, H, ctypes.byref(pool), kv_indptr.data_ptr(),
         kv_indices.data_ptr() if kv_indices.numel() else kv_indptr.data_ptr(), _ptr(sink), float(softmax_scale),
         workspace.view.data_ptr(), workspace.nbytes, workspace.num_partitions, out.data_ptr(), lse.data_ptr(),
-        _stream(q_nope))
+        ctypes.byref(opts) if opts is not None else None, _stream(q_nope))
     _check("smd_sparse_mla_decode_persistent", rc)
     return out, lse
 

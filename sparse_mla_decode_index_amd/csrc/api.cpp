@@ -140,7 +140,11 @@ int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t 
       set_error("%s: unknown kernel choice %d", fn, opt->kernel);
       return SMD_ERR_INVALID_ARG;
     }
-    for (int i = 0; i < 7; ++i) {
+    if (opt->merge != SMD_MERGE_AUTO) {
+      set_error("%s: options.merge applies to the persistent decode only", fn);
+      return SMD_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 6; ++i) {
       if (opt->reserved[i] != 0) {
         set_error("%s: options.reserved must be zero", fn);
         return SMD_ERR_INVALID_ARG;
@@ -423,14 +427,30 @@ extern "C" int smd_persistent_workspace_reset(void *workspace, size_t bytes, voi
   return SMD_OK;
 }
 
-extern "C" int smd_sparse_mla_decode_persistent(const void *q_nope, const void *q_rope, int32_t num_seqs,
-                                                int32_t q_per_seq, int32_t num_heads, const smd_kv_pool *kv,
-                                                const int32_t *kv_indptr, const int32_t *kv_indices,
-                                                const float *sink, float softmax_scale, void *workspace,
-                                                size_t workspace_bytes, int32_t num_partitions, void *out,
-                                                float *lse, void *stream) {
+extern "C" int smd_sparse_mla_decode_persistent_ex(const void *q_nope, const void *q_rope, int32_t num_seqs,
+                                                   int32_t q_per_seq, int32_t num_heads, const smd_kv_pool *kv,
+                                                   const int32_t *kv_indptr, const int32_t *kv_indices,
+                                                   const float *sink, float softmax_scale, void *workspace,
+                                                   size_t workspace_bytes, int32_t num_partitions, void *out,
+                                                   float *lse, const smd_decode_options *opt, void *stream) {
   static const char *fn = "smd_sparse_mla_decode_persistent";
   g_err[0] = 0;
+  if (opt != nullptr) {
+    if (opt->kernel != SMD_KERNEL_AUTO) {
+      set_error("%s: the persistent decode takes SMD_KERNEL_AUTO only (got %d)", fn, opt->kernel);
+      return SMD_ERR_INVALID_ARG;
+    }
+    if (opt->merge != SMD_MERGE_AUTO && opt->merge != SMD_MERGE_WORKSPACE) {
+      set_error("%s: unknown merge choice %d", fn, opt->merge);
+      return SMD_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 6; ++i) {
+      if (opt->reserved[i] != 0) {
+        set_error("%s: options.reserved must be zero", fn);
+        return SMD_ERR_INVALID_ARG;
+      }
+    }
+  }
   if (num_seqs < 0) {
     set_error("%s: negative num_seqs=%d", fn, num_seqs);
     return SMD_ERR_INVALID_ARG;
@@ -503,12 +523,24 @@ extern "C" int smd_sparse_mla_decode_persistent(const void *q_nope, const void *
   pa.plan = (int32_t *)(ws + lay.plan_off);
   pa.counters = (uint32_t *)(ws + lay.ctr_off);
   pa.slots = (float *)(ws + lay.slot_off);
+  pa.reg_merge = opt == nullptr || opt->merge == SMD_MERGE_AUTO;
   hipError_t e = launch_persistent(pa, rb, kv->dtype == SMD_KV_FP8_E4M3_UE8M0, (hipStream_t)stream);
   if (e != hipSuccess) {
     set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
     return SMD_ERR_HIP;
   }
   return SMD_OK;
+}
+
+extern "C" int smd_sparse_mla_decode_persistent(const void *q_nope, const void *q_rope, int32_t num_seqs,
+                                                int32_t q_per_seq, int32_t num_heads, const smd_kv_pool *kv,
+                                                const int32_t *kv_indptr, const int32_t *kv_indices,
+                                                const float *sink, float softmax_scale, void *workspace,
+                                                size_t workspace_bytes, int32_t num_partitions, void *out,
+                                                float *lse, void *stream) {
+  return smd_sparse_mla_decode_persistent_ex(q_nope, q_rope, num_seqs, q_per_seq, num_heads, kv, kv_indptr,
+                                             kv_indices, sink, softmax_scale, workspace, workspace_bytes,
+                                             num_partitions, out, lse, nullptr, stream);
 }
 
 // ----------------------------------------------------------------------------

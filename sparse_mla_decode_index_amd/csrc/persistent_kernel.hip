@@ -188,8 +188,8 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
             z[u] += wq;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              o[u][e] += wq * v[i][u][0][e];
-              o[u][4 + e] += wq * v[i][u][1][e];
+              o[u][e] = __builtin_fmaf(wq, v[i][u][0][e], o[u][e]);
+              o[u][4 + e] = __builtin_fmaf(wq, v[i][u][1][e], o[u][4 + e]);
             }
           }
         }
@@ -282,8 +282,8 @@ __device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b
           z[u] += wq;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[u][e] += wq * v[i][u][0][e];
-            o[u][4 + e] += wq * v[i][u][1][e];
+            o[u][e] = __builtin_fmaf(wq, v[i][u][0][e], o[u][e]);
+            o[u][4 + e] = __builtin_fmaf(wq, v[i][u][1][e], o[u][4 + e]);
           }
         }
       }
@@ -416,6 +416,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int lp = tile_owner(start + tb - 1, total, pa.P);
 
     const int slot = 2 * p + (lo == t0 ? 0 : 1);
+    bool merged = false;  // this piece merged its row group from registers
     float *sb = pa.slots + slot * slot_floats;
     if constexpr (WIDE) {
       // wave w owns query rows 32w .. 32w+31 of the group: the consecutive
@@ -438,12 +439,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const float l_tot = half_sum(w.l_run);
       const bool lse_lane = lane < 32;
       uint8_t SMD_LDS *stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
-      if (fp == lp)
-        write_direct_wide(w, l_tot, a.sink ? a.sink[hq] : -INFINITY, a.out + qbase * kDim, kDim,
-                          (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr, stage, lane);
+      float SMD_LDS *tbl = (float SMD_LDS *)&sm.qs[wave][0][0];  // free until the next piece's Q^T load
+      const int t0_fp = (int)((int64_t)fp * total / pa.P);
+      // the k-th other piece of a merge: partition fp + k, skipping this one
+      // (the register merge runs only when every partition of the span holds a piece)
+      auto part = [&](int k) {
+        const int qp = fp + k + (fp + k >= p ? 1 : 0);
+        const int sl = qp == fp ? 2 * fp + (start == t0_fp ? 0 : 1) : 2 * qp;
+        const float *base = pa.slots + (size_t)sl * slot_floats;
+        return PiecePtrs{base + (size_t)mq0 * kDim, base + (size_t)a.M * kDim + mq0};
+      };
+      const float sink_ln = a.sink ? a.sink[hq] : -INFINITY;
+      float scale, lse_v, w_own = 0.f, inv_l = 0.f;
+      bool f32 = false;
+      void *dst = a.out + qbase * kDim;
+      float *lse_dst = (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr;
+      if (fp == lp) {
+        const OutScale sc = direct_scale(w.m_ref, l_tot, sink_ln);
+        scale = sc.inv;
+        lse_v = sc.lse;
+      } else {
+        // When every other piece has arrived already (the usual case for the
+        // piece that finishes last), this one merges from its registers and
+        // writes no partial: nobody else can be last, since the count never
+        // reaches the others' number of pieces from their side.  Both ways
+        // of merging give the same bits.
+        const int pieces = total >= pa.P ? lp - fp + 1 : tb;
+        uint32_t *ctr = pa.counters + (size_t)g * pa.P + fp;
+        if (threadIdx.x == 0) s_arrived = __hip_atomic_load(ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        merged = pa.reg_merge && s_arrived == (uint32_t)(pieces - 1) && pieces - 1 <= kRegMergeMax &&
+                 total >= pa.P;
+        __syncthreads();  // s_arrived is rewritten below
+        if (merged) {
+          __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire the other pieces
+          merge_weights_wide(w, l_tot, sink_ln, part, pieces - 1, p - fp, tbl, w_own, inv_l, scale, lse_v);
+          if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        } else {
+          const OutScale sc = partial_scale(w.m_ref, l_tot);
+          scale = sc.inv;
+          lse_v = sc.lse;
+          f32 = true;
+          dst = sb + (size_t)mq0 * kDim;
+          lse_dst = lse_lane ? sb + (size_t)a.M * kDim + mq0 + (lane & 31) : nullptr;
+        }
+      }
+      if (merged)
+        store_rows_wide<true>(w, scale, false, dst, kDim, stage, part, lp - fp, p - fp, w_own, inv_l, tbl);
       else
-        write_partial_wide(w, l_tot, sb + (size_t)mq0 * kDim, kDim,
-                           lse_lane ? sb + (size_t)a.M * kDim + mq0 + (lane & 31) : nullptr, stage, lane);
+        store_rows_wide<false>(w, scale, f32, dst, kDim, stage);
+      if (lse_dst != nullptr) *lse_dst = lse_v;
     } else {
       const int64_t qrow = (int64_t)(b * a.qps + m / a.H) * a.H + head;
       bf16x8 qreg[NC];
@@ -458,7 +503,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       else
         write_partial(w, l_tot, sb + (size_t)m * kDim + dcol, lse_lane ? sb + (size_t)a.M * kDim + m : nullptr);
     }
-    if (fp != lp) {
+    if (fp != lp && !merged) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release this piece (other XCDs read it)
       __syncthreads();
       uint32_t *ctr = pa.counters + (size_t)g * pa.P + fp;

@@ -80,6 +80,7 @@ struct PersistArgs {
   int32_t *plan;              // [P][4]: t0, t1, first and last sequence
   uint32_t *counters;         // [M / 16][P] arrival counters (row group g, first partition)
   float *slots;               // [2P][M * 513]: per slot o [M][512] then lse [M]
+  bool reg_merge;             // SMD_MERGE_AUTO: the last piece may merge from its registers
 };
 
 // Workspace layout of the persistent kernel (byte offsets, 256-byte aligned).

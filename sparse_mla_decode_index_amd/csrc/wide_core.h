@@ -298,7 +298,7 @@ __device__ __forceinline__ void run_split_wide(const DecodeArgs &a, SmemWide<fal
     const int blk = load_idx_block(row_idx, p0, p1, nb);
     uint8_t SMD_LDS *next = tile0 + ((t + 1) & 1) * kTileBytes;
     auto mid = [&](int i) {
-      if (i < kStorePieces<FP8>) store_row_piece<FP8, kLay32>(next, wave, lane, sa, i);
+      if (i < kStorePieces<FP8>) store_row_piece<FP8, kLay32>(next, wave, opaque_lane(), sa, i);
     };
     auto post = [&](int) { load_rows<FP8, PACKED>(a, zrow, gl, tidx(t + 2), p0 + (t + 2) * kBK, p1, wave, lane, sa); };
     compute_tile_wide<kQRegStaged, PASS, P_HILO>(tile0 + (t & 1) * kTileBytes, qreg, qs, L, v_cur, lane,
@@ -582,7 +582,7 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
       const int nb = t / kTilesPerIdxBlock + 1;
       dma_idx_block(row_idx, p0, p1, nb, wave, lane, ib0 + (nb & 1) * kIdxBlock);
     }
-    store_rows<true, kLay32>(tile, wave, lane, st);
+    store_rows<true, kLay32>(tile, wave, opaque_lane(), st);  // row offsets recomputed, not kept
     barrier_lds();  // B
     compute_tile_wide<kQRegDma, PASS, P_HILO>(tile, qreg, qs, L, v_cur, lane, a.scale_log2, w);
   }
@@ -635,72 +635,197 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
 
 // Outputs of a wide wave's 32 query rows, stored row-wise through the wave's
 // staging slice (the accumulators hold dims 32D + 8b + 4u .. +4 of row
-// lane % 32 in acc[D][4b .. 4b+3], u = lane / 32).  dst points at dim 0 of the
-// wave's first row; rows are row_stride elements apart.
+// lane % 32 in acc[D][4b .. 4b+3], u = lane / 32).
 __device__ __forceinline__ f32x4 wide_quad(const f32x16 &v, int b) {
   return f32x4{v[4 * b], v[4 * b + 1], v[4 * b + 2], v[4 * b + 3]};
 }
 
-// bf16 rows, two passes of 256 dims (512 bytes per row).
-__device__ __forceinline__ void store_rows_bf16(const WideState &w, float inv, uint16_t *dst, int64_t row_stride,
-                                                uint8_t SMD_LDS *stage, int) {
-  const int lane = opaque_lane();
-  const int q = lane & 31, u = lane >> 5;
-#pragma unroll
-  for (int pass = 0; pass < 2; ++pass) {
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-#pragma unroll
-      for (int b = 0; b < 4; ++b)  // dims 32dd + 8b + 4u of the pass: chunk 4dd + b, half u
-        *(u32x2 SMD_LDS *)(stage + stage_off(q, 4 * dd + b) + 8 * u) = pack_bf16x4(wide_quad(w.acc[8 * pass + dd], b), inv);
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {  // rows 2k + u, chunk q
-      const int r = 2 * k + u;
-      const u32x4 v = *(const u32x4 SMD_LDS *)(stage + stage_off(r, q));
-      *(u32x4 *)(dst + r * row_stride + 256 * pass + 8 * q) = v;
-    }
-  }
-}
 
-// fp32 rows, four passes of 128 dims (512 bytes per row).
-__device__ __forceinline__ void store_rows_f32(const WideState &w, float inv, float *dst, int64_t row_stride,
-                                               uint8_t SMD_LDS *stage, int) {
-  const int lane = opaque_lane();
-  const int q = lane & 31, u = lane >> 5;
+// The other pieces of a split row group, for the merge below (at most
+// kRegMergeMax of them).
+constexpr int kRegMergeMax = 8;
+struct PiecePtrs {
+  const float *o, *lse;
+};
+struct NoPieces {
+  __device__ PiecePtrs operator()(int) const { return PiecePtrs{nullptr, nullptr}; }
+};
+
+// What a wide wave writes for its 32 rows, row-wise through its staging
+// slice:
+//   !MERGE: bf16 out = scale * O, or (f32) FP32 rows = scale * O (a split
+//           partial); scale belongs to this lane's row (lane % 32);
+//    MERGE: bf16 out = scale * o with o the merge of this piece (its partial
+//           O * inv_l, weight w_own, at position own_k of the span) and the n
+//           >= 1 other pieces part(0..n-1) (weight tbl[32 k + row]): per
+//           element, in span order from zero with one fused multiply-add per
+//           piece, the operations of merge_pieces_narrow, so a row group
+//           merged here and one merged from the workspace hold the same bits
+//           (merge_weights_wide gives the weights and scale = 1 / Z).
+// dst points at dim 0 of the wave's first row, rows row_stride elements
+// apart (uint16_t for bf16, float for FP32); part(k).o points at dim 0 of the
+// wave's first row in the k-th other piece's FP32 partial (rows kDim floats
+// apart).  Four passes of 128 dims: the wave's part goes to the stage in fp32
+// in the accumulator layout (lane (q, u) holds row q), and the rows leave in
+// 16-byte stores: FP32 lane (q, u) takes rows 2k + u, dims 4q..4q+3 of the
+// pass; bf16 lane l takes rows 4k + l / 16, dims 8 (l mod 16) .. +7.  A merge
+// loads each piece's 128 dims row-wise and turns them to the accumulator
+// layout through the stage; the first piece of the next pass is loaded
+// before this pass's stores go out, since a load waits for every store
+// issued before it.  Every LDS read of a phase is issued before its first
+// use, and global addresses are a wave-uniform row base plus a 32-bit lane
+// offset recomputed in each pass from a fresh lane id: 64-bit per-lane
+// offsets kept across passes get spilled, and every reload waits for all the
+// stores in flight.  (The passes are unrolled: acc may only be indexed by
+// constants.)
+template <bool MERGE, class Part = NoPieces>
+__device__ __forceinline__ void store_rows_wide(const WideState &w, float scale, bool f32, void *dst,
+                                                int64_t row_stride, uint8_t SMD_LDS *stage, Part part = Part(),
+                                                int n = 0, int own_k = 0, float w_own = 0.f, float inv_l = 0.f,
+                                                const float SMD_LDS *tbl = nullptr) {
+  auto piece_loads = [&](int pass, int j, f32x4 (&v)[16]) {
+    const int lane = opaque_lane();
+    const uint32_t poff = (uint32_t)((lane >> 5) * kDim + 128 * pass + 4 * (lane & 31)) * 4;
+    const char *src = (const char *)part(j).o;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) v[k] = *(const f32x4 *)(src + (size_t)(2 * k * kDim * 4) + poff);
+  };
+  f32x4 pre[16];  // MERGE: the first other piece's rows of the next pass
+  if constexpr (MERGE) piece_loads(0, 0, pre);
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
+    const int lane = opaque_lane();
+    const int q = lane & 31, u = lane >> 5;
+    if constexpr (MERGE) {
+      f32x4 o[16];
 #pragma unroll
-    for (int dd = 0; dd < 4; ++dd) {
+      for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto add_own = [&]() {
 #pragma unroll
-      for (int b = 0; b < 4; ++b)  // dims 32dd + 8b + 4u of the pass: chunk 8dd + 2b + u
-        *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * dd + 2 * b + u)) = wide_quad(w.acc[4 * pass + dd], b) * inv;
+        for (int i = 0; i < 16; ++i) {
+          const f32x4 t = wide_quad(w.acc[4 * pass + (i >> 2)], i & 3) * inv_l;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[i][e] = __builtin_fmaf(w_own, t[e], o[i][e]);
+        }
+      };
+#pragma unroll 1
+      for (int j = 0; j < n; ++j) {
+        if (j == own_k) add_own();
+        f32x4 v[16];
+        if (j == 0) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) v[k] = pre[k];
+        } else {
+          piece_loads(pass, j, v);
+        }
+#pragma unroll
+        for (int k = 0; k < 16; ++k) *(f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q)) = v[k];
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          v[i] = *(const f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u));
+        if (j == 0 && pass < 3) piece_loads(pass + 1, 0, pre);
+        const float c = tbl[j * 32 + q];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[i][e] = __builtin_fmaf(c, v[i][e], o[i][e]);
+        }
+      }
+      if (own_k == n) add_own();
+#pragma unroll
+      for (int i = 0; i < 16; ++i)  // i = 4dd + b: dims 32dd + 8b + 4u of the pass, chunk 8dd + 2b + u
+        *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u)) = o[i] * scale;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u)) =
+            wide_quad(w.acc[4 * pass + (i >> 2)], i & 3) * scale;
     }
+    char *drow = (char *)dst;
+    if (!MERGE && f32) {
+      const uint32_t voff = (uint32_t)(u * row_stride + 128 * pass + 4 * q) * 4;
+      f32x4 o[16];
 #pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const int r = 2 * k + u;
-      const f32x4 v = *(const f32x4 SMD_LDS *)(stage + stage_off(r, q));
-      *(f32x4 *)(dst + r * row_stride + 128 * pass + 4 * q) = v;
+      for (int k = 0; k < 16; ++k) o[k] = *(const f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q));
+#pragma unroll
+      for (int k = 0; k < 16; ++k) *(f32x4 *)(drow + (size_t)(2 * k * row_stride * 4) + voff) = o[k];
+    } else {
+      const int j = lane & 15, rr = lane >> 4;
+      const uint32_t voff = (uint32_t)(rr * row_stride + 128 * pass + 8 * j) * 2;
+      f32x4 o[8][2];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int r = 4 * k + rr;
+        o[k][0] = *(const f32x4 SMD_LDS *)(stage + stage_off(r, 2 * j));
+        o[k][1] = *(const f32x4 SMD_LDS *)(stage + stage_off(r, 2 * j + 1));
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        u32x4 v;
+        v[0] = pack_bf16x2(o[k][0][0], o[k][0][1]);
+        v[1] = pack_bf16x2(o[k][0][2], o[k][0][3]);
+        v[2] = pack_bf16x2(o[k][1][0], o[k][1][1]);
+        v[3] = pack_bf16x2(o[k][1][2], o[k][1][3]);
+        *(u32x4 *)(drow + (size_t)(4 * k * row_stride * 2) + voff) = v;
+      }
     }
   }
 }
 
-// bf16 output with the sink folded in; lse_dst (this lane's row) is written
-// when non-null.
-__device__ __forceinline__ void write_direct_wide(const WideState &w, float l_tot, float sink_ln, uint16_t *dst,
-                                                  int64_t row_stride, float *lse_dst, uint8_t SMD_LDS *stage,
-                                                  int lane) {
-  const OutScale sc = direct_scale(w.m_ref, l_tot, sink_ln);
-  store_rows_bf16(w, sc.inv, dst, row_stride, stage, lane);
-  if (lse_dst != nullptr) *lse_dst = sc.lse;
-}
-
-// FP32 partial (no sink).
-__device__ __forceinline__ void write_partial_wide(const WideState &w, float l_tot, float *dst, int64_t row_stride,
-                                                   float *lse_dst, uint8_t SMD_LDS *stage, int lane) {
-  const OutScale sc = partial_scale(w.m_ref, l_tot);
-  store_rows_f32(w, sc.inv, dst, row_stride, stage, lane);
-  if (lse_dst != nullptr) *lse_dst = sc.lse;
+// Weights for the piece of a split row group that finds every other piece
+// already arrived: it merges straight from its registers and never writes or
+// rereads a partial of its own.  The arithmetic is that of
+// merge_pieces_narrow, with this piece's partial (o = O / l_tot, lse = m_ref
+// ln 2 + ln l_tot, as partial_scale gives them) taken from registers:
+//   mx  = max(sink, lse of every piece),  w_i = 2^((lse_i - mx) log2 e),
+//   Z   = 2^((sink - mx) log2 e) + w_i summed in span order,
+//   out = (sum_i w_i o_i, in span order) / Z,  lse = mx + ln Z
+// (aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode
+// kernel", Summary part 1: pieces combine by their log-sum-exp, the sink
+// once).  The n <= kRegMergeMax other pieces are part(0..n-1) in span order
+// and this one sits at position own_k.  Leaves the other pieces' weights in
+// tbl[32 k + row] (tbl holds kRegMergeMax * 32 floats), and for this lane's
+// row its weight in w_own, its partial scale in inv_l, 1 / Z in fin and the
+// lse in lse_out.  An empty merge (no piece holds a row and no sink) gives
+// zero weights, fin = 0 and lse = -inf.
+template <class Part>
+__device__ __forceinline__ void merge_weights_wide(const WideState &w, float l_tot, float sink_ln, Part part, int n,
+                                                   int own_k, float SMD_LDS *tbl, float &w_own, float &inv_l,
+                                                   float &fin, float &lse_out) {
+  const int lane = opaque_lane();
+  const int q = lane & 31, u = lane >> 5;
+  const OutScale ps = partial_scale(w.m_ref, l_tot);
+  inv_l = ps.inv;
+  float lo[kRegMergeMax];
+#pragma unroll
+  for (int k = 0; k < kRegMergeMax; ++k) lo[k] = k < n ? part(k).lse[q] : -INFINITY;
+  float mx = fmaxf(sink_ln, ps.lse);
+#pragma unroll
+  for (int k = 0; k < kRegMergeMax; ++k) mx = fmaxf(mx, lo[k]);
+  float c[kRegMergeMax];
+  fin = 0.f;
+  w_own = 0.f;
+  lse_out = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kRegMergeMax; ++k) c[k] = 0.f;
+  if (mx != -INFINITY) {
+    float z = exp2_fast((sink_ln - mx) * kLog2e);
+    w_own = exp2_fast((ps.lse - mx) * kLog2e);
+#pragma unroll
+    for (int k = 0; k <= kRegMergeMax; ++k) {
+      if (k == own_k) z += w_own;
+      if (k < kRegMergeMax && k < n) {
+        c[k] = exp2_fast((lo[k] - mx) * kLog2e);
+        z += c[k];
+      }
+    }
+    fin = 1.f / z;
+    lse_out = mx + logf(z);
+  }
+  if (u == 0) {
+#pragma unroll
+    for (int k = 0; k < kRegMergeMax; ++k) tbl[k * 32 + q] = c[k];
+  }
 }
 
 }  // namespace smd

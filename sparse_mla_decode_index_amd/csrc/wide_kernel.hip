@@ -53,12 +53,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const float l_tot = half_sum(w.l_run);
   const bool lse_lane = lane < 32;
   uint8_t SMD_LDS *stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
-  if (a.S == 1 && a.out != nullptr)
-    write_direct_wide(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qbase * kDim, kDim,
-                      (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr, stage, lane);
+  const bool direct = a.S == 1 && a.out != nullptr;
+  const OutScale sc = direct ? direct_scale(w.m_ref, l_tot, a.sink ? a.sink[head] : -INFINITY)
+                             : partial_scale(w.m_ref, l_tot);
+  if (direct)
+    store_rows_wide<false>(w, sc.inv, false, a.out + qbase * kDim, kDim, stage);
   else
-    write_partial_wide(w, l_tot, a.part_o + (qbase * a.S + r) * kDim, (int64_t)a.S * kDim,
-                       lse_lane ? a.part_lse + qrow * a.S + r : nullptr, stage, lane);
+    store_rows_wide<false>(w, sc.inv, true, a.part_o + (qbase * a.S + r) * kDim, (int64_t)a.S * kDim, stage);
+  float *lse_dst = direct ? (a.lse != nullptr && lse_lane ? a.lse + qrow : nullptr)
+                          : (lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
 template <bool FP8, bool PACKED, bool P_HILO>

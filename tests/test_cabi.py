@@ -260,6 +260,45 @@ def test_persistent_empty_batch_launches_nothing():
     assert _persist(B=0)[0] == 0
 
 
+def _persist_ex(opts, **kw):
+    a = dict(q_nope=0x20000, q_rope=0x30000, B=4, qps=1, H=64, ptr=0x40000, flat=0x48000, sink=None, scale=0.04,
+             ws=0x100000, ws_bytes=1 << 30, P=8, out=0x50000, lse=0x60000)
+    a.update(kw)
+    p = _pool()
+    rc = smd.lib().smd_sparse_mla_decode_persistent_ex(a["q_nope"], a["q_rope"], a["B"], a["qps"], a["H"],
+                                                       ctypes.byref(p), a["ptr"], a["flat"], a["sink"], a["scale"],
+                                                       a["ws"], a["ws_bytes"], a["P"], a["out"], a["lse"],
+                                                       ctypes.byref(opts) if opts is not None else None, None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("opts,msg", [
+    (smd._DecodeOptions(kernel=smd.KERNEL_WIDE), "SMD_KERNEL_AUTO"),
+    (smd._DecodeOptions(merge=2), "merge"),
+    (smd._DecodeOptions(merge=-1), "merge"),
+    (smd._DecodeOptions(reserved=(ctypes.c_int32 * 6)(0, 0, 1, 0, 0, 0)), "reserved"),
+])
+def test_persistent_ex_rejects_bad_options(opts, msg):
+    rc, err = _persist_ex(opts)
+    assert rc == -1 and msg in err, (rc, err)
+
+
+@pytest.mark.parametrize("merge", [smd.MERGE_AUTO, smd.MERGE_WORKSPACE])
+def test_persistent_ex_empty_batch_launches_nothing(merge):
+    assert _persist_ex(smd._DecodeOptions(merge=merge), B=0)[0] == 0
+    assert _persist_ex(None, B=0)[0] == 0
+
+
+def test_split_kv_rejects_merge_option():
+    """SMD_MERGE_* belongs to the persistent decode; the split-KV entry points
+    take SMD_MERGE_AUTO only."""
+    opts = smd._DecodeOptions(merge=smd.MERGE_WORKSPACE)
+    p = _pool()
+    rc = smd.lib().smd_sparse_mla_decode_ex(0x20000, 0x30000, 4, 64, 1, ctypes.byref(p), 0x40000, 100, 100, None,
+                                            0.04, 1, None, None, 0x50000, 0x60000, ctypes.byref(opts), None)
+    assert rc == -1 and "persistent" in smd.lib().smd_last_error().decode()
+
+
 def test_persistent_workspace_reset_rejects_null():
     assert smd.lib().smd_persistent_workspace_reset(None, 100, None) == -1
 

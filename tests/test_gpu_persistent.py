@@ -131,6 +131,39 @@ def test_long_sequence_many_pieces(gpu, H, kv_dtype, P):
     run_persistent(w, gpu, P)
 
 
+@pytest.mark.parametrize("qps,kv_dtype,P,B", [(4, "fp8", 16, 12), (1, "bf16", 9, 8), (2, "fp8", 40, 30),
+                                              (1, "fp8", 5, 1)])
+def test_register_merge_matches_workspace_merge(gpu, qps, kv_dtype, P, B):
+    """Wide row groups (H = 128): a split row group is merged either by the
+    piece that finds every other piece arrived, straight from its registers,
+    or from the workspace by the last to arrive; which one happens depends on
+    timing, so both must give the same bits.  Five launches of each way agree
+    bit for bit, and the outputs meet the oracle.  (B = 1, P = 5: one
+    sequence in five pieces, most of them finishing together.)"""
+    w = wl.ragged_workload("persist merge ways", B=B, q_per_seq=qps, H=128, kv_dtype=kv_dtype, pool_rows=8192,
+                           max_k=3000, zero_rows=0, seed=140 + P + qps)
+    if B == 1:
+        K = 2500
+        w.arrays["kv_indptr"] = np.array([0, K], dtype=np.int32)
+        w.arrays["kv_indices"] = np.random.default_rng(5).choice(8192, K, replace=False).astype(np.int32)
+    q_nope, q_rope, sink, pool, ptr, flat = _ragged_inputs(w, gpu)
+    ws = smd.PersistentWorkspace(128, qps, P, device=gpu)
+    first = None
+    for merge in ("auto", "workspace"):
+        for rep in range(5):
+            out, lse = _filled(w, gpu)
+            print(f"merge ways qps={qps} {kv_dtype} P={P} B={B} {merge} launch {rep}", flush=True)
+            smd.sparse_mla_decode_persistent(q_nope, q_rope, pool, ptr, flat, sink, w.softmax_scale, q_per_seq=qps,
+                                             workspace=ws, out=out, lse=lse, merge=merge)
+            torch.cuda.synchronize()
+            if first is None:
+                first = (out, lse)
+                continue
+            assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), f"{merge} {rep} differs (out)"
+            assert torch.equal(lse, first[1]), f"{merge} {rep} differs (lse)"
+    _check_against_oracle(w, first[0], first[1])
+
+
 def test_all_sequences_empty(gpu):
     w = wl.ragged_workload("persist empty", B=4, q_per_seq=2, H=16, kv_dtype="bf16", pool_rows=512, max_k=10,
                            zero_rows=4, seed=93)
@@ -275,6 +308,14 @@ def test_config5_full_size(gpu):
             continue
         assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), f"launch {rep} differs (out)"
         assert torch.equal(lse, first[1]), f"launch {rep} differs (lse)"
+    for rep in range(3):  # every split row group merged from the workspace: the same bits
+        out, lse = _filled(w, gpu)
+        print(f"config 5 full size P={P} workspace merge launch {rep}", flush=True)
+        smd.sparse_mla_decode_persistent(q_nope, q_rope, pool, ptr, flat, sink, w.softmax_scale, q_per_seq=4,
+                                         workspace=ws, out=out, lse=lse, merge="workspace")
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), first[0].view(torch.int16)), f"workspace merge {rep} differs (out)"
+        assert torch.equal(lse, first[1]), f"workspace merge {rep} differs (lse)"
     out, lse = first
     _check_plan(ws, a["kv_indptr"], P)
     ptr_np = a["kv_indptr"]
