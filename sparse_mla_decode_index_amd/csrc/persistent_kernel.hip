@@ -450,7 +450,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return PiecePtrs{base + (size_t)mq0 * kDim, base + (size_t)a.M * kDim + mq0};
       };
       const float sink_ln = a.sink ? a.sink[hq] : -INFINITY;
-      float scale, lse_v, w_own = 0.f, inv_l = 0.f;
+      float scale, lse_v;
       bool f32 = false;
       void *dst = a.out + qbase * kDim;
       float *lse_dst = (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr;
@@ -473,7 +473,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         __syncthreads();  // s_arrived is rewritten below
         if (merged) {
           __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");  // acquire the other pieces
-          merge_weights_wide(w, l_tot, sink_ln, part, pieces - 1, p - fp, tbl, w_own, inv_l, scale, lse_v);
+          merge_weights_wide(w, l_tot, sink_ln, part, pieces - 1, p - fp, tbl, scale, lse_v);
           if (threadIdx.x == 0) __hip_atomic_store(ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         } else {
           const OutScale sc = partial_scale(w.m_ref, l_tot);
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
       }
       if (merged)
-        store_rows_wide<true>(w, scale, false, dst, kDim, stage, part, lp - fp, p - fp, w_own, inv_l, tbl);
+        store_rows_wide<true>(w, scale, false, dst, kDim, stage, part, lp - fp, p - fp, tbl);
       else
         store_rows_wide<false>(w, scale, f32, dst, kDim, stage);
       if (lse_dst != nullptr) *lse_dst = lse_v;

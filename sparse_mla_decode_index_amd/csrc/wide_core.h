@@ -655,34 +655,37 @@ struct NoPieces {
 // slice:
 //   !MERGE: bf16 out = scale * O, or (f32) FP32 rows = scale * O (a split
 //           partial); scale belongs to this lane's row (lane % 32);
-//    MERGE: bf16 out = scale * o with o the merge of this piece (its partial
-//           O * inv_l, weight w_own, at position own_k of the span) and the n
-//           >= 1 other pieces part(0..n-1) (weight tbl[32 k + row]): per
-//           element, in span order from zero with one fused multiply-add per
-//           piece, the operations of merge_pieces_narrow, so a row group
-//           merged here and one merged from the workspace hold the same bits
-//           (merge_weights_wide gives the weights and scale = 1 / Z).
+//    MERGE: bf16 out = the merge of this piece and the n >= 1 other pieces
+//           part(0..n-1) of a split row group (merge_weights_wide gives the
+//           weights): this piece's partial is scale * O (scale = 1 / l_tot,
+//           the value its partial would hold) at position own_k of the span;
+//           for row r the other pieces' weights sit at tbl[32 k + r], this
+//           piece's at tbl[32 kRegMergeMax + r] and 1 / Z at
+//           tbl[32 (kRegMergeMax + 1) + r].  Per element, in span order from
+//           zero with one fused multiply-add per piece, then times 1 / Z: the
+//           operations of merge_pieces_narrow, so a row group merged here and
+//           one merged from the workspace hold the same bits.
 // dst points at dim 0 of the wave's first row, rows row_stride elements
 // apart (uint16_t for bf16, float for FP32); part(k).o points at dim 0 of the
 // wave's first row in the k-th other piece's FP32 partial (rows kDim floats
 // apart).  Four passes of 128 dims: the wave's part goes to the stage in fp32
-// in the accumulator layout (lane (q, u) holds row q), and the rows leave in
-// 16-byte stores: FP32 lane (q, u) takes rows 2k + u, dims 4q..4q+3 of the
-// pass; bf16 lane l takes rows 4k + l / 16, dims 8 (l mod 16) .. +7.  A merge
-// loads each piece's 128 dims row-wise and turns them to the accumulator
-// layout through the stage; the first piece of the next pass is loaded
-// before this pass's stores go out, since a load waits for every store
-// issued before it.  Every LDS read of a phase is issued before its first
-// use, and global addresses are a wave-uniform row base plus a 32-bit lane
-// offset recomputed in each pass from a fresh lane id: 64-bit per-lane
-// offsets kept across passes get spilled, and every reload waits for all the
-// stores in flight.  (The passes are unrolled: acc may only be indexed by
-// constants.)
+// in the accumulator layout (lane (q, u) holds row q); a merge then works
+// row-wise (lane (q, u): rows 2k + u, dims 4q..4q+3 of the pass), loading the
+// other pieces' rows in that layout, and writes its sums back to the stage;
+// the rows leave in 16-byte stores: FP32 lane (q, u) takes rows 2k + u, dims
+// 4q..4q+3; bf16 lane l takes rows 4k + l / 16, dims 8 (l mod 16) .. +7.  The
+// first other piece's rows of the next pass are loaded before this pass's
+// stores go out (a load waits for every store issued before it), once this
+// pass's sums no longer need the registers.  Every LDS read of a phase is
+// issued before its first use, and global addresses are a wave-uniform row
+// base plus a 32-bit lane offset recomputed in each pass from a fresh lane
+// id: 64-bit per-lane offsets kept across passes get spilled, and every
+// reload waits for all the stores in flight.  (The passes are unrolled: acc
+// may only be indexed by constants.)
 template <bool MERGE, class Part = NoPieces>
 __device__ __forceinline__ void store_rows_wide(const WideState &w, float scale, bool f32, void *dst,
                                                 int64_t row_stride, uint8_t SMD_LDS *stage, Part part = Part(),
-                                                int n = 0, int own_k = 0, float w_own = 0.f, float inv_l = 0.f,
-                                                const float SMD_LDS *tbl = nullptr) {
+                                                int n = 0, int own_k = 0, const float SMD_LDS *tbl = nullptr) {
   auto piece_loads = [&](int pass, int j, f32x4 (&v)[16]) {
     const int lane = opaque_lane();
     const uint32_t poff = (uint32_t)((lane >> 5) * kDim + 128 * pass + 4 * (lane & 31)) * 4;
@@ -696,50 +699,46 @@ __device__ __forceinline__ void store_rows_wide(const WideState &w, float scale,
   for (int pass = 0; pass < 4; ++pass) {
     const int lane = opaque_lane();
     const int q = lane & 31, u = lane >> 5;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)  // i = 4dd + b: dims 32dd + 8b + 4u of the pass, chunk 8dd + 2b + u
+      *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u)) =
+          wide_quad(w.acc[4 * pass + (i >> 2)], i & 3) * scale;
     if constexpr (MERGE) {
       f32x4 o[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto add_own = [&]() {
+      for (int k = 0; k < 16; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+      auto add = [&](const f32x4 (&v)[16], const float SMD_LDS *wt) {  // o += wt[row] * v, row 2k + u
+        float c[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const f32x4 t = wide_quad(w.acc[4 * pass + (i >> 2)], i & 3) * inv_l;
+        for (int k = 0; k < 16; ++k) c[k] = wt[2 * k + u];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) o[i][e] = __builtin_fmaf(w_own, t[e], o[i][e]);
+        for (int k = 0; k < 16; ++k) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[k][e] = __builtin_fmaf(c[k], v[k][e], o[k][e]);
         }
       };
+      auto add_own = [&]() {
+        f32x4 t[16];
+#pragma unroll
+        for (int k = 0; k < 16; ++k) t[k] = *(const f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q));
+        add(t, tbl + kRegMergeMax * 32);
+      };
+      if (own_k == 0) add_own();
+      add(pre, tbl);  // the first other piece (the registers of pre are free after this)
 #pragma unroll 1
-      for (int j = 0; j < n; ++j) {
+      for (int j = 1; j < n; ++j) {
         if (j == own_k) add_own();
         f32x4 v[16];
-        if (j == 0) {
-#pragma unroll
-          for (int k = 0; k < 16; ++k) v[k] = pre[k];
-        } else {
-          piece_loads(pass, j, v);
-        }
-#pragma unroll
-        for (int k = 0; k < 16; ++k) *(f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q)) = v[k];
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-          v[i] = *(const f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u));
-        if (j == 0 && pass < 3) piece_loads(pass + 1, 0, pre);
-        const float c = tbl[j * 32 + q];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[i][e] = __builtin_fmaf(c, v[i][e], o[i][e]);
-        }
+        piece_loads(pass, j, v);
+        add(v, tbl + j * 32);
       }
       if (own_k == n) add_own();
+      if (pass < 3) piece_loads(pass + 1, 0, pre);
+      float fin[16];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)  // i = 4dd + b: dims 32dd + 8b + 4u of the pass, chunk 8dd + 2b + u
-        *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u)) = o[i] * scale;
-    } else {
+      for (int k = 0; k < 16; ++k) fin[k] = tbl[(kRegMergeMax + 1) * 32 + 2 * k + u];
 #pragma unroll
-      for (int i = 0; i < 16; ++i)
-        *(f32x4 SMD_LDS *)(stage + stage_off(q, 8 * (i >> 2) + 2 * (i & 3) + u)) =
-            wide_quad(w.acc[4 * pass + (i >> 2)], i & 3) * scale;
+      for (int k = 0; k < 16; ++k) *(f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q)) = o[k] * fin[k];
     }
     char *drow = (char *)dst;
     if (!MERGE && f32) {
@@ -783,15 +782,15 @@ __device__ __forceinline__ void store_rows_wide(const WideState &w, float scale,
 // (aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode
 // kernel", Summary part 1: pieces combine by their log-sum-exp, the sink
 // once).  The n <= kRegMergeMax other pieces are part(0..n-1) in span order
-// and this one sits at position own_k.  Leaves the other pieces' weights in
-// tbl[32 k + row] (tbl holds kRegMergeMax * 32 floats), and for this lane's
-// row its weight in w_own, its partial scale in inv_l, 1 / Z in fin and the
-// lse in lse_out.  An empty merge (no piece holds a row and no sink) gives
-// zero weights, fin = 0 and lse = -inf.
+// and this one sits at position own_k.  Leaves, for row r, the other pieces'
+// weights in tbl[32 k + r], this piece's in tbl[32 kRegMergeMax + r] and 1 / Z
+// in tbl[32 (kRegMergeMax + 1) + r] (tbl holds (kRegMergeMax + 2) * 32
+// floats), and for this lane's row its partial scale in inv_l and the lse in
+// lse_out.  An empty merge (no piece holds a row and no sink) gives zero
+// weights and 1 / Z = 0 (zero output) and lse = -inf.
 template <class Part>
 __device__ __forceinline__ void merge_weights_wide(const WideState &w, float l_tot, float sink_ln, Part part, int n,
-                                                   int own_k, float SMD_LDS *tbl, float &w_own, float &inv_l,
-                                                   float &fin, float &lse_out) {
+                                                   int own_k, float SMD_LDS *tbl, float &inv_l, float &lse_out) {
   const int lane = opaque_lane();
   const int q = lane & 31, u = lane >> 5;
   const OutScale ps = partial_scale(w.m_ref, l_tot);
@@ -802,9 +801,7 @@ __device__ __forceinline__ void merge_weights_wide(const WideState &w, float l_t
   float mx = fmaxf(sink_ln, ps.lse);
 #pragma unroll
   for (int k = 0; k < kRegMergeMax; ++k) mx = fmaxf(mx, lo[k]);
-  float c[kRegMergeMax];
-  fin = 0.f;
-  w_own = 0.f;
+  float c[kRegMergeMax], fin = 0.f, w_own = 0.f;
   lse_out = -INFINITY;
 #pragma unroll
   for (int k = 0; k < kRegMergeMax; ++k) c[k] = 0.f;
@@ -825,6 +822,8 @@ __device__ __forceinline__ void merge_weights_wide(const WideState &w, float l_t
   if (u == 0) {
 #pragma unroll
     for (int k = 0; k < kRegMergeMax; ++k) tbl[k * 32 + q] = c[k];
+    tbl[kRegMergeMax * 32 + q] = w_own;
+    tbl[(kRegMergeMax + 1) * 32 + q] = fin;
   }
 }
 
