@@ -199,8 +199,8 @@ def summarize_trace(path: str) -> None:
                       f"median {v[len(v) // 2]:9.3f} us, min {v[0]:9.3f} us, max {v[-1]:9.3f} us")
 
 
-KERNEL_SOURCE = {"smd::decode_kernel": "decode_kernels.hip", "smd::persistent_kernel": "persistent_kernel.hip",
-                 "smd::write_kv_fp8_kernel": "writer_kernel.hip"}
+KERNEL_SOURCE = {"smd::decode_kernel": "decode_kernels.hip", "smd::decode_wide_kernel": "wide_kernel.hip",
+                 "smd::persistent_kernel": "persistent_kernel.hip", "smd::write_kv_fp8_kernel": "writer_kernel.hip"}
 
 
 def kernel_sources_sha(kernel: str) -> str:
@@ -539,8 +539,9 @@ def main():
         def merge_only():
             smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
-        kernel_name = "smd::decode_kernel"
-        cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv " + (args.kernel or "auto")})
+        family = smd.decode_kernel_choice(w.num_tokens, H, qps, s, two_source=two, kernel=args.kernel)
+        kernel_name = "smd::decode_wide_kernel" if family == "wide" else "smd::decode_kernel"
+        cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv " + family})
         if two:
             cfg.update({"main_topk": w.arrays["main_indices"].shape[1], "swa_window": w.arrays["swa_indices"].shape[1],
                         "sources": 2})

@@ -200,8 +200,8 @@ int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t 
  *   SMD_KERNEL_WIDE    128 query rows per workgroup, 4 waves of 32 rows on
  *                      32x32 MFMAs sharing every gathered row (M a multiple of
  *                      128, one source).
- * SMD_KERNEL_AUTO picks WIDE when it fits and the grid, (num_tokens /
- * q_per_seq) * num_splits workgroups per group of 128 rows, is at least 128;
+ * SMD_KERNEL_AUTO picks WIDE when it fits and its grid, (num_tokens /
+ * q_per_seq) * num_splits * (M / 128) workgroups, is at least 128;
  * otherwise PAIRS when M is a multiple of 32 and, with W = (num_tokens /
  * q_per_seq) * num_splits * (M / 32), 7 * ceil(W / 256) < 4 * ceil(2W / 256);
  * otherwise ROWS16.  A named family that does not fit the shape is
@@ -229,6 +229,14 @@ enum {
   SMD_MERGE_AUTO = 0,
   SMD_MERGE_WORKSPACE = 1
 };
+
+/* The kernel family a split-KV call with these shapes runs (SMD_KERNEL_ROWS16,
+ * SMD_KERNEL_PAIRS or SMD_KERNEL_WIDE): `requested` is options->kernel, and
+ * SMD_KERNEL_AUTO applies the rule above.  two_source != 0 for the two-source
+ * entry points.  SMD_ERR_UNSUPPORTED for a named family that does not fit,
+ * SMD_ERR_INVALID_ARG for bad shapes.  Host only. */
+int32_t smd_decode_kernel_choice(int32_t num_tokens, int32_t num_heads, int32_t q_per_seq, int32_t num_splits,
+                                 int32_t two_source, int32_t requested);
 
 /* Options of the _ex entry points; NULL means all defaults (zero). */
 typedef struct smd_decode_options {

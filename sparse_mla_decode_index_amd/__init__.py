@@ -160,6 +160,8 @@ def lib() -> ctypes.CDLL:
     L.smd_sparse_mla_decode_persistent_ex.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, vp, vp,
                                                       f32, vp, ctypes.c_size_t, i32, vp, vp,
                                                       ctypes.POINTER(_DecodeOptions), vp]
+    L.smd_decode_kernel_choice.restype = ctypes.c_int32
+    L.smd_decode_kernel_choice.argtypes = [i32, i32, i32, i32, i32, i32]
     _lib = L
     return L
 
@@ -253,6 +255,16 @@ class KVPool:
 # ----------------------------------------------------------------------------
 # planner
 # ----------------------------------------------------------------------------
+def decode_kernel_choice(num_tokens: int, num_heads: int, q_per_seq: int = 1, num_splits: int = 1,
+                         two_source: bool = False, kernel=None) -> str:
+    """The kernel family ("rows16", "pairs" or "wide") a split-KV call with
+    these shapes runs (smd.h smd_decode_kernel_choice)."""
+    k = 0 if kernel is None else (_KERNELS[kernel] if isinstance(kernel, str) else int(kernel))
+    rc = lib().smd_decode_kernel_choice(num_tokens, num_heads, q_per_seq, num_splits, int(bool(two_source)), k)
+    _check("smd_decode_kernel_choice", rc)
+    return {KERNEL_ROWS16: "rows16", KERNEL_PAIRS: "pairs", KERNEL_WIDE: "wide"}[rc]
+
+
 def plan_num_kv_splits(num_seqs: int, num_heads: int, kv_len: int, q_per_seq: int = 1,
                        kv_dtype: int = KV_BF16, num_cus: int = 0,
                        model: Optional[PlanModel] = None) -> int:

@@ -107,7 +107,8 @@ static bool pairs_pay(int32_t M, int64_t units) {
 // The wide kernel (128 query rows per workgroup on 32x32 MFMAs) shares each
 // gathered row among 128 query rows; it needs M % 128 == 0 and one source,
 // and it pays once its grid fills at least half the GPU.
-static bool wide_fits(int32_t M, bool two) { return M % 128 == 0 && !two; }
+constexpr int32_t kWideRowsPerGroup = 128;
+static bool wide_fits(int32_t M, bool two) { return M % kWideRowsPerGroup == 0 && !two; }
 
 // Kernel of a split-KV call: the caller's choice when it names one (checked
 // against the shape), else the rule above.  Returns 0 for an impossible choice.
@@ -118,13 +119,31 @@ static int pick_kernel(int32_t requested, int32_t M, int64_t units, bool two) {
     case SMD_KERNEL_WIDE: return wide_fits(M, two) ? kKernWide : 0;
     default: break;
   }
-  if (wide_fits(M, two) && units >= 128) return kKernWide;
+  if (wide_fits(M, two) && units * (M / kWideRowsPerGroup) >= 128) return kKernWide;  // the grid
   return pairs_pay(M, units) ? kKernPairs : kKernRows16;
 }
 
 }  // namespace smd
 
 using namespace smd;
+
+extern "C" int32_t smd_decode_kernel_choice(int32_t num_tokens, int32_t num_heads, int32_t q_per_seq,
+                                            int32_t num_splits, int32_t two_source, int32_t requested) {
+  static const char *fn = "smd_decode_kernel_choice";
+  g_err[0] = 0;
+  if (num_tokens < 0 || num_heads <= 0 || q_per_seq < 1 || num_splits < 1 || num_tokens % q_per_seq != 0 ||
+      requested < SMD_KERNEL_AUTO || requested > SMD_KERNEL_WIDE) {
+    set_error("%s: bad shapes or kernel choice", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  const int32_t M = num_heads * q_per_seq;
+  const int k = pick_kernel(requested, M, (int64_t)(num_tokens / q_per_seq) * num_splits, two_source != 0);
+  if (k == 0) {
+    set_error("%s: kernel choice %d does not fit M = %d query rows per index row", fn, requested, M);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  return k == kKernWide ? SMD_KERNEL_WIDE : k == kKernPairs ? SMD_KERNEL_PAIRS : SMD_KERNEL_ROWS16;
+}
 
 extern "C" const char *smd_last_error(void) { return g_err; }
 

@@ -422,3 +422,31 @@ def test_two_source_null_swa_pool():
 def test_two_source_empty_launches_nothing():
     assert _two(km=0, ks=0, mi=None, si=None)[0] == 0
     assert _two(T=0)[0] == 0
+
+
+@pytest.mark.parametrize("T,H,qps,s,two,req,want", [
+    (32, 128, 1, 4, False, None, "wide"),      # 128 workgroups of 128 rows
+    (32, 128, 1, 2, False, None, "pairs"),     # 64 units: below the wide threshold
+    (8, 64, 1, 1, False, None, "rows16"),      # M = 64: no wide; 16 pair workgroups do not pay
+    (256, 128, 4, 1, False, None, "wide"),     # MTP4: M = 512, 64 rows x 4 groups
+    (32, 128, 1, 8, True, None, "pairs"),      # two sources never take the wide kernel
+    (32, 128, 1, 1, False, "rows16", "rows16"),
+    (4, 64, 1, 1, False, "pairs", "pairs"),
+])
+def test_decode_kernel_choice(T, H, qps, s, two, req, want):
+    """smd_decode_kernel_choice applies the documented rule: wide when 128
+    divides M, one source and at least 128 units; else pairs when they pay;
+    else rows16; a named family is returned as is when it fits."""
+    assert smd.decode_kernel_choice(T, H, qps, s, two_source=two, kernel=req) == want
+
+
+@pytest.mark.parametrize("args,code", [
+    ((32, 64, 1, 1, 0, smd.KERNEL_WIDE), -2),   # M = 64 cannot take the wide kernel
+    ((32, 128, 1, 1, 1, smd.KERNEL_WIDE), -2),  # nor two sources
+    ((32, 16, 1, 1, 0, smd.KERNEL_PAIRS), -2),  # M = 16: no pairs
+    ((3, 16, 2, 1, 0, 0), -1),                  # tokens not a multiple of q_per_seq
+    ((4, 16, 1, 0, 0, 0), -1),                  # no split
+    ((4, 16, 1, 1, 0, 9), -1),                  # unknown family
+])
+def test_decode_kernel_choice_rejects(args, code):
+    assert smd.lib().smd_decode_kernel_choice(*args) == code
