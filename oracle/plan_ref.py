@@ -2,9 +2,9 @@
 
 * ``num_kv_splits`` -- the host split-count cost model.  The aiter page
   "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode kernel"
-  (Summary, part 1) states what it minimises: workgroup waves times per-wave
-  KV time, plus the partial-write / stage-2 cost of splitting, computed on the
-  host from (num_seqs, num_heads, kv_len) only.  The vLLM page "[ROCm][DSV4]
+  (Summary, part 1) prices a split count by its rounds of workgroups times the
+  KV time of one round, plus what splitting adds (writing the partials and
+  merging them), from (num_seqs, num_heads, kv_len) alone, on the host.  The vLLM page "[ROCm][DSV4]
   [Perf] Optimize Triton sparse-MLA decode on gfx950" (Design) caps short
   workloads at four splits and allows up to 32 for long contexts.  The fitted
   coefficients are not printed on either page; here they are an explicit
