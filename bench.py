@@ -517,7 +517,7 @@ def main():
         R = w.num_index_rows
 
         def plan():
-            return args.splits or smd.plan_num_kv_splits(R, H, K, qps, kvd)
+            return args.splits or smd.plan_num_kv_splits(R, H, K, qps, kvd, two_source=two)
 
         s = plan()
         po = torch.empty((T, H, s, 512), dtype=torch.float32, device=dev)
@@ -539,7 +539,7 @@ def main():
         def merge_only():
             smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
-        family = smd.decode_kernel_choice(w.num_tokens, H, qps, s, two_source=two, kernel=args.kernel)
+        family = smd.decode_kernel_choice(w.num_tokens, H, qps, s, K, kvd, two_source=two, kernel=args.kernel)
         kernel_name = "smd::decode_wide_kernel" if family == "wide" else "smd::decode_kernel"
         cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv " + family})
         if two:

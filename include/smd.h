@@ -109,9 +109,11 @@ typedef struct smd_kv_pool {
  * that grows with the rounds of workgroups the GPU must run and with the
  * extra partial traffic and merge that each split adds.  This library's
  * formula, all times in picoseconds (the terms are ours; the page prints no
- * formula or coefficients): a decode workgroup owns rows_per_wg query rows of
- * one index row and one split, and its waves_per_wg waves share the split's
- * positions in steps of 16.
+ * formula or coefficients), prices its two kinds of split-KV workgroup:
+ *
+ * Narrow (SMD_KERNEL_ROWS16 / PAIRS): a workgroup owns rows_per_wg query rows
+ * of one index row and one split, and its waves_per_wg waves share the
+ * split's positions in steps of 16.
  *
  *   M         = num_heads * q_per_seq,   G = ceil(M / rows_per_wg)
  *   slots     = num_cus * wg_per_cu
@@ -119,13 +121,24 @@ typedef struct smd_kv_pool {
  *   waves(s)  = ceil(wgs(s) / slots),    busy(s) = min(wgs(s), slots)
  *   chunk(s)  = roundup(ceil(kv_len / s), 64)   (the split length)
  *   steps(s)  = ceil(ceil(min(chunk(s), kv_len) / 16) / waves_per_wg)
- *   cost(s)   = waves(s) * (fixed + steps(s) * (step + floor(step_load * busy(s) / slots)))
- *             + (s > 1) * (merge + part * num_seqs * M * s)
+ *   tail(s)   = (s > 1) * (merge + part * num_seqs * M * s)
+ *   narrow(s) = waves(s) * (fixed + steps(s) * (step + floor(step_load * busy(s) / slots))) + tail(s)
  *
+ * Wide (SMD_KERNEL_WIDE), when wide_rows > 0, M % wide_rows == 0 and the call
+ * has one source: a workgroup owns wide_rows query rows and walks the split in
+ * tiles of wide_tile positions, one workgroup per CU.
+ *
+ *   wgs_w(s)  = num_seqs * (M / wide_rows) * s
+ *   waves_w(s)= ceil(wgs_w(s) / num_cus),   busy_w(s) = min(wgs_w(s), num_cus)
+ *   tiles(s)  = ceil(min(chunk(s), kv_len) / wide_tile)
+ *   tile      = wide_tile_fp8 for an fp8 pool, else wide_tile
+ *   wide(s)   = waves_w(s) * (wide_fixed + tiles(s) * (tile + floor(wide_tile_load * busy_w(s) / num_cus)))
+ *               + tail(s)
+ *
+ * cost(s) = min(narrow(s), wide(s)) (narrow alone when wide does not apply).
  * s ranges over [1, min(cap, ceil(kv_len / 64))] with cap = short_cap when
  * kv_len < long_kv, else long_cap (both <= SMD_MAX_SPLITS); the smallest s of
- * minimum cost wins.  bf16 and fp8 pools run the same kernel and share the
- * coefficients.
+ * minimum cost wins, and its family is wide when wide(s) < narrow(s).
  */
 typedef struct smd_plan_model {
   int64_t fixed_ps;     /* per workgroup wave: prologue, wave merge, epilogue */
@@ -139,6 +152,12 @@ typedef struct smd_plan_model {
   int32_t short_cap;    /* split cap when kv_len < long_kv                    */
   int32_t long_cap;     /* split cap otherwise                                */
   int32_t long_kv;      /* threshold between the two caps                     */
+  int32_t wide_rows;    /* query rows per wide workgroup; 0: no wide family   */
+  int32_t wide_tile;    /* positions per wide tile                            */
+  int64_t wide_fixed_ps;     /* per wide workgroup round                      */
+  int64_t wide_tile_ps;      /* per wide tile, bf16 pool, GPU otherwise idle  */
+  int64_t wide_tile_fp8_ps;  /* per wide tile, fp8 pool, GPU otherwise idle   */
+  int64_t wide_tile_load_ps; /* added per wide tile with every CU busy        */
 } smd_plan_model;
 
 /*
@@ -158,6 +177,18 @@ int smd_plan_num_kv_splits(int32_t num_seqs, int32_t num_heads, int32_t q_per_se
 int smd_plan_num_kv_splits_model(int32_t num_seqs, int32_t num_heads, int32_t q_per_seq,
                                  int32_t kv_len, int32_t kv_dtype, int32_t num_cus,
                                  const smd_plan_model *model);
+
+/*
+ * The planner with the kernel family it priced: returns s like
+ * smd_plan_num_kv_splits_model and, when `kernel` is not NULL, stores
+ * SMD_KERNEL_WIDE if the wide family won at that s, else SMD_KERNEL_AUTO (a
+ * narrow family; smd_decode_kernel_choice names which).  two_source != 0
+ * prices the two-source entry points, which have no wide family.  model ==
+ * NULL uses the built-in coefficients.  Host only, pure.
+ */
+int smd_plan_decode(int32_t num_seqs, int32_t num_heads, int32_t q_per_seq, int32_t kv_len,
+                    int32_t kv_dtype, int32_t num_cus, int32_t two_source, const smd_plan_model *model,
+                    int32_t *kernel);
 
 /* Copy the library's built-in coefficient table into *model. */
 int smd_plan_default_model(smd_plan_model *model);
@@ -200,12 +231,13 @@ int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t 
  *   SMD_KERNEL_WIDE    128 query rows per workgroup, 4 waves of 32 rows on
  *                      32x32 MFMAs sharing every gathered row (M a multiple of
  *                      128, one source).
- * SMD_KERNEL_AUTO picks WIDE when it fits and its grid, (num_tokens /
- * q_per_seq) * num_splits * (M / 128) workgroups, is at least 128;
- * otherwise PAIRS when M is a multiple of 32 and, with W = (num_tokens /
- * q_per_seq) * num_splits * (M / 32), 7 * ceil(W / 256) < 4 * ceil(2W / 256);
- * otherwise ROWS16.  A named family that does not fit the shape is
- * SMD_ERR_UNSUPPORTED.
+ * SMD_KERNEL_AUTO picks WIDE when it fits and the built-in planner model
+ * prices it below the narrow kernels at the call's split count (wide(s) <
+ * narrow(s) in the model above, with num_seqs = num_tokens / q_per_seq and
+ * kv_len = the index count); otherwise PAIRS when M is a multiple of 32 and,
+ * with W = (num_tokens / q_per_seq) * num_splits * (M / 32), 7 * ceil(W /
+ * 256) < 4 * ceil(2W / 256); otherwise ROWS16.  A named family that does not
+ * fit the shape is SMD_ERR_UNSUPPORTED.
  */
 enum {
   SMD_KERNEL_AUTO = 0,
@@ -232,11 +264,12 @@ enum {
 
 /* The kernel family a split-KV call with these shapes runs (SMD_KERNEL_ROWS16,
  * SMD_KERNEL_PAIRS or SMD_KERNEL_WIDE): `requested` is options->kernel, and
- * SMD_KERNEL_AUTO applies the rule above.  two_source != 0 for the two-source
- * entry points.  SMD_ERR_UNSUPPORTED for a named family that does not fit,
- * SMD_ERR_INVALID_ARG for bad shapes.  Host only. */
+ * SMD_KERNEL_AUTO applies the rule above.  kv_len is the index count per index
+ * row (topk), kv_dtype the pool's SMD_KV_*, two_source != 0 for the two-source
+ * entry points.  SMD_ERR_UNSUPPORTED for a named family that does not fit or
+ * an unknown kv_dtype, SMD_ERR_INVALID_ARG for bad shapes.  Host only. */
 int32_t smd_decode_kernel_choice(int32_t num_tokens, int32_t num_heads, int32_t q_per_seq, int32_t num_splits,
-                                 int32_t two_source, int32_t requested);
+                                 int32_t kv_len, int32_t kv_dtype, int32_t two_source, int32_t requested);
 
 /* Options of the _ex entry points; NULL means all defaults (zero). */
 typedef struct smd_decode_options {

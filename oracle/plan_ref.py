@@ -1,15 +1,18 @@
 """Integer plans of sparse MLA decode -- test infrastructure only.
 
-* ``num_kv_splits`` -- the host split-count cost model.  The aiter page
-  "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode kernel"
-  (Summary, part 1) prices a split count by its rounds of workgroups times the
-  KV time of one round, plus what splitting adds (writing the partials and
-  merging them), from (num_seqs, num_heads, kv_len) alone, on the host.  The vLLM page "[ROCm][DSV4]
-  [Perf] Optimize Triton sparse-MLA decode on gfx950" (Design) caps short
-  workloads at four splits and allows up to 32 for long contexts.  The fitted
-  coefficients are not printed on either page; here they are an explicit
-  argument, so the formula is pinned while the library's fitted values are
-  parity unpinned.
+* ``num_kv_splits`` / ``plan_decode`` -- the host split-count cost model.  The
+  aiter page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode
+  kernel" (Summary, part 1) prices a split count by its rounds of workgroups
+  times the KV time of one round, plus what splitting adds (writing the
+  partials and merging them), from (num_seqs, num_heads, kv_len) alone, on
+  the host.  The library has two kinds of decode workgroup (narrow: 16 query
+  rows; wide: 128 query rows sharing each gathered row), so the modelled time
+  of a split count is that of the cheaper kind, and the plan also names which
+  kind won.  The vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
+  decode on gfx950" (Design) caps short workloads at four splits and allows
+  up to 32 for long contexts.  The fitted coefficients are not printed on
+  either page; here they are an explicit argument, so the formula is pinned
+  while the library's fitted values are parity unpinned.
 * ``split_bounds`` lives in ``oracle.ref`` (it defines the partial semantics).
 """
 from __future__ import annotations
@@ -37,6 +40,12 @@ class PlanModel:
     short_cap: int
     long_cap: int
     long_kv: int
+    wide_rows: int = 0
+    wide_tile: int = 32
+    wide_fixed_ps: int = 0
+    wide_tile_ps: int = 0
+    wide_tile_fp8_ps: int = 0
+    wide_tile_load_ps: int = 0
 
 
 def split_cost(s: int, num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, num_cus: int,
@@ -66,23 +75,64 @@ def split_cost(s: int, num_seqs: int, num_heads: int, q_per_seq: int, kv_len: in
     return cost
 
 
-def num_kv_splits(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv_dtype: int, num_cus: int,
-                  model: PlanModel) -> int:
-    """argmin of ``split_cost`` over s = 1 .. min(cap, ceil(kv_len / 64)), cap =
-    short_cap below long_kv indices, long_cap from there on; ties keep the
-    smaller s.  Empty problems plan one split; kv_dtype does not enter the cost."""
+def wide_split_cost(s: int, num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv_dtype: int,
+                    num_cus: int, model: PlanModel) -> int | None:
+    """Modelled picoseconds of s splits on the wide workgroups, or None where
+    they do not apply (wide_rows == 0 or M not a multiple of wide_rows):
+
+        waves_w(s) * (wide_fixed + tiles(s) * (tile + floor(wide_tile_load * busy_w(s) / cus)))
+          + [s > 1] * (merge + part * num_seqs * M * s)
+
+    one workgroup per CU: wgs_w(s) = num_seqs * (M / wide_rows) * s,
+    waves_w(s) = ceil(wgs_w(s) / cus), busy_w(s) = min(wgs_w(s), cus);
+    tiles(s) = ceil(min(chunk(s), kv_len) / wide_tile) with chunk(s) as in
+    ``split_cost``; tile = wide_tile_fp8 for kv_dtype 1 (fp8), else wide_tile."""
+    M = num_heads * q_per_seq
+    if model.wide_rows <= 0 or M % model.wide_rows != 0:
+        return None
+    cus = num_cus if num_cus > 0 else 256
+    wgs = num_seqs * (M // model.wide_rows) * s
+    waves = _cdiv(wgs, cus)
+    busy = min(wgs, cus)
+    chunk = _cdiv(_cdiv(kv_len, s), SPLIT_ALIGN) * SPLIT_ALIGN
+    tiles = _cdiv(min(chunk, kv_len), model.wide_tile)
+    tile = model.wide_tile_fp8_ps if kv_dtype == 1 else model.wide_tile_ps
+    cost = waves * (model.wide_fixed_ps + tiles * (tile + model.wide_tile_load_ps * busy // cus))
+    if s > 1:
+        cost += model.merge_ps + model.part_ps * num_seqs * M * s
+    return cost
+
+
+def plan_decode(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv_dtype: int, num_cus: int,
+                model: PlanModel, two_source: bool = False) -> tuple[int, bool]:
+    """(s, wide): s is the argmin of min(``split_cost``, ``wide_split_cost``)
+    over s = 1 .. min(cap, ceil(kv_len / 64)), cap = short_cap below long_kv
+    indices, long_cap from there on; ties keep the smaller s.  wide says the
+    wide cost was strictly below the narrow one at that s.  A two-source call
+    has no wide workgroups.  Empty problems plan (1, False)."""
     if min(num_seqs, num_heads, q_per_seq, kv_len) < 0:
         raise ValueError("negative size")
     if num_seqs == 0 or kv_len == 0 or num_heads == 0 or q_per_seq == 0:
-        return 1
+        return 1, False
     cap = model.short_cap if kv_len < model.long_kv else model.long_cap
     cap = min(cap, _cdiv(kv_len, SPLIT_ALIGN))
-    best_s, best = 1, None
+    best_s, best, best_wide = 1, None, False
     for s in range(1, cap + 1):
         cost = split_cost(s, num_seqs, num_heads, q_per_seq, kv_len, num_cus, model)
+        wide = False
+        if not two_source:
+            cw = wide_split_cost(s, num_seqs, num_heads, q_per_seq, kv_len, kv_dtype, num_cus, model)
+            if cw is not None and cw < cost:
+                cost, wide = cw, True
         if best is None or cost < best:
-            best, best_s = cost, s
-    return best_s
+            best, best_s, best_wide = cost, s, wide
+    return best_s, best_wide
+
+
+def num_kv_splits(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv_dtype: int, num_cus: int,
+                  model: PlanModel) -> int:
+    """The split count of ``plan_decode`` for a one-source call."""
+    return plan_decode(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype, num_cus, model)[0]
 
 
 # ----------------------------------------------------------------------------

@@ -96,6 +96,12 @@ class PlanModel(ctypes.Structure):
         ("short_cap", ctypes.c_int32),
         ("long_cap", ctypes.c_int32),
         ("long_kv", ctypes.c_int32),
+        ("wide_rows", ctypes.c_int32),
+        ("wide_tile", ctypes.c_int32),
+        ("wide_fixed_ps", ctypes.c_int64),
+        ("wide_tile_ps", ctypes.c_int64),
+        ("wide_tile_fp8_ps", ctypes.c_int64),
+        ("wide_tile_load_ps", ctypes.c_int64),
     ]
 
 
@@ -119,6 +125,9 @@ def lib() -> ctypes.CDLL:
     L.smd_plan_num_kv_splits.argtypes = [i32, i32, i32, i32, i32, i32]
     L.smd_plan_num_kv_splits_model.restype = ctypes.c_int
     L.smd_plan_num_kv_splits_model.argtypes = [i32, i32, i32, i32, i32, i32, ctypes.POINTER(PlanModel)]
+    L.smd_plan_decode.restype = ctypes.c_int
+    L.smd_plan_decode.argtypes = [i32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(PlanModel),
+                                  ctypes.POINTER(i32)]
     L.smd_plan_default_model.restype = ctypes.c_int
     L.smd_plan_default_model.argtypes = [ctypes.POINTER(PlanModel)]
     L.smd_partials_bytes.restype = ctypes.c_size_t
@@ -161,7 +170,7 @@ def lib() -> ctypes.CDLL:
                                                       f32, vp, ctypes.c_size_t, i32, vp, vp,
                                                       ctypes.POINTER(_DecodeOptions), vp]
     L.smd_decode_kernel_choice.restype = ctypes.c_int32
-    L.smd_decode_kernel_choice.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.smd_decode_kernel_choice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     _lib = L
     return L
 
@@ -256,26 +265,35 @@ class KVPool:
 # planner
 # ----------------------------------------------------------------------------
 def decode_kernel_choice(num_tokens: int, num_heads: int, q_per_seq: int = 1, num_splits: int = 1,
-                         two_source: bool = False, kernel=None) -> str:
+                         kv_len: int = 0, kv_dtype: int = KV_BF16, two_source: bool = False, kernel=None) -> str:
     """The kernel family ("rows16", "pairs" or "wide") a split-KV call with
-    these shapes runs (smd.h smd_decode_kernel_choice)."""
+    these shapes runs (smd.h smd_decode_kernel_choice); kv_len is the index
+    count per index row."""
     k = 0 if kernel is None else (_KERNELS[kernel] if isinstance(kernel, str) else int(kernel))
-    rc = lib().smd_decode_kernel_choice(num_tokens, num_heads, q_per_seq, num_splits, int(bool(two_source)), k)
+    rc = lib().smd_decode_kernel_choice(num_tokens, num_heads, q_per_seq, num_splits, kv_len, kv_dtype,
+                                        int(bool(two_source)), k)
     _check("smd_decode_kernel_choice", rc)
     return {KERNEL_ROWS16: "rows16", KERNEL_PAIRS: "pairs", KERNEL_WIDE: "wide"}[rc]
 
 
 def plan_num_kv_splits(num_seqs: int, num_heads: int, kv_len: int, q_per_seq: int = 1,
                        kv_dtype: int = KV_BF16, num_cus: int = 0,
-                       model: Optional[PlanModel] = None) -> int:
+                       model: Optional[PlanModel] = None, two_source: bool = False) -> int:
     """Host split count in [1, 32] from the cost model (no device work)."""
-    L = lib()
-    if model is None:
-        return _check("smd_plan_num_kv_splits",
-                      L.smd_plan_num_kv_splits(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype, num_cus))
-    return _check("smd_plan_num_kv_splits_model",
-                  L.smd_plan_num_kv_splits_model(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype,
-                                                 num_cus, ctypes.byref(model)))
+    return plan_decode(num_seqs, num_heads, kv_len, q_per_seq, kv_dtype, num_cus, model, two_source)[0]
+
+
+def plan_decode(num_seqs: int, num_heads: int, kv_len: int, q_per_seq: int = 1, kv_dtype: int = KV_BF16,
+                num_cus: int = 0, model: Optional[PlanModel] = None,
+                two_source: bool = False) -> tuple[int, bool]:
+    """(split count, whether the wide family won the cost model at that count)
+    (smd.h smd_plan_decode; model None = the built-in coefficients)."""
+    k = ctypes.c_int32(-1)
+    s = _check("smd_plan_decode",
+               lib().smd_plan_decode(num_seqs, num_heads, q_per_seq, kv_len, kv_dtype, num_cus,
+                                     int(bool(two_source)), ctypes.byref(model) if model is not None else None,
+                                     ctypes.byref(k)))
+    return s, k.value == KERNEL_WIDE
 
 
 def partials_bytes(num_tokens: int, num_heads: int, num_splits: int) -> int:
@@ -323,7 +341,8 @@ def _decode_buffers(q_nope, q_rope, index_lists, sink, pools, q_per_seq, num_spl
             raise ValueError("kv pool must be on the same device as q")
     K = sum(idx.shape[1] for _, idx in index_lists)
     if num_splits is None:
-        num_splits = plan_num_kv_splits(T // q_per_seq, H, K, q_per_seq, pools[0].dtype if K > 0 else KV_BF16)
+        num_splits = plan_num_kv_splits(T // q_per_seq, H, K, q_per_seq, pools[0].dtype if K > 0 else KV_BF16,
+                                        two_source=len(pools) > 1)
     need_partials = allocate and (partials_only or num_splits > 1)
     if need_partials:
         if partial_o is None:
@@ -564,11 +583,11 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
     _check("smd_sparse_mla_decode_persistent", rc)
     return out, lse
 
-__all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_default_model", "split_bounds",
-           "partials_bytes", "write_kv_fp8",
-           "sparse_mla_decode", "sparse_mla_decode_noalloc", "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions", "persistent_workspace_bytes",
-           "PersistentWorkspace", "sparse_mla_decode_persistent", "lib", "library_path", "KV_BF16",
-           "KV_FP8_E4M3_UE8M0"]
+__all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_decode", "plan_default_model",
+           "split_bounds", "partials_bytes", "write_kv_fp8", "sparse_mla_decode", "sparse_mla_decode_noalloc",
+           "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions",
+           "persistent_workspace_bytes", "PersistentWorkspace", "sparse_mla_decode_persistent", "lib",
+           "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0"]
 
 if os.environ.get("SMD_EAGER_LOAD") == "1":
     lib()

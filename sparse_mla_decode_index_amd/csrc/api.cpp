@@ -105,22 +105,30 @@ static bool pairs_pay(int32_t M, int64_t units) {
 }
 
 // The wide kernel (128 query rows per workgroup on 32x32 MFMAs) shares each
-// gathered row among 128 query rows; it needs M % 128 == 0 and one source,
-// and it pays once its grid fills at least half the GPU.
+// gathered row among 128 query rows; it needs M % 128 == 0 and one source.
+// It runs when the planner's cost model prices it below the narrow kernels at
+// the call's split count: it pays once its grid fills the GPU and each
+// workgroup has enough tiles to hide its fixed cost.
 constexpr int32_t kWideRowsPerGroup = 128;
 static bool wide_fits(int32_t M, bool two) { return M % kWideRowsPerGroup == 0 && !two; }
 
-// Kernel of a split-KV call: the caller's choice when it names one (checked
-// against the shape), else the rule above.  Returns 0 for an impossible choice.
-static int pick_kernel(int32_t requested, int32_t M, int64_t units, bool two) {
+// Kernel of a split-KV call of `rows` index rows, s splits and kv_len indices
+// per row: the caller's choice when it names one (checked against the shape),
+// else the rule above.  Returns 0 for an impossible choice.
+static int pick_kernel(int32_t requested, int32_t M, int64_t rows, int32_t s, int64_t kv_len, int32_t kv_dtype,
+                       bool two) {
   switch (requested) {
     case SMD_KERNEL_ROWS16: return kKernRows16;
     case SMD_KERNEL_PAIRS: return M % 32 == 0 ? kKernPairs : 0;
     case SMD_KERNEL_WIDE: return wide_fits(M, two) ? kKernWide : 0;
     default: break;
   }
-  if (wide_fits(M, two) && units * (M / kWideRowsPerGroup) >= 128) return kKernWide;  // the grid
-  return pairs_pay(M, units) ? kKernPairs : kKernRows16;
+  const smd_plan_model &pm = default_plan_model();
+  static_assert(kWideRowsPerGroup == 128, "the planner's wide_rows");
+  if (wide_fits(M, two) && rows > 0 && kv_len > 0 && wide_priced(pm, M, two) &&
+      wide_cost(pm, rows, M, kv_len, kv_dtype, 256, s) < narrow_cost(pm, rows, M, kv_len, 256, s))
+    return kKernWide;
+  return pairs_pay(M, rows * s) ? kKernPairs : kKernRows16;
 }
 
 }  // namespace smd
@@ -128,16 +136,21 @@ static int pick_kernel(int32_t requested, int32_t M, int64_t units, bool two) {
 using namespace smd;
 
 extern "C" int32_t smd_decode_kernel_choice(int32_t num_tokens, int32_t num_heads, int32_t q_per_seq,
-                                            int32_t num_splits, int32_t two_source, int32_t requested) {
+                                            int32_t num_splits, int32_t kv_len, int32_t kv_dtype,
+                                            int32_t two_source, int32_t requested) {
   static const char *fn = "smd_decode_kernel_choice";
   g_err[0] = 0;
-  if (num_tokens < 0 || num_heads <= 0 || q_per_seq < 1 || num_splits < 1 || num_tokens % q_per_seq != 0 ||
-      requested < SMD_KERNEL_AUTO || requested > SMD_KERNEL_WIDE) {
+  if (num_tokens < 0 || num_heads <= 0 || q_per_seq < 1 || num_splits < 1 || kv_len < 0 ||
+      num_tokens % q_per_seq != 0 || requested < SMD_KERNEL_AUTO || requested > SMD_KERNEL_WIDE) {
     set_error("%s: bad shapes or kernel choice", fn);
     return SMD_ERR_INVALID_ARG;
   }
+  if (kv_dtype != SMD_KV_BF16 && kv_dtype != SMD_KV_FP8_E4M3_UE8M0) {
+    set_error("%s: unknown kv_dtype %d", fn, kv_dtype);
+    return SMD_ERR_UNSUPPORTED;
+  }
   const int32_t M = num_heads * q_per_seq;
-  const int k = pick_kernel(requested, M, (int64_t)(num_tokens / q_per_seq) * num_splits, two_source != 0);
+  const int k = pick_kernel(requested, M, num_tokens / q_per_seq, num_splits, kv_len, kv_dtype, two_source != 0);
   if (k == 0) {
     set_error("%s: kernel choice %d does not fit M = %d query rows per index row", fn, requested, M);
     return SMD_ERR_UNSUPPORTED;
@@ -289,7 +302,7 @@ int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t 
   a.S = num_splits;
   a.num_units = rows * num_splits;
   const bool fp8 = kv->dtype == SMD_KV_FP8_E4M3_UE8M0;
-  const int kern = pick_kernel(opt ? opt->kernel : SMD_KERNEL_AUTO, M, (int64_t)rows * num_splits,
+  const int kern = pick_kernel(opt ? opt->kernel : SMD_KERNEL_AUTO, M, rows, num_splits, K, kv->dtype,
                                a.indices2 != nullptr);
   if (kern == 0) {
     set_error("%s: kernel choice %d does not fit M = %d query rows per index row%s", fn, opt->kernel, M,

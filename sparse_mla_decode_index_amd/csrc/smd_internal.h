@@ -112,6 +112,15 @@ hipError_t launch_write_kv_fp8(const WriterArgs &a, hipStream_t stream);
 // Error message of the calling thread's last failure (set by every entry point).
 void set_error(const char *fmt, ...);
 
+// The host planner's cost terms (plan.cpp; the formula is documented with
+// smd_plan_model): the built-in coefficients, the narrow and wide kernels'
+// modelled picoseconds at s splits, and whether the wide family is priced.
+const smd_plan_model &default_plan_model();
+int64_t narrow_cost(const smd_plan_model &m, int64_t num_seqs, int64_t M, int64_t kv_len, int64_t cus, int64_t s);
+int64_t wide_cost(const smd_plan_model &m, int64_t num_seqs, int64_t M, int64_t kv_len, int32_t kv_dtype,
+                  int64_t cus, int64_t s);
+bool wide_priced(const smd_plan_model &m, int64_t M, bool two_source);
+
 // Second source of a two-source decode (the sliding-window pool and its index
 // list); null for one source.
 struct SecondSource {

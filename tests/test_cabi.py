@@ -54,7 +54,10 @@ def _model_pair(rng):
              part_ps=int(rng.integers(0, 5_000)), rows_per_wg=int(rng.choice([16, 32, 64])),
              waves_per_wg=int(rng.choice([1, 4, 8])), wg_per_cu=int(rng.integers(1, 4)),
              short_cap=int(rng.integers(1, 33)), long_cap=int(rng.integers(1, 33)),
-             long_kv=int(rng.integers(1, 20000)))
+             long_kv=int(rng.integers(1, 20000)), wide_rows=int(rng.choice([0, 64, 128, 256])),
+             wide_tile=int(rng.choice([16, 32, 64])), wide_fixed_ps=int(rng.integers(0, 30_000_000)),
+             wide_tile_ps=int(rng.integers(1, 4_000_000)), wide_tile_fp8_ps=int(rng.integers(1, 4_000_000)),
+             wide_tile_load_ps=int(rng.integers(0, 2_000_000)))
     c = smd.PlanModel()
     for k, x in v.items():
         setattr(c, k, x)
@@ -67,9 +70,20 @@ def test_planner_formula_bit_exact_vs_oracle():
         cm, pm = _model_pair(rng)
         args = (int(rng.integers(0, 300)), int(rng.choice([16, 32, 64, 128])), int(rng.integers(1, 9)),
                 int(rng.integers(0, 200000)), int(rng.integers(0, 2)), int(rng.choice([0, 80, 256, 304])))
-        got = smd.plan_num_kv_splits(args[0], args[1], args[3], args[2], args[4], args[5], model=cm)
-        want = plan_ref.num_kv_splits(*args, pm)
-        assert got == want, (args, pm)
+        two = bool(rng.integers(0, 2))
+        got = smd.plan_decode(args[0], args[1], args[3], args[2], args[4], args[5], model=cm, two_source=two)
+        want = plan_ref.plan_decode(*args, pm, two_source=two)
+        assert got == want, (args, two, pm)
+        if not two:
+            assert smd.plan_num_kv_splits(args[0], args[1], args[3], args[2], args[4], args[5],
+                                          model=cm) == want[0]
+
+
+def test_default_model_fields_round_trip():
+    """Every coefficient of the built-in model reaches the oracle's mirror."""
+    pm = _library_model()
+    assert pm.wide_rows == 128 and pm.wide_tile == 32 and pm.rows_per_wg == 16
+    assert set(vars(pm)) == {name for name, _ in smd.PlanModel._fields_}
 
 
 def test_default_planner_properties():
@@ -424,29 +438,62 @@ def test_two_source_empty_launches_nothing():
     assert _two(T=0)[0] == 0
 
 
-@pytest.mark.parametrize("T,H,qps,s,two,req,want", [
-    (32, 128, 1, 4, False, None, "wide"),      # 128 workgroups of 128 rows
-    (32, 128, 1, 2, False, None, "pairs"),     # 64 units: below the wide threshold
-    (8, 64, 1, 1, False, None, "rows16"),      # M = 64: no wide; 16 pair workgroups do not pay
-    (256, 128, 4, 1, False, None, "wide"),     # MTP4: M = 512, 64 rows x 4 groups
-    (32, 128, 1, 8, True, None, "pairs"),      # two sources never take the wide kernel
-    (32, 128, 1, 1, False, "rows16", "rows16"),
-    (4, 64, 1, 1, False, "pairs", "pairs"),
+def _library_model():
+    c = smd.plan_default_model()
+    return plan_ref.PlanModel(**{name: getattr(c, name) for name, _ in smd.PlanModel._fields_})
+
+
+@pytest.mark.parametrize("T,H,qps,s,K,kvd,two,req,want", [
+    (64, 128, 1, 4, 65664, 1, False, None, "wide"),   # 256 wide workgroups of 514 tiles each
+    (32, 128, 1, 1, 2176, 0, False, None, "rows16"),  # 32 wide workgroups: the narrow grid is cheaper
+    (1, 128, 1, 31, 65664, 0, False, None, "rows16"),  # low batch, long list: narrow, 248 workgroups
+    (256, 128, 4, 1, 4096, 1, False, None, "wide"),   # MTP4: M = 512, 64 rows x 4 groups
+    (64, 128, 1, 1, 384, 0, False, None, "pairs"),    # short list: wide's fixed cost loses; pairs pay
+    (32, 128, 1, 8, 65664, 1, True, None, "pairs"),   # two sources never take the wide kernel
+    (8, 64, 1, 1, 2176, 0, False, None, "rows16"),    # M = 64: no wide; 16 pair workgroups do not pay
+    (32, 128, 1, 1, 2176, 0, False, "rows16", "rows16"),
+    (4, 64, 1, 1, 100, 0, False, "pairs", "pairs"),
+    (1, 128, 1, 1, 64, 0, False, "wide", "wide"),
 ])
-def test_decode_kernel_choice(T, H, qps, s, two, req, want):
+def test_decode_kernel_choice(T, H, qps, s, K, kvd, two, req, want):
     """smd_decode_kernel_choice applies the documented rule: wide when 128
-    divides M, one source and at least 128 units; else pairs when they pay;
-    else rows16; a named family is returned as is when it fits."""
-    assert smd.decode_kernel_choice(T, H, qps, s, two_source=two, kernel=req) == want
+    divides M, one source and the planner's model prices it below the narrow
+    kernels at this s; else pairs when they pay; else rows16; a named family
+    is returned as is when it fits."""
+    assert smd.decode_kernel_choice(T, H, qps, s, K, kvd, two_source=two, kernel=req) == want
+
+
+def test_decode_kernel_choice_follows_the_cost_model():
+    """AUTO picks wide exactly where the oracle's cost formula, with the
+    library's coefficients, prices the wide workgroups strictly below the
+    narrow ones, and the planner's own family agrees at its chosen s."""
+    pm = _library_model()
+    rng = np.random.default_rng(5)
+    for _ in range(300):
+        rows = int(rng.integers(1, 200))
+        H = int(rng.choice([16, 64, 128]))
+        qps = int(rng.choice([1, 2, 4]))
+        K = int(rng.integers(1, 70000))
+        kvd = int(rng.integers(0, 2))
+        s = int(rng.integers(1, 33))
+        cw = plan_ref.wide_split_cost(s, rows, H, qps, K, kvd, 256, pm)
+        wide = cw is not None and cw < plan_ref.split_cost(s, rows, H, qps, K, 256, pm)
+        got = smd.decode_kernel_choice(rows * qps, H, qps, s, K, kvd)
+        assert (got == "wide") == wide, (rows, H, qps, K, kvd, s)
+        ps, pw = smd.plan_decode(rows, H, K, qps, kvd)
+        assert (ps, pw) == plan_ref.plan_decode(rows, H, qps, K, kvd, 0, pm)
+        assert (smd.decode_kernel_choice(rows * qps, H, qps, ps, K, kvd) == "wide") == pw
 
 
 @pytest.mark.parametrize("args,code", [
-    ((32, 64, 1, 1, 0, smd.KERNEL_WIDE), -2),   # M = 64 cannot take the wide kernel
-    ((32, 128, 1, 1, 1, smd.KERNEL_WIDE), -2),  # nor two sources
-    ((32, 16, 1, 1, 0, smd.KERNEL_PAIRS), -2),  # M = 16: no pairs
-    ((3, 16, 2, 1, 0, 0), -1),                  # tokens not a multiple of q_per_seq
-    ((4, 16, 1, 0, 0, 0), -1),                  # no split
-    ((4, 16, 1, 1, 0, 9), -1),                  # unknown family
+    ((32, 64, 1, 1, 100, 0, 0, smd.KERNEL_WIDE), -2),   # M = 64 cannot take the wide kernel
+    ((32, 128, 1, 1, 100, 0, 1, smd.KERNEL_WIDE), -2),  # nor two sources
+    ((32, 16, 1, 1, 100, 0, 0, smd.KERNEL_PAIRS), -2),  # M = 16: no pairs
+    ((4, 16, 1, 1, 100, 5, 0, 0), -2),                  # unknown kv dtype
+    ((3, 16, 2, 1, 100, 0, 0, 0), -1),                  # tokens not a multiple of q_per_seq
+    ((4, 16, 1, 0, 100, 0, 0, 0), -1),                  # no split
+    ((4, 16, 1, 1, -1, 0, 0, 0), -1),                   # negative index count
+    ((4, 16, 1, 1, 100, 0, 0, 9), -1),                  # unknown family
 ])
 def test_decode_kernel_choice_rejects(args, code):
     assert smd.lib().smd_decode_kernel_choice(*args) == code

@@ -83,3 +83,34 @@ def test_long_context_partials_full_size(gpu):
     po_ref, pl_ref = ref.sparse_mla_decode_partials(w.arrays["q_nope"], w.arrays["q_rope"], oracle_pool(w),
                                                     w.arrays["indices"], w.softmax_scale, 32)
     check_partials(po, pl, po_ref, pl_ref)
+
+
+@pytest.mark.parametrize("T,ctx,var", [(64, 1048576, "fp8_h128"), (16, 102400, "bf16_h128"),
+                                       (64, 32768, "bf16_h128")])
+def test_matrix_cell_wide_plan_sampled(gpu, T, ctx, var):
+    """T x ctx matrix cells where the host planner prices the wide kernel
+    cheapest, in the launch `bench.py --matrix` times (the planner's split
+    count, the library's kernel choice, decode + merge): the first, a middle
+    and the last token, every head, against the oracle, and a second launch
+    bit-identical to the first."""
+    w = wl.matrix_cell(T, ctx, var)
+    q_nope, q_rope, sink, pool = device_inputs(w, gpu)
+    idx = torch.from_numpy(w.arrays["indices"]).to(gpu)
+    K = idx.shape[1]
+    kvd = smd.KV_BF16 if w.kv_dtype == "bf16" else smd.KV_FP8_E4M3_UE8M0
+    s, wide = smd.plan_decode(w.num_index_rows, w.num_heads, K, 1, kvd)
+    assert wide and smd.decode_kernel_choice(T, w.num_heads, 1, s, K, kvd) == "wide"
+    runs = []
+    for rep in range(2):
+        print(f"matrix cell {w.name} K={K} s={s} wide launch {rep}", flush=True)
+        runs.append(smd.sparse_mla_decode(q_nope, q_rope, pool, idx, sink, w.softmax_scale, num_splits=s))
+        torch.cuda.synchronize()
+    out, lse = runs[0]
+    assert torch.equal(out.view(torch.int16), runs[1][0].view(torch.int16))
+    assert torch.equal(lse, runs[1][1])
+    a = w.arrays
+    for t in (0, T // 2, T - 1):
+        o_ref, l_ref = ref.sparse_mla_decode(a["q_nope"][t:t + 1], a["q_rope"][t:t + 1], oracle_pool(w),
+                                             a["indices"][t:t + 1], a["sink"], w.softmax_scale)
+        check_out(out[t:t + 1], o_ref, f"{w.name} token {t}")
+        check_lse(lse[t:t + 1], l_ref, f"{w.name} token {t}")

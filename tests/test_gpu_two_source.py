@@ -164,7 +164,7 @@ def test_fullsize_fp8_top2048_window128(gpu):
     a = w.arrays
     qn, qr, sk, mp, mi, sp, si = _inputs(w, gpu)
     K = a["main_indices"].shape[1] + a["swa_indices"].shape[1]
-    s = smd.plan_num_kv_splits(w.num_index_rows, w.num_heads, K, 1, smd.KV_FP8_E4M3_UE8M0)
+    s = smd.plan_num_kv_splits(w.num_index_rows, w.num_heads, K, 1, smd.KV_FP8_E4M3_UE8M0, two_source=True)
     print(f"two-source full size s={s}", flush=True)
     out, lse = smd.sparse_mla_decode_two_source(qn, qr, mp, mi, sp, si, sk, w.softmax_scale, num_splits=s)
     torch.cuda.synchronize()

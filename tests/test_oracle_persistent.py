@@ -205,10 +205,14 @@ def test_piecewise_merge_equals_unsplit(seed, P):
 # ----------------------------------------------------------------------------
 # host split planner: the cost formula worked out by hand
 # ----------------------------------------------------------------------------
-def _fitted_model():
+def _fitted_model(wide: bool = True):
+    """The library's built-in coefficients; wide=False leaves out the wide
+    family (wide_rows = 0), so that only the narrow formula prices a plan."""
     return pr.PlanModel(fixed_ps=7194000, step_ps=1971000, step_load_ps=569000, merge_ps=4065000,
-                              part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
-                              long_cap=32, long_kv=4096)
+                        part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
+                        long_cap=32, long_kv=4096, wide_rows=128 if wide else 0, wide_tile=32,
+                        wide_fixed_ps=13648000, wide_tile_ps=1774000, wide_tile_fp8_ps=2192000,
+                        wide_tile_load_ps=536000)
 
 
 def test_planner_cost_worked_example_short_list():
@@ -223,7 +227,7 @@ def test_planner_cost_worked_example_short_list():
       s=4: 544 -> chunk 576 -> 36 -> 5 steps, step 2255500;
            7194000 + 5*2255500 + 4065000 + 287*8*64*4                = 23124276
     and the short-list cap (2176 < 4096) stops at s = 4."""
-    m = _fitted_model()
+    m = _fitted_model(wide=False)
     want = {1: 41910125, 2: 30572138, 3: 24806082, 4: 23124276}
     for s, c in want.items():
         assert pr.split_cost(s, 8, 64, 1, 2176, 256, m) == c, s
@@ -243,8 +247,8 @@ def test_planner_cost_worked_example_long_list_and_waves():
     300 rows x 128 heads x 2048 indices: s=1 runs 2400 workgroups in 10 waves
     of 16 full-load steps, 10*(7194000 + 16*2540000) = 478340000; s=2 needs 19
     waves of 8 steps plus the merge, 19*27514000 + 4065000 + 287*300*128*2
-    = 548872600."""
-    m = _fitted_model()
+    = 548872600.  (Narrow family alone; the wide terms are in the next test.)"""
+    m = _fitted_model(wide=False)
     assert pr.split_cost(32, 1, 128, 1, 65664, 256, m) == 55614552
     assert pr.split_cost(31, 1, 128, 1, 65664, 256, m) == 55275522
     assert pr.split_cost(30, 1, 128, 1, 65664, 256, m) == 57440946
@@ -252,4 +256,34 @@ def test_planner_cost_worked_example_long_list_and_waves():
     assert pr.split_cost(1, 300, 128, 1, 2048, 256, m) == 478340000
     assert pr.split_cost(2, 300, 128, 1, 2048, 256, m) == 548872600
     assert pr.num_kv_splits(300, 128, 1, 2048, 1, 256, m) == 1
+
+
+def test_planner_cost_worked_example_wide_family():
+    """The same calls with the wide terms (128 query rows per workgroup, tiles
+    of 32 positions, one workgroup per CU; every tile at full load costs
+    2192000 + 536000 = 2728000 for fp8).  300 rows x 128 heads x 2048 fp8
+    indices:
+      s=1: 300 workgroups, 2 waves of 64 tiles: 2*(13648000 + 64*2728000)   = 376480000
+      s=2: 600 workgroups, 3 waves of 32 tiles: 3*(13648000 + 32*2728000)
+           + 4065000 + 287*300*128*2                                        = 328938600
+      s=3: 900 -> 4 waves; chunk 683 -> 704, 22 tiles: 4*(13648000 + 22*2728000)
+           + 4065000 + 287*300*128*3                                        = 331783400
+      s=4: 1200 -> 5 waves; chunk 512, 16 tiles: 5*(13648000 + 16*2728000)
+           + 4065000 + 287*300*128*4                                        = 334628200
+    all below the narrow 478340000 and 548872600 of s = 1, 2, so the plan is
+    two splits on the wide kernel.  One row x 128 heads x 65664 bf16 indices,
+    s=32: 32 workgroups of 66 tiles at 1774000 + 536000*32//256 = 1841000:
+    13648000 + 66*1841000 + 4065000 + 287*128*32 = 140394552, far above the
+    narrow 55275522 of s = 31, which stays the plan."""
+    m = _fitted_model()
+    assert pr.wide_split_cost(1, 300, 128, 1, 2048, 1, 256, m) == 376480000
+    assert pr.wide_split_cost(2, 300, 128, 1, 2048, 1, 256, m) == 328938600
+    assert pr.wide_split_cost(3, 300, 128, 1, 2048, 1, 256, m) == 331783400
+    assert pr.wide_split_cost(4, 300, 128, 1, 2048, 1, 256, m) == 334628200
+    assert pr.plan_decode(300, 128, 1, 2048, 1, 256, m) == (2, True)
+    assert pr.plan_decode(300, 128, 1, 2048, 1, 256, m, two_source=True) == (1, False)
+    assert pr.wide_split_cost(32, 1, 128, 1, 65664, 0, 256, m) == 140394552
+    assert pr.plan_decode(1, 128, 1, 65664, 0, 256, m) == (31, False)
+    # M = 64 is not a multiple of 128: no wide cost at all
+    assert pr.wide_split_cost(1, 8, 64, 1, 2176, 0, 256, m) is None
 
