@@ -40,6 +40,12 @@ import numpy as np  # noqa: E402
 METRIC = "sparse-MLA decode µs/call + achieved HBM GB/s (% roofline), T x ctx matrix"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA
+FP8_MFMA_PEAK_TFS = 5000.0   # MI355X dense fp8 MFMA
+# The fp8 QK ("--qk fp8") runs the 896 NoPE flops of QK per (kv row, query
+# row) at the fp8 rate and the other 1152 (RoPE QK and PV) at the bf16 rate:
+# its ideal time per 2048 flops is 896/5000 + 1152/2500, an effective peak of
+# 2048 / 0.64 = 3200 TFLOP/s.
+QK_FP8_MFMA_PEAK_TFS = 2048.0 / (896.0 / FP8_MFMA_PEAK_TFS + 1152.0 / BF16_MFMA_PEAK_TFS)
 
 
 def parse():
@@ -56,6 +62,9 @@ def parse():
     ap.add_argument("--kernel", type=str, default=None, choices=["rows16", "pairs", "wide"],
                     help="split-KV kernel family (default: the library's choice)")
     ap.add_argument("--partitions", type=int, default=None, help="persistent kernel: override the partition count")
+    ap.add_argument("--qk", type=str, default="bf16", choices=["bf16", "fp8"],
+                    help="QK arithmetic: bf16 (exact; default) or fp8 (q_nope quantised like the cache, the NoPE "
+                         "QK on the block-scaled fp8 MFMA; fp8 pools, H x MTP a multiple of 128)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     ap.add_argument("--kernel-launches", type=int, default=50)
@@ -494,6 +503,10 @@ def main():
     stream = torch.cuda.Stream()
     cfg = {"workload": w.name, "num_tokens": T, "num_heads": H, "q_per_seq": qps, "pool_rows": w.pool_rows,
            "kv_dtype": w.kv_dtype, "parallelism": "1 gpu"}
+    qk = None if args.qk == "bf16" else "fp8"
+    mfma_peak = BF16_MFMA_PEAK_TFS if qk is None else QK_FP8_MFMA_PEAK_TFS
+    if qk is not None:
+        cfg["qk"] = "fp8 (q_nope quantised per 64-dim block, UE8M0 + e4m3)"
 
     if w.ragged:
         P = args.partitions or smd.persistent_default_partitions(H, qps)
@@ -503,7 +516,7 @@ def main():
         def step():
             smd.sparse_mla_decode_persistent(d["q_nope"], d["q_rope"], d["pool"], d["kv_indptr"], d["kv_indices"],
                                              d["sink"], w.softmax_scale, q_per_seq=qps, workspace=ws, out=out,
-                                             lse=lse)
+                                             lse=lse, qk=qk)
 
         plan = None
         kernel_step = step
@@ -532,14 +545,15 @@ def main():
             else:
                 smd.sparse_mla_decode(d["q_nope"], d["q_rope"], d["pool"], d["indices"], d["sink"], w.softmax_scale,
                                       num_splits=s, q_per_seq=qps, out=out, lse=lse, kernel=args.kernel,
-                                      partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None)
+                                      partial_o=po if s > 1 else None, partial_lse=pl if s > 1 else None, qk=qk)
 
         kernel_step = step  # decode (+ merge when split; its time is subtracted below)
 
         def merge_only():
             smd.merge_partials(po, pl, d["sink"], out=out, lse=lse)
 
-        family = smd.decode_kernel_choice(w.num_tokens, H, qps, s, K, kvd, two_source=two, kernel=args.kernel)
+        family = "wide" if qk is not None else smd.decode_kernel_choice(w.num_tokens, H, qps, s, K, kvd,
+                                                                         two_source=two, kernel=args.kernel)
         kernel_name = "smd::decode_wide_kernel" if family == "wide" else "smd::decode_kernel"
         cfg.update({"topk": K, "num_splits": s, "kernel": "split-kv " + family})
         if two:
@@ -600,13 +614,13 @@ def main():
     kern_gbs = alg_bytes / (kern_us * 1e3)
     kern_tfs = alg_flops / (kern_us * 1e6)
     t_hbm = alg_bytes / (HBM_PEAK_GBS * 1e3)
-    t_mfma = alg_flops / (BF16_MFMA_PEAK_TFS * 1e6)
+    t_mfma = alg_flops / (mfma_peak * 1e6)
     if t_hbm >= t_mfma:
         roof = {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(kern_gbs / HBM_PEAK_GBS, 4), "traffic": None}
     else:
-        roof = {"bound": "mfma", "achieved": round(kern_tfs, 1), "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
-                "frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4), "traffic": None}
+        roof = {"bound": "mfma", "achieved": round(kern_tfs, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                "frac": round(kern_tfs / mfma_peak, 4), "traffic": None}
     traffic, traffic_src = measured_traffic(w.name, kernel_name)
     roof["traffic"] = traffic
     if traffic_src:
@@ -615,7 +629,7 @@ def main():
     roof.update({"kernel": kernel_name, "kernel_us": round(kern_us, 3), "merge_us": round(merge_us, 3),
                  "alg_bytes_per_launch": alg_bytes,
                  "alg_flops_per_launch": alg_flops, "hbm_frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                 "mfma_frac": round(kern_tfs / BF16_MFMA_PEAK_TFS, 4)})
+                 "mfma_frac": round(kern_tfs / mfma_peak, 4)})
 
     cold = None
     if cold_us is not None:
@@ -625,7 +639,7 @@ def main():
             c_frac = c_ach / HBM_PEAK_GBS
         else:
             c_ach = alg_flops / (cold_us * 1e6)
-            c_frac = c_ach / BF16_MFMA_PEAK_TFS
+            c_frac = c_ach / mfma_peak
         cold = {"us_per_call": round(cold_us, 3), "achieved": round(c_ach, 1), "unit": roof["unit"],
                 "frac": round(c_frac, 4), "calls": args.cold_calls, "flush_bytes": 1 << 30,
                 "note": "median of single calls, each after a 1 GiB device write; decode + merge"}
@@ -652,7 +666,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if w.kv_dtype == "bf16" else "fp8-e4m3/ue8m0 in, bf16 mfma",
+        "dtype": ("bf16" if w.kv_dtype == "bf16" else "fp8-e4m3/ue8m0 in, bf16 mfma") if qk is None
+                 else "fp8-e4m3/ue8m0 in, fp8 qk (q quantised) + bf16 pv mfma",
         "data": "synthetic",
         "config": cfg,
         "roofline": roof,

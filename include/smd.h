@@ -271,11 +271,36 @@ enum {
 int32_t smd_decode_kernel_choice(int32_t num_tokens, int32_t num_heads, int32_t q_per_seq, int32_t num_splits,
                                  int32_t kv_len, int32_t kv_dtype, int32_t two_source, int32_t requested);
 
+/*
+ * How QK runs (options->qk):
+ *   SMD_QK_BF16  exact: an fp8 pool's NoPE is dequantised to bf16 (exact,
+ *                e4m3 x 2^(code - 127)) and QK runs on bf16 MFMAs.
+ *   SMD_QK_FP8   "a8w8" (the persistent decode object of the aiter page
+ *                "[ASM][HIP][MLA v4 nm] Split plan helper and persistent
+ *                decode kernel", Summary part 2): q_nope is quantised the way
+ *                the cache writer quantises a latent row's NoPE (per 64-dim
+ *                block, code c = clamp(ceil(log2(amax / 448)) + 127, 0, 254),
+ *                each value the E4M3FN byte nearest to x * 2^(127 - c), ties
+ *                to even; c = 0 for an all-zero block), and the NoPE part of QK
+ *                runs on the block-scaled fp8 MFMA straight from the pool's
+ *                bytes and codes.  RoPE, P and PV stay bf16.  The result is the
+ *                exact decode's with q_nope replaced by its quantised values,
+ *                up to rounding order.  For fp8 pools, one source, M a
+ *                multiple of 128: the wide kernel of the split-KV entry points
+ *                (with options->kernel SMD_KERNEL_AUTO or SMD_KERNEL_WIDE) and
+ *                the persistent decode.  Anything else is SMD_ERR_UNSUPPORTED.
+ */
+enum {
+  SMD_QK_BF16 = 0,
+  SMD_QK_FP8 = 1
+};
+
 /* Options of the _ex entry points; NULL means all defaults (zero). */
 typedef struct smd_decode_options {
   int32_t kernel;      /* SMD_KERNEL_* (SMD_KERNEL_AUTO for the persistent decode) */
   int32_t merge;       /* SMD_MERGE_* */
-  int32_t reserved[6]; /* must be zero */
+  int32_t qk;          /* SMD_QK_* */
+  int32_t reserved[5]; /* must be zero */
 } smd_decode_options;
 
 /*
@@ -316,7 +341,8 @@ int smd_sparse_mla_decode(const void *q_nope, const void *q_rope, int32_t num_to
                           void *stream);
 
 /* smd_sparse_mla_decode with explicit options (options may be NULL); an
- * unknown kernel value or a non-zero reserved field is SMD_ERR_INVALID_ARG. */
+ * unknown kernel or qk value or a non-zero reserved field is
+ * SMD_ERR_INVALID_ARG, a qk choice the call cannot take SMD_ERR_UNSUPPORTED. */
 int smd_sparse_mla_decode_ex(const void *q_nope, const void *q_rope, int32_t num_tokens,
                              int32_t num_heads, int32_t q_per_seq, const smd_kv_pool *kv,
                              const int32_t *indices, int64_t indices_stride, int32_t topk,

@@ -11,7 +11,10 @@ Modules:
                        split partials and their merge, row decoding of bf16
                        and fp8-e4m3 / UE8M0 pools;
 * ``oracle.plan_ref``  the integer plans: the host split-count cost model and
-                       the persistent kernel's balanced tile partition.
+                       the persistent kernel's balanced tile partition;
+* ``oracle.writer_ref`` the fp8/UE8M0 cache writer's rule;
+* ``oracle.a8_ref``    the fp8 ("a8w8") QK: q quantised as the writer
+                       quantises, then the decode of ``oracle.ref``.
 
 Parity status of each function is stated in its docstring.  The host
 planner's exact split count with the library's fitted coefficients is

@@ -137,11 +137,13 @@ def _sink64(sink, H):
     return np.asarray(sink, dtype=np.float32).astype(np.float64).reshape(H)
 
 
-def sparse_mla_decode(q_nope, q_rope, pool: dict, indices, sink, softmax_scale: float, q_per_seq: int = 1):
-    """Dense-index decode: token t uses index row t // q_per_seq.
+def sparse_mla_decode(q_nope, q_rope, pool: dict, indices, sink, softmax_scale: float, q_per_seq: int = 1, *,
+                      queries64=None):
+    """Dense-index decode: token t uses index row t // q_per_seq.  queries64
+    (float64 [T, H, 512]) replaces the queries that q_nope / q_rope encode.
 
     Returns out float64 [T, H, 512] and lse float64 [T, H]."""
-    q = queries(q_nope, q_rope)
+    q = queries(q_nope, q_rope) if queries64 is None else np.asarray(queries64, dtype=np.float64)
     T, H, _ = q.shape
     n = pool_size(pool)
     sk = _sink64(sink, H)
@@ -162,13 +164,14 @@ def sparse_mla_decode(q_nope, q_rope, pool: dict, indices, sink, softmax_scale: 
 
 
 def sparse_mla_decode_ragged(q_nope, q_rope, pool: dict, kv_indptr, kv_indices, sink, softmax_scale: float,
-                             q_per_seq: int):
+                             q_per_seq: int, *, queries64=None):
     """Ragged decode: sequence b owns kv_indices[kv_indptr[b]:kv_indptr[b+1]] and
     tokens b*q_per_seq .. (b+1)*q_per_seq-1, which all share that index list.
 
     Returns (out, lse, written): rows of sequences with K_b = 0 are not written
-    (the pages leave them untouched); `written` is a bool [T] mask."""
-    q = queries(q_nope, q_rope)
+    (the pages leave them untouched); `written` is a bool [T] mask.
+    queries64 as in sparse_mla_decode."""
+    q = queries(q_nope, q_rope) if queries64 is None else np.asarray(queries64, dtype=np.float64)
     T, H, _ = q.shape
     n = pool_size(pool)
     sk = _sink64(sink, H)
@@ -224,10 +227,11 @@ def partial_one(q: np.ndarray, k: np.ndarray, softmax_scale: float):
 
 
 def sparse_mla_decode_partials(q_nope, q_rope, pool: dict, indices, softmax_scale: float, num_splits: int,
-                               q_per_seq: int = 1):
+                               q_per_seq: int = 1, *, queries64=None):
     """Per-split FP32-partial semantics in float64: o [T, H, s, 512], lse [T, H, s].
-    Split r of index row b covers positions split_bounds(K, s)[r] of that row."""
-    q = queries(q_nope, q_rope)
+    Split r of index row b covers positions split_bounds(K, s)[r] of that row.
+    queries64 as in sparse_mla_decode."""
+    q = queries(q_nope, q_rope) if queries64 is None else np.asarray(queries64, dtype=np.float64)
     T, H, _ = q.shape
     n = pool_size(pool)
     idx_all = np.asarray(indices)

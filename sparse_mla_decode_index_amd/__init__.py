@@ -62,23 +62,28 @@ class _KVPool(ctypes.Structure):
 
 
 class _DecodeOptions(ctypes.Structure):
-    _fields_ = [("kernel", ctypes.c_int32), ("merge", ctypes.c_int32), ("reserved", ctypes.c_int32 * 6)]
+    _fields_ = [("kernel", ctypes.c_int32), ("merge", ctypes.c_int32), ("qk", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 5)]
 
 
 MERGE_AUTO = 0
 MERGE_WORKSPACE = 1
 _MERGES = {"auto": MERGE_AUTO, "workspace": MERGE_WORKSPACE}
+QK_BF16 = 0
+QK_FP8 = 1
+_QKS = {"bf16": QK_BF16, "fp8": QK_FP8}
 
 
-def _options(kernel=None, merge=None) -> Optional[_DecodeOptions]:
-    """A smd_decode_options for `kernel` (a KERNEL_* value or its name) and
-    `merge` (a MERGE_* value or its name), or None for the library's
-    defaults."""
-    if kernel is None and merge is None:
+def _options(kernel=None, merge=None, qk=None) -> Optional[_DecodeOptions]:
+    """A smd_decode_options for `kernel` (a KERNEL_* value or its name),
+    `merge` (a MERGE_* value or its name) and `qk` (a QK_* value, "bf16" or
+    "fp8"), or None for the library's defaults."""
+    if kernel is None and merge is None and qk is None:
         return None
     k = 0 if kernel is None else (_KERNELS[kernel] if isinstance(kernel, str) else int(kernel))
     m = 0 if merge is None else (_MERGES[merge] if isinstance(merge, str) else int(merge))
-    return _DecodeOptions(kernel=k, merge=m)
+    q = 0 if qk is None else (_QKS[qk] if isinstance(qk, str) else int(qk))
+    return _DecodeOptions(kernel=k, merge=m, qk=q)
 
 
 class PlanModel(ctypes.Structure):
@@ -375,7 +380,7 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
                       out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                       partial_o: Optional[torch.Tensor] = None,
                       partial_lse: Optional[torch.Tensor] = None,
-                      partials_only: bool = False, kernel=None):
+                      partials_only: bool = False, kernel=None, qk=None):
     """Split-KV sparse MLA decode.
 
     q_nope bf16 [T,H,448], q_rope bf16 [T,H,64], indices int32 [T/q_per_seq, K]
@@ -383,13 +388,15 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
     [T,H,512] and fp32 [T,H] — or, with partials_only, (partial_o, partial_lse)
     of shapes [T,H,s,512] and [T,H,s].  num_splits=None asks the host planner.
     kernel: None (the library's choice) or a kernel family ("rows16", "pairs",
-    "wide" or a KERNEL_* value).
+    "wide" or a KERNEL_* value).  qk: None / "bf16" (exact) or "fp8" (q_nope
+    quantised like the cache, NoPE QK on the block-scaled fp8 MFMA; fp8 pools,
+    M a multiple of 128; smd.h SMD_QK_*).
     """
     T, H, num_splits, out, lse, partial_o, partial_lse = _decode_buffers(
         q_nope, q_rope, [("indices", indices)], sink, [kv], q_per_seq, num_splits, out, lse, partial_o,
         partial_lse, partials_only)
     pool = kv._struct()
-    opt = _options(kernel)
+    opt = _options(kernel, qk=qk)
     rc = lib().smd_sparse_mla_decode_ex(
         q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool), *_idx_args(indices),
         _ptr(sink), float(softmax_scale), num_splits,
@@ -405,16 +412,17 @@ def sparse_mla_decode(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, in
 def sparse_mla_decode_noalloc(q_nope: torch.Tensor, q_rope: torch.Tensor, kv: KVPool, indices: torch.Tensor,
                               sink: Optional[torch.Tensor], softmax_scale: float, *, out: torch.Tensor,
                               lse: Optional[torch.Tensor] = None, num_splits: Optional[int] = None,
-                              q_per_seq: int = 1, kernel=None):
+                              q_per_seq: int = 1, kernel=None, qk=None):
     """sparse_mla_decode through the allocation-free entry point: the FP32
     partials of a split plan stay in the library's per-GPU scratch array
     (NOALLOC_SCRATCH_BYTES), so neither this call nor the library allocates.
-    out (bf16 [T,H,512]) must be given; lse (fp32 [T,H]) is optional."""
+    out (bf16 [T,H,512]) must be given; lse (fp32 [T,H]) is optional; kernel
+    and qk as in sparse_mla_decode."""
     T, H, num_splits, out, lse, _, _ = _decode_buffers(q_nope, q_rope, [("indices", indices)], sink, [kv], q_per_seq,
                                                        num_splits, out, lse, None, None, partials_only=False,
                                                        allocate=False)
     pool = kv._struct()
-    opt = _options(kernel)
+    opt = _options(kernel, qk=qk)
     rc = lib().smd_sparse_mla_decode_noalloc(
         q_nope.data_ptr(), q_rope.data_ptr(), T, H, q_per_seq, ctypes.byref(pool), *_idx_args(indices),
         _ptr(sink), float(softmax_scale), num_splits, out.data_ptr(), _ptr(lse),
@@ -541,11 +549,13 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
                                  sink: Optional[torch.Tensor], softmax_scale: float, *,
                                  q_per_seq: int = 1, workspace: PersistentWorkspace,
                                  out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                                 merge=None):
+                                 merge=None, qk=None):
     """Persistent decode over ragged sequences: q bf16 [B*q_per_seq, H, 448/64],
     kv_indptr int32 [B+1], kv_indices int32 flat.  Returns (out, lse); rows of
     sequences with no index are left as they were in `out` / `lse`.  merge:
-    None / "auto" or "workspace" (smd.h SMD_MERGE_*; both give the same bits)."""
+    None / "auto" or "workspace" (smd.h SMD_MERGE_*; both give the same bits).
+    qk: None / "bf16" or "fp8" (as in sparse_mla_decode; fp8 pools, M a
+    multiple of 128)."""
     dev = q_nope.device
     _need(q_nope, "q_nope", torch.bfloat16, device=dev)
     if q_nope.dim() != 3 or q_nope.shape[2] != NOPE:
@@ -574,7 +584,7 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
     _need(out, "out", torch.bfloat16, (T, H, DIM), dev)
     _need(lse, "lse", torch.float32, (T, H), dev)
     pool = kv._struct()
-    opts = _options(merge=merge)
+    opts = _options(merge=merge, qk=qk)
     rc = lib().smd_sparse_mla_decode_persistent_ex(
         q_nope.data_ptr(), q_rope.data_ptr(), B, q_per_seq, H, ctypes.byref(pool), kv_indptr.data_ptr(),
         kv_indices.data_ptr() if kv_indices.numel() else kv_indptr.data_ptr(), _ptr(sink), float(softmax_scale),
@@ -587,7 +597,7 @@ __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_decode
            "split_bounds", "partials_bytes", "write_kv_fp8", "sparse_mla_decode", "sparse_mla_decode_noalloc",
            "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions",
            "persistent_workspace_bytes", "PersistentWorkspace", "sparse_mla_decode_persistent", "lib",
-           "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0"]
+           "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0", "QK_BF16", "QK_FP8"]
 
 if os.environ.get("SMD_EAGER_LOAD") == "1":
     lib()

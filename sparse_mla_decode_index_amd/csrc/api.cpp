@@ -176,13 +176,18 @@ int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t 
       set_error("%s: options.merge applies to the persistent decode only", fn);
       return SMD_ERR_INVALID_ARG;
     }
-    for (int i = 0; i < 6; ++i) {
+    if (opt->qk != SMD_QK_BF16 && opt->qk != SMD_QK_FP8) {
+      set_error("%s: unknown qk choice %d", fn, opt->qk);
+      return SMD_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 5; ++i) {
       if (opt->reserved[i] != 0) {
         set_error("%s: options.reserved must be zero", fn);
         return SMD_ERR_INVALID_ARG;
       }
     }
   }
+  const bool qk_fp8 = opt != nullptr && opt->qk == SMD_QK_FP8;
   if (num_tokens < 0 || topk < 0 || indices_stride < 0 ||
       (two && (two->count < 0 || two->indices_stride < 0))) {
     set_error("%s: negative size (num_tokens=%d counts=%d,%d strides=%lld,%lld)", fn, num_tokens, topk,
@@ -302,8 +307,17 @@ int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t 
   a.S = num_splits;
   a.num_units = rows * num_splits;
   const bool fp8 = kv->dtype == SMD_KV_FP8_E4M3_UE8M0;
-  const int kern = pick_kernel(opt ? opt->kernel : SMD_KERNEL_AUTO, M, rows, num_splits, K, kv->dtype,
-                               a.indices2 != nullptr);
+  if (qk_fp8) {  // the fp8 QK exists on the wide kernel over one fp8 source
+    if (!fp8 || two != nullptr || !wide_fits(M, false) ||
+        (opt->kernel != SMD_KERNEL_AUTO && opt->kernel != SMD_KERNEL_WIDE)) {
+      set_error("%s: qk = SMD_QK_FP8 needs an fp8 pool, one source, M = %d a multiple of 128 and the wide "
+                "kernel (kernel choice %d)", fn, M, opt->kernel);
+      return SMD_ERR_UNSUPPORTED;
+    }
+  }
+  const int kern = qk_fp8 ? kKernWide
+                          : pick_kernel(opt ? opt->kernel : SMD_KERNEL_AUTO, M, rows, num_splits, K, kv->dtype,
+                                        a.indices2 != nullptr);
   if (kern == 0) {
     set_error("%s: kernel choice %d does not fit M = %d query rows per index row%s", fn, opt->kernel, M,
               a.indices2 ? " with two sources" : "");
@@ -315,6 +329,7 @@ int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t 
   a.out = need_partials ? nullptr : (uint16_t *)out;
   a.lse = need_partials ? nullptr : lse;
   a.hilo = out == nullptr;  // FP32 partials are the result only without out
+  a.qk_fp8 = qk_fp8;
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = kern == kKernWide ? launch_decode_wide(a, fp8, st) : launch_decode(a, fp8, kern == kKernPairs, st);
   if (e != hipSuccess) {
@@ -476,7 +491,11 @@ extern "C" int smd_sparse_mla_decode_persistent_ex(const void *q_nope, const voi
       set_error("%s: unknown merge choice %d", fn, opt->merge);
       return SMD_ERR_INVALID_ARG;
     }
-    for (int i = 0; i < 6; ++i) {
+    if (opt->qk != SMD_QK_BF16 && opt->qk != SMD_QK_FP8) {
+      set_error("%s: unknown qk choice %d", fn, opt->qk);
+      return SMD_ERR_INVALID_ARG;
+    }
+    for (int i = 0; i < 5; ++i) {
       if (opt->reserved[i] != 0) {
         set_error("%s: options.reserved must be zero", fn);
         return SMD_ERR_INVALID_ARG;
@@ -534,6 +553,11 @@ extern "C" int smd_sparse_mla_decode_persistent_ex(const void *q_nope, const voi
   if (num_seqs == 0) return SMD_OK;
 
   const int rb = persist_rb(M);
+  const bool qk_fp8 = opt != nullptr && opt->qk == SMD_QK_FP8;
+  if (qk_fp8 && (kv->dtype != SMD_KV_FP8_E4M3_UE8M0 || rb != 8)) {
+    set_error("%s: qk = SMD_QK_FP8 needs an fp8 pool and M = %d a multiple of 128", fn, M);
+    return SMD_ERR_UNSUPPORTED;
+  }
   PersistArgs pa = {};
   a.q_nope = (const uint16_t *)q_nope;
   a.q_rope = (const uint16_t *)q_rope;
@@ -546,6 +570,7 @@ extern "C" int smd_sparse_mla_decode_persistent_ex(const void *q_nope, const voi
   a.G = persist_groups(M);
   a.out = (uint16_t *)out;
   a.lse = lse;
+  a.qk_fp8 = qk_fp8;
   pa.d = a;
   pa.kv_indptr = kv_indptr;
   pa.kv_indices = kv_indices;

@@ -364,13 +364,17 @@ __device__ __forceinline__ bool plan_partition(const PersistArgs &pa, int p, int
 
 // RB = 8 runs the wide waves of wide_core.h: wave w owns rows 32w .. 32w+31
 // of the group's 128 rows, all 512 dims.
-template <int RB, bool FP8, bool PACKED>
+// QF8: the fp8 QK of wide_core.h (wide waves over an fp8 pool; options qk =
+// SMD_QK_FP8).
+template <int RB, bool FP8, bool PACKED, bool QF8 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void persistent_kernel(PersistArgs pa) {
   constexpr bool WIDE = RB == 8;
+  static_assert(!QF8 || (WIDE && FP8), "the fp8 QK runs on the wide waves over an fp8 pool");
   constexpr int DS = WIDE ? 1 : 4 / RB;
   constexpr int NC = 16 / DS, ND = 32 / DS;
   constexpr int ROWS = 16 * RB;
-  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemWide<wide_ring<FP8>()>, Smem<DS>> sm;
+  using SmemW = std::conditional_t<QF8, SmemWideQ<7>, SmemWide<wide_ring<FP8>()>>;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<WIDE, SmemW, Smem<DS>> sm;
   __shared__ int s_red[4];
   __shared__ int s_last;
   __shared__ uint32_t s_arrived;
@@ -426,20 +430,33 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
       const int64_t qbase = (int64_t)b * a.M + mq0;
       const int64_t qrow = qbase + (lane & 31);
       const int hq = (int)(qrow % a.H);
-      bf16x8 qreg[wide_qreg<wide_ring<FP8>()>()];  // loaded by attend_range_wide
       WideState w;
       WideDma dm = {nullptr, nullptr};
       if constexpr (WIDE && wide_ring<FP8>()) {
-        __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kRawSlots * kRawSlot];
+        __shared__ __attribute__((aligned(1024))) uint8_t s_raw[raw_slots<QF8>() * raw_slot<QF8>()];
         __shared__ __attribute__((aligned(16))) int32_t s_ibuf[2 * kIdxBlock];
         dm = WideDma{(uint8_t SMD_LDS *)s_raw, (int32_t SMD_LDS *)s_ibuf};
       }
-      attend_range_wide<FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, qbase, qreg,
-                                            wl, w);
+      uint8_t SMD_LDS *stage;
+      float SMD_LDS *tbl;  // merge weights: free until the next piece's walk
+      if constexpr (QF8) {
+        // the walk recomputes its lane offsets: this kernel's other live state
+        // leaves no registers for them (kept, they spill inside the loop, even
+        // with two of q's blocks moved to LDS)
+        QF8Regs<7> q;  // loaded by attend_range_wide_qf8
+        attend_range_wide_qf8<false, false, 7>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, qbase, q, wl,
+                                               w);
+        stage = dm.raw + wave * kStageWave;
+        tbl = (float SMD_LDS *)&sm.tile[0][0] + wave * 512;
+      } else {
+        bf16x8 qreg[wide_qreg<wide_ring<FP8>()>()];  // loaded by attend_range_wide
+        attend_range_wide<FP8, PACKED, false>(a, sm, dm, pa.kv_indices + k0, pos0, pos1, wave, lane, qbase, qreg,
+                                              wl, w);
+        stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
+        tbl = (float SMD_LDS *)&sm.qs[wave][0][0];
+      }
       const float l_tot = half_sum(w.l_run);
       const bool lse_lane = lane < 32;
-      uint8_t SMD_LDS *stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
-      float SMD_LDS *tbl = (float SMD_LDS *)&sm.qs[wave][0][0];  // free until the next piece's Q^T load
       const int t0_fp = (int)((int64_t)fp * total / pa.P);
       // the k-th other piece of a merge: partition fp + k, skipping this one
       // (the register merge runs only when every partition of the span holds a piece)
@@ -528,16 +545,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   }
 }
 
-template <int RB, bool FP8, bool PACKED>
+template <int RB, bool FP8, bool PACKED, bool QF8 = false>
 static hipError_t launch_persistent_t(const PersistArgs &a, hipStream_t stream) {
   const int blocks8 = (a.P + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.d.G));
-  hipLaunchKernelGGL((persistent_kernel<RB, FP8, PACKED>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((persistent_kernel<RB, FP8, PACKED, QF8>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
 template <int RB>
 static hipError_t launch_persistent_rb(const PersistArgs &a, bool fp8, hipStream_t stream) {
+  if constexpr (RB == 8) {
+    if (a.d.qk_fp8) return fp8 ? launch_persistent_t<8, true, false, true>(a, stream) : hipErrorInvalidValue;
+  } else {
+    if (a.d.qk_fp8) return hipErrorInvalidValue;
+  }
   if (fp8) return launch_persistent_t<RB, true, false>(a, stream);
   return a.d.packed ? launch_persistent_t<RB, false, true>(a, stream)
                     : launch_persistent_t<RB, false, false>(a, stream);

@@ -42,6 +42,7 @@ struct DecodeArgs {
   uint16_t *out;           // bf16 [T, H, 512] (direct output when S == 1)
   float *lse;              // [T, H] or null
   int32_t hilo;            // partials are returned to the caller: carry p as bf16 hi + lo
+  bool qk_fp8;             // fp8 QK (options qk = SMD_QK_FP8): wide waves over an fp8 pool only
   // Second source (the sliding-window pool and its index list), same format
   // and strides as the first; indices2 null for one source.  Positions
   // [0, k_main) of an index row are entries of `indices`, [k_main, topk)

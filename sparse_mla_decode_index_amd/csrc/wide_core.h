@@ -40,6 +40,7 @@
 #pragma once
 
 #include "decode_core.h"
+#include "quant.h"
 
 #include <type_traits>
 
@@ -64,14 +65,53 @@ constexpr int kQkPre = 3;          // QK: LDS reads in flight ahead of their MFM
 constexpr int kPvPre = 4;          // PV: V^T operands in flight ahead of their MFMA
 
 // Raw fp8 rows of one tile as the direct-to-LDS loads leave them, per wave
-// (rows 8w..8w+7 of the tile): NoPE [8][32][16 B] at 0 (chunks 28..31 of a
-// row are padding), RoPE [8][8][16 B] at 4096, UE8M0 codes [8][8 B] at 5120
-// (then padding, so that the three slots also hold four 16 KiB staging
-// slices).
+// (rows 8w..8w+7 of the tile, local row r = 0..7): NoPE [8][32][16 B] at 0
+// (logical chunks 28..31 of a row are padding), RoPE [8][8][16 B] at 4096,
+// UE8M0 codes [8][8 B] at 5120, then padding, so that the slots also hold the
+// four 16 KiB staging slices.  Two variants:
+//   - plain (SWZ = false): chunks in order, regions 5504 bytes apart;
+//     only the owning wave reads a region (its dequantisation);
+//   - swizzled (SWZ = true, the fp8 QK): the 16-byte chunks of a row are
+//     permuted (raw_swz_nope / raw_swz_rope) and the regions are 64 mod 256
+//     bytes (16 banks) apart, so that the fp8 QK's operand reads -- one
+//     chunk column of 16 rows of two neighbouring regions per 16 lanes --
+//     touch all 64 banks once.  (Measured on the plain walk, which does not
+//     need it, the swizzle cost 2%.)
 constexpr int kRawNope = 0, kRawRope = 4096, kRawCode = 5120;
-constexpr int kRawWave = 5120 + 384;
-constexpr int kRawSlot = 4 * kRawWave;
-constexpr int kRawSlots = 3;
+template <bool SWZ>
+constexpr int raw_wave() {
+  return SWZ ? 5696 : 5120 + 384;
+}
+template <bool SWZ>
+constexpr int raw_slot() {
+  return 4 * raw_wave<SWZ>();
+}
+static_assert(raw_wave<true>() % 256 == 64 && raw_wave<true>() >= kRawCode + 64, "raw region spacing");
+
+// Position of logical chunk c of local row r in the swizzled layout:
+// c ^ raw_swz_nope(r) (NoPE), c ^ raw_swz_rope(r) (RoPE).  NoPE rows are 512
+// bytes apart (the same banks): the XOR spreads the 8 rows of a region over
+// chunk columns {x, x^1, x^2, x^3, x^8 .. x^11} mod 16, and the next region,
+// 4 columns further, takes the other 8.  RoPE rows are 128 bytes apart (odd
+// rows 8 columns further); the XOR spreads each parity over 4 columns and
+// the next region again takes the rest.
+template <bool SWZ>
+__device__ __forceinline__ int raw_swz_nope(int r) {
+  return SWZ ? ((r & 3) | ((r >> 2) << 3)) : 0;
+}
+template <bool SWZ>
+__device__ __forceinline__ int raw_swz_rope(int r) {
+  return SWZ ? ((r >> 1) & 3) : 0;
+}
+
+// Slots of the raw ring: the plain walk reads tile t out of its slot before
+// the loads of t+3 reuse it; the fp8 QK reads tile t's slot during its
+// compute, so it keeps a fourth.
+template <bool QF8>
+constexpr int raw_slots() {
+  return QF8 ? 4 : 3;
+}
+constexpr int kRawAhead = 3;  // tiles whose loads are in flight ahead of the one computed
 
 template <bool FP8>
 struct SmemWide;
@@ -95,7 +135,7 @@ struct SmemWide<true> {
 };
 
 struct WideDma {
-  uint8_t SMD_LDS *raw;   // [kRawSlots][kRawSlot]: ring of raw fp8 tiles
+  uint8_t SMD_LDS *raw;   // [raw_slots][raw_slot]: ring of raw fp8 tiles
   int32_t SMD_LDS *ibuf;  // [2][kIdxBlock]: index blocks
 };
 
@@ -165,6 +205,83 @@ struct NoWork {
 // is busy.  It must not touch `tile`.
 constexpr int kMidSlots = 8;
 
+// Softmax weights of a tile's scores for a wide wave: score e of this lane is
+// kv row 8(e/4) + 4u + e%4.  Returns false in the max-only pass (nothing to
+// accumulate).  pb (and pl with P_HILO) become PV's B operands.
+template <int PASS, bool P_HILO>
+__device__ __forceinline__ bool softmax_wide(f32x16 &s, uint32_t vbits, int lane, float scale_log2, WideState &w,
+                                             bf16x8 (&pb)[2], bf16x8 (&pl)[2]) {
+  // A tile whose 32 rows are all valid (wave-uniform) skips the masking; the
+  // max then comes from the raw scores (scale_log2 > 0 keeps the order).
+  float tmax;
+  const bool all_valid = vbits == 0xffffffffu && scale_log2 > 0.f;
+  if (all_valid) {
+    tmax = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+    tmax *= scale_log2;
+  } else {
+    const uint32_t vb = vbits >> (4 * (lane >> 5));
+#pragma unroll
+    for (int e = 0; e < 16; ++e)
+      s[e] = ((vb >> (8 * (e >> 2) + (e & 3))) & 1) ? s[e] * scale_log2 : -INFINITY;
+    tmax = s[0];
+#pragma unroll
+    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
+  }
+  tmax = half_max(tmax);
+  if constexpr (PASS == kPassMax) {
+    w.m_ref = fmaxf(w.m_ref, tmax);
+    return false;
+  }
+  if constexpr (PASS == kPassMain) {
+    if (w.m_ref == -INFINITY) w.m_ref = tmax;  // nothing accumulated yet for this row
+    w.overflow |= tmax > w.m_ref + kRefSlackLog2;
+  }
+  const float m_use = (w.m_ref == -INFINITY) ? 0.f : w.m_ref;
+  // p = 2^(x - m_use) with x = s * scale_log2 (unmasked) or s (masked, already scaled)
+  const float mul = all_valid ? scale_log2 : 1.f;
+  float psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const float p = exp2_fast(__builtin_fmaf(s[e], mul, -m_use));
+    psum += p;
+    pb[e >> 3][e & 7] = (__bf16)p;
+    // P_HILO: p = hi + lo with both parts bf16, so the PV product carries
+    // about 16 significant bits of p instead of 8 (FP32-partial precision).
+    if constexpr (P_HILO) pl[e >> 3][e & 7] = (__bf16)(p - (float)pb[e >> 3][e & 7]);
+  }
+  w.l_run += psum;
+  return true;
+}
+
+// PV of a tile for a wide wave: MFMA i = 16h + D covers dims 32D.. and kv
+// rows 16h..16h+15, the V^T operand read from the bf16 tile.
+template <bool P_HILO>
+__device__ __forceinline__ void pv_wide(const uint8_t SMD_LDS *tile, const WideLanes &L, const bf16x8 (&pb)[2],
+                                        const bf16x8 (&pl)[2], WideState &w) {
+  bf16x8 va[kPvPre];
+  auto pv_load = [&](int i) {
+    const int h = i >> 4, D = i & 15;
+    const uint8_t SMD_LDS *base = tile + 16 * kLdsRow * h + 256 * (D >> 2);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(base + L.pv[D & 3]));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(base + L.pv[4 + (D & 3)]));
+    va[i % kPvPre] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+#pragma unroll
+  for (int i = 0; i < kPvPre; ++i) pv_load(i);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const bf16x8 av = va[i % kPvPre];
+    if (i + kPvPre < 32) pv_load(i + kPvPre);
+    const int h = i >> 4, D = i & 15;
+    w.acc[D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[h], w.acc[D], 0, 0, 0);
+    if constexpr (P_HILO) w.acc[D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pl[h], w.acc[D], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int KQ, int PASS, bool P_HILO, class Mid = NoWork, class Post = NoWork>
 __device__ __forceinline__ void compute_tile_wide(const uint8_t SMD_LDS *tile, const bf16x8 (&qreg)[KQ],
                                                   const uint8_t SMD_LDS *qs, const WideLanes &L, uint32_t vbits,
@@ -193,71 +310,8 @@ __device__ __forceinline__ void compute_tile_wide(const uint8_t SMD_LDS *tile, c
   }
   post(0);
 
-  // ---- softmax weights: score e of this lane is kv row 8(e/4) + 4u + e%4.
-  // A tile whose 32 rows are all valid (wave-uniform) skips the masking; the
-  // max then comes from the raw scores (scale_log2 > 0 keeps the order).
-  float tmax;
-  const bool all_valid = vbits == 0xffffffffu && scale_log2 > 0.f;
-  if (all_valid) {
-    tmax = s[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
-    tmax *= scale_log2;
-  } else {
-    const uint32_t vb = vbits >> (4 * (lane >> 5));
-#pragma unroll
-    for (int e = 0; e < 16; ++e)
-      s[e] = ((vb >> (8 * (e >> 2) + (e & 3))) & 1) ? s[e] * scale_log2 : -INFINITY;
-    tmax = s[0];
-#pragma unroll
-    for (int e = 1; e < 16; ++e) tmax = fmaxf(tmax, s[e]);
-  }
-  tmax = half_max(tmax);
-  if constexpr (PASS == kPassMax) {
-    w.m_ref = fmaxf(w.m_ref, tmax);
-    return;
-  }
-  if constexpr (PASS == kPassMain) {
-    if (w.m_ref == -INFINITY) w.m_ref = tmax;  // nothing accumulated yet for this row
-    w.overflow |= tmax > w.m_ref + kRefSlackLog2;
-  }
-  const float m_use = (w.m_ref == -INFINITY) ? 0.f : w.m_ref;
-  // p = 2^(x - m_use) with x = s * scale_log2 (unmasked) or s (masked, already scaled)
-  const float mul = all_valid ? scale_log2 : 1.f;
-  float psum = 0.f;
   bf16x8 pb[2], pl[2];
-#pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const float p = exp2_fast(__builtin_fmaf(s[e], mul, -m_use));
-    psum += p;
-    pb[e >> 3][e & 7] = (__bf16)p;
-    // P_HILO: p = hi + lo with both parts bf16, so the PV product carries
-    // about 16 significant bits of p instead of 8 (FP32-partial precision).
-    if constexpr (P_HILO) pl[e >> 3][e & 7] = (__bf16)(p - (float)pb[e >> 3][e & 7]);
-  }
-  w.l_run += psum;
-
-  // ---- PV: MFMA i = 16h + D covers dims 32D.. and kv rows 16h..16h+15
-  bf16x8 va[kPvPre];
-  auto pv_load = [&](int i) {
-    const int h = i >> 4, D = i & 15;
-    const uint8_t SMD_LDS *base = tile + 16 * kLdsRow * h + 256 * (D >> 2);
-    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(base + L.pv[D & 3]));
-    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(base + L.pv[4 + (D & 3)]));
-    va[i % kPvPre] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  };
-#pragma unroll
-  for (int i = 0; i < kPvPre; ++i) pv_load(i);
-  __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const bf16x8 av = va[i % kPvPre];
-    if (i + kPvPre < 32) pv_load(i + kPvPre);
-    const int h = i >> 4, D = i & 15;
-    w.acc[D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pb[h], w.acc[D], 0, 0, 0);
-    if constexpr (P_HILO) w.acc[D] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, pl[h], w.acc[D], 0, 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-  }
+  if (softmax_wide<PASS, P_HILO>(s, vbits, lane, scale_log2, w, pb, pl)) pv_wide<P_HILO>(tile, L, pb, pl, w);
 }
 
 // Walk the range's tiles once with one staged register set (bf16 and fp8
@@ -324,11 +378,6 @@ __device__ __forceinline__ void lds_dma(const void *src, uint8_t SMD_LDS *dst) {
     asm volatile("global_load_lds_dword %0, off" ::"v"(va), "{m0}"(m0) : "memory");
 }
 
-// Direct-to-LDS loads of this wave's 8 rows of a tile (indices at tidx) into
-// its raw region `dst` (layout above): loads 0..3 bring the NoPE of rows
-// 2k + (lane >> 5), load 4 the RoPE of row lane >> 3, load 5 the codes, 4
-// bytes per lane (lanes 0..15: row lane / 2, half lane % 2).  Invalid rows and positions past p1 read the
-// zero row, as in load_rows.
 // The 8 indices at p (the same for every lane), read behind the compiler's back.
 __device__ __forceinline__ void lds_read_idx8(const int32_t SMD_LDS *p, uint32_t (&w)[8]) {
   u32x4 lo, hi;
@@ -368,29 +417,44 @@ __device__ __forceinline__ uint32_t pick8(const uint32_t (&w)[8], int r) {
   return (r & 4) ? f : e;
 }
 
-__device__ __forceinline__ void dma_rows_fp8(const DecodeArgs &a, const int32_t SMD_LDS *tidx, int first_pos, int p1,
-                                             int wave, int lane, uint8_t SMD_LDS *dst) {
-  uint32_t widx[8];
-  lds_read_idx8(tidx + wave * (kBK / 4), widx);
+// Direct-to-LDS loads of this wave's 8 rows of a tile (indices at tidx) into
+// its raw region `dst` (layout above): loads 0..3 bring the NoPE of rows
+// 2k + (lane >> 5), load 4 the RoPE of row lane >> 3, load 5 the codes, 4
+// bytes per lane (lanes 0..15: row lane / 2, half lane % 2).  Invalid rows
+// and positions past p1 read the zero row, as in load_rows.
+// dma_rows_fp8_part issues part `part` of them: 0 and 1 the NoPE of rows
+// 0..3 and 4..7 (two loads each), 2 the RoPE and the codes; widx holds the
+// wave's 8 indices.
+template <bool SWZ>
+__device__ __forceinline__ void dma_rows_fp8_part(const DecodeArgs &a, const uint32_t (&widx)[8], int first_pos,
+                                                  int p1, int wave, int lane, uint8_t SMD_LDS *dst, int part) {
   const int rows_left = p1 - first_pos - wave * (kBK / 4);
   const uint8_t *z = g_zero_row;
-  // Padding lanes re-read a chunk of their own row (lanes 28..31 of a half
-  // read chunk 27, code lanes 16..63 repeat lanes 0..15): the zero row is one
-  // cache line that every wave would hit at once.
-  const int c = min(lane & 31, 27);
+  // Padding positions re-read a chunk of their own row (chunk 27; code lanes
+  // 16..63 repeat lanes 0..15): the zero row is one cache line that every
+  // wave would hit at once.
+  if (part < 2) {
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    const int r = 2 * k + (lane >> 5);
-    const uint32_t idx = (lane >> 5) ? widx[2 * k + 1] : widx[2 * k];
-    const bool v = r < rows_left && idx < a.num_rows32;
-    const uint8_t *src = v ? a.kv_nope + (uint64_t)idx * (uint64_t)a.nope_stride_b + 16 * c : z + 16 * c;
-    lds_dma<16>(src, dst + kRawNope + 1024 * k);
+    for (int kk = 0; kk < 2; ++kk) {
+      const int k = 2 * part + kk;
+      const int r = 2 * k + (lane >> 5);
+      const int c = min((lane & 31) ^ raw_swz_nope<SWZ>(r), 27);  // the logical chunk landing at position lane & 31
+      // widx[2k + (lane >> 5)] with a mask, not a select: a select between two
+      // elements of widx may be folded into an indexed load, which goes through
+      // scratch memory
+      const uint32_t idx = widx[2 * k] ^ ((widx[2 * k] ^ widx[2 * k + 1]) & (0u - (uint32_t)(lane >> 5)));
+      const bool v = r < rows_left && idx < a.num_rows32;
+      const uint8_t *src = v ? a.kv_nope + (uint64_t)idx * (uint64_t)a.nope_stride_b + 16 * c : z + 16 * c;
+      lds_dma<16>(src, dst + kRawNope + 1024 * k);
+    }
+    return;
   }
   {
     const int r = lane >> 3;
+    const int c = (lane & 7) ^ raw_swz_rope<SWZ>(r);
     const uint32_t idx = pick8(widx, r);
     const bool v = r < rows_left && idx < a.num_rows32;
-    const uint8_t *src = (v ? a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b : z) + 16 * (lane & 7);
+    const uint8_t *src = (v ? a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b : z) + 16 * c;
     lds_dma<16>(src, dst + kRawRope);
   }
   const int r = (lane >> 1) & 7;
@@ -398,6 +462,15 @@ __device__ __forceinline__ void dma_rows_fp8(const DecodeArgs &a, const int32_t 
   const bool v = r < rows_left && idx < a.num_rows32;
   const uint8_t *src = (v ? a.kv_scale + (uint64_t)idx * (uint64_t)a.scale_stride_b : z) + 4 * (lane & 1);
   lds_dma<4>(src, dst + kRawCode);
+}
+
+template <bool SWZ>
+__device__ __forceinline__ void dma_rows_fp8(const DecodeArgs &a, const int32_t SMD_LDS *tidx, int first_pos, int p1,
+                                             int wave, int lane, uint8_t SMD_LDS *dst) {
+  uint32_t widx[8];
+  lds_read_idx8(tidx + wave * (kBK / 4), widx);
+#pragma unroll
+  for (int part = 0; part < 3; ++part) dma_rows_fp8_part<SWZ>(a, widx, first_pos, p1, wave, lane, dst, part);
 }
 
 // Index block k straight into LDS: wave w's lanes load positions
@@ -410,31 +483,38 @@ __device__ __forceinline__ void dma_idx_block(const int32_t *row_idx, int p0, in
 
 // This wave's raw rows (its own region, landed) in the register layout of
 // Staged<true>, ready for store_rows<true>; read behind the compiler's back.
+template <bool SWZ>
 __device__ __forceinline__ void raw_to_staged(const uint8_t SMD_LDS *src, Staged<true> &st) {
   // The lane id comes from an opaque asm so that the lane offsets below are
   // recomputed in the loop rather than hoisted: hoisted, they get spilled,
   // and the wait for their reload would land in the loop and drain the ring.
   const int lane = opaque_lane();
+  const int h = lane >> 5;
   const int c = min(lane & 31, 27);
-  const uint32_t a1 = (uint32_t)(uintptr_t)(src + kRawNope + ((lane >> 5) * 32 + c) * 16);
-  const uint32_t a2 = (uint32_t)(uintptr_t)(src + kRawCode + (lane >> 5) * 8 + (c >> 2));
-  const uint32_t a3 = (uint32_t)(uintptr_t)(src + kRawRope + lane * 16);
-  // row 2j + (lane >> 5): NoPE at a1 + 1024 j, code at a2 + 16 j
-  static_assert(kRawCode <= 65535 - 48 && kRawNope + 3072 <= 65535, "ds offsets");
+  // logical chunk c of row 2j + h sits at position c ^ raw_swz_nope(2j + h)
+  const uint32_t a0 = (uint32_t)(uintptr_t)(src + kRawNope + 512 * h);
+  uint32_t an[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) an[j] = a0 + 1024 * j + 16 * (c ^ raw_swz_nope<SWZ>(2 * j + h));
+  const uint32_t a2 = (uint32_t)(uintptr_t)(src + kRawCode + h * 8 + (c >> 2));
+  const int rr = lane >> 3;  // RoPE: logical chunk lane & 7 of row lane >> 3
+  const uint32_t a3 = (uint32_t)(uintptr_t)(src + kRawRope + 128 * rr + 16 * ((lane & 7) ^ raw_swz_rope<SWZ>(rr)));
+  // the code of row 2j + h at a2 + 16 j
+  static_assert(kRawCode <= 65535 - 48, "ds offsets");
   asm volatile(
       "ds_read_b128 %0, %9\n\t"
-      "ds_read_b128 %1, %9 offset:1024\n\t"
-      "ds_read_b128 %2, %9 offset:2048\n\t"
-      "ds_read_b128 %3, %9 offset:3072\n\t"
-      "ds_read_u8 %4, %10\n\t"
-      "ds_read_u8 %5, %10 offset:16\n\t"
-      "ds_read_u8 %6, %10 offset:32\n\t"
-      "ds_read_u8 %7, %10 offset:48\n\t"
-      "ds_read_b128 %8, %11\n\t"
+      "ds_read_b128 %1, %10\n\t"
+      "ds_read_b128 %2, %11\n\t"
+      "ds_read_b128 %3, %12\n\t"
+      "ds_read_u8 %4, %13\n\t"
+      "ds_read_u8 %5, %13 offset:16\n\t"
+      "ds_read_u8 %6, %13 offset:32\n\t"
+      "ds_read_u8 %7, %13 offset:48\n\t"
+      "ds_read_b128 %8, %14\n\t"
       "s_waitcnt lgkmcnt(0)"
       : "=&v"(st.v[0]), "=&v"(st.v[1]), "=&v"(st.v[2]), "=&v"(st.v[3]), "=&v"(st.code[0]), "=&v"(st.code[1]),
         "=&v"(st.code[2]), "=&v"(st.code[3]), "=&v"(st.rope)
-      : "v"(a1), "v"(a2), "v"(a3)
+      : "v"(an[0]), "v"(an[1]), "v"(an[2]), "v"(an[3]), "v"(a2), "v"(a3)
       : "memory");
 }
 
@@ -476,7 +556,7 @@ __device__ __forceinline__ int stage_off(int q, int c) { return q * kStageRow + 
 template <bool RING>
 __device__ __forceinline__ uint8_t SMD_LDS *wide_stage(SmemWide<RING> &sm, const WideDma &dm, int wave) {
   if constexpr (RING) {
-    static_assert(kRawSlots * kRawSlot >= 4 * kStageWave, "staging slices fit the raw ring");
+    static_assert(raw_slots<false>() * raw_slot<false>() >= 4 * kStageWave, "staging slices fit the raw ring");
     return dm.raw + wave * kStageWave;
   } else {
     static_assert(sizeof(sm.tile) >= 4 * kStageWave, "staging slices fit the tiles");
@@ -557,7 +637,8 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
   auto tidx = [&](int k) {
     return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
   };
-  auto slot = [&](int k) { return raw + (k % kRawSlots) * kRawSlot + wave * kRawWave; };
+  constexpr int kSlots = raw_slots<false>();
+  auto slot = [&](int k) { return raw + (k % kSlots) * raw_slot<false>() + wave * raw_wave<false>(); };
   // A real vmcnt(0) (not inline asm) so that the compiler's wait bookkeeping
   // starts the walk with nothing in flight: the loads it cannot see are
   // counted by the hardware too, and a wait it would otherwise keep for an
@@ -570,14 +651,14 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
   }
   __syncthreads();
 #pragma unroll
-  for (int k = 0; k < kRawSlots; ++k) dma_rows_fp8(a, tidx(k), p0 + k * kBK, p1, wave, lane, slot(k));
+  for (int k = 0; k < kRawAhead; ++k) dma_rows_fp8<false>(a, tidx(k), p0 + k * kBK, p1, wave, lane, slot(k));
   for (int t = 0; t < ntiles; ++t) {
-    wait_vm<6 * (kRawSlots - 1)>();
+    wait_vm<6 * (kRawAhead - 1)>();
     Staged<true> st;
-    raw_to_staged(slot(t), st);
+    raw_to_staged<false>(slot(t), st);
     const uint32_t v_cur = tile_valid_bits_dma(tidx(t), p0 + t * kBK, p1, lane, a.num_rows32);
     barrier_lds();  // A (this wave's raw reads of slot t % 3 are done too)
-    dma_rows_fp8(a, tidx(t + kRawSlots), p0 + (t + kRawSlots) * kBK, p1, wave, lane, slot(t));
+    dma_rows_fp8<false>(a, tidx(t + kRawAhead), p0 + (t + kRawAhead) * kBK, p1, wave, lane, slot(t + kRawAhead));
     if (t % kTilesPerIdxBlock == 0) {
       const int nb = t / kTilesPerIdxBlock + 1;
       dma_idx_block(row_idx, p0, p1, nb, wave, lane, ib0 + (nb & 1) * kIdxBlock);
@@ -587,6 +668,322 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
     compute_tile_wide<kQRegDma, PASS, P_HILO>(tile, qreg, qs, L, v_cur, lane, a.scale_log2, w);
   }
   wait_vm<0>();  // no load may land in LDS after the walk
+}
+
+// ---------------------------------------------------------------------------
+// fp8 QK ("a8w8", the persistent decode object of the aiter page "[ASM][HIP]
+// [MLA v4 nm] Split plan helper and persistent decode kernel", Summary part
+// 2): q_nope is quantised the way the cache writer quantises a latent row's
+// NoPE (UE8M0 code per 64-dim block, E4M3FN bytes; quant.h), and the NoPE
+// half of QK runs on v_mfma_scale_f32_32x32x64_f8f6f4 straight from the
+// pool's bytes, the pool's UE8M0 codes and q's codes as the E8M0 block scales
+// of the two operands.  RoPE (bf16 in the pool) stays on the bf16 MFMA, and P
+// and PV stay bf16: V's scales vary along PV's contraction (one code per kv
+// row and 64 dims), which the block scales of the MFMA cannot express.
+//
+// Operand layout of the scaled MFMA (checked on gfx950 with an in-bounds
+// probe): lane l feeds row (A) / column (B) l mod 32 with 32 bytes, the
+// first 16 in k-block 0 and the next 16 in k-block 1 of the 64 k, paired
+// byte for byte between A and B; the scale of k-block kb of row / column r
+// comes from lane r + 32 kb (byte opsel of its scale register).  Here both
+// k-blocks of a lane carry one 64-dim block's values, so lane (r, u = l / 32)
+// holds dims 64b + 32u .. +32 in order on both sides and the two lanes of a
+// row carry the same code.
+
+// q of a wide wave's 32 query rows (lane l: row l mod 32, u = l / 32).
+// NQF of the 7 blocks sit in registers, the others in the wave's LDS region.
+template <int NQF>
+struct QF8Regs {
+  i32x8 f[NQF];      // e4m3 bytes of NoPE dims 64b + 32u .. +32 (block b < NQF)
+  uint32_t code[2];  // UE8M0 code of block b in byte b mod 4 of code[b / 4]
+};
+
+// q's operands in LDS, per wave: the RoPE part (bf16 B operands of 4
+// k-steps; k-step j of lane l at (64 j + l) * 16, dims 448 + 16j + 8u .. +8),
+// then NoPE blocks b >= NQF (block b of lane l at kQRopeWave + ((b - NQF) * 64
+// + l) * 32).
+constexpr int kQRopeWave = 4 * 64 * 16;
+template <int NQF>
+constexpr int qf8_lds_wave() {
+  return kQRopeWave + (7 - NQF) * 64 * 32;
+}
+
+// Load and quantise q for the fp8 QK: the rows go row-wise through the
+// wave's staging slice as in load_q_wide; lane (r, u) then picks up the 32
+// values of its half of each block, the pair (r, u = 0 / 1) agrees on the
+// block's code with one permlane32 swap, and each value is stored as the
+// E4M3FN byte nearest to x * 2^(127 - code) (the hardware conversion rounds
+// to nearest even; the scaling by a power of two is exact).
+template <int NQF>
+__device__ __forceinline__ void load_q_wide_fp8(const DecodeArgs &a, int64_t qbase, uint8_t SMD_LDS *stage,
+                                                uint8_t SMD_LDS *qrope, QF8Regs<NQF> &q) {
+  const int lane = opaque_lane();
+  const int c = lane & 31, hr = lane >> 5;
+  u32x4 v[2][16];
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {  // rows 2k + hr, 16-byte chunk c of this half
+      const int64_t row = qbase + 2 * k + hr;
+      const uint16_t *src;
+      if (half == 0)
+        src = a.q_nope + row * kNope + 8 * c;
+      else
+        src = c < 24 ? a.q_nope + row * kNope + 256 + 8 * c : a.q_rope + row * kRope + 8 * (c - 24);
+      v[half][k] = *(const u32x4 *)src;
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  q.code[0] = q.code[1] = 0u;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) *(u32x4 SMD_LDS *)(stage + stage_off(2 * k + hr, c)) = v[half][k];
+    // block b of this half: chunks 8(b mod 4) + 4 hr + i of row c (dims 64b + 32 hr + 8i ..)
+#pragma unroll
+    for (int bb = 0; bb < (half == 0 ? 4 : 3); ++bb) {
+      const int b = 4 * half + bb;
+      float x[32];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const u32x4 w4 = *(const u32x4 SMD_LDS *)(stage + stage_off(c, 8 * bb + 4 * hr + i));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[8 * i + 2 * e] = __uint_as_float(w4[e] << 16);
+          x[8 * i + 2 * e + 1] = __uint_as_float(w4[e] & 0xFFFF0000u);
+        }
+      }
+      float m = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) m = fmaxf(m, fabsf(x[i]));  // fmaxf ignores NaN
+      const uint32_t code = ue8m0_code(half_max(m));
+      const int e = 127 - (int)code;
+      i32x8 f;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        int wd = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * k], e), ldexpf(x[4 * k + 1], e), 0, false);
+        wd = __builtin_amdgcn_cvt_pk_fp8_f32(ldexpf(x[4 * k + 2], e), ldexpf(x[4 * k + 3], e), wd, true);
+        f[k] = wd;
+      }
+      if (b < NQF)
+        q.f[b < NQF ? b : 0] = f;
+      else
+        *(i32x8 SMD_LDS *)(qrope + kQRopeWave + ((b - NQF) * 64 + lane) * 32) = f;
+      q.code[b >> 2] |= code << (8 * (b & 3));
+    }
+    if (half == 1) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(bf16x8 SMD_LDS *)(qrope + (64 * j + lane) * 16) = *(const bf16x8 SMD_LDS *)(stage + stage_off(c, 24 + 2 * j + hr));
+    }
+  }
+}
+
+// Per-lane byte offsets, from a slot's first region, of the fp8 QK's A
+// operands in the swizzled ring (lane l: kv row R = l mod 32 of the tile,
+// which is local row r = R mod 8 of region R / 8; u = l / 32).  NoPE block b,
+// half e: logical chunk 4b + 2u + e sits at position 4 (b ^ 2 hi) + ((2u + e)
+// ^ (r mod 4)) with hi = r / 4, i.e. at nope[e][(b / 2) mod 2] + 64 b.  RoPE
+// k-step j: chunk 2j + u at position 2 (j ^ (s / 2)) + (u ^ (s mod 2)) with
+// s = raw_swz_rope(r), i.e. at rope[j mod 2] + 32 j.  code: the row's 8 code
+// bytes.
+struct RawLanes {
+  uint32_t nope[2][2];
+  uint32_t rope[2];
+  uint32_t code;
+};
+
+__device__ __forceinline__ RawLanes raw_lanes(int lane) {
+  constexpr int W = raw_wave<true>();
+  const int R = lane & 31, u = lane >> 5, reg = R >> 3, r = R & 7, hi = r >> 2;
+  const int rowbase = reg * W + kRawNope + (r >> 1) * 1024 + (r & 1) * 512;
+  RawLanes K;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int lo = (2 * u + e) ^ (r & 3);
+    K.nope[e][0] = (uint32_t)(rowbase + 16 * lo + 128 * hi);
+    K.nope[e][1] = (uint32_t)(rowbase + 16 * lo - 128 * hi);
+  }
+  const int sr = raw_swz_rope<true>(r);
+  const int rb = reg * W + kRawRope + 128 * r + 16 * (u ^ (sr & 1));
+  K.rope[0] = (uint32_t)(rb + 32 * (sr >> 1));
+  K.rope[1] = (uint32_t)(rb - 32 * (sr >> 1));
+  K.code = (uint32_t)(reg * W + kRawCode + 8 * r);
+  return K;
+}
+
+// One scaled fp8 MFMA (e4m3 A and B) whose block scales are byte `sel` of the
+// scale registers (the byte select is an immediate; sel folds to a constant
+// once the caller's loop is unrolled).
+__device__ __forceinline__ f32x16 mfma_fp8_block(int sel, const i32x8 &a, const i32x8 &b, const f32x16 &c, int sa,
+                                                 int sb) {
+  switch (sel) {
+    case 0: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, sa, 0, sb);
+    case 1: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 1, sa, 1, sb);
+    case 2: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 2, sa, 2, sb);
+    default: return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 3, sa, 3, sb);
+  }
+}
+
+// S^T[32 kv x 32 q] of one tile from its raw slot: 7 scaled fp8 MFMAs (k = 64
+// dims each) and 4 bf16 MFMAs (RoPE).  The slot is read with plain LDS loads:
+// its loads have landed and been published by a barrier before this runs.
+template <int NQF>
+__device__ __forceinline__ f32x16 qk_wide_fp8(const uint8_t SMD_LDS *slot, const QF8Regs<NQF> &q,
+                                              const uint8_t SMD_LDS *qrope, int lane, const RawLanes &K) {
+  f32x16 s;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) s[e] = 0.f;
+  const u32x2 kc = *(const u32x2 SMD_LDS *)(slot + K.code);
+  u32x4 ka[2][2];
+  i32x8 qa[2];  // q blocks >= NQF, read with their K operands
+  auto ld = [&](int b) {
+    const int sel = (b >> 1) & 1;
+    ka[b & 1][0] = *(const u32x4 SMD_LDS *)(slot + K.nope[0][sel] + 64 * b);
+    ka[b & 1][1] = *(const u32x4 SMD_LDS *)(slot + K.nope[1][sel] + 64 * b);
+    if (b >= NQF) qa[b & 1] = *(const i32x8 SMD_LDS *)(qrope + kQRopeWave + ((b - NQF) * 64 + lane) * 32);
+  };
+  bf16x8 kr[2], qr[2];
+  auto ldr = [&](int j) {
+    kr[j & 1] = *(const bf16x8 SMD_LDS *)(slot + K.rope[j & 1] + 32 * j);
+    qr[j & 1] = *(const bf16x8 SMD_LDS *)(qrope + (64 * j + lane) * 16);
+  };
+  ld(0);
+  ld(1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int b = 0; b < 7; ++b) {
+    const u32x4 lo = ka[b & 1][0], hi = ka[b & 1][1];
+    const i32x8 av = {(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    if (b + 2 < 7) ld(b + 2);
+    if (b >= 5) ldr(b - 5);  // the RoPE operands take the freed NoPE buffers' turn
+    const i32x8 bv = b < NQF ? q.f[b < NQF ? b : 0] : qa[b & 1];
+    s = mfma_fp8_block(b & 3, av, bv, s, (int)kc[b >> 2], (int)q.code[b >> 2]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const bf16x8 av = kr[j & 1], bv = qr[j & 1];
+    if (j + 2 < 4) ldr(j + 2);
+    s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, s, 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  return s;
+}
+
+// Walk the range's tiles once with the fp8 QK: a ring of four swizzled raw
+// slots, tile k's loads going to slot k % 4 at step k - 3.  Step t:
+//   wait for this wave's loads of tile t (12 younger loads allowed: tiles
+//   t+1 and t+2);
+//   barrier A (every wave's rows of tile t have landed; everyone is done with
+//   the PV of t-1, so the bf16 tile is free, and with the QK of t-1, so slot
+//   (t+3) % 4 is free);
+//   issue the loads of tile t+3 (and, at t % 8 == 0, index block t/8 + 1);
+//   dequantise this wave's rows of tile t (read out of the slot before
+//   barrier A) into the bf16 tile for PV; QK of tile t from its raw slot;
+//   softmax weights;
+//   barrier B (the bf16 tile is complete), PV.
+// (Issuing the loads and the stores between the QK MFMAs instead ran 9%
+// slower on the ragged MTP4 fp8 workload.)
+// The index blocks follow run_split_wide_dma's schedule.
+template <bool P_HILO, int PASS, bool RESIDENT, int NQF>
+__device__ __forceinline__ void run_split_wide_qf8(const DecodeArgs &a, uint8_t SMD_LDS *tile,
+                                                   const uint8_t SMD_LDS *qrope, const WideDma &dm,
+                                                   const int32_t *row_idx, int p0, int p1, int wave, int lane,
+                                                   const QF8Regs<NQF> &q, const WideLanes &L, WideState &w) {
+  const int ntiles = (p1 - p0 + kBK - 1) / kBK;
+  if (ntiles <= 0) return;
+  constexpr int kSlots = raw_slots<true>();
+  uint8_t SMD_LDS *raw = dm.raw;
+  int32_t SMD_LDS *ib0 = dm.ibuf;
+  auto tidx = [&](int k) {
+    return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
+  };
+  auto slot = [&](int k) { return raw + (k % kSlots) * raw_slot<true>(); };
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), as in run_split_wide_dma
+  if constexpr (PASS != kPassMain) {
+    __syncthreads();
+    dma_idx_block(row_idx, p0, p1, 0, wave, lane, ib0);
+    wait_vm<0>();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kRawAhead; ++k)
+    dma_rows_fp8<true>(a, tidx(k), p0 + k * kBK, p1, wave, lane, slot(k) + wave * raw_wave<true>());
+  // Lane offsets inside the loop come from opaque_lane(): recomputed (a few
+  // VALU) rather than hoisted and spilled, since every spill reload would
+  // wait for the whole ring of loads in flight.
+  const RawLanes K0 = raw_lanes(lane);
+  const WideLanes L0 = wide_lanes(lane);
+  for (int t = 0; t < ntiles; ++t) {
+    // RESIDENT keeps the lane offsets in registers; otherwise they come from
+    // opaque_lane() and are recomputed (a few VALU) rather than hoisted and
+    // spilled, since every spill reload would wait for the whole ring of
+    // loads in flight
+    const int ln = RESIDENT ? lane : opaque_lane();
+    wait_vm<6 * (kRawAhead - 1)>();
+    Staged<true> st;
+    if constexpr (PASS != kPassMax) raw_to_staged<true>(slot(t) + wave * raw_wave<true>(), st);
+    const uint32_t v_cur = tile_valid_bits_dma(tidx(t), p0 + t * kBK, p1, ln, a.num_rows32);
+    barrier_lds();  // A
+    dma_rows_fp8<true>(a, tidx(t + kRawAhead), p0 + (t + kRawAhead) * kBK, p1, wave,
+                       RESIDENT ? lane : opaque_lane(), slot(t + kRawAhead) + wave * raw_wave<true>());
+    if (t % kTilesPerIdxBlock == 0) {
+      const int nb = t / kTilesPerIdxBlock + 1;
+      dma_idx_block(row_idx, p0, p1, nb, wave, lane, ib0 + (nb & 1) * kIdxBlock);
+    }
+    if constexpr (PASS != kPassMax) store_rows<true, kLay32>(tile, wave, RESIDENT ? lane : opaque_lane(), st);
+    f32x16 s = qk_wide_fp8(slot(t), q, qrope, ln, RESIDENT ? K0 : raw_lanes(opaque_lane()));
+    bf16x8 pb[2], pl[2];
+    const bool acc = softmax_wide<PASS, P_HILO>(s, v_cur, ln, a.scale_log2, w, pb, pl);
+    barrier_lds();  // B
+    if (acc) pv_wide<P_HILO>(tile, RESIDENT ? L0 : wide_lanes(opaque_lane()), pb, pl, w);
+  }
+  wait_vm<0>();  // no load may land in LDS after the walk
+}
+
+// The bf16 tile of the fp8-QK walk and q's RoPE operands (its raw ring and
+// index blocks are the WideDma objects).
+template <int NQF>
+struct SmemWideQ {
+  uint8_t tile[1][kTileBytes];
+  uint8_t qrope[4][qf8_lds_wave<NQF>()];  // q's operands in LDS, per wave
+};
+
+// attend_range_wide for the fp8 QK (fp8 pools): the main pass, and the
+// exact-max two-pass redo when some score overflowed its reference max.
+// Ends with a barrier; the tile and the ring are then free.  RESIDENT: the
+// walk keeps its lane offsets in registers (a caller with registers to
+// spare), else it recomputes them each tile.  NQF of q's 7 fp8 blocks stay
+// in registers, the rest in LDS.
+template <bool P_HILO, bool RESIDENT, int NQF>
+__device__ __forceinline__ void attend_range_wide_qf8(const DecodeArgs &a, SmemWideQ<NQF> &sm, const WideDma &dm,
+                                                      const int32_t *row_idx, int p0, int p1, int wave, int lane,
+                                                      int64_t qbase, QF8Regs<NQF> &q, const WideLanes &L,
+                                                      WideState &w) {
+  auto reset = [&]() {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w.acc[d][e] = 0.f;
+    }
+    w.m_ref = -INFINITY;
+    w.l_run = 0.f;
+  };
+  uint8_t SMD_LDS *tile = (uint8_t SMD_LDS *)&sm.tile[0][0];
+  uint8_t SMD_LDS *qrope = (uint8_t SMD_LDS *)&sm.qrope[wave][0];
+  __syncthreads();  // the tile, the ring and the index blocks may still be in use by a previous range
+  if (p1 > p0) dma_idx_block(row_idx, p0, p1, 0, wave, lane, dm.ibuf);
+  load_q_wide_fp8(a, qbase, dm.raw + wave * kStageWave, qrope, q);
+  reset();
+  w.overflow = false;
+  run_split_wide_qf8<P_HILO, kPassMain, RESIDENT, NQF>(a, tile, qrope, dm, row_idx, p0, p1, wave, lane, q, L, w);
+  if (__syncthreads_or(w.overflow)) {
+    reset();
+    run_split_wide_qf8<P_HILO, kPassMax, RESIDENT, NQF>(a, tile, qrope, dm, row_idx, p0, p1, wave, lane, q, L, w);
+    run_split_wide_qf8<P_HILO, kPassFixed, RESIDENT, NQF>(a, tile, qrope, dm, row_idx, p0, p1, wave, lane, q, L, w);
+  }
+  __syncthreads();  // as in attend_range_wide
 }
 
 // Attend the wide wave's 32 query rows (rows qbase .. qbase + 31 of the
@@ -631,6 +1028,9 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
     walk(std::integral_constant<int, kPassMax>{});
     walk(std::integral_constant<int, kPassFixed>{});
   }
+  // every wave's loads have landed (each waited for its own) and its tile
+  // reads are done before the epilogue stages through the ring or the tiles
+  __syncthreads();
 }
 
 // Outputs of a wide wave's 32 query rows, stored row-wise through the wave's

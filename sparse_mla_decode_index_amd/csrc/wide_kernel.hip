@@ -13,10 +13,12 @@
 
 namespace smd {
 
-template <bool FP8, bool PACKED, bool P_HILO>
+// QF8: the fp8 QK of wide_core.h (fp8 pools; options qk = SMD_QK_FP8).
+template <bool FP8, bool PACKED, bool P_HILO, bool QF8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_wide_kernel(DecodeArgs a) {
+  static_assert(!QF8 || FP8, "the fp8 QK reads an fp8 pool");
   constexpr bool RING = wide_ring<FP8>();
-  __shared__ __attribute__((aligned(1024))) SmemWide<RING> sm;
+  __shared__ __attribute__((aligned(1024))) std::conditional_t<QF8, SmemWideQ<7>, SmemWide<RING>> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -41,18 +43,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 
   WideDma dm = {nullptr, nullptr};
   if constexpr (RING) {
-    __shared__ __attribute__((aligned(1024))) uint8_t s_raw[kRawSlots * kRawSlot];
+    __shared__ __attribute__((aligned(1024))) uint8_t s_raw[raw_slots<QF8>() * raw_slot<QF8>()];
     __shared__ __attribute__((aligned(16))) int32_t s_ibuf[2 * kIdxBlock];
     dm = WideDma{(uint8_t SMD_LDS *)s_raw, (int32_t SMD_LDS *)s_ibuf};
   }
-  bf16x8 qreg[wide_qreg<wide_ring<FP8>()>()];  // loaded by attend_range_wide
   WideState w;
   const WideLanes L = wide_lanes(lane);
-  attend_range_wide<FP8, PACKED, P_HILO>(a, sm, dm, a.indices + (int64_t)b * a.indices_stride, p0, p1, wave, lane,
-                                         qbase, qreg, L, w);
+  uint8_t SMD_LDS *stage;
+  if constexpr (QF8) {
+    QF8Regs<7> q;  // loaded by attend_range_wide_qf8
+    attend_range_wide_qf8<P_HILO, true, 7>(a, sm, dm, a.indices + (int64_t)b * a.indices_stride, p0, p1, wave, lane,
+                                        qbase, q, L, w);
+    static_assert(raw_slots<true>() * raw_slot<true>() >= 4 * kStageWave, "staging slices fit the raw ring");
+    stage = dm.raw + wave * kStageWave;
+  } else {
+    bf16x8 qreg[wide_qreg<wide_ring<FP8>()>()];  // loaded by attend_range_wide
+    attend_range_wide<FP8, PACKED, P_HILO>(a, sm, dm, a.indices + (int64_t)b * a.indices_stride, p0, p1, wave,
+                                           lane, qbase, qreg, L, w);
+    stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
+  }
   const float l_tot = half_sum(w.l_run);
   const bool lse_lane = lane < 32;
-  uint8_t SMD_LDS *stage = wide_stage<wide_ring<FP8>()>(sm, dm, wave);
   const bool direct = a.S == 1 && a.out != nullptr;
   const OutScale sc = direct ? direct_scale(w.m_ref, l_tot, a.sink ? a.sink[head] : -INFINITY)
                              : partial_scale(w.m_ref, l_tot);
@@ -65,23 +76,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
-template <bool FP8, bool PACKED, bool P_HILO>
+template <bool FP8, bool PACKED, bool P_HILO, bool QF8>
 static hipError_t launch_wide_t(const DecodeArgs &a, hipStream_t stream) {
   const int blocks8 = (a.num_units + 7) / 8;
   const dim3 grid((unsigned)(blocks8 * 8 * a.G));
-  hipLaunchKernelGGL((decode_wide_kernel<FP8, PACKED, P_HILO>), grid, dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((decode_wide_kernel<FP8, PACKED, P_HILO, QF8>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
-template <bool FP8, bool PACKED>
+template <bool FP8, bool PACKED, bool QF8 = false>
 static hipError_t launch_wide_f(const DecodeArgs &a, hipStream_t stream) {
-  return a.hilo ? launch_wide_t<FP8, PACKED, true>(a, stream) : launch_wide_t<FP8, PACKED, false>(a, stream);
+  return a.hilo ? launch_wide_t<FP8, PACKED, true, QF8>(a, stream) : launch_wide_t<FP8, PACKED, false, QF8>(a, stream);
 }
 
-// a.G = M / 128; one source only (a.indices2 null).
+// a.G = M / 128; one source only (a.indices2 null); a.qk_fp8 needs an fp8 pool.
 hipError_t launch_decode_wide(const DecodeArgs &a, bool fp8, hipStream_t stream) {
-  if (a.indices2 != nullptr || a.M % kWideRows != 0) return hipErrorInvalidValue;
-  if (fp8) return launch_wide_f<true, false>(a, stream);
+  if (a.indices2 != nullptr || a.M % kWideRows != 0 || (a.qk_fp8 && !fp8)) return hipErrorInvalidValue;
+  if (fp8) return a.qk_fp8 ? launch_wide_f<true, false, true>(a, stream) : launch_wide_f<true, false>(a, stream);
   return a.packed ? launch_wide_f<false, true>(a, stream) : launch_wide_f<false, false>(a, stream);
 }
 

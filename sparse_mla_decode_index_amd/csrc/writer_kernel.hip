@@ -14,47 +14,12 @@
 // (16 bytes) per lane: lanes 0..55 the NoPE dims (lanes 8b..8b+7 = block b),
 // lanes 56..63 the RoPE dims.  HBM-bound: 1 KiB read and 584 bytes written
 // per row, coalesced.
-#include "smd_internal.h"
-
-#include <math.h>
+#include "quant.h"
 
 namespace smd {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// ceil(log2(amax / 448)) + 127 clamped to [0, 254] for amax > 0 (finite or
-// infinite), from the float's fields: amax = (1 + f) 2^E, 448 = 1.75 * 2^8,
-// so the ceiling is E - 8, plus one when the mantissa exceeds 1.75.
-__device__ __forceinline__ uint32_t ue8m0_code(float amax) {
-  if (!(amax > 0.f)) return 0u;       // zero, or every value NaN
-  if (isinf(amax)) return 254u;
-  int bias = 0;
-  if (amax < 1.17549435e-38f) {       // fp32 subnormal: scale into the normal range (exact)
-    amax *= 18446744073709551616.f;   // 2^64
-    bias = 64;
-  }
-  const uint32_t u = __float_as_uint(amax);
-  const int e = (int)(u >> 23) - 127 - bias;
-  const int up = (u & 0x7FFFFFu) > 0x600000u;  // mantissa above 1.75
-  const int c = e - 8 + up + 127;
-  return (uint32_t)(c < 0 ? 0 : (c > 254 ? 254 : c));
-}
-
-// OCP E4M3FN byte of y, round to nearest even, non-saturating, branch-free:
-// below 2^-6 the result is a multiple of 2^-9, which the fp32 add to 2^14
-// rounds to (its ulp is 2^-9); above, the mantissa is rounded to 3 bits with
-// the carry into the exponent, and anything that lands past 0x7E (values
-// beyond 464, infinities, NaN) saturates at the NaN code 0x7F.
-__device__ __forceinline__ uint32_t e4m3fn_rne(float y) {
-  const uint32_t u = __float_as_uint(y);
-  const uint32_t a = u & 0x7FFFFFFFu;
-  const uint32_t sub = __float_as_uint(fabsf(y) + 16384.0f) - 0x46800000u;
-  const uint32_t r = a + 0x7FFFFu + ((a >> 20) & 1u);
-  const uint32_t nrm = (r >> 20) - 960u;  // ((biased exponent - 120) << 3) | mantissa
-  const uint32_t b = a < 0x3C800000u ? sub : nrm;
-  return (b < 0x7Fu ? b : 0x7Fu) | ((u >> 24) & 0x80u);
-}
 
 // Largest value over each group of 8 lanes: swaps within quads (lane ^ 1,
 // lane ^ 2), then lane i with lane 7 - i of its half-row.

@@ -290,7 +290,8 @@ def _persist_ex(opts, **kw):
     (smd._DecodeOptions(kernel=smd.KERNEL_WIDE), "SMD_KERNEL_AUTO"),
     (smd._DecodeOptions(merge=2), "merge"),
     (smd._DecodeOptions(merge=-1), "merge"),
-    (smd._DecodeOptions(reserved=(ctypes.c_int32 * 6)(0, 0, 1, 0, 0, 0)), "reserved"),
+    (smd._DecodeOptions(reserved=(ctypes.c_int32 * 5)(0, 0, 1, 0, 0)), "reserved"),
+    (smd._DecodeOptions(qk=2), "qk"),
 ])
 def test_persistent_ex_rejects_bad_options(opts, msg):
     rc, err = _persist_ex(opts)
@@ -311,6 +312,65 @@ def test_split_kv_rejects_merge_option():
     rc = smd.lib().smd_sparse_mla_decode_ex(0x20000, 0x30000, 4, 64, 1, ctypes.byref(p), 0x40000, 100, 100, None,
                                             0.04, 1, None, None, 0x50000, 0x60000, ctypes.byref(opts), None)
     assert rc == -1 and "persistent" in smd.lib().smd_last_error().decode()
+
+
+def _fp8_pool():
+    return _pool(dtype=smd.KV_FP8_E4M3_UE8M0, nope_stride=448, rope=0x80000, rope_stride=64, scale=0x90000,
+                 scale_stride=8)
+
+
+def _split_ex(opts, pool, H=128, T=4):
+    rc = smd.lib().smd_sparse_mla_decode_ex(0x20000, 0x30000, T, H, 1, ctypes.byref(pool), 0x40000, 100, 100, None,
+                                            0.04, 1, None, None, 0x50000, 0x60000, ctypes.byref(opts), None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("case,code", [
+    ("unknown qk", -1),
+    ("bf16 pool", -2),
+    ("M = 64", -2),
+    ("rows16 kernel", -2),
+    ("pairs kernel", -2),
+])
+def test_split_kv_rejects_qk_fp8_where_it_does_not_run(case, code):
+    """The fp8 QK runs on the wide kernel over one fp8 pool with M a multiple
+    of 128; any other call that asks for it is rejected before a launch."""
+    opts = smd._DecodeOptions(qk=smd.QK_FP8)
+    pool, H = _fp8_pool(), 128
+    if case == "unknown qk":
+        opts = smd._DecodeOptions(qk=3)
+    elif case == "bf16 pool":
+        pool = _pool()
+    elif case == "M = 64":
+        H = 64
+    elif case == "rows16 kernel":
+        opts = smd._DecodeOptions(kernel=smd.KERNEL_ROWS16, qk=smd.QK_FP8)
+    else:
+        opts = smd._DecodeOptions(kernel=smd.KERNEL_PAIRS, qk=smd.QK_FP8)
+    rc, err = _split_ex(opts, pool, H=H)
+    assert rc == code and "qk" in err, (rc, err)
+
+
+def test_two_source_rejects_qk_fp8():
+    opts = smd._DecodeOptions(qk=smd.QK_FP8)
+    p = _fp8_pool()
+    rc = smd.lib().smd_sparse_mla_decode_two_source_ex(0x20000, 0x30000, 4, 128, 1, ctypes.byref(p), 0x40000, 100,
+                                                       100, ctypes.byref(p), 0x48000, 128, 128, None, 0.04, 1, None,
+                                                       None, 0x50000, 0x60000, ctypes.byref(opts), None)
+    assert rc == -2 and "qk" in smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("H,fp8", [(128, False), (64, True)])
+def test_persistent_rejects_qk_fp8_where_it_does_not_run(H, fp8):
+    a = dict(q_nope=0x20000, q_rope=0x30000, B=4, qps=1, ptr=0x40000, flat=0x48000, sink=None, scale=0.04,
+             ws=0x100000, ws_bytes=1 << 30, P=8, out=0x50000, lse=0x60000)
+    p = _fp8_pool() if fp8 else _pool()
+    opts = smd._DecodeOptions(qk=smd.QK_FP8)
+    rc = smd.lib().smd_sparse_mla_decode_persistent_ex(a["q_nope"], a["q_rope"], a["B"], a["qps"], H,
+                                                       ctypes.byref(p), a["ptr"], a["flat"], a["sink"], a["scale"],
+                                                       a["ws"], a["ws_bytes"], a["P"], a["out"], a["lse"],
+                                                       ctypes.byref(opts), None)
+    assert rc == -2 and "qk" in smd.lib().smd_last_error().decode()
 
 
 def test_persistent_workspace_reset_rejects_null():
