@@ -14,7 +14,9 @@ Modules:
                        the persistent kernel's balanced tile partition;
 * ``oracle.writer_ref`` the fp8/UE8M0 cache writer's rule;
 * ``oracle.a8_ref``    the fp8 ("a8w8") QK: q quantised as the writer
-                       quantises, then the decode of ``oracle.ref``.
+                       quantises, then the decode of ``oracle.ref``;
+* ``oracle.paged_ref`` the dense paged GQA decode (separate K and V caches,
+                       a block table, MTP tokens causal among themselves).
 
 Parity status of each function is stated in its docstring.  The host
 planner's exact split count with the library's fitted coefficients is
