@@ -75,6 +75,9 @@ def parse():
     ap.add_argument("--writer", action="store_true",
                     help="time the fp8/UE8M0 cache writer instead of the decode")
     ap.add_argument("--writer-rows", type=int, default=131072, help="latent rows per writer call")
+    ap.add_argument("--paged", action="store_true",
+                    help="time the dense paged GQA decode (the pa_decode page's BF16 D512 MTP4 GQA16 B16 ctx8K "
+                         "case) instead of the sparse decode")
     ap.add_argument("--summarize-trace", type=str, default=None,
                     help="print the per-kernel summary of a rocprofv3 kernel-trace CSV (cold launches apart)")
     ap.add_argument("--matrix", type=str, default=None,
@@ -467,10 +470,147 @@ def writer_main(args):
     print(json.dumps(res), flush=True)
 
 
+def paged_cpu_baseline(w, target_s: float):
+    """The float64 paged oracle on whole sequences (all KV heads) until about
+    target_s seconds of CPU work, scaled to a call by the share of positions."""
+    from oracle import paged_ref
+    mtp = w["mtp"]
+    cl = w["context_lens"]
+    done_pos, elapsed, seqs = 0, 0.0, 0
+    t0 = time.perf_counter()
+    for b in range(w["B"]):
+        sl = slice(b * mtp, (b + 1) * mtp)
+        paged_ref.paged_decode(w["q"][sl], w["k"], w["v"], w["block_tables"][b:b + 1], cl[b:b + 1], w["page"], mtp,
+                               w["softmax_scale"])
+        done_pos += int(cl[b])
+        seqs += 1
+        elapsed = time.perf_counter() - t0
+        if elapsed >= target_s:
+            break
+    per_call = elapsed * float(cl.sum()) / max(done_pos, 1)
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = 1
+    return per_call, f"{seqs} of {w['B']} sequences (all heads, {elapsed:.1f} s), scaled to one call by positions", cores
+
+
+def paged_main(args):
+    """The dense paged GQA decode: one step = one smd_paged_decode call
+    (decode and, for a split plan, the merge) over the pa_decode page's BF16
+    D512 MTP4 GQA16 B16 ctx8K case.  HBM-bound: every position's K and V rows
+    are read once."""
+    import torch
+    import sparse_mla_decode_index_amd as smd
+    import workloads as wl
+
+    dev = torch.device("cuda:0")
+    w = wl.paged_config()
+    T, Hq = w["B"] * w["mtp"], w["Hq"]
+
+    def bf(x):
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    q, k, v = bf(w["q"]), bf(w["k"]), bf(w["v"])
+    bt = torch.from_numpy(w["block_tables"]).to(dev)
+    cl = torch.from_numpy(w["context_lens"]).to(dev)
+    s = args.splits or smd.paged_num_splits(w["B"], w["Hkv"], w["max_ctx"], w["page"])
+    out = torch.empty((T, Hq, 512), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+    po = torch.empty((T, Hq, s, 512), dtype=torch.float32, device=dev) if s > 1 else None
+    pl = torch.empty((T, Hq, s), dtype=torch.float32, device=dev) if s > 1 else None
+    stream = torch.cuda.Stream()
+
+    def step():
+        smd.paged_decode(q, k, v, bt, cl, w["max_ctx"], w["softmax_scale"], mtp=w["mtp"], num_splits=s, out=out,
+                         lse=lse, partial_o=po, partial_lse=pl)
+
+    def merge_only():
+        smd.merge_partials(po, pl, None, out=out, lse=lse)
+
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        for _ in range(args.warmup):
+            step()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        for _ in range(args.steps):
+            step()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    with torch.cuda.stream(stream):
+        g.replay()
+    torch.cuda.synchronize()
+    ms_per_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    step_us = graph_time(torch, stream, step, args.kernel_launches)
+    merge_us = graph_time(torch, stream, merge_only, args.kernel_launches) if s > 1 else 0.0
+    kern_us = step_us - merge_us  # the decode launch of the step
+    cold_us = cold_time(torch, stream, step, args.cold_calls) if args.cold_calls > 0 else None
+    alg_bytes = wl.paged_algorithmic_bytes(w)
+    alg_flops = wl.paged_algorithmic_flops(w)
+    us = ms_per_step * 1e3
+    kernel_name = "smd::(anonymous namespace)::paged_decode_kernel"
+    roof = {"bound": "hbm", "achieved": round(alg_bytes / (step_us * 1e3), 1), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(alg_bytes / (step_us * 1e3) / HBM_PEAK_GBS, 4), "traffic": None,
+            "timing": "warm: whole call (decode + merge), average of back-to-back launches in a graph",
+            "kernel": kernel_name, "kernel_us": round(kern_us, 3), "merge_us": round(merge_us, 3),
+            "step_us": round(step_us, 3),
+            "alg_bytes_per_launch": alg_bytes, "alg_flops_per_launch": alg_flops,
+            "mfma_frac": round(alg_flops / (step_us * 1e6) / BF16_MFMA_PEAK_TFS, 4)}
+    traffic, traffic_src = measured_traffic(w["name"], kernel_name)
+    roof["traffic"] = traffic
+    if traffic_src:
+        roof["traffic_source"] = traffic_src
+    res = {
+        "metric": "dense paged GQA decode (pa_decode workload): µs/call + achieved HBM GB/s (% roofline)",
+        "value": round(alg_bytes / (us * 1e3), 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 6),
+        "us_per_call": round(us, 3),
+        "tokens_per_s": round(T / (us * 1e-6), 1),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w["name"], "num_seqs": w["B"], "mtp": w["mtp"], "num_q_heads": Hq,
+                   "num_kv_heads": w["Hkv"], "context": w["max_ctx"], "page_size": w["page"], "num_splits": s,
+                   "parallelism": "1 gpu"},
+        "roofline": roof,
+        "context_published": {"us_per_call": 91.5, "source": "pa_decode page, Performance table (MI355X, "
+                              "FlyDSL; KV head count not printed)"},
+    }
+    if cold_us is not None:
+        res["cold"] = {"us_per_call": round(cold_us, 3),
+                       "frac": round(alg_bytes / (cold_us * 1e3) / HBM_PEAK_GBS, 4), "calls": args.cold_calls,
+                       "note": "median of single calls, each after a 1 GiB device write; decode + merge"}
+    if not args.no_cpu_baseline:
+        per_call, sample, cores = paged_cpu_baseline(w, args.cpu_seconds)
+        res["cpu_baseline"] = {"value": round(alg_bytes / (per_call * 1e9), 4), "unit": "GB/s", "cores": cores,
+                               "kind": "oracle", "us_per_call": round(per_call * 1e6, 1), "sample": sample,
+                               "cpu": cpu_model()}
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
+        return
+    if args.paged:
+        if args.gpus != 1:
+            print(json.dumps({"error": "this build runs on exactly one GPU; --gpus must be 1",
+                              "n_gpus_requested": args.gpus}))
+            sys.exit(2)
+        paged_main(args)
         return
     if args.writer:
         if args.gpus != 1:

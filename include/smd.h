@@ -541,6 +541,56 @@ int smd_sparse_mla_decode_persistent_ex(const void *q_nope, const void *q_rope, 
 int smd_write_kv_fp8(const void *kv, int64_t kv_stride, int32_t num_rows, const int32_t *slots,
                      const smd_kv_pool *pool, void *stream);
 
+/*
+ * Dense paged GQA decode: the pa_decode workload of the aiter page "[FlyDSL]
+ * [Perf] pa_decode: K/V streaming, MTP query split and sparse split-major on
+ * gfx950" (Summary, Performance: paged grouped-query attention with separate
+ * K and V rows, MTP query positions and split plans).  The page prints no
+ * definition; this is the usual paged decode:
+ *
+ *  q        bf16 [num_seqs * mtp, num_q_heads, 512], contiguous, 16-byte
+ *           aligned; token t = b * mtp + i is MTP position i of sequence b.
+ *  k_cache, v_cache  bf16 [num_blocks, page_size, num_kv_heads, 512],
+ *           contiguous, 16-byte aligned.  Position p of sequence b is slot
+ *           p % page_size of block block_tables[b * block_tables_stride +
+ *           p / page_size].
+ *  Query head h reads KV head h / (num_q_heads / num_kv_heads).  Supported:
+ *  (num_q_heads / num_kv_heads) * mtp == 64 (e.g. GQA 16 x MTP 4, GQA 64 x
+ *  MTP 1), page_size a power of two >= 16; otherwise SMD_ERR_UNSUPPORTED.
+ *  context_lens int32 [num_seqs] (device), each clamped to [0,
+ *           max_context_len]; block_tables_stride >= ceil(max_context_len /
+ *           page_size).  The last mtp positions of a context are its MTP
+ *           tokens, causal among themselves: token i attends to positions
+ *           p < context_lens[b] - (mtp - 1 - i).
+ *  A block-table entry outside [0, num_blocks) reads nothing: its positions
+ *  are masked (not an error the call reports).
+ *  s_p = softmax_scale * <q, k_p>; out = sum_p softmax(s)_p v_p (bf16
+ *  [num_seqs * mtp, num_q_heads, 512]); lse = ln sum_p e^{s_p} (fp32, natural
+ *  log, no sink); a token with no position gets out = 0, lse = -inf.
+ *  num_splits in [1, SMD_MAX_SPLITS]: split r covers positions [r c, (r+1) c)
+ *  with c = smd_split_bounds' chunk of max_context_len (a split may span at
+ *  most 4095 pages, else SMD_ERR_INVALID_ARG).  partial_o fp32 [tokens,
+ *  num_q_heads, s, 512] and partial_lse [tokens, num_q_heads, s] are required
+ *  when s > 1 or out == NULL (then they are the result; with out the call
+ *  also runs smd_merge_partials without a sink).  num_seqs == 0 or
+ *  max_context_len == 0 launches nothing.  Returns SMD_OK or SMD_ERR_*.
+ */
+int smd_paged_decode(const void *q, int32_t num_seqs, int32_t mtp, int32_t num_q_heads, const void *k_cache,
+                     const void *v_cache, int64_t num_blocks, int32_t page_size, int32_t num_kv_heads,
+                     const int32_t *block_tables, int64_t block_tables_stride, const int32_t *context_lens,
+                     int32_t max_context_len, float softmax_scale, int32_t num_splits, float *partial_o,
+                     float *partial_lse, void *out, float *lse, void *stream);
+
+/*
+ * A split count for smd_paged_decode: enough splits for num_seqs *
+ * num_kv_heads * s workgroups to cover num_cus (<= 0: 256) once, capped by
+ * SMD_MAX_SPLITS and ceil(max_context_len / 64), raised until a split spans
+ * at most 4095 pages.  A heuristic of this library (the page's planner and
+ * budgets are not printed).  Host only, pure; SMD_ERR_* on bad sizes.
+ */
+int32_t smd_paged_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t page_size,
+                             int32_t num_cus);
+
 #ifdef __cplusplus
 }
 #endif

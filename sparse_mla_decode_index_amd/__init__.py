@@ -174,6 +174,11 @@ def lib() -> ctypes.CDLL:
     L.smd_sparse_mla_decode_persistent_ex.argtypes = [vp, vp, i32, i32, i32, ctypes.POINTER(_KVPool), vp, vp, vp,
                                                       f32, vp, ctypes.c_size_t, i32, vp, vp,
                                                       ctypes.POINTER(_DecodeOptions), vp]
+    L.smd_paged_decode.restype = ctypes.c_int
+    L.smd_paged_decode.argtypes = [vp, i32, i32, i32, vp, vp, i64, i32, i32, vp, i64, vp, i32, f32, i32, vp, vp, vp,
+                                   vp, vp]
+    L.smd_paged_num_splits.restype = ctypes.c_int32
+    L.smd_paged_num_splits.argtypes = [i32, i32, i32, i32, i32]
     L.smd_decode_kernel_choice.restype = ctypes.c_int32
     L.smd_decode_kernel_choice.argtypes = [i32, i32, i32, i32, i32, i32, i32, i32]
     _lib = L
@@ -593,11 +598,74 @@ def sparse_mla_decode_persistent(q_nope: torch.Tensor, q_rope: torch.Tensor, kv:
     _check("smd_sparse_mla_decode_persistent", rc)
     return out, lse
 
+def paged_num_splits(num_seqs: int, num_kv_heads: int, max_context_len: int, page_size: int,
+                     num_cus: int = 0) -> int:
+    """Split count for paged_decode (smd.h smd_paged_num_splits)."""
+    return _check("smd_paged_num_splits",
+                  lib().smd_paged_num_splits(num_seqs, num_kv_heads, max_context_len, page_size, num_cus))
+
+
+def paged_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor, block_tables: torch.Tensor,
+                 context_lens: torch.Tensor, max_context_len: int, softmax_scale: float, *, mtp: int = 1,
+                 num_splits: Optional[int] = None, out: Optional[torch.Tensor] = None,
+                 lse: Optional[torch.Tensor] = None, partial_o: Optional[torch.Tensor] = None,
+                 partial_lse: Optional[torch.Tensor] = None, partials_only: bool = False):
+    """Dense paged GQA decode (smd.h smd_paged_decode): q bf16 [B*mtp, Hq, 512],
+    caches bf16 [num_blocks, page, Hkv, 512], block_tables int32 [B, >= pages],
+    context_lens int32 [B].  Returns (out, lse), or with partials_only
+    (partial_o, partial_lse) of shapes [T, Hq, s, 512] and [T, Hq, s]."""
+    dev = q.device
+    _need(q, "q", torch.bfloat16, device=dev)
+    if q.dim() != 3 or q.shape[2] != DIM or not q.is_contiguous():
+        raise ValueError("q must be a contiguous [B * mtp, Hq, 512] tensor")
+    T, Hq, _ = q.shape
+    if T % mtp:
+        raise ValueError("the token count must be a multiple of mtp")
+    B = T // mtp
+    for name, c in (("k_cache", k_cache), ("v_cache", v_cache)):
+        _need(c, name, torch.bfloat16, device=dev)
+        if c.dim() != 4 or c.shape[3] != DIM or not c.is_contiguous() or c.shape != k_cache.shape:
+            raise ValueError(f"{name} must be a contiguous [num_blocks, page, Hkv, 512] tensor like k_cache")
+    nblk, page, Hkv, _ = k_cache.shape
+    _need(block_tables, "block_tables", torch.int32, device=dev)
+    _need(context_lens, "context_lens", torch.int32, (B,), dev)
+    if block_tables.dim() != 2 or block_tables.shape[0] != B or block_tables.stride(1) != 1:
+        raise ValueError("block_tables must be [B, pages] with unit column stride")
+    if num_splits is None:
+        num_splits = paged_num_splits(B, Hkv, max_context_len, page)
+    s = num_splits
+    need_partials = partials_only or s > 1
+    if need_partials:
+        if partial_o is None:
+            partial_o = torch.empty((T, Hq, s, DIM), dtype=torch.float32, device=dev)
+        if partial_lse is None:
+            partial_lse = torch.empty((T, Hq, s), dtype=torch.float32, device=dev)
+        _need(partial_o, "partial_o", torch.float32, (T, Hq, s, DIM), dev)
+        _need(partial_lse, "partial_lse", torch.float32, (T, Hq, s), dev)
+    if not partials_only:
+        if out is None:
+            out = torch.empty((T, Hq, DIM), dtype=torch.bfloat16, device=dev)
+        if lse is None:
+            lse = torch.empty((T, Hq), dtype=torch.float32, device=dev)
+        _need(out, "out", torch.bfloat16, (T, Hq, DIM), dev)
+        _need(lse, "lse", torch.float32, (T, Hq), dev)
+    rc = lib().smd_paged_decode(q.data_ptr(), B, mtp, Hq, k_cache.data_ptr(), v_cache.data_ptr(), nblk, page, Hkv,
+                                block_tables.data_ptr(), block_tables.stride(0), context_lens.data_ptr(),
+                                int(max_context_len), float(softmax_scale), s, _ptr(partial_o), _ptr(partial_lse),
+                                None if partials_only else out.data_ptr(), None if partials_only else lse.data_ptr(),
+                                _stream(q))
+    _check("smd_paged_decode", rc)
+    if partials_only:
+        return partial_o, partial_lse
+    return out, lse
+
+
 __all__ = ["KVPool", "PlanModel", "SmdError", "plan_num_kv_splits", "plan_decode", "plan_default_model",
            "split_bounds", "partials_bytes", "write_kv_fp8", "sparse_mla_decode", "sparse_mla_decode_noalloc",
            "sparse_mla_decode_two_source", "merge_partials", "persistent_default_partitions",
            "persistent_workspace_bytes", "PersistentWorkspace", "sparse_mla_decode_persistent", "lib",
-           "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0", "QK_BF16", "QK_FP8"]
+           "library_path", "KV_BF16", "KV_FP8_E4M3_UE8M0", "QK_BF16", "QK_FP8", "paged_decode",
+           "paged_num_splits"]
 
 if os.environ.get("SMD_EAGER_LOAD") == "1":
     lib()

@@ -19,7 +19,7 @@ LIB = PKG / "libsmd.so"
 BUILD_DIR = PKG.parent / "_build"
 
 SOURCES = ["api.cpp", "plan.cpp", "noalloc.hip", "decode_kernels.hip", "wide_kernel.hip", "persistent_kernel.hip",
-           "writer_kernel.hip"]
+           "writer_kernel.hip", "paged_kernel.hip"]
 ARCH = os.environ.get("SMD_OFFLOAD_ARCH", "gfx950")
 
 

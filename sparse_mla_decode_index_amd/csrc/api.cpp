@@ -647,3 +647,140 @@ extern "C" int smd_write_kv_fp8(const void *kv, int64_t kv_stride, int32_t num_r
   }
   return SMD_OK;
 }
+
+// ---------------------------------------------------------------------------
+// dense paged GQA decode
+// ---------------------------------------------------------------------------
+namespace smd {
+constexpr int32_t kPagedRows = 64;     // (Hq / Hkv) * mtp query rows per workgroup
+constexpr int32_t kPagedBtMax = 4096;  // block-table entries a split may span
+
+static int64_t paged_chunk(int32_t max_ctx, int32_t s) {
+  const int64_t per = ((int64_t)max_ctx + s - 1) / s;
+  return (per + kSplitAlign - 1) / kSplitAlign * kSplitAlign;
+}
+
+static bool paged_chunk_fits(int64_t chunk, int32_t page) { return (chunk + page - 1) / page + 1 <= kPagedBtMax; }
+}  // namespace smd
+
+extern "C" int32_t smd_paged_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len,
+                                        int32_t page_size, int32_t num_cus) {
+  g_err[0] = 0;
+  if (num_seqs < 0 || num_kv_heads < 1 || max_context_len < 0 || page_size < 16 || (page_size & (page_size - 1))) {
+    set_error("smd_paged_num_splits: bad sizes");
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (num_seqs == 0 || max_context_len == 0) return 1;
+  const int64_t cus = num_cus > 0 ? num_cus : 256;
+  const int64_t units = (int64_t)num_seqs * num_kv_heads;
+  const int64_t cap_len = (max_context_len + kSplitAlign - 1) / kSplitAlign;
+  int64_t s = (cus + units - 1) / units;  // fill the GPU once
+  if (s > cap_len) s = cap_len;
+  if (s > SMD_MAX_SPLITS) s = SMD_MAX_SPLITS;
+  if (s < 1) s = 1;
+  while (s < SMD_MAX_SPLITS && !paged_chunk_fits(paged_chunk(max_context_len, (int32_t)s), page_size)) ++s;
+  if (!paged_chunk_fits(paged_chunk(max_context_len, (int32_t)s), page_size)) {
+    set_error("smd_paged_num_splits: max_context_len %d needs more than %d splits at page size %d", max_context_len,
+              SMD_MAX_SPLITS, page_size);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  return (int32_t)s;
+}
+
+extern "C" int smd_paged_decode(const void *q, int32_t num_seqs, int32_t mtp, int32_t num_q_heads,
+                                const void *k_cache, const void *v_cache, int64_t num_blocks, int32_t page_size,
+                                int32_t num_kv_heads, const int32_t *block_tables, int64_t block_tables_stride,
+                                const int32_t *context_lens, int32_t max_context_len, float softmax_scale,
+                                int32_t num_splits, float *partial_o, float *partial_lse, void *out, float *lse,
+                                void *stream) {
+  static const char *fn = "smd_paged_decode";
+  g_err[0] = 0;
+  if (num_seqs < 0 || mtp < 1 || num_q_heads < 1 || num_kv_heads < 1 || num_blocks < 0 || max_context_len < 0 ||
+      block_tables_stride < 0) {
+    set_error("%s: negative or zero size", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (num_q_heads % num_kv_heads != 0 || (num_q_heads / num_kv_heads) * mtp != kPagedRows) {
+    set_error("%s: (num_q_heads / num_kv_heads) * mtp must be %d (got %d / %d, mtp %d)", fn, kPagedRows, num_q_heads,
+              num_kv_heads, mtp);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (page_size < 16 || page_size > (1 << 20) || (page_size & (page_size - 1))) {
+    set_error("%s: page_size=%d must be a power of two >= 16", fn, page_size);
+    return SMD_ERR_UNSUPPORTED;
+  }
+  if (num_splits < 1 || num_splits > SMD_MAX_SPLITS) {
+    set_error("%s: num_splits=%d not in [1,%d]", fn, num_splits, SMD_MAX_SPLITS);
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!isfinite(softmax_scale)) {
+    set_error("%s: softmax_scale is not finite", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  const int64_t chunk = paged_chunk(max_context_len, num_splits);
+  if (!paged_chunk_fits(chunk, page_size)) {
+    set_error("%s: a split of %lld positions spans more than %d pages of %d; use more splits "
+              "(smd_paged_num_splits)", fn, (long long)chunk, kPagedBtMax - 1, page_size);
+    return SMD_ERR_INVALID_ARG;
+  }
+  const int64_t pages = ((int64_t)max_context_len + page_size - 1) / page_size;
+  if (num_seqs > 0 && max_context_len > 0 && block_tables_stride < pages) {
+    set_error("%s: block_tables_stride=%lld below the %lld pages of max_context_len", fn,
+              (long long)block_tables_stride, (long long)pages);
+    return SMD_ERR_INVALID_ARG;
+  }
+  const bool need_partials = num_splits > 1 || out == nullptr;
+  if (num_seqs == 0 || max_context_len == 0) return SMD_OK;
+  if (!q || !k_cache || !v_cache || !block_tables || !context_lens || (need_partials && (!partial_o || !partial_lse))) {
+    set_error("%s: q, the caches, block_tables, context_lens%s are required", fn,
+              need_partials ? " and the partials" : "");
+    return SMD_ERR_INVALID_ARG;
+  }
+  if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || (out && !aligned16(out)) ||
+      (partial_o && !aligned16(partial_o)) || ((uintptr_t)block_tables & 3) || ((uintptr_t)context_lens & 3) ||
+      (lse && ((uintptr_t)lse & 3)) || (partial_lse && ((uintptr_t)partial_lse & 3))) {
+    set_error("%s: q, caches, out and partial_o must be 16-byte aligned; tables, lengths and lse 4-byte", fn);
+    return SMD_ERR_INVALID_ARG;
+  }
+  PagedArgs a = {};
+  a.q = (const uint16_t *)q;
+  a.k_cache = (const uint8_t *)k_cache;
+  a.v_cache = (const uint8_t *)v_cache;
+  a.block_tables = block_tables;
+  a.bt_stride = block_tables_stride;
+  a.context_lens = context_lens;
+  a.num_blocks = num_blocks;
+  a.num_seqs = num_seqs;
+  a.mtp = mtp;
+  a.Hq = num_q_heads;
+  a.Hkv = num_kv_heads;
+  a.R = num_q_heads / num_kv_heads;
+  a.page = page_size;
+  int sh = 0;
+  while ((1 << sh) < page_size) ++sh;
+  a.page_shift = sh;
+  a.max_ctx = max_context_len;
+  a.scale_log2 = softmax_scale * 1.4426950408889634f;
+  a.S = num_splits;
+  a.chunk = (int32_t)chunk;
+  a.part_o = need_partials ? partial_o : nullptr;
+  a.part_lse = need_partials ? partial_lse : nullptr;
+  a.out = need_partials ? nullptr : (uint16_t *)out;
+  a.lse = need_partials ? nullptr : lse;
+  a.hilo = out == nullptr;
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = launch_paged_decode(a, st);
+  if (e != hipSuccess) {
+    set_error("%s: launch failed: %s", fn, hipGetErrorString(e));
+    return SMD_ERR_HIP;
+  }
+  if (need_partials && out) {
+    e = launch_merge(partial_o, partial_lse, num_seqs * mtp * num_q_heads, num_q_heads, num_splits, nullptr,
+                     (uint16_t *)out, lse, st);
+    if (e != hipSuccess) {
+      set_error("%s: merge launch failed: %s", fn, hipGetErrorString(e));
+      return SMD_ERR_HIP;
+    }
+  }
+  return SMD_OK;
+}

@@ -69,6 +69,29 @@ hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows
                         int32_t S, const float *sink, uint16_t *out, float *lse,
                         hipStream_t stream);
 
+// Arguments of the dense paged GQA decode (smd_paged_decode).  Pointers are
+// device pointers; caches are bf16 [num_blocks, page, Hkv, 512].
+struct PagedArgs {
+  const uint16_t *q;             // bf16 [num_seqs * mtp, Hq, 512]
+  const uint8_t *k_cache;
+  const uint8_t *v_cache;
+  const int32_t *block_tables;   // [num_seqs, bt_stride]
+  int64_t bt_stride;             // elements
+  const int32_t *context_lens;   // [num_seqs]
+  int64_t num_blocks;
+  int32_t num_seqs, mtp, Hq, Hkv, R;  // R = Hq / Hkv; R * mtp == 64
+  int32_t page, page_shift;      // page a power of two >= 16
+  int32_t max_ctx;               // context lengths are clamped to it
+  float scale_log2;
+  int32_t S, chunk;              // split count and length (split r: [r chunk, (r+1) chunk))
+  float *part_o, *part_lse;      // fp32 [T, Hq, S, 512], [T, Hq, S] when S > 1 or out is null
+  uint16_t *out;                 // bf16 [T, Hq, 512] when S == 1
+  float *lse;
+  int32_t hilo;                  // partials are the result: carry p as bf16 hi + lo
+};
+
+hipError_t launch_paged_decode(const PagedArgs &a, hipStream_t stream);
+
 // Arguments of the persistent kernel.  The decode fields carry the queries,
 // pool, sink, scale, H, qps, M, G, out and lse (indices, chunk, S and the
 // partial pointers are unused).

@@ -557,3 +557,49 @@ def test_decode_kernel_choice_follows_the_cost_model():
 ])
 def test_decode_kernel_choice_rejects(args, code):
     assert smd.lib().smd_decode_kernel_choice(*args) == code
+
+
+def _paged(**kw):
+    a = dict(q=0x20000, B=2, mtp=4, Hq=16, k=0x30000, v=0x40000, nblk=100, page=16, Hkv=1, bt=0x50000, bts=64,
+             cl=0x60000, max_ctx=1000, scale=0.04, s=1, po=None, pl=None, out=0x70000, lse=0x80000)
+    a.update(kw)
+    rc = smd.lib().smd_paged_decode(a["q"], a["B"], a["mtp"], a["Hq"], a["k"], a["v"], a["nblk"], a["page"], a["Hkv"],
+                                    a["bt"], a["bts"], a["cl"], a["max_ctx"], a["scale"], a["s"], a["po"], a["pl"],
+                                    a["out"], a["lse"], None)
+    return rc, smd.lib().smd_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(Hq=8), -2, "64"),                       # GQA 8 x MTP 4 = 32 rows
+    (dict(Hq=16, Hkv=3), -2, "64"),               # heads not a multiple of the KV heads
+    (dict(page=24), -2, "page_size"),             # not a power of two
+    (dict(page=8), -2, "page_size"),              # below 16
+    (dict(s=0), -1, "num_splits"),
+    (dict(s=33), -1, "num_splits"),
+    (dict(bts=10), -1, "block_tables_stride"),    # 1000 positions need 63 pages
+    (dict(max_ctx=1 << 20, bts=1 << 16), -1, "splits"),  # one split spanning 65536 pages
+    (dict(scale=float("nan")), -1, "softmax_scale"),
+    (dict(s=2), -1, "partials"),                  # a split plan without partials
+    (dict(q=0x20008), -1, "aligned"),
+    (dict(mtp=0), -1, "size"),
+])
+def test_paged_decode_rejects(kw, code, msg):
+    rc, err = _paged(**kw)
+    assert rc == code and msg in err, (rc, err)
+
+
+def test_paged_decode_empty_launches_nothing():
+    assert _paged(B=0)[0] == 0
+    assert _paged(max_ctx=0)[0] == 0
+
+
+def test_paged_num_splits():
+    """Enough splits to cover 256 CUs once, capped at 32 and ceil(ctx / 64),
+    raised until a split spans at most 4095 pages."""
+    assert smd.paged_num_splits(16, 1, 8192, 16) == 16
+    assert smd.paged_num_splits(64, 8, 32768, 16) == 1
+    assert smd.paged_num_splits(1, 1, 100, 16) == 2        # ceil(100 / 64)
+    assert smd.paged_num_splits(300, 1, 1 << 20, 16) == 17  # 1M / 16 pages needs >= 17 splits of <= 65520
+    assert smd.paged_num_splits(2, 1, 0, 16) == 1
+    with pytest.raises(smd.SmdError):
+        smd.paged_num_splits(1, 1, 1 << 30, 16)

@@ -399,3 +399,52 @@ def writer_workload(rows: int, pool_rows: int, seed: int = 7) -> dict:
 def writer_algorithmic_bytes(rows: int) -> int:
     """Each latent row read once, its fp8 row (bytes, codes, RoPE) written once, one slot read."""
     return rows * (WRITER_ROW_READ + WRITER_ROW_WRITE + WRITER_SLOT)
+
+
+# ----------------------------------------------------------------------------
+# dense paged GQA decode (pa_decode)
+# ----------------------------------------------------------------------------
+def paged_workload(name: str, *, B: int, mtp: int, Hq: int, Hkv: int, max_ctx: int, page: int, seed: int,
+                   lens=None, spare_blocks: int = 3, softmax_scale: float | None = None) -> dict:
+    """q ~ N(0,1) bf16 [B*mtp, Hq, 512]; K and V caches ~ N(0,1) bf16
+    [num_blocks, page, Hkv, 512] with every sequence's pages at distinct
+    random blocks (a random permutation, spare_blocks never referenced);
+    context lengths `lens` (default: every sequence at max_ctx)."""
+    rng = np.random.default_rng(seed)
+    pages = -(-max_ctx // page)
+    nblk = B * pages + spare_blocks
+    q = _normal_bf16(rng, (B * mtp, Hq, DIM))
+    k = _normal_bf16(rng, (nblk, page, Hkv, DIM))
+    v = _normal_bf16(rng, (nblk, page, Hkv, DIM))
+    bt = rng.permutation(nblk)[:B * pages].reshape(B, pages).astype(np.int32)
+    cl = np.full(B, max_ctx, dtype=np.int32) if lens is None else np.asarray(lens, dtype=np.int32)
+    return {"name": name, "q": q, "k": k, "v": v, "block_tables": bt, "context_lens": cl, "B": B, "mtp": mtp,
+            "Hq": Hq, "Hkv": Hkv, "max_ctx": max_ctx, "page": page, "num_blocks": nblk,
+            "softmax_scale": float(np.float32(1.0 / np.sqrt(DIM))) if softmax_scale is None else softmax_scale}
+
+
+def paged_config() -> dict:
+    """The pa_decode page's BF16 D512 MTP4 GQA16 case at batch 16 and an 8K
+    context, with one KV head (the page does not print the KV head count) and
+    16-row pages; every sequence at the full 8192 positions."""
+    return paged_workload("paged bf16 D512 MTP4 GQA16 B16 ctx8K", B=16, mtp=4, Hq=16, Hkv=1, max_ctx=8192, page=16,
+                          seed=41)
+
+
+def paged_algorithmic_bytes(w: dict) -> int:
+    """Each position's K and V row of every KV head read once (MTP-causal
+    positions included once), q read, out (bf16) and lse (fp32) written, the
+    block-table entries and lengths read."""
+    cl = np.minimum(np.maximum(w["context_lens"], 0), w["max_ctx"]).astype(np.int64)
+    rows = int(cl.sum()) * w["Hkv"]
+    T, Hq = w["B"] * w["mtp"], w["Hq"]
+    pages = int(np.sum(-(-cl // w["page"])))
+    return rows * 2 * DIM * 2 + T * Hq * DIM * 2 * 2 + T * Hq * 4 + pages * 4 + w["B"] * 4
+
+
+def paged_algorithmic_flops(w: dict) -> int:
+    """2*512 (QK) + 2*512 (PV) flops per (query row, visible position)."""
+    cl = np.minimum(np.maximum(w["context_lens"], 0), w["max_ctx"]).astype(np.int64)
+    mtp = w["mtp"]
+    vis = sum(max(int(L) - (mtp - 1 - i), 0) for L in cl for i in range(mtp))
+    return 2048 * w["Hq"] * vis
