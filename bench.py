@@ -277,17 +277,26 @@ def graph_time(torch, stream, fn, n):
     return e0.elapsed_time(e1) * 1e3 / n
 
 
-def cold_time(torch, stream, fn, n, flush_bytes=1 << 30):
+def cold_time(torch, stream, fn, n, flush_bytes=1 << 30, flush="write"):
     """Median GPU time of one call of `fn` (all its launches) right after a
-    1 GiB device write, which evicts the pool and the queries from the L2
-    caches and the 256 MB Infinity Cache.  HIP events on the stream fn runs on
-    bracket the call only; the write runs before the first event."""
+    1 GiB device write (flush="write"), which evicts the pool and the queries
+    from the L2 caches and the 256 MB Infinity Cache, or after a 1 GiB read
+    (flush="read"), which evicts them as well but leaves the caches holding
+    clean lines: after the write, a call that reads more than the Infinity
+    Cache holds also pays for writing the flush buffer's dirty lines back to
+    HBM.  HIP events on the stream fn runs on bracket the call only; the flush
+    runs before the first event."""
     buf = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+    words = buf.view(torch.int32)
+    total = torch.empty((), dtype=torch.int64, device="cuda")
     marks = []
     torch.cuda.synchronize()
     with torch.cuda.stream(stream):
         for i in range(n):
-            buf.fill_(i & 0xFF)
+            if flush == "read":
+                torch.sum(words, dim=0, dtype=torch.int64, out=total)
+            else:
+                buf.fill_(i & 0xFF)
             a = torch.cuda.Event(enable_timing=True)
             b = torch.cuda.Event(enable_timing=True)
             a.record(stream)
@@ -551,6 +560,7 @@ def paged_main(args):
     merge_us = graph_time(torch, stream, merge_only, args.kernel_launches) if s > 1 else 0.0
     kern_us = step_us - merge_us  # the decode launch of the step
     cold_us = cold_time(torch, stream, step, args.cold_calls) if args.cold_calls > 0 else None
+    cold_r_us = cold_time(torch, stream, step, args.cold_calls, flush="read") if args.cold_calls > 0 else None
     alg_bytes = wl.paged_algorithmic_bytes(w)
     alg_flops = wl.paged_algorithmic_flops(w)
     us = ms_per_step * 1e3
@@ -592,6 +602,11 @@ def paged_main(args):
         res["cold"] = {"us_per_call": round(cold_us, 3),
                        "frac": round(alg_bytes / (cold_us * 1e3) / HBM_PEAK_GBS, 4), "calls": args.cold_calls,
                        "note": "median of single calls, each after a 1 GiB device write; decode + merge"}
+        res["cold_read_flush"] = {"us_per_call": round(cold_r_us, 3),
+                                  "frac": round(alg_bytes / (cold_r_us * 1e3) / HBM_PEAK_GBS, 4),
+                                  "calls": args.cold_calls,
+                                  "note": "median of single calls, each after a 1 GiB device read (caches hold "
+                                          "clean lines: no write-back of a flush buffer); decode + merge"}
     if not args.no_cpu_baseline:
         per_call, sample, cores = paged_cpu_baseline(w, args.cpu_seconds)
         res["cpu_baseline"] = {"value": round(alg_bytes / (per_call * 1e9), 4), "unit": "GB/s", "cores": cores,
@@ -738,6 +753,7 @@ def main():
         kern_us -= merge_us
 
     cold_us = cold_time(torch, stream, step, args.cold_calls) if args.cold_calls > 0 else None
+    cold_r_us = cold_time(torch, stream, step, args.cold_calls, flush="read") if args.cold_calls > 0 else None
 
     if args.copy_calibration:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -814,6 +830,9 @@ def main():
     }
     if cold is not None:
         res["cold"] = cold
+        res["cold_read_flush"] = {"us_per_call": round(cold_r_us, 3), "calls": args.cold_calls,
+                                  "note": "median of single calls, each after a 1 GiB device read (caches hold "
+                                          "clean lines: no write-back of a flush buffer)"}
     if not args.no_cpu_baseline:
         per_call, sample, cores = cpu_baseline(w, args.cpu_seconds)
         res["cpu_baseline"] = {"value": round(alg_bytes / (per_call * 1e9), 4), "unit": "GB/s", "cores": cores,
