@@ -18,6 +18,8 @@ The reading used here is the usual paged decode:
   (mtp - 1 - i);
 * s_p = scale * <q, k_p>, out = sum_p softmax(s)_p v_p, lse = ln sum_p e^{s_p}
   (natural log, no sink); a token with no position gets out = 0, lse = -inf;
+* a block-table entry outside [0, num_blocks) names no block: the positions
+  of that page are masked (a reading; the page does not say);
 * split partials as in ``oracle.ref``: split r covers positions [a_r, e_r)
   of ``ref.split_bounds(max_context_len, s)`` (one plan per call, cut at each
   token's own limit); lse_r = ln sum_{p in r} e^{s_p}, o_r = sum_{p in r}
@@ -33,16 +35,22 @@ import numpy as np
 from oracle import ref
 
 
-def _positions(block_tables, b: int, n: int, page_size: int):
-    """Physical (block, slot) of positions 0 .. n-1 of sequence b."""
+def _positions(block_tables, b: int, n: int, page_size: int, num_blocks: int):
+    """Physical (block, slot) of positions 0 .. n-1 of sequence b, and whether
+    the block-table entry names a block (block 0 stands in where it does not)."""
     p = np.arange(n)
-    return np.asarray(block_tables)[b, p // page_size], p % page_size
+    blk = np.asarray(block_tables)[b, p // page_size].astype(np.int64)
+    ok = (blk >= 0) & (blk < num_blocks)
+    return np.where(ok, blk, 0), p % page_size, ok
 
 
-def gather_kv(cache: np.ndarray, block_tables, b: int, g: int, n: int, page_size: int) -> np.ndarray:
-    """float64 [n, D] rows of KV head g at positions 0 .. n-1 of sequence b."""
-    blk, slot = _positions(block_tables, b, n, page_size)
-    return ref.bf16_to_f64(np.asarray(cache)[blk, slot, g])
+def gather_kv(cache: np.ndarray, block_tables, b: int, g: int, n: int, page_size: int):
+    """float64 [n, D] rows of KV head g at positions 0 .. n-1 of sequence b,
+    and bool [n]: the position's page names a block (rows of the others are
+    placeholders, never attended)."""
+    cache = np.asarray(cache)
+    blk, slot, ok = _positions(block_tables, b, n, page_size, cache.shape[0])
+    return ref.bf16_to_f64(cache[blk, slot, g]), ok
 
 
 def _attend_kv(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
@@ -68,14 +76,15 @@ def paged_decode(q, k_cache, v_cache, block_tables, context_lens, page_size: int
     for b in range(T // mtp):
         L = int(context_lens[b])
         for g in range(Hkv):
-            kk = gather_kv(k_cache, block_tables, b, g, L, page_size)
-            vv = gather_kv(v_cache, block_tables, b, g, L, page_size)
+            kk, ok = gather_kv(k_cache, block_tables, b, g, L, page_size)
+            vv, _ = gather_kv(v_cache, block_tables, b, g, L, page_size)
             for i in range(mtp):
                 n = max(L - (mtp - 1 - i), 0)
                 t = b * mtp + i
+                sel = ok[:n]
                 for j in range(R):
                     h = g * R + j
-                    out[t, h], lse[t, h] = _attend_kv(qf[t, h], kk[:n], vv[:n], softmax_scale)
+                    out[t, h], lse[t, h] = _attend_kv(qf[t, h], kk[:n][sel], vv[:n][sel], softmax_scale)
     return out, lse
 
 
@@ -95,14 +104,16 @@ def paged_decode_partials(q, k_cache, v_cache, block_tables, context_lens, page_
     for b in range(T // mtp):
         L = int(context_lens[b])
         for g in range(Hkv):
-            kk = gather_kv(k_cache, block_tables, b, g, L, page_size)
-            vv = gather_kv(v_cache, block_tables, b, g, L, page_size)
+            kk, ok = gather_kv(k_cache, block_tables, b, g, L, page_size)
+            vv, _ = gather_kv(v_cache, block_tables, b, g, L, page_size)
             for i in range(mtp):
                 n = max(L - (mtp - 1 - i), 0)
                 t = b * mtp + i
                 for r, (a, e) in enumerate(bounds):
                     a2, e2 = min(a, n), min(e, n)
+                    sel = ok[a2:e2]
                     for j in range(R):
                         h = g * R + j
-                        o[t, h, r], lse[t, h, r] = _attend_kv(qf[t, h], kk[a2:e2], vv[a2:e2], softmax_scale)
+                        o[t, h, r], lse[t, h, r] = _attend_kv(qf[t, h], kk[a2:e2][sel], vv[a2:e2][sel],
+                                                              softmax_scale)
     return o, lse

@@ -2,7 +2,8 @@
 the gathered rows with the MTP-causal mask, the sparse decode oracle on a
 one-head cache with K = V, invariance under a permutation of the physical
 blocks, the MTP positions against shorter contexts, the split-merge
-identity, and empty contexts."""
+identity, empty contexts, and block-table entries that name no block against
+the same sequence with that page taken out."""
 import numpy as np
 import torch
 
@@ -102,3 +103,28 @@ def test_empty_context():
     out, lse = paged_ref.paged_decode(q, k, v, bt, cl, 8, 3, 0.1)
     assert np.all(out[:2] == 0) and np.all(np.isneginf(lse[:2]))
     assert np.all(np.isfinite(lse[2]))
+
+
+def test_invalid_block_entries_equal_the_page_taken_out():
+    """A page whose block-table entry is outside [0, num_blocks) is masked: a
+    sequence with such a page below every token's limit decodes as the same
+    sequence with that page removed (the table shifted left, the context one
+    page shorter), bit for bit; the split partials still merge to it."""
+    page, mtp = 8, 2
+    q, k, v, bt, cl = _case(7, B=3, mtp=mtp, page=page, max_ctx=40, lens=[40, 33, 25])
+    nblk = k.shape[0]
+    bad = bt.copy()
+    bad[0, 1] = -1            # page 1 of sequence 0
+    bad[1, 0] = nblk + 3      # page 0 of sequence 1
+    bad[2, 2] = np.iinfo(np.int32).min
+    out, lse = paged_ref.paged_decode(q, k, v, bad, cl, page, mtp, 0.1)
+    for b, j in ((0, 1), (1, 0), (2, 2)):
+        short = np.concatenate([bt[b, :j], bt[b, j + 1:], bt[b, :1]])[None].astype(np.int32)
+        sl = slice(b * mtp, (b + 1) * mtp)
+        o2, l2 = paged_ref.paged_decode(q[sl], k, v, short, cl[b:b + 1] - page, page, mtp, 0.1)
+        np.testing.assert_array_equal(out[sl], o2)
+        np.testing.assert_array_equal(lse[sl], l2)
+    po, pl = paged_ref.paged_decode_partials(q, k, v, bad, cl, page, mtp, 0.1, 3, 40)
+    mo, ml = ref.merge_partials(po, pl, None)
+    np.testing.assert_allclose(mo, out, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(ml, lse, rtol=0, atol=1e-12)
