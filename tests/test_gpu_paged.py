@@ -2,7 +2,8 @@
 float64 oracle (oracle.paged_ref), through the C ABI: ragged context lengths
 (tails of every size, contexts shorter than the MTP span), GQA x MTP shapes
 of 64 query rows per KV head, several KV heads, page sizes 16 to 128, one
-split and several, FP32 partials, repeated launches bit-identical, the
+split and several, FP32 partials, block-table entries that name no block,
+repeated launches bit-identical, the
 pa_decode page's BF16 D512 MTP4 GQA16 B16 ctx8K case at full size (sampled
 tokens), and the calls the entry point rejects.  Bars: bf16 out
 atol = rtol = 2e-2, FP32 partials and LSE 1e-3 (as for the sparse decode)."""
@@ -71,6 +72,24 @@ def test_partials_with_empty_splits(gpu):
     sequence's later splits are empty (o = 0, lse = -inf)."""
     w = wl.paged_workload("paged partials", B=2, mtp=4, Hq=16, Hkv=1, max_ctx=700, page=16, seed=931, lens=[700, 90])
     _run(w, gpu, 6, partials=True)
+
+
+@pytest.mark.parametrize("s", [1, 4])
+def test_invalid_block_entries_are_masked(gpu, s):
+    """Block-table entries -1, num_blocks, num_blocks + 7 and INT32_MIN name no
+    block: their pages are masked, including a page that holds the MTP
+    tokens' limits and the last page of a ragged context."""
+    w = wl.paged_workload("paged bad blocks", B=3, mtp=4, Hq=16, Hkv=1, max_ctx=400, page=16, seed=940 + s,
+                          lens=[400, 250, 37])
+    bt = w["block_tables"].copy()
+    nblk = w["num_blocks"]
+    bt[0, 3] = -1
+    bt[0, 24] = nblk          # positions 384..399: the page of every MTP limit
+    bt[1, 0] = nblk + 7
+    bt[1, 15] = np.iinfo(np.int32).min  # positions 240..255, the ragged tail's page
+    bt[2, 1] = -1
+    w["block_tables"] = bt
+    _run(w, gpu, s)
 
 
 def test_repeat_launches_bit_exact(gpu):
