@@ -670,6 +670,95 @@ __device__ __forceinline__ void run_split_wide_dma(const DecodeArgs &a, SmemWide
   wait_vm<0>();  // no load may land in LDS after the walk
 }
 
+// bf16 pools on a direct-to-LDS ring (the split-KV wide kernel): the slots
+// are bf16 tiles in the compute layout -- lane x of a row's load fetches
+// logical chunk x ^ swz32(r) and lands at chunk x -- so a tile is computed
+// straight from its slot, with no staging registers and no LDS stores.
+// Three slots: the tile computed and the two whose loads are in flight.
+#ifndef SMD_WIDE_BF16_RING
+#define SMD_WIDE_BF16_RING 1
+#endif
+constexpr bool kWideBf16Ring = SMD_WIDE_BF16_RING != 0;
+constexpr int kRingBSlots = 3;
+struct SmemWideB {
+  uint8_t qs[4][32 - kQRegDma][64 * 16];  // Q^T k-steps kQRegDma .. 31 per wave
+};
+
+// Direct-to-LDS loads of this wave's 8 rows of a bf16 tile (rows 8w .. 8w+7,
+// indices at tidx), one 1 KiB row per load.  Invalid rows and positions past
+// p1 read the zero row.
+template <bool PACKED>
+__device__ __forceinline__ void dma_rows_bf16(const DecodeArgs &a, const int32_t SMD_LDS *tidx, int first_pos, int p1,
+                                              int wave, int lane, uint8_t SMD_LDS *tile) {
+  uint32_t widx[8];
+  lds_read_idx8(tidx + wave * (kBK / 4), widx);
+  const int rows_left = p1 - first_pos - wave * (kBK / 4);
+  const uint8_t *z = g_zero_row;
+#pragma unroll
+  for (int i = 0; i < kBK / 4; ++i) {
+    const int r = wave * (kBK / 4) + i;
+    const int c = lane ^ swz32(r);
+    const uint32_t idx = widx[i];
+    const bool v = i < rows_left && idx < a.num_rows32;
+    const uint8_t *src;
+    if constexpr (PACKED)
+      src = v ? a.kv_nope + (uint64_t)idx * a.row_stride32 + 16 * c : z + 16 * c;
+    else if (!v)
+      src = z + 16 * c;
+    else
+      src = c < kNope / 8 ? a.kv_nope + (uint64_t)idx * (uint64_t)a.nope_stride_b + 16 * c
+                          : a.kv_rope + (uint64_t)idx * (uint64_t)a.rope_stride_b + 16 * (c - kNope / 8);
+    lds_dma<16>(src, tile + r * kLdsRow);
+  }
+}
+
+// Walk the range's tiles once (bf16 pools) on the bf16 ring.  Step t: wait
+// for this wave's loads of tile t (the 8 of tile t+1 may still fly), read its
+// valid bits, barrier (everyone's rows of t have landed and tile t-1 is done:
+// its slot is free), issue tile t+2 into that slot (and, at t % 8 == 0,
+// index block t/8 + 1), compute t from its slot.  Index block k is read from
+// step 8k - 2 on; issued at step 8(k-1), it has landed by the wait of step
+// 8k - 3 and that step's barrier publishes it.  The block it replaces was
+// last read at step 8k - 9.
+template <bool PACKED, bool P_HILO, int PASS>
+__device__ __forceinline__ void run_split_wide_ringb(const DecodeArgs &a, SmemWideB &sm, const WideDma &dm,
+                                                     const int32_t *row_idx, int p0, int p1, int wave, int lane,
+                                                     const bf16x8 (&qreg)[kQRegDma], const WideLanes &L,
+                                                     WideState &w) {
+  const int ntiles = (p1 - p0 + kBK - 1) / kBK;
+  if (ntiles <= 0) return;
+  uint8_t SMD_LDS *raw = dm.raw;
+  int32_t SMD_LDS *ib0 = dm.ibuf;
+  const uint8_t SMD_LDS *qs = (const uint8_t SMD_LDS *)&sm.qs[wave][0][0];
+  auto tidx = [&](int k) {
+    return ib0 + ((k / kTilesPerIdxBlock) & 1) * kIdxBlock + (k % kTilesPerIdxBlock) * kBK;
+  };
+  auto slot = [&](int k) { return raw + (k % kRingBSlots) * kTileBytes; };
+  constexpr int kAhead = kRingBSlots - 1;
+  // A real vmcnt(0), as in run_split_wide_dma.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  if constexpr (PASS != kPassMain) {  // the main pass's caller has done this, with the Q^T load
+    __syncthreads();  // the ring may still be read by a previous pass
+    dma_idx_block(row_idx, p0, p1, 0, wave, lane, ib0);
+    wait_vm<0>();
+  }
+  __syncthreads();
+#pragma unroll
+  for (int k = 0; k < kAhead; ++k) dma_rows_bf16<PACKED>(a, tidx(k), p0 + k * kBK, p1, wave, lane, slot(k));
+  for (int t = 0; t < ntiles; ++t) {
+    wait_vm<(kBK / 4) * (kAhead - 1)>();
+    const uint32_t v_cur = tile_valid_bits_dma(tidx(t), p0 + t * kBK, p1, lane, a.num_rows32);
+    barrier_lds();
+    dma_rows_bf16<PACKED>(a, tidx(t + kAhead), p0 + (t + kAhead) * kBK, p1, wave, lane, slot(t + kAhead));
+    if (t % kTilesPerIdxBlock == 0) {
+      const int nb = t / kTilesPerIdxBlock + 1;
+      dma_idx_block(row_idx, p0, p1, nb, wave, lane, ib0 + (nb & 1) * kIdxBlock);
+    }
+    compute_tile_wide<kQRegDma, PASS, P_HILO>(slot(t), qreg, qs, L, v_cur, lane, a.scale_log2, w);
+  }
+  wait_vm<0>();  // no load may land in LDS after the walk
+}
+
 // ---------------------------------------------------------------------------
 // fp8 QK ("a8w8", the persistent decode object of the aiter page "[ASM][HIP]
 // [MLA v4 nm] Split plan helper and persistent decode kernel", Summary part
@@ -1031,6 +1120,36 @@ __device__ __forceinline__ void attend_range_wide(const DecodeArgs &a, SmemWide<
   // every wave's loads have landed (each waited for its own) and its tile
   // reads are done before the epilogue stages through the ring or the tiles
   __syncthreads();
+}
+
+// attend_range_wide for bf16 pools on the bf16 ring (run_split_wide_ringb).
+template <bool PACKED, bool P_HILO>
+__device__ __forceinline__ void attend_range_wide_b(const DecodeArgs &a, SmemWideB &sm, const WideDma &dm,
+                                                    const int32_t *row_idx, int p0, int p1, int wave, int lane,
+                                                    int64_t qbase, bf16x8 (&qreg)[kQRegDma], const WideLanes &L,
+                                                    WideState &w) {
+  auto reset = [&]() {
+#pragma unroll
+    for (int d = 0; d < 16; ++d) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) w.acc[d][e] = 0.f;
+    }
+    w.m_ref = -INFINITY;
+    w.l_run = 0.f;
+  };
+  __syncthreads();  // the ring and the index blocks may still be in use by a previous range
+  if (p1 > p0) dma_idx_block(row_idx, p0, p1, 0, wave, lane, dm.ibuf);
+  static_assert(kRingBSlots * kTileBytes >= 4 * kStageWave, "staging slices fit the ring");
+  load_q_wide<kQRegDma>(a, qbase, lane, dm.raw + wave * kStageWave, (uint8_t SMD_LDS *)&sm.qs[wave][0][0], qreg);
+  reset();
+  w.overflow = false;
+  run_split_wide_ringb<PACKED, P_HILO, kPassMain>(a, sm, dm, row_idx, p0, p1, wave, lane, qreg, L, w);
+  if (__syncthreads_or(w.overflow)) {
+    reset();
+    run_split_wide_ringb<PACKED, P_HILO, kPassMax>(a, sm, dm, row_idx, p0, p1, wave, lane, qreg, L, w);
+    run_split_wide_ringb<PACKED, P_HILO, kPassFixed>(a, sm, dm, row_idx, p0, p1, wave, lane, qreg, L, w);
+  }
+  __syncthreads();  // as in attend_range_wide
 }
 
 // Outputs of a wide wave's 32 query rows, stored row-wise through the wave's

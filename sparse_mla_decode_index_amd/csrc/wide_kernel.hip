@@ -18,7 +18,9 @@ template <bool FP8, bool PACKED, bool P_HILO, bool QF8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void decode_wide_kernel(DecodeArgs a) {
   static_assert(!QF8 || FP8, "the fp8 QK reads an fp8 pool");
   constexpr bool RING = wide_ring<FP8>();
-  __shared__ __attribute__((aligned(1024))) std::conditional_t<QF8, SmemWideQ<7>, SmemWide<RING>> sm;
+  constexpr bool RINGB = !FP8 && kWideBf16Ring;  // bf16 pools on the bf16 ring
+  __shared__ __attribute__((aligned(1024)))
+  std::conditional_t<QF8, SmemWideQ<7>, std::conditional_t<RINGB, SmemWideB, SmemWide<RING>>> sm;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 
@@ -46,6 +48,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     __shared__ __attribute__((aligned(1024))) uint8_t s_raw[raw_slots<QF8>() * raw_slot<QF8>()];
     __shared__ __attribute__((aligned(16))) int32_t s_ibuf[2 * kIdxBlock];
     dm = WideDma{(uint8_t SMD_LDS *)s_raw, (int32_t SMD_LDS *)s_ibuf};
+  } else if constexpr (RINGB) {
+    __shared__ __attribute__((aligned(1024))) uint8_t s_rawb[kRingBSlots * kTileBytes];
+    __shared__ __attribute__((aligned(16))) int32_t s_ibufb[2 * kIdxBlock];
+    dm = WideDma{(uint8_t SMD_LDS *)s_rawb, (int32_t SMD_LDS *)s_ibufb};
   }
   WideState w;
   const WideLanes L = wide_lanes(lane);
@@ -55,6 +61,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     attend_range_wide_qf8<P_HILO, true, 7>(a, sm, dm, a.indices + (int64_t)b * a.indices_stride, p0, p1, wave, lane,
                                         qbase, q, L, w);
     static_assert(raw_slots<true>() * raw_slot<true>() >= 4 * kStageWave, "staging slices fit the raw ring");
+    stage = dm.raw + wave * kStageWave;
+  } else if constexpr (RINGB) {
+    bf16x8 qreg[kQRegDma];  // loaded by attend_range_wide_b
+    attend_range_wide_b<PACKED, P_HILO>(a, sm, dm, a.indices + (int64_t)b * a.indices_stride, p0, p1, wave, lane,
+                                        qbase, qreg, L, w);
     stage = dm.raw + wave * kStageWave;
   } else {
     bf16x8 qreg[wide_qreg<wide_ring<FP8>()>()];  // loaded by attend_range_wide
