@@ -58,7 +58,7 @@ enum {
 };
 
 /* Largest split count of the split-KV entry points. */
-#define SMD_MAX_SPLITS 32
+#define SMD_MAX_SPLITS 128
 /* Largest number of partials one merge (smd_merge_partials) combines, e.g.
  * the splits of several callers' partial decodes of one index list. */
 #define SMD_MAX_MERGE_SPLITS 1024
@@ -135,10 +135,13 @@ typedef struct smd_kv_pool {
  *   wide(s)   = waves_w(s) * (wide_fixed + tiles(s) * (tile + floor(wide_tile_load * busy_w(s) / num_cus)))
  *               + tail(s)
  *
- * cost(s) = min(narrow(s), wide(s)) (narrow alone when wide does not apply).
- * s ranges over [1, min(cap, ceil(kv_len / 64))] with cap = short_cap when
- * kv_len < long_kv, else long_cap (both <= SMD_MAX_SPLITS); the smallest s of
- * minimum cost wins, and its family is wide when wide(s) < narrow(s).
+ * Caps, each also at most ceil(kv_len / 64): below long_kv indices both
+ * families take s <= short_cap; from there on narrow takes s <= long_cap and
+ * wide s <= wide_cap (0: long_cap).  All caps are <= SMD_MAX_SPLITS.
+ * cost(s) = min of the families that take s; the smallest s of minimum cost
+ * wins, and its family is wide when wide(s) is below narrow(s) or narrow does
+ * not take s.  (A wide workgroup covers 8 narrow ones' query rows, so the
+ * wide family reaches the same grid size with up to 8 times the splits.)
  */
 typedef struct smd_plan_model {
   int64_t fixed_ps;     /* per workgroup wave: prologue, wave merge, epilogue */
@@ -158,6 +161,8 @@ typedef struct smd_plan_model {
   int64_t wide_tile_ps;      /* per wide tile, bf16 pool, GPU otherwise idle  */
   int64_t wide_tile_fp8_ps;  /* per wide tile, fp8 pool, GPU otherwise idle   */
   int64_t wide_tile_load_ps; /* added per wide tile with every CU busy        */
+  int32_t wide_cap;          /* wide split cap from long_kv on; 0: long_cap   */
+  int32_t reserved;          /* must be 0                                     */
 } smd_plan_model;
 
 /*
@@ -231,10 +236,11 @@ int smd_split_bounds(int32_t kv_len, int32_t num_splits, int32_t split, int32_t 
  *   SMD_KERNEL_WIDE    128 query rows per workgroup, 4 waves of 32 rows on
  *                      32x32 MFMAs sharing every gathered row (M a multiple of
  *                      128, one source).
- * SMD_KERNEL_AUTO picks WIDE when it fits and the built-in planner model
- * prices it below the narrow kernels at the call's split count (wide(s) <
- * narrow(s) in the model above, with num_seqs = num_tokens / q_per_seq and
- * kv_len = the index count); otherwise PAIRS when M is a multiple of 32 and,
+ * SMD_KERNEL_AUTO picks WIDE when it fits and either the built-in planner
+ * model prices it below the narrow kernels at the call's split count (wide(s)
+ * < narrow(s) in the model above, with num_seqs = num_tokens / q_per_seq and
+ * kv_len = the index count) or that count exceeds the narrow family's cap
+ * (short_cap below long_kv indices, long_cap from there on); otherwise PAIRS when M is a multiple of 32 and,
  * with W = (num_tokens / q_per_seq) * num_splits * (M / 32), 7 * ceil(W /
  * 256) < 4 * ceil(2W / 256); otherwise ROWS16.  A named family that does not
  * fit the shape is SMD_ERR_UNSUPPORTED.
@@ -583,9 +589,9 @@ int smd_paged_decode(const void *q, int32_t num_seqs, int32_t mtp, int32_t num_q
 
 /*
  * A split count for smd_paged_decode: enough splits for num_seqs *
- * num_kv_heads * s workgroups to cover num_cus (<= 0: 256) once, capped by
- * SMD_MAX_SPLITS and ceil(max_context_len / 64), raised until a split spans
- * at most 4095 pages.  A heuristic of this library (the page's planner and
+ * num_kv_heads * s workgroups to cover num_cus (<= 0: 256) once, capped at 32
+ * and ceil(max_context_len / 64), raised (up to SMD_MAX_SPLITS) until a split
+ * spans at most 4095 pages.  A heuristic of this library (the page's planner and
  * budgets are not printed).  Host only, pure; SMD_ERR_* on bad sizes.
  */
 int32_t smd_paged_num_splits(int32_t num_seqs, int32_t num_kv_heads, int32_t max_context_len, int32_t page_size,

@@ -46,6 +46,7 @@ class PlanModel:
     wide_tile_ps: int = 0
     wide_tile_fp8_ps: int = 0
     wide_tile_load_ps: int = 0
+    wide_cap: int = 0  # wide split cap from long_kv on; 0: long_cap
 
 
 def split_cost(s: int, num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, num_cus: int,
@@ -105,26 +106,31 @@ def wide_split_cost(s: int, num_seqs: int, num_heads: int, q_per_seq: int, kv_le
 
 def plan_decode(num_seqs: int, num_heads: int, q_per_seq: int, kv_len: int, kv_dtype: int, num_cus: int,
                 model: PlanModel, two_source: bool = False) -> tuple[int, bool]:
-    """(s, wide): s is the argmin of min(``split_cost``, ``wide_split_cost``)
-    over s = 1 .. min(cap, ceil(kv_len / 64)), cap = short_cap below long_kv
-    indices, long_cap from there on; ties keep the smaller s.  wide says the
-    wide cost was strictly below the narrow one at that s.  A two-source call
-    has no wide workgroups.  Empty problems plan (1, False)."""
+    """(s, wide): s is the argmin over the split counts each family takes of
+    the family's cost (``split_cost`` narrow, ``wide_split_cost`` wide); ties
+    keep the smaller s, and at one s wide wins only when strictly cheaper.
+    Below long_kv indices both families take s <= short_cap; from there on
+    narrow takes s <= long_cap and wide s <= wide_cap (0: long_cap); every cap
+    is also at most ceil(kv_len / 64).  A two-source call, or a model without
+    wide workgroups, prices narrow alone.  Empty problems plan (1, False)."""
     if min(num_seqs, num_heads, q_per_seq, kv_len) < 0:
         raise ValueError("negative size")
     if num_seqs == 0 or kv_len == 0 or num_heads == 0 or q_per_seq == 0:
         return 1, False
-    cap = model.short_cap if kv_len < model.long_kv else model.long_cap
-    cap = min(cap, _cdiv(kv_len, SPLIT_ALIGN))
+    tiles = _cdiv(kv_len, SPLIT_ALIGN)
+    short = kv_len < model.long_kv
+    cap_n = min(model.short_cap if short else model.long_cap, tiles)
+    cap_w = min(model.short_cap if short else (model.wide_cap or model.long_cap), tiles)
     best_s, best, best_wide = 1, None, False
-    for s in range(1, cap + 1):
-        cost = split_cost(s, num_seqs, num_heads, q_per_seq, kv_len, num_cus, model)
-        wide = False
-        if not two_source:
+    for s in range(1, max(cap_n, cap_w) + 1):
+        cost, wide = None, False
+        if s <= cap_n:
+            cost = split_cost(s, num_seqs, num_heads, q_per_seq, kv_len, num_cus, model)
+        if not two_source and s <= cap_w:
             cw = wide_split_cost(s, num_seqs, num_heads, q_per_seq, kv_len, kv_dtype, num_cus, model)
-            if cw is not None and cw < cost:
+            if cw is not None and (cost is None or cw < cost):
                 cost, wide = cw, True
-        if best is None or cost < best:
+        if cost is not None and (best is None or cost < best):
             best, best_s, best_wide = cost, s, wide
     return best_s, best_wide
 

@@ -19,7 +19,7 @@ import torch
 NOPE = 448
 ROPE = 64
 DIM = 512
-MAX_SPLITS = 32
+MAX_SPLITS = 128
 MAX_MERGE_SPLITS = 1024
 NOALLOC_SCRATCH_BYTES = 32 << 20
 SPLIT_ALIGN = 64
@@ -107,6 +107,8 @@ class PlanModel(ctypes.Structure):
         ("wide_tile_ps", ctypes.c_int64),
         ("wide_tile_fp8_ps", ctypes.c_int64),
         ("wide_tile_load_ps", ctypes.c_int64),
+        ("wide_cap", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 

@@ -125,8 +125,12 @@ static int pick_kernel(int32_t requested, int32_t M, int64_t rows, int32_t s, in
   }
   const smd_plan_model &pm = default_plan_model();
   static_assert(kWideRowsPerGroup == 128, "the planner's wide_rows");
+  // the planner prices the narrow family up to its cap only: beyond it a
+  // split count is a wide plan
+  const int64_t narrow_cap = kv_len < pm.long_kv ? pm.short_cap : pm.long_cap;
   if (wide_fits(M, two) && rows > 0 && kv_len > 0 && wide_priced(pm, M, two) &&
-      wide_cost(pm, rows, M, kv_len, kv_dtype, 256, s) < narrow_cost(pm, rows, M, kv_len, 256, s))
+      (s > narrow_cap ||
+       wide_cost(pm, rows, M, kv_len, kv_dtype, 256, s) < narrow_cost(pm, rows, M, kv_len, 256, s)))
     return kKernWide;
   return pairs_pay(M, rows * s) ? kKernPairs : kKernRows16;
 }
@@ -654,6 +658,7 @@ extern "C" int smd_write_kv_fp8(const void *kv, int64_t kv_stride, int32_t num_r
 namespace smd {
 constexpr int32_t kPagedRows = 64;     // (Hq / Hkv) * mtp query rows per workgroup
 constexpr int32_t kPagedBtMax = 4096;  // block-table entries a split may span
+constexpr int32_t kPagedMaxSplits = 32;  // smd_paged_num_splits' cap
 
 static int64_t paged_chunk(int32_t max_ctx, int32_t s) {
   const int64_t per = ((int64_t)max_ctx + s - 1) / s;
@@ -676,7 +681,7 @@ extern "C" int32_t smd_paged_num_splits(int32_t num_seqs, int32_t num_kv_heads, 
   const int64_t cap_len = (max_context_len + kSplitAlign - 1) / kSplitAlign;
   int64_t s = (cus + units - 1) / units;  // fill the GPU once
   if (s > cap_len) s = cap_len;
-  if (s > SMD_MAX_SPLITS) s = SMD_MAX_SPLITS;
+  if (s > kPagedMaxSplits) s = kPagedMaxSplits;
   if (s < 1) s = 1;
   while (s < SMD_MAX_SPLITS && !paged_chunk_fits(paged_chunk(max_context_len, (int32_t)s), page_size)) ++s;
   if (!paged_chunk_fits(paged_chunk(max_context_len, (int32_t)s), page_size)) {

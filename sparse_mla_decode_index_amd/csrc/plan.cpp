@@ -8,7 +8,9 @@
 // CU, one tile per 32 positions); a step or tile costs more the fuller the
 // GPU.  The caps follow the vLLM page "[ROCm][DSV4][Perf] Optimize Triton
 // sparse-MLA decode on gfx950", Design: at most four splits for short index
-// lists, up to 32 for long ones.
+// lists, up to 32 for long ones -- for the narrow family; the wide family,
+// whose workgroup covers eight narrow ones' query rows, may take up to 128
+// splits of a long list to fill the same grid.
 //
 // Pure integer arithmetic in picoseconds; no device access, so it may run
 // during graph capture.
@@ -43,6 +45,8 @@ static const smd_plan_model kDefaultModel = {
     /*wide_tile_ps=*/1774000,
     /*wide_tile_fp8_ps=*/2192000,
     /*wide_tile_load_ps=*/536000,
+    /*wide_cap=*/128,
+    /*reserved=*/0,
 };
 
 static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -100,9 +104,10 @@ static bool model_ok(const smd_plan_model *model, const char *fn) {
   }
   if (model->wg_per_cu < 1 || model->rows_per_wg < 1 || model->waves_per_wg < 1 || model->short_cap < 1 ||
       model->long_cap < 1 || model->short_cap > SMD_MAX_SPLITS || model->long_cap > SMD_MAX_SPLITS ||
+      model->wide_cap < 0 || model->wide_cap > SMD_MAX_SPLITS || model->reserved != 0 ||
       model->wide_rows < 0 || (model->wide_rows > 0 && model->wide_tile < 1)) {
-    set_error("%s: invalid model (sizes and caps must be >= 1, caps <= %d, wide_rows >= 0, wide_tile >= 1 "
-              "when wide_rows > 0)", fn, SMD_MAX_SPLITS);
+    set_error("%s: invalid model (sizes and caps must be >= 1, caps <= %d, wide_cap in [0, %d], reserved 0, "
+              "wide_rows >= 0, wide_tile >= 1 when wide_rows > 0)", fn, SMD_MAX_SPLITS, SMD_MAX_SPLITS);
     return false;
   }
   return true;
@@ -136,16 +141,20 @@ extern "C" int smd_plan_decode(int32_t num_seqs, int32_t num_heads, int32_t q_pe
   const int64_t cus = num_cus > 0 ? num_cus : 256;
   const int64_t M = (int64_t)num_heads * q_per_seq;
   const bool wide = wide_priced(*model, M, two_source != 0);
-  const int64_t cap_len = kv_len < model->long_kv ? model->short_cap : model->long_cap;
+  const bool is_short = kv_len < model->long_kv;
   const int64_t cap_tiles = ceil_div(kv_len, SMD_SPLIT_ALIGN);
-  const int64_t cap = cap_len < cap_tiles ? cap_len : cap_tiles;
+  const int64_t cap_n0 = is_short ? model->short_cap : model->long_cap;
+  const int64_t cap_w0 = is_short ? model->short_cap : (model->wide_cap > 0 ? model->wide_cap : model->long_cap);
+  const int64_t cap_n = cap_n0 < cap_tiles ? cap_n0 : cap_tiles;
+  const int64_t cap_w = wide ? (cap_w0 < cap_tiles ? cap_w0 : cap_tiles) : 0;
+  const int64_t cap = cap_n > cap_w ? cap_n : cap_w;
   int best_s = 1;
   bool best_wide = false;
   int64_t best_cost = INT64_MAX;
   for (int64_t s = 1; s <= cap; ++s) {
-    int64_t cost = narrow_cost(*model, num_seqs, M, kv_len, cus, s);
+    int64_t cost = s <= cap_n ? narrow_cost(*model, num_seqs, M, kv_len, cus, s) : INT64_MAX;
     bool w = false;
-    if (wide) {
+    if (s <= cap_w) {
       const int64_t cw = wide_cost(*model, num_seqs, M, kv_len, kv_dtype, cus, s);
       if (cw < cost) {
         cost = cw;

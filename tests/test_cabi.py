@@ -57,7 +57,7 @@ def _model_pair(rng):
              long_kv=int(rng.integers(1, 20000)), wide_rows=int(rng.choice([0, 64, 128, 256])),
              wide_tile=int(rng.choice([16, 32, 64])), wide_fixed_ps=int(rng.integers(0, 30_000_000)),
              wide_tile_ps=int(rng.integers(1, 4_000_000)), wide_tile_fp8_ps=int(rng.integers(1, 4_000_000)),
-             wide_tile_load_ps=int(rng.integers(0, 2_000_000)))
+             wide_tile_load_ps=int(rng.integers(0, 2_000_000)), wide_cap=int(rng.choice([0, 1, 16, 64, 128])))
     c = smd.PlanModel()
     for k, x in v.items():
         setattr(c, k, x)
@@ -82,8 +82,9 @@ def test_planner_formula_bit_exact_vs_oracle():
 def test_default_model_fields_round_trip():
     """Every coefficient of the built-in model reaches the oracle's mirror."""
     pm = _library_model()
-    assert pm.wide_rows == 128 and pm.wide_tile == 32 and pm.rows_per_wg == 16
-    assert set(vars(pm)) == {name for name, _ in smd.PlanModel._fields_}
+    assert pm.wide_rows == 128 and pm.wide_tile == 32 and pm.rows_per_wg == 16 and pm.wide_cap == 128
+    assert smd.plan_default_model().reserved == 0
+    assert set(vars(pm)) == {name for name, _ in smd.PlanModel._fields_ if name != "reserved"}
 
 
 def test_default_planner_properties():
@@ -91,8 +92,9 @@ def test_default_planner_properties():
     for rows in [1, 2, 8, 32, 64, 256]:
         for H in [16, 64, 128]:
             for K in [64, 384, 2176, 6528, 32128, 65664]:
-                s = smd.plan_num_kv_splits(rows, H, K)
-                assert 1 <= s <= 32
+                s, wide = smd.plan_decode(rows, H, K)
+                assert s == smd.plan_num_kv_splits(rows, H, K)
+                assert 1 <= s <= (128 if wide else 32)  # the narrow family: at most 32
                 if K < 4096:
                     assert s <= 4          # short workloads: at most four splits
                 assert s <= -(-K // 64)    # never more splits than 64-row chunks
@@ -144,7 +146,7 @@ def _decode(pool=None, **kw):
     (dict(qps=9), -2, "q_per_seq"),
     (dict(T=3, qps=2), -1, "multiple"),
     (dict(s=0), -1, "num_splits"),
-    (dict(s=33), -1, "num_splits"),
+    (dict(s=129), -1, "num_splits"),
     (dict(T=-1), -1, "negative"),
     (dict(topk=-5), -1, "negative"),
     (dict(s=2), -3, "partial_o"),
@@ -500,13 +502,15 @@ def test_two_source_empty_launches_nothing():
 
 def _library_model():
     c = smd.plan_default_model()
-    return plan_ref.PlanModel(**{name: getattr(c, name) for name, _ in smd.PlanModel._fields_})
+    return plan_ref.PlanModel(**{name: getattr(c, name) for name, _ in smd.PlanModel._fields_ if name != "reserved"})
 
 
 @pytest.mark.parametrize("T,H,qps,s,K,kvd,two,req,want", [
     (64, 128, 1, 4, 65664, 1, False, None, "wide"),   # 256 wide workgroups of 514 tiles each
     (32, 128, 1, 1, 2176, 0, False, None, "rows16"),  # 32 wide workgroups: the narrow grid is cheaper
     (1, 128, 1, 31, 65664, 0, False, None, "rows16"),  # low batch, long list: narrow, 248 workgroups
+    (4, 128, 1, 61, 65664, 0, False, None, "wide"),   # beyond the narrow cap of 32: a wide plan
+    (4, 64, 1, 61, 65664, 0, False, None, "pairs"),   # M = 64 has no wide family: narrow at any s
     (256, 128, 4, 1, 4096, 1, False, None, "wide"),   # MTP4: M = 512, 64 rows x 4 groups
     (64, 128, 1, 1, 384, 0, False, None, "pairs"),    # short list: wide's fixed cost loses; pairs pay
     (32, 128, 1, 8, 65664, 1, True, None, "pairs"),   # two sources never take the wide kernel
@@ -526,7 +530,8 @@ def test_decode_kernel_choice(T, H, qps, s, K, kvd, two, req, want):
 def test_decode_kernel_choice_follows_the_cost_model():
     """AUTO picks wide exactly where the oracle's cost formula, with the
     library's coefficients, prices the wide workgroups strictly below the
-    narrow ones, and the planner's own family agrees at its chosen s."""
+    narrow ones or the split count is beyond the narrow family's cap, and the
+    planner's own family agrees at its chosen s."""
     pm = _library_model()
     rng = np.random.default_rng(5)
     for _ in range(300):
@@ -535,9 +540,10 @@ def test_decode_kernel_choice_follows_the_cost_model():
         qps = int(rng.choice([1, 2, 4]))
         K = int(rng.integers(1, 70000))
         kvd = int(rng.integers(0, 2))
-        s = int(rng.integers(1, 33))
+        s = int(rng.integers(1, 129))
         cw = plan_ref.wide_split_cost(s, rows, H, qps, K, kvd, 256, pm)
-        wide = cw is not None and cw < plan_ref.split_cost(s, rows, H, qps, K, 256, pm)
+        narrow_cap = pm.short_cap if K < pm.long_kv else pm.long_cap
+        wide = cw is not None and (s > narrow_cap or cw < plan_ref.split_cost(s, rows, H, qps, K, 256, pm))
         got = smd.decode_kernel_choice(rows * qps, H, qps, s, K, kvd)
         assert (got == "wide") == wide, (rows, H, qps, K, kvd, s)
         ps, pw = smd.plan_decode(rows, H, K, qps, kvd)
@@ -575,7 +581,7 @@ def _paged(**kw):
     (dict(page=24), -2, "page_size"),             # not a power of two
     (dict(page=8), -2, "page_size"),              # below 16
     (dict(s=0), -1, "num_splits"),
-    (dict(s=33), -1, "num_splits"),
+    (dict(s=129), -1, "num_splits"),
     (dict(bts=10), -1, "block_tables_stride"),    # 1000 positions need 63 pages
     (dict(max_ctx=1 << 20, bts=1 << 16), -1, "splits"),  # one split spanning 65536 pages
     (dict(scale=float("nan")), -1, "softmax_scale"),

@@ -2,6 +2,8 @@
 the sequences' plan units -- two charged per sequence, then one per
 64-position tile -- over P partitions) and of the piecewise merge it implies.
 CPU only."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -212,7 +214,35 @@ def _fitted_model(wide: bool = True):
                         part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
                         long_cap=32, long_kv=4096, wide_rows=128 if wide else 0, wide_tile=32,
                         wide_fixed_ps=13648000, wide_tile_ps=1774000, wide_tile_fp8_ps=2192000,
-                        wide_tile_load_ps=536000)
+                        wide_tile_load_ps=536000, wide_cap=128 if wide else 0)
+
+
+def test_planner_wide_cap_worked_example():
+    """4 index rows x 128 heads x 65664 bf16 indices: from long_kv on, the
+    wide family takes up to wide_cap = 128 splits, the narrow one 32.
+      s=61: 4*61 = 244 workgroups, one round; ceil(65664/61) = 1077 -> chunk
+            1088, 34 tiles at 1774000 + 536000*244//256 = 2284875:
+            13648000 + 34*2284875 + 4065000 + 287*4*128*61          = 104362334
+      s=60: chunk ceil(1095/64)*64 = 1152, 36 tiles at 2276500:
+            13648000 + 36*2276500 + 4065000 + 287*4*128*60          = 108483640
+      s=62: 248 workgroups, chunk 1088, 34 tiles at 2293250:
+            13648000 + 34*2293250 + 4065000 + 287*4*128*62          = 104794028
+      s=64: 256 workgroups, 34 tiles at 2310000                      = 105657416
+      s=65: 260 workgroups take two rounds                           = 188752360
+    so the plan is 61 splits on the wide kernel.  With wide_cap = 0 (the long
+    cap, 32) it is 32 splits on the wide kernel (157187208), below the
+    narrow family's best, s = 8 (177534552)."""
+    m = _fitted_model()
+    want = {61: 104362334, 60: 108483640, 62: 104794028, 64: 105657416, 65: 188752360}
+    for s, c in want.items():
+        assert pr.wide_split_cost(s, 4, 128, 1, 65664, 0, 256, m) == c, s
+    assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m) == (61, True)
+    m32 = dataclasses.replace(m, wide_cap=0)
+    assert pr.wide_split_cost(32, 4, 128, 1, 65664, 0, 256, m32) == 157187208
+    assert pr.split_cost(8, 4, 128, 1, 65664, 256, m32) == 177534552
+    assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m32) == (32, True)
+    # a short list keeps both families within short_cap
+    assert pr.plan_decode(4, 128, 1, 2176, 0, 256, m)[0] <= 4
 
 
 def test_planner_cost_worked_example_short_list():
