@@ -6,11 +6,12 @@
 // narrow kernels' (16 query rows, eight waves, one step per 16 positions of
 // each wave's share) and the wide kernel's (128 query rows, one workgroup per
 // CU, one tile per 32 positions); a step or tile costs more the fuller the
-// GPU.  The caps follow the vLLM page "[ROCm][DSV4][Perf] Optimize Triton
-// sparse-MLA decode on gfx950", Design: at most four splits for short index
-// lists, up to 32 for long ones -- for the narrow family; the wide family,
-// whose workgroup covers eight narrow ones' query rows, may take up to 128
-// splits of a long list to fill the same grid.
+// GPU.  The caps: at most four splits for short index lists, as the vLLM
+// page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on gfx950",
+// Design, caps them; for long lists that page allows up to 32 splits of its
+// kernel's programs, and here both families may take up to 128 -- the model
+// prices what each split adds, and grids of few query rows (16 heads, one
+// token) fill the GPU only beyond 32 splits.
 //
 // Pure integer arithmetic in picoseconds; no device access, so it may run
 // during graph capture.
@@ -37,7 +38,7 @@ static const smd_plan_model kDefaultModel = {
     /*waves_per_wg=*/8,
     /*wg_per_cu=*/1,
     /*short_cap=*/4,
-    /*long_cap=*/32,
+    /*long_cap=*/128,
     /*long_kv=*/4096,
     /*wide_rows=*/128,
     /*wide_tile=*/32,
@@ -45,7 +46,7 @@ static const smd_plan_model kDefaultModel = {
     /*wide_tile_ps=*/1774000,
     /*wide_tile_fp8_ps=*/2192000,
     /*wide_tile_load_ps=*/536000,
-    /*wide_cap=*/128,
+    /*wide_cap=*/0,
     /*reserved=*/0,
 };
 

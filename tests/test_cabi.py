@@ -82,7 +82,7 @@ def test_planner_formula_bit_exact_vs_oracle():
 def test_default_model_fields_round_trip():
     """Every coefficient of the built-in model reaches the oracle's mirror."""
     pm = _library_model()
-    assert pm.wide_rows == 128 and pm.wide_tile == 32 and pm.rows_per_wg == 16 and pm.wide_cap == 128
+    assert pm.wide_rows == 128 and pm.wide_tile == 32 and pm.rows_per_wg == 16 and pm.long_cap == 128
     assert smd.plan_default_model().reserved == 0
     assert set(vars(pm)) == {name for name, _ in smd.PlanModel._fields_ if name != "reserved"}
 
@@ -94,7 +94,7 @@ def test_default_planner_properties():
             for K in [64, 384, 2176, 6528, 32128, 65664]:
                 s, wide = smd.plan_decode(rows, H, K)
                 assert s == smd.plan_num_kv_splits(rows, H, K)
-                assert 1 <= s <= (128 if wide else 32)  # the narrow family: at most 32
+                assert 1 <= s <= 128
                 if K < 4096:
                     assert s <= 4          # short workloads: at most four splits
                 assert s <= -(-K // 64)    # never more splits than 64-row chunks

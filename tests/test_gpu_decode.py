@@ -55,6 +55,18 @@ def test_bf16_ragged_tail(gpu, H, s):
     run_case(w, gpu, s)
 
 
+@pytest.mark.parametrize("H,kv_dtype,s,partials", [(16, "bf16", 103, False), (16, "fp8", 128, False),
+                                                    (32, "bf16", 64, False), (16, "bf16", 77, True)])
+def test_narrow_beyond_32_splits(gpu, H, kv_dtype, s, partials):
+    """The narrow kernels at the split counts the planner reaches for grids of
+    few query rows (16 heads, one or two tokens): 8300 positions in splits of
+    128 (s = 103, 128 and 77: 65 non-empty) or of 192 (s = 64: 44 non-empty),
+    the empty ones included, through the merge or as FP32 partials."""
+    w = wl.dense_workload("narrow many splits", T=2, H=H, kv_dtype=kv_dtype, pool_rows=16384, topk=8250, swa=50,
+                          invalid=40, seed=21 + H + s)
+    run_case(w, gpu, s, partials=partials)
+
+
 @pytest.mark.parametrize("s", [1, 4])
 def test_bf16_partials(gpu, s):
     w = wl.dense_workload("bf16 partials", T=2, H=64, kv_dtype="bf16", pool_rows=2048, topk=500, invalid=5,

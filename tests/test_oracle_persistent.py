@@ -212,14 +212,14 @@ def _fitted_model(wide: bool = True):
     family (wide_rows = 0), so that only the narrow formula prices a plan."""
     return pr.PlanModel(fixed_ps=7194000, step_ps=1971000, step_load_ps=569000, merge_ps=4065000,
                         part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
-                        long_cap=32, long_kv=4096, wide_rows=128 if wide else 0, wide_tile=32,
+                        long_cap=128, long_kv=4096, wide_rows=128 if wide else 0, wide_tile=32,
                         wide_fixed_ps=13648000, wide_tile_ps=1774000, wide_tile_fp8_ps=2192000,
-                        wide_tile_load_ps=536000, wide_cap=128 if wide else 0)
+                        wide_tile_load_ps=536000, wide_cap=0)
 
 
 def test_planner_wide_cap_worked_example():
-    """4 index rows x 128 heads x 65664 bf16 indices: from long_kv on, the
-    wide family takes up to wide_cap = 128 splits, the narrow one 32.
+    """4 index rows x 128 heads x 65664 bf16 indices: from long_kv on, both
+    families take up to long_cap = 128 splits (wide_cap 0: the same).
       s=61: 4*61 = 244 workgroups, one round; ceil(65664/61) = 1077 -> chunk
             1088, 34 tiles at 1774000 + 536000*244//256 = 2284875:
             13648000 + 34*2284875 + 4065000 + 287*4*128*61          = 104362334
@@ -229,18 +229,20 @@ def test_planner_wide_cap_worked_example():
             13648000 + 34*2293250 + 4065000 + 287*4*128*62          = 104794028
       s=64: 256 workgroups, 34 tiles at 2310000                      = 105657416
       s=65: 260 workgroups take two rounds                           = 188752360
-    so the plan is 61 splits on the wide kernel.  With wide_cap = 0 (the long
-    cap, 32) it is 32 splits on the wide kernel (157187208), below the
-    narrow family's best, s = 8 (177534552)."""
+    so the plan is 61 splits on the wide kernel.  With both caps at 32
+    (long_cap = 32) it is 32 splits on the wide kernel (157187208), below the
+    narrow family's best, s = 8 (177534552); with the narrow family at 32 and
+    wide_cap = 128 it is 61 wide splits again."""
     m = _fitted_model()
     want = {61: 104362334, 60: 108483640, 62: 104794028, 64: 105657416, 65: 188752360}
     for s, c in want.items():
         assert pr.wide_split_cost(s, 4, 128, 1, 65664, 0, 256, m) == c, s
     assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m) == (61, True)
-    m32 = dataclasses.replace(m, wide_cap=0)
+    m32 = dataclasses.replace(m, long_cap=32)
     assert pr.wide_split_cost(32, 4, 128, 1, 65664, 0, 256, m32) == 157187208
     assert pr.split_cost(8, 4, 128, 1, 65664, 256, m32) == 177534552
     assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m32) == (32, True)
+    assert pr.plan_decode(4, 128, 1, 65664, 0, 256, dataclasses.replace(m32, wide_cap=128)) == (61, True)
     # a short list keeps both families within short_cap
     assert pr.plan_decode(4, 128, 1, 2176, 0, 256, m)[0] <= 4
 
@@ -265,7 +267,8 @@ def test_planner_cost_worked_example_short_list():
 
 
 def test_planner_cost_worked_example_long_list_and_waves():
-    """One row x 128 heads x 65664 indices (long cap 32):
+    """One row x 128 heads x 65664 indices (beyond 32 splits its 8 s
+    workgroups take two rounds, so the plan stays below 33):
       s=32: chunk ceil(65664/32)=2052 -> 2112, 132 half-tiles -> 17 steps, all
             256 slots busy (step 2540000): 7194000 + 17*2540000 + 4065000
             + 287*128*32                                            = 55614552
