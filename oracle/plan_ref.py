@@ -10,7 +10,8 @@
   of a split count is that of the cheaper kind, and the plan also names which
   kind won.  The vLLM page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA
   decode on gfx950" (Design) caps short workloads at four splits and allows
-  up to 32 for long contexts.  The fitted coefficients are not printed on
+  more for long contexts (32 for its kernel; the caps are model fields
+  here).  The fitted coefficients are not printed on
   either page; here they are an explicit argument, so the formula is pinned
   while the library's fitted values are parity unpinned.
 * ``split_bounds`` lives in ``oracle.ref`` (it defines the partial semantics).
@@ -20,7 +21,7 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 SPLIT_ALIGN = 64
-MAX_SPLITS = 32
+MAX_SPLITS = 128
 
 
 def _cdiv(a: int, b: int) -> int:
