@@ -6,12 +6,12 @@
 // narrow kernels' (16 query rows, eight waves, one step per 16 positions of
 // each wave's share) and the wide kernel's (128 query rows, one workgroup per
 // CU, one tile per 32 positions); a step or tile costs more the fuller the
-// GPU.  The caps: at most four splits for short index lists, as the vLLM
-// page "[ROCm][DSV4][Perf] Optimize Triton sparse-MLA decode on gfx950",
-// Design, caps them; for long lists that page allows up to 32 splits of its
-// kernel's programs, and here both families may take up to 128 -- the model
-// prices what each split adds, and grids of few query rows (16 heads, one
-// token) fill the GPU only beyond 32 splits.
+// GPU.  The caps are model fields (short_cap below long_kv indices,
+// long_cap from there on).  The vLLM page "[ROCm][DSV4][Perf] Optimize Triton
+// sparse-MLA decode on gfx950", Design, caps its kernel at four splits for
+// short workloads and 32 for long ones; here the model prices what each
+// split adds, and grids of few query rows fill the GPU only with more
+// splits, so both defaults are 128.
 //
 // Pure integer arithmetic in picoseconds; no device access, so it may run
 // during graph capture.
@@ -37,7 +37,7 @@ static const smd_plan_model kDefaultModel = {
     /*rows_per_wg=*/16,
     /*waves_per_wg=*/8,
     /*wg_per_cu=*/1,
-    /*short_cap=*/4,
+    /*short_cap=*/128,
     /*long_cap=*/128,
     /*long_kv=*/4096,
     /*wide_rows=*/128,

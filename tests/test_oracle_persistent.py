@@ -211,7 +211,7 @@ def _fitted_model(wide: bool = True):
     """The library's built-in coefficients; wide=False leaves out the wide
     family (wide_rows = 0), so that only the narrow formula prices a plan."""
     return pr.PlanModel(fixed_ps=7194000, step_ps=1971000, step_load_ps=569000, merge_ps=4065000,
-                        part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=4,
+                        part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=128,
                         long_cap=128, long_kv=4096, wide_rows=128 if wide else 0, wide_tile=32,
                         wide_fixed_ps=13648000, wide_tile_ps=1774000, wide_tile_fp8_ps=2192000,
                         wide_tile_load_ps=536000, wide_cap=0)
@@ -244,7 +244,7 @@ def test_planner_wide_cap_worked_example():
     assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m32) == (32, True)
     assert pr.plan_decode(4, 128, 1, 65664, 0, 256, dataclasses.replace(m32, wide_cap=128)) == (61, True)
     # a short list keeps both families within short_cap
-    assert pr.plan_decode(4, 128, 1, 2176, 0, 256, m)[0] <= 4
+    assert pr.plan_decode(4, 128, 1, 2176, 0, 256, dataclasses.replace(m, short_cap=4))[0] <= 4
 
 
 def test_planner_cost_worked_example_short_list():
@@ -258,8 +258,9 @@ def test_planner_cost_worked_example_short_list():
            7194000 + 6*2184375 + 4065000 + 287*8*64*3                = 24806082
       s=4: 544 -> chunk 576 -> 36 -> 5 steps, step 2255500;
            7194000 + 5*2255500 + 4065000 + 287*8*64*4                = 23124276
-    and the short-list cap (2176 < 4096) stops at s = 4."""
-    m = _fitted_model(wide=False)
+    and a short-list cap of 4 (2176 < 4096; the library's default is 128) stops
+    at s = 4."""
+    m = dataclasses.replace(_fitted_model(wide=False), short_cap=4)
     want = {1: 41910125, 2: 30572138, 3: 24806082, 4: 23124276}
     for s, c in want.items():
         assert pr.split_cost(s, 8, 64, 1, 2176, 256, m) == c, s
