@@ -327,14 +327,17 @@ typedef struct smd_decode_options {
  *           smd_split_bounds() gives.
  *  partial_o   fp32 [num_tokens, num_heads, num_splits, 512]
  *  partial_lse fp32 [num_tokens, num_heads, num_splits]
- *           Required when num_splits > 1 or out == NULL.  Partial r holds
+ *           Required when num_splits > 1 or out == NULL.  With out == NULL
+ *           they are the result: partial r holds
  *           o_r = sum_{j in r} e^{s_j - lse_r} row_j and
  *           lse_r = ln sum_{j in r} e^{s_j} (no sink); an empty or
- *           all-invalid split holds o_r = 0, lse_r = -inf.
+ *           all-invalid split holds o_r = 0, lse_r = -inf.  With out they
+ *           are scratch for the merge (o_r kept as bf16 in the buffer's
+ *           first half; contents afterwards unspecified).
  *  out      bf16 [num_tokens, num_heads, 512] or NULL (partials only)
  *  lse      fp32 [num_tokens, num_heads] or NULL; ln Z including the sink.
  *  With num_splits > 1 and out != NULL the call also launches the merge
- *  (smd_merge_partials).  A row with no valid index gets out = 0 and
+ *  (smd_merge_partials' operation, on the bf16 scratch partials).  A row with no valid index gets out = 0 and
  *  lse = sink_h (-inf without a sink).  topk == 0 or num_tokens == 0
  *  launches nothing.
  *  The kernel family is SMD_KERNEL_AUTO's choice (see above).
@@ -577,8 +580,8 @@ int smd_write_kv_fp8(const void *kv, int64_t kv_stride, int32_t num_rows, const 
  *  with c = smd_split_bounds' chunk of max_context_len (a split may span at
  *  most 4095 pages, else SMD_ERR_INVALID_ARG).  partial_o fp32 [tokens,
  *  num_q_heads, s, 512] and partial_lse [tokens, num_q_heads, s] are required
- *  when s > 1 or out == NULL (then they are the result; with out the call
- *  also runs smd_merge_partials without a sink).  num_seqs == 0 or
+ *  when s > 1 or out == NULL (then they are the result; with out they are
+ *  scratch, o kept as bf16, and the call also merges them without a sink).  num_seqs == 0 or
  *  max_context_len == 0 launches nothing.  Returns SMD_OK or SMD_ERR_*.
  */
 int smd_paged_decode(const void *q, int32_t num_seqs, int32_t mtp, int32_t num_q_heads, const void *k_cache,

@@ -342,7 +342,7 @@ int decode_impl(const char *fn, const void *q_nope, const void *q_rope, int32_t 
   }
   if (need_partials && out) {
     e = launch_merge(partial_o, partial_lse, num_tokens * num_heads, num_heads, num_splits, sink,
-                     (uint16_t *)out, lse, st);
+                     (uint16_t *)out, lse, st, /*bf16_parts=*/true);
     if (e != hipSuccess) {
       set_error("%s: merge launch failed: %s", fn, hipGetErrorString(e));
       return SMD_ERR_HIP;
@@ -423,7 +423,7 @@ extern "C" int smd_merge_partials(const float *partial_o, const float *partial_l
     return SMD_ERR_INVALID_ARG;
   }
   hipError_t e = launch_merge(partial_o, partial_lse, num_tokens * num_heads, num_heads, num_splits,
-                              sink, (uint16_t *)out, lse, (hipStream_t)stream);
+                              sink, (uint16_t *)out, lse, (hipStream_t)stream, /*bf16_parts=*/false);
   if (e != hipSuccess) {
     set_error("%s: merge launch failed: %s", fn, hipGetErrorString(e));
     return SMD_ERR_HIP;
@@ -781,7 +781,7 @@ extern "C" int smd_paged_decode(const void *q, int32_t num_seqs, int32_t mtp, in
   }
   if (need_partials && out) {
     e = launch_merge(partial_o, partial_lse, num_seqs * mtp * num_q_heads, num_q_heads, num_splits, nullptr,
-                     (uint16_t *)out, lse, st);
+                     (uint16_t *)out, lse, st, /*bf16_parts=*/true);
     if (e != hipSuccess) {
       set_error("%s: merge launch failed: %s", fn, hipGetErrorString(e));
       return SMD_ERR_HIP;

@@ -60,8 +60,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     ks::write_direct(o, mm, ll, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
                      (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
   } else {
-    ks::write_partial(o, mm, ll, a.part_o + (qrow * a.S + r) * kDim + dcol,
-                      lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
+    ks::write_partial_any(a.hilo != 0, o, mm, ll, a.part_o, (qrow * a.S + r) * kDim + dcol,
+                          lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
   }
 }
 
@@ -123,9 +123,10 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       ks::write_direct(lo, st.m_ref[qb], l, sk, dst, (a.lse != nullptr && lse_lane) ? a.lse + qrow[qb] : nullptr);
       ks::write_direct(hi, st.m_ref[qb], l, sk, dst + 128, nullptr);
     } else {
-      float *dst = a.part_o + (qrow[qb] * a.S + r) * kDim + dcol;
-      ks::write_partial(lo, st.m_ref[qb], l, dst, lse_lane ? a.part_lse + qrow[qb] * a.S + r : nullptr);
-      ks::write_partial(hi, st.m_ref[qb], l, dst + 128, nullptr);
+      const int64_t off = (qrow[qb] * a.S + r) * kDim + dcol;
+      ks::write_partial_any(a.hilo != 0, lo, st.m_ref[qb], l, a.part_o, off,
+                            lse_lane ? a.part_lse + qrow[qb] * a.S + r : nullptr);
+      ks::write_partial_any(a.hilo != 0, hi, st.m_ref[qb], l, a.part_o, off + 128, nullptr);
     }
   }
 }
@@ -135,7 +136,9 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // reading CH of them (their lse and o) per round trip, so a plan of up to
 // CH * WPR splits costs one round trip.  The row's waves then combine
 // their states through LDS and the row's first wave writes the result.
-template <int WPR, int CH>
+// BF16: the partials' o values are bf16 (in the FP32 buffer's first half),
+// the form of partials that only feed this merge.
+template <int WPR, int CH, bool BF16>
 __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po,
                                                     const float *__restrict__ plse, int rows, int H,
                                                     int S, const float *__restrict__ sink,
@@ -153,6 +156,7 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
   if (live) {
     const float *ls = plse + (int64_t)row * S;
     const float *src = po + (int64_t)row * S * kDim + lane * 8;
+    const uint16_t *srcb = (const uint16_t *)po + (int64_t)row * S * kDim + lane * 8;
     if (w == 0 && sink) {
       mx = sink[row % H];
       z = mx == -INFINITY ? 0.f : 1.f;
@@ -160,13 +164,18 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
     for (int r0 = w; r0 < S; r0 += CH * WPR) {
       float l[CH];
       f32x4 v[CH][2];
+      u32x4 vb[CH];  // BF16: the raw values, widened where they are used (all loads issue first)
 #pragma unroll
       for (int c = 0; c < CH; ++c) {
         const int rr = r0 + c * WPR;
         const int r = rr < S ? rr : r0;  // clamped: every chunk issues the same loads
         l[c] = rr < S ? ls[r] : -INFINITY;
-        v[c][0] = *(const f32x4 *)(src + (int64_t)r * kDim);
-        v[c][1] = *(const f32x4 *)(src + (int64_t)r * kDim + 4);
+        if constexpr (BF16) {
+          vb[c] = *(const u32x4 *)(srcb + (int64_t)r * kDim);
+        } else {
+          v[c][0] = *(const f32x4 *)(src + (int64_t)r * kDim);
+          v[c][1] = *(const f32x4 *)(src + (int64_t)r * kDim + 4);
+        }
       }
       float cm = l[0];
 #pragma unroll
@@ -181,6 +190,15 @@ __global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po
       for (int c = 0; c < CH; ++c) {
         const float e = l[c] == -INFINITY ? 0.f : exp2_fast((l[c] - nm) * kLog2e);
         z += e;
+        if constexpr (BF16) {
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            v[c][i][0] = __uint_as_float(vb[c][2 * i] << 16);
+            v[c][i][1] = __uint_as_float(vb[c][2 * i] & 0xffff0000u);
+            v[c][i][2] = __uint_as_float(vb[c][2 * i + 1] << 16);
+            v[c][i][3] = __uint_as_float(vb[c][2 * i + 1] & 0xffff0000u);
+          }
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           o[i] += e * v[c][0][i];
@@ -279,24 +297,32 @@ hipError_t launch_decode(const DecodeArgs &a, bool fp8, bool pairs, hipStream_t 
                   : launch_decode_f<ks8::kBf16Split>(a, pairs, stream);
 }
 
-template <int WPR, int CH>
+template <int WPR, int CH, bool BF16>
 static hipError_t launch_merge_t(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                                  int32_t S, const float *sink, uint16_t *out, float *lse,
                                  hipStream_t stream) {
   const int rpb = 4 / WPR;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  hipLaunchKernelGGL((merge_kernel<WPR, CH>), grid, dim3(256), 0, stream, part_o, part_lse, rows, H, S,
+  hipLaunchKernelGGL((merge_kernel<WPR, CH, BF16>), grid, dim3(256), 0, stream, part_o, part_lse, rows, H, S,
                      sink, out, lse);
   return hipGetLastError();
 }
 
+template <bool BF16>
+static hipError_t launch_merge_f(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
+                                 int32_t S, const float *sink, uint16_t *out, float *lse,
+                                 hipStream_t stream) {
+  if (S <= 4) return launch_merge_t<1, 4, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  if (S <= 8) return launch_merge_t<2, 4, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  if (S <= 16) return launch_merge_t<4, 4, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  return launch_merge_t<4, 8, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+}
+
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
-                        hipStream_t stream) {
-  if (S <= 4) return launch_merge_t<1, 4>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
-  if (S <= 8) return launch_merge_t<2, 4>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
-  if (S <= 16) return launch_merge_t<4, 4>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
-  return launch_merge_t<4, 8>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+                        hipStream_t stream, bool bf16_parts) {
+  return bf16_parts ? launch_merge_f<true>(part_o, part_lse, rows, H, S, sink, out, lse, stream)
+                    : launch_merge_f<false>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
 }
 
 }  // namespace smd

@@ -255,5 +255,26 @@ __device__ __forceinline__ void write_partial(const f32x4 (&o)[8], float m, floa
   if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
+// The same partial with o rounded to bf16 (lse stays FP32): the form of
+// partials that only feed the merge.  dst indexes bf16 elements.
+__device__ __forceinline__ void write_partial_bf16(const f32x4 (&o)[8], float m, float l, uint16_t *dst,
+                                                   float *lse_dst) {
+  const OutScale sc = partial_scale(m, l);
+#pragma unroll
+  for (int d = 0; d < 8; ++d) *(u32x2 *)(dst + 16 * d) = pack_bf16x4(o[d], sc.inv);
+  if (lse_dst != nullptr) *lse_dst = sc.lse;
+}
+
+// A partial as the call needs it: FP32 when the caller reads the partials
+// (hilo), bf16 in the same buffer when they only feed the merge.  off is the
+// element offset of the row's first dim.
+__device__ __forceinline__ void write_partial_any(bool f32, const f32x4 (&o)[8], float m, float l, float *part_o,
+                                                  int64_t off, float *lse_dst) {
+  if (f32)
+    write_partial(o, m, l, part_o + off, lse_dst);
+  else
+    write_partial_bf16(o, m, l, (uint16_t *)part_o + off, lse_dst);
+}
+
 }  // namespace ks
 }  // namespace smd

@@ -179,11 +179,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
 #pragma unroll
     for (int d = 0; d < 32; ++d) *(u32x2 *)(dst + 16 * d) = pack_bf16x4(st.acc[d], sc.inv);
     if (a.lse != nullptr && lse_lane) a.lse[row] = sc.lse;
-  } else {
+  } else if (a.hilo) {  // FP32 partials, returned to the caller
     const OutScale sc = partial_scale(st.m_ref, l_tot);
     float *dst = a.part_o + (row * a.S + r) * kDim + 4 * Lk.g;
 #pragma unroll
     for (int d = 0; d < 32; ++d) *(f32x4 *)(dst + 16 * d) = st.acc[d] * sc.inv;
+    if (lse_lane) a.part_lse[row * a.S + r] = sc.lse;
+  } else {  // bf16 partials in the same buffer: they only feed the merge
+    const OutScale sc = partial_scale(st.m_ref, l_tot);
+    uint16_t *dst = (uint16_t *)a.part_o + (row * a.S + r) * kDim + 4 * Lk.g;
+#pragma unroll
+    for (int d = 0; d < 32; ++d) *(u32x2 *)(dst + 16 * d) = pack_bf16x4(st.acc[d], sc.inv);
     if (lse_lane) a.part_lse[row * a.S + r] = sc.lse;
   }
 }

@@ -65,9 +65,12 @@ hipError_t launch_decode(const DecodeArgs &a, bool fp8, bool pairs, hipStream_t 
 // split, group of 128 query rows); a.G = M / 128, one source only.
 hipError_t launch_decode_wide(const DecodeArgs &a, bool fp8, hipStream_t stream);
 
+// bf16_parts: the partials' o values are bf16 (the decode kernels write
+// them so when the partials only feed this merge, i.e. hilo == 0); FP32
+// otherwise.
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                         int32_t S, const float *sink, uint16_t *out, float *lse,
-                        hipStream_t stream);
+                        hipStream_t stream, bool bf16_parts);
 
 // Arguments of the dense paged GQA decode (smd_paged_decode).  Pointers are
 // device pointers; caches are bf16 [num_blocks, page, Hkv, 512].

@@ -80,8 +80,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                              : partial_scale(w.m_ref, l_tot);
   if (direct)
     store_rows_wide<false>(w, sc.inv, false, a.out + qbase * kDim, kDim, stage);
-  else
+  else if (a.hilo)  // FP32 partials, returned to the caller
     store_rows_wide<false>(w, sc.inv, true, a.part_o + (qbase * a.S + r) * kDim, (int64_t)a.S * kDim, stage);
+  else  // bf16 partials in the same buffer: they only feed the merge
+    store_rows_wide<false>(w, sc.inv, false, (uint16_t *)a.part_o + (qbase * a.S + r) * kDim, (int64_t)a.S * kDim,
+                           stage);
   float *lse_dst = direct ? (a.lse != nullptr && lse_lane ? a.lse + qrow : nullptr)
                           : (lse_lane ? a.part_lse + qrow * a.S + r : nullptr);
   if (lse_dst != nullptr) *lse_dst = sc.lse;
