@@ -92,6 +92,47 @@ def test_invalid_block_entries_are_masked(gpu, s):
     _run(w, gpu, s)
 
 
+def test_graph_replays_match_eager(gpu):
+    """A captured call (split plan: decode + merge, caller buffers, nothing
+    allocated) replays bit-identically to the eager call, four times, with
+    the outputs cleared between replays."""
+    w = wl.paged_workload("paged graph", B=3, mtp=4, Hq=32, Hkv=2, max_ctx=900, page=32, seed=951,
+                          lens=[900, 513, 40])
+    q, k, v, bt, cl = _dev(w, gpu)
+    T, Hq, s = w["B"] * w["mtp"], w["Hq"], 5
+    eager_out, eager_lse = smd.paged_decode(q, k, v, bt, cl, w["max_ctx"], w["softmax_scale"], mtp=w["mtp"],
+                                            num_splits=s)
+    out = torch.empty((T, Hq, 512), dtype=torch.bfloat16, device=gpu)
+    lse = torch.empty((T, Hq), dtype=torch.float32, device=gpu)
+    po = torch.empty((T, Hq, s, 512), dtype=torch.float32, device=gpu)
+    pl = torch.empty((T, Hq, s), dtype=torch.float32, device=gpu)
+    stream = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        smd.paged_decode(q, k, v, bt, cl, w["max_ctx"], w["softmax_scale"], mtp=w["mtp"], num_splits=s, out=out,
+                         lse=lse, partial_o=po, partial_lse=pl)
+    torch.cuda.synchronize()
+    for i in range(4):
+        out.fill_(0)
+        lse.fill_(0)
+        torch.cuda.synchronize()
+        print(f"paged graph replay {i}", flush=True)
+        with torch.cuda.stream(stream):
+            g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), eager_out.view(torch.int16))
+        assert torch.equal(lse, eager_lse)
+
+
+def test_many_splits(gpu):
+    """More splits than the heuristic picks (s = 40 over 2500 positions:
+    splits of 64, the last ones empty), merged from bf16 scratch partials."""
+    w = wl.paged_workload("paged many splits", B=2, mtp=4, Hq=16, Hkv=1, max_ctx=2500, page=16, seed=952,
+                          lens=[2500, 1100])
+    _run(w, gpu, 40)
+
+
 def test_repeat_launches_bit_exact(gpu):
     w = wl.paged_workload("paged repeat", B=4, mtp=4, Hq=32, Hkv=2, max_ctx=1500, page=16, seed=932)
     _run(w, gpu, 4, repeats=10)
