@@ -9,24 +9,26 @@
 // all 512 dims.  The split's positions are walked in half-tiles of 16: the K
 // rows and the V rows of a half-tile (16 KiB each) arrive by direct-to-LDS
 // loads, one 1 KiB row per load instruction, into a ring of 4 slots that all
-// four waves share, so three half-tiles are in flight while one is computed
-// and no VGPRs hold rows ("K/V streaming" without a register prefetch).  With
-// page sizes a power of two of at least 16, a half-tile lies in one page: one
-// block-table entry per half-tile, read from an LDS copy of the split's slice
-// of the table.
+// four waves share, so no VGPRs hold rows ("K/V streaming" without a
+// register prefetch): two half-tiles are in flight while one is computed and
+// the slot before it waits for its pair's PV.  With page sizes a power of two
+// of at least 16, a half-tile lies in one page: one block-table entry per
+// half-tile, read from an LDS copy of the split's slice of the table.
 //
 // Per half-tile and wave: QK S^T[16 kv x 16 q] on v_mfma_f32_16x16x32_bf16
-// (Q in VGPRs, K from the ring), the fixed-reference softmax of the other
-// decode kernels (reference max per query row, exact-max redo on overflow),
-// and PV O^T[512 x 16 q] += V^T . P^T on v_mfma_f32_16x16x16_bf16 with V^T
-// from transposed LDS reads (the 16-row kernel's building blocks,
-// ks_core.h / ks8_core.h, on the same swizzled 16-row layout).  The MTP tokens
-// are causal among themselves: a lane masks the positions at or beyond its
-// query row's limit, so the mask is per row, not per tile.
+// (Q in VGPRs, K from the ring) and the fixed-reference softmax of the other
+// decode kernels (reference max per query row, exact-max redo on overflow).
+// Per pair of half-tiles: PV O^T[512 x 16 q] += V^T . P^T on
+// v_mfma_f32_16x16x32_bf16 with V^T from transposed LDS reads (the 16-row
+// kernel's building blocks, ks_core.h / ks8_core.h, on the same swizzled
+// 16-row layout).  The MTP tokens are causal among themselves: a lane masks
+// the positions at or beyond its query row's limit, so the mask is per row,
+// not per tile.
 //
-// One split writes bf16 out and lse; several write FP32 partials that the
-// stage-2 merge reduces (aiter page "[ASM][HIP][MLA v4 nm] Split plan helper
-// and persistent decode kernel", Summary part 1).
+// One split writes bf16 out and lse; several write partials (FP32 when the
+// caller reads them, else bf16 scratch) that the stage-2 merge reduces (aiter
+// page "[ASM][HIP][MLA v4 nm] Split plan helper and persistent decode
+// kernel", Summary part 1).
 #include "ks8_core.h"
 #include "wide_core.h"
 
@@ -38,7 +40,10 @@ constexpr int kPgRows = 16 * kPgWaves;          // query rows per workgroup
 constexpr int kPgHalf = 16;                     // positions per half-tile
 constexpr int kPgSlot = 2 * kPgHalf * 1024;     // K then V rows of a half-tile
 constexpr int kPgSlots = 4;
-constexpr int kPgAhead = kPgSlots - 1;          // half-tiles in flight ahead of the one computed
+// Half-tiles in flight ahead of the one computed: two, so that the slot of
+// half-tile k - 1 stays until its V has gone through the pair's PV at step k
+// (three measured no faster).
+constexpr int kPgAhead = 2;
 
 // Q of this lane's query row as QK B operands: k-step ks holds dims
 // 32 ks + 8 (lane / 16) .. +8.
@@ -56,6 +61,37 @@ __device__ __forceinline__ f32x4 qk_regs(const bf16x8 (&q)[16], const uint8_t SM
     s = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k, q[ks], s, 0, 0, 0);
   }
   return s;
+}
+
+// PV of a pair of half-tiles (V rows at va_buf, vb_buf) on
+// v_mfma_f32_16x16x32_bf16, the rate of which is twice that of the 16-deep
+// shape: the contraction index k = 8 (lane / 16) + e stands for row
+// 4 (lane / 16) + e mod 4 of the first half-tile (e < 4) or of the second
+// (e >= 4), the order in which the two half-tiles' P leave the lane, and the
+// V^T operand is two transposed reads of 4 rows, one per half-tile.
+template <bool P_HILO>
+__device__ __forceinline__ void pv_pair(const uint8_t SMD_LDS *va_buf, const uint8_t SMD_LDS *vb_buf, bf16x4 pa,
+                                        bf16x4 pb, bf16x4 pla, bf16x4 plb, const ks::Lane &L, ks::State &st) {
+  const bf16x8 p = __builtin_shufflevector(pa, pb, 0, 1, 2, 3, 4, 5, 6, 7);
+  bf16x8 pl;
+  if constexpr (P_HILO) pl = __builtin_shufflevector(pla, plb, 0, 1, 2, 3, 4, 5, 6, 7);
+  constexpr int kPre = 4;
+  bf16x8 v[kPre];
+  auto load = [&](int d) {
+    const int off = L.pv[d & 7] + 256 * (d >> 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(va_buf + off));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((bf16x4 SMD_LDS *)(vb_buf + off));
+    v[d % kPre] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+#pragma unroll
+  for (int d = 0; d < kPre; ++d) load(d);
+#pragma unroll
+  for (int d = 0; d < 32; ++d) {
+    const bf16x8 va = v[d % kPre];
+    if (d + kPre < 32) load(d + kPre);
+    st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, p, st.acc[d], 0, 0, 0);
+    if constexpr (P_HILO) st.acc[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pl, st.acc[d], 0, 0, 0);
+  }
 }
 
 // Valid-row bits of half-tile positions [pos0, pos0 + 16) for a query row
@@ -100,9 +136,12 @@ __device__ __forceinline__ void paged_walk(const PagedArgs &a, uint8_t SMD_LDS *
   __syncthreads();  // the ring may still be read by a previous pass
 #pragma unroll
   for (int k = 0; k < kPgAhead; ++k) issue(k);
+  bf16x4 pp = {}, ppl = {};  // P of the even half-tile k - 1, waiting for its pair
   for (int k = 0; k < nh; ++k) {
     wait_vm<8 * (kPgAhead - 1)>();  // this wave's rows of half-tile k have landed
-    barrier_lds();                  // everyone's have, and half-tile k-1 is done: its slot is free
+    // everyone's have, and step k - 1 is done: the pair that ended at step
+    // k - 1 or k - 2 has been through PV, so slot (k + 2) mod 4 is free
+    barrier_lds();
     issue(k + kPgAhead);
     const int pos0 = p0 + kPgHalf * k;
     // a half-tile in a page outside the cache reads zero rows; mask them
@@ -110,7 +149,19 @@ __device__ __forceinline__ void paged_walk(const PagedArgs &a, uint8_t SMD_LDS *
     const f32x4 s = qk_regs(q, slot(k), L);
     bf16x4 p, pl;
     ks::softmax_step<PASS, P_HILO>(s, vb, a.scale_log2, L, st.m_ref, st.l_run, st.overflow, p, pl);
-    if constexpr (PASS != kPassMax) ks8::pv_half<P_HILO>(slot(k) + kPgHalf * 1024, p, pl, L, st);
+    if constexpr (PASS != kPassMax) {
+      const bool odd = k & 1;
+      if (odd || k == nh - 1) {
+        // half-tiles k - 1 and k in one PV; the last half-tile, when it has
+        // no pair, goes with itself and a zero P for the second half
+        const bf16x4 zero = {};
+        pv_pair<P_HILO>(slot(odd ? k - 1 : k) + kPgHalf * 1024, slot(k) + kPgHalf * 1024, odd ? pp : p,
+                        odd ? p : zero, odd ? ppl : pl, odd ? pl : zero, L, st);
+      } else {
+        pp = p;
+        if constexpr (P_HILO) ppl = pl;
+      }
+    }
   }
   wait_vm<0>();  // no load may land in LDS after the walk
 }
