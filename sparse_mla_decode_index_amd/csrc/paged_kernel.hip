@@ -136,32 +136,30 @@ __device__ __forceinline__ void paged_walk(const PagedArgs &a, uint8_t SMD_LDS *
   __syncthreads();  // the ring may still be read by a previous pass
 #pragma unroll
   for (int k = 0; k < kPgAhead; ++k) issue(k);
-  bf16x4 pp = {}, ppl = {};  // P of the even half-tile k - 1, waiting for its pair
-  for (int k = 0; k < nh; ++k) {
+  // one half-tile's QK and softmax (p, pl: its P)
+  auto half = [&](int k, bf16x4 &p, bf16x4 &pl) {
     wait_vm<8 * (kPgAhead - 1)>();  // this wave's rows of half-tile k have landed
-    // everyone's have, and step k - 1 is done: the pair that ended at step
-    // k - 1 or k - 2 has been through PV, so slot (k + 2) mod 4 is free
-    barrier_lds();
+    barrier_lds();                  // everyone's have; the slot of k + 2 has been through its pair's PV
     issue(k + kPgAhead);
     const int pos0 = p0 + kPgHalf * k;
-    // a half-tile in a page outside the cache reads zero rows; mask them
     const uint32_t vb = bt[(pos0 >> a.page_shift) - pg0] >= 0 ? limit_bits(pos0, lim) : 0u;
     const f32x4 s = qk_regs(q, slot(k), L);
-    bf16x4 p, pl;
     ks::softmax_step<PASS, P_HILO>(s, vb, a.scale_log2, L, st.m_ref, st.l_run, st.overflow, p, pl);
-    if constexpr (PASS != kPassMax) {
-      const bool odd = k & 1;
-      if (odd || k == nh - 1) {
-        // half-tiles k - 1 and k in one PV; the last half-tile, when it has
-        // no pair, goes with itself and a zero P for the second half
-        const bf16x4 zero = {};
-        pv_pair<P_HILO>(slot(odd ? k - 1 : k) + kPgHalf * 1024, slot(k) + kPgHalf * 1024, odd ? pp : p,
-                        odd ? p : zero, odd ? ppl : pl, odd ? pl : zero, L, st);
-      } else {
-        pp = p;
-        if constexpr (P_HILO) ppl = pl;
-      }
-    }
+  };
+  const int npairs = nh >> 1;
+  for (int j = 0; j < npairs; ++j) {
+    bf16x4 pa, pla, pb, plb;
+    half(2 * j, pa, pla);
+    half(2 * j + 1, pb, plb);
+    if constexpr (PASS != kPassMax)
+      pv_pair<P_HILO>(slot(2 * j) + kPgHalf * 1024, slot(2 * j + 1) + kPgHalf * 1024, pa, pb, pla, plb, L, st);
+  }
+  if (nh & 1) {  // the last half-tile has no pair: it goes with itself and a zero P
+    bf16x4 pa, pla;
+    half(nh - 1, pa, pla);
+    const bf16x4 zero = {};
+    if constexpr (PASS != kPassMax)
+      pv_pair<P_HILO>(slot(nh - 1) + kPgHalf * 1024, slot(nh - 1) + kPgHalf * 1024, pa, zero, pla, zero, L, st);
   }
   wait_vm<0>();  // no load may land in LDS after the walk
 }
