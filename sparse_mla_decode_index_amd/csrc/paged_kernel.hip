@@ -142,6 +142,7 @@ __device__ __forceinline__ void paged_walk(const PagedArgs &a, uint8_t SMD_LDS *
     barrier_lds();                  // everyone's have; the slot of k + 2 has been through its pair's PV
     issue(k + kPgAhead);
     const int pos0 = p0 + kPgHalf * k;
+    // a half-tile in a page outside the cache reads zero rows; mask them
     const uint32_t vb = bt[(pos0 >> a.page_shift) - pg0] >= 0 ? limit_bits(pos0, lim) : 0u;
     const f32x4 s = qk_regs(q, slot(k), L);
     ks::softmax_step<PASS, P_HILO>(s, vb, a.scale_log2, L, st.m_ref, st.l_run, st.overflow, p, pl);
