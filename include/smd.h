@@ -448,8 +448,8 @@ int smd_merge_partials(const float *partial_o, const float *partial_lse, int32_t
  * decode kernel" (Summary, part 2): one launch with a fixed grid; every
  * workgroup computes the split plan inside the kernel from the live
  * kv_indptr; rows held by one partition are written as bf16 directly, split
- * rows write FP32 partials into the workspace and the workgroup that arrives
- * last merges them; sequences with no index are left unwritten.  (Here the
+ * rows write partials into the workspace (o in bf16, lse in fp32: the merged
+ * result is bf16) and the workgroup that arrives last merges them; sequences with no index are left unwritten.  (Here the
  * piece that finds all the others arrived merges without writing a partial
  * of its own when the row group has 128 rows; see SMD_MERGE_*.)  Because the
  * plan is read from device memory on every launch, a captured graph stays
@@ -474,7 +474,8 @@ int32_t smd_persistent_default_partitions(int32_t num_heads, int32_t q_per_seq, 
 
 /* Bytes of workspace the persistent decode needs for these shapes: the plan
  * (16 bytes per partition), arrival counters (4 bytes per partition and
- * 16-row group) and 2 * num_partitions partial slots of M * 513 fp32.
+ * 16-row group) and 2 * num_partitions partial slots of M * 1028 bytes (o of
+ * M rows as 512 bf16, then the M lse as fp32).
  * Returns 0 for unsupported shapes (smd_last_error says why).  Host only. */
 size_t smd_persistent_workspace_bytes(int32_t num_heads, int32_t q_per_seq, int32_t num_partitions);
 

@@ -100,6 +100,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
+// Two packed bf16 (pack_bf16x2 order) back to fp32.
+__device__ __forceinline__ float bf16_lo(uint32_t v) { return __uint_as_float(v << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v & 0xffff0000u); }
+
 // Four fp32 values x scale -> four bf16 (round to nearest even), 8 bytes.
 __device__ __forceinline__ u32x2 pack_bf16x4(f32x4 v, float scale) {
   u32x2 r;

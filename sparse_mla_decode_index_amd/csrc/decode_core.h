@@ -477,12 +477,14 @@ __device__ __forceinline__ void write_direct(const WaveState<ND> &w, float l_tot
   if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 
-// FP32 partial of one query row (no sink, partial_scale).  dst as in write_direct.
+// Partial of one query row (no sink, partial_scale): o in bf16, the lse in
+// fp32.  dst as in write_direct.
 template <int ND>
-__device__ __forceinline__ void write_partial(const WaveState<ND> &w, float l_tot, float *dst, float *lse_dst) {
+__device__ __forceinline__ void write_partial_bf16(const WaveState<ND> &w, float l_tot, uint16_t *dst,
+                                                   float *lse_dst) {
   const OutScale sc = partial_scale(w.m_ref, l_tot);
 #pragma unroll
-  for (int d = 0; d < ND; ++d) *(f32x4 *)(dst + 16 * d) = w.acc[d] * sc.inv;
+  for (int d = 0; d < ND; ++d) *(u32x2 *)(dst + 16 * d) = pack_bf16x4(w.acc[d], sc.inv);
   if (lse_dst != nullptr) *lse_dst = sc.lse;
 }
 

@@ -18,7 +18,8 @@
 // p and attends row group g of each over the piece of its index list that p
 // owns.  A sequence inside one partition is
 // written directly.  A sequence spread over partitions fp..lp is split: each
-// piece writes an FP32 partial (o = O/l, lse = m + ln l) to its slot, releases
+// piece writes a partial (o = O/l in bf16, lse = m + ln l in fp32; the merged
+// result is bf16, so o needs no more) to its slot, releases
 // it with an agent-scope fence and bumps the arrival counter of (g, fp); the
 // workgroup that sees the count of the other pieces (the non-empty partitions
 // of the span, minus one) merges the pieces in partition order
@@ -37,7 +38,7 @@ PersistLayout persist_layout(int64_t M, int64_t P) {
   l.plan_off = 0;
   l.ctr_off = up((size_t)P * 4 * sizeof(int32_t));
   l.slot_off = l.ctr_off + up((size_t)(M / 16) * (size_t)P * sizeof(uint32_t));
-  l.total = l.slot_off + (size_t)2 * (size_t)P * (size_t)M * 513 * sizeof(float);
+  l.total = l.slot_off + (size_t)2 * (size_t)P * (size_t)M * kSlotRowFloats * sizeof(float);
   return l;
 }
 
@@ -109,7 +110,7 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
   const DecodeArgs &a = pa.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int n = lp - fp + 1;  // partitions in the span (empty ones hold nothing)
-  const size_t slot_floats = (size_t)a.M * 513;
+  const size_t slot_floats = (size_t)a.M * kSlotRowFloats;
   auto slot_base = [&](int q) { return pa.slots + (size_t)(q == 0 ? first_slot : 2 * (fp + q)) * slot_floats; };
   for (int r0 = wave; r0 < rows; r0 += NW * RU) {
     int m[RU];
@@ -130,7 +131,7 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
     for (int q0 = 0; q0 < n; q0 += 64) {
       const int q = q0 + lane;
       const bool held = q < n && !part_empty(fp + q, total, pa.P);
-      const float *ls = slot_base(held ? q : 0) + (size_t)a.M * kDim;
+      const float *ls = slot_base(held ? q : 0) + (size_t)a.M * kSlotORowFloats;
       float l[RU];
 #pragma unroll
       for (int u = 0; u < RU; ++u) l[u] = ls[m[u]];
@@ -151,7 +152,7 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
     for (int q0 = 0; q0 < n; q0 += 64) {
       const int ql = q0 + lane;
       const bool held = ql < n && !part_empty(fp + ql, total, pa.P);
-      const float *ls = slot_base(held ? ql : 0) + (size_t)a.M * kDim;
+      const float *ls = slot_base(held ? ql : 0) + (size_t)a.M * kSlotORowFloats;
       float wl[RU];
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
@@ -170,15 +171,12 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
           kk[i] = has[i] ? __builtin_ctzll(mask) : kk[0];
           if (has[i]) mask &= mask - 1;
         }
-        f32x4 v[KP][RU][2];
+        u32x4 v[KP][RU];  // 8 bf16 dims per lane
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-          const float *sp = slot_base(q0 + kk[i]) + lane * 8;
+          const uint16_t *sp = (const uint16_t *)slot_base(q0 + kk[i]) + lane * 8;
 #pragma unroll
-          for (int u = 0; u < RU; ++u) {
-            v[i][u][0] = *(const f32x4 *)(sp + (size_t)m[u] * kDim);
-            v[i][u][1] = *(const f32x4 *)(sp + (size_t)m[u] * kDim + 4);
-          }
+          for (int u = 0; u < RU; ++u) v[i][u] = *(const u32x4 *)(sp + (size_t)m[u] * kDim);
         }
 #pragma unroll
         for (int u = 0; u < RU; ++u) {
@@ -188,8 +186,8 @@ __device__ __forceinline__ void merge_pieces(const PersistArgs &pa, int b, int g
             z[u] += wq;
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-              o[u][e] = __builtin_fmaf(wq, v[i][u][0][e], o[u][e]);
-              o[u][4 + e] = __builtin_fmaf(wq, v[i][u][1][e], o[u][4 + e]);
+              o[u][2 * e] = __builtin_fmaf(wq, bf16_lo(v[i][u][e]), o[u][2 * e]);
+              o[u][2 * e + 1] = __builtin_fmaf(wq, bf16_hi(v[i][u][e]), o[u][2 * e + 1]);
             }
           }
         }
@@ -227,11 +225,11 @@ __device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b
   static_assert(ROWS % NW == 0 && RPW % RU == 0, "rows per wave");
   const DecodeArgs &a = pa.d;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const size_t slot_floats = (size_t)a.M * 513;
+  const size_t slot_floats = (size_t)a.M * kSlotRowFloats;
   auto slot_base = [&](int q) { return pa.slots + (size_t)(q == 0 ? first_slot : 2 * (fp + q)) * slot_floats; };
   const bool held = lane < n && !part_empty(fp + lane, total, pa.P);
   const uint64_t held_mask = __ballot(held);  // wave-uniform
-  const float *ls = slot_base(held ? lane : 0) + (size_t)a.M * kDim;
+  const float *ls = slot_base(held ? lane : 0) + (size_t)a.M * kSlotORowFloats;
   float l[RPW];
 #pragma unroll
   for (int i = 0; i < RPW; ++i) l[i] = ls[g * ROWS + wave + NW * i];
@@ -264,15 +262,12 @@ __device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b
         kk[i] = has[i] ? __builtin_ctzll(mask) : kk[0];
         if (has[i]) mask &= mask - 1;
       }
-      f32x4 v[KP][RU][2];
+      u32x4 v[KP][RU];  // 8 bf16 dims per lane
 #pragma unroll
       for (int i = 0; i < KP; ++i) {
-        const float *sp = slot_base(kk[i]) + lane * 8;
+        const uint16_t *sp = (const uint16_t *)slot_base(kk[i]) + lane * 8;
 #pragma unroll
-        for (int u = 0; u < RU; ++u) {
-          v[i][u][0] = *(const f32x4 *)(sp + (size_t)m[u] * kDim);
-          v[i][u][1] = *(const f32x4 *)(sp + (size_t)m[u] * kDim + 4);
-        }
+        for (int u = 0; u < RU; ++u) v[i][u] = *(const u32x4 *)(sp + (size_t)m[u] * kDim);
       }
 #pragma unroll
       for (int u = 0; u < RU; ++u) {
@@ -282,8 +277,8 @@ __device__ __forceinline__ void merge_pieces_narrow(const PersistArgs &pa, int b
           z[u] += wq;
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            o[u][e] = __builtin_fmaf(wq, v[i][u][0][e], o[u][e]);
-            o[u][4 + e] = __builtin_fmaf(wq, v[i][u][1][e], o[u][4 + e]);
+            o[u][2 * e] = __builtin_fmaf(wq, bf16_lo(v[i][u][e]), o[u][2 * e]);
+            o[u][2 * e + 1] = __builtin_fmaf(wq, bf16_hi(v[i][u][e]), o[u][2 * e + 1]);
           }
         }
       }
@@ -405,7 +400,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   const bool lse_lane = grp == 0 && ds == 0;
   const int m = g * ROWS + rb * 16 + j;  // this lane's query row within a sequence
   const int head = m % a.H;
-  const size_t slot_floats = (size_t)a.M * 513;
+  const size_t slot_floats = (size_t)a.M * kSlotRowFloats;
 
   for (int b = b_first; b <= b_last; ++b) {
     const int k0 = ptr[b];
@@ -464,11 +459,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int qp = fp + k + (fp + k >= p ? 1 : 0);
         const int sl = qp == fp ? 2 * fp + (start == t0_fp ? 0 : 1) : 2 * qp;
         const float *base = pa.slots + (size_t)sl * slot_floats;
-        return PiecePtrs{base + (size_t)mq0 * kDim, base + (size_t)a.M * kDim + mq0};
+        return PiecePtrs{(const uint16_t *)base + (size_t)mq0 * kDim, base + (size_t)a.M * kSlotORowFloats + mq0};
       };
       const float sink_ln = a.sink ? a.sink[hq] : -INFINITY;
       float scale, lse_v;
-      bool f32 = false;
       void *dst = a.out + qbase * kDim;
       float *lse_dst = (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr;
       if (fp == lp) {
@@ -496,15 +490,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
           const OutScale sc = partial_scale(w.m_ref, l_tot);
           scale = sc.inv;
           lse_v = sc.lse;
-          f32 = true;
-          dst = sb + (size_t)mq0 * kDim;
-          lse_dst = lse_lane ? sb + (size_t)a.M * kDim + mq0 + (lane & 31) : nullptr;
+          dst = (uint16_t *)sb + (size_t)mq0 * kDim;
+          lse_dst = lse_lane ? sb + (size_t)a.M * kSlotORowFloats + mq0 + (lane & 31) : nullptr;
         }
       }
       if (merged)
         store_rows_wide<true>(w, scale, false, dst, kDim, stage, part, lp - fp, p - fp, tbl);
       else
-        store_rows_wide<false>(w, scale, f32, dst, kDim, stage);
+        store_rows_wide<false>(w, scale, false, dst, kDim, stage);  // bf16 out or a bf16 partial
       if (lse_dst != nullptr) *lse_dst = lse_v;
     } else {
       const int64_t qrow = (int64_t)(b * a.qps + m / a.H) * a.H + head;
@@ -518,7 +511,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         write_direct(w, l_tot, a.sink ? a.sink[head] : -INFINITY, a.out + qrow * kDim + dcol,
                      (a.lse != nullptr && lse_lane) ? a.lse + qrow : nullptr);
       else
-        write_partial(w, l_tot, sb + (size_t)m * kDim + dcol, lse_lane ? sb + (size_t)a.M * kDim + m : nullptr);
+        write_partial_bf16(w, l_tot, (uint16_t *)sb + (size_t)m * kDim + dcol,
+                           lse_lane ? sb + (size_t)a.M * kSlotORowFloats + m : nullptr);
     }
     if (fp != lp && !merged) {
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");  // release this piece (other XCDs read it)

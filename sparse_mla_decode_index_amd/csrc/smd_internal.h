@@ -106,7 +106,7 @@ struct PersistArgs {
   int32_t P;                  // partitions
   int32_t *plan;              // [P][4]: t0, t1, first and last sequence
   uint32_t *counters;         // [M / 16][P] arrival counters (row group g, first partition)
-  float *slots;               // [2P][M * 513]: per slot o [M][512] then lse [M]
+  float *slots;               // [2P][M * kSlotRowFloats]: per slot o [M][512] bf16, then lse [M] fp32
   bool reg_merge;             // SMD_MERGE_AUTO: the last piece may merge from its registers
 };
 
@@ -115,6 +115,12 @@ struct PersistLayout {
   size_t plan_off, ctr_off, slot_off, total;
 };
 PersistLayout persist_layout(int64_t M, int64_t P);
+
+// A persistent slot per query row: its o as 512 bf16 (256 floats' room) in
+// the o region, its lse as one fp32 in the lse region that follows the M rows.
+// The partials only feed the merge, whose result is bf16.
+constexpr int kSlotORowFloats = 256;
+constexpr int kSlotRowFloats = kSlotORowFloats + 1;
 
 // rb in {1, 2, 4, 8} query-row blocks of 16 per workgroup; a.d.G = M / (16 rb).
 hipError_t launch_persistent(const PersistArgs &a, int rb, bool fp8, hipStream_t stream);

@@ -1161,7 +1161,8 @@ __device__ __forceinline__ f32x4 wide_quad(const f32x16 &v, int b) {
 // kRegMergeMax of them).
 constexpr int kRegMergeMax = 8;
 struct PiecePtrs {
-  const float *o, *lse;
+  const uint16_t *o;  // bf16 rows, kDim apart
+  const float *lse;
 };
 struct NoPieces {
   __device__ PiecePtrs operator()(int) const { return PiecePtrs{nullptr, nullptr}; }
@@ -1180,11 +1181,12 @@ struct NoPieces {
 //           tbl[32 (kRegMergeMax + 1) + r].  Per element, in span order from
 //           zero with one fused multiply-add per piece, then times 1 / Z: the
 //           operations of merge_pieces_narrow, so a row group merged here and
-//           one merged from the workspace hold the same bits.
+//           one merged from the workspace hold the same bits (this piece's
+//           partial is rounded to bf16 first, as its slot would hold it).
 // dst points at dim 0 of the wave's first row, rows row_stride elements
 // apart (uint16_t for bf16, float for FP32); part(k).o points at dim 0 of the
-// wave's first row in the k-th other piece's FP32 partial (rows kDim floats
-// apart).  Four passes of 128 dims: the wave's part goes to the stage in fp32
+// wave's first row in the k-th other piece's bf16 partial (rows kDim
+// elements apart).  Four passes of 128 dims: the wave's part goes to the stage in fp32
 // in the accumulator layout (lane (q, u) holds row q); a merge then works
 // row-wise (lane (q, u): rows 2k + u, dims 4q..4q+3 of the pass), loading the
 // other pieces' rows in that layout, and writes its sums back to the stage;
@@ -1202,14 +1204,14 @@ template <bool MERGE, class Part = NoPieces>
 __device__ __forceinline__ void store_rows_wide(const WideState &w, float scale, bool f32, void *dst,
                                                 int64_t row_stride, uint8_t SMD_LDS *stage, Part part = Part(),
                                                 int n = 0, int own_k = 0, const float SMD_LDS *tbl = nullptr) {
-  auto piece_loads = [&](int pass, int j, f32x4 (&v)[16]) {
+  auto piece_loads = [&](int pass, int j, u32x2 (&v)[16]) {
     const int lane = opaque_lane();
-    const uint32_t poff = (uint32_t)((lane >> 5) * kDim + 128 * pass + 4 * (lane & 31)) * 4;
+    const uint32_t poff = (uint32_t)((lane >> 5) * kDim + 128 * pass + 4 * (lane & 31)) * 2;
     const char *src = (const char *)part(j).o;
 #pragma unroll
-    for (int k = 0; k < 16; ++k) v[k] = *(const f32x4 *)(src + (size_t)(2 * k * kDim * 4) + poff);
+    for (int k = 0; k < 16; ++k) v[k] = *(const u32x2 *)(src + (size_t)(2 * k * kDim * 2) + poff);
   };
-  f32x4 pre[16];  // MERGE: the first other piece's rows of the next pass
+  u32x2 pre[16];  // MERGE: the first other piece's rows of the next pass
   if constexpr (MERGE) piece_loads(0, 0, pre);
 #pragma unroll
   for (int pass = 0; pass < 4; ++pass) {
@@ -1223,20 +1225,25 @@ __device__ __forceinline__ void store_rows_wide(const WideState &w, float scale,
       f32x4 o[16];
 #pragma unroll
       for (int k = 0; k < 16; ++k) o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      auto add = [&](const f32x4 (&v)[16], const float SMD_LDS *wt) {  // o += wt[row] * v, row 2k + u
+      auto add = [&](const u32x2 (&v)[16], const float SMD_LDS *wt) {  // o += wt[row] * v, row 2k + u
         float c[16];
 #pragma unroll
         for (int k = 0; k < 16; ++k) c[k] = wt[2 * k + u];
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[k][e] = __builtin_fmaf(c[k], v[k][e], o[k][e]);
+          o[k][0] = __builtin_fmaf(c[k], bf16_lo(v[k][0]), o[k][0]);
+          o[k][1] = __builtin_fmaf(c[k], bf16_hi(v[k][0]), o[k][1]);
+          o[k][2] = __builtin_fmaf(c[k], bf16_lo(v[k][1]), o[k][2]);
+          o[k][3] = __builtin_fmaf(c[k], bf16_hi(v[k][1]), o[k][3]);
         }
       };
-      auto add_own = [&]() {
-        f32x4 t[16];
+      auto add_own = [&]() {  // this piece's partial, rounded to bf16 as its slot would hold it
+        u32x2 t[16];
 #pragma unroll
-        for (int k = 0; k < 16; ++k) t[k] = *(const f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q));
+        for (int k = 0; k < 16; ++k) {
+          const f32x4 x = *(const f32x4 SMD_LDS *)(stage + stage_off(2 * k + u, q));
+          t[k] = u32x2{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3])};
+        }
         add(t, tbl + kRegMergeMax * 32);
       };
       if (own_k == 0) add_own();
@@ -1244,7 +1251,7 @@ __device__ __forceinline__ void store_rows_wide(const WideState &w, float scale,
 #pragma unroll 1
       for (int j = 1; j < n; ++j) {
         if (j == own_k) add_own();
-        f32x4 v[16];
+        u32x2 v[16];
         piece_loads(pass, j, v);
         add(v, tbl + j * 32);
       }

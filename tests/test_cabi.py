@@ -213,9 +213,10 @@ def _up256(x):
 @pytest.mark.parametrize("H,qps,P", [(128, 4, 32), (16, 1, 256), (64, 2, 7), (32, 8, 1), (128, 1, 16384)])
 def test_persistent_workspace_bytes(H, qps, P):
     # plan 16 B per partition, counters 4 B per (16-row group, partition), then
-    # 2P slots of M x 513 fp32; each region starts 256-byte aligned
+    # 2P slots of M rows x (512 bf16 + one fp32 lse); each region starts
+    # 256-byte aligned
     M = H * qps
-    want = _up256(16 * P) + _up256(4 * (M // 16) * P) + 2 * P * M * 513 * 4
+    want = _up256(16 * P) + _up256(4 * (M // 16) * P) + 2 * P * M * (512 * 2 + 4)
     assert smd.persistent_workspace_bytes(H, qps, P) == want
 
 
