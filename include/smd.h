@@ -58,7 +58,7 @@ enum {
 };
 
 /* Largest split count of the split-KV entry points. */
-#define SMD_MAX_SPLITS 128
+#define SMD_MAX_SPLITS 256
 /* Largest number of partials one merge (smd_merge_partials) combines, e.g.
  * the splits of several callers' partial decodes of one index list. */
 #define SMD_MAX_MERGE_SPLITS 1024

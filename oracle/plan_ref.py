@@ -21,7 +21,7 @@ from __future__ import annotations
 from dataclasses import dataclass
 
 SPLIT_ALIGN = 64
-MAX_SPLITS = 128
+MAX_SPLITS = 256
 
 
 def _cdiv(a: int, b: int) -> int:

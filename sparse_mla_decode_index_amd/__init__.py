@@ -19,7 +19,7 @@ import torch
 NOPE = 448
 ROPE = 64
 DIM = 512
-MAX_SPLITS = 128
+MAX_SPLITS = 256
 MAX_MERGE_SPLITS = 1024
 NOALLOC_SCRATCH_BYTES = 32 << 20
 SPLIT_ALIGN = 64

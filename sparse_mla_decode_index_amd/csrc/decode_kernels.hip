@@ -136,19 +136,27 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
 // reading CH of them (their lse and o) per round trip, so a plan of up to
 // CH * WPR splits costs one round trip.  The row's waves then combine
 // their states through LDS and the row's first wave writes the result.
+// A workgroup has max(4, WPR) waves, so 4 / WPR rows or one.
 // BF16: the partials' o values are bf16 (in the FP32 buffer's first half),
 // the form of partials that only feed this merge.
+template <int WPR>
+constexpr int merge_waves() {
+  return WPR > 4 ? WPR : 4;
+}
+
 template <int WPR, int CH, bool BF16>
-__global__ __launch_bounds__(256) void merge_kernel(const float *__restrict__ po,
-                                                    const float *__restrict__ plse, int rows, int H,
-                                                    int S, const float *__restrict__ sink,
-                                                    uint16_t *__restrict__ out, float *__restrict__ lse) {
-  __shared__ float xo[4][8][64];  // [wave][dim][lane]: bank-conflict-free
-  __shared__ float xs[4][2];      // [wave] {max, sum}
+__global__ __launch_bounds__(64 * merge_waves<WPR>()) void merge_kernel(const float *__restrict__ po,
+                                                                        const float *__restrict__ plse, int rows,
+                                                                        int H, int S, const float *__restrict__ sink,
+                                                                        uint16_t *__restrict__ out,
+                                                                        float *__restrict__ lse) {
+  constexpr int NW = merge_waves<WPR>();
+  __shared__ float xo[NW][8][64];  // [wave][dim][lane]: bank-conflict-free
+  __shared__ float xs[NW][2];      // [wave] {max, sum}
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
   const int w = wave % WPR;
-  const int row = blockIdx.x * (4 / WPR) + wave / WPR;
+  const int row = blockIdx.x * (NW / WPR) + wave / WPR;
   const bool live = row < rows;
   float mx = -INFINITY;  // running max of the lse terms (natural log)
   float z = 0.f;         // sum of e^(term - mx)
@@ -301,10 +309,11 @@ template <int WPR, int CH, bool BF16>
 static hipError_t launch_merge_t(const float *part_o, const float *part_lse, int32_t rows, int32_t H,
                                  int32_t S, const float *sink, uint16_t *out, float *lse,
                                  hipStream_t stream) {
-  const int rpb = 4 / WPR;
+  constexpr int NW = merge_waves<WPR>();
+  const int rpb = NW / WPR;
   const dim3 grid((unsigned)((rows + rpb - 1) / rpb));
-  hipLaunchKernelGGL((merge_kernel<WPR, CH, BF16>), grid, dim3(256), 0, stream, part_o, part_lse, rows, H, S,
-                     sink, out, lse);
+  hipLaunchKernelGGL((merge_kernel<WPR, CH, BF16>), grid, dim3(64 * NW), 0, stream, part_o, part_lse, rows, H,
+                     S, sink, out, lse);
   return hipGetLastError();
 }
 
@@ -315,7 +324,9 @@ static hipError_t launch_merge_f(const float *part_o, const float *part_lse, int
   if (S <= 4) return launch_merge_t<1, 4, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
   if (S <= 8) return launch_merge_t<2, 4, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
   if (S <= 16) return launch_merge_t<4, 4, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
-  return launch_merge_t<4, 8, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  if (S <= 64) return launch_merge_t<4, 8, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
+  // long plans: 16 waves per row, so up to 128 splits cost one round trip
+  return launch_merge_t<16, 8, BF16>(part_o, part_lse, rows, H, S, sink, out, lse, stream);
 }
 
 hipError_t launch_merge(const float *part_o, const float *part_lse, int32_t rows, int32_t H,

@@ -46,7 +46,7 @@ static const smd_plan_model kDefaultModel = {
     /*wide_tile_ps=*/1774000,
     /*wide_tile_fp8_ps=*/2192000,
     /*wide_tile_load_ps=*/536000,
-    /*wide_cap=*/0,
+    /*wide_cap=*/256,
     /*reserved=*/0,
 };
 

@@ -57,7 +57,7 @@ def _model_pair(rng):
              long_kv=int(rng.integers(1, 20000)), wide_rows=int(rng.choice([0, 64, 128, 256])),
              wide_tile=int(rng.choice([16, 32, 64])), wide_fixed_ps=int(rng.integers(0, 30_000_000)),
              wide_tile_ps=int(rng.integers(1, 4_000_000)), wide_tile_fp8_ps=int(rng.integers(1, 4_000_000)),
-             wide_tile_load_ps=int(rng.integers(0, 2_000_000)), wide_cap=int(rng.choice([0, 1, 16, 64, 128])))
+             wide_tile_load_ps=int(rng.integers(0, 2_000_000)), wide_cap=int(rng.choice([0, 1, 16, 64, 128, 256])))
     c = smd.PlanModel()
     for k, x in v.items():
         setattr(c, k, x)
@@ -94,7 +94,7 @@ def test_default_planner_properties():
             for K in [64, 384, 2176, 6528, 32128, 65664]:
                 s, wide = smd.plan_decode(rows, H, K)
                 assert s == smd.plan_num_kv_splits(rows, H, K)
-                assert 1 <= s <= 128
+                assert 1 <= s <= 256
                 assert s <= -(-K // 64)    # never more splits than 64-row chunks
     # depends only on its arguments
     assert smd.plan_num_kv_splits(8, 64, 2176) == smd.plan_num_kv_splits(8, 64, 2176)
@@ -144,7 +144,7 @@ def _decode(pool=None, **kw):
     (dict(qps=9), -2, "q_per_seq"),
     (dict(T=3, qps=2), -1, "multiple"),
     (dict(s=0), -1, "num_splits"),
-    (dict(s=129), -1, "num_splits"),
+    (dict(s=257), -1, "num_splits"),
     (dict(T=-1), -1, "negative"),
     (dict(topk=-5), -1, "negative"),
     (dict(s=2), -3, "partial_o"),
@@ -539,7 +539,7 @@ def test_decode_kernel_choice_follows_the_cost_model():
         qps = int(rng.choice([1, 2, 4]))
         K = int(rng.integers(1, 70000))
         kvd = int(rng.integers(0, 2))
-        s = int(rng.integers(1, 129))
+        s = int(rng.integers(1, 257))
         cw = plan_ref.wide_split_cost(s, rows, H, qps, K, kvd, 256, pm)
         narrow_cap = pm.short_cap if K < pm.long_kv else pm.long_cap
         wide = cw is not None and (s > narrow_cap or cw < plan_ref.split_cost(s, rows, H, qps, K, 256, pm))
@@ -580,7 +580,7 @@ def _paged(**kw):
     (dict(page=24), -2, "page_size"),             # not a power of two
     (dict(page=8), -2, "page_size"),              # below 16
     (dict(s=0), -1, "num_splits"),
-    (dict(s=129), -1, "num_splits"),
+    (dict(s=257), -1, "num_splits"),
     (dict(bts=10), -1, "block_tables_stride"),    # 1000 positions need 63 pages
     (dict(max_ctx=1 << 20, bts=1 << 16), -1, "splits"),  # one split spanning 65536 pages
     (dict(scale=float("nan")), -1, "softmax_scale"),

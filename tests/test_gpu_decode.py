@@ -95,10 +95,11 @@ def test_mtp_shared_rows(gpu, qps):
 
 
 @pytest.mark.parametrize("S,topk,sink", [(6, 200, True), (13, 700, True), (13, 130, False), (32, 2100, True),
-                                          (32, 130, False)])
+                                          (32, 130, False), (100, 4000, True), (300, 2000, False)])
 def test_merge_kernel_alone(gpu, S, topk, sink):
-    """smd_merge_partials on oracle-computed partials: one to four waves per
-    row, including splits that are all empty and a token with no valid index."""
+    """smd_merge_partials on oracle-computed partials: one to sixteen waves
+    per row, including splits that are all empty and a token with no valid
+    index."""
     w = wl.dense_workload("merge", T=3, H=32, kv_dtype="bf16", pool_rows=4096, topk=topk, invalid=2, seed=61 + S)
     w.arrays["indices"][1, :] = -1
     po, pl = ref.sparse_mla_decode_partials(w.arrays["q_nope"], w.arrays["q_rope"], oracle_pool(w),

@@ -65,12 +65,12 @@ def test_wide_fp8_ragged_tail(gpu, H, qps, s):
     _run(w, gpu, s)
 
 
-@pytest.mark.parametrize("kv_dtype,s", [("bf16", 61), ("bf16", 128), ("fp8", 100)])
+@pytest.mark.parametrize("kv_dtype,s", [("bf16", 61), ("bf16", 128), ("fp8", 100), ("bf16", 256), ("fp8", 200)])
 def test_wide_beyond_32_splits(gpu, kv_dtype, s):
-    """The wide family's split counts above the narrow cap: 8250 positions
-    cut into splits of 192 (s = 61: 43 non-empty, 18 empty) and of 128
-    (s = 128: 65 non-empty, 63 empty; s = 100: 65 and 35); bf16 out through
-    the merge of up to 128 partials."""
+    """The wide family's split counts above 32: 8250 positions cut into
+    splits of 192 (s = 61: 43 non-empty, 18 empty), of 128 (s = 128: 65
+    non-empty, 63 empty; s = 100: 65 and 35) and of 64 (s = 256: 129 and 127;
+    s = 200: 129 and 71); bf16 out through the merge of up to 256 partials."""
     w = wl.dense_workload("wide many splits", T=2, H=128, kv_dtype=kv_dtype, pool_rows=16384, topk=8200, swa=50,
                           invalid=40, seed=671 + s)
     _run(w, gpu, s)

@@ -214,12 +214,12 @@ def _fitted_model(wide: bool = True):
                         part_ps=287, rows_per_wg=16, waves_per_wg=8, wg_per_cu=1, short_cap=128,
                         long_cap=128, long_kv=4096, wide_rows=128 if wide else 0, wide_tile=32,
                         wide_fixed_ps=13648000, wide_tile_ps=1774000, wide_tile_fp8_ps=2192000,
-                        wide_tile_load_ps=536000, wide_cap=0)
+                        wide_tile_load_ps=536000, wide_cap=256)
 
 
 def test_planner_wide_cap_worked_example():
-    """4 index rows x 128 heads x 65664 bf16 indices: from long_kv on, both
-    families take up to long_cap = 128 splits (wide_cap 0: the same).
+    """4 index rows x 128 heads x 65664 bf16 indices: from long_kv on, narrow
+    takes up to long_cap = 128 splits and wide up to wide_cap = 256.
       s=61: 4*61 = 244 workgroups, one round; ceil(65664/61) = 1077 -> chunk
             1088, 34 tiles at 1774000 + 536000*244//256 = 2284875:
             13648000 + 34*2284875 + 4065000 + 287*4*128*61          = 104362334
@@ -229,16 +229,19 @@ def test_planner_wide_cap_worked_example():
             13648000 + 34*2293250 + 4065000 + 287*4*128*62          = 104794028
       s=64: 256 workgroups, 34 tiles at 2310000                      = 105657416
       s=65: 260 workgroups take two rounds                           = 188752360
+      s=128: 512 workgroups in two rounds, ceil(65664/128) = 513 -> chunk
+            576, 18 tiles at 2310000:
+            2*(13648000 + 18*2310000) + 4065000 + 287*4*128*128     = 133329832
     so the plan is 61 splits on the wide kernel.  With both caps at 32
     (long_cap = 32) it is 32 splits on the wide kernel (157187208), below the
     narrow family's best, s = 8 (177534552); with the narrow family at 32 and
     wide_cap = 128 it is 61 wide splits again."""
     m = _fitted_model()
-    want = {61: 104362334, 60: 108483640, 62: 104794028, 64: 105657416, 65: 188752360}
+    want = {61: 104362334, 60: 108483640, 62: 104794028, 64: 105657416, 65: 188752360, 128: 133329832}
     for s, c in want.items():
         assert pr.wide_split_cost(s, 4, 128, 1, 65664, 0, 256, m) == c, s
     assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m) == (61, True)
-    m32 = dataclasses.replace(m, long_cap=32)
+    m32 = dataclasses.replace(m, long_cap=32, wide_cap=0)
     assert pr.wide_split_cost(32, 4, 128, 1, 65664, 0, 256, m32) == 157187208
     assert pr.split_cost(8, 4, 128, 1, 65664, 256, m32) == 177534552
     assert pr.plan_decode(4, 128, 1, 65664, 0, 256, m32) == (32, True)
@@ -308,7 +311,12 @@ def test_planner_cost_worked_example_wide_family():
     two splits on the wide kernel.  One row x 128 heads x 65664 bf16 indices,
     s=32: 32 workgroups of 66 tiles at 1774000 + 536000*32//256 = 1841000:
     13648000 + 66*1841000 + 4065000 + 287*128*32 = 140394552, far above the
-    narrow 55275522 of s = 31, which stays the plan."""
+    narrow 55275522 of s = 31.  Beyond 128 splits (wide_cap = 256) the wide
+    family wins there: s=206, 206 workgroups in one round at 1774000 +
+    536000*206//256 = 2205312 per tile; ceil(65664/206) = 319 -> chunk 320,
+    10 tiles: 13648000 + 10*2205312 + 4065000 + 287*128*206 = 47333736
+    (s=205: chunk 384, 12 tiles, 51682496; s=207: 47391412).  With wide_cap =
+    128 the best wide plan is s=128 (59171208) and the plan stays 31 narrow."""
     m = _fitted_model()
     assert pr.wide_split_cost(1, 300, 128, 1, 2048, 1, 256, m) == 376480000
     assert pr.wide_split_cost(2, 300, 128, 1, 2048, 1, 256, m) == 328938600
@@ -317,7 +325,13 @@ def test_planner_cost_worked_example_wide_family():
     assert pr.plan_decode(300, 128, 1, 2048, 1, 256, m) == (2, True)
     assert pr.plan_decode(300, 128, 1, 2048, 1, 256, m, two_source=True) == (1, False)
     assert pr.wide_split_cost(32, 1, 128, 1, 65664, 0, 256, m) == 140394552
-    assert pr.plan_decode(1, 128, 1, 65664, 0, 256, m) == (31, False)
+    assert pr.wide_split_cost(206, 1, 128, 1, 65664, 0, 256, m) == 47333736
+    assert pr.wide_split_cost(205, 1, 128, 1, 65664, 0, 256, m) == 51682496
+    assert pr.wide_split_cost(207, 1, 128, 1, 65664, 0, 256, m) == 47391412
+    assert pr.split_cost(31, 1, 128, 1, 65664, 256, m) == 55275522
+    assert pr.plan_decode(1, 128, 1, 65664, 0, 256, m) == (206, True)
+    assert pr.wide_split_cost(128, 1, 128, 1, 65664, 0, 256, m) == 59171208
+    assert pr.plan_decode(1, 128, 1, 65664, 0, 256, dataclasses.replace(m, wide_cap=128)) == (31, False)
     # M = 64 is not a multiple of 128: no wide cost at all
     assert pr.wide_split_cost(1, 8, 64, 1, 2176, 0, 256, m) is None
 
